@@ -1,0 +1,285 @@
+"""CPU oracle of the intra-expert-sparse MoE decode layer.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+execute this module: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code, header,
+table or helper with the HIP library; its only shared dependency is the
+seeded input generator ``moe_synth`` (which holds no arithmetic of the
+method).
+
+It is a plain, slow, float64 restatement of what the layer computes.
+Citations name sections of the page "Uncovering Intra-expert Activation
+Sparsity for Efficient Mixture-of-Expert Model Execution" (gist.science
+explainer of the paper by Park, Kim, Gu, Stoica and Cheung), called "the
+page" below.
+
+Layer definition (one token t):
+
+    l[e]   = x_t . W_r[e] + b[e]                 router logits
+    S_t    = the top_k experts by l (ties: lower e)
+    p      = softmax(l) over all E; w_e = p_e (e in S_t),
+             divided by sum_{S_t} p when norm_topk
+    g, u   = W_g^e x_t, W_u^e x_t;  h = silu(g) * u     (dense, SwiGLU)
+    K_t,e  = the k_keep neurons of largest |h_j| (ties: lower j)
+    y_t    = sum_{e in S_t} w_e * sum_{j in K_t,e} h_j W_d^e[j, :]
+             + sum over shared experts e' (weight 1, own mask) of the same
+
+The sparse down projection reaches exactly (up to rounding order) the dense
+down projection of the masked activation, so this file writes that
+definition out directly and touches only kept W_d rows.
+
+Every function below is pinned by tests (tests/test_oracle_pins.py) against
+closed forms, brute force, library routines or invariants; none is
+"parity unpinned".
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import Dict, Optional, Sequence, Tuple
+
+import numpy as np
+
+
+# ---------------------------------------------------------------- inputs
+
+def to_f64(a, dtype: str) -> np.ndarray:
+    """Exact float64 value of an input tensor.
+
+    ``dtype`` is "f32" (float32 array) or "bf16" (uint16 bit patterns:
+    the value is the float32 whose upper 16 bits are the pattern).  bf16
+    rounding is part of the input, never an error of the method."""
+    a = np.asarray(a)
+    if dtype == "f32":
+        return a.astype(np.float64)
+    if dtype == "bf16":
+        if a.dtype != np.uint16:
+            raise TypeError("bf16 inputs are passed as uint16 bit patterns")
+        return (a.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def _check_finite(name, a):
+    if not np.all(np.isfinite(a)):
+        raise ValueError(f"oracle: {name} holds NaN or Inf; such inputs are undefined")
+
+
+# ---------------------------------------------------------------- router
+
+def router_logits(x: np.ndarray, w_router: np.ndarray,
+                  bias: Optional[np.ndarray]) -> np.ndarray:
+    """l[t, e] = sum_h x[t, h] * W_r[e, h] + b[e]  ->  [T, E].
+
+    The router is kept unchanged by the method (the page, technical summary,
+    Methodology: vLLM implementation keeps the router logic).  A plain
+    linear router with an optional additive per-expert bias."""
+    l = x @ w_router.T
+    if bias is not None:
+        l = l + np.asarray(bias, dtype=np.float64)[None, :]
+    return l
+
+
+def softmax(l: np.ndarray) -> np.ndarray:
+    """Row softmax over the last axis: p_e = exp(l_e) / sum_e' exp(l_e')."""
+    m = np.max(l, axis=-1, keepdims=True)
+    z = np.exp(l - m)
+    return z / np.sum(z, axis=-1, keepdims=True)
+
+
+def top_experts(l_row: np.ndarray, top_k: int) -> np.ndarray:
+    """The top_k experts of one token by logit, in descending logit order;
+    equal logits go to the lower expert id (stable order of (-l, e)).
+
+    Selecting on logits selects the same set as selecting on softmax
+    probabilities, since softmax is monotone."""
+    E = l_row.shape[0]
+    order = sorted(range(E), key=lambda e: (-float(l_row[e]), e))
+    return np.asarray(order[:top_k], dtype=np.int64)
+
+
+def route(x, w_router, bias, top_k: int, norm_topk: bool):
+    """Router top-k with softmax weights.
+
+    Returns (ids [T, top_k] int64 in descending-logit slot order,
+    weights [T, top_k] float64, logits [T, E], probs [T, E])."""
+    l = router_logits(x, w_router, bias)
+    p = softmax(l)
+    T = l.shape[0]
+    ids = np.zeros((T, top_k), dtype=np.int64)
+    w = np.zeros((T, top_k), dtype=np.float64)
+    for t in range(T):
+        ids[t] = top_experts(l[t], top_k)
+        w[t] = p[t, ids[t]]
+        if norm_topk:
+            w[t] = w[t] / np.sum(w[t])
+    return ids, w, l, p
+
+
+# ---------------------------------------------------------------- expert FFN
+
+def keep_count(sparsity: float, d_ff: int) -> int:
+    """Kept neurons per (token, expert): ceil((1 - s) * d_ff), clamped to
+    [0, d_ff].
+
+    The page zeroes the lowest-scoring fraction s of each selected expert's
+    neurons (technical summary, Methodology: empirical analysis; Results:
+    sparsity levels).  A 1e-9 guard stops float noise from rounding an exact
+    integer up (naive float gives 301 for s=0.7, d_ff=1000)."""
+    k = math.ceil((1.0 - float(sparsity)) * d_ff - 1e-9)
+    return max(0, min(d_ff, k))
+
+
+def silu(z: np.ndarray) -> np.ndarray:
+    """silu(z) = z * sigmoid(z) = z / (1 + exp(-z))."""
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
+
+
+def expert_activation(x_t: np.ndarray, w_gate_e: np.ndarray,
+                      w_up_e: np.ndarray) -> np.ndarray:
+    """h = silu(W_g x) * (W_u x) for one token and one expert  ->  [d_ff].
+
+    Gate and up run densely for every selected (token, expert) pair; their
+    SwiGLU product is the activation whose magnitude scores the neurons (the
+    page, technical summary, Methodology: vLLM implementation, gate
+    projection run densely to produce activation scores)."""
+    g = w_gate_e @ x_t
+    u = w_up_e @ x_t
+    return silu(g) * u
+
+
+def kept_neurons(h: np.ndarray, k: int) -> np.ndarray:
+    """The k neurons of largest |h| (ties: lower index), ascending.
+
+    The lowest-scoring activations inside an expert are set to zero (the
+    page, technical summary, Methodology: empirical analysis and activation
+    masking).  -0 and +0 score equal."""
+    d = h.shape[0]
+    a = np.abs(h)
+    order = sorted(range(d), key=lambda j: (-float(a[j]), j))
+    return np.asarray(sorted(order[:k]), dtype=np.int64)
+
+
+def sparse_down(h: np.ndarray, keep: np.ndarray, w_down_e: np.ndarray) -> np.ndarray:
+    """sum_{j in keep} h_j * W_d[j, :]  ->  [H].
+
+    Only the kept neurons' down-projection rows are read; the zeroed neurons
+    are never loaded (the page, "how it runs: skip-list system": unneeded
+    neurons are not even loaded; technical summary, fused up-down projection
+    gathers only the active neurons' weights)."""
+    if keep.size == 0:
+        return np.zeros(w_down_e.shape[1], dtype=np.float64)
+    return h[keep] @ w_down_e[keep, :]
+
+
+# ---------------------------------------------------------------- layer
+
+@dataclass
+class LayerResult:
+    y: np.ndarray                       # [T, H] float64, routed + shared
+    y_routed: np.ndarray                # [T, H]
+    y_shared: np.ndarray                # [T, H]
+    ids: np.ndarray                     # [T, top_k]
+    weights: np.ndarray                 # [T, top_k]
+    logits: np.ndarray                  # [T, E]
+    probs: np.ndarray                   # [T, E]
+    h: Dict[Tuple[int, int], np.ndarray] = field(default_factory=dict)        # (t, slot) -> [d_ff]
+    keep: Dict[Tuple[int, int], np.ndarray] = field(default_factory=dict)     # (t, slot) -> idx
+    h_shared: Dict[Tuple[int, int], np.ndarray] = field(default_factory=dict)     # (t, j)
+    keep_shared: Dict[Tuple[int, int], np.ndarray] = field(default_factory=dict)  # (t, j)
+
+
+def routed_experts(x, ids, weights, w_gate, w_up, w_down, k_keep, dtype,
+                   forced_keep=None, keep_h=True):
+    """Routed contribution sum_{slot} w * sum_{j in K} h_j W_d^e[j, :].
+
+    Pairs are visited expert by expert so each expert's weights are
+    converted once.  ``forced_keep[(t, slot)]`` replaces the computed kept
+    set (used when a tested implementation's selection differs only on
+    scores inside the comparison window).  Returns (y [T, H], h, keep)."""
+    T, H = x.shape
+    y = np.zeros((T, H), dtype=np.float64)
+    hs, keeps = {}, {}
+    by_expert: Dict[int, list] = {}
+    for t in range(T):
+        for s in range(ids.shape[1]):
+            by_expert.setdefault(int(ids[t, s]), []).append((t, s))
+    for e in sorted(by_expert):
+        wg, wu, wd = (to_f64(w[e], dtype) for w in (w_gate, w_up, w_down))
+        for (t, s) in by_expert[e]:
+            h = expert_activation(x[t], wg, wu)
+            keep = (np.asarray(forced_keep[(t, s)], dtype=np.int64)
+                    if forced_keep is not None and (t, s) in forced_keep
+                    else kept_neurons(h, k_keep))
+            y[t] += weights[t, s] * sparse_down(h, keep, wd)
+            if keep_h:
+                hs[(t, s)] = h
+            keeps[(t, s)] = keep
+    return y, hs, keeps
+
+
+def shared_experts(x, w_gate, w_up, w_down, n_shared, k_keep, dtype,
+                   forced_keep=None, keep_h=True):
+    """Always-on shared experts: every token, weight 1, each expert with its
+    own per-(token, expert) mask of k_keep neurons.
+
+    The page treats shared experts apart from routed ones (technical
+    summary, Methodology: empirical analysis; vLLM implementation keeps
+    shared-expert execution); with k_keep = d_ff they run dense."""
+    T, H = x.shape
+    y = np.zeros((T, H), dtype=np.float64)
+    hs, keeps = {}, {}
+    for j in range(n_shared):
+        wg, wu, wd = (to_f64(w[j], dtype) for w in (w_gate, w_up, w_down))
+        for t in range(T):
+            h = expert_activation(x[t], wg, wu)
+            keep = (np.asarray(forced_keep[(t, j)], dtype=np.int64)
+                    if forced_keep is not None and (t, j) in forced_keep
+                    else kept_neurons(h, k_keep))
+            y[t] += sparse_down(h, keep, wd)
+            if keep_h:
+                hs[(t, j)] = h
+            keeps[(t, j)] = keep
+    return y, hs, keeps
+
+
+def moe_layer(x, w_router, bias, w_gate, w_up, w_down, *, top_k: int,
+              norm_topk: bool, k_keep: int, dtype: str,
+              shared: Optional[Sequence] = None, k_keep_shared: Optional[int] = None,
+              forced_ids: Optional[np.ndarray] = None,
+              forced_keep: Optional[dict] = None,
+              forced_keep_shared: Optional[dict] = None,
+              keep_h: bool = True) -> LayerResult:
+    """The whole layer for a token batch.
+
+    x [T, H], w_router [E, H] and the expert weights (indexable by expert,
+    each [d_ff, H] neuron-major) are in the layer's input dtype ("f32" arrays
+    or "bf16" uint16 bit patterns); bias is float32 [E] or None.  ``shared``
+    is (w_gate, w_up, w_down) of the shared experts or None.
+
+    ``forced_ids`` replaces the routed expert sets (slot order as given);
+    the weights are then the softmax probabilities of those experts, so a
+    tested implementation whose selection differs from this one only on
+    logits inside the comparison window can be scored exactly."""
+    xf = to_f64(x, dtype)
+    _check_finite("x", xf)
+    wr = to_f64(w_router, dtype)
+    ids, w, l, p = route(xf, wr, bias, top_k, norm_topk)
+    if forced_ids is not None:
+        ids = np.asarray(forced_ids, dtype=np.int64).reshape(ids.shape)
+        w = np.take_along_axis(p, ids, axis=1)
+        if norm_topk:
+            w = w / np.sum(w, axis=1, keepdims=True)
+    y_r, hs, keeps = routed_experts(xf, ids, w, w_gate, w_up, w_down, k_keep,
+                                    dtype, forced_keep, keep_h)
+    T, H = xf.shape
+    y_s = np.zeros((T, H))
+    hs_s, keeps_s = {}, {}
+    if shared is not None:
+        n_sh = len(shared[0])
+        ks = k_keep_shared if k_keep_shared is not None else shared[0][0].shape[0]
+        y_s, hs_s, keeps_s = shared_experts(xf, shared[0], shared[1], shared[2],
+                                            n_sh, ks, dtype, forced_keep_shared, keep_h)
+    return LayerResult(y=y_r + y_s, y_routed=y_r, y_shared=y_s, ids=ids, weights=w,
+                       logits=l, probs=p, h=hs, keep=keeps, h_shared=hs_s,
+                       keep_shared=keeps_s)

@@ -1,0 +1,374 @@
+"""Pins of the CPU oracle to things other than itself.
+
+Each test checks the oracle against a closed form, a hand-derived worked
+example, brute-force enumeration, a library routine or an invariant of the
+definition, chosen so that a plausible slip (|h| vs h, largest vs smallest,
+a tie going the wrong way, gate and up swapped, a dropped router weight or
+renormalisation, a wrong W_d row) fails at least one of them.  CPU only.
+"""
+import itertools
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+import torch.nn.functional as F
+
+import oracle
+from oracle import moe_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ------------------------------------------------------------ keep count
+
+def _golden_keep_rows():
+    rows = []
+    with open(os.path.join(GOLDEN, "keep_counts.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            s, d, k = line.split()[:3]
+            rows.append((s, int(d), int(k)))
+    return rows
+
+
+@pytest.mark.parametrize("s,d_ff,k", _golden_keep_rows())
+def test_keep_count_golden(s, d_ff, k):
+    # fixture value, and the exact rational ceiling of (1 - s) * d_ff
+    exact = math.ceil((1 - Fraction(s)) * d_ff)
+    assert exact == k
+    assert O.keep_count(float(s), d_ff) == k
+
+
+def test_keep_count_exact_rational_sweep():
+    # every sparsity with up to 3 decimals against exact rationals
+    for d_ff in (512, 768, 1000, 1024, 1536, 8192):
+        for m in range(0, 1001):
+            s = Fraction(m, 1000)
+            assert O.keep_count(float(s), d_ff) == math.ceil((1 - s) * d_ff), (m, d_ff)
+
+
+# ------------------------------------------------------------ selection
+
+def _dominates(score, K, n):
+    """Brute-force definition: K holds the |K| best by (score desc, index asc)."""
+    Ks = set(K)
+    for i in Ks:
+        for j in range(n):
+            if j in Ks:
+                continue
+            if not (score[i] > score[j] or (score[i] == score[j] and i < j)):
+                return False
+    return True
+
+
+def _tie_heavy(rng, n):
+    vals = np.array([-2.0, -1.0, -0.0, 0.0, 1.0, 2.0, 0.5, -0.5])
+    return vals[rng.integers(0, len(vals), n)]
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_kept_neurons_brute_force(seed):
+    rng = np.random.default_rng(seed)
+    n = int(rng.integers(1, 10))
+    h = _tie_heavy(rng, n) if seed % 2 else rng.standard_normal(n)
+    for k in range(n + 1):
+        got = O.kept_neurons(h, k)
+        assert list(got) == sorted(got)
+        winners = [c for c in itertools.combinations(range(n), k)
+                   if _dominates(np.abs(h), c, n)]
+        assert len(winners) == 1
+        assert tuple(got) == winners[0]
+
+
+def test_kept_neurons_uses_magnitude_and_zero_signs():
+    h = np.array([-3.0, 1.0, 2.0, -0.0, 0.0])
+    assert list(O.kept_neurons(h, 1)) == [0]           # |-3| wins: magnitude, not value
+    assert list(O.kept_neurons(h, 2)) == [0, 2]
+    assert list(O.kept_neurons(h, 4)) == [0, 1, 2, 3]  # -0 == +0, lower index first
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_top_experts_brute_force(seed):
+    rng = np.random.default_rng(100 + seed)
+    E = int(rng.integers(1, 9))
+    l = _tie_heavy(rng, E) if seed % 2 else rng.standard_normal(E)
+    for k in range(1, E + 1):
+        got = O.top_experts(l, k)
+        winners = [c for c in itertools.combinations(range(E), k) if _dominates(l, c, E)]
+        assert len(winners) == 1
+        assert sorted(got) == list(winners[0])          # signed logits, not |l|
+        # slot order: descending logit, ties to the lower id
+        keys = [(-l[e], e) for e in got]
+        assert keys == sorted(keys)
+
+
+# ------------------------------------------------------------ softmax / route
+
+def test_softmax_closed_form():
+    l = np.array([[math.log(3.0), 0.0, math.log(4.0)]])
+    np.testing.assert_allclose(O.softmax(l), [[3 / 8, 1 / 8, 4 / 8]], rtol=1e-15)
+    np.testing.assert_allclose(O.softmax(np.array([[1000.0, 1000.0]])), [[0.5, 0.5]])
+    # ratio property p_i / p_j = exp(l_i - l_j)
+    rng = np.random.default_rng(1)
+    l = rng.standard_normal((4, 7)) * 3
+    p = O.softmax(l)
+    np.testing.assert_allclose(p[:, 1] / p[:, 4], np.exp(l[:, 1] - l[:, 4]), rtol=1e-12)
+    np.testing.assert_allclose(p.sum(axis=1), 1.0, rtol=1e-14)
+
+
+@pytest.mark.parametrize("norm", [False, True])
+def test_route_against_torch(norm):
+    rng = np.random.default_rng(7)
+    T, H, E, k = 6, 32, 12, 3
+    x = rng.standard_normal((T, H))
+    wr = rng.standard_normal((E, H)) / np.sqrt(H)
+    b = rng.standard_normal(E).astype(np.float32)
+    ids, w, l, p = O.route(x, wr, b, k, norm)
+    lt = F.linear(torch.from_numpy(x), torch.from_numpy(wr)) + torch.from_numpy(b).double()
+    pt = torch.softmax(lt, dim=-1)
+    tv, ti = torch.topk(pt, k, dim=-1)          # random data: no ties
+    if norm:
+        tv = tv / tv.sum(dim=-1, keepdim=True)
+    np.testing.assert_array_equal(ids, ti.numpy())
+    np.testing.assert_allclose(w, tv.numpy(), rtol=1e-13)
+    if norm:
+        np.testing.assert_allclose(w.sum(axis=1), 1.0, rtol=1e-14)
+
+
+# ------------------------------------------------------------ activation
+
+def test_silu_library_and_limits():
+    z = np.linspace(-30, 30, 1001)
+    np.testing.assert_allclose(O.silu(z), z * scipy.special.expit(z), rtol=1e-13, atol=1e-300)
+    assert O.silu(np.array([0.0]))[0] == 0.0
+    big = O.silu(np.array([-800.0, 800.0]))
+    assert np.all(np.isfinite(big)) and big[0] == 0.0 and big[1] == 800.0
+
+
+def test_expert_activation_against_torch():
+    rng = np.random.default_rng(3)
+    H, d = 48, 40
+    x = rng.standard_normal(H)
+    wg, wu = rng.standard_normal((d, H)), rng.standard_normal((d, H))
+    want = (F.silu(F.linear(torch.from_numpy(x), torch.from_numpy(wg)))
+            * F.linear(torch.from_numpy(x), torch.from_numpy(wu))).numpy()
+    np.testing.assert_allclose(O.expert_activation(x, wg, wu), want, rtol=1e-12, atol=1e-14)
+    # gate and up are not interchangeable
+    assert not np.allclose(O.expert_activation(x, wu, wg), want)
+
+
+def test_sparse_down_reads_only_kept_rows():
+    rng = np.random.default_rng(4)
+    d, H = 20, 16
+    h = rng.standard_normal(d)
+    wd = rng.standard_normal((d, H))
+    keep = O.kept_neurons(h, 5)
+    poisoned = np.full_like(wd, np.nan)
+    poisoned[keep] = wd[keep]
+    got = O.sparse_down(h, keep, poisoned)
+    hm = np.zeros(d)
+    hm[keep] = h[keep]
+    assert np.all(np.isfinite(got))
+    np.testing.assert_allclose(got, hm @ wd, rtol=1e-13)
+    assert np.all(O.sparse_down(h, keep[:0], poisoned) == 0)
+
+
+# ------------------------------------------------------------ worked examples
+
+def _eval_expr(s):
+    return float(eval(s, {"__builtins__": {}}, {"exp": math.exp}))
+
+
+def _golden_cases():
+    with open(os.path.join(GOLDEN, "worked_examples.json")) as f:
+        return json.load(f)["cases"]
+
+
+@pytest.mark.parametrize("case", _golden_cases(), ids=lambda c: c["name"])
+def test_worked_example(case):
+    f32 = lambda a: np.asarray(a, dtype=np.float32)
+    bias = None if case["bias"] is None else f32(case["bias"])
+    r = oracle.moe_layer(f32(case["x"]), f32(case["w_router"]), bias,
+                         f32(case["w_gate"]), f32(case["w_up"]), f32(case["w_down"]),
+                         top_k=case["top_k"], norm_topk=case["norm_topk"],
+                         k_keep=case["k_keep"], dtype="f32")
+    np.testing.assert_array_equal(r.ids, case["expect_ids"])
+    want = np.array([[_eval_expr(s) for s in row] for row in case["expect"]])
+    np.testing.assert_allclose(r.y, want, rtol=1e-14, atol=1e-15)
+
+
+# ------------------------------------------------------------ whole layer
+
+def _rand_layer(seed, T=3, H=16, E=6, d=12, dtype="f32"):
+    rng = np.random.default_rng(seed)
+    f = lambda *s: (rng.standard_normal(s) / np.sqrt(s[-1])).astype(np.float32)
+    return dict(x=rng.standard_normal((T, H)).astype(np.float32), wr=f(E, H),
+                bias=rng.standard_normal(E).astype(np.float32) * 0.1,
+                wg=f(E, d, H), wu=f(E, d, H), wd=(rng.standard_normal((E, d, H)) / np.sqrt(d)).astype(np.float32))
+
+
+def _run(L, top_k, norm, k, **kw):
+    return oracle.moe_layer(L["x"], L["wr"], L["bias"], L["wg"], L["wu"], L["wd"],
+                            top_k=top_k, norm_topk=norm, k_keep=k, dtype="f32", **kw)
+
+
+def _brute_layer(L, top_k, norm, k):
+    """Scalar float64 loops; mask by brute-force subset enumeration."""
+    x, wr, b, wg, wu, wd = (np.asarray(L[n], dtype=np.float64) for n in ("x", "wr", "bias", "wg", "wu", "wd"))
+    T, H = x.shape
+    E, d, _ = wg.shape
+    y = [[0.0] * H for _ in range(T)]
+    for t in range(T):
+        logit = [sum(x[t, i] * wr[e, i] for i in range(H)) + b[e] for e in range(E)]
+        sel = next(c for c in itertools.combinations(range(E), top_k) if _dominates(logit, c, E))
+        m = max(logit)
+        z = sum(math.exp(v - m) for v in logit)
+        p = {e: math.exp(logit[e] - m) / z for e in sel}
+        tot = sum(p.values())
+        for e in sel:
+            w = p[e] / tot if norm else p[e]
+            h = []
+            for j in range(d):
+                g = sum(wg[e, j, i] * x[t, i] for i in range(H))
+                u = sum(wu[e, j, i] * x[t, i] for i in range(H))
+                h.append(g / (1 + math.exp(-g)) * u)
+            K = next(c for c in itertools.combinations(range(d), k)
+                     if _dominates([abs(v) for v in h], c, d))
+            for j in K:
+                for i in range(H):
+                    y[t][i] += w * h[j] * wd[e, j, i]
+    return np.array(y)
+
+
+@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("top_k,norm,k", [(2, False, 3), (3, True, 1), (1, True, 12), (2, False, 0)])
+def test_layer_brute_force(seed, top_k, norm, k):
+    L = _rand_layer(seed, T=2, H=8, E=5, d=8 if k != 12 else 12)
+    r = _run(L, top_k, norm, k)
+    np.testing.assert_allclose(r.y, _brute_layer(L, top_k, norm, k), rtol=1e-11, atol=1e-13)
+
+
+def _torch_dense_moe(L, top_k, norm):
+    """A dense MoE layer from torch library calls (no masking)."""
+    td = lambda a: torch.from_numpy(np.asarray(a, dtype=np.float64))
+    x = td(L["x"])
+    p = torch.softmax(F.linear(x, td(L["wr"])) + td(L["bias"]), dim=-1)
+    val, idx = torch.topk(p, top_k, dim=-1)
+    if norm:
+        val = val / val.sum(-1, keepdim=True)
+    y = torch.zeros_like(x)
+    for t in range(x.shape[0]):
+        for s in range(top_k):
+            e = int(idx[t, s])
+            act = F.silu(F.linear(x[t], td(L["wg"][e]))) * F.linear(x[t], td(L["wu"][e]))
+            y[t] += val[t, s] * F.linear(act, td(L["wd"][e]).T)   # down_proj.weight is W_d^T
+    return y.numpy()
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_sparsity_zero_is_dense_moe(seed):
+    L = _rand_layer(seed, T=4, H=32, E=8, d=24)
+    for top_k, norm in ((2, False), (3, True)):
+        r = _run(L, top_k, norm, O.keep_count(0.0, 24))
+        np.testing.assert_allclose(r.y, _torch_dense_moe(L, top_k, norm), rtol=1e-12, atol=1e-14)
+
+
+def test_single_expert_is_textbook_swiglu_ffn():
+    L = _rand_layer(9, T=3, H=32, E=1, d=24)
+    r = _run(L, 1, True, 24)
+    x = torch.from_numpy(L["x"]).double()
+    ffn = F.linear(F.silu(F.linear(x, torch.from_numpy(L["wg"][0]).double()))
+                   * F.linear(x, torch.from_numpy(L["wu"][0]).double()),
+                   torch.from_numpy(L["wd"][0]).double().T)
+    np.testing.assert_allclose(r.y, ffn.numpy(), rtol=1e-12, atol=1e-14)
+
+
+def test_zeroed_neurons_contribute_nothing():
+    L = _rand_layer(11, T=4, H=32, E=8, d=40)
+    r = _run(L, 2, False, 4)
+    # poison every W_d row that no pair keeps
+    wd = L["wd"].copy()
+    used = {}
+    for (t, s), keep in r.keep.items():
+        used.setdefault(int(r.ids[t, s]), set()).update(int(j) for j in keep)
+    for e in range(wd.shape[0]):
+        for j in range(wd.shape[1]):
+            if j not in used.get(e, ()):
+                wd[e, j] = np.nan
+    r2 = _run(dict(L, wd=wd), 2, False, 4)
+    assert np.all(np.isfinite(r2.y))
+    np.testing.assert_array_equal(r2.y, r.y)
+    # and the kept count is exactly k for every pair
+    assert all(len(v) == 4 for v in r.keep.values())
+
+
+def test_batch_invariance():
+    L = _rand_layer(12, T=5, H=32, E=8, d=24)
+    full = _run(L, 2, True, 5)
+    for t in range(5):
+        one = _run(dict(L, x=L["x"][t:t + 1]), 2, True, 5)
+        # equal up to BLAS blocking order; the same experts and neurons
+        np.testing.assert_allclose(one.y[0], full.y[t], rtol=1e-13, atol=1e-16)
+        assert np.array_equal(one.ids[0], full.ids[t])
+
+
+def test_expert_permutation_invariance():
+    L = _rand_layer(13, T=4, H=32, E=8, d=24)
+    perm = np.random.default_rng(0).permutation(8)
+    P = {n: L[n][perm] for n in ("wr", "bias", "wg", "wu", "wd")}
+    a = _run(L, 3, False, 6)
+    b = _run(dict(L, **P), 3, False, 6)
+    np.testing.assert_allclose(a.y, b.y, rtol=1e-13, atol=1e-15)
+    np.testing.assert_array_equal(perm[b.ids], a.ids)
+
+
+def test_up_scaling_and_sign_flip_keep_mask():
+    L = _rand_layer(14, T=3, H=32, E=4, d=24)
+    a = _run(L, 1, True, 5)
+    wu = L["wu"].copy()
+    wu *= 2.0                                    # exact in binary
+    b = _run(dict(L, wu=wu), 1, True, 5)
+    assert all(np.array_equal(a.keep[key], b.keep[key]) for key in a.keep)
+    np.testing.assert_allclose(b.y, 2.0 * a.y, rtol=1e-14)
+    wu = L["wu"].copy()
+    wu[:, ::2] *= -1                             # flip the sign of every even neuron
+    c = _run(dict(L, wu=wu), 1, True, 5)
+    assert all(np.array_equal(a.keep[key], c.keep[key]) for key in a.keep)
+
+
+def test_shared_experts_weight_one_own_mask():
+    L = _rand_layer(15, T=3, H=32, E=4, d=24)
+    S = _rand_layer(16, T=3, H=32, E=2, d=16)
+    r = _run(L, 2, False, 5, shared=(S["wg"], S["wu"], S["wd"]), k_keep_shared=16)
+    # shared part at k = d_ff is two dense SwiGLU FFNs summed with weight 1
+    x = torch.from_numpy(L["x"]).double()
+    want = sum(F.linear(F.silu(F.linear(x, torch.from_numpy(S["wg"][j]).double()))
+                        * F.linear(x, torch.from_numpy(S["wu"][j]).double()),
+                        torch.from_numpy(S["wd"][j]).double().T) for j in range(2))
+    np.testing.assert_allclose(r.y_shared, want.numpy(), rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(r.y, r.y_routed + r.y_shared, rtol=0, atol=0)
+    r2 = _run(L, 2, False, 5, shared=(S["wg"], S["wu"], S["wd"]), k_keep_shared=8)
+    assert all(len(v) == 8 for v in r2.keep_shared.values())
+
+
+def test_forced_mode_reproduces_own_choice():
+    L = _rand_layer(17, T=4, H=32, E=8, d=24)
+    a = _run(L, 3, True, 5)
+    b = _run(L, 3, True, 5, forced_ids=a.ids, forced_keep=a.keep)
+    np.testing.assert_array_equal(a.y, b.y)
+
+
+def test_bf16_inputs_are_exact_bit_patterns():
+    bits = np.array([0x3F80, 0xBF80, 0x4049, 0x0000, 0x8000, 0x3E80], dtype=np.uint16)
+    np.testing.assert_array_equal(O.to_f64(bits, "bf16"), [1.0, -1.0, 3.140625, 0.0, -0.0, 0.25])
+    with pytest.raises(ValueError):
+        oracle.moe_layer(np.array([[np.nan, 0.0]], dtype=np.float32), np.zeros((2, 2), np.float32),
+                         None, np.zeros((2, 2, 2), np.float32), np.zeros((2, 2, 2), np.float32),
+                         np.zeros((2, 2, 2), np.float32), top_k=1, norm_topk=False, k_keep=1, dtype="f32")
