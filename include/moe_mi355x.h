@@ -1,0 +1,203 @@
+/*
+ * moe_mi355x.h -- C ABI of the intra-expert-sparse MoE decode layer for
+ * AMD MI355X (gfx950).  Library: libmoe_mi355x.so.
+ *
+ * The layer (router top-k -> dense SwiGLU gate/up -> zero the lowest-|h|
+ * neurons -> down projection over the surviving rows only) follows the page
+ * "Uncovering Intra-expert Activation Sparsity for Efficient
+ * Mixture-of-Expert Model Execution" (gist.science explainer of the paper by
+ * Park, Kim, Gu, Stoica and Cheung), called "the page" below; each entry
+ * point names the section of the page it implements.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every tensor pointer is caller-owned DEVICE memory on the current HIP
+ *   device.  The library never allocates, frees or keeps a pointer after
+ *   returning.  Scratch memory comes from the caller's `workspace`, sized by
+ *   the matching *_workspace_size() call (the workspace contents between
+ *   calls are not needed by the library; it may be reused freely once the
+ *   stream has consumed the call).
+ * - Calls only ENQUEUE kernels on `stream` (0 = the null stream).  They never
+ *   synchronise, copy to the host or allocate, so a sequence of them can be
+ *   captured into a HIP graph.  Grids depend on shapes only; data-dependent
+ *   counts (active experts, tokens per expert) are read on the device.
+ * - Arguments are validated before anything is enqueued; on any error
+ *   nothing is enqueued and every output is untouched.  moe_last_error()
+ *   then gives a description (thread-local).  MOE_ERR_HIP means a launch
+ *   failed; the stream's contents are then unspecified.
+ * - T == 0 is a valid no-op returning MOE_OK.
+ * - NaN or Inf in x or weights gives unspecified (but memory-safe) results.
+ * - Every tensor base pointer must be 16-byte aligned (MOE_ERR_MISALIGNED).
+ * - Layouts are row-major.  Expert weights are [E, d_ff, H] NEURON-MAJOR for
+ *   gate, up AND down: row j of the down matrix is neuron j's H-vector
+ *   contribution (the transpose of a torch down_proj.weight [H, d_ff]), so
+ *   a kept neuron's down row is one contiguous H * elem_bytes stream.
+ * - dtype MOE_BF16: x, router and expert weights are bf16 (raw bits,
+ *   round-to-nearest-even), every accumulation is fp32; MOE_F32: all fp32.
+ *   Router logits, softmax weights, h and y are fp32 in both.
+ * - The library holds no global state and is reentrant; two calls that
+ *   share a workspace must be ordered on one stream.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,  /* NULL where a tensor is required, bad size, k out of range */
+  MOE_ERR_MISALIGNED = 2,   /* a tensor base pointer is not 16-byte aligned              */
+  MOE_ERR_WORKSPACE = 3,    /* workspace NULL or smaller than *_workspace_size()          */
+  MOE_ERR_UNSUPPORTED = 4,  /* shape outside the limits below, unknown dtype or path      */
+  MOE_ERR_HIP = 5           /* a kernel launch failed                                     */
+} moe_status;
+
+typedef enum { MOE_PATH_SPARSE = 0, MOE_PATH_DENSE = 1 } moe_path;
+
+/* Limits (MOE_ERR_UNSUPPORTED outside them). */
+#define MOE_MAX_HIDDEN 16384   /* H: multiple of 64                        */
+#define MOE_MAX_EXPERTS 1024   /* E                                        */
+#define MOE_MAX_DFF 8192       /* d_ff: multiple of 64                     */
+#define MOE_MAX_TOPK 32        /* router top_k, <= E                       */
+#define MOE_MAX_TOKENS 65536   /* T per call                               */
+
+/* Geometry of ONE expert group (the routed experts, or the shared ones). */
+typedef struct {
+  int32_t hidden;     /* H                                                        */
+  int32_t n_experts;  /* E                                                        */
+  int32_t d_ff;       /* per-expert intermediate size                             */
+  int32_t top_k;      /* experts per token; for a shared group (routing == NULL)
+                         it must equal n_experts                                  */
+  int32_t norm_topk;  /* 1: renormalise the selected softmax weights to sum 1    */
+  int32_t dtype;      /* moe_dtype                                                */
+} moe_desc;
+
+/* Routing of a token batch, written by moe_route, read by the FFN calls.
+ * All device pointers, caller-owned.  A pair is one (token, slot):
+ * pair id p = t * top_k + slot, P = T * top_k. */
+typedef struct {
+  int32_t *topk_ids;        /* [T, top_k] expert ids; slot order = descending logit,
+                               equal logits -> lower expert id                       */
+  float *topk_w;            /* [T, top_k] softmax weight of each selected expert
+                               (renormalised over the selection if norm_topk)        */
+  int32_t *expert_offsets;  /* [E + 1] CSR offsets into pair_by_expert               */
+  int32_t *pair_by_expert;  /* [P] pair ids grouped by expert; within an expert in
+                               ascending token order (stable counting sort)          */
+  int32_t *active_experts;  /* [E] ids of experts with >= 1 pair, ascending; entries
+                               at and after n_active are unspecified                 */
+  int32_t *n_active;        /* [1] number of active experts                          */
+} moe_routing;
+
+/*
+ * moe_route -- router logits, softmax, top-k selection and the
+ * token -> expert grouping.
+ *
+ * The page keeps the router unchanged (technical summary, Methodology: vLLM
+ * implementation, router logic preserved); the grouping lets each expert's
+ * tokens run as one batched product (same section: the gate projection
+ * runs as a batched matrix multiply).
+ *
+ *   l[t, e] = sum_h x[t, h] * w_router[e, h] + bias[e]       (fp32 accumulate)
+ *   S_t     = top_k experts by l[t, :], ties -> lower e
+ *   topk_w  = softmax over ALL E of l[t, :], taken at S_t; divided by its
+ *             sum over S_t when norm_topk
+ *
+ * x [T, H] and w_router [E, H] in desc->dtype; bias [E] fp32 or NULL.
+ * Writes every field of *out.  workspace: moe_route_workspace_size(d, T).
+ */
+moe_status moe_route(const moe_desc *d, int32_t T, const void *x, const void *w_router,
+                     const float *bias, const moe_routing *out, void *workspace,
+                     size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * moe_expert_ffn_sparse -- the expert FFN with intra-expert activation
+ * sparsity, for the small-batch path.
+ *
+ * For every pair (t, e) of `routing` (or, with routing == NULL, every token
+ * with every expert of the group at weight 1, as for always-on shared
+ * experts):
+ *   h   = silu(W_g^e x_t) * (W_u^e x_t)         dense, fp32   (page: technical
+ *         summary, Methodology: vLLM implementation, gate projection run
+ *         densely to give activation scores)
+ *   K   = the k_keep neurons of largest |h|, ties -> lower index (page:
+ *         activation masking, a single O(n) pass with no sort; here an exact
+ *         radix select of the k-th |h| then one threshold pass)
+ *   y_t (+)= w_te * sum_{j in K} h_j * W_d^e[j, :]  only the kept rows of
+ *         W_d are read (page: "how it runs: skip-list system", unneeded
+ *         neurons are never loaded; fused up-down projection gathers only
+ *         the active neurons' weights)
+ * y [T, H] fp32 is overwritten (accumulate == 0) or added to (== 1); the sum
+ * over a token's experts runs in slot order with no atomics, so results are
+ * bitwise reproducible.
+ *
+ * k_keep in [0, d_ff]; k_keep == d_ff keeps every neuron, 0 adds nothing.
+ * x [T, H] and w_gate, w_up, w_down [E, d_ff, H] in desc->dtype.
+ * active_idx_out: optional [T * top_k, k_keep] int32, the kept neuron ids of
+ * each pair in ascending order (NULL to skip).
+ * workspace: moe_ffn_workspace_size(d, T, k_keep, MOE_PATH_SPARSE).
+ */
+moe_status moe_expert_ffn_sparse(const moe_desc *d, int32_t T, int32_t k_keep, const void *x,
+                                 const void *w_gate, const void *w_up, const void *w_down,
+                                 const moe_routing *routing, float *y, int32_t accumulate,
+                                 int32_t *active_idx_out, void *workspace,
+                                 size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * moe_expert_ffn_dense -- the same layer function on the dense path the
+ * page switches to at large batch (technical summary, Methodology: dynamic
+ * switch between sparse and dense code paths by batch size).  Gate/up and
+ * down run as grouped MFMA GEMMs over every row of each active expert; the
+ * k_keep mask is applied to h in between, so the result equals
+ * moe_expert_ffn_sparse's up to fp32 rounding order (bf16: h is rounded to
+ * bf16 for the down GEMM).  k_keep == d_ff is the plain dense MoE.
+ * Parameters as moe_expert_ffn_sparse;
+ * workspace: moe_ffn_workspace_size(d, T, k_keep, MOE_PATH_DENSE).
+ */
+moe_status moe_expert_ffn_dense(const moe_desc *d, int32_t T, int32_t k_keep, const void *x,
+                                const void *w_gate, const void *w_up, const void *w_down,
+                                const moe_routing *routing, float *y, int32_t accumulate,
+                                int32_t *active_idx_out, void *workspace,
+                                size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes for moe_route over at most T tokens (0 on invalid input). */
+size_t moe_route_workspace_size(const moe_desc *d, int32_t T);
+
+/* Workspace bytes for an FFN call over at most T tokens with this k_keep and
+ * path (0 on invalid input).  A workspace sized for (T, k_keep) serves any
+ * call with fewer tokens and the same k_keep. */
+size_t moe_ffn_workspace_size(const moe_desc *d, int32_t T, int32_t k_keep, moe_path path);
+
+/* Kept neurons per (token, expert) at sparsity s: ceil((1 - s) * d_ff),
+ * computed as ceil((1 - s) * d_ff - 1e-9) so that exact products do not
+ * round up, clamped to [0, d_ff]; -1 if d_ff < 0 or s is not finite. */
+int32_t moe_keep_count(double sparsity, int32_t d_ff);
+
+/* Host-side, shape-only choice between the sparse and dense paths for T
+ * tokens at this k_keep (the page's batch-size switch).  Never reads device
+ * memory; safe during graph capture.  Returns MOE_PATH_SPARSE on invalid
+ * input.  MOE_FORCE_PATH=sparse|dense in the environment overrides it. */
+moe_path moe_select_path(const moe_desc *d, int32_t T, int32_t k_keep);
+
+/* Static name of a status code. */
+const char *moe_status_string(moe_status s);
+
+/* Detail of the last error returned on this thread ("" if none). */
+const char *moe_last_error(void);
+
+/* Library version string. */
+const char *moe_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

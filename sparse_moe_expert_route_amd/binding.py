@@ -1,0 +1,202 @@
+"""ctypes binding of libmoe_mi355x.so (include/moe_mi355x.h).
+
+Argument marshalling only: torch tensors supply device pointers, the
+current torch stream supplies the HIP stream, and every step of the layer
+runs in the library's kernels.  If the library is not built, loading fails
+loudly; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from dataclasses import dataclass
+from typing import Optional
+
+from .build import INCLUDE, LIB_PATH
+
+MOE_F32, MOE_BF16 = 0, 1
+MOE_PATH_SPARSE, MOE_PATH_DENSE = 0, 1
+STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_MISALIGNED", 3: "MOE_ERR_WORKSPACE",
+          4: "MOE_ERR_UNSUPPORTED", 5: "MOE_ERR_HIP"}
+HEADER = os.path.join(INCLUDE, "moe_mi355x.h")
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{STATUS.get(status, status)}: {detail}")
+        self.status = status
+        self.detail = detail
+
+
+class MoeDesc(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("n_experts", ctypes.c_int32),
+                ("d_ff", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("norm_topk", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+class MoeRouting(ctypes.Structure):
+    _fields_ = [("topk_ids", ctypes.c_void_p), ("topk_w", ctypes.c_void_p),
+                ("expert_offsets", ctypes.c_void_p), ("pair_by_expert", ctypes.c_void_p),
+                ("active_experts", ctypes.c_void_p), ("n_active", ctypes.c_void_p)]
+
+
+_V, _I32, _SZ, _D = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_double
+_PD, _PR = ctypes.POINTER(MoeDesc), ctypes.POINTER(MoeRouting)
+_SIGS = {
+    "moe_route": (_I32, [_PD, _I32, _V, _V, _V, _PR, _V, _SZ, _V]),
+    "moe_expert_ffn_sparse": (_I32, [_PD, _I32, _I32, _V, _V, _V, _V, _PR, _V, _I32, _V, _V, _SZ, _V]),
+    "moe_expert_ffn_dense": (_I32, [_PD, _I32, _I32, _V, _V, _V, _V, _PR, _V, _I32, _V, _V, _SZ, _V]),
+    "moe_route_workspace_size": (_SZ, [_PD, _I32]),
+    "moe_ffn_workspace_size": (_SZ, [_PD, _I32, _I32, _I32]),
+    "moe_keep_count": (_I32, [_D, _I32]),
+    "moe_select_path": (_I32, [_PD, _I32, _I32]),
+    "moe_status_string": (ctypes.c_char_p, [_I32]),
+    "moe_last_error": (ctypes.c_char_p, []),
+    "moe_version": (ctypes.c_char_p, []),
+}
+
+_lib = None
+
+
+def header_functions():
+    """Names of the functions include/moe_mi355x.h declares."""
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m sparse_moe_expert_route_amd.build` "
+                "(the layer has no fallback)")
+        # torch ships its own HIP runtime under the same soname; loading torch
+        # first makes this library bind to that one, so the process holds a
+        # single runtime (two runtimes in one process do not share devices).
+        import torch  # noqa: F401
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.restype, fn.argtypes = res, args
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise MoeError(status, lib().moe_last_error().decode())
+
+
+def make_desc(hidden, n_experts, d_ff, top_k, norm_topk, dtype) -> MoeDesc:
+    dt = {"f32": MOE_F32, "bf16": MOE_BF16, MOE_F32: MOE_F32, MOE_BF16: MOE_BF16}[dtype]
+    return MoeDesc(int(hidden), int(n_experts), int(d_ff), int(top_k), int(bool(norm_topk)), dt)
+
+
+# ------------------------------------------------------------ tensor marshalling
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError("tensors passed to the HIP library must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the HIP library must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+@dataclass
+class Routing:
+    """Device buffers of one token batch's routing (moe_routing)."""
+    topk_ids: "object"
+    topk_w: "object"
+    expert_offsets: "object"
+    pair_by_expert: "object"
+    active_experts: "object"
+    n_active: "object"
+
+    @classmethod
+    def allocate(cls, T: int, top_k: int, n_experts: int, device="cuda"):
+        import torch
+        P = max(1, T * top_k)
+        i32 = dict(dtype=torch.int32, device=device)
+        return cls(torch.empty((max(T, 1), top_k), **i32),
+                   torch.empty((max(T, 1), top_k), dtype=torch.float32, device=device),
+                   torch.empty(n_experts + 1, **i32), torch.empty(P, **i32),
+                   torch.empty(n_experts, **i32), torch.empty(1, **i32))
+
+    def as_c(self) -> MoeRouting:
+        return MoeRouting(*(_ptr(getattr(self, f)) for f, _ in MoeRouting._fields_))
+
+
+# ------------------------------------------------------------ the C entry points
+
+def moe_route(desc: MoeDesc, T: int, x, w_router, bias, routing: Routing, workspace, stream=None):
+    r = routing.as_c()
+    ws = _ptr(workspace)
+    _check(lib().moe_route(ctypes.byref(desc), int(T), _ptr(x), _ptr(w_router), _ptr(bias),
+                           ctypes.byref(r), ws, workspace.numel() * workspace.element_size() if ws else 0,
+                           _stream(stream)))
+
+
+def _ffn(fn, desc, T, k_keep, x, w_gate, w_up, w_down, routing, y, accumulate, active_idx_out,
+         workspace, stream):
+    r = routing.as_c() if routing is not None else None
+    ws = _ptr(workspace)
+    _check(fn(ctypes.byref(desc), int(T), int(k_keep), _ptr(x), _ptr(w_gate), _ptr(w_up),
+              _ptr(w_down), ctypes.byref(r) if r is not None else None, _ptr(y), int(accumulate),
+              _ptr(active_idx_out), ws,
+              workspace.numel() * workspace.element_size() if ws else 0, _stream(stream)))
+
+
+def moe_expert_ffn_sparse(desc, T, k_keep, x, w_gate, w_up, w_down, routing, y, accumulate=0,
+                          active_idx_out=None, workspace=None, stream=None):
+    _ffn(lib().moe_expert_ffn_sparse, desc, T, k_keep, x, w_gate, w_up, w_down, routing, y,
+         accumulate, active_idx_out, workspace, stream)
+
+
+def moe_expert_ffn_dense(desc, T, k_keep, x, w_gate, w_up, w_down, routing, y, accumulate=0,
+                         active_idx_out=None, workspace=None, stream=None):
+    _ffn(lib().moe_expert_ffn_dense, desc, T, k_keep, x, w_gate, w_up, w_down, routing, y,
+         accumulate, active_idx_out, workspace, stream)
+
+
+def moe_route_workspace_size(desc: MoeDesc, T: int) -> int:
+    return int(lib().moe_route_workspace_size(ctypes.byref(desc), int(T)))
+
+
+def moe_ffn_workspace_size(desc: MoeDesc, T: int, k_keep: int, path: int) -> int:
+    return int(lib().moe_ffn_workspace_size(ctypes.byref(desc), int(T), int(k_keep), int(path)))
+
+
+def moe_keep_count(sparsity: float, d_ff: int) -> int:
+    return int(lib().moe_keep_count(float(sparsity), int(d_ff)))
+
+
+def moe_select_path(desc: MoeDesc, T: int, k_keep: int) -> int:
+    return int(lib().moe_select_path(ctypes.byref(desc), int(T), int(k_keep)))
+
+
+def moe_status_string(status: int) -> str:
+    return lib().moe_status_string(int(status)).decode()
+
+
+def moe_last_error() -> str:
+    return lib().moe_last_error().decode()
+
+
+def moe_version() -> str:
+    return lib().moe_version().decode()

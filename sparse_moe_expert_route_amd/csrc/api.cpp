@@ -1,0 +1,294 @@
+// C ABI of libmoe_mi355x.so: argument validation, workspace carve-up and
+// launch sequencing.  Every check runs before anything is enqueued, so an
+// error leaves the stream and all outputs untouched.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "moe_mi355x.h"
+#include "internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+moe_status fail(moe_status s, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+constexpr size_t kAlign = 256;
+size_t up(size_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+moe_status check_desc(const moe_desc *d) {
+  if (!d) return fail(MOE_ERR_INVALID_ARG, "desc is NULL");
+  if (d->dtype != MOE_F32 && d->dtype != MOE_BF16)
+    return fail(MOE_ERR_UNSUPPORTED, "dtype %d is not MOE_F32 or MOE_BF16", d->dtype);
+  if (d->hidden <= 0 || d->n_experts <= 0 || d->d_ff <= 0 || d->top_k <= 0)
+    return fail(MOE_ERR_INVALID_ARG, "hidden, n_experts, d_ff and top_k must be positive");
+  if (d->top_k > d->n_experts)
+    return fail(MOE_ERR_INVALID_ARG, "top_k %d exceeds n_experts %d", d->top_k, d->n_experts);
+  if (d->norm_topk != 0 && d->norm_topk != 1)
+    return fail(MOE_ERR_INVALID_ARG, "norm_topk must be 0 or 1");
+  if (d->hidden > MOE_MAX_HIDDEN || d->hidden % 64)
+    return fail(MOE_ERR_UNSUPPORTED, "hidden %d: need a multiple of 64 up to %d", d->hidden,
+                MOE_MAX_HIDDEN);
+  if (d->d_ff > MOE_MAX_DFF || d->d_ff % 64)
+    return fail(MOE_ERR_UNSUPPORTED, "d_ff %d: need a multiple of 64 up to %d", d->d_ff, MOE_MAX_DFF);
+  if (d->n_experts > MOE_MAX_EXPERTS)
+    return fail(MOE_ERR_UNSUPPORTED, "n_experts %d exceeds %d", d->n_experts, MOE_MAX_EXPERTS);
+  if (d->top_k > MOE_MAX_TOPK)
+    return fail(MOE_ERR_UNSUPPORTED, "top_k %d exceeds %d", d->top_k, MOE_MAX_TOPK);
+  return MOE_OK;
+}
+
+moe_status check_T(int32_t T) {
+  if (T < 0) return fail(MOE_ERR_INVALID_ARG, "T %d is negative", T);
+  if (T > MOE_MAX_TOKENS) return fail(MOE_ERR_UNSUPPORTED, "T %d exceeds %d", T, MOE_MAX_TOKENS);
+  return MOE_OK;
+}
+
+moe_status need_ptr(const void *p, const char *name) {
+  if (!p) return fail(MOE_ERR_INVALID_ARG, "%s is NULL", name);
+  if (!aligned16(p)) return fail(MOE_ERR_MISALIGNED, "%s is not 16-byte aligned", name);
+  return MOE_OK;
+}
+
+#define TRY(expr)                      \
+  do {                                 \
+    moe_status _s = (expr);            \
+    if (_s != MOE_OK) return _s;       \
+  } while (0)
+
+size_t elem_bytes(const moe_desc *d) { return d->dtype == MOE_BF16 ? 2 : 4; }
+
+// FFN workspace layout (each segment 256-byte aligned).
+struct FfnLayout {
+  size_t h, idx, hact, partial, hm, total;
+};
+
+FfnLayout ffn_layout(const moe_desc *d, int32_t T, int32_t k, moe_path path) {
+  const size_t P = (size_t)T * d->top_k;
+  const int bf16 = d->dtype == MOE_BF16;
+  FfnLayout L{};
+  size_t off = 0;
+  L.h = off;
+  off += up(P * d->d_ff * 4);
+  L.idx = off;
+  off += up(P * (size_t)k * 4);
+  L.hact = off;
+  if (path == MOE_PATH_SPARSE) off += up(P * (size_t)k * 4);
+  L.partial = off;
+  size_t rows;
+  if (path == MOE_PATH_SPARSE)
+    rows = moe::max_partial_rows((int)P, k, d->hidden, bf16);
+  else
+    rows = bf16 ? P : moe::max_partial_rows((int)P, d->d_ff, d->hidden, 0);
+  off += up(rows * d->hidden * 4);
+  L.hm = off;
+  if (path == MOE_PATH_DENSE) off += up(P * d->d_ff * elem_bytes(d));
+  L.total = off;
+  return L;
+}
+
+moe_status run_ffn(moe_path path, const moe_desc *d, int32_t T, int32_t k_keep, const void *x,
+                   const void *w_gate, const void *w_up, const void *w_down,
+                   const moe_routing *routing, float *y, int32_t accumulate,
+                   int32_t *active_idx_out, void *workspace, size_t workspace_bytes,
+                   hipStream_t stream) {
+  g_err[0] = 0;
+  TRY(check_desc(d));
+  TRY(check_T(T));
+  if (k_keep < 0 || k_keep > d->d_ff)
+    return fail(MOE_ERR_INVALID_ARG, "k_keep %d outside [0, d_ff=%d]", k_keep, d->d_ff);
+  if (accumulate != 0 && accumulate != 1)
+    return fail(MOE_ERR_INVALID_ARG, "accumulate must be 0 or 1");
+  if (!routing && d->top_k != d->n_experts)
+    return fail(MOE_ERR_INVALID_ARG,
+                "routing == NULL (always-on group) needs top_k == n_experts (%d != %d)", d->top_k,
+                d->n_experts);
+  if (T == 0) return MOE_OK;
+  TRY(need_ptr(x, "x"));
+  TRY(need_ptr(w_gate, "w_gate"));
+  TRY(need_ptr(w_up, "w_up"));
+  TRY(need_ptr(w_down, "w_down"));
+  TRY(need_ptr(y, "y"));
+  if (routing) {
+    TRY(need_ptr(routing->topk_ids, "routing->topk_ids"));
+    TRY(need_ptr(routing->topk_w, "routing->topk_w"));
+    TRY(need_ptr(routing->expert_offsets, "routing->expert_offsets"));
+    TRY(need_ptr(routing->pair_by_expert, "routing->pair_by_expert"));
+    TRY(need_ptr(routing->active_experts, "routing->active_experts"));
+    TRY(need_ptr(routing->n_active, "routing->n_active"));
+  }
+  if (active_idx_out && !aligned16(active_idx_out))
+    return fail(MOE_ERR_MISALIGNED, "active_idx_out is not 16-byte aligned");
+  const FfnLayout L = ffn_layout(d, T, k_keep, path);
+  if (!workspace) return fail(MOE_ERR_WORKSPACE, "workspace is NULL");
+  if (!aligned16(workspace)) return fail(MOE_ERR_MISALIGNED, "workspace is not 16-byte aligned");
+  if (workspace_bytes < L.total)
+    return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, L.total);
+
+  char *ws = static_cast<char *>(workspace);
+  moe::FfnArgs a{};
+  a.T = T;
+  a.H = d->hidden;
+  a.E = d->n_experts;
+  a.d_ff = d->d_ff;
+  a.top_k = d->top_k;
+  a.k_keep = k_keep;
+  a.bf16 = d->dtype == MOE_BF16;
+  a.implicit = routing == nullptr;
+  a.accumulate = accumulate;
+  a.x = x;
+  a.w_gate = w_gate;
+  a.w_up = w_up;
+  a.w_down = w_down;
+  if (routing) {
+    a.topk_ids = routing->topk_ids;
+    a.topk_w = routing->topk_w;
+    a.offsets = routing->expert_offsets;
+    a.pair_by_expert = routing->pair_by_expert;
+    a.active = routing->active_experts;
+    a.n_active = routing->n_active;
+  }
+  a.y = y;
+  a.h = reinterpret_cast<float *>(ws + L.h);
+  a.idx = active_idx_out ? active_idx_out : reinterpret_cast<int32_t *>(ws + L.idx);
+  a.hact = path == MOE_PATH_SPARSE ? reinterpret_cast<float *>(ws + L.hact) : nullptr;
+  a.partial = reinterpret_cast<float *>(ws + L.partial);
+  a.hm = path == MOE_PATH_DENSE ? static_cast<void *>(ws + L.hm) : nullptr;
+  const hipError_t e =
+      path == MOE_PATH_SPARSE ? moe::launch_ffn_sparse(a, stream) : moe::launch_ffn_dense(a, stream);
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_route(const moe_desc *d, int32_t T, const void *x, const void *w_router,
+                     const float *bias, const moe_routing *out, void *workspace,
+                     size_t workspace_bytes, hipStream_t stream) {
+  g_err[0] = 0;
+  TRY(check_desc(d));
+  TRY(check_T(T));
+  if (!out) return fail(MOE_ERR_INVALID_ARG, "routing output struct is NULL");
+  if (T == 0) return MOE_OK;
+  TRY(need_ptr(x, "x"));
+  TRY(need_ptr(w_router, "w_router"));
+  if (bias && ((uintptr_t)bias & 3u)) return fail(MOE_ERR_MISALIGNED, "bias is not 4-byte aligned");
+  TRY(need_ptr(out->topk_ids, "out->topk_ids"));
+  TRY(need_ptr(out->topk_w, "out->topk_w"));
+  TRY(need_ptr(out->expert_offsets, "out->expert_offsets"));
+  TRY(need_ptr(out->pair_by_expert, "out->pair_by_expert"));
+  TRY(need_ptr(out->active_experts, "out->active_experts"));
+  TRY(need_ptr(out->n_active, "out->n_active"));
+  const size_t need = moe_route_workspace_size(d, T);
+  if (!workspace) return fail(MOE_ERR_WORKSPACE, "workspace is NULL");
+  if (!aligned16(workspace)) return fail(MOE_ERR_MISALIGNED, "workspace is not 16-byte aligned");
+  if (workspace_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+  moe::RouteArgs a{};
+  a.T = T;
+  a.H = d->hidden;
+  a.E = d->n_experts;
+  a.top_k = d->top_k;
+  a.norm_topk = d->norm_topk;
+  a.bf16 = d->dtype == MOE_BF16;
+  a.x = x;
+  a.w_router = w_router;
+  a.bias = bias;
+  a.logits = static_cast<float *>(workspace);
+  a.topk_ids = out->topk_ids;
+  a.topk_w = out->topk_w;
+  a.offsets = out->expert_offsets;
+  a.pair_by_expert = out->pair_by_expert;
+  a.active = out->active_experts;
+  a.n_active = out->n_active;
+  const hipError_t e = moe::launch_route(a, stream);
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return MOE_OK;
+}
+
+moe_status moe_expert_ffn_sparse(const moe_desc *d, int32_t T, int32_t k_keep, const void *x,
+                                 const void *w_gate, const void *w_up, const void *w_down,
+                                 const moe_routing *routing, float *y, int32_t accumulate,
+                                 int32_t *active_idx_out, void *workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
+  return run_ffn(MOE_PATH_SPARSE, d, T, k_keep, x, w_gate, w_up, w_down, routing, y, accumulate,
+                 active_idx_out, workspace, workspace_bytes, stream);
+}
+
+moe_status moe_expert_ffn_dense(const moe_desc *d, int32_t T, int32_t k_keep, const void *x,
+                                const void *w_gate, const void *w_up, const void *w_down,
+                                const moe_routing *routing, float *y, int32_t accumulate,
+                                int32_t *active_idx_out, void *workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+  return run_ffn(MOE_PATH_DENSE, d, T, k_keep, x, w_gate, w_up, w_down, routing, y, accumulate,
+                 active_idx_out, workspace, workspace_bytes, stream);
+}
+
+size_t moe_route_workspace_size(const moe_desc *d, int32_t T) {
+  if (check_desc(d) != MOE_OK || check_T(T) != MOE_OK) return 0;
+  return up((size_t)(T > 0 ? T : 1) * d->n_experts * 4);
+}
+
+size_t moe_ffn_workspace_size(const moe_desc *d, int32_t T, int32_t k_keep, moe_path path) {
+  if (check_desc(d) != MOE_OK || check_T(T) != MOE_OK) return 0;
+  if (k_keep < 0 || k_keep > d->d_ff) return 0;
+  if (path != MOE_PATH_SPARSE && path != MOE_PATH_DENSE) return 0;
+  return ffn_layout(d, T > 0 ? T : 1, k_keep, path).total;
+}
+
+int32_t moe_keep_count(double sparsity, int32_t d_ff) {
+  if (d_ff < 0 || !isfinite(sparsity)) return -1;
+  double k = ceil((1.0 - sparsity) * (double)d_ff - 1e-9);
+  if (k < 0) k = 0;
+  if (k > d_ff) k = d_ff;
+  return (int32_t)k;
+}
+
+moe_path moe_select_path(const moe_desc *d, int32_t T, int32_t k_keep) {
+  const char *force = getenv("MOE_FORCE_PATH");
+  if (force) {
+    if (!strcmp(force, "sparse")) return MOE_PATH_SPARSE;
+    if (!strcmp(force, "dense")) return MOE_PATH_DENSE;
+  }
+  if (check_desc(d) != MOE_OK || T <= 0 || k_keep < 0 || k_keep > d->d_ff) return MOE_PATH_SPARSE;
+  // Both paths stream the same gate/up bytes; they differ in the down
+  // projection: the sparse path reads k_keep rows per (token, expert) pair,
+  // the dense path every d_ff row once per active expert.  Expected active
+  // experts under uniform routing: E * (1 - (1 - top_k / E)^T).
+  const double E = d->n_experts, K = d->top_k;
+  const double active = E * (1.0 - pow(1.0 - K / E, (double)T));
+  const double sparse_rows = (double)T * K * k_keep;
+  const double dense_rows = active * d->d_ff;
+  return sparse_rows < dense_rows ? MOE_PATH_SPARSE : MOE_PATH_DENSE;
+}
+
+const char *moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_MISALIGNED: return "MOE_ERR_MISALIGNED";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+  }
+  return "MOE_ERR_UNKNOWN";
+}
+
+const char *moe_last_error(void) { return g_err; }
+
+const char *moe_version(void) { return "moe_mi355x 0.1 (gfx950)"; }
+
+}  // extern "C"

@@ -1,0 +1,132 @@
+// Device-side building blocks shared by the gfx950 kernels of the MoE layer:
+// vector types, bf16 handling, MFMA wrappers, the routing view and
+// wavefront/block scans.  gfx950 (CDNA4): wave64, 16x16 MFMA tiles.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kWave = 64;
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// One 16-byte global load (dwordx4).
+__device__ __forceinline__ u32x4 ld16(const void *p) {
+  return *reinterpret_cast<const u32x4 *>(p);
+}
+
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// D += A * B for a 16x16 output tile, K = 32 bf16.  Lane l supplies row
+// (l % 16) of A and column (l % 16) of B, each with the 8 consecutive k of
+// k-group (l / 16); it receives D rows 4 * (l / 16) + r, column l % 16.
+__device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+// Same tile shape with fp32 operands and K = 4: lane l supplies A[l % 16][l / 16]
+// and B[l / 16][l % 16].
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// Routing of one FFN call as the kernels see it.  `implicit` is the
+// always-on (shared) group: every token pairs with every expert, weight 1,
+// pair p = t * E + e, and expert e's tokens sit at positions [e*T, (e+1)*T).
+struct RouteView {
+  const int32_t *topk_ids;
+  const float *topk_w;
+  const int32_t *offsets;
+  const int32_t *pair_by_expert;
+  const int32_t *active;
+  const int32_t *n_active;
+  int32_t implicit;
+  int32_t T;
+  int32_t top_k;
+  int32_t E;
+
+  __device__ __forceinline__ int nact() const { return implicit ? E : *n_active; }
+  __device__ __forceinline__ int expert(int s) const { return implicit ? s : active[s]; }
+  __device__ __forceinline__ int begin(int e) const { return implicit ? e * T : offsets[e]; }
+  __device__ __forceinline__ int end(int e) const { return implicit ? (e + 1) * T : offsets[e + 1]; }
+  __device__ __forceinline__ int pair_at(int q) const {
+    return implicit ? (q % T) * top_k + q / T : pair_by_expert[q];
+  }
+  __device__ __forceinline__ int expert_of_pair(int p) const {
+    return implicit ? p % top_k : topk_ids[p];
+  }
+  __device__ __forceinline__ float weight(int p) const { return implicit ? 1.0f : topk_w[p]; }
+};
+
+// ---- wavefront reductions and scans (fixed butterfly order: deterministic)
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    uint64_t w = __shfl_xor(v, o, kWave);
+    v = w > v ? w : v;
+  }
+  return v;
+}
+
+// Inclusive prefix sum over the lanes of a wave.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    int w = __shfl_up(v, o, kWave);
+    if (lane >= o) v += w;
+  }
+  return v;
+}
+
+// Inclusive prefix sum over a whole block of NT threads (NT/64 <= 64 waves).
+// `tmp` is __shared__ scratch of at least NT/64 ints.  Ends with a barrier.
+template <int NT>
+__device__ __forceinline__ int block_incl_scan(int v, int *tmp, int *total = nullptr) {
+  constexpr int NW = NT / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wid = threadIdx.x / kWave;
+  int s = wave_incl_scan(v);
+  if (lane == kWave - 1) tmp[wid] = s;
+  __syncthreads();
+  if (wid == 0) {
+    int t = lane < NW ? tmp[lane] : 0;
+    t = wave_incl_scan(t);
+    if (lane < NW) tmp[lane] = t;
+  }
+  __syncthreads();
+  if (wid > 0) s += tmp[wid - 1];
+  if (total) *total = tmp[NW - 1];
+  __syncthreads();
+  return s;
+}
+
+// Order-preserving map of a float to uint32 (larger float -> larger key);
+// -0 is folded onto +0 first.
+__device__ __forceinline__ uint32_t ordered_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) == 0u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+}  // namespace moe

@@ -1,0 +1,52 @@
+// Host-side launch interface between the C ABI (api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+struct RouteArgs {
+  int T, H, E, top_k, norm_topk, bf16;
+  const void *x, *w_router;
+  const float *bias;
+  float *logits;  // workspace [T, E]
+  int32_t *topk_ids;
+  float *topk_w;
+  int32_t *offsets, *pair_by_expert, *active, *n_active;
+};
+
+hipError_t launch_route(const RouteArgs &a, hipStream_t stream);
+
+// One FFN call (routed group, or an implicit shared group).
+struct FfnArgs {
+  int T, H, E, d_ff, top_k, k_keep, bf16, implicit, accumulate;
+  const void *x, *w_gate, *w_up, *w_down;
+  // routing (ignored when implicit)
+  const int32_t *topk_ids;
+  const float *topk_w;
+  const int32_t *offsets, *pair_by_expert, *active, *n_active;
+  float *y;
+  // workspace carve-up
+  float *h;          // [P, d_ff] fp32
+  int32_t *idx;      // [P, k_keep]
+  float *hact;       // [P, k_keep]   w * h at the kept neurons
+  float *partial;    // [P * n_chunks, H]
+  void *hm;          // dense path: [P, d_ff] masked, weighted h (bf16 or fp32)
+  int n_chunks;      // down-projection row chunks per pair
+};
+
+// Down-projection work split: rows of each pair are cut into n_chunks chunks.
+struct DownPlan {
+  int n_chunks;
+  int rows_per_chunk;
+};
+DownPlan plan_down(int P, int k_keep, int H, int bf16);
+// Upper bound of P * n_chunks over every P' <= P (sizes the partial buffer).
+size_t max_partial_rows(int P, int k_keep, int H, int bf16);
+
+hipError_t launch_ffn_sparse(const FfnArgs &a, hipStream_t stream);
+hipError_t launch_ffn_dense(const FfnArgs &a, hipStream_t stream);
+
+}  // namespace moe

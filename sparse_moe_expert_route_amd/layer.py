@@ -1,0 +1,69 @@
+"""MoELayer: the decode MoE layer as a sequence of C-ABI calls.
+
+route -> routed experts (sparse or dense path, overwriting y) -> always-on
+shared experts (accumulating into y).  Torch provides device memory and the
+stream; every step runs in libmoe_mi355x's kernels.
+"""
+from __future__ import annotations
+
+from typing import Optional, Sequence
+
+import torch
+
+from . import binding as B
+
+
+class MoELayer:
+    def __init__(self, *, hidden: int, n_experts: int, d_ff: int, top_k: int, norm_topk: bool,
+                 dtype: str, w_router, w_gate, w_up, w_down, bias=None,
+                 shared: Optional[Sequence] = None, d_ff_shared: Optional[int] = None):
+        self.desc = B.make_desc(hidden, n_experts, d_ff, top_k, norm_topk, dtype)
+        self.w_router, self.bias = w_router, bias
+        self.w = (w_gate, w_up, w_down)
+        self.shared = tuple(shared) if shared is not None else None
+        self.desc_shared = None
+        if self.shared is not None:
+            n_sh = self.shared[0].shape[0]
+            self.desc_shared = B.make_desc(hidden, n_sh, d_ff_shared or self.shared[0].shape[1],
+                                           n_sh, False, dtype)
+        self._ws = {}
+
+    def _workspace(self, key, nbytes: int, device):
+        buf = self._ws.get(key)
+        if buf is None or buf.numel() < nbytes:
+            buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+            self._ws[key] = buf
+        return buf
+
+    def select_path(self, T: int, k_keep: int, shared: bool = False) -> int:
+        return B.moe_select_path(self.desc_shared if shared else self.desc, T, k_keep)
+
+    def route(self, x, routing: Optional[B.Routing] = None) -> B.Routing:
+        T = x.shape[0]
+        d = self.desc
+        routing = routing or B.Routing.allocate(T, d.top_k, d.n_experts, x.device)
+        ws = self._workspace("route", B.moe_route_workspace_size(d, T), x.device)
+        B.moe_route(d, T, x, self.w_router, self.bias, routing, ws)
+        return routing
+
+    def forward(self, x, k_keep: int, k_keep_shared: Optional[int] = None,
+                path: Optional[int] = None, path_shared: Optional[int] = None,
+                y=None, active_idx=None, routing: Optional[B.Routing] = None):
+        """y [T, H] fp32 for tokens x [T, H]; k_keep kept neurons per pair."""
+        T = x.shape[0]
+        d = self.desc
+        if y is None:
+            y = torch.empty((T, d.hidden), dtype=torch.float32, device=x.device)
+        routing = self.route(x, routing)
+        path = self.select_path(T, k_keep) if path is None else path
+        fn = B.moe_expert_ffn_sparse if path == B.MOE_PATH_SPARSE else B.moe_expert_ffn_dense
+        ws = self._workspace(("ffn", path), B.moe_ffn_workspace_size(d, T, k_keep, path), x.device)
+        fn(d, T, k_keep, x, *self.w, routing, y, 0, active_idx, ws)
+        if self.shared is not None:
+            ds = self.desc_shared
+            ks = ds.d_ff if k_keep_shared is None else k_keep_shared
+            ps = self.select_path(T, ks, shared=True) if path_shared is None else path_shared
+            fs = B.moe_expert_ffn_sparse if ps == B.MOE_PATH_SPARSE else B.moe_expert_ffn_dense
+            wss = self._workspace(("shared", ps), B.moe_ffn_workspace_size(ds, T, ks, ps), x.device)
+            fs(ds, T, ks, x, *self.shared, None, y, 1, None, wss)
+        return y

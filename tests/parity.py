@@ -1,0 +1,206 @@
+"""Parity helpers: run the HIP layer through its C ABI, run the oracle on the
+same seeded inputs, and compare them with the selection-window rule.
+
+Rule (floating point decides which experts / neurons are kept, so an index
+whose score lies within 1e-4 relative of the selection boundary may go
+either way):
+  1. for a score row v with kept count k < n, beta = (v_(k) + v_(k+1)) / 2;
+     index i is ambiguous if |v_i - beta| <= 1e-4 * max(|beta|, 1e-30);
+  2. the tested selection must equal the oracle's on every non-ambiguous
+     index;
+  3. the oracle then re-runs with the tested selection forced, and the
+     outputs are compared by relative L2 over [T, H]: <= 1e-5 for the fp32
+     layer, <= 1e-2 for the bf16 layer.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import moe_synth as S
+import oracle
+from sparse_moe_expert_route_amd import binding as B
+
+WINDOW = 1e-4
+TOL = {"f32": 1e-5, "bf16": 1e-2}
+
+
+# ------------------------------------------------------------------ inputs
+
+class LayerInputs:
+    """Seeded host inputs of one layer (weights as stacked arrays)."""
+
+    def __init__(self, shape: S.LayerShape, seed: int = 0):
+        self.shape = shape
+        self.seed = seed
+        self.w_router = S.router_matrix(shape, seed)
+        self.bias = S.router_bias(shape)
+        self.wg, self.wu, self.wd = S.expert_weights(shape, seed)
+        self.shared = (S.expert_weights(shape, seed, group=S.SHARED)
+                       if shape.n_shared else None)
+
+    def tokens(self, T: int, seed: int = 1):
+        return S.tokens(self.shape, seed, T)
+
+
+def to_dev(a: np.ndarray):
+    """numpy float32, or bf16 bits as uint16, to a contiguous device tensor."""
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+class DeviceLayer:
+    """Device copies of a LayerInputs' weights."""
+
+    def __init__(self, inp: LayerInputs):
+        self.inp = inp
+        sh = inp.shape
+        self.desc = B.make_desc(sh.hidden, sh.n_experts, sh.d_ff, sh.top_k, sh.norm_topk, sh.dtype)
+        self.w_router = to_dev(inp.w_router)
+        self.bias = to_dev(inp.bias) if inp.bias is not None else None
+        self.w = tuple(to_dev(a) for a in (inp.wg, inp.wu, inp.wd))
+        self.desc_sh = None
+        if inp.shared is not None:
+            self.desc_sh = B.make_desc(sh.hidden, sh.n_shared, sh.d_ff_shared, sh.n_shared, False,
+                                       sh.dtype)
+            self.w_sh = tuple(to_dev(a) for a in inp.shared)
+
+    def run(self, x_host: np.ndarray, k: int, path: int, k_sh=None, path_sh=None,
+            poison_rows=None):
+        """One layer call; returns host copies of routing, masks and y."""
+        sh = self.inp.shape
+        T = x_host.shape[0]
+        x = to_dev(x_host)
+        R = B.Routing.allocate(T, sh.top_k, sh.n_experts)
+        ws_r = torch.empty(B.moe_route_workspace_size(self.desc, T), dtype=torch.uint8, device="cuda")
+        B.moe_route(self.desc, T, x, self.w_router, self.bias, R, ws_r)
+        y = torch.full((T, sh.hidden), float("nan"), dtype=torch.float32, device="cuda")
+        idx = torch.full((max(1, T * sh.top_k), max(1, k)), -1, dtype=torch.int32, device="cuda")
+        ws = torch.empty(B.moe_ffn_workspace_size(self.desc, T, k, path), dtype=torch.uint8, device="cuda")
+        fn = B.moe_expert_ffn_sparse if path == B.MOE_PATH_SPARSE else B.moe_expert_ffn_dense
+        wd = self.w[2] if poison_rows is None else poison_rows
+        fn(self.desc, T, k, x, self.w[0], self.w[1], wd, R, y, 0, idx if k > 0 else None, ws)
+        out = dict(T=T, k=k)
+        idx_sh = None
+        if self.desc_sh is not None:
+            ds = self.desc_sh
+            k_sh = ds.d_ff if k_sh is None else k_sh
+            path_sh = path if path_sh is None else path_sh
+            idx_sh = torch.full((max(1, T * ds.top_k), max(1, k_sh)), -1, dtype=torch.int32, device="cuda")
+            ws2 = torch.empty(B.moe_ffn_workspace_size(ds, T, k_sh, path_sh), dtype=torch.uint8, device="cuda")
+            fs = B.moe_expert_ffn_sparse if path_sh == B.MOE_PATH_SPARSE else B.moe_expert_ffn_dense
+            fs(ds, T, k_sh, x, *self.w_sh, None, y, 1, idx_sh if k_sh > 0 else None, ws2)
+            out["k_sh"] = k_sh
+        torch.cuda.synchronize()
+        out.update(ids=R.topk_ids.cpu().numpy()[:T], w=R.topk_w.cpu().numpy()[:T],
+                   offsets=R.expert_offsets.cpu().numpy(), pairs=R.pair_by_expert.cpu().numpy(),
+                   active=R.active_experts.cpu().numpy(), n_active=int(R.n_active.cpu()[0]),
+                   idx=idx.cpu().numpy(), y=y.cpu().numpy())
+        if idx_sh is not None:
+            out["idx_sh"] = idx_sh.cpu().numpy()
+        return out
+
+
+# ------------------------------------------------------------------ comparison
+
+def ambiguous(scores: np.ndarray, k: int) -> np.ndarray:
+    """Boolean mask of indices within the window of the k-selection boundary."""
+    n = scores.shape[0]
+    if k <= 0 or k >= n:
+        return np.zeros(n, dtype=bool)
+    order = np.lexsort((np.arange(n), -scores))
+    beta = 0.5 * (scores[order[k - 1]] + scores[order[k]])
+    return np.abs(scores - beta) <= WINDOW * max(abs(beta), 1e-30)
+
+
+def check_selection(got, want, scores, k, what):
+    """Sets must agree except on ambiguous indices; returns True if they differ."""
+    got, want = set(int(i) for i in got), set(int(i) for i in want)
+    assert len(got) == len(want) == min(k, len(scores)), (what, len(got), len(want), k)
+    diff = got ^ want
+    if not diff:
+        return False
+    amb = ambiguous(scores, k)
+    bad = [i for i in diff if not amb[i]]
+    assert not bad, f"{what}: selection differs on non-ambiguous indices {bad}"
+    return True
+
+
+def rel_l2(a, b) -> float:
+    a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+def compare_layer(inp: LayerInputs, x_host, got, k, k_sh=None, tokens=None):
+    """Check a GPU layer result against the oracle; returns the rel L2 error.
+
+    ``tokens`` restricts the check to a sample of token rows (the layer is
+    token-separable, so the oracle runs on just those tokens)."""
+    sh = inp.shape
+    T = x_host.shape[0]
+    tokens = np.arange(T) if tokens is None else np.asarray(tokens)
+    xs = x_host[tokens]
+    shared = inp.shared
+    ks = None
+    if shared is not None:
+        ks = k_sh if k_sh is not None else sh.d_ff_shared
+    kw = dict(top_k=sh.top_k, norm_topk=sh.norm_topk, k_keep=k, dtype=sh.dtype,
+              shared=shared, k_keep_shared=ks)
+    ids0, _, logits0, _ = oracle.route(oracle.to_f64(xs, sh.dtype),
+                                       oracle.to_f64(inp.w_router, sh.dtype),
+                                       inp.bias, sh.top_k, sh.norm_topk)
+    ids_g = got["ids"][tokens]
+    # 1. routing: as sets, window rule on the logits; slot order descending
+    for i, t in enumerate(tokens):
+        check_selection(ids_g[i], ids0[i], logits0[i], sh.top_k, f"route t={t}")
+        lg = logits0[i][ids_g[i]]
+        assert np.all(np.diff(lg) <= WINDOW * np.abs(lg[:-1]) + 1e-30), f"slot order t={t}"
+    # 2. masks against the oracle forced to the GPU's experts
+    r1 = oracle.moe_layer(xs, inp.w_router, inp.bias, inp.wg, inp.wu, inp.wd,
+                          forced_ids=ids_g, **kw)
+    np.testing.assert_allclose(got["w"][tokens], r1.weights, rtol=1e-4, atol=1e-7)
+    forced_keep, forced_keep_sh = {}, {}
+    differs = False
+    if k > 0:
+        for i, t in enumerate(tokens):
+            for s in range(sh.top_k):
+                g = got["idx"][t * sh.top_k + s, :k]
+                assert np.all(np.diff(g) > 0), f"kept ids not ascending t={t} s={s}"
+                differs |= check_selection(g, r1.keep[(i, s)], np.abs(r1.h[(i, s)]), k,
+                                           f"mask t={t} s={s}")
+                forced_keep[(i, s)] = g
+    if shared is not None and ks and ks > 0:
+        for i, t in enumerate(tokens):
+            for j in range(sh.n_shared):
+                g = got["idx_sh"][t * sh.n_shared + j, :ks]
+                assert np.all(np.diff(g) > 0)
+                differs |= check_selection(g, r1.keep_shared[(i, j)],
+                                           np.abs(r1.h_shared[(i, j)]), ks,
+                                           f"shared mask t={t} j={j}")
+                forced_keep_sh[(i, j)] = g
+    r2 = r1
+    if differs:
+        r2 = oracle.moe_layer(xs, inp.w_router, inp.bias, inp.wg, inp.wu, inp.wd,
+                              forced_ids=ids_g, forced_keep=forced_keep or None,
+                              forced_keep_shared=forced_keep_sh or None, keep_h=False, **kw)
+    y_g = got["y"][tokens]
+    assert np.all(np.isfinite(y_g)), "non-finite output"
+    err = rel_l2(y_g, r2.y)
+    assert err <= TOL[sh.dtype], f"rel L2 {err:.3e} > {TOL[sh.dtype]}"
+    return err
+
+
+def check_grouping(got, E, top_k):
+    """moe_route's grouping outputs are a stable counting sort of topk_ids."""
+    ids = got["ids"].reshape(-1)
+    P = ids.shape[0]
+    counts = np.bincount(ids, minlength=E)
+    np.testing.assert_array_equal(got["offsets"], np.concatenate([[0], np.cumsum(counts)]))
+    want = np.lexsort((np.arange(P), ids))          # by expert, then pair id
+    np.testing.assert_array_equal(got["pairs"][:P], want)
+    act = np.nonzero(counts)[0]
+    assert got["n_active"] == len(act)
+    np.testing.assert_array_equal(got["active"][:len(act)], act)
+    for t in range(ids.shape[0] // top_k):       # distinct experts per token
+        assert len(set(ids[t * top_k:(t + 1) * top_k])) == top_k

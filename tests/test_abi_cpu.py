@@ -1,0 +1,160 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+the header declares, and rejects every invalid argument before it enqueues
+anything (so no HIP call is made).  Pointers here are fake, aligned
+integers: the calls must return on validation alone."""
+import ctypes
+import math
+import os
+import subprocess
+from fractions import Fraction
+
+import pytest
+
+from oracle import moe_oracle as O
+from sparse_moe_expert_route_amd import binding as B
+from sparse_moe_expert_route_amd.build import LIB_PATH
+
+L = B.lib()
+FAKE = 0x7F0000000000          # 16-byte aligned, never dereferenced
+MIS = FAKE + 4                 # misaligned
+
+
+def test_exports_every_header_function():
+    declared = B.header_functions()
+    assert declared == sorted(B._SIGS)           # the binding covers the header
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for name in declared:
+        assert name in exported, name
+
+
+def test_version_and_status_strings():
+    assert "gfx950" in B.moe_version()
+    for code, name in B.STATUS.items():
+        assert B.moe_status_string(code) == name
+    assert B.moe_status_string(99) == "MOE_ERR_UNKNOWN"
+
+
+def _golden_keep():
+    rows = []
+    with open(os.path.join(os.path.dirname(__file__), "golden", "keep_counts.txt")) as f:
+        for line in f:
+            if line.strip() and not line.startswith("#"):
+                s, d, k = line.split()[:3]
+                rows.append((float(s), int(d), int(k)))
+    return rows
+
+
+@pytest.mark.parametrize("s,d,k", _golden_keep())
+def test_keep_count_golden(s, d, k):
+    assert B.moe_keep_count(s, d) == k
+
+
+def test_keep_count_matches_exact_rationals():
+    for d in (512, 768, 1000, 1024, 1536, 8192):
+        for m in range(1001):
+            s = Fraction(m, 1000)
+            assert B.moe_keep_count(float(s), d) == math.ceil((1 - s) * d) == O.keep_count(float(s), d)
+    assert B.moe_keep_count(1.5, 64) == 0 and B.moe_keep_count(-0.5, 64) == 64
+    assert B.moe_keep_count(float("nan"), 64) == -1 and B.moe_keep_count(0.5, -1) == -1
+
+
+def _desc(**kw):
+    base = dict(hidden=2048, n_experts=64, d_ff=1024, top_k=8, norm_topk=False, dtype="bf16")
+    base.update(kw)
+    return B.make_desc(**base)
+
+
+def test_select_path_is_shape_only_and_monotone(monkeypatch):
+    monkeypatch.delenv("MOE_FORCE_PATH", raising=False)
+    d = _desc(hidden=5120, n_experts=16, d_ff=8192, top_k=1)
+    k = B.moe_keep_count(0.9, 8192)
+    paths = [B.moe_select_path(d, T, k) for T in (1, 8, 64, 256, 1024)]
+    assert paths[0] == B.MOE_PATH_SPARSE and paths[-1] == B.MOE_PATH_DENSE
+    assert paths == sorted(paths)                         # switches once, sparse -> dense
+    assert B.moe_select_path(d, 1, 8192) == B.MOE_PATH_DENSE   # no masking: dense rows
+    monkeypatch.setenv("MOE_FORCE_PATH", "dense")
+    assert B.moe_select_path(d, 1, k) == B.MOE_PATH_DENSE
+    monkeypatch.setenv("MOE_FORCE_PATH", "sparse")
+    assert B.moe_select_path(d, 1024, k) == B.MOE_PATH_SPARSE
+
+
+def test_workspace_sizes():
+    d = _desc()
+    for path in (B.MOE_PATH_SPARSE, B.MOE_PATH_DENSE):
+        sizes = [B.moe_ffn_workspace_size(d, T, 103, path) for T in (1, 2, 4, 16, 64, 1024)]
+        assert all(s > 0 and s % 256 == 0 for s in sizes)
+        assert sizes == sorted(sizes)
+        # a workspace for T serves every smaller T
+        assert all(B.moe_ffn_workspace_size(d, t, 103, path) <= sizes[-1] for t in range(1, 1025, 37))
+    assert B.moe_ffn_workspace_size(d, 4, 2000, 0) == 0
+    assert B.moe_ffn_workspace_size(_desc(hidden=100), 4, 10, 0) == 0
+    assert B.moe_route_workspace_size(d, 16) >= 16 * 64 * 4
+
+
+def _route(d, T, x=FAKE, w=FAKE, bias=None, out="ok", ws=FAKE, wsb=1 << 30):
+    r = B.MoeRouting(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE) if out == "ok" else out
+    return L.moe_route(ctypes.byref(d) if d is not None else None, T, x, w, bias,
+                       ctypes.byref(r) if r is not None else None, ws, wsb, None)
+
+
+def _ffn(fn, d, T, k, x=FAKE, wg=FAKE, wu=FAKE, wd=FAKE, routing="ok", y=FAKE, acc=0, idx=None,
+         ws=FAKE, wsb=1 << 34):
+    r = B.MoeRouting(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE) if routing == "ok" else routing
+    return fn(ctypes.byref(d) if d is not None else None, T, k, x, wg, wu, wd,
+              ctypes.byref(r) if r is not None else None, y, acc, idx, ws, wsb, None)
+
+
+INV, MISA, WSP, UNS = 1, 2, 3, 4
+
+
+@pytest.mark.parametrize("fn_name", ["moe_expert_ffn_sparse", "moe_expert_ffn_dense"])
+def test_ffn_validation(fn_name):
+    fn = getattr(L, fn_name)
+    d = _desc()
+    assert _ffn(fn, None, 4, 10) == INV
+    assert _ffn(fn, _desc(top_k=65), 4, 10) == INV
+    assert _ffn(fn, _desc(hidden=100), 4, 10) == UNS
+    assert _ffn(fn, _desc(d_ff=96), 4, 10) == UNS
+    assert _ffn(fn, _desc(d_ff=16384), 4, 10) == UNS
+    assert _ffn(fn, _desc(n_experts=2048), 4, 10) == UNS
+    assert _ffn(fn, _desc(dtype=0).__class__(2048, 64, 1024, 8, 0, 7), 4, 10) == UNS
+    assert _ffn(fn, _desc(norm_topk=False).__class__(2048, 64, 1024, 8, 2, 1), 4, 10) == INV
+    assert _ffn(fn, d, -1, 10) == INV
+    assert _ffn(fn, d, 1 << 20, 10) == UNS
+    assert _ffn(fn, d, 4, -1) == INV
+    assert _ffn(fn, d, 4, 1025) == INV
+    assert _ffn(fn, d, 4, 10, acc=2) == INV
+    assert _ffn(fn, d, 4, 10, routing=None) == INV          # always-on group needs top_k == E
+    assert _ffn(fn, d, 4, 10, x=None) == INV
+    assert _ffn(fn, d, 4, 10, wd=None) == INV
+    assert _ffn(fn, d, 4, 10, y=None) == INV
+    assert _ffn(fn, d, 4, 10, x=MIS) == MISA
+    assert _ffn(fn, d, 4, 10, wg=MIS) == MISA
+    assert _ffn(fn, d, 4, 10, idx=MIS) == MISA
+    assert _ffn(fn, d, 4, 10, routing=B.MoeRouting(FAKE, FAKE, None, FAKE, FAKE, FAKE)) == INV
+    assert _ffn(fn, d, 4, 10, routing=B.MoeRouting(FAKE, FAKE, FAKE, MIS, FAKE, FAKE)) == MISA
+    assert _ffn(fn, d, 4, 10, ws=None) == WSP
+    assert _ffn(fn, d, 4, 10, ws=MIS) == MISA
+    path = 0 if "sparse" in fn_name else 1
+    need = B.moe_ffn_workspace_size(d, 4, 10, path)
+    assert _ffn(fn, d, 4, 10, wsb=need - 1) == WSP
+    assert "workspace" in B.moe_last_error()
+    # T == 0 is a valid no-op, even with NULL tensors
+    assert _ffn(fn, d, 0, 10, x=None, y=None, ws=None) == 0
+    assert B.moe_last_error() == ""
+
+
+def test_route_validation():
+    d = _desc()
+    assert _route(None, 4) == INV
+    assert _route(d, 4, out=None) == INV
+    assert _route(d, -3) == INV
+    assert _route(d, 4, x=None) == INV
+    assert _route(d, 4, w=MIS) == MISA
+    assert _route(d, 4, bias=FAKE + 2) == MISA
+    assert _route(d, 4, out=B.MoeRouting(FAKE, None, FAKE, FAKE, FAKE, FAKE)) == INV
+    assert _route(d, 4, ws=None) == WSP
+    assert _route(d, 4, wsb=B.moe_route_workspace_size(d, 4) - 1) == WSP
+    assert _route(d, 0, x=None) == 0

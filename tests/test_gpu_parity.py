@@ -1,0 +1,233 @@
+"""GPU parity of the HIP layer against the CPU oracle, through the C ABI.
+
+Every layer workload is run at its own shapes (full size; large batches
+are checked on a sample of token rows, the layer being token-separable),
+on both paths, plus ragged shapes that leave partial tiles everywhere and
+the edge cases of the method (k = 0, k = d_ff, T = 0, one token, all
+experts selected, skewed routing).  Selection and output comparison follow
+tests/parity.py.
+"""
+import functools
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import moe_synth as S
+from oracle import moe_oracle as O
+from sparse_moe_expert_route_amd import binding as B
+
+from parity import DeviceLayer, LayerInputs, check_grouping, compare_layer, rel_l2, to_dev
+
+pytestmark = pytest.mark.gpu
+SP, DN = B.MOE_PATH_SPARSE, B.MOE_PATH_DENSE
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@functools.lru_cache(maxsize=2)
+def layer(name: str, **over):
+    shape = S.LAYERS[name].with_(**over) if over else S.LAYERS[name]
+    inp = LayerInputs(shape, seed=0)
+    return inp, DeviceLayer(inp)
+
+
+def _sample(T, n=6):
+    if T <= n:
+        return None
+    return np.unique(np.linspace(0, T - 1, n).round().astype(int))
+
+
+def run_case(name, T, s, path, s_sh=None, path_sh=None, sample=8, seed=1, **over):
+    inp, dev = layer(name, **over)
+    sh = inp.shape
+    k = O.keep_count(s, sh.d_ff)
+    k_sh = O.keep_count(s_sh, sh.d_ff_shared) if (sh.n_shared and s_sh is not None) else None
+    x = inp.tokens(T, seed)
+    say(f"[case] {sh.name} T={T} s={s} k={k} path={path} s_sh={s_sh} over={over}")
+    got = dev.run(x, k, path, k_sh, path_sh)
+    check_grouping(got, sh.n_experts, sh.top_k)
+    err = compare_layer(inp, x, got, k, k_sh, tokens=_sample(T, sample))
+    say(f"   rel_l2={err:.3e}")
+    return got
+
+
+# ------------------------------------------------------------------ the workloads
+
+@pytest.mark.parametrize("path", [SP, DN])
+@pytest.mark.parametrize("s", [0.9, 0.0, 0.5])
+def test_tiny_f32_layer(s, path):
+    run_case("tiny-f32", 4, s, path)
+
+
+@pytest.mark.parametrize("T", [1, 4, 16])
+@pytest.mark.parametrize("s", [0.9, 0.75, 0.5, 0.0])
+def test_olmoe_like_sparse(T, s):
+    run_case("olmoe-like", T, s, SP)
+
+
+@pytest.mark.parametrize("T", [1, 16])
+def test_olmoe_like_dense(T):
+    run_case("olmoe-like", T, 0.9, DN)
+
+
+@pytest.mark.parametrize("T,path", [(1, SP), (4, SP), (16, SP), (32, SP), (64, SP), (64, DN)])
+def test_qwen3_like_zipf(T, path):
+    got = run_case("qwen3-moe-like", T, 0.9, path)
+    if T == 64:   # the Zipf bias concentrates load on the lowest expert ids
+        counts = np.diff(got["offsets"])
+        assert counts[0] == counts.max() and counts[0] > 2 * T * 8 / 128
+
+
+@pytest.mark.parametrize("T,s_sh", [(1, 0.0), (1, 0.5), (8, 0.0), (32, 0.5)])
+def test_deepseek_v2_like(T, s_sh):
+    run_case("deepseek-v2-like", T, 0.9, SP, s_sh=s_sh, path_sh=SP)
+
+
+def test_deepseek_v2_like_dense():
+    run_case("deepseek-v2-like", 32, 0.9, DN, s_sh=0.5, path_sh=DN)
+
+
+@pytest.mark.parametrize("T", [1, 8, 64, 256, 1024])
+@pytest.mark.parametrize("path", [SP, DN])
+def test_llama4_like(T, path):
+    run_case("llama4-like", T, 0.9, path, s_sh=0.9, path_sh=path, sample=4)
+
+
+# ------------------------------------------------------------------ ragged shapes and edges
+
+RAGGED = dict(hidden=320, n_experts=12, d_ff=192, top_k=3, norm_topk=True, n_shared=1,
+              d_ff_shared=128, zipf_bias=None)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("T", [1, 17, 37, 130])
+@pytest.mark.parametrize("path", [SP, DN])
+def test_ragged_shapes(dtype, T, path):
+    run_case("olmoe-like", T, 0.7, path, s_sh=0.5, path_sh=1 - path, dtype=dtype, **RAGGED)
+
+
+@pytest.mark.parametrize("k", [0, 1, 191, 192])
+def test_keep_extremes(k):
+    inp, dev = layer("olmoe-like", dtype="f32", **RAGGED)
+    x = inp.tokens(9, 3)
+    for path in (SP, DN):
+        say(f"[case] ragged f32 k={k} path={path}")
+        got = dev.run(x, k, path, k_sh=64, path_sh=SP)
+        compare_layer(inp, x, got, k, k_sh=64)
+
+
+def test_all_experts_selected_and_single_expert():
+    run_case("olmoe-like", 5, 0.5, SP, s_sh=0.0, dtype="f32", **dict(RAGGED, top_k=12))
+    run_case("olmoe-like", 5, 0.5, DN, s_sh=0.0, dtype="f32", **dict(RAGGED, n_experts=1, top_k=1))
+
+
+def test_many_tokens_max_T():
+    # the largest token count the ABI takes, on the small fp32 layer, sampled rows
+    run_case("tiny-f32", 65536, 0.9, SP, sample=5)
+
+
+# ------------------------------------------------------------------ properties
+
+def test_deterministic_and_sparse_equals_dense():
+    inp, dev = layer("olmoe-like")
+    x = inp.tokens(16, 5)
+    k = O.keep_count(0.9, 1024)
+    say("[case] determinism olmoe-like T=16")
+    a = dev.run(x, k, SP)
+    b = dev.run(x, k, SP)
+    np.testing.assert_array_equal(a["y"], b["y"])
+    np.testing.assert_array_equal(a["idx"], b["idx"])
+    c = dev.run(x, k, DN)
+    np.testing.assert_array_equal(a["idx"], c["idx"])
+    assert rel_l2(c["y"], a["y"]) < 1e-2
+
+
+def test_unkept_rows_are_never_read():
+    # Poison every W_d row no pair keeps with NaN: the sparse path must give
+    # the same bits (a load-and-multiply by zero would give NaN).
+    inp, dev = layer("olmoe-like")
+    x = inp.tokens(4, 7)
+    k = O.keep_count(0.9, 1024)
+    say("[case] NaN-poisoned W_d rows")
+    a = dev.run(x, k, SP)
+    wd = dev.w[2].clone()
+    keep = np.zeros((64, 1024), dtype=bool)
+    ids = a["ids"].reshape(-1)
+    for p, e in enumerate(ids):
+        keep[e, a["idx"][p, :k]] = True
+    poison = torch.from_numpy(~keep).cuda()
+    wd[poison] = float("nan")
+    b = dev.run(x, k, SP, poison_rows=wd)
+    assert np.all(np.isfinite(b["y"]))
+    np.testing.assert_array_equal(a["y"], b["y"])
+
+
+def test_outputs_outside_bounds_untouched_and_accumulate():
+    inp, dev = layer("olmoe-like")
+    sh = inp.shape
+    T = 3
+    k = O.keep_count(0.9, 1024)
+    x = to_dev(inp.tokens(T, 9))
+    R = B.Routing.allocate(T, sh.top_k, sh.n_experts)
+    B.moe_route(dev.desc, T, x, dev.w_router, None, R,
+                torch.empty(B.moe_route_workspace_size(dev.desc, T), dtype=torch.uint8, device="cuda"))
+    for path in (SP, DN):
+        buf = torch.full((T + 2, sh.hidden), 12345.0, device="cuda")
+        y = buf[1:T + 1]
+        ws = torch.empty(B.moe_ffn_workspace_size(dev.desc, T, k, path), dtype=torch.uint8, device="cuda")
+        fn = B.moe_expert_ffn_sparse if path == SP else B.moe_expert_ffn_dense
+        fn(dev.desc, T, k, x, *dev.w, R, y, 0, None, ws)
+        y1 = y.clone()
+        y.zero_()
+        fn(dev.desc, T, k, x, *dev.w, R, y, 1, None, ws)      # 0 + contribution: same bits
+        torch.cuda.synchronize()
+        assert torch.all(buf[0] == 12345.0) and torch.all(buf[T + 1] == 12345.0)
+        torch.testing.assert_close(y, y1, rtol=0, atol=0)
+        fn(dev.desc, T, k, x, *dev.w, R, y, 1, None, ws)      # y1 + contribution
+        torch.testing.assert_close(y, 2 * y1, rtol=1e-6, atol=1e-7)
+        y2 = y.clone()
+        fn(dev.desc, T, 0, x, *dev.w, R, y, 1, None, ws)      # k = 0 adds nothing
+        torch.testing.assert_close(y, y2, rtol=0, atol=0)
+        fn(dev.desc, T, 0, x, *dev.w, R, y, 0, None, ws)      # ... and overwrites with 0
+        torch.cuda.synchronize()
+        assert torch.all(y == 0) and torch.all(buf[T + 1] == 12345.0)
+        fn(dev.desc, 0, k, x, *dev.w, R, y, 0, None, ws)      # T = 0 is a no-op
+        torch.cuda.synchronize()
+        assert torch.all(y == 0)
+
+
+def test_errors_leave_outputs_untouched():
+    inp, dev = layer("olmoe-like")
+    T = 2
+    x = to_dev(inp.tokens(T, 2))
+    R = B.Routing.allocate(T, 8, 64)
+    y = torch.full((T, 2048), 7.0, device="cuda")
+    ws = torch.empty(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(B.MoeError) as ei:
+        B.moe_expert_ffn_sparse(dev.desc, T, 103, x, *dev.w, R, y, 0, None, ws)
+    assert ei.value.status == 3
+    with pytest.raises(B.MoeError):
+        B.moe_expert_ffn_dense(dev.desc, T, 2000, x, *dev.w, R, y, 0, None, ws)
+    torch.cuda.synchronize()
+    assert torch.all(y == 7.0)
+
+
+def test_layer_class_matches_direct_calls():
+    from sparse_moe_expert_route_amd.layer import MoELayer
+    inp, dev = layer("deepseek-v2-like")
+    sh = inp.shape
+    x_host = inp.tokens(4, 11)
+    k, k_sh = O.keep_count(0.9, sh.d_ff), O.keep_count(0.5, sh.d_ff_shared)
+    m = MoELayer(hidden=sh.hidden, n_experts=sh.n_experts, d_ff=sh.d_ff, top_k=sh.top_k,
+                 norm_topk=sh.norm_topk, dtype=sh.dtype, w_router=dev.w_router,
+                 w_gate=dev.w[0], w_up=dev.w[1], w_down=dev.w[2], shared=dev.w_sh)
+    say("[case] MoELayer deepseek-v2-like T=4")
+    y = m.forward(to_dev(x_host), k, k_sh, path=SP, path_shared=SP)
+    got = dev.run(x_host, k, SP, k_sh, SP)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(y.cpu().numpy(), got["y"])
