@@ -1,0 +1,335 @@
+#!/usr/bin/env python3
+"""Benchmark of the intra-expert-sparse MoE decode layer on one MI355X.
+
+Workload: the OLMoE-like layer (bf16 weights and tokens, fp32 accumulation;
+hidden 2048, 64 routed experts, d_ff 1024, top-8, no shared expert) at 90%
+intra-expert sparsity (k = 103 kept neurons per token-expert pair),
+synthetic seeded inputs.  One step = one whole layer call on one token
+batch: moe_route, then the routed expert FFN on the path the shape-only
+dispatcher picks.  The headline batch is 16 tokens; batches 1 and 4 are
+measured the same way and reported under "batches".
+
+Timing: every step is a replay of a captured HIP graph of the layer's
+library calls (replays are first checked bitwise against eager calls).
+The weights are cycled over enough device copies, and the token batches
+over as many seeded batches, that >= 1 GB is touched between reuses of a
+copy, so the ~256 MB Infinity Cache cannot serve the weight stream.
+Per-kernel durations come from HIP events the library records around each
+of its launches, on the launch stream; the dominant kernel's roofline uses
+its algorithmic bytes per launch.  The CPU oracle is timed on a bounded
+sample of the same workload on the host cores as a reported baseline.
+
+    python bench.py [--steps K] [--warmup W] [--batch T] [--sweep 1,4,16]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak, GB/s
+LAYER = "olmoe-like"
+MALL_DEFEAT_BYTES = 1 << 30    # bytes touched between reuses of one weight copy
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--batch", type=int, default=16)
+    ap.add_argument("--sparsity", type=float, default=0.9)
+    ap.add_argument("--sweep", default="1,4,16", help="extra batch sizes, or 'none'")
+    ap.add_argument("--path", choices=["auto", "sparse", "dense"], default="auto")
+    ap.add_argument("--timer-steps", type=int, default=50, help="eager steps timed per kernel")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    return ap.parse_args()
+
+
+class Workload:
+    """Device-resident layer copies and token batches for one batch size."""
+
+    def __init__(self, shape, host_w, dev_w0, T, sparsity, path_arg):
+        import torch
+        import moe_synth as S
+        from sparse_moe_expert_route_amd import binding as B
+        self.B, self.torch = B, torch
+        self.shape, self.T = shape, T
+        sh = shape
+        self.desc = B.make_desc(sh.hidden, sh.n_experts, sh.d_ff, sh.top_k, sh.norm_topk, sh.dtype)
+        self.k = B.moe_keep_count(sparsity, sh.d_ff)
+        self.path = {"sparse": B.MOE_PATH_SPARSE, "dense": B.MOE_PATH_DENSE}.get(
+            path_arg, B.moe_select_path(self.desc, T, self.k))
+        # bytes one call touches (gate/up of the expected active experts dominate)
+        E, K = sh.n_experts, sh.top_k
+        act = E * (1 - (1 - K / E) ** T)
+        per_call = act * 3 * sh.hidden * sh.d_ff * 2
+        self.L = max(2, min(24, 1 + math.ceil(MALL_DEFEAT_BYTES / per_call)))
+        self.copies = [dev_w0] + [tuple(w.clone() for w in dev_w0) for _ in range(self.L - 1)]
+        self.x_host = [S.tokens(sh, 1 + i, T) for i in range(self.L)]
+        self.x = [host_w.to_dev(x) for x in self.x_host]
+        self.routing = [B.Routing.allocate(T, K, E) for _ in range(self.L)]
+        self.ws_r = torch.empty(B.moe_route_workspace_size(self.desc, T), dtype=torch.uint8, device="cuda")
+        self.ws = torch.empty(B.moe_ffn_workspace_size(self.desc, T, self.k, self.path),
+                              dtype=torch.uint8, device="cuda")
+        self.y = [torch.empty((T, sh.hidden), dtype=torch.float32, device="cuda") for _ in range(self.L)]
+        self.idx = torch.empty((T * K, max(1, self.k)), dtype=torch.int32, device="cuda")
+        self.ffn = B.moe_expert_ffn_sparse if self.path == B.MOE_PATH_SPARSE else B.moe_expert_ffn_dense
+        self.graphs = []
+
+    def step(self, i, idx=None):
+        B = self.B
+        j = i % self.L
+        wr, wg, wu, wd = self.copies[j]
+        B.moe_route(self.desc, self.T, self.x[j], wr, None, self.routing[j], self.ws_r)
+        self.ffn(self.desc, self.T, self.k, self.x[j], wg, wu, wd, self.routing[j], self.y[j], 0,
+                 idx, self.ws)
+
+    def capture(self):
+        torch = self.torch
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for i in range(self.L):        # warm the allocator / code objects off-graph
+                self.step(i)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        for i in range(self.L):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                self.step(i)
+            self.graphs.append(g)
+        torch.cuda.synchronize()
+
+    def check_replays(self):
+        """Graph replays reproduce eager calls bit for bit, replay after replay."""
+        torch = self.torch
+        ref = []
+        for i in range(self.L):
+            self.step(i)
+            torch.cuda.synchronize()
+            ref.append(self.y[i].clone())
+        for rep in range(3):
+            for i in range(self.L):
+                self.y[i].fill_(float("nan"))
+                self.graphs[i].replay()
+                torch.cuda.synchronize()
+                if not torch.equal(self.y[i], ref[i]):
+                    raise RuntimeError(f"graph replay {rep} of copy {i} differs from the eager call")
+                self.step(i)              # eager work between replays
+                torch.cuda.synchronize()
+
+    def bytes_per_call(self):
+        """Algorithmic HBM bytes of each batch's layer call, from its routing and masks."""
+        import numpy as np
+        torch, sh, B = self.torch, self.shape, self.B
+        out = []
+        for i in range(self.L):
+            self.step(i, idx=self.idx)
+            torch.cuda.synchronize()
+            ids = self.routing[i].topk_ids.cpu().numpy().reshape(-1)
+            idx = self.idx.cpu().numpy()
+            active = np.unique(ids)
+            P = ids.shape[0]
+            bw = 2 if sh.dtype == "bf16" else 4
+            H, d = sh.hidden, sh.d_ff
+            union = sum(len(np.unique(idx[ids == e, :self.k])) for e in active)
+            rec = dict(
+                active=int(len(active)), pairs=int(P),
+                router=sh.n_experts * H * bw,
+                gateup=int(len(active)) * 2 * H * d * bw + self.T * H * bw + P * d * 4,
+                down_rows=P * self.k * H * bw,
+                down_union=union * H * bw,
+                down_dense=int(len(active)) * d * H * bw,
+                io=self.T * H * (bw + 4))
+            path_down = rec["down_rows"] if self.path == B.MOE_PATH_SPARSE else rec["down_dense"]
+            rec["layer"] = rec["router"] + rec["gateup"] + path_down + rec["io"]
+            rec["layer_min"] = rec["router"] + rec["gateup"] + rec["down_union"] + rec["io"]
+            out.append(rec)
+        return out
+
+
+def time_graphs(wl, steps, warmup):
+    torch = wl.torch
+    for i in range(warmup):
+        wl.graphs[i % wl.L].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        wl.graphs[i % wl.L].replay()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
+
+
+def time_kernels(wl, steps):
+    from sparse_moe_expert_route_amd import binding as B
+    torch = wl.torch
+    timer = B.StageTimer(capacity=steps * 8 + 8)
+    torch.cuda.synchronize()
+    with timer:
+        for i in range(steps):
+            wl.step(i)
+    torch.cuda.synchronize()
+    d = timer.durations()
+    timer.close()
+    return {k: dict(n=len(v), avg_us=1e3 * sum(v) / len(v)) for k, v in d.items()}
+
+
+def cpu_baseline(shape, host, wl, seconds):
+    """The oracle as it stands, on the host, over a bounded sample of steps."""
+    import oracle
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        cores = max([i.get("num_threads", 1) for i in info] or [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    T = wl.T
+    done, t0 = 0, time.perf_counter()
+    while True:
+        x = wl.x_host[done % wl.L]
+        oracle.moe_layer(x, host.w_router, None, host.wg, host.wu, host.wd, top_k=shape.top_k,
+                         norm_topk=shape.norm_topk, k_keep=wl.k, dtype=shape.dtype, keep_h=False)
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or done >= 50:
+            break
+    us_per_token = el * 1e6 / (done * T)
+    return {"value": round(us_per_token, 1), "unit": "us/token", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"{done} layer calls of {T} tokens ({done * T} tokens) of the same layer, "
+                      f"{el:.1f} s, float64 numpy oracle"}
+
+
+class HostLayer:
+    def __init__(self, shape):
+        import moe_synth as S
+        self.w_router = S.router_matrix(shape, 0)
+        self.wg, self.wu, self.wd = S.expert_weights(shape, 0)
+
+    @staticmethod
+    def to_dev(a):
+        import numpy as np
+        import torch
+        if a.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def measure(shape, host, dev_w0, T, args):
+    wl = Workload(shape, host, dev_w0, T, args.sparsity, args.path)
+    log(f"[bench] T={T} k={wl.k} path={'sparse' if wl.path == 0 else 'dense'} copies={wl.L}")
+    wl.capture()
+    wl.check_replays()
+    bpc = wl.bytes_per_call()
+    sec = time_graphs(wl, args.steps, args.warmup)
+    kern = time_kernels(wl, args.timer_steps)
+    mean = lambda key: sum(r[key] for r in bpc) / len(bpc)
+    res = dict(T=T, k=wl.k, path="sparse" if wl.path == 0 else "dense", copies=wl.L,
+               us_per_call=sec * 1e6, us_per_token=sec * 1e6 / T, tokens_per_s=T / sec,
+               layer_bytes=mean("layer"), layer_min_bytes=mean("layer_min"),
+               gateup_bytes=mean("gateup"), down_bytes=mean("down_rows"),
+               down_union_bytes=mean("down_union"), active_experts=mean("active"),
+               kernels=kern)
+    res["hbm_gbs"] = res["layer_bytes"] / sec / 1e9
+    res["hbm_frac"] = res["hbm_gbs"] / HBM_PEAK_GBS
+    return wl, res
+
+
+def roofline(res, stage, bytes_key):
+    k = res["kernels"].get(stage)
+    if not k:
+        return None
+    gbs = res[bytes_key] / (k["avg_us"] * 1e-6) / 1e9
+    return {"bound": "hbm", "kernel": stage, "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+            "avg_us": round(k["avg_us"], 2), "bytes_per_launch": int(res[bytes_key])}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU: the layer is a single-GPU kernel path and this build "
+              f"has no multi-GPU mode (asked for --gpus {args.gpus}, WORLD_SIZE {world}).",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import moe_synth as S
+    from sparse_moe_expert_route_amd import binding as B
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    B.lib()
+    shape = S.LAYERS[LAYER]
+    log(f"[bench] generating {LAYER} weights")
+    host = HostLayer(shape)
+    dev_w0 = tuple(host.to_dev(a) for a in (host.w_router, host.wg, host.wu, host.wd))
+    sweep = [] if args.sweep == "none" else [int(t) for t in args.sweep.split(",") if t]
+    batches = {}
+    main_wl, main_res = None, None
+    for T in sorted(set(sweep + [args.batch])):
+        wl, res = measure(shape, host, dev_w0, T, args)
+        batches[str(T)] = {k: (round(v, 3) if isinstance(v, float) else v)
+                           for k, v in res.items() if k != "kernels"}
+        batches[str(T)]["kernels_us"] = {k: round(v["avg_us"], 2) for k, v in res["kernels"].items()}
+        log(f"[bench] T={T}: {res['us_per_call']:.1f} us/call, {res['us_per_token']:.2f} us/token, "
+            f"{res['hbm_gbs']:.0f} GB/s ({100 * res['hbm_frac']:.1f}% of 8 TB/s); kernels "
+            + ", ".join(f"{k} {v['avg_us']:.1f}" for k, v in res["kernels"].items()))
+        if T == args.batch:
+            main_wl, main_res = wl, res
+        else:
+            del wl
+            torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu:
+        log("[bench] timing the CPU oracle")
+        cpu = cpu_baseline(shape, host, main_wl, args.cpu_seconds)
+    r = main_res
+    line = {
+        "metric": "MoE-layer us/token + achieved HBM GB/s (% of peak) at batch 1-16, 90% sparsity",
+        "value": round(r["us_per_token"], 3),
+        "unit": "us/token",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["us_per_call"] / 1e3, 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{LAYER} MoE layer: hidden 2048, 64 routed experts, d_ff 1024, "
+                               f"top-8, bf16 weights/tokens with fp32 accumulation, "
+                               f"sparsity {args.sparsity} (k={r['k']}), batch {args.batch} tokens",
+                   "batch": args.batch, "sparsity": args.sparsity, "k_keep": r["k"],
+                   "path": r["path"], "launch": "hip-graph replay per step",
+                   "weight_copies": r["copies"], "global_batch": args.batch},
+        "tokens_per_s": round(r["tokens_per_s"], 1),
+        "hbm_gbs": round(r["hbm_gbs"], 1),
+        "hbm_frac": round(r["hbm_frac"], 4),
+        "layer_bytes": int(r["layer_bytes"]),
+        "roofline": roofline(r, "gateup_swiglu", "gateup_bytes"),
+        "roofline_down": roofline(r, "down_rows", "down_bytes"),
+        "cpu_baseline": cpu,
+        "batches": batches,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

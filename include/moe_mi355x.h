@@ -187,6 +187,34 @@ int32_t moe_keep_count(double sparsity, int32_t d_ff);
  * input.  MOE_FORCE_PATH=sparse|dense in the environment overrides it. */
 moe_path moe_select_path(const moe_desc *d, int32_t T, int32_t k_keep);
 
+/*
+ * Measurement hook (not part of the layer's function).  Kernel stages the
+ * library launches: */
+typedef enum {
+  MOE_STAGE_ROUTER_LOGITS = 0,
+  MOE_STAGE_ROUTER_TOPK = 1,
+  MOE_STAGE_ROUTE_GROUP = 2,
+  MOE_STAGE_GATEUP = 3,
+  MOE_STAGE_NEURON_MASK = 4,
+  MOE_STAGE_DOWN_ROWS = 5,
+  MOE_STAGE_DOWN_DENSE = 6,
+  MOE_STAGE_COMBINE = 7,
+  MOE_STAGE_ZERO = 8,
+  MOE_N_STAGES = 9
+} moe_stage;
+
+/* While attached, every kernel the library launches from this thread is
+ * bracketed by two caller-created timing events recorded on its launch
+ * stream: the i-th launch records events[2i] before and events[2i+1] after
+ * itself and writes its moe_stage to stages[i]; once `capacity` launches are
+ * recorded, further launches are not bracketed.  events: 2 * capacity
+ * caller-owned hipEvent_t (host array); stages: capacity int32 (host).
+ * Nothing is allocated.  Recording adds a marker per launch to the stream,
+ * so time the layer without the hook attached. */
+moe_status moe_timer_attach(hipEvent_t *events, int32_t *stages, int32_t capacity);
+/* Detach; returns the number of launches recorded since attaching. */
+int32_t moe_timer_detach(void);
+
 /* Static name of a status code. */
 const char *moe_status_string(moe_status s);
 

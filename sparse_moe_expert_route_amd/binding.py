@@ -51,6 +51,8 @@ _SIGS = {
     "moe_ffn_workspace_size": (_SZ, [_PD, _I32, _I32, _I32]),
     "moe_keep_count": (_I32, [_D, _I32]),
     "moe_select_path": (_I32, [_PD, _I32, _I32]),
+    "moe_timer_attach": (_I32, [ctypes.POINTER(_V), ctypes.POINTER(_I32), _I32]),
+    "moe_timer_detach": (_I32, []),
     "moe_status_string": (ctypes.c_char_p, [_I32]),
     "moe_last_error": (ctypes.c_char_p, []),
     "moe_version": (ctypes.c_char_p, []),
@@ -200,3 +202,52 @@ def moe_last_error() -> str:
 
 def moe_version() -> str:
     return lib().moe_version().decode()
+
+
+# ------------------------------------------------------------ per-kernel timing
+
+class StageTimer:
+    """Brackets every kernel the library launches with HIP timing events
+    (moe_timer_attach), then reports per-stage durations.  Host-side
+    plumbing for measurement; events come from the process's HIP runtime."""
+
+    STAGES = ["router_logits", "router_topk", "route_group", "gateup_swiglu", "neuron_topk",
+              "down_rows", "down_dense", "combine", "zero"]
+
+    def __init__(self, capacity: int):
+        lib()
+        self.hip = ctypes.CDLL("libamdhip64.so.7")   # the runtime already loaded by torch
+        self.cap = int(capacity)
+        self.events = (ctypes.c_void_p * (2 * self.cap))()
+        self.stages = (ctypes.c_int32 * self.cap)()
+        for i in range(2 * self.cap):
+            rc = self.hip.hipEventCreate(ctypes.byref(self.events, i * ctypes.sizeof(ctypes.c_void_p)))
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreate failed ({rc})")
+        self.n = 0
+
+    def __enter__(self):
+        _check(lib().moe_timer_attach(self.events, self.stages, self.cap))
+        return self
+
+    def __exit__(self, *exc):
+        self.n = lib().moe_timer_detach()
+        return False
+
+    def durations(self):
+        """{stage name: [ms, ...]} of the recorded launches (synchronises)."""
+        out = {}
+        ms = ctypes.c_float()
+        for i in range(self.n):
+            self.hip.hipEventSynchronize(ctypes.c_void_p(self.events[2 * i + 1]))
+            rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(self.events[2 * i]),
+                                              ctypes.c_void_p(self.events[2 * i + 1]))
+            if rc != 0:
+                raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+            out.setdefault(self.STAGES[self.stages[i]], []).append(ms.value)
+        return out
+
+    def close(self):
+        for i in range(2 * self.cap):
+            self.hip.hipEventDestroy(ctypes.c_void_p(self.events[i]))
+        self.cap = 0

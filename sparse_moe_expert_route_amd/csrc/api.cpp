@@ -10,6 +10,13 @@
 #include "moe_mi355x.h"
 #include "internal.h"
 
+namespace moe {
+StageTimer &stage_timer() {
+  static thread_local StageTimer t;
+  return t;
+}
+}  // namespace moe
+
 namespace {
 
 thread_local char g_err[512] = "";
@@ -285,6 +292,25 @@ const char *moe_status_string(moe_status s) {
     case MOE_ERR_HIP: return "MOE_ERR_HIP";
   }
   return "MOE_ERR_UNKNOWN";
+}
+
+moe_status moe_timer_attach(hipEvent_t *events, int32_t *stages, int32_t capacity) {
+  g_err[0] = 0;
+  if (!events || !stages || capacity <= 0)
+    return fail(MOE_ERR_INVALID_ARG, "timer needs events, stages and a positive capacity");
+  moe::StageTimer &t = moe::stage_timer();
+  t.events = events;
+  t.stages = stages;
+  t.capacity = capacity;
+  t.n = 0;
+  return MOE_OK;
+}
+
+int32_t moe_timer_detach(void) {
+  moe::StageTimer &t = moe::stage_timer();
+  const int32_t n = t.n;
+  t = moe::StageTimer{};
+  return n;
 }
 
 const char *moe_last_error(void) { return g_err; }

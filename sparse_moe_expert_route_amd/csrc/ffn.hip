@@ -531,8 +531,10 @@ size_t max_partial_rows(int P, int k, int H, int bf16) {
 static void launch_mask(const FfnArgs &a, const RouteView &rv, int32_t *idx, float *hact, void *hm,
                         int hm_bf16, hipStream_t stream) {
   const int P = a.T * a.top_k;
+  timer_begin(kStageMask, stream);
   neuron_topk_kernel<<<P, 256, (size_t)a.d_ff * 4, stream>>>(a.h, rv, a.d_ff, a.k_keep, idx, hact,
                                                               hm, hm_bf16);
+  timer_end(stream);
 }
 
 // A routed expert never holds more than T tokens, so at T <= 16 one token
@@ -540,6 +542,7 @@ static void launch_mask(const FfnArgs &a, const RouteView &rv, int32_t *idx, flo
 static void launch_gateup(const FfnArgs &a, const RouteView &rv, hipStream_t stream) {
   const bool one = a.T <= 16;
   dim3 grid(n_items(a, one ? 16 : 64), a.d_ff / 16);
+  timer_begin(kStageGateup, stream);
   if (a.bf16) {
     if (one) gateup_swiglu_kernel<true, 1><<<grid, 256, 0, stream>>>(a.x, a.w_gate, a.w_up, rv, a.H, a.d_ff, a.h);
     else gateup_swiglu_kernel<true, 4><<<grid, 256, 0, stream>>>(a.x, a.w_gate, a.w_up, rv, a.H, a.d_ff, a.h);
@@ -547,20 +550,39 @@ static void launch_gateup(const FfnArgs &a, const RouteView &rv, hipStream_t str
     if (one) gateup_swiglu_kernel<false, 1><<<grid, 256, 0, stream>>>(a.x, a.w_gate, a.w_up, rv, a.H, a.d_ff, a.h);
     else gateup_swiglu_kernel<false, 4><<<grid, 256, 0, stream>>>(a.x, a.w_gate, a.w_up, rv, a.H, a.d_ff, a.h);
   }
+  timer_end(stream);
 }
 
 static void launch_combine(const FfnArgs &a, int n_chunks, hipStream_t stream) {
   dim3 grid(a.T, (a.H + 1023) / 1024);
+  timer_begin(kStageCombine, stream);
   combine_kernel<<<grid, 256, 0, stream>>>(a.partial, a.H, a.top_k, n_chunks, a.accumulate, a.y);
+  timer_end(stream);
 }
 
 static bool zero_contribution(const FfnArgs &a, hipStream_t stream) {
   if (a.k_keep > 0) return false;
   if (!a.accumulate) {
     const size_t n = (size_t)a.T * a.H;
+    timer_begin(kStageZero, stream);
     zero_kernel<<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(a.y, n);
+    timer_end(stream);
   }
   return true;
+}
+
+static void launch_down_rows(const FfnArgs &a, const RouteView &rv, const int32_t *idx,
+                             const float *coef, int k, const DownPlan &dp, hipStream_t stream) {
+  const int P = a.T * a.top_k;
+  dim3 grid(P * dp.n_chunks, (a.H + slice_width(a.bf16) - 1) / slice_width(a.bf16));
+  timer_begin(kStageDownRows, stream);
+  if (a.bf16)
+    down_rows_kernel<true><<<grid, 256, 0, stream>>>(a.w_down, idx, coef, rv, a.H, a.d_ff, k,
+                                                     dp.n_chunks, dp.rows_per_chunk, a.partial);
+  else
+    down_rows_kernel<false><<<grid, 256, 0, stream>>>(a.w_down, idx, coef, rv, a.H, a.d_ff, k,
+                                                      dp.n_chunks, dp.rows_per_chunk, a.partial);
+  timer_end(stream);
 }
 
 hipError_t launch_ffn_sparse(const FfnArgs &a, hipStream_t stream) {
@@ -571,15 +593,7 @@ hipError_t launch_ffn_sparse(const FfnArgs &a, hipStream_t stream) {
   launch_gateup(a, rv, stream);
   launch_mask(a, rv, a.idx, a.hact, nullptr, 0, stream);
   const DownPlan dp = plan_down(P, a.k_keep, a.H, a.bf16);
-  dim3 grid(P * dp.n_chunks, (a.H + slice_width(a.bf16) - 1) / slice_width(a.bf16));
-  if (a.bf16)
-    down_rows_kernel<true><<<grid, 256, 0, stream>>>(a.w_down, a.idx, a.hact, rv, a.H, a.d_ff,
-                                                     a.k_keep, dp.n_chunks, dp.rows_per_chunk,
-                                                     a.partial);
-  else
-    down_rows_kernel<false><<<grid, 256, 0, stream>>>(a.w_down, a.idx, a.hact, rv, a.H, a.d_ff,
-                                                      a.k_keep, dp.n_chunks, dp.rows_per_chunk,
-                                                      a.partial);
+  launch_down_rows(a, rv, a.idx, a.hact, a.k_keep, dp, stream);
   launch_combine(a, dp.n_chunks, stream);
   return hipGetLastError();
 }
@@ -593,18 +607,16 @@ hipError_t launch_ffn_dense(const FfnArgs &a, hipStream_t stream) {
   launch_mask(a, rv, a.idx, nullptr, a.hm, a.bf16, stream);
   if (a.bf16) {
     dim3 grid(n_items(a, kDenseTokGroup), a.H / 64);
+    timer_begin(kStageDownDense, stream);
     down_dense_bf16_kernel<<<grid, 256, 0, stream>>>(static_cast<const uint16_t *>(a.w_down),
                                                      static_cast<const uint16_t *>(a.hm), rv, a.H,
                                                      a.d_ff, a.partial);
+    timer_end(stream);
     launch_combine(a, 1, stream);
   } else {
     // fp32: every row of W_d against the dense masked row, on the row kernel
     const DownPlan dp = plan_down(P, a.d_ff, a.H, 0);
-    dim3 grid(P * dp.n_chunks, (a.H + slice_width(0) - 1) / slice_width(0));
-    down_rows_kernel<false><<<grid, 256, 0, stream>>>(a.w_down, nullptr,
-                                                      static_cast<const float *>(a.hm), rv, a.H,
-                                                      a.d_ff, a.d_ff, dp.n_chunks,
-                                                      dp.rows_per_chunk, a.partial);
+    launch_down_rows(a, rv, nullptr, static_cast<const float *>(a.hm), a.d_ff, dp, stream);
     launch_combine(a, dp.n_chunks, stream);
   }
   return hipGetLastError();

@@ -7,6 +7,34 @@
 
 namespace moe {
 
+// Optional per-launch event bracketing (the moe_timer_attach hook).
+struct StageTimer {
+  hipEvent_t *events = nullptr;
+  int32_t *stages = nullptr;
+  int capacity = 0;
+  int n = 0;
+};
+StageTimer &stage_timer();
+
+inline void timer_begin(int stage, hipStream_t s) {
+  StageTimer &t = stage_timer();
+  if (t.events && t.n < t.capacity) {
+    (void)hipEventRecord(t.events[2 * t.n], s);
+    t.stages[t.n] = stage;
+  }
+}
+inline void timer_end(hipStream_t s) {
+  StageTimer &t = stage_timer();
+  if (t.events && t.n < t.capacity) {
+    (void)hipEventRecord(t.events[2 * t.n + 1], s);
+    ++t.n;
+  }
+}
+
+// Stage ids (mirror moe_stage in the public header).
+enum { kStageLogits = 0, kStageTopk, kStageGroup, kStageGateup, kStageMask, kStageDownRows,
+       kStageDownDense, kStageCombine, kStageZero };
+
 struct RouteArgs {
   int T, H, E, top_k, norm_topk, bf16;
   const void *x, *w_router;

@@ -200,11 +200,14 @@ __global__ __launch_bounds__(1024) void route_group_kernel(const int32_t *__rest
 hipError_t launch_route(const RouteArgs &a, hipStream_t stream) {
   if (a.T == 0) return hipSuccess;
   dim3 g1((a.E + 3) / 4, (a.T + kLogitTokens - 1) / kLogitTokens);
+  timer_begin(kStageLogits, stream);
   if (a.bf16)
     router_logits_kernel<true><<<g1, 256, 0, stream>>>(a.x, a.w_router, a.bias, a.T, a.H, a.E, a.logits);
   else
     router_logits_kernel<false><<<g1, 256, 0, stream>>>(a.x, a.w_router, a.bias, a.T, a.H, a.E, a.logits);
+  timer_end(stream);
   dim3 g2((a.T + 3) / 4);
+  timer_begin(kStageTopk, stream);
   if (a.E <= 64)
     router_topk_kernel<1><<<g2, 256, 0, stream>>>(a.logits, a.T, a.E, a.top_k, a.norm_topk, a.topk_ids, a.topk_w);
   else if (a.E <= 128)
@@ -213,8 +216,11 @@ hipError_t launch_route(const RouteArgs &a, hipStream_t stream) {
     router_topk_kernel<4><<<g2, 256, 0, stream>>>(a.logits, a.T, a.E, a.top_k, a.norm_topk, a.topk_ids, a.topk_w);
   else
     router_topk_kernel<16><<<g2, 256, 0, stream>>>(a.logits, a.T, a.E, a.top_k, a.norm_topk, a.topk_ids, a.topk_w);
+  timer_end(stream);
+  timer_begin(kStageGroup, stream);
   route_group_kernel<<<1, 1024, 0, stream>>>(a.topk_ids, a.T * a.top_k, a.E, a.offsets,
                                              a.pair_by_expert, a.active, a.n_active);
+  timer_end(stream);
   return hipGetLastError();
 }
 
