@@ -32,6 +32,9 @@
  *   gate, up AND down: row j of the down matrix is neuron j's H-vector
  *   contribution (the transpose of a torch down_proj.weight [H, d_ff]), so
  *   a kept neuron's down row is one contiguous H * elem_bytes stream.
+ *   The FFN calls read gate and up in the PACKED layout that
+ *   moe_pack_gate_up produces from that row-major form (once, at load time);
+ *   down and the router matrix stay row-major.
  * - dtype MOE_BF16: x, router and expert weights are bf16 (raw bits,
  *   round-to-nearest-even), every accumulation is fp32; MOE_F32: all fp32.
  *   Router logits, softmax weights, h and y are fp32 in both.
@@ -140,7 +143,8 @@ moe_status moe_route(const moe_desc *d, int32_t T, const void *x, const void *w_
  * bitwise reproducible.
  *
  * k_keep in [0, d_ff]; k_keep == d_ff keeps every neuron, 0 adds nothing.
- * x [T, H] and w_gate, w_up, w_down [E, d_ff, H] in desc->dtype.
+ * x [T, H] and w_down [E, d_ff, H] in desc->dtype; w_gate and w_up the
+ * same tensors packed by moe_pack_gate_up.
  * active_idx_out: optional [T * top_k, k_keep] int32, the kept neuron ids of
  * each pair in ascending order (NULL to skip).
  * workspace: moe_ffn_workspace_size(d, T, k_keep, MOE_PATH_SPARSE).
@@ -167,6 +171,23 @@ moe_status moe_expert_ffn_dense(const moe_desc *d, int32_t T, int32_t k_keep, co
                                 const moe_routing *routing, float *y, int32_t accumulate,
                                 int32_t *active_idx_out, void *workspace,
                                 size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * moe_pack_gate_up -- rearrange one gate or up tensor [E, d_ff, H] from
+ * row-major into the packed layout the FFN calls read: for each expert e,
+ * neuron tile nt (16 neurons) and k-step ks (KS = 32 bf16 or 16 fp32
+ * columns), one contiguous 1 KB fragment holds W[e, 16 nt + r, KS ks + c]
+ * at element offset (r + 16 * (c / (KS/4))) * (KS/4) + c % (KS/4), for
+ * r < 16, c < KS; fragment index (e * d_ff/16 + nt) * (H/KS) + ks.  So a
+ * wave loads one MFMA operand fragment as 1 KB of consecutive bytes.  Only
+ * 16-byte chunks move, so packing is exact.  src and dst must not overlap;
+ * both are E * d_ff * H elements of desc->dtype.  moe_unpack_gate_up is the
+ * inverse.
+ */
+moe_status moe_pack_gate_up(const moe_desc *d, const void *src_rowmajor, void *dst_packed,
+                            hipStream_t stream);
+moe_status moe_unpack_gate_up(const moe_desc *d, const void *src_packed, void *dst_rowmajor,
+                              hipStream_t stream);
 
 /* Workspace bytes for moe_route over at most T tokens (0 on invalid input). */
 size_t moe_route_workspace_size(const moe_desc *d, int32_t T);

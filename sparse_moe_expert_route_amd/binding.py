@@ -47,6 +47,8 @@ _SIGS = {
     "moe_route": (_I32, [_PD, _I32, _V, _V, _V, _PR, _V, _SZ, _V]),
     "moe_expert_ffn_sparse": (_I32, [_PD, _I32, _I32, _V, _V, _V, _V, _PR, _V, _I32, _V, _V, _SZ, _V]),
     "moe_expert_ffn_dense": (_I32, [_PD, _I32, _I32, _V, _V, _V, _V, _PR, _V, _I32, _V, _V, _SZ, _V]),
+    "moe_pack_gate_up": (_I32, [_PD, _V, _V, _V]),
+    "moe_unpack_gate_up": (_I32, [_PD, _V, _V, _V]),
     "moe_route_workspace_size": (_SZ, [_PD, _I32]),
     "moe_ffn_workspace_size": (_SZ, [_PD, _I32, _I32, _I32]),
     "moe_keep_count": (_I32, [_D, _I32]),
@@ -174,6 +176,22 @@ def moe_expert_ffn_dense(desc, T, k_keep, x, w_gate, w_up, w_down, routing, y, a
                          active_idx_out=None, workspace=None, stream=None):
     _ffn(lib().moe_expert_ffn_dense, desc, T, k_keep, x, w_gate, w_up, w_down, routing, y,
          accumulate, active_idx_out, workspace, stream)
+
+
+def moe_pack_gate_up(desc: MoeDesc, src, dst=None, stream=None):
+    """Pack a row-major gate or up tensor [E, d_ff, H]; returns dst."""
+    import torch
+    dst = torch.empty_like(src) if dst is None else dst
+    _check(lib().moe_pack_gate_up(ctypes.byref(desc), _ptr(src), _ptr(dst), _stream(stream)))
+    return dst
+
+
+def moe_unpack_gate_up(desc: MoeDesc, src, dst=None, stream=None):
+    """Inverse of moe_pack_gate_up; returns dst."""
+    import torch
+    dst = torch.empty_like(src) if dst is None else dst
+    _check(lib().moe_unpack_gate_up(ctypes.byref(desc), _ptr(src), _ptr(dst), _stream(stream)))
+    return dst
 
 
 def moe_route_workspace_size(desc: MoeDesc, T: int) -> int:

@@ -93,12 +93,7 @@ FfnLayout ffn_layout(const moe_desc *d, int32_t T, int32_t k, moe_path path) {
   L.hact = off;
   if (path == MOE_PATH_SPARSE) off += up(P * (size_t)k * 4);
   L.partial = off;
-  size_t rows;
-  if (path == MOE_PATH_SPARSE)
-    rows = moe::max_partial_rows((int)P, k, d->hidden, bf16);
-  else
-    rows = bf16 ? P : moe::max_partial_rows((int)P, d->d_ff, d->hidden, 0);
-  off += up(rows * d->hidden * 4);
+  if (path == MOE_PATH_DENSE && bf16) off += up(P * d->hidden * 4);
   L.hm = off;
   if (path == MOE_PATH_DENSE) off += up(P * d->d_ff * elem_bytes(d));
   L.total = off;
@@ -244,9 +239,34 @@ moe_status moe_expert_ffn_dense(const moe_desc *d, int32_t T, int32_t k_keep, co
                  active_idx_out, workspace, workspace_bytes, stream);
 }
 
+static moe_status pack_impl(const moe_desc *d, const void *src, void *dst, int unpack,
+                            hipStream_t stream) {
+  g_err[0] = 0;
+  TRY(check_desc(d));
+  TRY(need_ptr(src, "src"));
+  TRY(need_ptr(dst, "dst"));
+  const size_t bytes = (size_t)d->n_experts * d->d_ff * d->hidden * elem_bytes(d);
+  const char *s = static_cast<const char *>(src), *t = static_cast<const char *>(dst);
+  if (s < t + bytes && t < s + bytes) return fail(MOE_ERR_INVALID_ARG, "src and dst overlap");
+  const hipError_t e = moe::launch_pack_gate_up(src, dst, d->n_experts, d->d_ff, d->hidden,
+                                                d->dtype == MOE_BF16, unpack, stream);
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return MOE_OK;
+}
+
+moe_status moe_pack_gate_up(const moe_desc *d, const void *src_rowmajor, void *dst_packed,
+                            hipStream_t stream) {
+  return pack_impl(d, src_rowmajor, dst_packed, 0, stream);
+}
+
+moe_status moe_unpack_gate_up(const moe_desc *d, const void *src_packed, void *dst_rowmajor,
+                              hipStream_t stream) {
+  return pack_impl(d, src_packed, dst_rowmajor, 1, stream);
+}
+
 size_t moe_route_workspace_size(const moe_desc *d, int32_t T) {
   if (check_desc(d) != MOE_OK || check_T(T) != MOE_OK) return 0;
-  return up((size_t)(T > 0 ? T : 1) * d->n_experts * 4);
+  return up((size_t)moe::kRouterSplits * (T > 0 ? T : 1) * d->n_experts * 4);
 }
 
 size_t moe_ffn_workspace_size(const moe_desc *d, int32_t T, int32_t k_keep, moe_path path) {

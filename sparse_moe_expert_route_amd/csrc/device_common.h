@@ -19,6 +19,12 @@ __device__ __forceinline__ u32x4 ld16(const void *p) {
   return *reinterpret_cast<const u32x4 *>(p);
 }
 
+// 16-byte load with the non-temporal (streaming) hint: for weight streams
+// that are read exactly once per call.
+__device__ __forceinline__ u32x4 ld16_nt(const void *p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+}
+
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
@@ -71,32 +77,66 @@ struct RouteView {
   __device__ __forceinline__ float weight(int p) const { return implicit ? 1.0f : topk_w[p]; }
 };
 
-// ---- wavefront reductions and scans (fixed butterfly order: deterministic)
+// ---- wavefront reductions and scans
+// Built on DPP row shifts and row broadcasts (register-to-register, no LDS
+// round trip): row_shr:1,2,4,8 scan each row of 16 lanes, row_bcast:15 and
+// row_bcast:31 carry row totals into the following rows.  Every caller runs
+// them with all 64 lanes active.  The order of operations is fixed, so the
+// results are deterministic.
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+template <int CTRL, int ROW_MASK, bool BOUND_ZERO>
+__device__ __forceinline__ int dpp(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xf, BOUND_ZERO);
 }
-
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    uint64_t w = __shfl_xor(v, o, kWave);
-    v = w > v ? w : v;
-  }
-  return v;
-}
+constexpr int kShr1 = 0x111, kShr2 = 0x112, kShr4 = 0x114, kShr8 = 0x118;
+constexpr int kBcast15 = 0x142, kBcast31 = 0x143;
 
 // Inclusive prefix sum over the lanes of a wave.
 __device__ __forceinline__ int wave_incl_scan(int v) {
-  const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    int w = __shfl_up(v, o, kWave);
-    if (lane >= o) v += w;
-  }
+  v += dpp<kShr1, 0xf, true>(v);
+  v += dpp<kShr2, 0xf, true>(v);
+  v += dpp<kShr4, 0xf, true>(v);
+  v += dpp<kShr8, 0xf, true>(v);
+  v += dpp<kBcast15, 0xa, false>(v);
+  v += dpp<kBcast31, 0xc, false>(v);
   return v;
+}
+
+__device__ __forceinline__ int lane_value(int v, int lane) {
+  return __builtin_amdgcn_readlane(v, lane);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#define MOE_FADD(C, M, B) v += __int_as_float(dpp<C, M, B>(__float_as_int(v)))
+  MOE_FADD(kShr1, 0xf, true);
+  MOE_FADD(kShr2, 0xf, true);
+  MOE_FADD(kShr4, 0xf, true);
+  MOE_FADD(kShr8, 0xf, true);
+  MOE_FADD(kBcast15, 0xa, false);
+  MOE_FADD(kBcast31, 0xc, false);
+#undef MOE_FADD
+  return __int_as_float(lane_value(__float_as_int(v), 63));
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#define MOE_UMAX(C, M, B) v = max(v, (uint32_t)dpp<C, M, B>((int)v))
+  MOE_UMAX(kShr1, 0xf, true);
+  MOE_UMAX(kShr2, 0xf, true);
+  MOE_UMAX(kShr4, 0xf, true);
+  MOE_UMAX(kShr8, 0xf, true);
+  MOE_UMAX(kBcast15, 0xa, false);
+  MOE_UMAX(kBcast31, 0xc, false);
+#undef MOE_UMAX
+  return (uint32_t)lane_value((int)v, 63);
+}
+
+// Maximum 64-bit key over the wave: the high words first, then the low
+// words among the lanes that hold the maximal high word.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  const uint32_t hi = (uint32_t)(v >> 32), lo = (uint32_t)v;
+  const uint32_t mh = wave_max_u32(hi);
+  const uint32_t ml = wave_max_u32(hi == mh ? lo : 0u);
+  return ((uint64_t)mh << 32) | ml;
 }
 
 // Inclusive prefix sum over a whole block of NT threads (NT/64 <= 64 waves).
@@ -127,6 +167,12 @@ __device__ __forceinline__ uint32_t ordered_key(float f) {
   uint32_t u = __float_as_uint(f);
   if ((u & 0x7fffffffu) == 0u) u = 0u;
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Inverse of ordered_key on the upper 32 bits of a 64-bit selection key.
+__device__ __forceinline__ float key_value(uint64_t key) {
+  const uint32_t u = (uint32_t)(key >> 32);
+  return __uint_as_float((u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
 }
 
 }  // namespace moe

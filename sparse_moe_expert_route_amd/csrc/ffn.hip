@@ -48,13 +48,13 @@ __device__ __forceinline__ bool find_item(const RouteView &rv, int item, int &e,
       cnt = (n + kTokGroup - 1) / kTokGroup;
     }
     const int incl = wave_incl_scan(cnt);
-    const int tot = __shfl(incl, 63, 64);
+    const int tot = lane_value(incl, 63);
     if (item < base + tot) {
       const uint64_t m = __ballot(s < nact && item < base + incl);
       const int L = __ffsll((unsigned long long)m) - 1;
-      e = __shfl(ee, L, 64);
-      const int bb = __shfl(b, L, 64), nn = __shfl(n, L, 64);
-      const int before = __shfl(incl - cnt, L, 64);
+      e = lane_value(ee, L);
+      const int bb = lane_value(b, L), nn = lane_value(n, L);
+      const int before = lane_value(incl - cnt, L);
       const int gi = item - base - before;
       q0 = bb + gi * kTokGroup;
       ntok = min(kTokGroup, nn - gi * kTokGroup);
@@ -74,20 +74,30 @@ __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 // keeps 16x16 MFMA accumulators for gate and up for MT token tiles; weights
 // are loaded once, token rows (16 B per lane) come from L2.  The wave
 // partials meet in LDS, where h = silu(g) * u is formed and written per pair.
-template <bool BF16, int MT>
-__global__ __launch_bounds__(256) void gateup_swiglu_kernel(const void *__restrict__ xv,
+template <bool BF16, int MT, int W>
+__global__ __launch_bounds__(64 * W, MT == 1 ? 8 : 1) void gateup_swiglu_kernel(const void *__restrict__ xv,
                                                             const void *__restrict__ wgv,
                                                             const void *__restrict__ wuv,
                                                             RouteView rv, int H, int d_ff,
                                                             float *__restrict__ hout) {
-  __shared__ float red[4][2][MT][4][64];
+  __shared__ float red[W][2][MT][4][64];
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   int e, q0, ntok;
-  if (!find_item<16 * MT>(rv, blockIdx.x, e, q0, ntok)) return;  // block-uniform
+  if (MT == 1 && rv.T <= 16) {
+    // every active expert holds <= T <= 16 tokens: work item == active slot
+    const int s = blockIdx.x;
+    if (s >= rv.nact()) return;  // block-uniform
+    e = rv.expert(s);
+    q0 = rv.begin(e);
+    ntok = rv.end(e) - q0;
+  } else if (!find_item<16 * MT>(rv, blockIdx.x, e, q0, ntok)) {
+    return;  // block-uniform
+  }
   const int ntiles = (ntok + 15) >> 4;
   const int r = lane & 15, g = lane >> 4;
   const int row0 = blockIdx.y * 16;
-  const size_t wrow = ((size_t)e * d_ff + row0 + r) * (size_t)H;
+  // packed weights: fragment (e, neuron tile, k-step) is 1 KB, lane-ordered
+  const size_t ftile = (size_t)e * (d_ff / 16) + blockIdx.y;
 
   size_t xoff[MT];
   bool xval[MT];
@@ -102,26 +112,25 @@ __global__ __launch_bounds__(256) void gateup_swiglu_kernel(const void *__restri
 #pragma unroll
   for (int tl = 0; tl < MT; ++tl) { accg[tl] = f32x4{0, 0, 0, 0}; accu[tl] = f32x4{0, 0, 0, 0}; }
 
-  constexpr int U = 4;
+  constexpr int U = 4;  // k-steps in flight per wave
   if (BF16) {
-    const uint16_t *wg = static_cast<const uint16_t *>(wgv) + wrow;
-    const uint16_t *wu = static_cast<const uint16_t *>(wuv) + wrow;
-    const uint16_t *x = static_cast<const uint16_t *>(xv);
     const int nsteps = H / 32;
-    for (int s = wid; s < nsteps; s += 4 * U) {
+    const uint16_t *wg = static_cast<const uint16_t *>(wgv) + ftile * nsteps * 512 + lane * 8;
+    const uint16_t *wu = static_cast<const uint16_t *>(wuv) + ftile * nsteps * 512 + lane * 8;
+    const uint16_t *x = static_cast<const uint16_t *>(xv);
+    for (int s = wid; s < nsteps; s += W * U) {
       u32x4 ag[U], au[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int ks = s + 4 * u;
+        const int ks = s + W * u;
         if (ks < nsteps) {
-          const int k = ks * 32 + g * 8;
-          ag[u] = ld16(wg + k);
-          au[u] = ld16(wu + k);
+          ag[u] = ld16_nt(wg + (size_t)ks * 512);
+          au[u] = ld16_nt(wu + (size_t)ks * 512);
         }
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int ks = s + 4 * u;
+        const int ks = s + W * u;
         if (ks < nsteps) {
           const int k = ks * 32 + g * 8;
 #pragma unroll
@@ -136,24 +145,23 @@ __global__ __launch_bounds__(256) void gateup_swiglu_kernel(const void *__restri
       }
     }
   } else {
-    const float *wg = static_cast<const float *>(wgv) + wrow;
-    const float *wu = static_cast<const float *>(wuv) + wrow;
-    const float *x = static_cast<const float *>(xv);
     const int nsteps = H / 16;
-    for (int s = wid; s < nsteps; s += 4 * U) {
+    const float *wg = static_cast<const float *>(wgv) + ftile * nsteps * 256 + lane * 4;
+    const float *wu = static_cast<const float *>(wuv) + ftile * nsteps * 256 + lane * 4;
+    const float *x = static_cast<const float *>(xv);
+    for (int s = wid; s < nsteps; s += W * U) {
       u32x4 ag[U], au[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int ks = s + 4 * u;
+        const int ks = s + W * u;
         if (ks < nsteps) {
-          const int k = ks * 16 + g * 4;
-          ag[u] = ld16(wg + k);
-          au[u] = ld16(wu + k);
+          ag[u] = ld16_nt(wg + (size_t)ks * 256);
+          au[u] = ld16_nt(wu + (size_t)ks * 256);
         }
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int ks = s + 4 * u;
+        const int ks = s + W * u;
         if (ks < nsteps) {
           const int k = ks * 16 + g * 4;
 #pragma unroll
@@ -183,14 +191,16 @@ __global__ __launch_bounds__(256) void gateup_swiglu_kernel(const void *__restri
     }
   }
   __syncthreads();
-  for (int o = threadIdx.x; o < ntiles * 256; o += 256) {
+  for (int o = threadIdx.x; o < ntiles * 256; o += 64 * W) {
     const int tl = o >> 8, rr = (o >> 6) & 3, ln = o & 63;
     const int c = tl * 16 + (ln & 15);
     if (c < ntok) {
-      const float gs = red[0][0][tl][rr][ln] + red[1][0][tl][rr][ln] + red[2][0][tl][rr][ln] +
-                       red[3][0][tl][rr][ln];
-      const float us = red[0][1][tl][rr][ln] + red[1][1][tl][rr][ln] + red[2][1][tl][rr][ln] +
-                       red[3][1][tl][rr][ln];
+      float gs = 0.f, us = 0.f;
+#pragma unroll
+      for (int w = 0; w < W; ++w) {  // wave partials in fixed order
+        gs += red[w][0][tl][rr][ln];
+        us += red[w][1][tl][rr][ln];
+      }
       const int neuron = row0 + 4 * (ln >> 4) + rr;
       const int p = rv.pair_at(q0 + c);
       hout[(size_t)p * d_ff + neuron] = silu(gs) * us;
@@ -292,55 +302,179 @@ __global__ __launch_bounds__(256) void neuron_topk_kernel(const float *__restric
   }
 }
 
+// Wave-per-pair variant for d_ff = 64 * V: one wave per pair keeps the
+// pair's V activations per lane in registers (a contiguous index segment
+// per lane) and a 256-bin histogram in LDS.  The radix digits follow the
+// float fields of |h| (bits 30..23 = exponent, then 22..15, 14..7, 6..0), so
+// the first pass already spreads the values.  Digit search and compaction
+// use DPP wavefront scans; barriers are single-wave.
+template <int V>
+__global__ __launch_bounds__(64) void neuron_topk_wave_kernel(const float *__restrict__ h,
+                                                              RouteView rv, int P, int d_ff,
+                                                              int k, int32_t *__restrict__ idx,
+                                                              float *__restrict__ hact,
+                                                              void *__restrict__ hm,
+                                                              int hm_bf16) {
+  __shared__ int hist[256];
+  const int lane = threadIdx.x & 63;
+  const int p = blockIdx.x;
+  const float w = rv.weight(p);
+  const float *hp = h + (size_t)p * d_ff + (size_t)lane * V;
+  uint32_t bits[V];
+#pragma unroll
+  for (int i = 0; i < V; ++i) bits[i] = __float_as_uint(hp[i]);
+
+  const bool keep_all = k >= d_ff;
+  uint32_t tau = 0, pmask = 0;
+  int krem = k;
+  if (!keep_all && k > 0) {
+#pragma unroll
+    for (int pass = 0; pass < 4; ++pass) {
+      const int shift = pass == 0 ? 23 : pass == 1 ? 15 : pass == 2 ? 7 : 0;
+      const uint32_t dmask = pass == 3 ? 0x7fu : 0xffu;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) hist[lane * 4 + b] = 0;
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < V; ++i) {
+        const uint32_t key = bits[i] & 0x7fffffffu;
+        if ((key & pmask) == tau) atomicAdd(&hist[(key >> shift) & dmask], 1);
+      }
+      __syncthreads();
+      // lane owns digits 255 - 4 lane - b, b = 0..3 (descending)
+      int c[4], local = 0;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) { c[b] = hist[255 - 4 * lane - b]; local += c[b]; }
+      int run = wave_incl_scan(local) - local;  // keys with a larger digit
+      int dsel = -1, knew = 0;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        if (dsel < 0 && run + c[b] >= krem && run < krem) { dsel = 255 - 4 * lane - b; knew = krem - run; }
+        run += c[b];
+      }
+      const uint64_t m = __ballot(dsel >= 0);
+      const int L = __ffsll((unsigned long long)m) - 1;  // exactly one lane (counts are exact)
+      dsel = lane_value(dsel, L);
+      knew = lane_value(knew, L);
+      tau |= (uint32_t)dsel << shift;
+      pmask |= dmask << shift;
+      krem = knew;
+      __syncthreads();
+    }
+  }
+  int ngt = 0, neq = 0;
+  if (!keep_all && k > 0) {
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      const uint32_t key = bits[i] & 0x7fffffffu;
+      ngt += key > tau;
+      neq += key == tau;
+    }
+  }
+  const int gt_before = wave_incl_scan(ngt) - ngt;
+  const int eq_before = wave_incl_scan(neq) - neq;
+  int pos = keep_all ? lane * V : gt_before + min(eq_before, krem);
+  int eq_seen = eq_before;
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+    const int j = lane * V + i;
+    const uint32_t key = bits[i] & 0x7fffffffu;
+    bool keep;
+    if (keep_all) keep = true;
+    else if (k == 0) keep = false;
+    else if (key > tau) keep = true;
+    else if (key == tau) keep = eq_seen++ < krem;
+    else keep = false;
+    const float v = w * __uint_as_float(bits[i]);
+    if (keep) {
+      if (pos < k) {  // always true for finite input; keeps NaN input memory-safe
+        if (idx) idx[(size_t)p * k + pos] = j;
+        if (hact) hact[(size_t)p * k + pos] = v;
+      }
+      ++pos;
+    }
+    if (hm) {
+      const float mv = keep ? v : 0.0f;
+      if (hm_bf16)
+        static_cast<uint16_t *>(hm)[(size_t)p * d_ff + j] = (uint16_t)f32_to_bf16_bits(mv);
+      else
+        static_cast<float *>(hm)[(size_t)p * d_ff + j] = mv;
+    }
+  }
+}
+
 // ---------------------------------------------------------------- sparse down
-// Block = (pair, row chunk) x a slice of 64 * VEC output columns.  Each wave
-// streams whole row slices (bf16: 1 KB, one 16-byte load per lane; fp32:
-// 1 KB) of the kept rows i = chunk start + wave, +4, ..., 4 rows in flight,
-// multiplying by the row's coefficient.  With idx == nullptr the rows are
-// 0..k-1 (dense rows, coefficient row stride k).  The four wave partials
-// are added in fixed order into partial[pair * n_chunks + chunk].
+// y[t, cols] (+)= sum over the token's pairs (slot order) and their kept rows
+// (ascending) of coef * W_d^e[row, cols]: the down projection streams only
+// the kept rows, and the weighted scatter-add of the token's experts happens
+// in the same block, in a fixed order (no atomics, bitwise reproducible).
+// Block = 16 waves, one token x 64 output columns; each kept row contributes
+// one 128-byte (bf16) or 256-byte (fp32) run, 8 or 4 rows per wave load
+// instruction.  The token's row list (expert, row, coefficient) is staged in
+// LDS first so the weight loads issue back to back.  With idx == nullptr the
+// rows are 0..k-1 (the dense fp32 path, coefficient row stride k).
+constexpr int kDownWaves = 16;
+constexpr int kDownSW = 64;          // output columns per block
+constexpr int kDownStage = 4096;     // row-list entries staged in LDS
+
 template <bool BF16>
-__global__ __launch_bounds__(256) void down_rows_kernel(const void *__restrict__ wdv,
-                                                        const int32_t *__restrict__ idx,
-                                                        const float *__restrict__ coef,
-                                                        RouteView rv, int H, int d_ff, int k,
-                                                        int n_chunks, int R,
-                                                        float *__restrict__ partial) {
-  constexpr int VEC = BF16 ? 8 : 4;
-  constexpr int SW = 64 * VEC;
-  __shared__ float red[4][SW];
+__global__ __launch_bounds__(1024) void down_token_kernel(const void *__restrict__ wdv,
+                                                          const int32_t *__restrict__ idx,
+                                                          const float *__restrict__ coef,
+                                                          RouteView rv, int H, int d_ff, int k,
+                                                          int accumulate, float *__restrict__ y) {
+  constexpr int VEC = BF16 ? 8 : 4;   // elements per 16-byte load
+  constexpr int LPR = kDownSW / VEC;  // lanes per row
+  constexpr int RPI = 64 / LPR;       // rows per wave instruction
+  __shared__ float red[kDownWaves][kDownSW];
+  __shared__ uint32_t srow[kDownStage];  // expert * d_ff + row
+  __shared__ float scoef[kDownStage];
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int pc = blockIdx.x;
-  const int p = pc / n_chunks, c = pc - p * n_chunks;
-  const int e = rv.expert_of_pair(p);
-  const int i0 = c * R, i1 = min(k, i0 + R);
-  const int col = blockIdx.y * SW + lane * VEC;
-  const bool cv = col < H;
-  const int32_t *ip = idx ? idx + (size_t)p * k : nullptr;
-  const float *cp = coef + (size_t)p * k;
-  const size_t ebase = (size_t)e * d_ff * H;
+  const int t = blockIdx.x, col0 = blockIdx.y * kDownSW;
+  const int top_k = rv.top_k;
+  const int nrows = top_k * k;
+  const bool staged = nrows <= kDownStage;
+  if (staged) {
+    for (int q = threadIdx.x; q < nrows; q += 1024) {
+      const int s = q / k, i = q - s * k;
+      const int p = t * top_k + s;
+      int j = idx ? idx[(size_t)p * k + i] : i;
+      j = (unsigned)j < (unsigned)d_ff ? j : 0;
+      srow[q] = (uint32_t)rv.expert_of_pair(p) * (uint32_t)d_ff + (uint32_t)j;
+      scoef[q] = coef[(size_t)p * k + i];
+    }
+    __syncthreads();
+  }
+  const int sub = lane % LPR, rsel = lane / LPR;
+  const size_t colo = (size_t)col0 + sub * VEC;
   float acc[VEC];
 #pragma unroll
   for (int v = 0; v < VEC; ++v) acc[v] = 0.f;
-
-  constexpr int U = 4;
-  for (int i = i0 + wid; i < i1; i += 4 * U) {
+  constexpr int U = 4;  // row groups in flight per wave
+  for (int b0 = wid; b0 * RPI < nrows; b0 += kDownWaves * U) {
     u32x4 q[U];
-    float hv[U];
+    float c[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int ii = i + 4 * u;
-      hv[u] = 0.f;
+      const int qq = (b0 + kDownWaves * u) * RPI + rsel;
+      c[u] = 0.f;
       q[u] = u32x4{0, 0, 0, 0};
-      if (ii < i1) {
-        int j = ip ? ip[ii] : ii;
-        j = (unsigned)j < (unsigned)d_ff ? j : 0;  // memory-safe on any index input
-        hv[u] = cp[ii];
-        if (cv) {
-          const size_t off = ebase + (size_t)j * H + col;
-          q[u] = BF16 ? ld16(static_cast<const uint16_t *>(wdv) + off)
-                      : ld16(static_cast<const float *>(wdv) + off);
+      if (qq < nrows) {
+        uint32_t rowid;
+        if (staged) {
+          rowid = srow[qq];
+          c[u] = scoef[qq];
+        } else {
+          const int s = qq / k, i = qq - s * k;
+          const int p = t * top_k + s;
+          int j = idx ? idx[(size_t)p * k + i] : i;
+          j = (unsigned)j < (unsigned)d_ff ? j : 0;
+          rowid = (uint32_t)rv.expert_of_pair(p) * (uint32_t)d_ff + (uint32_t)j;
+          c[u] = coef[(size_t)p * k + i];
         }
+        const size_t off = (size_t)rowid * H + colo;
+        q[u] = BF16 ? ld16_nt(static_cast<const uint16_t *>(wdv) + off)
+                    : ld16_nt(static_cast<const float *>(wdv) + off);
       }
     }
 #pragma unroll
@@ -348,22 +482,32 @@ __global__ __launch_bounds__(256) void down_rows_kernel(const void *__restrict__
       if (BF16) {
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
-          acc[2 * jj] = fmaf(hv[u], bf16lo(q[u][jj]), acc[2 * jj]);
-          acc[2 * jj + 1] = fmaf(hv[u], bf16hi(q[u][jj]), acc[2 * jj + 1]);
+          acc[2 * jj] = fmaf(c[u], bf16lo(q[u][jj]), acc[2 * jj]);
+          acc[2 * jj + 1] = fmaf(c[u], bf16hi(q[u][jj]), acc[2 * jj + 1]);
         }
       } else {
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) acc[jj] = fmaf(hv[u], __uint_as_float(q[u][jj]), acc[jj]);
+        for (int jj = 0; jj < 4; ++jj) acc[jj] = fmaf(c[u], __uint_as_float(q[u][jj]), acc[jj]);
       }
     }
   }
+  // lanes with the same columns (same sub) hold different rows: fold them
 #pragma unroll
-  for (int v = 0; v < VEC; ++v) red[wid][lane * VEC + v] = acc[v];
+  for (int o = LPR; o < 64; o <<= 1) {
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) acc[v] += __shfl_xor(acc[v], o, 64);
+  }
+  if (rsel == 0) {
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) red[wid][sub * VEC + v] = acc[v];
+  }
   __syncthreads();
-  for (int o = threadIdx.x; o < SW; o += 256) {
-    const int cc = blockIdx.y * SW + o;
-    if (cc < H)
-      partial[(size_t)pc * H + cc] = red[0][o] + red[1][o] + red[2][o] + red[3][o];
+  if (threadIdx.x < kDownSW) {
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < kDownWaves; ++w) v += red[w][threadIdx.x];
+    float *yp = y + (size_t)t * H + col0 + threadIdx.x;
+    *yp = accumulate ? *yp + v : v;
   }
 }
 
@@ -459,17 +603,25 @@ __global__ __launch_bounds__(256) void down_dense_bf16_kernel(const uint16_t *__
 // ---------------------------------------------------------------- combine
 // y[t, :] = (accumulate ? y[t, :] : 0) + sum over slots, then chunks, of
 // the token's partial rows: a fixed order, so reruns are bitwise equal.
-__global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ partial, int H,
+__global__ __launch_bounds__(64) void combine_kernel(const float *__restrict__ partial, int H,
                                                       int top_k, int n_chunks, int accumulate,
                                                       float *__restrict__ y) {
   const int t = blockIdx.x;
-  const int col = (blockIdx.y * 256 + threadIdx.x) * 4;
+  const int col = (blockIdx.y * 64 + threadIdx.x) * 4;
   if (col >= H) return;
   f32x4 s = accumulate ? *reinterpret_cast<const f32x4 *>(y + (size_t)t * H + col)
                        : f32x4{0, 0, 0, 0};
-  const size_t rows = (size_t)top_k * n_chunks;
+  const int rows = top_k * n_chunks;
   const float *pp = partial + (size_t)t * rows * H + col;
-  for (size_t i = 0; i < rows; ++i) s += *reinterpret_cast<const f32x4 *>(pp + i * H);
+  int i = 0;
+  for (; i + 8 <= rows; i += 8) {  // 8 loads in flight, added in row order
+    f32x4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const f32x4 *>(pp + (size_t)(i + u) * H);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s += v[u];
+  }
+  for (; i < rows; ++i) s += *reinterpret_cast<const f32x4 *>(pp + (size_t)i * H);
   *reinterpret_cast<f32x4 *>(y + (size_t)t * H + col) = s;
 }
 
@@ -503,60 +655,48 @@ static int n_items(const FfnArgs &a, int TG) {
   return (a.E < P ? a.E : P) + P / TG;
 }
 
-static constexpr int kDownTargetBlocks = 2048;
-static constexpr int kDownMinRows = 8;
-
-static int slice_width(int bf16) { return bf16 ? 512 : 256; }
-
-DownPlan plan_down(int P, int k, int H, int bf16) {
-  DownPlan d{1, k > 0 ? k : 1};
-  if (P <= 0 || k <= 0) return d;
-  const int slices = (H + slice_width(bf16) - 1) / slice_width(bf16);
-  long long want = (kDownTargetBlocks + (long long)P * slices - 1) / ((long long)P * slices);
-  int maxc = k / kDownMinRows;
-  if (maxc < 1) maxc = 1;
-  int nc = (int)(want < maxc ? want : maxc);
-  if (nc < 1) nc = 1;
-  const int R = (k + nc - 1) / nc;
-  d.rows_per_chunk = R;
-  d.n_chunks = (k + R - 1) / R;
-  return d;
-}
-
-size_t max_partial_rows(int P, int k, int H, int bf16) {
-  const int slices = (H + slice_width(bf16) - 1) / slice_width(bf16);
-  return (size_t)P + (size_t)(kDownTargetBlocks + slices - 1) / slices + 1;
-}
-
 static void launch_mask(const FfnArgs &a, const RouteView &rv, int32_t *idx, float *hact, void *hm,
                         int hm_bf16, hipStream_t stream) {
   const int P = a.T * a.top_k;
   timer_begin(kStageMask, stream);
-  neuron_topk_kernel<<<P, 256, (size_t)a.d_ff * 4, stream>>>(a.h, rv, a.d_ff, a.k_keep, idx, hact,
-                                                              hm, hm_bf16);
+  switch (a.d_ff) {  // one wave per pair where d_ff / 64 values fit in registers
+#define MOE_MASK_CASE(V)                                                                    \
+  case 64 * V:                                                                              \
+    neuron_topk_wave_kernel<V><<<P, 64, 0, stream>>>(a.h, rv, P, a.d_ff, a.k_keep, idx, hact, \
+                                                     hm, hm_bf16);                          \
+    break;
+    MOE_MASK_CASE(1) MOE_MASK_CASE(2) MOE_MASK_CASE(3) MOE_MASK_CASE(4) MOE_MASK_CASE(5)
+    MOE_MASK_CASE(6) MOE_MASK_CASE(8) MOE_MASK_CASE(10) MOE_MASK_CASE(12) MOE_MASK_CASE(16)
+    MOE_MASK_CASE(20) MOE_MASK_CASE(24) MOE_MASK_CASE(32)
+#undef MOE_MASK_CASE
+    default:
+      neuron_topk_kernel<<<P, 256, (size_t)a.d_ff * 4, stream>>>(a.h, rv, a.d_ff, a.k_keep, idx,
+                                                                  hact, hm, hm_bf16);
+  }
   timer_end(stream);
 }
 
 // A routed expert never holds more than T tokens, so at T <= 16 one token
-// tile per item suffices (and keeps the kernel at high occupancy).
+// tile per item suffices; that variant splits K over 8 waves (short blocks,
+// high occupancy, no tail of half-empty block rounds).
 static void launch_gateup(const FfnArgs &a, const RouteView &rv, hipStream_t stream) {
   const bool one = a.T <= 16;
   dim3 grid(n_items(a, one ? 16 : 64), a.d_ff / 16);
   timer_begin(kStageGateup, stream);
   if (a.bf16) {
-    if (one) gateup_swiglu_kernel<true, 1><<<grid, 256, 0, stream>>>(a.x, a.w_gate, a.w_up, rv, a.H, a.d_ff, a.h);
-    else gateup_swiglu_kernel<true, 4><<<grid, 256, 0, stream>>>(a.x, a.w_gate, a.w_up, rv, a.H, a.d_ff, a.h);
+    if (one) gateup_swiglu_kernel<true, 1, 8><<<grid, 512, 0, stream>>>(a.x, a.w_gate, a.w_up, rv, a.H, a.d_ff, a.h);
+    else gateup_swiglu_kernel<true, 4, 4><<<grid, 256, 0, stream>>>(a.x, a.w_gate, a.w_up, rv, a.H, a.d_ff, a.h);
   } else {
-    if (one) gateup_swiglu_kernel<false, 1><<<grid, 256, 0, stream>>>(a.x, a.w_gate, a.w_up, rv, a.H, a.d_ff, a.h);
-    else gateup_swiglu_kernel<false, 4><<<grid, 256, 0, stream>>>(a.x, a.w_gate, a.w_up, rv, a.H, a.d_ff, a.h);
+    if (one) gateup_swiglu_kernel<false, 1, 8><<<grid, 512, 0, stream>>>(a.x, a.w_gate, a.w_up, rv, a.H, a.d_ff, a.h);
+    else gateup_swiglu_kernel<false, 4, 4><<<grid, 256, 0, stream>>>(a.x, a.w_gate, a.w_up, rv, a.H, a.d_ff, a.h);
   }
   timer_end(stream);
 }
 
 static void launch_combine(const FfnArgs &a, int n_chunks, hipStream_t stream) {
-  dim3 grid(a.T, (a.H + 1023) / 1024);
+  dim3 grid(a.T, (a.H + 255) / 256);
   timer_begin(kStageCombine, stream);
-  combine_kernel<<<grid, 256, 0, stream>>>(a.partial, a.H, a.top_k, n_chunks, a.accumulate, a.y);
+  combine_kernel<<<grid, 64, 0, stream>>>(a.partial, a.H, a.top_k, n_chunks, a.accumulate, a.y);
   timer_end(stream);
 }
 
@@ -571,17 +711,16 @@ static bool zero_contribution(const FfnArgs &a, hipStream_t stream) {
   return true;
 }
 
-static void launch_down_rows(const FfnArgs &a, const RouteView &rv, const int32_t *idx,
-                             const float *coef, int k, const DownPlan &dp, hipStream_t stream) {
-  const int P = a.T * a.top_k;
-  dim3 grid(P * dp.n_chunks, (a.H + slice_width(a.bf16) - 1) / slice_width(a.bf16));
+static void launch_down_token(const FfnArgs &a, const RouteView &rv, const int32_t *idx,
+                              const float *coef, int k, hipStream_t stream) {
+  dim3 grid(a.T, a.H / kDownSW);
   timer_begin(kStageDownRows, stream);
   if (a.bf16)
-    down_rows_kernel<true><<<grid, 256, 0, stream>>>(a.w_down, idx, coef, rv, a.H, a.d_ff, k,
-                                                     dp.n_chunks, dp.rows_per_chunk, a.partial);
+    down_token_kernel<true><<<grid, 1024, 0, stream>>>(a.w_down, idx, coef, rv, a.H, a.d_ff, k,
+                                                       a.accumulate, a.y);
   else
-    down_rows_kernel<false><<<grid, 256, 0, stream>>>(a.w_down, idx, coef, rv, a.H, a.d_ff, k,
-                                                      dp.n_chunks, dp.rows_per_chunk, a.partial);
+    down_token_kernel<false><<<grid, 1024, 0, stream>>>(a.w_down, idx, coef, rv, a.H, a.d_ff, k,
+                                                        a.accumulate, a.y);
   timer_end(stream);
 }
 
@@ -589,12 +728,9 @@ hipError_t launch_ffn_sparse(const FfnArgs &a, hipStream_t stream) {
   if (a.T == 0) return hipSuccess;
   if (zero_contribution(a, stream)) return hipGetLastError();
   const RouteView rv = make_view(a);
-  const int P = a.T * a.top_k;
   launch_gateup(a, rv, stream);
   launch_mask(a, rv, a.idx, a.hact, nullptr, 0, stream);
-  const DownPlan dp = plan_down(P, a.k_keep, a.H, a.bf16);
-  launch_down_rows(a, rv, a.idx, a.hact, a.k_keep, dp, stream);
-  launch_combine(a, dp.n_chunks, stream);
+  launch_down_token(a, rv, a.idx, a.hact, a.k_keep, stream);
   return hipGetLastError();
 }
 
@@ -602,7 +738,6 @@ hipError_t launch_ffn_dense(const FfnArgs &a, hipStream_t stream) {
   if (a.T == 0) return hipSuccess;
   if (zero_contribution(a, stream)) return hipGetLastError();
   const RouteView rv = make_view(a);
-  const int P = a.T * a.top_k;
   launch_gateup(a, rv, stream);
   launch_mask(a, rv, a.idx, nullptr, a.hm, a.bf16, stream);
   if (a.bf16) {
@@ -615,9 +750,7 @@ hipError_t launch_ffn_dense(const FfnArgs &a, hipStream_t stream) {
     launch_combine(a, 1, stream);
   } else {
     // fp32: every row of W_d against the dense masked row, on the row kernel
-    const DownPlan dp = plan_down(P, a.d_ff, a.H, 0);
-    launch_down_rows(a, rv, nullptr, static_cast<const float *>(a.hm), a.d_ff, dp, stream);
-    launch_combine(a, dp.n_chunks, stream);
+    launch_down_token(a, rv, nullptr, static_cast<const float *>(a.hm), a.d_ff, stream);
   }
   return hipGetLastError();
 }

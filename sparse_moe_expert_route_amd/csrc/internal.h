@@ -39,12 +39,15 @@ struct RouteArgs {
   int T, H, E, top_k, norm_topk, bf16;
   const void *x, *w_router;
   const float *bias;
-  float *logits;  // workspace [T, E]
+  float *logits;  // workspace [kRouterSplits, T, E] partial logits
   int32_t *topk_ids;
   float *topk_w;
   int32_t *offsets, *pair_by_expert, *active, *n_active;
 };
 
+// Router split-K: logits are written as kRouterSplits-at-most partials.
+constexpr int kRouterSplits = 8;
+int router_splits(int T, int H, int E, int bf16);
 hipError_t launch_route(const RouteArgs &a, hipStream_t stream);
 
 // One FFN call (routed group, or an implicit shared group).
@@ -60,19 +63,12 @@ struct FfnArgs {
   float *h;          // [P, d_ff] fp32
   int32_t *idx;      // [P, k_keep]
   float *hact;       // [P, k_keep]   w * h at the kept neurons
-  float *partial;    // [P * n_chunks, H]
+  float *partial;    // dense bf16 path: [P, H] per-pair down outputs
   void *hm;          // dense path: [P, d_ff] masked, weighted h (bf16 or fp32)
-  int n_chunks;      // down-projection row chunks per pair
 };
 
-// Down-projection work split: rows of each pair are cut into n_chunks chunks.
-struct DownPlan {
-  int n_chunks;
-  int rows_per_chunk;
-};
-DownPlan plan_down(int P, int k_keep, int H, int bf16);
-// Upper bound of P * n_chunks over every P' <= P (sizes the partial buffer).
-size_t max_partial_rows(int P, int k_keep, int H, int bf16);
+hipError_t launch_pack_gate_up(const void *src, void *dst, int E, int d_ff, int H, int bf16,
+                               int unpack, hipStream_t stream);
 
 hipError_t launch_ffn_sparse(const FfnArgs &a, hipStream_t stream);
 hipError_t launch_ffn_dense(const FfnArgs &a, hipStream_t stream);

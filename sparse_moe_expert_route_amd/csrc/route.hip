@@ -10,105 +10,130 @@
 namespace moe {
 
 // ---------------------------------------------------------------- logits
-// l[t, e] = sum_h x[t, h] * w[e, h] + bias[e].  One wave per expert row,
-// TT tokens per block; each lane owns 8-element chunks of H strided by 512
-// and accumulates in fp32, then a butterfly sum.  The router matrix row is
-// read once per block; the token rows come from L2.
-constexpr int kLogitTokens = 8;
-
-template <bool BF16>
+// l[t, e] = sum_h x[t, h] * w[e, h] (+ bias[e], added by the selection) as a
+// small GEMM on MFMA.  Block = 16 experts x up to 16 * MT tokens x one of
+// gridDim.z contiguous K ranges (split-K, so that even one token spreads the
+// router matrix over many CUs); the 4 waves split the block's K range in
+// interleaved steps and meet in LDS.  Each split writes its own partial
+// [split][t][e]; the selection adds the splits in order.
+template <bool BF16, int MT>
 __global__ __launch_bounds__(256) void router_logits_kernel(const void *__restrict__ xv,
-                                                            const void *__restrict__ wv,
-                                                            const float *__restrict__ bias,
-                                                            int T, int H, int E,
-                                                            float *__restrict__ logits) {
+                                                            const void *__restrict__ wv, int T,
+                                                            int H, int E,
+                                                            float *__restrict__ partial) {
+  __shared__ float red[4][MT][4][64];
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int e = blockIdx.x * 4 + wid;
-  const int t0 = blockIdx.y * kLogitTokens;
-  if (e >= E) return;  // wave-uniform, no barrier below
-  const int nt = min(kLogitTokens, T - t0);
-  float acc[kLogitTokens];
+  const int r = lane & 15, g = lane >> 4;
+  const int e0 = blockIdx.x * 16, t0 = blockIdx.y * 16 * MT;
+  const int ntok = min(16 * MT, T - t0);
+  const int ntiles = (ntok + 15) >> 4;
+  const bool rv = e0 + r < E;
+  f32x4 acc[MT];
+  bool xval[MT];
+  size_t xoff[MT];
 #pragma unroll
-  for (int i = 0; i < kLogitTokens; ++i) acc[i] = 0.f;
-
-  for (int c = lane * 8; c < H; c += 512) {
-    float w[8];
-    if (BF16) {
-      const uint16_t *wr = static_cast<const uint16_t *>(wv) + (size_t)e * H;
-      u32x4 q = ld16(wr + c);
+  for (int tl = 0; tl < MT; ++tl) {
+    acc[tl] = f32x4{0, 0, 0, 0};
+    xval[tl] = tl * 16 + r < ntok;
+    xoff[tl] = xval[tl] ? (size_t)(t0 + tl * 16 + r) * H : 0;
+  }
+  constexpr int U = 8;
+  const int KS = BF16 ? 32 : 16;  // K elements per step
+  const int nall = H / KS;
+  const int per = (nall + gridDim.z - 1) / gridDim.z;  // k-steps of this split
+  const int kbeg = blockIdx.z * per;
+  const int nsteps = min(nall, kbeg + per);
+  const size_t wrow = (size_t)(rv ? e0 + r : 0) * H;
+  for (int s = kbeg + wid; s < nsteps; s += 4 * U) {
+    u32x4 a[U];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) { w[2 * j] = bf16lo(q[j]); w[2 * j + 1] = bf16hi(q[j]); }
-    } else {
-      const float *wr = static_cast<const float *>(wv) + (size_t)e * H;
-      u32x4 q0 = ld16(wr + c), q1 = ld16(wr + c + 4);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) { w[j] = __uint_as_float(q0[j]); w[4 + j] = __uint_as_float(q1[j]); }
+    for (int u = 0; u < U; ++u) {
+      const int ks = s + 4 * u;
+      const int k = ks * KS + g * (KS / 4);
+      a[u] = (ks < nsteps && rv)
+                 ? (BF16 ? ld16(static_cast<const uint16_t *>(wv) + wrow + k)
+                         : ld16(static_cast<const float *>(wv) + wrow + k))
+                 : u32x4{0, 0, 0, 0};
     }
 #pragma unroll
-    for (int i = 0; i < kLogitTokens; ++i) {
-      if (i < nt) {
-        float xs[8];
-        if (BF16) {
-          u32x4 q = ld16(static_cast<const uint16_t *>(xv) + (size_t)(t0 + i) * H + c);
+    for (int u = 0; u < U; ++u) {
+      const int ks = s + 4 * u;
+      if (ks < nsteps) {
+        const int k = ks * KS + g * (KS / 4);
 #pragma unroll
-          for (int j = 0; j < 4; ++j) { xs[2 * j] = bf16lo(q[j]); xs[2 * j + 1] = bf16hi(q[j]); }
-        } else {
-          const float *xr = static_cast<const float *>(xv) + (size_t)(t0 + i) * H + c;
-          u32x4 q0 = ld16(xr), q1 = ld16(xr + 4);
+        for (int tl = 0; tl < MT; ++tl) {
+          if (tl < ntiles) {
+            const u32x4 b = xval[tl] ? (BF16 ? ld16(static_cast<const uint16_t *>(xv) + xoff[tl] + k)
+                                             : ld16(static_cast<const float *>(xv) + xoff[tl] + k))
+                                     : u32x4{0, 0, 0, 0};
+            if (BF16) {
+              acc[tl] = mfma_bf16(a[u], b, acc[tl]);
+            } else {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) { xs[j] = __uint_as_float(q0[j]); xs[4 + j] = __uint_as_float(q1[j]); }
+              for (int j = 0; j < 4; ++j)
+                acc[tl] = mfma_f32(__uint_as_float(a[u][j]), __uint_as_float(b[j]), acc[tl]);
+            }
+          }
         }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i] = fmaf(xs[j], w[j], acc[i]);
       }
     }
   }
-  const float b = bias ? bias[e] : 0.f;
 #pragma unroll
-  for (int i = 0; i < kLogitTokens; ++i) {
-    float s = wave_sum(acc[i]);
-    if (lane == 0 && i < nt) logits[(size_t)(t0 + i) * E + e] = s + b;
+  for (int tl = 0; tl < MT; ++tl)
+    if (tl < ntiles) {
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) red[wid][tl][rr][lane] = acc[tl][rr];
+    }
+  __syncthreads();
+  for (int o = threadIdx.x; o < ntiles * 256; o += 256) {
+    const int tl = o >> 8, rr = (o >> 6) & 3, ln = o & 63;
+    const int c = tl * 16 + (ln & 15);           // token within the block
+    const int e = e0 + 4 * (ln >> 4) + rr;       // expert row of the tile
+    if (c < ntok && e < E) {
+      const float v = red[0][tl][rr][ln] + red[1][tl][rr][ln] + red[2][tl][rr][ln] + red[3][tl][rr][ln];
+      partial[((size_t)blockIdx.z * T + t0 + c) * E + e] = v;
+    }
   }
 }
 
 // ---------------------------------------------------------------- top-k
-// One wave per token.  Each lane holds V logits (expert lane + 64 i) as
-// 64-bit keys (order-preserving float bits, then the complement of the
-// expert id so that equal logits favour the lower id); top_k rounds of a
-// wavefront max-reduction pick the experts in descending-logit order.
-// Weights are the full softmax over all E experts at the picks, optionally
-// renormalised over the picks.
+// One wave selects one token's experts.  Each lane holds V logits (expert
+// lane + 64 i) as 64-bit keys (order-preserving float bits, then the
+// complement of the expert id so that equal logits favour the lower id);
+// top_k rounds of a wavefront max-reduction pick the experts in
+// descending-logit order.  Weights are the full softmax over all E experts
+// at the picks, optionally renormalised over the picks.  Lane r < top_k
+// returns slot r's (expert, weight).
 template <int V>
-__global__ __launch_bounds__(256) void router_topk_kernel(const float *__restrict__ logits, int T,
-                                                          int E, int top_k, int norm_topk,
-                                                          int32_t *__restrict__ ids,
-                                                          float *__restrict__ wout) {
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int t = blockIdx.x * 4 + wid;
-  if (t >= T) return;
-  const float *l = logits + (size_t)t * E;
+__device__ __forceinline__ void wave_topk(const float *__restrict__ part, size_t split_stride,
+                                          int nsplit, const float *__restrict__ bias, int E,
+                                          int top_k, int norm_topk, int &esel, float &wsel) {
+  const int lane = threadIdx.x & 63;
   float v[V];
   uint64_t key[V];
 #pragma unroll
   for (int i = 0; i < V; ++i) {
     const int e = lane + 64 * i;
-    v[i] = e < E ? l[e] : 0.f;
-    key[i] = e < E ? ((uint64_t)ordered_key(v[i]) << 32) | (uint32_t)(0xffffffffu - e) : 0ull;
+    float l = 0.f;
+    if (e < E) {
+      for (int c = 0; c < nsplit; ++c) l += part[c * split_stride + e];
+      if (bias) l += bias[e];
+    }
+    v[i] = l;
+    key[i] = e < E ? ((uint64_t)ordered_key(l) << 32) | (uint32_t)(0xffffffffu - e) : 0ull;
   }
-  // first pick = the maximum logit m
   uint64_t best = 0;
 #pragma unroll
   for (int i = 0; i < V; ++i) best = key[i] > best ? key[i] : best;
   best = wave_max_u64(best);
-  const float m = l[0xffffffffu - (uint32_t)best];
+  const float m = key_value(best);
   float z = 0.f;
 #pragma unroll
   for (int i = 0; i < V; ++i)
     if (lane + 64 * i < E) z += expf(v[i] - m);
   z = wave_sum(z);
-
-  float psel = 0.f;  // this lane's pick (lane r holds round r)
-  int esel = 0;
+  float psel = 0.f;
+  esel = 0;
   for (int r = 0; r < top_k; ++r) {
     uint64_t b = 0;
 #pragma unroll
@@ -118,31 +143,45 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float *__restric
 #pragma unroll
     for (int i = 0; i < V; ++i)
       if (lane + 64 * i == e) key[i] = 0ull;
-    if (lane == r) { esel = e; psel = expf(l[e] - m); }
+    if (lane == r) { esel = e; psel = expf(key_value(b) - m); }
   }
   float denom = z;
   if (norm_topk) denom = wave_sum(lane < top_k ? psel : 0.f);
+  wsel = psel / denom;
+}
+
+template <int V>
+__global__ __launch_bounds__(256) void router_topk_kernel(const float *__restrict__ part,
+                                                          int nsplit, const float *__restrict__ bias,
+                                                          int T, int E, int top_k, int norm_topk,
+                                                          int32_t *__restrict__ ids,
+                                                          float *__restrict__ wout) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int t = blockIdx.x * 4 + wid;
+  if (t >= T) return;
+  int e;
+  float w;
+  wave_topk<V>(part + (size_t)t * E, (size_t)T * E, nsplit, bias, E, top_k, norm_topk, e, w);
   if (lane < top_k) {
-    ids[(size_t)t * top_k + lane] = esel;
-    wout[(size_t)t * top_k + lane] = psel / denom;
+    ids[(size_t)t * top_k + lane] = e;
+    wout[(size_t)t * top_k + lane] = w;
   }
 }
 
 // ---------------------------------------------------------------- grouping
-// Single block, 1024 threads.  Counts pairs per expert, scans them into CSR
+// Block of 1024 threads.  Counts pairs per expert, scans them into CSR
 // offsets and the ascending active-expert list, then places pairs chunk by
 // chunk: inside a wave, lanes with the same expert are matched by ballots on
 // the expert id bits; across the 16 waves of a chunk, per-(wave, expert)
 // counts give each wave its base.  The result is a stable sort by (expert,
-// pair id), i.e. ascending token order within an expert.
-__global__ __launch_bounds__(1024) void route_group_kernel(const int32_t *__restrict__ ids, int P,
-                                                           int E, int32_t *__restrict__ offsets,
-                                                           int32_t *__restrict__ pair_by_expert,
-                                                           int32_t *__restrict__ active,
-                                                           int32_t *__restrict__ n_active) {
-  __shared__ int cursor[1024];
-  __shared__ uint8_t wcnt[16][1024];
-  __shared__ int tmp[16];
+// pair id), i.e. ascending token order within an expert.  `ids` may live in
+// LDS or global memory.
+__device__ __forceinline__ void block_group(const int32_t *ids, int P, int E,
+                                            int32_t *__restrict__ offsets,
+                                            int32_t *__restrict__ pair_by_expert,
+                                            int32_t *__restrict__ active,
+                                            int32_t *__restrict__ n_active, int *cursor,
+                                            uint8_t (*wcnt)[1024], int *tmp) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   cursor[tid] = 0;
   __syncthreads();
@@ -197,30 +236,99 @@ __global__ __launch_bounds__(1024) void route_group_kernel(const int32_t *__rest
   }
 }
 
-hipError_t launch_route(const RouteArgs &a, hipStream_t stream) {
-  if (a.T == 0) return hipSuccess;
-  dim3 g1((a.E + 3) / 4, (a.T + kLogitTokens - 1) / kLogitTokens);
-  timer_begin(kStageLogits, stream);
-  if (a.bf16)
-    router_logits_kernel<true><<<g1, 256, 0, stream>>>(a.x, a.w_router, a.bias, a.T, a.H, a.E, a.logits);
-  else
-    router_logits_kernel<false><<<g1, 256, 0, stream>>>(a.x, a.w_router, a.bias, a.T, a.H, a.E, a.logits);
-  timer_end(stream);
-  dim3 g2((a.T + 3) / 4);
+__global__ __launch_bounds__(1024) void route_group_kernel(const int32_t *__restrict__ ids, int P,
+                                                           int E, int32_t *__restrict__ offsets,
+                                                           int32_t *__restrict__ pair_by_expert,
+                                                           int32_t *__restrict__ active,
+                                                           int32_t *__restrict__ n_active) {
+  __shared__ int cursor[1024];
+  __shared__ uint8_t wcnt[16][1024];
+  __shared__ int tmp[16];
+  block_group(ids, P, E, offsets, pair_by_expert, active, n_active, cursor, wcnt, tmp);
+}
+
+// Small batches: one block selects every token's experts (16 waves, one
+// token each per round) into LDS and global memory, then groups the pairs.
+constexpr int kFusedMaxPairs = 2048;
+template <int V>
+__global__ __launch_bounds__(1024) void route_select_group_kernel(
+    const float *__restrict__ part, int nsplit, const float *__restrict__ bias, int T, int E,
+    int top_k, int norm_topk,
+    int32_t *__restrict__ ids, float *__restrict__ wout, int32_t *__restrict__ offsets,
+    int32_t *__restrict__ pair_by_expert, int32_t *__restrict__ active,
+    int32_t *__restrict__ n_active) {
+  __shared__ int sids[kFusedMaxPairs];
+  __shared__ int cursor[1024];
+  __shared__ uint8_t wcnt[16][1024];
+  __shared__ int tmp[16];
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  for (int t = wid; t < T; t += 16) {
+    int e;
+    float w;
+    wave_topk<V>(part + (size_t)t * E, (size_t)T * E, nsplit, bias, E, top_k, norm_topk, e, w);
+    if (lane < top_k) {
+      sids[t * top_k + lane] = e;
+      ids[(size_t)t * top_k + lane] = e;
+      wout[(size_t)t * top_k + lane] = w;
+    }
+  }
+  __syncthreads();
+  block_group(sids, T * top_k, E, offsets, pair_by_expert, active, n_active, cursor, wcnt, tmp);
+}
+
+template <int V>
+static void launch_select(const RouteArgs &a, int nsplit, hipStream_t stream) {
+  const int P = a.T * a.top_k;
+  if (P <= kFusedMaxPairs) {
+    timer_begin(kStageTopk, stream);
+    route_select_group_kernel<V><<<1, 1024, 0, stream>>>(a.logits, nsplit, a.bias, a.T, a.E,
+                                                         a.top_k, a.norm_topk, a.topk_ids,
+                                                         a.topk_w, a.offsets, a.pair_by_expert,
+                                                         a.active, a.n_active);
+    timer_end(stream);
+    return;
+  }
   timer_begin(kStageTopk, stream);
-  if (a.E <= 64)
-    router_topk_kernel<1><<<g2, 256, 0, stream>>>(a.logits, a.T, a.E, a.top_k, a.norm_topk, a.topk_ids, a.topk_w);
-  else if (a.E <= 128)
-    router_topk_kernel<2><<<g2, 256, 0, stream>>>(a.logits, a.T, a.E, a.top_k, a.norm_topk, a.topk_ids, a.topk_w);
-  else if (a.E <= 256)
-    router_topk_kernel<4><<<g2, 256, 0, stream>>>(a.logits, a.T, a.E, a.top_k, a.norm_topk, a.topk_ids, a.topk_w);
-  else
-    router_topk_kernel<16><<<g2, 256, 0, stream>>>(a.logits, a.T, a.E, a.top_k, a.norm_topk, a.topk_ids, a.topk_w);
+  router_topk_kernel<V><<<(a.T + 3) / 4, 256, 0, stream>>>(a.logits, nsplit, a.bias, a.T, a.E,
+                                                           a.top_k, a.norm_topk, a.topk_ids,
+                                                           a.topk_w);
   timer_end(stream);
   timer_begin(kStageGroup, stream);
-  route_group_kernel<<<1, 1024, 0, stream>>>(a.topk_ids, a.T * a.top_k, a.E, a.offsets,
-                                             a.pair_by_expert, a.active, a.n_active);
+  route_group_kernel<<<1, 1024, 0, stream>>>(a.topk_ids, P, a.E, a.offsets, a.pair_by_expert,
+                                             a.active, a.n_active);
   timer_end(stream);
+}
+
+// Split-K factor of the router GEMM: enough blocks to spread the router
+// matrix over many CUs, at least 4 k-steps per split, at most kRouterSplits.
+int router_splits(int T, int H, int E, int bf16) {
+  const int tg = T <= 16 ? 16 : 64;
+  const int blocks = ((E + 15) / 16) * ((T + tg - 1) / tg);
+  const int nsteps = H / (bf16 ? 32 : 16);
+  int sp = (64 + blocks - 1) / blocks;
+  sp = sp < nsteps / 4 ? sp : nsteps / 4;
+  sp = sp < kRouterSplits ? sp : kRouterSplits;
+  return sp < 1 ? 1 : sp;
+}
+
+hipError_t launch_route(const RouteArgs &a, hipStream_t stream) {
+  if (a.T == 0) return hipSuccess;
+  const bool one = a.T <= 16;
+  const int nsplit = router_splits(a.T, a.H, a.E, a.bf16);
+  dim3 g1((a.E + 15) / 16, (a.T + (one ? 16 : 64) - 1) / (one ? 16 : 64), nsplit);
+  timer_begin(kStageLogits, stream);
+  if (a.bf16) {
+    if (one) router_logits_kernel<true, 1><<<g1, 256, 0, stream>>>(a.x, a.w_router, a.T, a.H, a.E, a.logits);
+    else router_logits_kernel<true, 4><<<g1, 256, 0, stream>>>(a.x, a.w_router, a.T, a.H, a.E, a.logits);
+  } else {
+    if (one) router_logits_kernel<false, 1><<<g1, 256, 0, stream>>>(a.x, a.w_router, a.T, a.H, a.E, a.logits);
+    else router_logits_kernel<false, 4><<<g1, 256, 0, stream>>>(a.x, a.w_router, a.T, a.H, a.E, a.logits);
+  }
+  timer_end(stream);
+  if (a.E <= 64) launch_select<1>(a, nsplit, stream);
+  else if (a.E <= 128) launch_select<2>(a, nsplit, stream);
+  else if (a.E <= 256) launch_select<4>(a, nsplit, stream);
+  else launch_select<16>(a, nsplit, stream);
   return hipGetLastError();
 }
 

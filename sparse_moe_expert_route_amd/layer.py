@@ -16,16 +16,22 @@ from . import binding as B
 class MoELayer:
     def __init__(self, *, hidden: int, n_experts: int, d_ff: int, top_k: int, norm_topk: bool,
                  dtype: str, w_router, w_gate, w_up, w_down, bias=None,
-                 shared: Optional[Sequence] = None, d_ff_shared: Optional[int] = None):
+                 shared: Optional[Sequence] = None, d_ff_shared: Optional[int] = None,
+                 packed: bool = False):
+        """Weights are device tensors [E, d_ff, H] (router [E, H]).  Gate and
+        up are packed here with moe_pack_gate_up unless `packed` says the
+        caller already did."""
         self.desc = B.make_desc(hidden, n_experts, d_ff, top_k, norm_topk, dtype)
         self.w_router, self.bias = w_router, bias
-        self.w = (w_gate, w_up, w_down)
-        self.shared = tuple(shared) if shared is not None else None
+        pk = (lambda d, w: w) if packed else B.moe_pack_gate_up
+        self.w = (pk(self.desc, w_gate), pk(self.desc, w_up), w_down)
+        self.shared = None
         self.desc_shared = None
-        if self.shared is not None:
-            n_sh = self.shared[0].shape[0]
-            self.desc_shared = B.make_desc(hidden, n_sh, d_ff_shared or self.shared[0].shape[1],
-                                           n_sh, False, dtype)
+        if shared is not None:
+            g, u, dn = shared
+            n_sh = g.shape[0]
+            self.desc_shared = B.make_desc(hidden, n_sh, d_ff_shared or g.shape[1], n_sh, False, dtype)
+            self.shared = (pk(self.desc_shared, g), pk(self.desc_shared, u), dn)
         self._ws = {}
 
     def _workspace(self, key, nbytes: int, device):

@@ -59,12 +59,17 @@ class DeviceLayer:
         self.desc = B.make_desc(sh.hidden, sh.n_experts, sh.d_ff, sh.top_k, sh.norm_topk, sh.dtype)
         self.w_router = to_dev(inp.w_router)
         self.bias = to_dev(inp.bias) if inp.bias is not None else None
-        self.w = tuple(to_dev(a) for a in (inp.wg, inp.wu, inp.wd))
+        # gate/up go to the FFN calls packed (moe_pack_gate_up); down stays row-major
+        self.w = (B.moe_pack_gate_up(self.desc, to_dev(inp.wg)),
+                  B.moe_pack_gate_up(self.desc, to_dev(inp.wu)), to_dev(inp.wd))
         self.desc_sh = None
         if inp.shared is not None:
             self.desc_sh = B.make_desc(sh.hidden, sh.n_shared, sh.d_ff_shared, sh.n_shared, False,
                                        sh.dtype)
-            self.w_sh = tuple(to_dev(a) for a in inp.shared)
+            g, u, d = inp.shared
+            self.w_sh = (B.moe_pack_gate_up(self.desc_sh, to_dev(g)),
+                         B.moe_pack_gate_up(self.desc_sh, to_dev(u)), to_dev(d))
+        torch.cuda.synchronize()
 
     def run(self, x_host: np.ndarray, k: int, path: int, k_sh=None, path_sh=None,
             poison_rows=None):
@@ -125,6 +130,18 @@ def check_selection(got, want, scores, k, what):
     bad = [i for i in diff if not amb[i]]
     assert not bad, f"{what}: selection differs on non-ambiguous indices {bad}"
     return True
+
+
+def pack_reference(w: np.ndarray, dtype: str) -> np.ndarray:
+    """numpy statement of the packed gate/up layout (the header's formula):
+    fragment (e, nt, ks) holds W[e, 16 nt + r, KS ks + c] at element
+    (r + 16 (c // (KS/4))) * (KS/4) + c % (KS/4)."""
+    E, d, H = w.shape
+    KS = 32 if dtype == "bf16" else 16
+    q = KS // 4
+    v = w.reshape(E, d // 16, 16, H // KS, 4, q)          # e, nt, r, ks, group, c%q
+    v = v.transpose(0, 1, 3, 4, 2, 5)                      # e, nt, ks, group, r, c%q
+    return np.ascontiguousarray(v).reshape(E, d, H)
 
 
 def rel_l2(a, b) -> float:

@@ -146,6 +146,17 @@ def test_ffn_validation(fn_name):
     assert B.moe_last_error() == ""
 
 
+def test_pack_validation():
+    d = _desc()
+    nbytes = 64 * 1024 * 2048 * 2
+    P = L.moe_pack_gate_up
+    assert P(None, FAKE, FAKE + nbytes, None) == INV
+    assert P(ctypes.byref(d), None, FAKE + nbytes, None) == INV
+    assert P(ctypes.byref(d), MIS, FAKE + nbytes, None) == MISA
+    assert P(ctypes.byref(d), FAKE, FAKE + nbytes - 4096, None) == INV     # overlap
+    assert L.moe_unpack_gate_up(ctypes.byref(_desc(hidden=96)), FAKE, FAKE + nbytes, None) == UNS
+
+
 def test_route_validation():
     d = _desc()
     assert _route(None, 4) == INV

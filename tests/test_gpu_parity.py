@@ -18,7 +18,8 @@ import moe_synth as S
 from oracle import moe_oracle as O
 from sparse_moe_expert_route_amd import binding as B
 
-from parity import DeviceLayer, LayerInputs, check_grouping, compare_layer, rel_l2, to_dev
+from parity import (DeviceLayer, LayerInputs, check_grouping, compare_layer, pack_reference,
+                    rel_l2, to_dev)
 
 pytestmark = pytest.mark.gpu
 SP, DN = B.MOE_PATH_SPARSE, B.MOE_PATH_DENSE
@@ -133,6 +134,27 @@ def test_many_tokens_max_T():
 
 # ------------------------------------------------------------------ properties
 
+@pytest.mark.parametrize("dtype,E,d,H", [("bf16", 3, 64, 128), ("f32", 2, 128, 320),
+                                         ("bf16", 5, 1536, 5120)])
+def test_pack_gate_up_layout(dtype, E, d, H):
+    rng = np.random.default_rng(0)
+    a = rng.standard_normal((E, d, H)).astype(np.float32)
+    host = S.round_to_bf16_bits(a) if dtype == "bf16" else a
+    desc = B.make_desc(H, E, d, 1, False, dtype)
+    w = to_dev(host)
+    pk = B.moe_pack_gate_up(desc, w)
+    back = B.moe_unpack_gate_up(desc, pk)
+    torch.cuda.synchronize()
+    view = np.int16 if dtype == "bf16" else np.float32
+    got = pk.view(torch.int16 if dtype == "bf16" else torch.float32).cpu().numpy()
+    want = pack_reference(host.view(view) if dtype == "bf16" else host, dtype)
+    np.testing.assert_array_equal(got, want)
+    assert torch.equal(back.view(torch.int16 if dtype == "bf16" else torch.int32),
+                       w.view(torch.int16 if dtype == "bf16" else torch.int32))
+    with pytest.raises(B.MoeError):
+        B.moe_pack_gate_up(desc, w, w)        # in place is refused
+
+
 def test_deterministic_and_sparse_equals_dense():
     inp, dev = layer("olmoe-like")
     x = inp.tokens(16, 5)
@@ -225,7 +247,7 @@ def test_layer_class_matches_direct_calls():
     k, k_sh = O.keep_count(0.9, sh.d_ff), O.keep_count(0.5, sh.d_ff_shared)
     m = MoELayer(hidden=sh.hidden, n_experts=sh.n_experts, d_ff=sh.d_ff, top_k=sh.top_k,
                  norm_topk=sh.norm_topk, dtype=sh.dtype, w_router=dev.w_router,
-                 w_gate=dev.w[0], w_up=dev.w[1], w_down=dev.w[2], shared=dev.w_sh)
+                 w_gate=dev.w[0], w_up=dev.w[1], w_down=dev.w[2], shared=dev.w_sh, packed=True)
     say("[case] MoELayer deepseek-v2-like T=4")
     y = m.forward(to_dev(x_host), k, k_sh, path=SP, path_shared=SP)
     got = dev.run(x_host, k, SP, k_sh, SP)
