@@ -681,7 +681,10 @@ static void launch_mask(const FfnArgs &a, const RouteView &rv, int32_t *idx, flo
 // high occupancy, no tail of half-empty block rounds).
 static void launch_gateup(const FfnArgs &a, const RouteView &rv, hipStream_t stream) {
   const bool one = a.T <= 16;
-  dim3 grid(n_items(a, one ? 16 : 64), a.d_ff / 16);
+  // at T <= 16 an item is an active-expert slot: at most min(E, P) of them
+  const int P = a.T * a.top_k;
+  const int items = one ? (a.implicit ? a.E : (a.E < P ? a.E : P)) : n_items(a, 64);
+  dim3 grid(items, a.d_ff / 16);
   timer_begin(kStageGateup, stream);
   if (a.bf16) {
     if (one) gateup_swiglu_kernel<true, 1, 8><<<grid, 512, 0, stream>>>(a.x, a.w_gate, a.w_up, rv, a.H, a.d_ff, a.h);
