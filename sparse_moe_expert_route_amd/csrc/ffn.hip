@@ -408,29 +408,33 @@ __global__ __launch_bounds__(64) void neuron_topk_wave_kernel(const float *__res
 // (ascending) of coef * W_d^e[row, cols]: the down projection streams only
 // the kept rows, and the weighted scatter-add of the token's experts happens
 // in the same block, in a fixed order (no atomics, bitwise reproducible).
-// Block = 16 waves, one token x 64 output columns; each kept row contributes
-// one 128-byte (bf16) or 256-byte (fp32) run, 8 or 4 rows per wave load
-// instruction.  The token's row list (expert, row, coefficient) is staged in
-// LDS first so the weight loads issue back to back.  With idx == nullptr the
-// rows are 0..k-1 (the dense fp32 path, coefficient row stride k).
+// Block = 16 waves, one token x SW output columns (SW = 64 or 128); each
+// kept row contributes one SW-element run (128 to 512 bytes), 64 / (SW /
+// elements-per-16-bytes) rows per wave load instruction.  The host takes the
+// wider blocks when the grid still holds >= 256 of them: longer runs per row
+// and half the per-block fixed cost.  Rows are read through the caches (a
+// partial-line gather, where the non-temporal hint measured slower).  The
+// token's row list (expert, row, coefficient) is staged in LDS first so the
+// weight loads issue back to back.  With idx == nullptr the rows are 0..k-1
+// (the dense fp32 path, coefficient row stride k).
 constexpr int kDownWaves = 16;
-constexpr int kDownSW = 64;          // output columns per block
 constexpr int kDownStage = 4096;     // row-list entries staged in LDS
 
-template <bool BF16>
+template <bool BF16, int SW>
 __global__ __launch_bounds__(1024) void down_token_kernel(const void *__restrict__ wdv,
                                                           const int32_t *__restrict__ idx,
                                                           const float *__restrict__ coef,
                                                           RouteView rv, int H, int d_ff, int k,
                                                           int accumulate, float *__restrict__ y) {
   constexpr int VEC = BF16 ? 8 : 4;   // elements per 16-byte load
-  constexpr int LPR = kDownSW / VEC;  // lanes per row
+  constexpr int LPR = SW / VEC;       // lanes per row
   constexpr int RPI = 64 / LPR;       // rows per wave instruction
-  __shared__ float red[kDownWaves][kDownSW];
+  static_assert(LPR <= 64 && 64 % LPR == 0, "a row run must fit one wave");
+  __shared__ float red[kDownWaves][SW];
   __shared__ uint32_t srow[kDownStage];  // expert * d_ff + row
   __shared__ float scoef[kDownStage];
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int t = blockIdx.x, col0 = blockIdx.y * kDownSW;
+  const int t = blockIdx.x, col0 = blockIdx.y * SW;
   const int top_k = rv.top_k;
   const int nrows = top_k * k;
   const bool staged = nrows <= kDownStage;
@@ -473,8 +477,8 @@ __global__ __launch_bounds__(1024) void down_token_kernel(const void *__restrict
           c[u] = coef[(size_t)p * k + i];
         }
         const size_t off = (size_t)rowid * H + colo;
-        q[u] = BF16 ? ld16_nt(static_cast<const uint16_t *>(wdv) + off)
-                    : ld16_nt(static_cast<const float *>(wdv) + off);
+        q[u] = BF16 ? ld16(static_cast<const uint16_t *>(wdv) + off)
+                    : ld16(static_cast<const float *>(wdv) + off);
       }
     }
 #pragma unroll
@@ -502,7 +506,7 @@ __global__ __launch_bounds__(1024) void down_token_kernel(const void *__restrict
     for (int v = 0; v < VEC; ++v) red[wid][sub * VEC + v] = acc[v];
   }
   __syncthreads();
-  if (threadIdx.x < kDownSW) {
+  if (threadIdx.x < SW) {
     float v = 0.f;
 #pragma unroll
     for (int w = 0; w < kDownWaves; ++w) v += red[w][threadIdx.x];
@@ -714,16 +718,26 @@ static bool zero_contribution(const FfnArgs &a, hipStream_t stream) {
   return true;
 }
 
+// Output columns per down block: 128 while that still gives >= 256 blocks
+// (one per CU), else 64 so that small batches spread over more CUs.
+static int down_block_cols(int T, int H) {
+  return H % 128 == 0 && (long)T * (H / 128) >= 256 ? 128 : 64;
+}
+
 static void launch_down_token(const FfnArgs &a, const RouteView &rv, const int32_t *idx,
                               const float *coef, int k, hipStream_t stream) {
-  dim3 grid(a.T, a.H / kDownSW);
+  const int sw = down_block_cols(a.T, a.H);
+  dim3 grid(a.T, a.H / sw);
   timer_begin(kStageDownRows, stream);
-  if (a.bf16)
-    down_token_kernel<true><<<grid, 1024, 0, stream>>>(a.w_down, idx, coef, rv, a.H, a.d_ff, k,
-                                                       a.accumulate, a.y);
-  else
-    down_token_kernel<false><<<grid, 1024, 0, stream>>>(a.w_down, idx, coef, rv, a.H, a.d_ff, k,
-                                                        a.accumulate, a.y);
+#define MOE_DOWN(BF, SWV)                                                                     \
+  down_token_kernel<BF, SWV><<<grid, 1024, 0, stream>>>(a.w_down, idx, coef, rv, a.H, a.d_ff, k, \
+                                                        a.accumulate, a.y)
+  if (a.bf16) {
+    if (sw == 128) MOE_DOWN(true, 128); else MOE_DOWN(true, 64);
+  } else {
+    if (sw == 128) MOE_DOWN(false, 128); else MOE_DOWN(false, 64);
+  }
+#undef MOE_DOWN
   timer_end(stream);
 }
 
