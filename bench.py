@@ -20,6 +20,12 @@ its algorithmic bytes per launch.  The CPU oracle is timed on a bounded
 sample of the same workload on the host cores as a reported baseline.
 
     python bench.py [--steps K] [--warmup W] [--batch T] [--sweep 1,4,16]
+
+`--crossover` instead times the whole Llama-4-like layer (hidden 5120, 16
+routed experts and 1 shared expert of d_ff 8192, top-1, 90% sparsity) on
+both forced paths at batches 1, 8, 64, 256 and 1024, and prints one JSON
+line with the per-batch timings, the path the shape-only dispatcher picks
+and the faster one.
 """
 from __future__ import annotations
 
@@ -55,6 +61,10 @@ def parse():
     ap.add_argument("--timer-steps", type=int, default=50, help="eager steps timed per kernel")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--crossover", action="store_true",
+                    help="sparse-vs-dense sweep of the Llama-4-like layer (its own JSON line)")
+    ap.add_argument("--layer", default=None, help="layer of the crossover sweep")
+    ap.add_argument("--batches", default=None, help="batches of the crossover sweep")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration) and exit")
     return ap.parse_args()
@@ -63,7 +73,8 @@ def parse():
 class Workload:
     """Device-resident layer copies and token batches for one batch size."""
 
-    def __init__(self, shape, host_w, dev_w0, T, sparsity, path_arg):
+    def __init__(self, shape, host_w, dev_w0, T, sparsity, path_arg, dev_sh0=None,
+                 sparsity_shared=None):
         import torch
         import moe_synth as S
         from sparse_moe_expert_route_amd import binding as B
@@ -72,14 +83,33 @@ class Workload:
         sh = shape
         self.desc = B.make_desc(sh.hidden, sh.n_experts, sh.d_ff, sh.top_k, sh.norm_topk, sh.dtype)
         self.k = B.moe_keep_count(sparsity, sh.d_ff)
-        self.path = {"sparse": B.MOE_PATH_SPARSE, "dense": B.MOE_PATH_DENSE}.get(
-            path_arg, B.moe_select_path(self.desc, T, self.k))
+        forced = {"sparse": B.MOE_PATH_SPARSE, "dense": B.MOE_PATH_DENSE}.get(path_arg)
+        self.auto_path = B.moe_select_path(self.desc, T, self.k)
+        self.path = self.auto_path if forced is None else forced
+        # always-on shared experts (routing NULL, accumulated into y)
+        self.desc_sh = None
+        if dev_sh0 is not None:
+            n_sh, d_sh = sh.n_shared, sh.d_ff_shared
+            self.desc_sh = B.make_desc(sh.hidden, n_sh, d_sh, n_sh, False, sh.dtype)
+            s_sh = sparsity if sparsity_shared is None else sparsity_shared
+            self.k_sh = B.moe_keep_count(s_sh, d_sh)
+            self.auto_path_sh = B.moe_select_path(self.desc_sh, T, self.k_sh)
+            self.path_sh = self.auto_path_sh if forced is None else forced
+            self.ws_sh = torch.empty(B.moe_ffn_workspace_size(self.desc_sh, T, self.k_sh, self.path_sh),
+                                     dtype=torch.uint8, device="cuda")
+            self.ffn_sh = (B.moe_expert_ffn_sparse if self.path_sh == B.MOE_PATH_SPARSE
+                           else B.moe_expert_ffn_dense)
         # bytes one call touches (gate/up of the expected active experts dominate)
         E, K = sh.n_experts, sh.top_k
         act = E * (1 - (1 - K / E) ** T)
         per_call = act * 3 * sh.hidden * sh.d_ff * 2
+        if dev_sh0 is not None:
+            per_call += sh.n_shared * 3 * sh.hidden * sh.d_ff_shared * 2
         self.L = max(2, min(24, 1 + math.ceil(MALL_DEFEAT_BYTES / per_call)))
         self.copies = [dev_w0] + [tuple(w.clone() for w in dev_w0) for _ in range(self.L - 1)]
+        self.copies_sh = None
+        if dev_sh0 is not None:
+            self.copies_sh = [dev_sh0] + [tuple(w.clone() for w in dev_sh0) for _ in range(self.L - 1)]
         self.x_host = [S.tokens(sh, 1 + i, T) for i in range(self.L)]
         self.x = [host_w.to_dev(x) for x in self.x_host]
         self.routing = [B.Routing.allocate(T, K, E) for _ in range(self.L)]
@@ -98,6 +128,10 @@ class Workload:
         B.moe_route(self.desc, self.T, self.x[j], wr, None, self.routing[j], self.ws_r)
         self.ffn(self.desc, self.T, self.k, self.x[j], wg, wu, wd, self.routing[j], self.y[j], 0,
                  idx, self.ws)
+        if self.copies_sh is not None:
+            sg, su, sd = self.copies_sh[j]
+            self.ffn_sh(self.desc_sh, self.T, self.k_sh, self.x[j], sg, su, sd, None, self.y[j], 1,
+                        None, self.ws_sh)
 
     def capture(self):
         torch = self.torch
@@ -159,6 +193,19 @@ class Workload:
             path_down = rec["down_rows"] if self.path == B.MOE_PATH_SPARSE else rec["down_dense"]
             rec["layer"] = rec["router"] + rec["gateup"] + path_down + rec["io"]
             rec["layer_min"] = rec["router"] + rec["gateup"] + rec["down_union"] + rec["io"]
+            # MFMA work of the dense contractions (2 flops per multiply-add)
+            rec["flops_gateup"] = 2 * 2 * P * H * d
+            rec["flops_down_dense"] = 2 * P * d * H
+            if self.copies_sh is not None:
+                n_sh, d_sh = sh.n_shared, sh.d_ff_shared
+                sh_gu = n_sh * 2 * H * d_sh * bw + self.T * n_sh * d_sh * 4
+                sh_dn = (self.T * n_sh * self.k_sh * H * bw if self.path_sh == B.MOE_PATH_SPARSE
+                         else n_sh * d_sh * H * bw)
+                rec["shared"] = sh_gu + sh_dn + self.T * H * 4
+                rec["layer"] += rec["shared"]
+                rec["layer_min"] += rec["shared"]
+                rec["flops_gateup"] += 2 * 2 * self.T * n_sh * H * d_sh
+                rec["flops_down_dense"] += 2 * self.T * n_sh * d_sh * H
             out.append(rec)
         return out
 
@@ -183,7 +230,7 @@ def time_kernels(wl, steps):
     torch = wl.torch
     if steps <= 0:
         return {}
-    timer = B.StageTimer(capacity=steps * 8 + 8)
+    timer = B.StageTimer(capacity=steps * 16 + 16)
     for i in range(wl.L):                 # warm the eager path
         wl.step(i)
     torch.cuda.synchronize()
@@ -193,7 +240,8 @@ def time_kernels(wl, steps):
     torch.cuda.synchronize()
     d = timer.durations()
     timer.close()
-    return {k: dict(n=len(v), avg_us=1e3 * sum(v) / len(v)) for k, v in d.items()}
+    return {k: dict(n=len(v), avg_us=1e3 * sum(v) / len(v), per_step_us=1e3 * sum(v) / steps)
+            for k, v in d.items()}
 
 
 def cpu_baseline(shape, host, wl, seconds):
@@ -223,10 +271,11 @@ def cpu_baseline(shape, host, wl, seconds):
 
 
 class HostLayer:
-    def __init__(self, shape):
+    def __init__(self, shape, shared=False):
         import moe_synth as S
         self.w_router = S.router_matrix(shape, 0)
         self.wg, self.wu, self.wd = S.expert_weights(shape, 0)
+        self.shared = S.expert_weights(shape, 0, group=S.SHARED) if shared else None
 
     @staticmethod
     def to_dev(a):
@@ -237,9 +286,10 @@ class HostLayer:
         return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
-def measure(shape, host, dev_w0, T, args):
-    wl = Workload(shape, host, dev_w0, T, args.sparsity, args.path)
-    log(f"[bench] T={T} k={wl.k} path={'sparse' if wl.path == 0 else 'dense'} copies={wl.L}")
+def measure(shape, host, dev_w0, T, args, path=None, dev_sh0=None):
+    wl = Workload(shape, host, dev_w0, T, args.sparsity, path or args.path, dev_sh0=dev_sh0)
+    log(f"[bench] {shape.name} T={T} k={wl.k} path={'sparse' if wl.path == 0 else 'dense'} "
+        f"copies={wl.L}")
     wl.capture()
     wl.check_replays()
     bpc = wl.bytes_per_call()
@@ -251,7 +301,8 @@ def measure(shape, host, dev_w0, T, args):
                layer_bytes=mean("layer"), layer_min_bytes=mean("layer_min"),
                gateup_bytes=mean("gateup"), down_bytes=mean("down_rows"),
                down_union_bytes=mean("down_union"), active_experts=mean("active"),
-               kernels=kern)
+               flops_gateup=mean("flops_gateup"), flops_down_dense=mean("flops_down_dense"),
+               auto_path="sparse" if wl.auto_path == 0 else "dense", kernels=kern)
     res["hbm_gbs"] = res["layer_bytes"] / sec / 1e9
     res["hbm_frac"] = res["hbm_gbs"] / HBM_PEAK_GBS
     return wl, res
@@ -323,6 +374,64 @@ def calibrate_copy():
                       "read_plus_write_gbs": round(2 * n / dt / 1e9, 1)}), flush=True)
 
 
+def dev_layer(shape, host, B):
+    desc = B.make_desc(shape.hidden, shape.n_experts, shape.d_ff, shape.top_k, shape.norm_topk,
+                       shape.dtype)
+    dev_w0 = (host.to_dev(host.w_router), B.moe_pack_gate_up(desc, host.to_dev(host.wg)),
+              B.moe_pack_gate_up(desc, host.to_dev(host.wu)), host.to_dev(host.wd))
+    dev_sh0 = None
+    if host.shared is not None:
+        n_sh = shape.n_shared
+        dsh = B.make_desc(shape.hidden, n_sh, shape.d_ff_shared, n_sh, False, shape.dtype)
+        g, u, d = host.shared
+        dev_sh0 = (B.moe_pack_gate_up(dsh, host.to_dev(g)), B.moe_pack_gate_up(dsh, host.to_dev(u)),
+                   host.to_dev(d))
+    return dev_w0, dev_sh0
+
+
+def crossover(args):
+    """Both forced paths of one layer over a batch sweep: where the dense
+    MFMA path overtakes the sparse one, next to the dispatcher's pick."""
+    import torch
+    import moe_synth as S
+    from sparse_moe_expert_route_amd import binding as B
+    shape = S.LAYERS[args.layer or "llama4-like"]
+    batches = ([int(t) for t in args.batches.split(",")] if args.batches else list(shape.batches))
+    log(f"[bench] generating {shape.name} weights")
+    host = HostLayer(shape, shared=shape.n_shared > 0)
+    dev_w0, dev_sh0 = dev_layer(shape, host, B)
+    host.wg = host.wu = host.wd = host.shared = None     # device copies suffice from here on
+    torch.cuda.synchronize()
+    rows = []
+    for T in batches:
+        row = {"T": T}
+        for path in ("sparse", "dense"):
+            wl, res = measure(shape, host, dev_w0, T, args, path=path, dev_sh0=dev_sh0)
+            kern = {k: round(v["per_step_us"], 2) for k, v in res["kernels"].items()}
+            ent = {"us_per_call": round(res["us_per_call"], 2),
+                   "us_per_token": round(res["us_per_token"], 3),
+                   "layer_bytes": int(res["layer_bytes"]),
+                   "hbm_gbs": round(res["hbm_gbs"], 1), "kernels_us_per_step": kern}
+            if path == "dense" and "down_dense" in res["kernels"]:
+                k = res["kernels"]["down_dense"]
+                ent["down_dense_tflops"] = round(res["flops_down_dense"] / (k["per_step_us"] * 1e-6) / 1e12, 2)
+            if "gateup_swiglu" in res["kernels"]:
+                k = res["kernels"]["gateup_swiglu"]
+                ent["gateup_tflops"] = round(res["flops_gateup"] / (k["per_step_us"] * 1e-6) / 1e12, 2)
+            row[path] = ent
+            row["auto"] = res["auto_path"]
+            log(f"[bench] {shape.name} T={T} {path}: {res['us_per_call']:.1f} us/call; kernels/step "
+                + ", ".join(f"{k} {v}" for k, v in kern.items()))
+            del wl
+            torch.cuda.empty_cache()
+        row["faster"] = "sparse" if row["sparse"]["us_per_call"] <= row["dense"]["us_per_call"] else "dense"
+        rows.append(row)
+    print(json.dumps({"metric": "sparse-vs-dense crossover: MoE-layer us/call per forced path",
+                      "layer": shape.name, "sparsity": args.sparsity,
+                      "steps": args.steps, "warmup": args.warmup, "launch": "hip-graph replay per step",
+                      "rows": rows}), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -342,13 +451,13 @@ def main():
         calibrate_copy()
         return
     B.lib()
+    if args.crossover:
+        crossover(args)
+        return
     shape = S.LAYERS[LAYER]
     log(f"[bench] generating {LAYER} weights")
     host = HostLayer(shape)
-    desc = B.make_desc(shape.hidden, shape.n_experts, shape.d_ff, shape.top_k, shape.norm_topk,
-                       shape.dtype)
-    dev_w0 = (host.to_dev(host.w_router), B.moe_pack_gate_up(desc, host.to_dev(host.wg)),
-              B.moe_pack_gate_up(desc, host.to_dev(host.wu)), host.to_dev(host.wd))
+    dev_w0, _ = dev_layer(shape, host, B)
     torch.cuda.synchronize()
     sweep = [] if args.sweep == "none" else [int(t) for t in args.sweep.split(",") if t]
     batches = {}

@@ -237,12 +237,14 @@ __global__ __launch_bounds__(256) void neuron_topk_kernel(const float *__restric
   int krem = k;
   if (!keep_all && k > 0) {
     for (int pass = 0; pass < 4; ++pass) {
-      const int shift = 24 - 8 * pass;
+      // float-field digits: exponent, then 8, 8 and 7 mantissa bits
+      const int shift = pass == 0 ? 23 : pass == 1 ? 15 : pass == 2 ? 7 : 0;
+      const uint32_t dmask = pass == 3 ? 0x7fu : 0xffu;
       hist[tid] = 0;
       __syncthreads();
       for (int j = tid; j < d_ff; j += 256) {
         const uint32_t key = sbits[j] & 0x7fffffffu;
-        if ((key & pmask) == tau) atomicAdd(&hist[(key >> shift) & 255u], 1);
+        if ((key & pmask) == tau) atomicAdd(&hist[(key >> shift) & dmask], 1);
       }
       __syncthreads();
       // thread tid owns digit 255 - tid: inclusive scan = keys with digit >= it
@@ -254,7 +256,7 @@ __global__ __launch_bounds__(256) void neuron_topk_kernel(const float *__restric
       }
       __syncthreads();
       tau |= (uint32_t)sel[0] << shift;
-      pmask |= 0xffu << shift;
+      pmask |= dmask << shift;
       krem = sel[1];
       __syncthreads();
     }
@@ -302,27 +304,40 @@ __global__ __launch_bounds__(256) void neuron_topk_kernel(const float *__restric
   }
 }
 
-// Wave-per-pair variant for d_ff = 64 * V: one wave per pair keeps the
-// pair's V activations per lane in registers (a contiguous index segment
-// per lane) and a 256-bin histogram in LDS.  The radix digits follow the
-// float fields of |h| (bits 30..23 = exponent, then 22..15, 14..7, 6..0), so
-// the first pass already spreads the values.  Digit search and compaction
-// use DPP wavefront scans; barriers are single-wave.
-template <int V>
-__global__ __launch_bounds__(64) void neuron_topk_wave_kernel(const float *__restrict__ h,
-                                                              RouteView rv, int P, int d_ff,
-                                                              int k, int32_t *__restrict__ idx,
-                                                              float *__restrict__ hact,
-                                                              void *__restrict__ hm,
-                                                              int hm_bf16) {
-  __shared__ int hist[256];
-  const int lane = threadIdx.x & 63;
+// Register-resident variant for d_ff = 64 * V * NW: a block of NW waves per
+// pair, each lane holding V activations of one contiguous index segment
+// (lane-major within a wave, waves in order), so the kept list comes out in
+// index order from prefix counts alone.  The radix digits follow the float
+// fields of |h| (bits 30..23 = exponent, then 22..15, 14..7, 6..0), so the
+// first pass already spreads the values.  Each wave counts into its own
+// 256-bin LDS histogram (no cross-wave atomic traffic); every wave then sums
+// the NW histograms and finds the digit itself from the same counts, so all
+// waves agree without a broadcast.  Scans are DPP wavefront scans.
+template <int V, int NW>
+__global__ __launch_bounds__(64 * NW) void neuron_topk_seg_kernel(const float *__restrict__ h,
+                                                                  RouteView rv, int d_ff, int k,
+                                                                  int32_t *__restrict__ idx,
+                                                                  float *__restrict__ hact,
+                                                                  void *__restrict__ hm,
+                                                                  int hm_bf16) {
+  __shared__ int hist[NW][256];
+  __shared__ int wtot[2][NW];
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int p = blockIdx.x;
   const float w = rv.weight(p);
-  const float *hp = h + (size_t)p * d_ff + (size_t)lane * V;
+  const int seg = (wid * 64 + lane) * V;  // first index of this lane's segment
+  const float *hp = h + (size_t)p * d_ff + seg;
   uint32_t bits[V];
+  if (V % 4 == 0) {  // 16-byte aligned: d_ff is a multiple of 64 and seg of 4
 #pragma unroll
-  for (int i = 0; i < V; ++i) bits[i] = __float_as_uint(hp[i]);
+    for (int i = 0; i < V; i += 4) {
+      const u32x4 q = ld16(hp + i);
+      bits[i] = q[0]; bits[i + 1] = q[1]; bits[i + 2] = q[2]; bits[i + 3] = q[3];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < V; ++i) bits[i] = __float_as_uint(hp[i]);
+  }
 
   const bool keep_all = k >= d_ff;
   uint32_t tau = 0, pmask = 0;
@@ -333,18 +348,23 @@ __global__ __launch_bounds__(64) void neuron_topk_wave_kernel(const float *__res
       const int shift = pass == 0 ? 23 : pass == 1 ? 15 : pass == 2 ? 7 : 0;
       const uint32_t dmask = pass == 3 ? 0x7fu : 0xffu;
 #pragma unroll
-      for (int b = 0; b < 4; ++b) hist[lane * 4 + b] = 0;
-      __syncthreads();
+      for (int b = 0; b < 4; ++b) hist[wid][lane * 4 + b] = 0;  // own histogram, in wave order
 #pragma unroll
       for (int i = 0; i < V; ++i) {
         const uint32_t key = bits[i] & 0x7fffffffu;
-        if ((key & pmask) == tau) atomicAdd(&hist[(key >> shift) & dmask], 1);
+        if ((key & pmask) == tau) atomicAdd(&hist[wid][(key >> shift) & dmask], 1);
       }
       __syncthreads();
       // lane owns digits 255 - 4 lane - b, b = 0..3 (descending)
       int c[4], local = 0;
 #pragma unroll
-      for (int b = 0; b < 4; ++b) { c[b] = hist[255 - 4 * lane - b]; local += c[b]; }
+      for (int b = 0; b < 4; ++b) {
+        int n = 0;
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) n += hist[ww][255 - 4 * lane - b];
+        c[b] = n;
+        local += n;
+      }
       int run = wave_incl_scan(local) - local;  // keys with a larger digit
       int dsel = -1, knew = 0;
 #pragma unroll
@@ -359,7 +379,7 @@ __global__ __launch_bounds__(64) void neuron_topk_wave_kernel(const float *__res
       tau |= (uint32_t)dsel << shift;
       pmask |= dmask << shift;
       krem = knew;
-      __syncthreads();
+      __syncthreads();  // every wave has read the histograms before the next pass clears them
     }
   }
   int ngt = 0, neq = 0;
@@ -371,13 +391,19 @@ __global__ __launch_bounds__(64) void neuron_topk_wave_kernel(const float *__res
       neq += key == tau;
     }
   }
-  const int gt_before = wave_incl_scan(ngt) - ngt;
-  const int eq_before = wave_incl_scan(neq) - neq;
-  int pos = keep_all ? lane * V : gt_before + min(eq_before, krem);
+  const int gt_incl = wave_incl_scan(ngt), eq_incl = wave_incl_scan(neq);
+  int gt_before = gt_incl - ngt, eq_before = eq_incl - neq;
+  if (NW > 1) {
+    if (lane == 63) { wtot[0][wid] = gt_incl; wtot[1][wid] = eq_incl; }
+    __syncthreads();
+    for (int ww = 0; ww < wid; ++ww) { gt_before += wtot[0][ww]; eq_before += wtot[1][ww]; }
+  }
+  int pos = keep_all ? seg : gt_before + min(eq_before, krem);
   int eq_seen = eq_before;
+  float mv[V];
 #pragma unroll
   for (int i = 0; i < V; ++i) {
-    const int j = lane * V + i;
+    const int j = seg + i;
     const uint32_t key = bits[i] & 0x7fffffffu;
     bool keep;
     if (keep_all) keep = true;
@@ -393,12 +419,34 @@ __global__ __launch_bounds__(64) void neuron_topk_wave_kernel(const float *__res
       }
       ++pos;
     }
-    if (hm) {
-      const float mv = keep ? v : 0.0f;
-      if (hm_bf16)
-        static_cast<uint16_t *>(hm)[(size_t)p * d_ff + j] = (uint16_t)f32_to_bf16_bits(mv);
-      else
-        static_cast<float *>(hm)[(size_t)p * d_ff + j] = mv;
+    mv[i] = keep ? v : 0.0f;
+  }
+  if (hm) {  // dense masked row: this lane's V consecutive entries
+    if (hm_bf16) {
+      uint16_t *o = static_cast<uint16_t *>(hm) + (size_t)p * d_ff + seg;
+      if (V % 8 == 0) {
+#pragma unroll
+        for (int i = 0; i < V; i += 8) {
+          u32x4 q;
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            q[c] = f32_to_bf16_bits(mv[i + 2 * c]) | (f32_to_bf16_bits(mv[i + 2 * c + 1]) << 16);
+          *reinterpret_cast<u32x4 *>(o + i) = q;
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < V; ++i) o[i] = (uint16_t)f32_to_bf16_bits(mv[i]);
+      }
+    } else {
+      float *o = static_cast<float *>(hm) + (size_t)p * d_ff + seg;
+      if (V % 4 == 0) {
+#pragma unroll
+        for (int i = 0; i < V; i += 4)
+          *reinterpret_cast<f32x4 *>(o + i) = f32x4{mv[i], mv[i + 1], mv[i + 2], mv[i + 3]};
+      } else {
+#pragma unroll
+        for (int i = 0; i < V; ++i) o[i] = mv[i];
+      }
     }
   }
 }
@@ -663,15 +711,19 @@ static void launch_mask(const FfnArgs &a, const RouteView &rv, int32_t *idx, flo
                         int hm_bf16, hipStream_t stream) {
   const int P = a.T * a.top_k;
   timer_begin(kStageMask, stream);
-  switch (a.d_ff) {  // one wave per pair where d_ff / 64 values fit in registers
-#define MOE_MASK_CASE(V)                                                                    \
-  case 64 * V:                                                                              \
-    neuron_topk_wave_kernel<V><<<P, 64, 0, stream>>>(a.h, rv, P, a.d_ff, a.k_keep, idx, hact, \
-                                                     hm, hm_bf16);                          \
+  switch (a.d_ff) {  // register-resident segments where d_ff / 64 or d_ff / 512 values fit
+#define MOE_MASK_CASE(V, NW)                                                                  \
+  case 64 * V * NW:                                                                           \
+    neuron_topk_seg_kernel<V, NW><<<P, 64 * NW, 0, stream>>>(a.h, rv, a.d_ff, a.k_keep, idx, \
+                                                            hact, hm, hm_bf16);              \
     break;
-    MOE_MASK_CASE(1) MOE_MASK_CASE(2) MOE_MASK_CASE(3) MOE_MASK_CASE(4) MOE_MASK_CASE(5)
-    MOE_MASK_CASE(6) MOE_MASK_CASE(8) MOE_MASK_CASE(10) MOE_MASK_CASE(12) MOE_MASK_CASE(16)
-    MOE_MASK_CASE(20) MOE_MASK_CASE(24) MOE_MASK_CASE(32)
+    MOE_MASK_CASE(1, 1) MOE_MASK_CASE(2, 1) MOE_MASK_CASE(3, 1) MOE_MASK_CASE(4, 1)
+    MOE_MASK_CASE(5, 1) MOE_MASK_CASE(6, 1) MOE_MASK_CASE(8, 1) MOE_MASK_CASE(10, 1)
+    MOE_MASK_CASE(12, 1) MOE_MASK_CASE(16, 1) MOE_MASK_CASE(20, 1) MOE_MASK_CASE(24, 1)
+    MOE_MASK_CASE(32, 1)
+    MOE_MASK_CASE(5, 8) MOE_MASK_CASE(6, 8) MOE_MASK_CASE(7, 8) MOE_MASK_CASE(8, 8)
+    MOE_MASK_CASE(9, 8) MOE_MASK_CASE(10, 8) MOE_MASK_CASE(11, 8) MOE_MASK_CASE(12, 8)
+    MOE_MASK_CASE(13, 8) MOE_MASK_CASE(14, 8) MOE_MASK_CASE(15, 8) MOE_MASK_CASE(16, 8)
 #undef MOE_MASK_CASE
     default:
       neuron_topk_kernel<<<P, 256, (size_t)a.d_ff * 4, stream>>>(a.h, rv, a.d_ff, a.k_keep, idx,

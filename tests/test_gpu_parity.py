@@ -112,6 +112,18 @@ def test_ragged_shapes(dtype, T, path):
     run_case("olmoe-like", T, 0.7, path, s_sh=0.5, path_sh=1 - path, dtype=dtype, **RAGGED)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("d_ff", [2112, 3584, 4096])
+@pytest.mark.parametrize("path", [SP, DN])
+def test_large_dff_masks(dtype, d_ff, path):
+    # d_ff past the one-wave mask: 8-wave segments with an odd and an even
+    # per-lane count (3584, 4096), the LDS fallback (2112), and a shared
+    # expert of d_ff 2560
+    run_case("olmoe-like", 5, 0.9, path, s_sh=0.5, path_sh=path, dtype=dtype,
+             **dict(hidden=128, n_experts=4, d_ff=d_ff, top_k=2, norm_topk=False, n_shared=1,
+                    d_ff_shared=2560, zipf_bias=None))
+
+
 @pytest.mark.parametrize("k", [0, 1, 191, 192])
 def test_keep_extremes(k):
     inp, dev = layer("olmoe-like", dtype="f32", **RAGGED)
