@@ -208,6 +208,127 @@ __global__ __launch_bounds__(64 * W, MT == 1 ? 8 : 1) void gateup_swiglu_kernel(
   }
 }
 
+// ---------------------------------------------------------------- gate / up GEMM
+// Grouped GEMM for batches where an expert holds many tokens: work item =
+// one expert and up to 128 of its tokens, block = 4 waves x 64 neurons
+// (wave w owns neuron tile 4 * blockIdx.y + w for all 8 token tiles).  Per
+// stage of two k-steps (128 bytes of every token row) the block gathers the
+// item's token rows into an LDS tile (double-buffered, rows padded to avoid
+// bank conflicts), while each wave streams its own packed gate and up
+// fragments from HBM one stage ahead.  Each weight byte thus feeds up to 128
+// tokens and each staged token row 4 neuron tiles; x is read from L2 once
+// per 64 neurons instead of once per 16.  Epilogue: h = silu(g) * u, four
+// consecutive neurons per lane, one 16-byte store per token.
+constexpr int kGemmTok = 128;               // tokens per work item (8 MFMA token tiles)
+constexpr int kGemmRowB = 128 + 16;         // LDS bytes per staged token row (+ pad)
+
+template <bool BF16>
+__global__ __launch_bounds__(256, 2) void gateup_gemm_kernel(const void *__restrict__ xv,
+                                                             const void *__restrict__ wgv,
+                                                             const void *__restrict__ wuv,
+                                                             RouteView rv, int H, int d_ff,
+                                                             float *__restrict__ hout) {
+  __shared__ __attribute__((aligned(16))) uint8_t xs[2][kGemmTok * kGemmRowB];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  int e, q0, ntok;
+  if (!find_item<kGemmTok>(rv, blockIdx.x, e, q0, ntok)) return;  // block-uniform
+  const int ntiles = (ntok + 15) >> 4;
+  constexpr int EB = BF16 ? 2 : 4;
+  constexpr int KS = BF16 ? 32 : 16;        // elements per k-step (64 bytes of a row)
+  const int nsteps = H / KS;                // even: H is a multiple of 64
+  const int nit = nsteps / 2;               // stages of two k-steps
+
+  // staging map: token rows tid / 8 + 32 i (i < 4), 16-byte chunk tid % 8
+  const int srow = tid >> 3, schunk = tid & 7;
+  const uint8_t *xrow[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = srow + 32 * i;
+    xrow[i] = c < ntok ? static_cast<const uint8_t *>(xv) +
+                             (size_t)(rv.pair_at(q0 + c) / rv.top_k) * H * EB + schunk * 16
+                       : nullptr;
+  }
+  const int nt = blockIdx.y * 4 + wid;
+  const size_t fbase = ((size_t)e * (d_ff / 16) + nt) * nsteps * 1024 + lane * 16;
+  const uint8_t *wg = static_cast<const uint8_t *>(wgv) + fbase;
+  const uint8_t *wu = static_cast<const uint8_t *>(wuv) + fbase;
+
+  f32x4 accg[8], accu[8];
+#pragma unroll
+  for (int tl = 0; tl < 8; ++tl) { accg[tl] = f32x4{0, 0, 0, 0}; accu[tl] = f32x4{0, 0, 0, 0}; }
+
+  u32x4 stg[4], ag[2], au[2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) stg[i] = xrow[i] ? ld16(xrow[i]) : u32x4{0, 0, 0, 0};
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    *reinterpret_cast<u32x4 *>(&xs[0][(srow + 32 * i) * kGemmRowB + schunk * 16]) = stg[i];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    ag[k] = ld16_nt(wg + (size_t)k * 1024);
+    au[k] = ld16_nt(wu + (size_t)k * 1024);
+  }
+  __syncthreads();
+
+  const int r = lane & 15, g = lane >> 4;
+  for (int it = 0; it < nit; ++it) {
+    const int cur = it & 1;
+    const bool more = it + 1 < nit;
+    u32x4 ng[2], nu[2];
+    if (more) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        stg[i] = xrow[i] ? ld16(xrow[i] + (size_t)(it + 1) * 128) : u32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        ng[k] = ld16_nt(wg + (size_t)(2 * it + 2 + k) * 1024);
+        nu[k] = ld16_nt(wu + (size_t)(2 * it + 2 + k) * 1024);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+#pragma unroll
+      for (int tl = 0; tl < 8; ++tl) {
+        if (tl < ntiles) {
+          const u32x4 b = *reinterpret_cast<const u32x4 *>(
+              &xs[cur][(tl * 16 + r) * kGemmRowB + k * 64 + g * 16]);
+          if (BF16) {
+            accg[tl] = mfma_bf16(ag[k], b, accg[tl]);
+            accu[tl] = mfma_bf16(au[k], b, accu[tl]);
+          } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              accg[tl] = mfma_f32(__uint_as_float(ag[k][j]), __uint_as_float(b[j]), accg[tl]);
+              accu[tl] = mfma_f32(__uint_as_float(au[k][j]), __uint_as_float(b[j]), accu[tl]);
+            }
+          }
+        }
+      }
+    }
+    if (more) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<u32x4 *>(&xs[cur ^ 1][(srow + 32 * i) * kGemmRowB + schunk * 16]) = stg[i];
+#pragma unroll
+      for (int k = 0; k < 2; ++k) { ag[k] = ng[k]; au[k] = nu[k]; }
+    }
+    __syncthreads();
+  }
+
+  const int neuron0 = nt * 16 + 4 * g;
+#pragma unroll
+  for (int tl = 0; tl < 8; ++tl) {
+    const int c = tl * 16 + r;
+    if (tl < ntiles && c < ntok) {
+      const int p = rv.pair_at(q0 + c);
+      f32x4 hv;
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) hv[rr] = silu(accg[tl][rr]) * accu[tl][rr];
+      *reinterpret_cast<f32x4 *>(hout + (size_t)p * d_ff + neuron0) = hv;
+    }
+  }
+}
+
 // ---------------------------------------------------------------- neuron mask
 // One block per pair.  The pair's d_ff activations sit in LDS as raw fp32
 // bits; the score key is the bit pattern of |h| (an order-preserving uint32
@@ -736,18 +857,21 @@ static void launch_mask(const FfnArgs &a, const RouteView &rv, int32_t *idx, flo
 // tile per item suffices; that variant splits K over 8 waves (short blocks,
 // high occupancy, no tail of half-empty block rounds).
 static void launch_gateup(const FfnArgs &a, const RouteView &rv, hipStream_t stream) {
-  const bool one = a.T <= 16;
-  // at T <= 16 an item is an active-expert slot: at most min(E, P) of them
-  const int P = a.T * a.top_k;
-  const int items = one ? (a.implicit ? a.E : (a.E < P ? a.E : P)) : n_items(a, 64);
-  dim3 grid(items, a.d_ff / 16);
   timer_begin(kStageGateup, stream);
-  if (a.bf16) {
-    if (one) gateup_swiglu_kernel<true, 1, 8><<<grid, 512, 0, stream>>>(a.x, a.w_gate, a.w_up, rv, a.H, a.d_ff, a.h);
-    else gateup_swiglu_kernel<true, 4, 4><<<grid, 256, 0, stream>>>(a.x, a.w_gate, a.w_up, rv, a.H, a.d_ff, a.h);
+  if (a.T <= 16) {
+    // an item is an active-expert slot: at most min(E, P) of them
+    const int P = a.T * a.top_k;
+    dim3 grid(a.implicit ? a.E : (a.E < P ? a.E : P), a.d_ff / 16);
+    if (a.bf16)
+      gateup_swiglu_kernel<true, 1, 8><<<grid, 512, 0, stream>>>(a.x, a.w_gate, a.w_up, rv, a.H, a.d_ff, a.h);
+    else
+      gateup_swiglu_kernel<false, 1, 8><<<grid, 512, 0, stream>>>(a.x, a.w_gate, a.w_up, rv, a.H, a.d_ff, a.h);
   } else {
-    if (one) gateup_swiglu_kernel<false, 1, 8><<<grid, 512, 0, stream>>>(a.x, a.w_gate, a.w_up, rv, a.H, a.d_ff, a.h);
-    else gateup_swiglu_kernel<false, 4, 4><<<grid, 256, 0, stream>>>(a.x, a.w_gate, a.w_up, rv, a.H, a.d_ff, a.h);
+    dim3 grid(n_items(a, kGemmTok), a.d_ff / 64);
+    if (a.bf16)
+      gateup_gemm_kernel<true><<<grid, 256, 0, stream>>>(a.x, a.w_gate, a.w_up, rv, a.H, a.d_ff, a.h);
+    else
+      gateup_gemm_kernel<false><<<grid, 256, 0, stream>>>(a.x, a.w_gate, a.w_up, rv, a.H, a.d_ff, a.h);
   }
   timer_end(stream);
 }
