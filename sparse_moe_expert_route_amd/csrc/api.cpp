@@ -93,7 +93,8 @@ FfnLayout ffn_layout(const moe_desc *d, int32_t T, int32_t k, moe_path path) {
   L.hact = off;
   if (path == MOE_PATH_SPARSE) off += up(P * (size_t)k * 4);
   L.partial = off;
-  if (path == MOE_PATH_DENSE && bf16) off += up(P * d->hidden * 4);
+  if (path == MOE_PATH_DENSE && bf16)
+    off += up(moe::dense_down_partial_rows(T, d->n_experts, d->top_k, d->hidden) * d->hidden * 4);
   L.hm = off;
   if (path == MOE_PATH_DENSE) off += up(P * d->d_ff * elem_bytes(d));
   L.total = off;

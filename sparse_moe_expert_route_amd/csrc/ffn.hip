@@ -685,92 +685,151 @@ __global__ __launch_bounds__(1024) void down_token_kernel(const void *__restrict
 }
 
 // ---------------------------------------------------------------- dense down (bf16)
-// Dense-path down GEMM for one work item (expert, <=64 tokens) and 64
-// output columns: out[tok, col] = sum_j hm[pair(tok), j] * W_d[e][j, col].
-// W_d's K (= d_ff) is its row index, so 128-row x 64-col tiles are staged
-// through LDS transposed ([col][k]) to give each lane the 8 consecutive k
-// the MFMA B operand wants; the next tile is prefetched into registers
-// while the current one is consumed.  Wave w owns columns 16w..16w+15 for
-// up to 4 token tiles.
-constexpr int kDKC = 128;
-constexpr int kDenseTokGroup = 64;
-__global__ __launch_bounds__(256) void down_dense_bf16_kernel(const uint16_t *__restrict__ wd,
-                                                              const uint16_t *__restrict__ hm,
-                                                              RouteView rv, int H, int d_ff,
-                                                              float *__restrict__ partial) {
-  __shared__ __attribute__((aligned(16))) uint16_t bt[64][kDKC + 8];
+// Dense-path down GEMM: partial[pair, chunk, col] = sum over the chunk's k of
+// hm[pair, k] * W_d[e][k, col], for a work item (expert, <= 128 of its
+// tokens) x 64 output columns x one K chunk (blockIdx.z).  MFMA A = the
+// masked h rows (k-contiguous, staged through LDS in padded rows); MFMA B
+// needs k-contiguous columns of the row-major W_d, so each stage of 64 rows
+// is packed into bf16 k-pairs and written transposed ([col][k]) into LDS.
+// The k-pair slot is XOR-swizzled by the column, so the transposing writes
+// and the 16-byte fragment reads both reach the 2-way minimum of bank
+// conflicts.  Waves form a 2 x 2 grid: each owns 4 token tiles x 2 column
+// tiles.  Both LDS tiles are double-buffered with one register stage.
+constexpr int kDnTok = 128;                 // tokens per work item
+constexpr int kDnCols = 64;                 // output columns per block
+constexpr int kDnK = 64;                    // k per stage
+constexpr int kDnArow = kDnK * 2 + 16;      // LDS bytes per staged hm row (+ pad)
+constexpr int kDnBrow = kDnK * 2;           // LDS bytes per transposed W_d column
+
+__device__ __forceinline__ int dn_swz(int col) { return 4 * ((col & 7) ^ ((col >> 3) & 7)); }
+
+__global__ __launch_bounds__(256, 2) void down_dense_gemm_kernel(const uint16_t *__restrict__ wd,
+                                                                 const uint16_t *__restrict__ hm,
+                                                                 RouteView rv, int H, int d_ff,
+                                                                 int kchunk,
+                                                                 float *__restrict__ partial) {
+  __shared__ __attribute__((aligned(16))) uint8_t as[2][kDnTok * kDnArow];
+  __shared__ __attribute__((aligned(16))) uint32_t bs[2][kDnCols * kDnBrow / 4];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   int e, q0, ntok;
-  if (!find_item<kDenseTokGroup>(rv, blockIdx.x, e, q0, ntok)) return;
+  if (!find_item<kDnTok>(rv, blockIdx.x, e, q0, ntok)) return;  // block-uniform
+  const int col0 = blockIdx.y * kDnCols;
+  const int S = gridDim.z, sidx = blockIdx.z;
+  const int k0 = sidx * kchunk;
+  const int nit = (min(d_ff, k0 + kchunk) - k0) / kDnK;
   const int ntiles = (ntok + 15) >> 4;
-  const int r = lane & 15, g = lane >> 4;
-  const int col0 = blockIdx.y * 64;
 
-  size_t aoff[4];
-  bool aval[4];
+  // A staging: rows tid / 8 + 32 i (i < 4), 16-byte chunk tid % 8 (8 k)
+  const int arow = tid >> 3, achunk = tid & 7;
+  const uint16_t *ap[4];
 #pragma unroll
-  for (int tl = 0; tl < 4; ++tl) {
-    const int c = tl * 16 + r;
-    aval[tl] = c < ntok;
-    aoff[tl] = aval[tl] ? (size_t)rv.pair_at(q0 + c) * d_ff : 0;
+  for (int i = 0; i < 4; ++i) {
+    const int c = arow + 32 * i;
+    ap[i] = c < ntok ? hm + (size_t)rv.pair_at(q0 + c) * d_ff + k0 + achunk * 8 : nullptr;
   }
-  f32x4 acc[4];
-#pragma unroll
-  for (int tl = 0; tl < 4; ++tl) acc[tl] = f32x4{0, 0, 0, 0};
+  // B staging: k-pair kp = tid / 8 (rows 2 kp, 2 kp + 1), columns 8 cg .. 8 cg + 7
+  const int kp = tid >> 3, cg = tid & 7;
+  const uint16_t *bp = wd + ((size_t)e * d_ff + k0 + 2 * kp) * H + col0 + 8 * cg;
 
-  // staging map: 128 rows x 64 cols = 4 rows per thread, 8 columns each
-  const int srow = tid >> 3, scol = (tid & 7) * 8;
-  const uint16_t *wbase = wd + (size_t)e * d_ff * H + col0 + scol;
-  u32x4 pf[4];
+  u32x4 sa[4], sb[2];
+  auto load_stage = [&](int it) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    pf[i] = srow + 32 * i < d_ff ? ld16(wbase + (size_t)(srow + 32 * i) * H) : u32x4{0, 0, 0, 0};
-
-  for (int kb = 0; kb < d_ff; kb += kDKC) {
+    for (int i = 0; i < 4; ++i) sa[i] = ap[i] ? ld16(ap[i] + it * kDnK) : u32x4{0, 0, 0, 0};
+    sb[0] = ld16_nt(bp + (size_t)it * kDnK * H);
+    sb[1] = ld16_nt(bp + (size_t)it * kDnK * H + H);
+  };
+  auto store_stage = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int kr = srow + 32 * i;
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<u32x4 *>(&as[buf][(arow + 32 * i) * kDnArow + achunk * 16]) = sa[i];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        bt[scol + 2 * j][kr] = (uint16_t)(pf[i][j] & 0xffffu);
-        bt[scol + 2 * j + 1][kr] = (uint16_t)(pf[i][j] >> 16);
-      }
+    for (int c = 0; c < 8; ++c) {  // column 8 cg + c gets the pair (row 2 kp, row 2 kp + 1)
+      const uint32_t lo = (sb[0][c >> 1] >> (16 * (c & 1))) & 0xffffu;
+      const uint32_t hi = (sb[1][c >> 1] >> (16 * (c & 1))) & 0xffffu;
+      const int col = 8 * cg + c;
+      bs[buf][col * (kDnBrow / 4) + (kp ^ dn_swz(col))] = lo | (hi << 16);
     }
-    __syncthreads();
-    if (kb + kDKC < d_ff) {
+  };
+
+  const int r = lane & 15, g = lane >> 4;
+  const int wt = wid >> 1, wc = wid & 1;  // token tiles 4 wt .. 4 wt + 3, column tiles 2 wc, 2 wc + 1
+  f32x4 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { acc[i][0] = f32x4{0, 0, 0, 0}; acc[i][1] = f32x4{0, 0, 0, 0}; }
+
+  if (nit > 0) {
+    load_stage(0);
+    store_stage(0);
+  }
+  __syncthreads();
+  for (int it = 0; it < nit; ++it) {
+    const int cur = it & 1;
+    const bool more = it + 1 < nit;
+    if (more) load_stage(it + 1);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      u32x4 b[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int col = (2 * wc + j) * 16 + r;
+        const int w0 = (ks * 16 + 4 * g) ^ dn_swz(col);  // 4 k-pairs = this lane's 8 k
+        b[j] = *reinterpret_cast<const u32x4 *>(&bs[cur][col * (kDnBrow / 4) + w0]);
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int kr = kb + kDKC + srow + 32 * i;
-        pf[i] = kr < d_ff ? ld16(wbase + (size_t)kr * H) : u32x4{0, 0, 0, 0};
-      }
-    }
-#pragma unroll
-    for (int ks = 0; ks < kDKC / 32; ++ks) {
-      if (kb + ks * 32 >= d_ff) break;  // d_ff is a multiple of 64, not of 128
-      const u32x4 b = *reinterpret_cast<const u32x4 *>(&bt[16 * wid + r][ks * 32 + 8 * g]);
-#pragma unroll
-      for (int tl = 0; tl < 4; ++tl) {
+        const int tl = 4 * wt + i;
         if (tl < ntiles) {
-          const u32x4 a = aval[tl] ? ld16(hm + aoff[tl] + kb + ks * 32 + 8 * g) : u32x4{0, 0, 0, 0};
-          acc[tl] = mfma_bf16(a, b, acc[tl]);
+          const u32x4 av = *reinterpret_cast<const u32x4 *>(
+              &as[cur][(tl * 16 + r) * kDnArow + ks * 64 + g * 16]);
+          acc[i][0] = mfma_bf16(av, b[0], acc[i][0]);
+          acc[i][1] = mfma_bf16(av, b[1], acc[i][1]);
         }
       }
     }
+    if (more) store_stage(cur ^ 1);
     __syncthreads();
   }
+  // D: lane holds column r of each column tile, token rows 4 g + rr of each token tile
 #pragma unroll
-  for (int tl = 0; tl < 4; ++tl) {
-    if (tl < ntiles) {
+  for (int i = 0; i < 4; ++i) {
+    const int tl = 4 * wt + i;
+    if (tl >= ntiles) continue;
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int c = tl * 16 + 4 * g + rr;
-        if (c < ntok) {
-          const int p = rv.pair_at(q0 + c);
-          partial[(size_t)p * H + col0 + 16 * wid + r] = acc[tl][rr];
-        }
+    for (int rr = 0; rr < 4; ++rr) {
+      const int c = tl * 16 + 4 * g + rr;
+      if (c < ntok) {
+        const size_t row = (size_t)rv.pair_at(q0 + c) * S + sidx;
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          partial[row * H + col0 + (2 * wc + j) * 16 + r] = acc[i][j][rr];
       }
     }
   }
+}
+
+// K chunks of the dense down GEMM: enough blocks to fill the chip when few
+// work items exist (small batches), each chunk a multiple of 64 rows and at
+// least 256.  A function of the shape only, so the workspace size and the
+// launch agree.
+static int dense_down_kchunk(int T, int E, int top_k, int H, int d_ff) {
+  const long P = (long)T * top_k;
+  const long items = (E < P ? E : P) + P / kDnTok;
+  const long base = items * (H / kDnCols);
+  long S = (1024 + base - 1) / base;
+  const long smax = d_ff / 256 > 0 ? d_ff / 256 : 1;
+  if (S > smax) S = smax;
+  if (S < 1) S = 1;
+  const long per = (d_ff + S - 1) / S;
+  return (int)((per + kDnK - 1) / kDnK * kDnK);
+}
+
+// Partial rows the dense down GEMM may write at most T tokens: P * chunks
+// <= P + 65536 P / (items H) with items >= min(E, P), so this bound holds for
+// every smaller T too (a workspace sized for T serves any shorter call).
+size_t dense_down_partial_rows(int T, int E, int top_k, int H) {
+  const size_t P = (size_t)T * top_k;
+  const size_t per_item = P > (size_t)E ? (P + E - 1) / E : 1;
+  return P + (size_t)((65536 + H - 1) / H) * per_item;
 }
 
 // ---------------------------------------------------------------- combine
@@ -934,13 +993,17 @@ hipError_t launch_ffn_dense(const FfnArgs &a, hipStream_t stream) {
   launch_gateup(a, rv, stream);
   launch_mask(a, rv, a.idx, nullptr, a.hm, a.bf16, stream);
   if (a.bf16) {
-    dim3 grid(n_items(a, kDenseTokGroup), a.H / 64);
+    const int kc = dense_down_kchunk(a.T, a.E, a.top_k, a.H, a.d_ff);
+    const int S = (a.d_ff + kc - 1) / kc;
+    if ((size_t)a.T * a.top_k * S > dense_down_partial_rows(a.T, a.E, a.top_k, a.H))
+      return hipErrorInvalidValue;  // cannot happen: the bound covers every split count
+    dim3 grid(n_items(a, kDnTok), a.H / kDnCols, S);
     timer_begin(kStageDownDense, stream);
-    down_dense_bf16_kernel<<<grid, 256, 0, stream>>>(static_cast<const uint16_t *>(a.w_down),
+    down_dense_gemm_kernel<<<grid, 256, 0, stream>>>(static_cast<const uint16_t *>(a.w_down),
                                                      static_cast<const uint16_t *>(a.hm), rv, a.H,
-                                                     a.d_ff, a.partial);
+                                                     a.d_ff, kc, a.partial);
     timer_end(stream);
-    launch_combine(a, 1, stream);
+    launch_combine(a, S, stream);
   } else {
     // fp32: every row of W_d against the dense masked row, on the row kernel
     launch_down_token(a, rv, nullptr, static_cast<const float *>(a.hm), a.d_ff, stream);

@@ -70,6 +70,8 @@ struct FfnArgs {
 hipError_t launch_pack_gate_up(const void *src, void *dst, int E, int d_ff, int H, int bf16,
                                int unpack, hipStream_t stream);
 
+// Rows of the dense-path down GEMM's partial buffer for calls of at most T tokens.
+size_t dense_down_partial_rows(int T, int E, int top_k, int H);
 hipError_t launch_ffn_sparse(const FfnArgs &a, hipStream_t stream);
 hipError_t launch_ffn_dense(const FfnArgs &a, hipStream_t stream);
 
