@@ -116,7 +116,13 @@ __device__ __forceinline__ void wave_topk(const float *__restrict__ part, size_t
     const int e = lane + 64 * i;
     float l = 0.f;
     if (e < E) {
-      for (int c = 0; c < nsplit; ++c) l += part[c * split_stride + e];
+      // all split partials in flight at once, then added in split order
+      float pv[kRouterSplits];
+#pragma unroll
+      for (int c = 0; c < kRouterSplits; ++c) pv[c] = c < nsplit ? part[c * split_stride + e] : 0.f;
+#pragma unroll
+      for (int c = 0; c < kRouterSplits; ++c)
+        if (c < nsplit) l += pv[c];
       if (bias) l += bias[e];
     }
     v[i] = l;
