@@ -433,7 +433,11 @@ __global__ __launch_bounds__(256) void neuron_topk_kernel(const float *__restric
 // first pass already spreads the values.  Each wave counts into its own
 // 256-bin LDS histogram (no cross-wave atomic traffic); every wave then sums
 // the NW histograms and finds the digit itself from the same counts, so all
-// waves agree without a broadcast.  Scans are DPP wavefront scans.
+// waves agree without a broadcast.  Scans are DPP wavefront scans.  The
+// kept list (ids, w * h) is compacted in LDS and written with coalesced
+// stores: per lane, kept entries are sparse among its V values, so direct
+// stores would be V mostly-masked scattered instructions.
+constexpr int kMaskStage = 4096;
 template <int V, int NW>
 __global__ __launch_bounds__(64 * NW) void neuron_topk_seg_kernel(const float *__restrict__ h,
                                                                   RouteView rv, int d_ff, int k,
@@ -443,6 +447,9 @@ __global__ __launch_bounds__(64 * NW) void neuron_topk_seg_kernel(const float *_
                                                                   int hm_bf16) {
   __shared__ int hist[NW][256];
   __shared__ int wtot[2][NW];
+  constexpr int SN = 64 * V * NW < kMaskStage ? 64 * V * NW : kMaskStage;  // k <= d_ff
+  __shared__ int s_idx[SN];
+  __shared__ float s_val[SN];
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int p = blockIdx.x;
   const float w = rv.weight(p);
@@ -521,6 +528,7 @@ __global__ __launch_bounds__(64 * NW) void neuron_topk_seg_kernel(const float *_
   }
   int pos = keep_all ? seg : gt_before + min(eq_before, krem);
   int eq_seen = eq_before;
+  const bool stage = k <= SN && (idx || hact);  // block-uniform
   float mv[V];
 #pragma unroll
   for (int i = 0; i < V; ++i) {
@@ -534,13 +542,25 @@ __global__ __launch_bounds__(64 * NW) void neuron_topk_seg_kernel(const float *_
     else keep = false;
     const float v = w * __uint_as_float(bits[i]);
     if (keep) {
-      if (pos < k) {  // always true for finite input; keeps NaN input memory-safe
-        if (idx) idx[(size_t)p * k + pos] = j;
-        if (hact) hact[(size_t)p * k + pos] = v;
+      if (pos < k) {  // always true: exactly k keys are kept
+        if (stage) {
+          s_idx[pos] = j;
+          s_val[pos] = v;
+        } else {
+          if (idx) idx[(size_t)p * k + pos] = j;
+          if (hact) hact[(size_t)p * k + pos] = v;
+        }
       }
       ++pos;
     }
     mv[i] = keep ? v : 0.0f;
+  }
+  if (stage) {
+    __syncthreads();
+    for (int q = threadIdx.x; q < k; q += 64 * NW) {
+      if (idx) idx[(size_t)p * k + q] = s_idx[q];
+      if (hact) hact[(size_t)p * k + q] = s_val[q];
+    }
   }
   if (hm) {  // dense masked row: this lane's V consecutive entries
     if (hm_bf16) {
@@ -891,16 +911,23 @@ static void launch_mask(const FfnArgs &a, const RouteView &rv, int32_t *idx, flo
                         int hm_bf16, hipStream_t stream) {
   const int P = a.T * a.top_k;
   timer_begin(kStageMask, stream);
-  switch (a.d_ff) {  // register-resident segments where d_ff / 64 or d_ff / 512 values fit
+  // register-resident segments: 4 waves per pair up to d_ff = 2048 (d_ff / 256
+  // values per lane), one wave for the other multiples of 64 up to 2048, 8
+  // waves from 2560 to 8192 (d_ff / 512 values per lane)
 #define MOE_MASK_CASE(V, NW)                                                                  \
   case 64 * V * NW:                                                                           \
     neuron_topk_seg_kernel<V, NW><<<P, 64 * NW, 0, stream>>>(a.h, rv, a.d_ff, a.k_keep, idx, \
                                                             hact, hm, hm_bf16);              \
     break;
-    MOE_MASK_CASE(1, 1) MOE_MASK_CASE(2, 1) MOE_MASK_CASE(3, 1) MOE_MASK_CASE(4, 1)
-    MOE_MASK_CASE(5, 1) MOE_MASK_CASE(6, 1) MOE_MASK_CASE(8, 1) MOE_MASK_CASE(10, 1)
-    MOE_MASK_CASE(12, 1) MOE_MASK_CASE(16, 1) MOE_MASK_CASE(20, 1) MOE_MASK_CASE(24, 1)
-    MOE_MASK_CASE(32, 1)
+  switch (a.d_ff) {
+    MOE_MASK_CASE(1, 4) MOE_MASK_CASE(2, 4) MOE_MASK_CASE(3, 4) MOE_MASK_CASE(4, 4)
+    MOE_MASK_CASE(5, 4) MOE_MASK_CASE(6, 4) MOE_MASK_CASE(7, 4) MOE_MASK_CASE(8, 4)
+    MOE_MASK_CASE(1, 1) MOE_MASK_CASE(2, 1) MOE_MASK_CASE(3, 1) MOE_MASK_CASE(5, 1)
+    MOE_MASK_CASE(6, 1) MOE_MASK_CASE(7, 1) MOE_MASK_CASE(9, 1) MOE_MASK_CASE(10, 1)
+    MOE_MASK_CASE(11, 1) MOE_MASK_CASE(13, 1) MOE_MASK_CASE(14, 1) MOE_MASK_CASE(15, 1)
+    MOE_MASK_CASE(17, 1) MOE_MASK_CASE(18, 1) MOE_MASK_CASE(19, 1) MOE_MASK_CASE(21, 1)
+    MOE_MASK_CASE(22, 1) MOE_MASK_CASE(23, 1) MOE_MASK_CASE(25, 1) MOE_MASK_CASE(26, 1)
+    MOE_MASK_CASE(27, 1) MOE_MASK_CASE(29, 1) MOE_MASK_CASE(30, 1) MOE_MASK_CASE(31, 1)
     MOE_MASK_CASE(5, 8) MOE_MASK_CASE(6, 8) MOE_MASK_CASE(7, 8) MOE_MASK_CASE(8, 8)
     MOE_MASK_CASE(9, 8) MOE_MASK_CASE(10, 8) MOE_MASK_CASE(11, 8) MOE_MASK_CASE(12, 8)
     MOE_MASK_CASE(13, 8) MOE_MASK_CASE(14, 8) MOE_MASK_CASE(15, 8) MOE_MASK_CASE(16, 8)
