@@ -15,9 +15,11 @@ The weights are cycled over enough device copies, and the token batches
 over as many seeded batches, that >= 1 GB is touched between reuses of a
 copy, so the ~256 MB Infinity Cache cannot serve the weight stream.
 Per-kernel durations come from HIP events the library records around each
-of its launches, on the launch stream; the dominant kernel's roofline uses
-its algorithmic bytes per launch.  The CPU oracle is timed on a bounded
-sample of the same workload on the host cores as a reported baseline.
+of its launches, on the launch stream, in eager steps queued ahead of the
+GPU (so each event pair spans its kernel, not the host's launch latency);
+the dominant kernel's roofline uses its algorithmic bytes per launch.  The
+CPU oracle is timed on a bounded sample of the same workload on the host
+cores as a reported baseline.
 
     python bench.py [--steps K] [--warmup W] [--batch T] [--sweep 1,4,16]
 
@@ -222,10 +224,13 @@ def time_graphs(wl, steps, warmup):
     return (time.perf_counter() - t0) / steps
 
 
-def time_kernels(wl, steps):
+def time_kernels(wl, steps, chunk=10):
     """Per-kernel durations from HIP events the library records around each
-    of its launches, on the launch stream (eager steps; every event pair
-    also spans the kernel's dispatch)."""
+    of its launches, on the launch stream (eager steps).  Each chunk of
+    steps is queued behind a short GPU spin on the same stream, so the host
+    has enqueued the whole chunk before the GPU reaches it: the event pairs
+    then run back to back with their kernels instead of waiting for the
+    host's next launch, and span little more than the kernel itself."""
     from sparse_moe_expert_route_amd import binding as B
     torch = wl.torch
     if steps <= 0:
@@ -234,10 +239,14 @@ def time_kernels(wl, steps):
     for i in range(wl.L):                 # warm the eager path
         wl.step(i)
     torch.cuda.synchronize()
+    spin = getattr(torch.cuda, "_sleep", None)
     with timer:
-        for i in range(steps):
-            wl.step(i)
-    torch.cuda.synchronize()
+        for c0 in range(0, steps, chunk):
+            if spin is not None:
+                spin(10_000_000)          # ~4 ms: longer than the host needs to enqueue a chunk
+            for i in range(c0, min(steps, c0 + chunk)):
+                wl.step(i)
+            torch.cuda.synchronize()
     d = timer.durations()
     timer.close()
     return {k: dict(n=len(v), avg_us=1e3 * sum(v) / len(v), per_step_us=1e3 * sum(v) / steps)
