@@ -236,6 +236,16 @@ moe_status moe_timer_attach(hipEvent_t *events, int32_t *stages, int32_t capacit
 /* Detach; returns the number of launches recorded since attaching. */
 int32_t moe_timer_detach(void);
 
+/* Measurement helper, not part of the layer: one plain streaming read of
+ * `bytes` of device memory at `src` (16-byte aligned, bytes a positive
+ * multiple of 16), with non-temporal 16-byte loads, 16384 blocks of 256
+ * threads (enough loads in flight to saturate HBM).  Timing it gives the practical HBM read peak that the layer's
+ * kernels are compared with.  Block b writes the XOR of its chunks to
+ * sink[4b .. 4b+3]: `sink` holds MOE_STREAM_READ_SINK_WORDS uint32 of device
+ * memory.  Errors as for the other calls; nothing is allocated. */
+#define MOE_STREAM_READ_SINK_WORDS 65536
+moe_status moe_stream_read(const void *src, size_t bytes, uint32_t *sink, hipStream_t stream);
+
 /* Static name of a status code. */
 const char *moe_status_string(moe_status s);
 

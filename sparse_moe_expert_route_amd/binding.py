@@ -55,6 +55,7 @@ _SIGS = {
     "moe_select_path": (_I32, [_PD, _I32, _I32]),
     "moe_timer_attach": (_I32, [ctypes.POINTER(_V), ctypes.POINTER(_I32), _I32]),
     "moe_timer_detach": (_I32, []),
+    "moe_stream_read": (_I32, [_V, _SZ, _V, _V]),
     "moe_status_string": (ctypes.c_char_p, [_I32]),
     "moe_last_error": (ctypes.c_char_p, []),
     "moe_version": (ctypes.c_char_p, []),
@@ -220,6 +221,17 @@ def moe_last_error() -> str:
 
 def moe_version() -> str:
     return lib().moe_version().decode()
+
+
+STREAM_READ_SINK_WORDS = 65536
+
+
+def moe_stream_read(buf, sink, stream=None) -> None:
+    """Measurement helper: one streaming read of every byte of `buf` (device
+    tensor); `sink` is a device int32 tensor of STREAM_READ_SINK_WORDS."""
+    assert sink.numel() * sink.element_size() >= 4 * STREAM_READ_SINK_WORDS
+    _check(lib().moe_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
+                                 _stream(stream)))
 
 
 # ------------------------------------------------------------ per-kernel timing

@@ -334,6 +334,16 @@ int32_t moe_timer_detach(void) {
   return n;
 }
 
+moe_status moe_stream_read(const void *src, size_t bytes, uint32_t *sink, hipStream_t stream) {
+  g_err[0] = 0;
+  if (!src || !sink) return fail(MOE_ERR_INVALID_ARG, "stream_read needs src and sink");
+  if (bytes == 0 || bytes % 16) return fail(MOE_ERR_INVALID_ARG, "bytes must be a positive multiple of 16");
+  if (!aligned16(src) || !aligned16(sink)) return fail(MOE_ERR_MISALIGNED, "src and sink must be 16-byte aligned");
+  const hipError_t e = moe::launch_stream_read(src, bytes, sink, MOE_STREAM_READ_SINK_WORDS / 4, stream);
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return MOE_OK;
+}
+
 const char *moe_last_error(void) { return g_err; }
 
 const char *moe_version(void) { return "moe_mi355x 0.1 (gfx950)"; }

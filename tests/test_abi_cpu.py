@@ -157,6 +157,16 @@ def test_pack_validation():
     assert L.moe_unpack_gate_up(ctypes.byref(_desc(hidden=96)), FAKE, FAKE + nbytes, None) == UNS
 
 
+def test_stream_read_validation():
+    S = L.moe_stream_read
+    assert S(None, 64, FAKE, None) == INV
+    assert S(FAKE, 64, None, None) == INV
+    assert S(FAKE, 0, FAKE, None) == INV
+    assert S(FAKE, 72, FAKE, None) == INV
+    assert S(MIS, 64, FAKE, None) == MISA
+    assert S(FAKE, 64, MIS, None) == MISA
+
+
 def test_route_validation():
     d = _desc()
     assert _route(None, 4) == INV

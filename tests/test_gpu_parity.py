@@ -181,6 +181,20 @@ def test_deterministic_and_sparse_equals_dense():
     assert rel_l2(c["y"], a["y"]) < 1e-2
 
 
+@pytest.mark.parametrize("nbytes", [16, 4096 * 16 + 48, 64 << 20])
+def test_stream_read_folds_every_chunk(nbytes):
+    # the calibration read touches every 16-byte chunk exactly once: the XOR
+    # of all block folds equals the XOR of all chunks
+    rng = np.random.default_rng(nbytes)
+    host = rng.integers(0, 2**32, size=nbytes // 4, dtype=np.uint32)
+    buf = torch.from_numpy(host.view(np.int32)).cuda()
+    sink = torch.zeros(B.STREAM_READ_SINK_WORDS, dtype=torch.int32, device="cuda")
+    B.moe_stream_read(buf, sink)
+    got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32).reshape(-1, 4), axis=0)
+    want = np.bitwise_xor.reduce(host.reshape(-1, 4), axis=0)
+    np.testing.assert_array_equal(got, want)
+
+
 def test_unkept_rows_are_never_read():
     # Poison every W_d row no pair keeps with NaN: the sparse path must give
     # the same bits (a load-and-multiply by zero would give NaN).
