@@ -28,6 +28,19 @@ The sparse down projection reaches exactly (up to rounding order) the dense
 down projection of the masked activation, so this file writes that
 definition out directly and touches only kept W_d rows.
 
+Gate-score variant (score="gate"), the page's own split (technical summary,
+Methodology, vLLM implementation: the gate projection alone runs densely
+and produces the activation scores; the fused up-down projection then
+gathers only the active neurons' weights):
+
+    s      = silu(W_g^e x_t)                      dense gate, the scores
+    K_t,e  = the k_keep neurons of largest |s_j| (ties: lower j)
+    h_j    = s_j * (W_u^e[j, :] . x_t)   for j in K_t,e only
+    y_t    = as above, with this h on K_t,e
+
+Only kept W_u and W_d rows are read.  With k_keep = d_ff both variants are
+the dense SwiGLU MoE.
+
 Every function below is pinned by tests (tests/test_oracle_pins.py) against
 closed forms, brute force, library routines or invariants; none is
 "parity unpinned".
@@ -148,6 +161,27 @@ def expert_activation(x_t: np.ndarray, w_gate_e: np.ndarray,
     return silu(g) * u
 
 
+def gate_scores(x_t: np.ndarray, w_gate_e: np.ndarray) -> np.ndarray:
+    """s = silu(W_g x) for one token and one expert  ->  [d_ff].
+
+    In the page's own split only the gate projection runs densely; its
+    activation is the score that decides which neurons stay (technical
+    summary, Methodology: vLLM implementation, gate projection)."""
+    return silu(w_gate_e @ x_t)
+
+
+def sparse_up(x_t: np.ndarray, s: np.ndarray, keep: np.ndarray,
+              w_up_e: np.ndarray) -> np.ndarray:
+    """h_j = s_j * (W_u[j, :] . x_t) for the kept neurons only  ->  [len(keep)].
+
+    The up projection gathers only the active neurons' rows (technical
+    summary, Methodology: fused up-down projection gathers only the active
+    neurons' weights); the rest of W_u is never read."""
+    if keep.size == 0:
+        return np.zeros(0, dtype=np.float64)
+    return s[keep] * (w_up_e[keep, :] @ x_t)
+
+
 def kept_neurons(h: np.ndarray, k: int) -> np.ndarray:
     """The k neurons of largest |h| (ties: lower index), ascending.
 
@@ -183,20 +217,40 @@ class LayerResult:
     weights: np.ndarray                 # [T, top_k]
     logits: np.ndarray                  # [T, E]
     probs: np.ndarray                   # [T, E]
-    h: Dict[Tuple[int, int], np.ndarray] = field(default_factory=dict)        # (t, slot) -> [d_ff]
+    h: Dict[Tuple[int, int], np.ndarray] = field(default_factory=dict)        # (t, slot) -> scores [d_ff]
     keep: Dict[Tuple[int, int], np.ndarray] = field(default_factory=dict)     # (t, slot) -> idx
     h_shared: Dict[Tuple[int, int], np.ndarray] = field(default_factory=dict)     # (t, j)
     keep_shared: Dict[Tuple[int, int], np.ndarray] = field(default_factory=dict)  # (t, j)
 
 
+def _pair_output(x_t, wg, wu, wd, k_keep, forced, score):
+    """One (token, expert) pair: (its contribution before the routing
+    weight [H], the selection scores [d_ff], the kept set)."""
+    if score == "swiglu":
+        h = expert_activation(x_t, wg, wu)
+        keep = (np.asarray(forced, dtype=np.int64) if forced is not None
+                else kept_neurons(h, k_keep))
+        return sparse_down(h, keep, wd), h, keep
+    if score == "gate":
+        sc = gate_scores(x_t, wg)
+        keep = (np.asarray(forced, dtype=np.int64) if forced is not None
+                else kept_neurons(sc, k_keep))
+        h = np.zeros_like(sc)
+        h[keep] = sparse_up(x_t, sc, keep, wu)
+        return sparse_down(h, keep, wd), sc, keep
+    raise ValueError(f"unknown score {score!r}")
+
+
 def routed_experts(x, ids, weights, w_gate, w_up, w_down, k_keep, dtype,
-                   forced_keep=None, keep_h=True):
+                   forced_keep=None, keep_h=True, score="swiglu"):
     """Routed contribution sum_{slot} w * sum_{j in K} h_j W_d^e[j, :].
 
     Pairs are visited expert by expert so each expert's weights are
     converted once.  ``forced_keep[(t, slot)]`` replaces the computed kept
     set (used when a tested implementation's selection differs only on
-    scores inside the comparison window).  Returns (y [T, H], h, keep)."""
+    scores inside the comparison window).  Returns (y [T, H], scores,
+    keep); the scores are h itself for score="swiglu" and silu(W_g x) for
+    score="gate"."""
     T, H = x.shape
     y = np.zeros((T, H), dtype=np.float64)
     hs, keeps = {}, {}
@@ -207,19 +261,17 @@ def routed_experts(x, ids, weights, w_gate, w_up, w_down, k_keep, dtype,
     for e in sorted(by_expert):
         wg, wu, wd = (to_f64(w[e], dtype) for w in (w_gate, w_up, w_down))
         for (t, s) in by_expert[e]:
-            h = expert_activation(x[t], wg, wu)
-            keep = (np.asarray(forced_keep[(t, s)], dtype=np.int64)
-                    if forced_keep is not None and (t, s) in forced_keep
-                    else kept_neurons(h, k_keep))
-            y[t] += weights[t, s] * sparse_down(h, keep, wd)
+            forced = forced_keep.get((t, s)) if forced_keep is not None else None
+            out, sc, keep = _pair_output(x[t], wg, wu, wd, k_keep, forced, score)
+            y[t] += weights[t, s] * out
             if keep_h:
-                hs[(t, s)] = h
+                hs[(t, s)] = sc
             keeps[(t, s)] = keep
     return y, hs, keeps
 
 
 def shared_experts(x, w_gate, w_up, w_down, n_shared, k_keep, dtype,
-                   forced_keep=None, keep_h=True):
+                   forced_keep=None, keep_h=True, score="swiglu"):
     """Always-on shared experts: every token, weight 1, each expert with its
     own per-(token, expert) mask of k_keep neurons.
 
@@ -232,13 +284,11 @@ def shared_experts(x, w_gate, w_up, w_down, n_shared, k_keep, dtype,
     for j in range(n_shared):
         wg, wu, wd = (to_f64(w[j], dtype) for w in (w_gate, w_up, w_down))
         for t in range(T):
-            h = expert_activation(x[t], wg, wu)
-            keep = (np.asarray(forced_keep[(t, j)], dtype=np.int64)
-                    if forced_keep is not None and (t, j) in forced_keep
-                    else kept_neurons(h, k_keep))
-            y[t] += sparse_down(h, keep, wd)
+            forced = forced_keep.get((t, j)) if forced_keep is not None else None
+            out, sc, keep = _pair_output(x[t], wg, wu, wd, k_keep, forced, score)
+            y[t] += out
             if keep_h:
-                hs[(t, j)] = h
+                hs[(t, j)] = sc
             keeps[(t, j)] = keep
     return y, hs, keeps
 
@@ -249,7 +299,7 @@ def moe_layer(x, w_router, bias, w_gate, w_up, w_down, *, top_k: int,
               forced_ids: Optional[np.ndarray] = None,
               forced_keep: Optional[dict] = None,
               forced_keep_shared: Optional[dict] = None,
-              keep_h: bool = True) -> LayerResult:
+              keep_h: bool = True, score: str = "swiglu") -> LayerResult:
     """The whole layer for a token batch.
 
     x [T, H], w_router [E, H] and the expert weights (indexable by expert,
@@ -260,7 +310,11 @@ def moe_layer(x, w_router, bias, w_gate, w_up, w_down, *, top_k: int,
     ``forced_ids`` replaces the routed expert sets (slot order as given);
     the weights are then the softmax probabilities of those experts, so a
     tested implementation whose selection differs from this one only on
-    logits inside the comparison window can be scored exactly."""
+    logits inside the comparison window can be scored exactly.
+
+    ``score`` is "swiglu" (mask by |silu(g) * u|, gate and up dense) or
+    "gate" (the page's own split: mask by |silu(g)|, up and down gathered
+    for the kept neurons only).  LayerResult.h holds the selection scores."""
     xf = to_f64(x, dtype)
     _check_finite("x", xf)
     wr = to_f64(w_router, dtype)
@@ -271,7 +325,7 @@ def moe_layer(x, w_router, bias, w_gate, w_up, w_down, *, top_k: int,
         if norm_topk:
             w = w / np.sum(w, axis=1, keepdims=True)
     y_r, hs, keeps = routed_experts(xf, ids, w, w_gate, w_up, w_down, k_keep,
-                                    dtype, forced_keep, keep_h)
+                                    dtype, forced_keep, keep_h, score)
     T, H = xf.shape
     y_s = np.zeros((T, H))
     hs_s, keeps_s = {}, {}
@@ -279,7 +333,7 @@ def moe_layer(x, w_router, bias, w_gate, w_up, w_down, *, top_k: int,
         n_sh = len(shared[0])
         ks = k_keep_shared if k_keep_shared is not None else shared[0][0].shape[0]
         y_s, hs_s, keeps_s = shared_experts(xf, shared[0], shared[1], shared[2],
-                                            n_sh, ks, dtype, forced_keep_shared, keep_h)
+                                            n_sh, ks, dtype, forced_keep_shared, keep_h, score)
     return LayerResult(y=y_r + y_s, y_routed=y_r, y_shared=y_s, ids=ids, weights=w,
                        logits=l, probs=p, h=hs, keep=keeps, h_shared=hs_s,
                        keep_shared=keeps_s)

@@ -198,7 +198,7 @@ def test_worked_example(case):
     r = oracle.moe_layer(f32(case["x"]), f32(case["w_router"]), bias,
                          f32(case["w_gate"]), f32(case["w_up"]), f32(case["w_down"]),
                          top_k=case["top_k"], norm_topk=case["norm_topk"],
-                         k_keep=case["k_keep"], dtype="f32")
+                         k_keep=case["k_keep"], dtype="f32", score=case.get("score", "swiglu"))
     np.testing.assert_array_equal(r.ids, case["expect_ids"])
     want = np.array([[_eval_expr(s) for s in row] for row in case["expect"]])
     np.testing.assert_allclose(r.y, want, rtol=1e-14, atol=1e-15)
@@ -219,8 +219,10 @@ def _run(L, top_k, norm, k, **kw):
                             top_k=top_k, norm_topk=norm, k_keep=k, dtype="f32", **kw)
 
 
-def _brute_layer(L, top_k, norm, k):
-    """Scalar float64 loops; mask by brute-force subset enumeration."""
+def _brute_layer(L, top_k, norm, k, score="swiglu"):
+    """Scalar float64 loops; mask by brute-force subset enumeration.  With
+    score="gate" neurons are ranked by |silu(g)| alone and u is formed for
+    the kept neurons only."""
     x, wr, b, wg, wu, wd = (np.asarray(L[n], dtype=np.float64) for n in ("x", "wr", "bias", "wg", "wu", "wd"))
     T, H = x.shape
     E, d, _ = wg.shape
@@ -234,13 +236,15 @@ def _brute_layer(L, top_k, norm, k):
         tot = sum(p.values())
         for e in sel:
             w = p[e] / tot if norm else p[e]
-            h = []
+            h, sg = [], []
             for j in range(d):
                 g = sum(wg[e, j, i] * x[t, i] for i in range(H))
                 u = sum(wu[e, j, i] * x[t, i] for i in range(H))
-                h.append(g / (1 + math.exp(-g)) * u)
+                sg.append(g / (1 + math.exp(-g)))
+                h.append(sg[-1] * u)
+            rank = h if score == "swiglu" else sg
             K = next(c for c in itertools.combinations(range(d), k)
-                     if _dominates([abs(v) for v in h], c, d))
+                     if _dominates([abs(v) for v in rank], c, d))
             for j in K:
                 for i in range(H):
                     y[t][i] += w * h[j] * wd[e, j, i]
@@ -253,6 +257,60 @@ def test_layer_brute_force(seed, top_k, norm, k):
     L = _rand_layer(seed, T=2, H=8, E=5, d=8 if k != 12 else 12)
     r = _run(L, top_k, norm, k)
     np.testing.assert_allclose(r.y, _brute_layer(L, top_k, norm, k), rtol=1e-11, atol=1e-13)
+
+
+@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("top_k,norm,k", [(2, False, 3), (3, True, 1), (1, True, 12), (2, False, 0)])
+def test_gate_score_layer_brute_force(seed, top_k, norm, k):
+    L = _rand_layer(100 + seed, T=2, H=8, E=5, d=8 if k != 12 else 12)
+    r = _run(L, top_k, norm, k, score="gate")
+    np.testing.assert_allclose(r.y, _brute_layer(L, top_k, norm, k, score="gate"),
+                               rtol=1e-11, atol=1e-13)
+
+
+def test_gate_score_mask_ignores_up_projection():
+    # the gate alone ranks the neurons: a new W_u changes no kept set (while
+    # it does change the SwiGLU-scored sets), and y scales with W_u
+    L = _rand_layer(21, T=4, H=32, E=4, d=24)
+    wu2 = _rand_layer(22, T=4, H=32, E=4, d=24)["wu"]
+    a = _run(L, 2, False, 5, score="gate")
+    b = _run(dict(L, wu=wu2), 2, False, 5, score="gate")
+    assert all(np.array_equal(a.keep[key], b.keep[key]) for key in a.keep)
+    sa = _run(L, 2, False, 5)
+    sb = _run(dict(L, wu=wu2), 2, False, 5)
+    assert any(not np.array_equal(sa.keep[key], sb.keep[key]) for key in sa.keep)
+    assert any(not np.array_equal(a.keep[key], sa.keep[key]) for key in a.keep)
+    c = _run(dict(L, wu=L["wu"] * 2.0), 2, False, 5, score="gate")
+    np.testing.assert_allclose(c.y, 2.0 * a.y, rtol=1e-14)
+    # the scores it reports are silu(W_g x)
+    for (t, s), sc in a.h.items():
+        e = int(a.ids[t, s])
+        g = L["wg"][e].astype(np.float64) @ L["x"][t].astype(np.float64)
+        np.testing.assert_allclose(sc, scipy.special.expit(g) * g, rtol=1e-13, atol=1e-15)
+
+
+def test_gate_score_reads_only_kept_up_and_down_rows():
+    L = _rand_layer(23, T=4, H=32, E=8, d=40)
+    r = _run(L, 2, False, 4, score="gate")
+    wu, wd = L["wu"].copy(), L["wd"].copy()
+    used = {}
+    for (t, s), keep in r.keep.items():
+        used.setdefault(int(r.ids[t, s]), set()).update(int(j) for j in keep)
+    for e in range(wd.shape[0]):
+        for j in range(wd.shape[1]):
+            if j not in used.get(e, ()):
+                wu[e, j] = np.nan
+                wd[e, j] = np.nan
+    r2 = _run(dict(L, wu=wu, wd=wd), 2, False, 4, score="gate")
+    assert np.all(np.isfinite(r2.y))
+    np.testing.assert_array_equal(r2.y, r.y)
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_gate_score_at_sparsity_zero_is_dense_moe(seed):
+    L = _rand_layer(30 + seed, T=4, H=32, E=8, d=24)
+    r = _run(L, 2, True, 24, score="gate")
+    np.testing.assert_allclose(r.y, _torch_dense_moe(L, 2, True), rtol=1e-12, atol=1e-14)
 
 
 def _torch_dense_moe(L, top_k, norm):
