@@ -173,6 +173,34 @@ moe_status moe_expert_ffn_dense(const moe_desc *d, int32_t T, int32_t k_keep, co
                                 size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * moe_expert_ffn_sparse_updown -- the page's own split of the sparse path
+ * (technical summary, Methodology, vLLM implementation: the gate projection
+ * alone runs densely and yields the activation scores; the fused up-down
+ * projection gathers only the active neurons' weights):
+ *
+ *   s      = silu(W_g^e x_t)                     dense, every pair
+ *   K      = the k_keep neurons of largest |s_j| (ties: lower j)
+ *   h_j    = s_j * (W_u^e[j, :] . x_t)            j in K only
+ *   y_t   (+)= sum over the token's experts (slot order) of w * sum_{j in K} h_j W_d^e[j, :]
+ *
+ * A different mask from moe_expert_ffn_sparse's (which scores |silu(g) * u|
+ * with gate and up both dense); with k_keep == d_ff both are the dense
+ * SwiGLU MoE.  Reads half the dense bytes of moe_expert_ffn_sparse plus the
+ * kept up rows.  Layouts differ in one place: w_gate is packed by
+ * moe_pack_gate_up, but w_up is the plain [E, d_ff, H] neuron-major tensor
+ * (like w_down), since its kept rows are gathered.  Other parameters,
+ * outputs and errors as moe_expert_ffn_sparse (active_idx_out: the kept ids
+ * by gate score); workspace: moe_ffn_workspace_size(d, T, k_keep,
+ * MOE_PATH_SPARSE).  There is no dense form of this variant.
+ */
+moe_status moe_expert_ffn_sparse_updown(const moe_desc *d, int32_t T, int32_t k_keep,
+                                        const void *x, const void *w_gate, const void *w_up,
+                                        const void *w_down, const moe_routing *routing, float *y,
+                                        int32_t accumulate, int32_t *active_idx_out,
+                                        void *workspace, size_t workspace_bytes,
+                                        hipStream_t stream);
+
+/*
  * moe_pack_gate_up -- rearrange one gate or up tensor [E, d_ff, H] from
  * row-major into the packed layout the FFN calls read: for each expert e,
  * neuron tile nt (16 neurons) and k-step ks (KS = 32 bf16 or 16 fp32
@@ -221,7 +249,8 @@ typedef enum {
   MOE_STAGE_DOWN_DENSE = 6,
   MOE_STAGE_COMBINE = 7,
   MOE_STAGE_ZERO = 8,
-  MOE_N_STAGES = 9
+  MOE_STAGE_UP_ROWS = 9,
+  MOE_N_STAGES = 10
 } moe_stage;
 
 /* While attached, every kernel the library launches from this thread is

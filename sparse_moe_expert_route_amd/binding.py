@@ -47,6 +47,7 @@ _SIGS = {
     "moe_route": (_I32, [_PD, _I32, _V, _V, _V, _PR, _V, _SZ, _V]),
     "moe_expert_ffn_sparse": (_I32, [_PD, _I32, _I32, _V, _V, _V, _V, _PR, _V, _I32, _V, _V, _SZ, _V]),
     "moe_expert_ffn_dense": (_I32, [_PD, _I32, _I32, _V, _V, _V, _V, _PR, _V, _I32, _V, _V, _SZ, _V]),
+    "moe_expert_ffn_sparse_updown": (_I32, [_PD, _I32, _I32, _V, _V, _V, _V, _PR, _V, _I32, _V, _V, _SZ, _V]),
     "moe_pack_gate_up": (_I32, [_PD, _V, _V, _V]),
     "moe_unpack_gate_up": (_I32, [_PD, _V, _V, _V]),
     "moe_route_workspace_size": (_SZ, [_PD, _I32]),
@@ -179,6 +180,13 @@ def moe_expert_ffn_dense(desc, T, k_keep, x, w_gate, w_up, w_down, routing, y, a
          accumulate, active_idx_out, workspace, stream)
 
 
+def moe_expert_ffn_sparse_updown(desc, T, k_keep, x, w_gate, w_up, w_down, routing, y,
+                                 accumulate=0, active_idx_out=None, workspace=None, stream=None):
+    """The gate-score split: w_gate packed, w_up and w_down row-major."""
+    _ffn(lib().moe_expert_ffn_sparse_updown, desc, T, k_keep, x, w_gate, w_up, w_down, routing,
+         y, accumulate, active_idx_out, workspace, stream)
+
+
 def moe_pack_gate_up(desc: MoeDesc, src, dst=None, stream=None):
     """Pack a row-major gate or up tensor [E, d_ff, H]; returns dst."""
     import torch
@@ -242,7 +250,7 @@ class StageTimer:
     plumbing for measurement; events come from the process's HIP runtime."""
 
     STAGES = ["router_logits", "router_topk", "route_group", "gateup_swiglu", "neuron_topk",
-              "down_rows", "down_dense", "combine", "zero"]
+              "down_rows", "down_dense", "combine", "zero", "up_rows"]
 
     def __init__(self, capacity: int):
         lib()

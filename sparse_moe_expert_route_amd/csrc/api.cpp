@@ -101,7 +101,8 @@ FfnLayout ffn_layout(const moe_desc *d, int32_t T, int32_t k, moe_path path) {
   return L;
 }
 
-moe_status run_ffn(moe_path path, const moe_desc *d, int32_t T, int32_t k_keep, const void *x,
+// updown: the gate-score split (sparse path only), see moe_expert_ffn_sparse_updown.
+moe_status run_ffn(moe_path path, bool updown, const moe_desc *d, int32_t T, int32_t k_keep, const void *x,
                    const void *w_gate, const void *w_up, const void *w_down,
                    const moe_routing *routing, float *y, int32_t accumulate,
                    int32_t *active_idx_out, void *workspace, size_t workspace_bytes,
@@ -169,7 +170,8 @@ moe_status run_ffn(moe_path path, const moe_desc *d, int32_t T, int32_t k_keep, 
   a.partial = reinterpret_cast<float *>(ws + L.partial);
   a.hm = path == MOE_PATH_DENSE ? static_cast<void *>(ws + L.hm) : nullptr;
   const hipError_t e =
-      path == MOE_PATH_SPARSE ? moe::launch_ffn_sparse(a, stream) : moe::launch_ffn_dense(a, stream);
+      updown ? moe::launch_ffn_updown(a, stream)
+             : path == MOE_PATH_SPARSE ? moe::launch_ffn_sparse(a, stream) : moe::launch_ffn_dense(a, stream);
   if (e != hipSuccess) return fail(MOE_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return MOE_OK;
 }
@@ -227,7 +229,7 @@ moe_status moe_expert_ffn_sparse(const moe_desc *d, int32_t T, int32_t k_keep, c
                                  const moe_routing *routing, float *y, int32_t accumulate,
                                  int32_t *active_idx_out, void *workspace,
                                  size_t workspace_bytes, hipStream_t stream) {
-  return run_ffn(MOE_PATH_SPARSE, d, T, k_keep, x, w_gate, w_up, w_down, routing, y, accumulate,
+  return run_ffn(MOE_PATH_SPARSE, false, d, T, k_keep, x, w_gate, w_up, w_down, routing, y, accumulate,
                  active_idx_out, workspace, workspace_bytes, stream);
 }
 
@@ -236,8 +238,18 @@ moe_status moe_expert_ffn_dense(const moe_desc *d, int32_t T, int32_t k_keep, co
                                 const moe_routing *routing, float *y, int32_t accumulate,
                                 int32_t *active_idx_out, void *workspace,
                                 size_t workspace_bytes, hipStream_t stream) {
-  return run_ffn(MOE_PATH_DENSE, d, T, k_keep, x, w_gate, w_up, w_down, routing, y, accumulate,
+  return run_ffn(MOE_PATH_DENSE, false, d, T, k_keep, x, w_gate, w_up, w_down, routing, y, accumulate,
                  active_idx_out, workspace, workspace_bytes, stream);
+}
+
+moe_status moe_expert_ffn_sparse_updown(const moe_desc *d, int32_t T, int32_t k_keep,
+                                        const void *x, const void *w_gate, const void *w_up,
+                                        const void *w_down, const moe_routing *routing, float *y,
+                                        int32_t accumulate, int32_t *active_idx_out,
+                                        void *workspace, size_t workspace_bytes,
+                                        hipStream_t stream) {
+  return run_ffn(MOE_PATH_SPARSE, true, d, T, k_keep, x, w_gate, w_up, w_down, routing, y,
+                 accumulate, active_idx_out, workspace, workspace_bytes, stream);
 }
 
 static moe_status pack_impl(const moe_desc *d, const void *src, void *dst, int unpack,

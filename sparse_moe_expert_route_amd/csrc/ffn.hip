@@ -74,7 +74,7 @@ __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 // keeps 16x16 MFMA accumulators for gate and up for MT token tiles; weights
 // are loaded once, token rows (16 B per lane) come from L2.  The wave
 // partials meet in LDS, where h = silu(g) * u is formed and written per pair.
-template <bool BF16, int MT, int W>
+template <bool BF16, int MT, int W, bool GO = false>
 __global__ __launch_bounds__(64 * W, MT == 1 ? 8 : 1) void gateup_swiglu_kernel(const void *__restrict__ xv,
                                                             const void *__restrict__ wgv,
                                                             const void *__restrict__ wuv,
@@ -125,7 +125,7 @@ __global__ __launch_bounds__(64 * W, MT == 1 ? 8 : 1) void gateup_swiglu_kernel(
         const int ks = s + W * u;
         if (ks < nsteps) {
           ag[u] = ld16_nt(wg + (size_t)ks * 512);
-          au[u] = ld16_nt(wu + (size_t)ks * 512);
+          if (!GO) au[u] = ld16_nt(wu + (size_t)ks * 512);
         }
       }
 #pragma unroll
@@ -138,7 +138,7 @@ __global__ __launch_bounds__(64 * W, MT == 1 ? 8 : 1) void gateup_swiglu_kernel(
             if (tl < ntiles) {
               const u32x4 b = xval[tl] ? ld16(x + xoff[tl] + k) : u32x4{0, 0, 0, 0};
               accg[tl] = mfma_bf16(ag[u], b, accg[tl]);
-              accu[tl] = mfma_bf16(au[u], b, accu[tl]);
+              if (!GO) accu[tl] = mfma_bf16(au[u], b, accu[tl]);
             }
           }
         }
@@ -156,7 +156,7 @@ __global__ __launch_bounds__(64 * W, MT == 1 ? 8 : 1) void gateup_swiglu_kernel(
         const int ks = s + W * u;
         if (ks < nsteps) {
           ag[u] = ld16_nt(wg + (size_t)ks * 256);
-          au[u] = ld16_nt(wu + (size_t)ks * 256);
+          if (!GO) au[u] = ld16_nt(wu + (size_t)ks * 256);
         }
       }
 #pragma unroll
@@ -171,7 +171,7 @@ __global__ __launch_bounds__(64 * W, MT == 1 ? 8 : 1) void gateup_swiglu_kernel(
 #pragma unroll
               for (int j = 0; j < 4; ++j) {
                 accg[tl] = mfma_f32(__uint_as_float(ag[u][j]), __uint_as_float(b[j]), accg[tl]);
-                accu[tl] = mfma_f32(__uint_as_float(au[u][j]), __uint_as_float(b[j]), accu[tl]);
+                if (!GO) accu[tl] = mfma_f32(__uint_as_float(au[u][j]), __uint_as_float(b[j]), accu[tl]);
               }
             }
           }
@@ -186,7 +186,7 @@ __global__ __launch_bounds__(64 * W, MT == 1 ? 8 : 1) void gateup_swiglu_kernel(
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         red[wid][0][tl][rr][lane] = accg[tl][rr];
-        red[wid][1][tl][rr][lane] = accu[tl][rr];
+        if (!GO) red[wid][1][tl][rr][lane] = accu[tl][rr];
       }
     }
   }
@@ -199,11 +199,11 @@ __global__ __launch_bounds__(64 * W, MT == 1 ? 8 : 1) void gateup_swiglu_kernel(
 #pragma unroll
       for (int w = 0; w < W; ++w) {  // wave partials in fixed order
         gs += red[w][0][tl][rr][ln];
-        us += red[w][1][tl][rr][ln];
+        if (!GO) us += red[w][1][tl][rr][ln];
       }
       const int neuron = row0 + 4 * (ln >> 4) + rr;
       const int p = rv.pair_at(q0 + c);
-      hout[(size_t)p * d_ff + neuron] = silu(gs) * us;
+      hout[(size_t)p * d_ff + neuron] = GO ? silu(gs) : silu(gs) * us;
     }
   }
 }
@@ -222,7 +222,7 @@ __global__ __launch_bounds__(64 * W, MT == 1 ? 8 : 1) void gateup_swiglu_kernel(
 constexpr int kGemmTok = 128;               // tokens per work item (8 MFMA token tiles)
 constexpr int kGemmRowB = 128 + 16;         // LDS bytes per staged token row (+ pad)
 
-template <bool BF16>
+template <bool BF16, bool GO = false>
 __global__ __launch_bounds__(256, 2) void gateup_gemm_kernel(const void *__restrict__ xv,
                                                              const void *__restrict__ wgv,
                                                              const void *__restrict__ wuv,
@@ -266,7 +266,7 @@ __global__ __launch_bounds__(256, 2) void gateup_gemm_kernel(const void *__restr
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
     ag[k] = ld16_nt(wg + (size_t)k * 1024);
-    au[k] = ld16_nt(wu + (size_t)k * 1024);
+    if (!GO) au[k] = ld16_nt(wu + (size_t)k * 1024);
   }
   __syncthreads();
 
@@ -282,7 +282,7 @@ __global__ __launch_bounds__(256, 2) void gateup_gemm_kernel(const void *__restr
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
         ng[k] = ld16_nt(wg + (size_t)(2 * it + 2 + k) * 1024);
-        nu[k] = ld16_nt(wu + (size_t)(2 * it + 2 + k) * 1024);
+        if (!GO) nu[k] = ld16_nt(wu + (size_t)(2 * it + 2 + k) * 1024);
       }
     }
 #pragma unroll
@@ -294,12 +294,12 @@ __global__ __launch_bounds__(256, 2) void gateup_gemm_kernel(const void *__restr
               &xs[cur][(tl * 16 + r) * kGemmRowB + k * 64 + g * 16]);
           if (BF16) {
             accg[tl] = mfma_bf16(ag[k], b, accg[tl]);
-            accu[tl] = mfma_bf16(au[k], b, accu[tl]);
+            if (!GO) accu[tl] = mfma_bf16(au[k], b, accu[tl]);
           } else {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
               accg[tl] = mfma_f32(__uint_as_float(ag[k][j]), __uint_as_float(b[j]), accg[tl]);
-              accu[tl] = mfma_f32(__uint_as_float(au[k][j]), __uint_as_float(b[j]), accu[tl]);
+              if (!GO) accu[tl] = mfma_f32(__uint_as_float(au[k][j]), __uint_as_float(b[j]), accu[tl]);
             }
           }
         }
@@ -310,7 +310,7 @@ __global__ __launch_bounds__(256, 2) void gateup_gemm_kernel(const void *__restr
       for (int i = 0; i < 4; ++i)
         *reinterpret_cast<u32x4 *>(&xs[cur ^ 1][(srow + 32 * i) * kGemmRowB + schunk * 16]) = stg[i];
 #pragma unroll
-      for (int k = 0; k < 2; ++k) { ag[k] = ng[k]; au[k] = nu[k]; }
+      for (int k = 0; k < 2; ++k) { ag[k] = ng[k]; if (!GO) au[k] = nu[k]; }
     }
     __syncthreads();
   }
@@ -323,7 +323,7 @@ __global__ __launch_bounds__(256, 2) void gateup_gemm_kernel(const void *__restr
       const int p = rv.pair_at(q0 + c);
       f32x4 hv;
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) hv[rr] = silu(accg[tl][rr]) * accu[tl][rr];
+      for (int rr = 0; rr < 4; ++rr) hv[rr] = GO ? silu(accg[tl][rr]) : silu(accg[tl][rr]) * accu[tl][rr];
       *reinterpret_cast<f32x4 *>(hout + (size_t)p * d_ff + neuron0) = hv;
     }
   }
@@ -589,6 +589,71 @@ __global__ __launch_bounds__(64 * NW) void neuron_topk_seg_kernel(const float *_
         for (int i = 0; i < V; ++i) o[i] = mv[i];
       }
     }
+  }
+}
+
+// ---------------------------------------------------------------- sparse up
+// The page's own split: the kept neurons' up projections, u_j = W_u[j, :] .
+// x_t, for j in the pair's kept list only (W_u row-major, neuron-major like
+// W_d).  One wave per (pair, 8 kept rows): per 1 KB chunk of a row (64 lanes
+// x 16 bytes), the lane's slice of the token row x is loaded once and the 8
+// rows' slices are loaded together and dotted with it; each row's partial
+// is then summed over the wave in a fixed DPP order.  The kept coefficient
+// (w * silu(g_j), from the mask) is multiplied by u_j in place, giving the
+// down projection's w * h_j.
+constexpr int kUpRows = 8;
+
+template <bool BF16>
+__global__ __launch_bounds__(64) void up_rows_kernel(const void *__restrict__ wuv,
+                                                     const void *__restrict__ xv, RouteView rv,
+                                                     int H, int d_ff, int k,
+                                                     const int32_t *__restrict__ idx,
+                                                     float *__restrict__ coef) {
+  constexpr int EB = BF16 ? 2 : 4;
+  const int lane = threadIdx.x;
+  const int p = blockIdx.x;
+  const int i0 = blockIdx.y * kUpRows;
+  const int t = p / rv.top_k;
+  const size_t e = (size_t)rv.expert_of_pair(p);
+  const uint8_t *rows[kUpRows];
+#pragma unroll
+  for (int r = 0; r < kUpRows; ++r) {
+    const int i = i0 + r;
+    int j = i < k ? idx[(size_t)p * k + i] : 0;
+    j = (unsigned)j < (unsigned)d_ff ? j : 0;
+    rows[r] = static_cast<const uint8_t *>(wuv) + (e * d_ff + j) * H * EB;
+  }
+  const uint8_t *xr = static_cast<const uint8_t *>(xv) + (size_t)t * H * EB;
+  const int row_bytes = H * EB;  // a multiple of 128: H is a multiple of 64
+  float acc[kUpRows];
+#pragma unroll
+  for (int r = 0; r < kUpRows; ++r) acc[r] = 0.f;
+  for (int off = lane * 16; off < row_bytes; off += 1024) {
+    const u32x4 xq = ld16(xr + off);
+    u32x4 q[kUpRows];
+#pragma unroll
+    for (int r = 0; r < kUpRows; ++r) q[r] = i0 + r < k ? ld16(rows[r] + off) : u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int r = 0; r < kUpRows; ++r) {
+      float a = 0.f;
+      if (BF16) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          a = fmaf(bf16lo(q[r][c]), bf16lo(xq[c]), a);
+          a = fmaf(bf16hi(q[r][c]), bf16hi(xq[c]), a);
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) a = fmaf(__uint_as_float(q[r][c]), __uint_as_float(xq[c]), a);
+      }
+      acc[r] += a;
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < kUpRows; ++r) {
+    const float u = wave_sum(acc[r]);
+    const int i = i0 + r;
+    if (lane == 0 && i < k) coef[(size_t)p * k + i] *= u;
   }
 }
 
@@ -942,22 +1007,26 @@ static void launch_mask(const FfnArgs &a, const RouteView &rv, int32_t *idx, flo
 // A routed expert never holds more than T tokens, so at T <= 16 one token
 // tile per item suffices; that variant splits K over 8 waves (short blocks,
 // high occupancy, no tail of half-empty block rounds).
-static void launch_gateup(const FfnArgs &a, const RouteView &rv, hipStream_t stream) {
+// gate_only: the page's own split, h <- silu(W_g x) (the scores), up skipped.
+static void launch_gateup(const FfnArgs &a, const RouteView &rv, hipStream_t stream,
+                          bool gate_only = false) {
   timer_begin(kStageGateup, stream);
   if (a.T <= 16) {
     // an item is an active-expert slot: at most min(E, P) of them
     const int P = a.T * a.top_k;
     dim3 grid(a.implicit ? a.E : (a.E < P ? a.E : P), a.d_ff / 16);
-    if (a.bf16)
-      gateup_swiglu_kernel<true, 1, 8><<<grid, 512, 0, stream>>>(a.x, a.w_gate, a.w_up, rv, a.H, a.d_ff, a.h);
-    else
-      gateup_swiglu_kernel<false, 1, 8><<<grid, 512, 0, stream>>>(a.x, a.w_gate, a.w_up, rv, a.H, a.d_ff, a.h);
+#define MOE_GU(BF, GOV) \
+  gateup_swiglu_kernel<BF, 1, 8, GOV><<<grid, 512, 0, stream>>>(a.x, a.w_gate, a.w_up, rv, a.H, a.d_ff, a.h)
+    if (a.bf16) { if (gate_only) MOE_GU(true, true); else MOE_GU(true, false); }
+    else { if (gate_only) MOE_GU(false, true); else MOE_GU(false, false); }
+#undef MOE_GU
   } else {
     dim3 grid(n_items(a, kGemmTok), a.d_ff / 64);
-    if (a.bf16)
-      gateup_gemm_kernel<true><<<grid, 256, 0, stream>>>(a.x, a.w_gate, a.w_up, rv, a.H, a.d_ff, a.h);
-    else
-      gateup_gemm_kernel<false><<<grid, 256, 0, stream>>>(a.x, a.w_gate, a.w_up, rv, a.H, a.d_ff, a.h);
+#define MOE_GG(BF, GOV) \
+  gateup_gemm_kernel<BF, GOV><<<grid, 256, 0, stream>>>(a.x, a.w_gate, a.w_up, rv, a.H, a.d_ff, a.h)
+    if (a.bf16) { if (gate_only) MOE_GG(true, true); else MOE_GG(true, false); }
+    else { if (gate_only) MOE_GG(false, true); else MOE_GG(false, false); }
+#undef MOE_GG
   }
   timer_end(stream);
 }
@@ -1009,6 +1078,27 @@ hipError_t launch_ffn_sparse(const FfnArgs &a, hipStream_t stream) {
   const RouteView rv = make_view(a);
   launch_gateup(a, rv, stream);
   launch_mask(a, rv, a.idx, a.hact, nullptr, 0, stream);
+  launch_down_token(a, rv, a.idx, a.hact, a.k_keep, stream);
+  return hipGetLastError();
+}
+
+// The page's own split: dense gate scores, mask on |silu(g)|, the kept
+// neurons' up rows (coefficients become w * silu(g_j) * u_j), then the same
+// sparse down projection.
+hipError_t launch_ffn_updown(const FfnArgs &a, hipStream_t stream) {
+  if (a.T == 0) return hipSuccess;
+  if (zero_contribution(a, stream)) return hipGetLastError();
+  const RouteView rv = make_view(a);
+  launch_gateup(a, rv, stream, true);
+  launch_mask(a, rv, a.idx, a.hact, nullptr, 0, stream);
+  const int P = a.T * a.top_k;
+  dim3 grid(P, (a.k_keep + kUpRows - 1) / kUpRows);
+  timer_begin(kStageUpRows, stream);
+  if (a.bf16)
+    up_rows_kernel<true><<<grid, 64, 0, stream>>>(a.w_up, a.x, rv, a.H, a.d_ff, a.k_keep, a.idx, a.hact);
+  else
+    up_rows_kernel<false><<<grid, 64, 0, stream>>>(a.w_up, a.x, rv, a.H, a.d_ff, a.k_keep, a.idx, a.hact);
+  timer_end(stream);
   launch_down_token(a, rv, a.idx, a.hact, a.k_keep, stream);
   return hipGetLastError();
 }

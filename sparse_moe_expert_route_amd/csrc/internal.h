@@ -33,7 +33,7 @@ inline void timer_end(hipStream_t s) {
 
 // Stage ids (mirror moe_stage in the public header).
 enum { kStageLogits = 0, kStageTopk, kStageGroup, kStageGateup, kStageMask, kStageDownRows,
-       kStageDownDense, kStageCombine, kStageZero };
+       kStageDownDense, kStageCombine, kStageZero, kStageUpRows };
 
 struct RouteArgs {
   int T, H, E, top_k, norm_topk, bf16;
@@ -76,5 +76,6 @@ hipError_t launch_pack_gate_up(const void *src, void *dst, int E, int d_ff, int 
 size_t dense_down_partial_rows(int T, int E, int top_k, int H);
 hipError_t launch_ffn_sparse(const FfnArgs &a, hipStream_t stream);
 hipError_t launch_ffn_dense(const FfnArgs &a, hipStream_t stream);
+hipError_t launch_ffn_updown(const FfnArgs &a, hipStream_t stream);
 
 }  // namespace moe

@@ -51,28 +51,39 @@ def to_dev(a: np.ndarray):
 
 
 class DeviceLayer:
-    """Device copies of a LayerInputs' weights."""
+    """Device copies of a LayerInputs' weights.  score="swiglu" runs
+    moe_expert_ffn_sparse / _dense (gate and up packed); score="gate" runs
+    moe_expert_ffn_sparse_updown (gate packed, up row-major)."""
 
-    def __init__(self, inp: LayerInputs):
+    def __init__(self, inp: LayerInputs, score: str = "swiglu"):
         self.inp = inp
+        self.score = score
         sh = inp.shape
         self.desc = B.make_desc(sh.hidden, sh.n_experts, sh.d_ff, sh.top_k, sh.norm_topk, sh.dtype)
         self.w_router = to_dev(inp.w_router)
         self.bias = to_dev(inp.bias) if inp.bias is not None else None
-        # gate/up go to the FFN calls packed (moe_pack_gate_up); down stays row-major
+        pk_up = B.moe_pack_gate_up if score == "swiglu" else (lambda d, w: w)
+        # gate (and, for the SwiGLU score, up) go to the FFN calls packed
+        # (moe_pack_gate_up); down stays row-major
         self.w = (B.moe_pack_gate_up(self.desc, to_dev(inp.wg)),
-                  B.moe_pack_gate_up(self.desc, to_dev(inp.wu)), to_dev(inp.wd))
+                  pk_up(self.desc, to_dev(inp.wu)), to_dev(inp.wd))
         self.desc_sh = None
         if inp.shared is not None:
             self.desc_sh = B.make_desc(sh.hidden, sh.n_shared, sh.d_ff_shared, sh.n_shared, False,
                                        sh.dtype)
             g, u, d = inp.shared
             self.w_sh = (B.moe_pack_gate_up(self.desc_sh, to_dev(g)),
-                         B.moe_pack_gate_up(self.desc_sh, to_dev(u)), to_dev(d))
+                         pk_up(self.desc_sh, to_dev(u)), to_dev(d))
         torch.cuda.synchronize()
 
+    def _fn(self, path):
+        if self.score == "gate":
+            assert path == B.MOE_PATH_SPARSE, "the gate-score split has no dense form"
+            return B.moe_expert_ffn_sparse_updown
+        return B.moe_expert_ffn_sparse if path == B.MOE_PATH_SPARSE else B.moe_expert_ffn_dense
+
     def run(self, x_host: np.ndarray, k: int, path: int, k_sh=None, path_sh=None,
-            poison_rows=None):
+            poison_rows=None, poison_up=None):
         """One layer call; returns host copies of routing, masks and y."""
         sh = self.inp.shape
         T = x_host.shape[0]
@@ -83,9 +94,10 @@ class DeviceLayer:
         y = torch.full((T, sh.hidden), float("nan"), dtype=torch.float32, device="cuda")
         idx = torch.full((max(1, T * sh.top_k), max(1, k)), -1, dtype=torch.int32, device="cuda")
         ws = torch.empty(B.moe_ffn_workspace_size(self.desc, T, k, path), dtype=torch.uint8, device="cuda")
-        fn = B.moe_expert_ffn_sparse if path == B.MOE_PATH_SPARSE else B.moe_expert_ffn_dense
+        fn = self._fn(path)
         wd = self.w[2] if poison_rows is None else poison_rows
-        fn(self.desc, T, k, x, self.w[0], self.w[1], wd, R, y, 0, idx if k > 0 else None, ws)
+        wu = self.w[1] if poison_up is None else poison_up
+        fn(self.desc, T, k, x, self.w[0], wu, wd, R, y, 0, idx if k > 0 else None, ws)
         out = dict(T=T, k=k)
         idx_sh = None
         if self.desc_sh is not None:
@@ -94,7 +106,7 @@ class DeviceLayer:
             path_sh = path if path_sh is None else path_sh
             idx_sh = torch.full((max(1, T * ds.top_k), max(1, k_sh)), -1, dtype=torch.int32, device="cuda")
             ws2 = torch.empty(B.moe_ffn_workspace_size(ds, T, k_sh, path_sh), dtype=torch.uint8, device="cuda")
-            fs = B.moe_expert_ffn_sparse if path_sh == B.MOE_PATH_SPARSE else B.moe_expert_ffn_dense
+            fs = self._fn(path_sh)
             fs(ds, T, k_sh, x, *self.w_sh, None, y, 1, idx_sh if k_sh > 0 else None, ws2)
             out["k_sh"] = k_sh
         torch.cuda.synchronize()
@@ -149,11 +161,12 @@ def rel_l2(a, b) -> float:
     return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
 
 
-def compare_layer(inp: LayerInputs, x_host, got, k, k_sh=None, tokens=None):
+def compare_layer(inp: LayerInputs, x_host, got, k, k_sh=None, tokens=None, score="swiglu"):
     """Check a GPU layer result against the oracle; returns the rel L2 error.
 
     ``tokens`` restricts the check to a sample of token rows (the layer is
-    token-separable, so the oracle runs on just those tokens)."""
+    token-separable, so the oracle runs on just those tokens); ``score``
+    selects the oracle's mask score (the layer variant the GPU ran)."""
     sh = inp.shape
     T = x_host.shape[0]
     tokens = np.arange(T) if tokens is None else np.asarray(tokens)
@@ -163,7 +176,7 @@ def compare_layer(inp: LayerInputs, x_host, got, k, k_sh=None, tokens=None):
     if shared is not None:
         ks = k_sh if k_sh is not None else sh.d_ff_shared
     kw = dict(top_k=sh.top_k, norm_topk=sh.norm_topk, k_keep=k, dtype=sh.dtype,
-              shared=shared, k_keep_shared=ks)
+              shared=shared, k_keep_shared=ks, score=score)
     ids0, _, logits0, _ = oracle.route(oracle.to_f64(xs, sh.dtype),
                                        oracle.to_f64(inp.w_router, sh.dtype),
                                        inp.bias, sh.top_k, sh.norm_topk)

@@ -109,7 +109,8 @@ def _ffn(fn, d, T, k, x=FAKE, wg=FAKE, wu=FAKE, wd=FAKE, routing="ok", y=FAKE, a
 INV, MISA, WSP, UNS = 1, 2, 3, 4
 
 
-@pytest.mark.parametrize("fn_name", ["moe_expert_ffn_sparse", "moe_expert_ffn_dense"])
+@pytest.mark.parametrize("fn_name", ["moe_expert_ffn_sparse", "moe_expert_ffn_dense",
+                                     "moe_expert_ffn_sparse_updown"])
 def test_ffn_validation(fn_name):
     fn = getattr(L, fn_name)
     d = _desc()

@@ -31,10 +31,15 @@ def say(*a):
 
 
 @functools.lru_cache(maxsize=2)
-def layer(name: str, **over):
+def _inputs(name: str, **over):
     shape = S.LAYERS[name].with_(**over) if over else S.LAYERS[name]
-    inp = LayerInputs(shape, seed=0)
-    return inp, DeviceLayer(inp)
+    return LayerInputs(shape, seed=0)
+
+
+@functools.lru_cache(maxsize=2)
+def layer(name: str, score: str = "swiglu", **over):
+    inp = _inputs(name, **over)
+    return inp, DeviceLayer(inp, score)
 
 
 def _sample(T, n=6):
@@ -43,16 +48,16 @@ def _sample(T, n=6):
     return np.unique(np.linspace(0, T - 1, n).round().astype(int))
 
 
-def run_case(name, T, s, path, s_sh=None, path_sh=None, sample=8, seed=1, **over):
-    inp, dev = layer(name, **over)
+def run_case(name, T, s, path, s_sh=None, path_sh=None, sample=8, seed=1, score="swiglu", **over):
+    inp, dev = layer(name, score, **over)
     sh = inp.shape
     k = O.keep_count(s, sh.d_ff)
     k_sh = O.keep_count(s_sh, sh.d_ff_shared) if (sh.n_shared and s_sh is not None) else None
     x = inp.tokens(T, seed)
-    say(f"[case] {sh.name} T={T} s={s} k={k} path={path} s_sh={s_sh} over={over}")
+    say(f"[case] {sh.name} T={T} s={s} k={k} path={path} s_sh={s_sh} score={score} over={over}")
     got = dev.run(x, k, path, k_sh, path_sh)
     check_grouping(got, sh.n_experts, sh.top_k)
-    err = compare_layer(inp, x, got, k, k_sh, tokens=_sample(T, sample))
+    err = compare_layer(inp, x, got, k, k_sh, tokens=_sample(T, sample), score=score)
     say(f"   rel_l2={err:.3e}")
     return got
 
@@ -97,6 +102,48 @@ def test_deepseek_v2_like_dense():
 @pytest.mark.parametrize("path", [SP, DN])
 def test_llama4_like(T, path):
     run_case("llama4-like", T, 0.9, path, s_sh=0.9, path_sh=path, sample=4)
+
+
+# ------------------------------------------------------------------ the page's own split
+
+UPDOWN = [("tiny-f32", 4, 0.9, None), ("tiny-f32", 4, 0.0, None), ("olmoe-like", 1, 0.9, None),
+          ("olmoe-like", 4, 0.9, None), ("olmoe-like", 16, 0.9, None), ("olmoe-like", 16, 0.5, None),
+          ("qwen3-moe-like", 4, 0.9, None), ("qwen3-moe-like", 32, 0.9, None),
+          ("deepseek-v2-like", 1, 0.9, 0.5), ("deepseek-v2-like", 8, 0.9, 0.0),
+          ("llama4-like", 1, 0.9, 0.9), ("llama4-like", 64, 0.9, 0.9)]
+
+
+@pytest.mark.parametrize("name,T,s,s_sh", UPDOWN)
+def test_updown_split(name, T, s, s_sh):
+    # scores from the dense gate alone; up and down gathered on kept rows
+    run_case(name, T, s, SP, s_sh=s_sh, path_sh=SP, score="gate", sample=4)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("T", [1, 17, 37])
+def test_updown_ragged(dtype, T):
+    run_case("olmoe-like", T, 0.7, SP, s_sh=0.5, path_sh=SP, score="gate", dtype=dtype, **RAGGED)
+
+
+def test_updown_reads_only_kept_up_and_down_rows_and_is_reproducible():
+    # NaN in every W_u and W_d row no pair keeps: same bits
+    inp, dev = layer("olmoe-like", "gate")
+    x = inp.tokens(4, 7)
+    k = O.keep_count(0.9, 1024)
+    say("[case] updown NaN-poisoned unkept W_u / W_d rows")
+    a = dev.run(x, k, SP)
+    b = dev.run(x, k, SP)
+    np.testing.assert_array_equal(a["y"], b["y"])
+    keep = np.zeros((64, 1024), dtype=bool)
+    for p, e in enumerate(a["ids"].reshape(-1)):
+        keep[e, a["idx"][p, :k]] = True
+    poison = torch.from_numpy(~keep).cuda()
+    wu, wd = dev.w[1].clone(), dev.w[2].clone()
+    wu[poison] = float("nan")
+    wd[poison] = float("nan")
+    c = dev.run(x, k, SP, poison_rows=wd, poison_up=wu)
+    assert np.all(np.isfinite(c["y"]))
+    np.testing.assert_array_equal(a["y"], c["y"])
 
 
 # ------------------------------------------------------------------ ragged shapes and edges
