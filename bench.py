@@ -63,6 +63,8 @@ def parse():
     ap.add_argument("--timer-steps", type=int, default=50, help="eager steps timed per kernel")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-variant", action="store_true",
+                    help="skip the gate-score split variant (moe_expert_ffn_sparse_updown)")
     ap.add_argument("--crossover", action="store_true",
                     help="sparse-vs-dense sweep of the Llama-4-like layer (its own JSON line)")
     ap.add_argument("--layer", default=None, help="layer of the crossover sweep")
@@ -76,7 +78,7 @@ class Workload:
     """Device-resident layer copies and token batches for one batch size."""
 
     def __init__(self, shape, host_w, dev_w0, T, sparsity, path_arg, dev_sh0=None,
-                 sparsity_shared=None):
+                 sparsity_shared=None, score="swiglu"):
         import torch
         import moe_synth as S
         from sparse_moe_expert_route_amd import binding as B
@@ -88,6 +90,9 @@ class Workload:
         forced = {"sparse": B.MOE_PATH_SPARSE, "dense": B.MOE_PATH_DENSE}.get(path_arg)
         self.auto_path = B.moe_select_path(self.desc, T, self.k)
         self.path = self.auto_path if forced is None else forced
+        self.score = score
+        if score == "gate":   # the split has a sparse form only
+            self.path = B.MOE_PATH_SPARSE
         # always-on shared experts (routing NULL, accumulated into y)
         self.desc_sh = None
         if dev_sh0 is not None:
@@ -121,6 +126,8 @@ class Workload:
         self.y = [torch.empty((T, sh.hidden), dtype=torch.float32, device="cuda") for _ in range(self.L)]
         self.idx = torch.empty((T * K, max(1, self.k)), dtype=torch.int32, device="cuda")
         self.ffn = B.moe_expert_ffn_sparse if self.path == B.MOE_PATH_SPARSE else B.moe_expert_ffn_dense
+        if score == "gate":   # the page's own split (w_up row-major in dev_w0)
+            self.ffn = B.moe_expert_ffn_sparse_updown
         self.graphs = []
 
     def step(self, i, idx=None):
@@ -187,14 +194,16 @@ class Workload:
             rec = dict(
                 active=int(len(active)), pairs=int(P),
                 router=sh.n_experts * H * bw,
-                gateup=int(len(active)) * 2 * H * d * bw + self.T * H * bw + P * d * 4,
+                gateup=(int(len(active)) * (2 if self.score == "swiglu" else 1) * H * d * bw
+                        + self.T * H * bw + P * d * 4),
+                up_rows=P * self.k * H * bw if self.score == "gate" else 0,
                 down_rows=P * self.k * H * bw,
                 down_union=union * H * bw,
                 down_dense=int(len(active)) * d * H * bw,
                 io=self.T * H * (bw + 4))
             path_down = rec["down_rows"] if self.path == B.MOE_PATH_SPARSE else rec["down_dense"]
-            rec["layer"] = rec["router"] + rec["gateup"] + path_down + rec["io"]
-            rec["layer_min"] = rec["router"] + rec["gateup"] + rec["down_union"] + rec["io"]
+            rec["layer"] = rec["router"] + rec["gateup"] + rec["up_rows"] + path_down + rec["io"]
+            rec["layer_min"] = rec["router"] + rec["gateup"] + rec["up_rows"] + rec["down_union"] + rec["io"]
             # MFMA work of the dense contractions (2 flops per multiply-add)
             rec["flops_gateup"] = 2 * 2 * P * H * d
             rec["flops_down_dense"] = 2 * P * d * H
@@ -295,8 +304,9 @@ class HostLayer:
         return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
-def measure(shape, host, dev_w0, T, args, path=None, dev_sh0=None):
-    wl = Workload(shape, host, dev_w0, T, args.sparsity, path or args.path, dev_sh0=dev_sh0)
+def measure(shape, host, dev_w0, T, args, path=None, dev_sh0=None, score="swiglu"):
+    wl = Workload(shape, host, dev_w0, T, args.sparsity, path or args.path, dev_sh0=dev_sh0,
+                  score=score)
     log(f"[bench] {shape.name} T={T} k={wl.k} path={'sparse' if wl.path == 0 else 'dense'} "
         f"copies={wl.L}")
     wl.capture()
@@ -516,6 +526,24 @@ def main():
     log("[bench] practical read peak")
     practical = practical_read_peak()
     log(f"[bench] moe_stream_read: {practical['gbs']:.0f} GB/s")
+    # the page's own split (gate-only scores, sparse up and down rows): a
+    # different mask, so reported beside the headline rather than as it
+    updown = {}
+    if not args.no_variant:
+        dev_gate = (dev_w0[0], dev_w0[1], host.to_dev(host.wu), dev_w0[3])
+        for T in sorted(set(sweep + [args.batch])):
+            wl, res = measure(shape, host, dev_gate, T, args, score="gate")
+            updown[str(T)] = {"us_per_call": round(res["us_per_call"], 3),
+                              "us_per_token": round(res["us_per_token"], 3),
+                              "layer_bytes": int(res["layer_bytes"]),
+                              "hbm_gbs": round(res["hbm_gbs"], 1),
+                              "kernels_us": {k: round(v["avg_us"], 2) for k, v in res["kernels"].items()}}
+            log(f"[bench] updown T={T}: {res['us_per_call']:.1f} us/call, "
+                f"{res['us_per_token']:.2f} us/token; kernels "
+                + ", ".join(f"{k} {v['avg_us']:.1f}" for k, v in res["kernels"].items()))
+            del wl
+            torch.cuda.empty_cache()
+        del dev_gate
     cpu = None
     if not args.no_cpu:
         log("[bench] timing the CPU oracle")
@@ -547,6 +575,9 @@ def main():
         "roofline": roofline(r, "gateup_swiglu", "gateup_bytes", practical),
         "roofline_down": roofline(r, "down_rows", "down_bytes", practical),
         "practical_read_peak": practical,
+        "updown_variant": {"what": "the page's own split: dense gate scores |silu(W_g x)|, "
+                                   "up and down gathered on the kept rows (a different mask)",
+                           "batches": updown} if updown else None,
         "cpu_baseline": cpu,
         "batches": batches,
     }
