@@ -253,8 +253,11 @@ __global__ __launch_bounds__(1024) void route_group_kernel(const int32_t *__rest
   block_group(ids, P, E, offsets, pair_by_expert, active, n_active, cursor, wcnt, tmp);
 }
 
-// Small batches: one block selects every token's experts (16 waves, one
-// token each per round) into LDS and global memory, then groups the pairs.
+// Decode batches (T <= 16): one block selects every token's experts (16
+// waves, one token each) into LDS and global memory, then groups the pairs.
+// Past one round of 16 tokens the selection is better spread over many
+// blocks (router_topk_kernel) ahead of the grouping kernel: at T = 256 the
+// one-block form took 56 us against ~10 us for the two kernels.
 constexpr int kFusedMaxPairs = 2048;
 template <int V>
 __global__ __launch_bounds__(1024) void route_select_group_kernel(
@@ -285,7 +288,7 @@ __global__ __launch_bounds__(1024) void route_select_group_kernel(
 template <int V>
 static void launch_select(const RouteArgs &a, int nsplit, hipStream_t stream) {
   const int P = a.T * a.top_k;
-  if (P <= kFusedMaxPairs) {
+  if (a.T <= 16 && P <= kFusedMaxPairs) {
     timer_begin(kStageTopk, stream);
     route_select_group_kernel<V><<<1, 1024, 0, stream>>>(a.logits, nsplit, a.bias, a.T, a.E,
                                                          a.top_k, a.norm_topk, a.topk_ids,

@@ -186,6 +186,20 @@ def test_all_experts_selected_and_single_expert():
     run_case("olmoe-like", 5, 0.5, DN, s_sh=0.0, dtype="f32", **dict(RAGGED, n_experts=1, top_k=1))
 
 
+@pytest.mark.parametrize("score,path", [("swiglu", SP), ("swiglu", DN), ("gate", SP)])
+def test_max_experts_and_top_k(score, path):
+    # E = 1024 experts and top-32 routing, the ABI's maxima
+    run_case("olmoe-like", 3, 0.75, path, score=score,
+             **dict(hidden=128, n_experts=1024, d_ff=64, top_k=32, norm_topk=True))
+
+
+@pytest.mark.parametrize("score,path", [("swiglu", SP), ("swiglu", DN), ("gate", SP)])
+def test_max_hidden(score, path):
+    # H = 16384, the ABI's maximum hidden size, on the fp32 layer
+    run_case("olmoe-like", 2, 0.75, path, score=score,
+             **dict(dtype="f32", hidden=16384, n_experts=2, d_ff=128, top_k=1, norm_topk=False))
+
+
 def test_many_tokens_max_T():
     # the largest token count the ABI takes, on the small fp32 layer, sampled rows
     run_case("tiny-f32", 65536, 0.9, SP, sample=5)
