@@ -452,7 +452,7 @@ def crossover(args):
     rows = []
     for T in batches:
         row = {"T": T}
-        for path in ("sparse", "dense"):
+        for path in ("sparse", "dense", "auto"):
             wl, res = measure(shape, host, dev_w0, T, args, path=path, dev_sh0=dev_sh0)
             kern = {k: round(v["per_step_us"], 2) for k, v in res["kernels"].items()}
             ent = {"us_per_call": round(res["us_per_call"], 2),
@@ -465,13 +465,18 @@ def crossover(args):
             if "gateup_swiglu" in res["kernels"]:
                 k = res["kernels"]["gateup_swiglu"]
                 ent["gateup_tflops"] = round(res["flops_gateup"] / (k["per_step_us"] * 1e-6) / 1e12, 2)
+            if path == "auto":   # the dispatcher's own choice, per routed / shared call
+                ent["routed"] = res["auto_path"]
+                if wl.desc_sh is not None:
+                    ent["shared"] = "sparse" if wl.auto_path_sh == 0 else "dense"
             row[path] = ent
-            row["auto"] = res["auto_path"]
             log(f"[bench] {shape.name} T={T} {path}: {res['us_per_call']:.1f} us/call; kernels/step "
                 + ", ".join(f"{k} {v}" for k, v in kern.items()))
             del wl
             torch.cuda.empty_cache()
         row["faster"] = "sparse" if row["sparse"]["us_per_call"] <= row["dense"]["us_per_call"] else "dense"
+        best = min(row["sparse"]["us_per_call"], row["dense"]["us_per_call"])
+        row["auto_vs_best"] = round(row["auto"]["us_per_call"] / best, 3)
         rows.append(row)
     print(json.dumps({"metric": "sparse-vs-dense crossover: MoE-layer us/call per forced path",
                       "layer": shape.name, "sparsity": args.sparsity,
