@@ -41,6 +41,16 @@ gathers only the active neurons' weights):
 Only kept W_u and W_d rows are read.  With k_keep = d_ff both variants are
 the dense SwiGLU MoE.
 
+Threshold variant (the page's literal masking: technical summary,
+Methodology, activation masking in one O(n) threshold pass without a sort,
+at a target sparsity): a per-expert threshold tau_e, calibrated offline,
+replaces the exact count:
+
+    K_t,e  = { j : |h_j| > tau_e }                 (variable count per pair)
+    tau_e  = the (c + 1)-th largest of the m calibration scores |h| of
+             expert e (its calibration pairs x d_ff neurons), c = ceil((1 - s) m);
+             the layer-wide value for an expert with no calibration pair
+
 Every function below is pinned by tests (tests/test_oracle_pins.py) against
 closed forms, brute force, library routines or invariants; none is
 "parity unpinned".
@@ -194,6 +204,25 @@ def kept_neurons(h: np.ndarray, k: int) -> np.ndarray:
     return np.asarray(sorted(order[:k]), dtype=np.int64)
 
 
+def threshold_neurons(h: np.ndarray, tau: float) -> np.ndarray:
+    """The neurons with |h_j| > tau, ascending (a variable count).
+
+    The page's literal masking: one pass comparing every activation with a
+    threshold set offline for a target sparsity, with no sort (technical
+    summary, Methodology: activation masking).  -0 and +0 score equal."""
+    return np.nonzero(np.abs(h) > tau)[0].astype(np.int64)
+
+
+def calibrated_threshold(scores: np.ndarray, sparsity: float) -> float:
+    """tau such that 'keep |h| > tau' keeps c = ceil((1 - s) m) of the m
+    calibration scores when they are distinct: the (c + 1)-th largest score
+    (the largest one not kept); -1 when c = m (keep everything)."""
+    v = np.sort(np.abs(np.asarray(scores, dtype=np.float64)).ravel())[::-1]
+    m = v.size
+    c = keep_count(sparsity, m)
+    return -1.0 if c >= m else float(v[c])
+
+
 def sparse_down(h: np.ndarray, keep: np.ndarray, w_down_e: np.ndarray) -> np.ndarray:
     """sum_{j in keep} h_j * W_d[j, :]  ->  [H].
 
@@ -223,18 +252,25 @@ class LayerResult:
     keep_shared: Dict[Tuple[int, int], np.ndarray] = field(default_factory=dict)  # (t, j)
 
 
-def _pair_output(x_t, wg, wu, wd, k_keep, forced, score):
+def _select(scores, k_keep, tau, forced):
+    if forced is not None:
+        return np.asarray(forced, dtype=np.int64)
+    if tau is not None:
+        return threshold_neurons(scores, tau)
+    return kept_neurons(scores, k_keep)
+
+
+def _pair_output(x_t, wg, wu, wd, k_keep, forced, score, tau=None):
     """One (token, expert) pair: (its contribution before the routing
-    weight [H], the selection scores [d_ff], the kept set)."""
+    weight [H], the selection scores [d_ff], the kept set).  ``tau`` (the
+    expert's calibrated threshold) replaces the exact count when given."""
     if score == "swiglu":
         h = expert_activation(x_t, wg, wu)
-        keep = (np.asarray(forced, dtype=np.int64) if forced is not None
-                else kept_neurons(h, k_keep))
+        keep = _select(h, k_keep, tau, forced)
         return sparse_down(h, keep, wd), h, keep
     if score == "gate":
         sc = gate_scores(x_t, wg)
-        keep = (np.asarray(forced, dtype=np.int64) if forced is not None
-                else kept_neurons(sc, k_keep))
+        keep = _select(sc, k_keep, tau, forced)
         h = np.zeros_like(sc)
         h[keep] = sparse_up(x_t, sc, keep, wu)
         return sparse_down(h, keep, wd), sc, keep
@@ -242,7 +278,7 @@ def _pair_output(x_t, wg, wu, wd, k_keep, forced, score):
 
 
 def routed_experts(x, ids, weights, w_gate, w_up, w_down, k_keep, dtype,
-                   forced_keep=None, keep_h=True, score="swiglu"):
+                   forced_keep=None, keep_h=True, score="swiglu", thresholds=None):
     """Routed contribution sum_{slot} w * sum_{j in K} h_j W_d^e[j, :].
 
     Pairs are visited expert by expert so each expert's weights are
@@ -262,7 +298,8 @@ def routed_experts(x, ids, weights, w_gate, w_up, w_down, k_keep, dtype,
         wg, wu, wd = (to_f64(w[e], dtype) for w in (w_gate, w_up, w_down))
         for (t, s) in by_expert[e]:
             forced = forced_keep.get((t, s)) if forced_keep is not None else None
-            out, sc, keep = _pair_output(x[t], wg, wu, wd, k_keep, forced, score)
+            tau = None if thresholds is None else float(thresholds[e])
+            out, sc, keep = _pair_output(x[t], wg, wu, wd, k_keep, forced, score, tau)
             y[t] += weights[t, s] * out
             if keep_h:
                 hs[(t, s)] = sc
@@ -271,7 +308,7 @@ def routed_experts(x, ids, weights, w_gate, w_up, w_down, k_keep, dtype,
 
 
 def shared_experts(x, w_gate, w_up, w_down, n_shared, k_keep, dtype,
-                   forced_keep=None, keep_h=True, score="swiglu"):
+                   forced_keep=None, keep_h=True, score="swiglu", thresholds=None):
     """Always-on shared experts: every token, weight 1, each expert with its
     own per-(token, expert) mask of k_keep neurons.
 
@@ -285,7 +322,8 @@ def shared_experts(x, w_gate, w_up, w_down, n_shared, k_keep, dtype,
         wg, wu, wd = (to_f64(w[j], dtype) for w in (w_gate, w_up, w_down))
         for t in range(T):
             forced = forced_keep.get((t, j)) if forced_keep is not None else None
-            out, sc, keep = _pair_output(x[t], wg, wu, wd, k_keep, forced, score)
+            tau = None if thresholds is None else float(thresholds[j])
+            out, sc, keep = _pair_output(x[t], wg, wu, wd, k_keep, forced, score, tau)
             y[t] += out
             if keep_h:
                 hs[(t, j)] = sc
@@ -299,7 +337,9 @@ def moe_layer(x, w_router, bias, w_gate, w_up, w_down, *, top_k: int,
               forced_ids: Optional[np.ndarray] = None,
               forced_keep: Optional[dict] = None,
               forced_keep_shared: Optional[dict] = None,
-              keep_h: bool = True, score: str = "swiglu") -> LayerResult:
+              keep_h: bool = True, score: str = "swiglu",
+              thresholds: Optional[np.ndarray] = None,
+              thresholds_shared: Optional[np.ndarray] = None) -> LayerResult:
     """The whole layer for a token batch.
 
     x [T, H], w_router [E, H] and the expert weights (indexable by expert,
@@ -314,7 +354,9 @@ def moe_layer(x, w_router, bias, w_gate, w_up, w_down, *, top_k: int,
 
     ``score`` is "swiglu" (mask by |silu(g) * u|, gate and up dense) or
     "gate" (the page's own split: mask by |silu(g)|, up and down gathered
-    for the kept neurons only).  LayerResult.h holds the selection scores."""
+    for the kept neurons only).  LayerResult.h holds the selection scores.
+    ``thresholds`` [E] (and ``thresholds_shared`` [n_shared]) switch the
+    mask from the exact count k_keep to 'score > tau_e' (variable count)."""
     xf = to_f64(x, dtype)
     _check_finite("x", xf)
     wr = to_f64(w_router, dtype)
@@ -325,7 +367,7 @@ def moe_layer(x, w_router, bias, w_gate, w_up, w_down, *, top_k: int,
         if norm_topk:
             w = w / np.sum(w, axis=1, keepdims=True)
     y_r, hs, keeps = routed_experts(xf, ids, w, w_gate, w_up, w_down, k_keep,
-                                    dtype, forced_keep, keep_h, score)
+                                    dtype, forced_keep, keep_h, score, thresholds)
     T, H = xf.shape
     y_s = np.zeros((T, H))
     hs_s, keeps_s = {}, {}
@@ -333,7 +375,47 @@ def moe_layer(x, w_router, bias, w_gate, w_up, w_down, *, top_k: int,
         n_sh = len(shared[0])
         ks = k_keep_shared if k_keep_shared is not None else shared[0][0].shape[0]
         y_s, hs_s, keeps_s = shared_experts(xf, shared[0], shared[1], shared[2],
-                                            n_sh, ks, dtype, forced_keep_shared, keep_h, score)
+                                            n_sh, ks, dtype, forced_keep_shared, keep_h, score,
+                                            thresholds_shared)
     return LayerResult(y=y_r + y_s, y_routed=y_r, y_shared=y_s, ids=ids, weights=w,
                        logits=l, probs=p, h=hs, keep=keeps, h_shared=hs_s,
                        keep_shared=keeps_s)
+
+
+def calibrate_thresholds(x, w_router, bias, w_gate, w_up, *, top_k: int, norm_topk: bool,
+                         dtype: str, sparsity: float, score: str = "swiglu",
+                         shared: Optional[Sequence] = None) -> Tuple[np.ndarray, Optional[np.ndarray]]:
+    """Per-expert thresholds from calibration tokens x [T, H]: each routed
+    expert's tau is calibrated_threshold over the scores of every
+    (calibration token routed to it, neuron) pair; an expert no token reaches
+    takes the value over all routed scores.  Shared experts (every token)
+    get their own.  The page sets the masking threshold offline for a target
+    sparsity (technical summary, Methodology: activation masking)."""
+    xf = to_f64(x, dtype)
+    _check_finite("x", xf)
+    ids, _, _, _ = route(xf, to_f64(w_router, dtype), bias, top_k, norm_topk)
+    E = len(w_gate)
+    per = {e: [] for e in range(E)}
+    for e in range(E):
+        rows = [t for t in range(xf.shape[0]) if e in ids[t]]
+        if not rows:
+            continue
+        wg = to_f64(w_gate[e], dtype)
+        wu = to_f64(w_up[e], dtype)
+        for t in rows:
+            per[e].append(gate_scores(xf[t], wg) if score == "gate"
+                          else expert_activation(xf[t], wg, wu))
+    everything = [v for e in range(E) for v in per[e]]
+    tau_all = calibrated_threshold(np.concatenate(everything), sparsity) if everything else -1.0
+    tau = np.array([calibrated_threshold(np.concatenate(per[e]), sparsity) if per[e] else tau_all
+                    for e in range(E)], dtype=np.float64)
+    tau_sh = None
+    if shared is not None:
+        tau_sh = []
+        for j in range(len(shared[0])):
+            wg, wu = to_f64(shared[0][j], dtype), to_f64(shared[1][j], dtype)
+            sc = [gate_scores(xf[t], wg) if score == "gate" else expert_activation(xf[t], wg, wu)
+                  for t in range(xf.shape[0])]
+            tau_sh.append(calibrated_threshold(np.concatenate(sc), sparsity))
+        tau_sh = np.array(tau_sh, dtype=np.float64)
+    return tau, tau_sh

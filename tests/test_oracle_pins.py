@@ -219,7 +219,7 @@ def _run(L, top_k, norm, k, **kw):
                             top_k=top_k, norm_topk=norm, k_keep=k, dtype="f32", **kw)
 
 
-def _brute_layer(L, top_k, norm, k, score="swiglu"):
+def _brute_layer(L, top_k, norm, k, score="swiglu", taus=None):
     """Scalar float64 loops; mask by brute-force subset enumeration.  With
     score="gate" neurons are ranked by |silu(g)| alone and u is formed for
     the kept neurons only."""
@@ -243,8 +243,11 @@ def _brute_layer(L, top_k, norm, k, score="swiglu"):
                 sg.append(g / (1 + math.exp(-g)))
                 h.append(sg[-1] * u)
             rank = h if score == "swiglu" else sg
-            K = next(c for c in itertools.combinations(range(d), k)
-                     if _dominates([abs(v) for v in rank], c, d))
+            if taus is not None:                  # threshold mask: a compare per neuron
+                K = [j for j in range(d) if abs(rank[j]) > taus[e]]
+            else:
+                K = next(c for c in itertools.combinations(range(d), k)
+                         if _dominates([abs(v) for v in rank], c, d))
             for j in K:
                 for i in range(H):
                     y[t][i] += w * h[j] * wd[e, j, i]
@@ -430,3 +433,88 @@ def test_bf16_inputs_are_exact_bit_patterns():
         oracle.moe_layer(np.array([[np.nan, 0.0]], dtype=np.float32), np.zeros((2, 2), np.float32),
                          None, np.zeros((2, 2, 2), np.float32), np.zeros((2, 2, 2), np.float32),
                          np.zeros((2, 2, 2), np.float32), top_k=1, norm_topk=False, k_keep=1, dtype="f32")
+
+
+# ------------------------------------------------------------ threshold masking
+
+@pytest.mark.parametrize("seed", range(20))
+def test_calibrated_threshold_keeps_the_target_count(seed):
+    rng = np.random.default_rng(200 + seed)
+    m = int(rng.integers(1, 60))
+    v = rng.standard_normal(m)
+    for s in (0.0, 0.3, 0.5, 0.9, 0.99, 1.0):
+        tau = O.calibrated_threshold(v, s)
+        c = math.ceil((1 - s) * m - 1e-9)
+        assert sum(1 for x in v if abs(x) > tau) == c
+        if c < m:   # tau is the largest score left out
+            assert tau == sorted(abs(x) for x in v)[m - c - 1]
+    assert O.calibrated_threshold(v, 0.0) == -1.0
+
+
+def test_threshold_mask_is_one_compare_pass():
+    rng = np.random.default_rng(5)
+    h = rng.standard_normal(50)
+    h[7] = -0.0
+    for tau in (-1.0, 0.0, 0.3, 1.1, 10.0):
+        want = [j for j in range(50) if abs(h[j]) > tau]
+        np.testing.assert_array_equal(O.threshold_neurons(h, tau), want)
+
+
+def _rand_taus(L, seed):
+    E = L["wg"].shape[0]
+    return np.random.default_rng(seed).uniform(0.01, 0.2, size=E)
+
+
+@pytest.mark.parametrize("seed", range(5))
+@pytest.mark.parametrize("top_k,norm", [(2, False), (3, True)])
+def test_threshold_layer_brute_force(seed, top_k, norm):
+    L = _rand_layer(300 + seed, T=2, H=8, E=5, d=8)
+    taus = _rand_taus(L, seed)
+    for score in ("swiglu", "gate"):
+        r = _run(L, top_k, norm, 0, score=score, thresholds=taus)
+        np.testing.assert_allclose(r.y, _brute_layer(L, top_k, norm, 0, score=score, taus=taus),
+                                   rtol=1e-11, atol=1e-13)
+
+
+def test_threshold_minus_one_is_dense_moe():
+    L = _rand_layer(40, T=4, H=32, E=8, d=24)
+    r = _run(L, 2, True, 0, thresholds=np.full(8, -1.0))
+    np.testing.assert_allclose(r.y, _torch_dense_moe(L, 2, True), rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("score", ["swiglu", "gate"])
+def test_calibration_hits_its_target_on_its_own_tokens(score):
+    # calibrated on a token batch, the thresholds keep exactly c_e of each
+    # expert's m_e scores on that batch (the scores are distinct)
+    L = _rand_layer(41, T=12, H=32, E=6, d=24)
+    S = _rand_layer(42, T=12, H=32, E=1, d=16)
+    sh = (S["wg"], S["wu"], S["wd"])
+    for s in (0.5, 0.9):
+        tau, tau_sh = O.calibrate_thresholds(L["x"], L["wr"], L["bias"], L["wg"], L["wu"],
+                                             top_k=2, norm_topk=False, dtype="f32", sparsity=s,
+                                             score=score, shared=sh)
+        r = _run(L, 2, False, 0, score=score, thresholds=tau, shared=sh, thresholds_shared=tau_sh)
+        kept = {}
+        for (t, slot), keep in r.keep.items():
+            e = int(r.ids[t, slot])
+            kept[e] = kept.get(e, 0) + len(keep)
+        for e, n in kept.items():
+            m = 24 * sum(1 for t in range(12) if e in r.ids[t])
+            assert n == math.ceil((1 - s) * m - 1e-9), (e, n, m)
+        assert sum(len(v) for v in r.keep_shared.values()) == math.ceil((1 - s) * 12 * 16 - 1e-9)
+
+
+def test_calibration_expert_without_tokens_takes_layer_value():
+    L = _rand_layer(43, T=2, H=32, E=8, d=24)
+    tau, _ = O.calibrate_thresholds(L["x"], L["wr"], L["bias"], L["wg"], L["wu"], top_k=1,
+                                    norm_topk=False, dtype="f32", sparsity=0.75)
+    ids, *_ = O.route(L["x"].astype(np.float64), L["wr"].astype(np.float64), L["bias"], 1, False)
+    used = set(int(e) for e in ids.ravel())
+    all_scores = np.concatenate([O.expert_activation(L["x"][t].astype(np.float64),
+                                                     L["wg"][int(ids[t, 0])].astype(np.float64),
+                                                     L["wu"][int(ids[t, 0])].astype(np.float64))
+                                 for t in range(2)])
+    layer_tau = O.calibrated_threshold(all_scores, 0.75)
+    for e in range(8):
+        if e not in used:
+            assert tau[e] == layer_tau
