@@ -217,6 +217,52 @@ moe_status moe_pack_gate_up(const moe_desc *d, const void *src_rowmajor, void *d
 moe_status moe_unpack_gate_up(const moe_desc *d, const void *src_packed, void *dst_rowmajor,
                               hipStream_t stream);
 
+/*
+ * moe_expert_ffn_sparse_threshold -- the sparse path with the page's literal
+ * masking (technical summary, Methodology: activation masking in one O(n)
+ * threshold pass, without a sort, at a target sparsity): neuron j of pair
+ * (t, e) is kept iff |h_j| > tau[e], with h = silu(W_g x) * (W_u x) as in
+ * moe_expert_ffn_sparse, so the kept count varies per pair.  tau [E] fp32
+ * device thresholds, e.g. from moe_calibrate_thresholds; tau[e] < 0 keeps
+ * every neuron of expert e.
+ * counts_out: optional [T * top_k] int32, kept count of each pair;
+ * active_idx_out: optional [T * top_k, d_ff] int32, the first counts_out[p]
+ * entries of row p are pair p's kept ids, ascending.  Other parameters,
+ * outputs and errors as moe_expert_ffn_sparse (no k_keep); d_ff up to 2048
+ * (a multiple of 64) or a multiple of 512 up to 8192, else
+ * MOE_ERR_UNSUPPORTED.  workspace: moe_ffn_threshold_workspace_size(d, T).
+ */
+moe_status moe_expert_ffn_sparse_threshold(const moe_desc *d, int32_t T, const float *tau,
+                                           const void *x, const void *w_gate, const void *w_up,
+                                           const void *w_down, const moe_routing *routing,
+                                           float *y, int32_t accumulate, int32_t *counts_out,
+                                           int32_t *active_idx_out, void *workspace,
+                                           size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * moe_calibrate_thresholds -- offline calibration of the thresholds for a
+ * target sparsity s (the page sets the masking threshold ahead of time for
+ * a target sparsity; technical summary, Methodology: activation masking).
+ * On T calibration tokens x with their routing (from moe_route; NULL for
+ * the always-on group, top_k == n_experts), with the scores
+ * |h| = |silu(W_g x) * (W_u x)| of every (calibration pair, neuron):
+ *   tau[e] = the (c + 1)-th largest of expert e's m scores, c = ceil((1 - s) m),
+ *            or -1 when c = m (keep everything);
+ *   an expert that no calibration token reaches gets the same statistic
+ *   over all routed scores.
+ * So 'keep |h| > tau[e]' keeps exactly c of expert e's m calibration scores
+ * when they are distinct.  w_gate and w_up packed (moe_pack_gate_up);
+ * tau_out [E] fp32 device.  d_ff as moe_expert_ffn_sparse_threshold.
+ * Errors: sparsity outside [0, 1] (or NaN), tau_out NULL ->
+ * MOE_ERR_INVALID_ARG; T * top_k * d_ff >= 2^31 -> MOE_ERR_UNSUPPORTED
+ * (calibrate on fewer tokens).  T == 0 leaves tau_out untouched.
+ * workspace: moe_calibrate_workspace_size(d, T).
+ */
+moe_status moe_calibrate_thresholds(const moe_desc *d, int32_t T, const void *x,
+                                    const void *w_gate, const void *w_up,
+                                    const moe_routing *routing, double sparsity, float *tau_out,
+                                    void *workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Workspace bytes for moe_route over at most T tokens (0 on invalid input). */
 size_t moe_route_workspace_size(const moe_desc *d, int32_t T);
 
@@ -224,6 +270,11 @@ size_t moe_route_workspace_size(const moe_desc *d, int32_t T);
  * path (0 on invalid input).  A workspace sized for (T, k_keep) serves any
  * call with fewer tokens and the same k_keep. */
 size_t moe_ffn_workspace_size(const moe_desc *d, int32_t T, int32_t k_keep, moe_path path);
+
+/* Workspace bytes for moe_expert_ffn_sparse_threshold and for
+ * moe_calibrate_thresholds over at most T tokens (0 on invalid input). */
+size_t moe_ffn_threshold_workspace_size(const moe_desc *d, int32_t T);
+size_t moe_calibrate_workspace_size(const moe_desc *d, int32_t T);
 
 /* Kept neurons per (token, expert) at sparsity s: ceil((1 - s) * d_ff),
  * computed as ceil((1 - s) * d_ff - 1e-9) so that exact products do not

@@ -384,16 +384,22 @@ def moe_layer(x, w_router, bias, w_gate, w_up, w_down, *, top_k: int,
 
 def calibrate_thresholds(x, w_router, bias, w_gate, w_up, *, top_k: int, norm_topk: bool,
                          dtype: str, sparsity: float, score: str = "swiglu",
-                         shared: Optional[Sequence] = None) -> Tuple[np.ndarray, Optional[np.ndarray]]:
+                         shared: Optional[Sequence] = None,
+                         forced_ids=None) -> Tuple[np.ndarray, Optional[np.ndarray]]:
     """Per-expert thresholds from calibration tokens x [T, H]: each routed
     expert's tau is calibrated_threshold over the scores of every
     (calibration token routed to it, neuron) pair; an expert no token reaches
     takes the value over all routed scores.  Shared experts (every token)
     get their own.  The page sets the masking threshold offline for a target
-    sparsity (technical summary, Methodology: activation masking)."""
+    sparsity (technical summary, Methodology: activation masking).
+    ``forced_ids`` replaces the router's choice (for checking a run whose
+    near-tied router logits broke the other way)."""
     xf = to_f64(x, dtype)
     _check_finite("x", xf)
-    ids, _, _, _ = route(xf, to_f64(w_router, dtype), bias, top_k, norm_topk)
+    if forced_ids is None:
+        ids, _, _, _ = route(xf, to_f64(w_router, dtype), bias, top_k, norm_topk)
+    else:
+        ids = np.asarray(forced_ids)
     E = len(w_gate)
     per = {e: [] for e in range(E)}
     for e in range(E):

@@ -48,6 +48,10 @@ _SIGS = {
     "moe_expert_ffn_sparse": (_I32, [_PD, _I32, _I32, _V, _V, _V, _V, _PR, _V, _I32, _V, _V, _SZ, _V]),
     "moe_expert_ffn_dense": (_I32, [_PD, _I32, _I32, _V, _V, _V, _V, _PR, _V, _I32, _V, _V, _SZ, _V]),
     "moe_expert_ffn_sparse_updown": (_I32, [_PD, _I32, _I32, _V, _V, _V, _V, _PR, _V, _I32, _V, _V, _SZ, _V]),
+    "moe_expert_ffn_sparse_threshold": (_I32, [_PD, _I32, _V, _V, _V, _V, _V, _PR, _V, _I32, _V, _V, _V, _SZ, _V]),
+    "moe_calibrate_thresholds": (_I32, [_PD, _I32, _V, _V, _V, _PR, _D, _V, _V, _SZ, _V]),
+    "moe_ffn_threshold_workspace_size": (_SZ, [_PD, _I32]),
+    "moe_calibrate_workspace_size": (_SZ, [_PD, _I32]),
     "moe_pack_gate_up": (_I32, [_PD, _V, _V, _V]),
     "moe_unpack_gate_up": (_I32, [_PD, _V, _V, _V]),
     "moe_route_workspace_size": (_SZ, [_PD, _I32]),
@@ -185,6 +189,38 @@ def moe_expert_ffn_sparse_updown(desc, T, k_keep, x, w_gate, w_up, w_down, routi
     """The gate-score split: w_gate packed, w_up and w_down row-major."""
     _ffn(lib().moe_expert_ffn_sparse_updown, desc, T, k_keep, x, w_gate, w_up, w_down, routing,
          y, accumulate, active_idx_out, workspace, stream)
+
+
+def moe_expert_ffn_sparse_threshold(desc, T, tau, x, w_gate, w_up, w_down, routing, y,
+                                    accumulate=0, counts_out=None, active_idx_out=None,
+                                    workspace=None, stream=None):
+    """Threshold masking: keep |h_j| > tau[e]; tau a device float32 [E]."""
+    r = routing.as_c() if routing is not None else None
+    ws = _ptr(workspace)
+    _check(lib().moe_expert_ffn_sparse_threshold(
+        ctypes.byref(desc), int(T), _ptr(tau), _ptr(x), _ptr(w_gate), _ptr(w_up), _ptr(w_down),
+        ctypes.byref(r) if r is not None else None, _ptr(y), int(accumulate), _ptr(counts_out),
+        _ptr(active_idx_out), ws, workspace.numel() * workspace.element_size() if ws else 0,
+        _stream(stream)))
+
+
+def moe_calibrate_thresholds(desc, T, x, w_gate, w_up, routing, sparsity, tau_out,
+                             workspace=None, stream=None):
+    """Per-expert thresholds for a target sparsity from calibration tokens."""
+    r = routing.as_c() if routing is not None else None
+    ws = _ptr(workspace)
+    _check(lib().moe_calibrate_thresholds(
+        ctypes.byref(desc), int(T), _ptr(x), _ptr(w_gate), _ptr(w_up),
+        ctypes.byref(r) if r is not None else None, float(sparsity), _ptr(tau_out), ws,
+        workspace.numel() * workspace.element_size() if ws else 0, _stream(stream)))
+
+
+def moe_ffn_threshold_workspace_size(desc: MoeDesc, T: int) -> int:
+    return int(lib().moe_ffn_threshold_workspace_size(ctypes.byref(desc), int(T)))
+
+
+def moe_calibrate_workspace_size(desc: MoeDesc, T: int) -> int:
+    return int(lib().moe_calibrate_workspace_size(ctypes.byref(desc), int(T)))
 
 
 def moe_pack_gate_up(desc: MoeDesc, src, dst=None, stream=None):

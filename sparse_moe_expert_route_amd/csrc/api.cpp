@@ -78,8 +78,11 @@ size_t elem_bytes(const moe_desc *d) { return d->dtype == MOE_BF16 ? 2 : 4; }
 
 // FFN workspace layout (each segment 256-byte aligned).
 struct FfnLayout {
-  size_t h, idx, hact, partial, hm, total;
+  size_t h, idx, hact, partial, hm, counts, total;
 };
+
+// What an FFN-shaped call does (all share validation and the carve-up).
+enum RunMode { kRunSparse, kRunDense, kRunUpdown, kRunThreshold, kRunCalibrate };
 
 FfnLayout ffn_layout(const moe_desc *d, int32_t T, int32_t k, moe_path path) {
   const size_t P = (size_t)T * d->top_k;
@@ -97,21 +100,64 @@ FfnLayout ffn_layout(const moe_desc *d, int32_t T, int32_t k, moe_path path) {
     off += up(moe::dense_down_partial_rows(T, d->n_experts, d->top_k, d->hidden) * d->hidden * 4);
   L.hm = off;
   if (path == MOE_PATH_DENSE) off += up(P * d->d_ff * elem_bytes(d));
+  L.counts = off;
   L.total = off;
   return L;
 }
 
-// updown: the gate-score split (sparse path only), see moe_expert_ffn_sparse_updown.
-moe_status run_ffn(moe_path path, bool updown, const moe_desc *d, int32_t T, int32_t k_keep, const void *x,
+// Threshold masking: kept lists at row stride d_ff, plus per-pair counts.
+FfnLayout threshold_layout(const moe_desc *d, int32_t T) {
+  FfnLayout L = ffn_layout(d, T, d->d_ff, MOE_PATH_SPARSE);
+  L.counts = L.total;
+  L.total += up((size_t)T * d->top_k * 4);
+  return L;
+}
+
+// Calibration: the scores h, then the layer-wide threshold (one float).
+FfnLayout calibrate_layout(const moe_desc *d, int32_t T) {
+  FfnLayout L{};
+  L.h = 0;
+  L.counts = up((size_t)T * d->top_k * d->d_ff * 4);
+  L.total = L.counts + kAlign;
+  return L;
+}
+
+// Extra inputs and outputs of the threshold and calibration modes.
+struct ModeArgs {
+  const float *tau = nullptr;   // threshold: [E] per-expert thresholds (device)
+  int32_t *counts = nullptr;    // threshold: optional [P] kept counts (device)
+  double sparsity = 0.0;        // calibrate: target sparsity
+  float *tau_out = nullptr;     // calibrate: [E] thresholds (device)
+};
+
+moe_status run_ffn(RunMode mode, const moe_desc *d, int32_t T, int32_t k_keep, const void *x,
                    const void *w_gate, const void *w_up, const void *w_down,
                    const moe_routing *routing, float *y, int32_t accumulate,
                    int32_t *active_idx_out, void *workspace, size_t workspace_bytes,
-                   hipStream_t stream) {
+                   hipStream_t stream, const ModeArgs &m = ModeArgs{}) {
   g_err[0] = 0;
   TRY(check_desc(d));
   TRY(check_T(T));
+  const moe_path path = mode == kRunDense ? MOE_PATH_DENSE : MOE_PATH_SPARSE;
+  const bool thr = mode == kRunThreshold, cal = mode == kRunCalibrate;
+  if (thr || cal) k_keep = d->d_ff;
   if (k_keep < 0 || k_keep > d->d_ff)
     return fail(MOE_ERR_INVALID_ARG, "k_keep %d outside [0, d_ff=%d]", k_keep, d->d_ff);
+  if ((thr || cal) && !moe::threshold_supported(d->d_ff))
+    return fail(MOE_ERR_UNSUPPORTED, "threshold masking needs d_ff <= 2048 (a multiple of 64) or "
+                "a multiple of 512 up to 8192; got %d", d->d_ff);
+  if (thr && !m.tau) return fail(MOE_ERR_INVALID_ARG, "tau is NULL");
+  if (thr && ((uintptr_t)m.tau & 3u)) return fail(MOE_ERR_MISALIGNED, "tau is not 4-byte aligned");
+  if (thr && m.counts && ((uintptr_t)m.counts & 3u))
+    return fail(MOE_ERR_MISALIGNED, "counts_out is not 4-byte aligned");
+  if (cal && !(m.sparsity >= 0.0 && m.sparsity <= 1.0))
+    return fail(MOE_ERR_INVALID_ARG, "sparsity must lie in [0, 1]");
+  if (cal && !m.tau_out) return fail(MOE_ERR_INVALID_ARG, "tau_out is NULL");
+  if (cal && (long long)T * d->top_k * d->d_ff > 0x7fffffffLL)
+    return fail(MOE_ERR_UNSUPPORTED, "calibration set too large: T * top_k * d_ff = %lld >= 2^31",
+                (long long)T * d->top_k * d->d_ff);
+  if (cal && ((uintptr_t)m.tau_out & 3u))
+    return fail(MOE_ERR_MISALIGNED, "tau_out is not 4-byte aligned");
   if (accumulate != 0 && accumulate != 1)
     return fail(MOE_ERR_INVALID_ARG, "accumulate must be 0 or 1");
   if (!routing && d->top_k != d->n_experts)
@@ -122,8 +168,10 @@ moe_status run_ffn(moe_path path, bool updown, const moe_desc *d, int32_t T, int
   TRY(need_ptr(x, "x"));
   TRY(need_ptr(w_gate, "w_gate"));
   TRY(need_ptr(w_up, "w_up"));
-  TRY(need_ptr(w_down, "w_down"));
-  TRY(need_ptr(y, "y"));
+  if (!cal) {
+    TRY(need_ptr(w_down, "w_down"));
+    TRY(need_ptr(y, "y"));
+  }
   if (routing) {
     TRY(need_ptr(routing->topk_ids, "routing->topk_ids"));
     TRY(need_ptr(routing->topk_w, "routing->topk_w"));
@@ -134,7 +182,8 @@ moe_status run_ffn(moe_path path, bool updown, const moe_desc *d, int32_t T, int
   }
   if (active_idx_out && !aligned16(active_idx_out))
     return fail(MOE_ERR_MISALIGNED, "active_idx_out is not 16-byte aligned");
-  const FfnLayout L = ffn_layout(d, T, k_keep, path);
+  const FfnLayout L = thr ? threshold_layout(d, T)
+                     : cal ? calibrate_layout(d, T) : ffn_layout(d, T, k_keep, path);
   if (!workspace) return fail(MOE_ERR_WORKSPACE, "workspace is NULL");
   if (!aligned16(workspace)) return fail(MOE_ERR_MISALIGNED, "workspace is not 16-byte aligned");
   if (workspace_bytes < L.total)
@@ -169,9 +218,20 @@ moe_status run_ffn(moe_path path, bool updown, const moe_desc *d, int32_t T, int
   a.hact = path == MOE_PATH_SPARSE ? reinterpret_cast<float *>(ws + L.hact) : nullptr;
   a.partial = reinterpret_cast<float *>(ws + L.partial);
   a.hm = path == MOE_PATH_DENSE ? static_cast<void *>(ws + L.hm) : nullptr;
-  const hipError_t e =
-      updown ? moe::launch_ffn_updown(a, stream)
-             : path == MOE_PATH_SPARSE ? moe::launch_ffn_sparse(a, stream) : moe::launch_ffn_dense(a, stream);
+  hipError_t e;
+  switch (mode) {
+    case kRunUpdown: e = moe::launch_ffn_updown(a, stream); break;
+    case kRunThreshold:
+      e = moe::launch_ffn_threshold(
+          a, m.tau, m.counts ? m.counts : reinterpret_cast<int32_t *>(ws + L.counts), stream);
+      break;
+    case kRunCalibrate:
+      e = moe::launch_calibrate(a, m.sparsity, m.tau_out, reinterpret_cast<float *>(ws + L.counts),
+                                stream);
+      break;
+    case kRunDense: e = moe::launch_ffn_dense(a, stream); break;
+    default: e = moe::launch_ffn_sparse(a, stream);
+  }
   if (e != hipSuccess) return fail(MOE_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return MOE_OK;
 }
@@ -229,7 +289,7 @@ moe_status moe_expert_ffn_sparse(const moe_desc *d, int32_t T, int32_t k_keep, c
                                  const moe_routing *routing, float *y, int32_t accumulate,
                                  int32_t *active_idx_out, void *workspace,
                                  size_t workspace_bytes, hipStream_t stream) {
-  return run_ffn(MOE_PATH_SPARSE, false, d, T, k_keep, x, w_gate, w_up, w_down, routing, y, accumulate,
+  return run_ffn(kRunSparse, d, T, k_keep, x, w_gate, w_up, w_down, routing, y, accumulate,
                  active_idx_out, workspace, workspace_bytes, stream);
 }
 
@@ -238,7 +298,7 @@ moe_status moe_expert_ffn_dense(const moe_desc *d, int32_t T, int32_t k_keep, co
                                 const moe_routing *routing, float *y, int32_t accumulate,
                                 int32_t *active_idx_out, void *workspace,
                                 size_t workspace_bytes, hipStream_t stream) {
-  return run_ffn(MOE_PATH_DENSE, false, d, T, k_keep, x, w_gate, w_up, w_down, routing, y, accumulate,
+  return run_ffn(kRunDense, d, T, k_keep, x, w_gate, w_up, w_down, routing, y, accumulate,
                  active_idx_out, workspace, workspace_bytes, stream);
 }
 
@@ -248,8 +308,32 @@ moe_status moe_expert_ffn_sparse_updown(const moe_desc *d, int32_t T, int32_t k_
                                         int32_t accumulate, int32_t *active_idx_out,
                                         void *workspace, size_t workspace_bytes,
                                         hipStream_t stream) {
-  return run_ffn(MOE_PATH_SPARSE, true, d, T, k_keep, x, w_gate, w_up, w_down, routing, y,
+  return run_ffn(kRunUpdown, d, T, k_keep, x, w_gate, w_up, w_down, routing, y,
                  accumulate, active_idx_out, workspace, workspace_bytes, stream);
+}
+
+moe_status moe_expert_ffn_sparse_threshold(const moe_desc *d, int32_t T, const float *tau,
+                                           const void *x, const void *w_gate, const void *w_up,
+                                           const void *w_down, const moe_routing *routing,
+                                           float *y, int32_t accumulate, int32_t *counts_out,
+                                           int32_t *active_idx_out, void *workspace,
+                                           size_t workspace_bytes, hipStream_t stream) {
+  ModeArgs m;
+  m.tau = tau;
+  m.counts = counts_out;
+  return run_ffn(kRunThreshold, d, T, 0, x, w_gate, w_up, w_down, routing, y, accumulate,
+                 active_idx_out, workspace, workspace_bytes, stream, m);
+}
+
+moe_status moe_calibrate_thresholds(const moe_desc *d, int32_t T, const void *x,
+                                    const void *w_gate, const void *w_up,
+                                    const moe_routing *routing, double sparsity, float *tau_out,
+                                    void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  ModeArgs m;
+  m.sparsity = sparsity;
+  m.tau_out = tau_out;
+  return run_ffn(kRunCalibrate, d, T, 0, x, w_gate, w_up, nullptr, routing, nullptr, 0, nullptr,
+                 workspace, workspace_bytes, stream, m);
 }
 
 static moe_status pack_impl(const moe_desc *d, const void *src, void *dst, int unpack,
@@ -287,6 +371,16 @@ size_t moe_ffn_workspace_size(const moe_desc *d, int32_t T, int32_t k_keep, moe_
   if (k_keep < 0 || k_keep > d->d_ff) return 0;
   if (path != MOE_PATH_SPARSE && path != MOE_PATH_DENSE) return 0;
   return ffn_layout(d, T > 0 ? T : 1, k_keep, path).total;
+}
+
+size_t moe_ffn_threshold_workspace_size(const moe_desc *d, int32_t T) {
+  if (check_desc(d) != MOE_OK || check_T(T) != MOE_OK) return 0;
+  return threshold_layout(d, T > 0 ? T : 1).total;
+}
+
+size_t moe_calibrate_workspace_size(const moe_desc *d, int32_t T) {
+  if (check_desc(d) != MOE_OK || check_T(T) != MOE_OK) return 0;
+  return calibrate_layout(d, T > 0 ? T : 1).total;
 }
 
 int32_t moe_keep_count(double sparsity, int32_t d_ff) {

@@ -769,6 +769,256 @@ __global__ __launch_bounds__(1024) void down_token_kernel(const void *__restrict
   }
 }
 
+// ---------------------------------------------------------------- threshold masking
+// The page's literal masking: one pass comparing each |h_j| with the
+// pair's expert threshold tau_e (calibrated offline), no select.  Kept
+// counts vary per pair; ids and w * h are written compacted in index order
+// at row stride d_ff, with the count per pair.  Layout as the register-
+// resident select (NW waves, V values per lane, contiguous segments), so
+// positions come from one wave scan plus the per-wave totals.  tau < 0
+// keeps every neuron; otherwise |h| > tau is a compare of the bit patterns
+// (order-preserving for non-negative floats).
+template <int V, int NW>
+__global__ __launch_bounds__(64 * NW) void neuron_threshold_kernel(const float *__restrict__ h,
+                                                                   RouteView rv, int d_ff,
+                                                                   const float *__restrict__ tau,
+                                                                   int32_t *__restrict__ idx,
+                                                                   float *__restrict__ coef,
+                                                                   int32_t *__restrict__ counts) {
+  __shared__ int wtot[NW];
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int p = blockIdx.x;
+  const float w = rv.weight(p);
+  const float te = tau[rv.expert_of_pair(p)];
+  const bool all = te < 0.f;
+  const uint32_t tkey = __float_as_uint(fabsf(te));
+  const int seg = (wid * 64 + lane) * V;
+  uint32_t bits[V];
+  const float *hp = h + (size_t)p * d_ff + seg;
+  if (V % 4 == 0) {
+#pragma unroll
+    for (int i = 0; i < V; i += 4) {
+      const u32x4 q = ld16(hp + i);
+      bits[i] = q[0]; bits[i + 1] = q[1]; bits[i + 2] = q[2]; bits[i + 3] = q[3];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < V; ++i) bits[i] = __float_as_uint(hp[i]);
+  }
+  int n = 0;
+#pragma unroll
+  for (int i = 0; i < V; ++i) n += all || (bits[i] & 0x7fffffffu) > tkey;
+  const int incl = wave_incl_scan(n);
+  int pos = incl - n;
+  if (NW > 1) {
+    if (lane == 63) wtot[wid] = incl;
+    __syncthreads();
+    for (int ww = 0; ww < wid; ++ww) pos += wtot[ww];
+  }
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+    if (all || (bits[i] & 0x7fffffffu) > tkey) {
+      idx[(size_t)p * d_ff + pos] = seg + i;
+      coef[(size_t)p * d_ff + pos] = w * __uint_as_float(bits[i]);
+      ++pos;
+    }
+  }
+  if (wid == NW - 1 && lane == 63) counts[p] = pos;  // the last segment's end = the count
+}
+
+// ---------------------------------------------------------------- variable-count sparse down
+// down_token_kernel for per-pair kept counts (threshold masking): the
+// token's pairs' lists (ids and coefficients at row stride d_ff, counts[p]
+// entries each) are concatenated in slot order and staged into LDS in
+// chunks of kDownStage rows, each chunk streamed like down_token_kernel's
+// (SW-column row slices, 4 load instructions in flight per wave) before
+// the next is staged; lane folds then waves reduce in a fixed order.
+template <bool BF16, int SW>
+__global__ __launch_bounds__(1024) void down_var_token_kernel(const void *__restrict__ wdv,
+                                                              const int32_t *__restrict__ idx,
+                                                              const float *__restrict__ coef,
+                                                              const int32_t *__restrict__ counts,
+                                                              RouteView rv, int H, int d_ff,
+                                                              int accumulate,
+                                                              float *__restrict__ y) {
+  constexpr int VEC = BF16 ? 8 : 4;
+  constexpr int LPR = SW / VEC;
+  constexpr int RPI = 64 / LPR;
+  __shared__ float red[kDownWaves][SW];
+  __shared__ uint32_t srow[kDownStage];
+  __shared__ float scoef[kDownStage];
+  __shared__ int pref[33];  // row offset of each slot's list (top_k <= 32)
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int t = blockIdx.x, col0 = blockIdx.y * SW;
+  const int top_k = rv.top_k;
+  if (threadIdx.x < top_k) {
+    const int c = counts[t * top_k + threadIdx.x];
+    pref[threadIdx.x + 1] = c < 0 ? 0 : (c > d_ff ? d_ff : c);
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    pref[0] = 0;
+    for (int s = 1; s <= top_k; ++s) pref[s] += pref[s - 1];
+  }
+  __syncthreads();
+  const int nrows = pref[top_k];
+  const int sub = lane % LPR, rsel = lane / LPR;
+  const size_t colo = (size_t)col0 + sub * VEC;
+  float acc[VEC];
+#pragma unroll
+  for (int v = 0; v < VEC; ++v) acc[v] = 0.f;
+  for (int base = 0; base < nrows; base += kDownStage) {
+    const int n = min(kDownStage, nrows - base);
+    for (int q = threadIdx.x; q < n; q += 1024) {
+      const int qq = base + q;
+      int lo = 0, hi = top_k;  // the slot s with pref[s] <= qq < pref[s + 1]
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (pref[mid] <= qq) lo = mid; else hi = mid;
+      }
+      const int p = t * top_k + lo, i = qq - pref[lo];
+      int j = idx[(size_t)p * d_ff + i];
+      j = (unsigned)j < (unsigned)d_ff ? j : 0;
+      srow[q] = (uint32_t)rv.expert_of_pair(p) * (uint32_t)d_ff + (uint32_t)j;
+      scoef[q] = coef[(size_t)p * d_ff + i];
+    }
+    __syncthreads();
+    constexpr int U = 4;
+    for (int b0 = wid; b0 * RPI < n; b0 += kDownWaves * U) {
+      u32x4 qv[U];
+      float c[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int qq = (b0 + kDownWaves * u) * RPI + rsel;
+        c[u] = 0.f;
+        qv[u] = u32x4{0, 0, 0, 0};
+        if (qq < n) {
+          const size_t off = (size_t)srow[qq] * H + colo;
+          c[u] = scoef[qq];
+          qv[u] = BF16 ? ld16(static_cast<const uint16_t *>(wdv) + off)
+                       : ld16(static_cast<const float *>(wdv) + off);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (BF16) {
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            acc[2 * jj] = fmaf(c[u], bf16lo(qv[u][jj]), acc[2 * jj]);
+            acc[2 * jj + 1] = fmaf(c[u], bf16hi(qv[u][jj]), acc[2 * jj + 1]);
+          }
+        } else {
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) acc[jj] = fmaf(c[u], __uint_as_float(qv[u][jj]), acc[jj]);
+        }
+      }
+    }
+    __syncthreads();  // the chunk is consumed before the next is staged
+  }
+#pragma unroll
+  for (int o = LPR; o < 64; o <<= 1) {
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) acc[v] += __shfl_xor(acc[v], o, 64);
+  }
+  if (rsel == 0) {
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) red[wid][sub * VEC + v] = acc[v];
+  }
+  __syncthreads();
+  if (threadIdx.x < SW) {
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < kDownWaves; ++w) v += red[w][threadIdx.x];
+    float *yp = y + (size_t)t * H + col0 + threadIdx.x;
+    *yp = accumulate ? *yp + v : v;
+  }
+}
+
+// ---------------------------------------------------------------- threshold calibration
+// tau for one score set: the (c + 1)-th largest |h| of its m scores, c =
+// ceil((1 - s) m - 1e-9) (the keep count), or -1 when c >= m.  Block b < E
+// takes expert b's scores (its pairs' h rows, all d_ff neurons); block E
+// takes every pair's.  An exact radix select over the float-field digits
+// of |h| in global memory: 4 passes of block histograms (per-wave LDS
+// histograms summed), each keeping the digit whose bucket holds the target
+// rank.  Experts with no scores are left for calibrate_fill_kernel.
+__global__ __launch_bounds__(1024) void calibrate_kernel(const float *__restrict__ h, RouteView rv,
+                                                         int d_ff, double sparsity,
+                                                         float *__restrict__ tau,
+                                                         float *__restrict__ tau_all) {
+  __shared__ int hist[16][256];
+  __shared__ int tot[256];
+  __shared__ int sel[2];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int e = blockIdx.x;
+  const bool layer = e == rv.E;
+  int q0 = 0, q1 = 0;
+  if (layer) {
+    q1 = rv.T * rv.top_k;     // every pair, in pair-id order
+  } else if (rv.implicit) {
+    q0 = e * rv.T;
+    q1 = q0 + rv.T;
+  } else {
+    q0 = rv.offsets[e];
+    q1 = rv.offsets[e + 1];
+  }
+  const long long m = (long long)(q1 - q0) * d_ff;
+  if (m == 0) return;  // block-uniform
+  const long long c = (long long)ceil((1.0 - sparsity) * (double)m - 1e-9);
+  float result = -1.f;
+  if (c < m) {
+    long long krem = c + 1;  // rank of tau among the keys, descending (1-based)
+    uint32_t pre = 0, pmask = 0;
+    for (int pass = 0; pass < 4; ++pass) {
+      const int shift = pass == 0 ? 23 : pass == 1 ? 15 : pass == 2 ? 7 : 0;
+      const uint32_t dmask = pass == 3 ? 0x7fu : 0xffu;
+      for (int i = lane; i < 256; i += 64) hist[wid][i] = 0;
+      __syncthreads();
+      for (long long z = tid; z < m; z += 1024) {
+        const int qi = (int)(z / d_ff), j = (int)(z - (long long)qi * d_ff);
+        const int p = layer ? q0 + qi : rv.pair_at(q0 + qi);
+        const uint32_t key = __float_as_uint(h[(size_t)p * d_ff + j]) & 0x7fffffffu;
+        if ((key & pmask) == pre) atomicAdd(&hist[wid][(key >> shift) & dmask], 1);
+      }
+      __syncthreads();
+      if (tid < 256) {
+        int n = 0;
+        for (int w = 0; w < 16; ++w) n += hist[w][tid];
+        tot[tid] = n;
+      }
+      __syncthreads();
+      if (tid == 0) {  // 256 buckets, descending: a short serial walk
+        long long run = 0;
+        int d = 255;
+        for (; d > 0; --d) {
+          if (run + tot[d] >= krem) break;
+          run += tot[d];
+        }
+        sel[0] = d;
+        sel[1] = (int)(krem - run);
+      }
+      __syncthreads();
+      pre |= (uint32_t)sel[0] << shift;
+      pmask |= dmask << shift;
+      krem = sel[1];
+      __syncthreads();
+    }
+    result = __uint_as_float(pre);
+  }
+  if (tid == 0) {
+    if (layer) *tau_all = result;
+    else tau[e] = result;
+  }
+}
+
+__global__ __launch_bounds__(64) void calibrate_fill_kernel(RouteView rv, const float *tau_all,
+                                                            float *__restrict__ tau) {
+  for (int e = threadIdx.x; e < rv.E; e += 64) {
+    const int n = rv.implicit ? rv.T : rv.offsets[e + 1] - rv.offsets[e];
+    if (n == 0) tau[e] = *tau_all;
+  }
+}
+
 // ---------------------------------------------------------------- dense down (bf16)
 // Dense-path down GEMM: partial[pair, chunk, col] = sum over the chunk's k of
 // hm[pair, k] * W_d[e][k, col], for a work item (expert, <= 128 of its
@@ -1100,6 +1350,71 @@ hipError_t launch_ffn_updown(const FfnArgs &a, hipStream_t stream) {
     up_rows_kernel<false><<<grid, 64, 0, stream>>>(a.w_up, a.x, rv, a.H, a.d_ff, a.k_keep, a.idx, a.hact);
   timer_end(stream);
   launch_down_token(a, rv, a.idx, a.hact, a.k_keep, stream);
+  return hipGetLastError();
+}
+
+// Register-segment layout of the threshold mask for this d_ff, as the
+// select's: 4 waves up to 2048 (multiples of 256), 1 wave for the other
+// multiples of 64 up to 2048, 8 waves from 2560 to 8192 (multiples of 512).
+bool threshold_supported(int d_ff) {
+  if (d_ff <= 2048) return d_ff % 64 == 0;
+  return d_ff % 512 == 0 && d_ff <= 8192;
+}
+
+// The page's literal masking: gate/up, one compare pass against tau[e],
+// then the variable-count sparse down projection.
+hipError_t launch_ffn_threshold(const FfnArgs &a, const float *tau, int32_t *counts,
+                                hipStream_t stream) {
+  if (a.T == 0) return hipSuccess;
+  const RouteView rv = make_view(a);
+  launch_gateup(a, rv, stream);
+  const int P = a.T * a.top_k;
+  timer_begin(kStageMask, stream);
+  switch (a.d_ff) {
+#define MOE_THR_CASE(V, NW)                                                                     \
+  case 64 * V * NW:                                                                             \
+    neuron_threshold_kernel<V, NW><<<P, 64 * NW, 0, stream>>>(a.h, rv, a.d_ff, tau, a.idx, a.hact, \
+                                                             counts);                           \
+    break;
+    MOE_THR_CASE(1, 4) MOE_THR_CASE(2, 4) MOE_THR_CASE(3, 4) MOE_THR_CASE(4, 4)
+    MOE_THR_CASE(5, 4) MOE_THR_CASE(6, 4) MOE_THR_CASE(7, 4) MOE_THR_CASE(8, 4)
+    MOE_THR_CASE(1, 1) MOE_THR_CASE(2, 1) MOE_THR_CASE(3, 1) MOE_THR_CASE(5, 1)
+    MOE_THR_CASE(6, 1) MOE_THR_CASE(7, 1) MOE_THR_CASE(9, 1) MOE_THR_CASE(10, 1)
+    MOE_THR_CASE(11, 1) MOE_THR_CASE(13, 1) MOE_THR_CASE(14, 1) MOE_THR_CASE(15, 1)
+    MOE_THR_CASE(17, 1) MOE_THR_CASE(18, 1) MOE_THR_CASE(19, 1) MOE_THR_CASE(21, 1)
+    MOE_THR_CASE(22, 1) MOE_THR_CASE(23, 1) MOE_THR_CASE(25, 1) MOE_THR_CASE(26, 1)
+    MOE_THR_CASE(27, 1) MOE_THR_CASE(29, 1) MOE_THR_CASE(30, 1) MOE_THR_CASE(31, 1)
+    MOE_THR_CASE(5, 8) MOE_THR_CASE(6, 8) MOE_THR_CASE(7, 8) MOE_THR_CASE(8, 8)
+    MOE_THR_CASE(9, 8) MOE_THR_CASE(10, 8) MOE_THR_CASE(11, 8) MOE_THR_CASE(12, 8)
+    MOE_THR_CASE(13, 8) MOE_THR_CASE(14, 8) MOE_THR_CASE(15, 8) MOE_THR_CASE(16, 8)
+#undef MOE_THR_CASE
+    default:
+      timer_end(stream);
+      return hipErrorInvalidValue;  // excluded by threshold_supported()
+  }
+  timer_end(stream);
+  const int sw = down_block_cols(a.T, a.H);
+  dim3 grid(a.T, a.H / sw);
+  timer_begin(kStageDownRows, stream);
+#define MOE_DV(BF, SWV)                                                                           \
+  down_var_token_kernel<BF, SWV><<<grid, 1024, 0, stream>>>(a.w_down, a.idx, a.hact, counts, rv, \
+                                                            a.H, a.d_ff, a.accumulate, a.y)
+  if (a.bf16) { if (sw == 128) MOE_DV(true, 128); else MOE_DV(true, 64); }
+  else { if (sw == 128) MOE_DV(false, 128); else MOE_DV(false, 64); }
+#undef MOE_DV
+  timer_end(stream);
+  return hipGetLastError();
+}
+
+// Calibration: gate/up on the calibration tokens, then the per-expert
+// order statistic (and the layer-wide one for experts without tokens).
+hipError_t launch_calibrate(const FfnArgs &a, double sparsity, float *tau, float *tau_all,
+                            hipStream_t stream) {
+  if (a.T == 0) return hipSuccess;
+  const RouteView rv = make_view(a);
+  launch_gateup(a, rv, stream);
+  calibrate_kernel<<<a.E + 1, 1024, 0, stream>>>(a.h, rv, a.d_ff, sparsity, tau, tau_all);
+  calibrate_fill_kernel<<<1, 64, 0, stream>>>(rv, tau_all, tau);
   return hipGetLastError();
 }
 

@@ -119,6 +119,65 @@ class DeviceLayer:
         return out
 
 
+    def run_threshold(self, x_host: np.ndarray, tau, tau_sh=None):
+        """One layer call with threshold masking (tau: device float32 [E])."""
+        sh = self.inp.shape
+        T = x_host.shape[0]
+        x = to_dev(x_host)
+        R = B.Routing.allocate(T, sh.top_k, sh.n_experts)
+        ws_r = torch.empty(B.moe_route_workspace_size(self.desc, T), dtype=torch.uint8, device="cuda")
+        B.moe_route(self.desc, T, x, self.w_router, self.bias, R, ws_r)
+        y = torch.full((T, sh.hidden), float("nan"), dtype=torch.float32, device="cuda")
+        P = T * sh.top_k
+        idx = torch.full((P, sh.d_ff), -1, dtype=torch.int32, device="cuda")
+        cnt = torch.full((P,), -1, dtype=torch.int32, device="cuda")
+        ws = torch.empty(B.moe_ffn_threshold_workspace_size(self.desc, T), dtype=torch.uint8,
+                         device="cuda")
+        B.moe_expert_ffn_sparse_threshold(self.desc, T, tau, x, *self.w, R, y, 0, cnt, idx, ws)
+        out = dict(T=T)
+        if self.desc_sh is not None:
+            ds = self.desc_sh
+            idx_sh = torch.full((T * ds.top_k, ds.d_ff), -1, dtype=torch.int32, device="cuda")
+            cnt_sh = torch.full((T * ds.top_k,), -1, dtype=torch.int32, device="cuda")
+            ws2 = torch.empty(B.moe_ffn_threshold_workspace_size(ds, T), dtype=torch.uint8,
+                              device="cuda")
+            B.moe_expert_ffn_sparse_threshold(ds, T, tau_sh, x, *self.w_sh, None, y, 1, cnt_sh,
+                                              idx_sh, ws2)
+            torch.cuda.synchronize()
+            out.update(idx_sh=idx_sh.cpu().numpy(), cnt_sh=cnt_sh.cpu().numpy())
+        torch.cuda.synchronize()
+        out.update(ids=R.topk_ids.cpu().numpy()[:T], w=R.topk_w.cpu().numpy()[:T],
+                   idx=idx.cpu().numpy(), cnt=cnt.cpu().numpy(), y=y.cpu().numpy())
+        return out
+
+    def route_ids(self, x_host: np.ndarray) -> np.ndarray:
+        """The library's expert ids [T, top_k] for tokens x."""
+        T = x_host.shape[0]
+        R = B.Routing.allocate(T, self.desc.top_k, self.desc.n_experts)
+        ws_r = torch.empty(B.moe_route_workspace_size(self.desc, T), dtype=torch.uint8,
+                           device="cuda")
+        B.moe_route(self.desc, T, to_dev(x_host), self.w_router, self.bias, R, ws_r)
+        torch.cuda.synchronize()
+        return R.topk_ids.cpu().numpy()[:T]
+
+    def calibrate(self, x_host: np.ndarray, sparsity: float, shared: bool = False):
+        """moe_calibrate_thresholds on calibration tokens; host float32 [E]."""
+        T = x_host.shape[0]
+        x = to_dev(x_host)
+        if shared:
+            desc, w, R = self.desc_sh, self.w_sh, None
+        else:
+            desc, w = self.desc, self.w
+            R = B.Routing.allocate(T, desc.top_k, desc.n_experts)
+            ws_r = torch.empty(B.moe_route_workspace_size(desc, T), dtype=torch.uint8, device="cuda")
+            B.moe_route(desc, T, x, self.w_router, self.bias, R, ws_r)
+        tau = torch.full((desc.n_experts,), float("nan"), dtype=torch.float32, device="cuda")
+        ws = torch.empty(B.moe_calibrate_workspace_size(desc, T), dtype=torch.uint8, device="cuda")
+        B.moe_calibrate_thresholds(desc, T, x, w[0], w[1], R, sparsity, tau, ws)
+        torch.cuda.synchronize()
+        return tau.cpu().numpy()
+
+
 # ------------------------------------------------------------------ comparison
 
 def ambiguous(scores: np.ndarray, k: int) -> np.ndarray:
@@ -161,6 +220,20 @@ def rel_l2(a, b) -> float:
     return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
 
 
+def check_routing(inp: LayerInputs, xs, ids_g, tokens=None):
+    """GPU expert ids for tokens xs against the oracle's router: equal as
+    sets up to the window rule on the logits, slots in descending logit."""
+    sh = inp.shape
+    tokens = np.arange(xs.shape[0]) if tokens is None else tokens
+    ids0, _, logits0, _ = oracle.route(oracle.to_f64(xs, sh.dtype),
+                                       oracle.to_f64(inp.w_router, sh.dtype),
+                                       inp.bias, sh.top_k, sh.norm_topk)
+    for i, t in enumerate(tokens):
+        check_selection(ids_g[i], ids0[i], logits0[i], sh.top_k, f"route t={t}")
+        lg = logits0[i][ids_g[i]]
+        assert np.all(np.diff(lg) <= WINDOW * np.abs(lg[:-1]) + 1e-30), f"slot order t={t}"
+
+
 def compare_layer(inp: LayerInputs, x_host, got, k, k_sh=None, tokens=None, score="swiglu"):
     """Check a GPU layer result against the oracle; returns the rel L2 error.
 
@@ -177,15 +250,9 @@ def compare_layer(inp: LayerInputs, x_host, got, k, k_sh=None, tokens=None, scor
         ks = k_sh if k_sh is not None else sh.d_ff_shared
     kw = dict(top_k=sh.top_k, norm_topk=sh.norm_topk, k_keep=k, dtype=sh.dtype,
               shared=shared, k_keep_shared=ks, score=score)
-    ids0, _, logits0, _ = oracle.route(oracle.to_f64(xs, sh.dtype),
-                                       oracle.to_f64(inp.w_router, sh.dtype),
-                                       inp.bias, sh.top_k, sh.norm_topk)
     ids_g = got["ids"][tokens]
     # 1. routing: as sets, window rule on the logits; slot order descending
-    for i, t in enumerate(tokens):
-        check_selection(ids_g[i], ids0[i], logits0[i], sh.top_k, f"route t={t}")
-        lg = logits0[i][ids_g[i]]
-        assert np.all(np.diff(lg) <= WINDOW * np.abs(lg[:-1]) + 1e-30), f"slot order t={t}"
+    check_routing(inp, xs, ids_g, tokens)
     # 2. masks against the oracle forced to the GPU's experts
     r1 = oracle.moe_layer(xs, inp.w_router, inp.bias, inp.wg, inp.wu, inp.wd,
                           forced_ids=ids_g, **kw)
@@ -214,6 +281,61 @@ def compare_layer(inp: LayerInputs, x_host, got, k, k_sh=None, tokens=None, scor
         r2 = oracle.moe_layer(xs, inp.w_router, inp.bias, inp.wg, inp.wu, inp.wd,
                               forced_ids=ids_g, forced_keep=forced_keep or None,
                               forced_keep_shared=forced_keep_sh or None, keep_h=False, **kw)
+    y_g = got["y"][tokens]
+    assert np.all(np.isfinite(y_g)), "non-finite output"
+    err = rel_l2(y_g, r2.y)
+    assert err <= TOL[sh.dtype], f"rel L2 {err:.3e} > {TOL[sh.dtype]}"
+    return err
+
+
+def check_threshold_selection(got, scores, tau, what):
+    """A threshold mask may differ from the oracle's only on scores within
+    the window of tau."""
+    want = set(int(j) for j in np.nonzero(np.abs(scores) > tau)[0])
+    got = set(int(j) for j in got)
+    diff = got ^ want
+    if tau >= 0:
+        bad = [j for j in diff if abs(abs(scores[j]) - tau) > WINDOW * max(tau, 1e-30)]
+    else:
+        bad = sorted(diff)
+    assert not bad, f"{what}: threshold mask differs away from tau at {bad[:8]}"
+    return bool(diff)
+
+
+def compare_threshold_layer(inp: LayerInputs, x_host, got, tau, tau_sh=None, tokens=None):
+    """Check a threshold-masked GPU layer against the oracle given the same
+    (float32) thresholds; returns the rel L2 error."""
+    sh = inp.shape
+    T = x_host.shape[0]
+    tokens = np.arange(T) if tokens is None else np.asarray(tokens)
+    xs = x_host[tokens]
+    tau64 = np.asarray(tau, dtype=np.float64)
+    tsh64 = None if tau_sh is None else np.asarray(tau_sh, dtype=np.float64)
+    kw = dict(top_k=sh.top_k, norm_topk=sh.norm_topk, k_keep=0, dtype=sh.dtype,
+              shared=inp.shared, thresholds=tau64, thresholds_shared=tsh64)
+    ids_g = got["ids"][tokens]
+    check_routing(inp, xs, ids_g, tokens)
+    r1 = oracle.moe_layer(xs, inp.w_router, inp.bias, inp.wg, inp.wu, inp.wd,
+                          forced_ids=ids_g, **kw)
+    np.testing.assert_allclose(got["w"][tokens], r1.weights, rtol=1e-4, atol=1e-7)
+    fk, fks = {}, {}
+    for i, t in enumerate(tokens):
+        for s in range(sh.top_k):
+            p = t * sh.top_k + s
+            n = int(got["cnt"][p])
+            g = got["idx"][p, :n]
+            assert np.all(np.diff(g) > 0), f"kept ids not ascending t={t} s={s}"
+            check_threshold_selection(g, r1.h[(i, s)], tau64[int(ids_g[i, s])], f"t={t} s={s}")
+            fk[(i, s)] = g
+        if inp.shared is not None:
+            for j in range(sh.n_shared):
+                p = t * sh.n_shared + j
+                n = int(got["cnt_sh"][p])
+                g = got["idx_sh"][p, :n]
+                check_threshold_selection(g, r1.h_shared[(i, j)], tsh64[j], f"shared t={t} j={j}")
+                fks[(i, j)] = g
+    r2 = oracle.moe_layer(xs, inp.w_router, inp.bias, inp.wg, inp.wu, inp.wd, forced_ids=ids_g,
+                          forced_keep=fk, forced_keep_shared=fks or None, keep_h=False, **kw)
     y_g = got["y"][tokens]
     assert np.all(np.isfinite(y_g)), "non-finite output"
     err = rel_l2(y_g, r2.y)

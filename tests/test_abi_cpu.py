@@ -147,6 +147,29 @@ def test_ffn_validation(fn_name):
     assert B.moe_last_error() == ""
 
 
+def test_threshold_and_calibration_validation():
+    d = _desc()
+    r = B.MoeRouting(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    ws = B.moe_ffn_threshold_workspace_size(d, 4)
+    assert ws > B.moe_ffn_workspace_size(d, 4, 1024, 0) - 1
+    F = lambda dd, tau=FAKE, counts=None, wsb=ws: L.moe_expert_ffn_sparse_threshold(
+        ctypes.byref(dd), 4, tau, FAKE, FAKE, FAKE, FAKE, ctypes.byref(r), FAKE, 0, counts, None,
+        FAKE, wsb, None)
+    assert F(d, tau=None) == INV
+    assert F(d, tau=FAKE + 2) == MISA
+    assert F(d, counts=FAKE + 2) == MISA
+    assert F(d, wsb=ws - 1) == WSP
+    assert F(_desc(d_ff=2112)) == UNS            # no register layout for this width
+    C = lambda dd, s=0.9, tau=FAKE, wsb=1 << 34: L.moe_calibrate_thresholds(
+        ctypes.byref(dd), 4, FAKE, FAKE, FAKE, ctypes.byref(r), s, tau, FAKE, wsb, None)
+    assert C(d, s=1.5) == INV
+    assert C(d, s=float("nan")) == INV
+    assert C(d, tau=None) == INV
+    assert C(d, wsb=B.moe_calibrate_workspace_size(d, 4) - 1) == WSP
+    assert C(_desc(d_ff=2112)) == UNS
+    assert B.moe_calibrate_workspace_size(_desc(hidden=100), 4) == 0
+
+
 def test_pack_validation():
     d = _desc()
     nbytes = 64 * 1024 * 2048 * 2

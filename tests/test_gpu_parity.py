@@ -18,8 +18,8 @@ import moe_synth as S
 from oracle import moe_oracle as O
 from sparse_moe_expert_route_amd import binding as B
 
-from parity import (DeviceLayer, LayerInputs, check_grouping, compare_layer, pack_reference,
-                    rel_l2, to_dev)
+from parity import (DeviceLayer, LayerInputs, check_grouping, check_routing, compare_layer,
+                    compare_threshold_layer, pack_reference, rel_l2, to_dev)
 
 pytestmark = pytest.mark.gpu
 SP, DN = B.MOE_PATH_SPARSE, B.MOE_PATH_DENSE
@@ -144,6 +144,62 @@ def test_updown_reads_only_kept_up_and_down_rows_and_is_reproducible():
     c = dev.run(x, k, SP, poison_rows=wd, poison_up=wu)
     assert np.all(np.isfinite(c["y"]))
     np.testing.assert_array_equal(a["y"], c["y"])
+
+
+# ------------------------------------------------------------------ threshold masking
+
+THRESH = [("tiny-f32", 8, 4, 0.9), ("olmoe-like", 32, 16, 0.9), ("olmoe-like", 32, 4, 0.5),
+          ("qwen3-moe-like", 64, 8, 0.9), ("deepseek-v2-like", 8, 4, 0.9),
+          ("llama4-like", 4, 2, 0.9)]
+
+
+@pytest.mark.parametrize("name,T_cal,T,s", THRESH)
+def test_threshold_calibration_and_masking(name, T_cal, T, s):
+    inp, dev = layer(name)
+    sh = inp.shape
+    x_cal = inp.tokens(T_cal, 21)
+    say(f"[case] threshold {name} T_cal={T_cal} T={T} s={s}")
+    tau = dev.calibrate(x_cal, s)
+    tau_sh = dev.calibrate(x_cal, s, shared=True) if sh.n_shared else None
+    ids_cal = dev.route_ids(x_cal)
+    check_routing(inp, x_cal, ids_cal)
+    t_or, t_or_sh = O.calibrate_thresholds(x_cal, inp.w_router, inp.bias, inp.wg, inp.wu,
+                                           top_k=sh.top_k, norm_topk=sh.norm_topk,
+                                           dtype=sh.dtype, sparsity=s, shared=inp.shared,
+                                           forced_ids=ids_cal)
+    # order statistics move by at most the scores' own rounding
+    np.testing.assert_allclose(tau, t_or, rtol=1e-4, atol=1e-7)
+    if tau_sh is not None:
+        np.testing.assert_allclose(tau_sh, t_or_sh, rtol=1e-4, atol=1e-7)
+    x = inp.tokens(T, 22)
+    got = dev.run_threshold(x, torch.from_numpy(tau).cuda(),
+                            torch.from_numpy(tau_sh).cuda() if tau_sh is not None else None)
+    err = compare_threshold_layer(inp, x, got, tau, tau_sh, tokens=_sample(T, 6))
+    say(f"   rel_l2={err:.3e} mean kept {got['cnt'].mean():.1f}")
+
+
+def test_threshold_extremes_and_calibration_target():
+    inp, dev = layer("olmoe-like")
+    x = inp.tokens(16, 23)
+    E = inp.shape.n_experts
+    say("[case] threshold extremes")
+    # tau < 0 keeps everything: the dense SwiGLU MoE, the same as k = d_ff
+    allk = dev.run_threshold(x, torch.full((E,), -1.0, device="cuda"))
+    assert np.all(allk["cnt"] == inp.shape.d_ff)
+    full = dev.run(x, inp.shape.d_ff, SP)
+    assert rel_l2(allk["y"], full["y"]) < 1e-5
+    # a huge tau keeps nothing: y == 0
+    none = dev.run_threshold(x, torch.full((E,), 1e30, device="cuda"))
+    assert np.all(none["cnt"] == 0) and np.all(none["y"] == 0)
+    # calibrated on these very tokens, each expert keeps its target count
+    for s in (0.5, 0.9):
+        tau = dev.calibrate(x, s)
+        got = dev.run_threshold(x, torch.from_numpy(tau).cuda())
+        ids = got["ids"].reshape(-1)
+        for e in np.unique(ids):
+            n = int(got["cnt"][ids == e].sum())
+            m = int((ids == e).sum()) * inp.shape.d_ff
+            assert n == O.keep_count(s, m), (e, n, m)
 
 
 # ------------------------------------------------------------------ ragged shapes and edges
