@@ -45,6 +45,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak, GB/s
 LAYER = "olmoe-like"
 MALL_DEFEAT_BYTES = 1 << 30    # bytes touched between reuses of one weight copy
+CAL_SEED, CAL_TOKENS = 1000, 256   # threshold calibration set (a seed no timed batch uses)
 
 
 def log(*a):
@@ -91,7 +92,7 @@ class Workload:
         self.auto_path = B.moe_select_path(self.desc, T, self.k)
         self.path = self.auto_path if forced is None else forced
         self.score = score
-        if score == "gate":   # the split has a sparse form only
+        if score in ("gate", "threshold"):   # these masks have a sparse form only
             self.path = B.MOE_PATH_SPARSE
         # always-on shared experts (routing NULL, accumulated into y)
         self.desc_sh = None
@@ -125,9 +126,33 @@ class Workload:
                               dtype=torch.uint8, device="cuda")
         self.y = [torch.empty((T, sh.hidden), dtype=torch.float32, device="cuda") for _ in range(self.L)]
         self.idx = torch.empty((T * K, max(1, self.k)), dtype=torch.int32, device="cuda")
+        if score == "threshold":
+            # per-expert tau for the target sparsity, calibrated once offline on
+            # tokens of another seed (the thresholds are fixed before serving)
+            x_cal = host_w.to_dev(S.tokens(sh, CAL_SEED, CAL_TOKENS))
+            r_cal = B.Routing.allocate(CAL_TOKENS, K, E)
+            ws_c = torch.empty(B.moe_route_workspace_size(self.desc, CAL_TOKENS), dtype=torch.uint8,
+                               device="cuda")
+            B.moe_route(self.desc, CAL_TOKENS, x_cal, dev_w0[0], None, r_cal, ws_c)
+            ws_c = torch.empty(B.moe_calibrate_workspace_size(self.desc, CAL_TOKENS),
+                               dtype=torch.uint8, device="cuda")
+            self.tau = torch.empty(E, dtype=torch.float32, device="cuda")
+            B.moe_calibrate_thresholds(self.desc, CAL_TOKENS, x_cal, dev_w0[1], dev_w0[2], r_cal,
+                                       sparsity, self.tau, ws_c)
+            torch.cuda.synchronize()
+            del ws_c, r_cal, x_cal
+            self.ws = torch.empty(B.moe_ffn_threshold_workspace_size(self.desc, T),
+                                  dtype=torch.uint8, device="cuda")
+            self.idx = torch.empty((T * K, sh.d_ff), dtype=torch.int32, device="cuda")
+            self.counts = torch.empty(T * K, dtype=torch.int32, device="cuda")
         self.ffn = B.moe_expert_ffn_sparse if self.path == B.MOE_PATH_SPARSE else B.moe_expert_ffn_dense
         if score == "gate":   # the page's own split (w_up row-major in dev_w0)
             self.ffn = B.moe_expert_ffn_sparse_updown
+        if score == "threshold":  # the page's literal mask: |h| > tau[e], counts vary
+            self.ffn = lambda d, T_, k, x, wg, wu, wd, r, y, acc, idx, ws: \
+                B.moe_expert_ffn_sparse_threshold(d, T_, self.tau, x, wg, wu, wd, r, y, acc,
+                                                  self.counts if idx is not None else None,
+                                                  idx, ws)
         self.graphs = []
 
     def step(self, i, idx=None):
@@ -190,14 +215,18 @@ class Workload:
             P = ids.shape[0]
             bw = 2 if sh.dtype == "bf16" else 4
             H, d = sh.hidden, sh.d_ff
-            union = sum(len(np.unique(idx[ids == e, :self.k])) for e in active)
+            cnt = (self.counts.cpu().numpy() if self.score == "threshold"
+                   else np.full(P, self.k, dtype=np.int64))
+            kept = [idx[p, :cnt[p]] for p in range(P)]
+            union = sum(len(np.unique(np.concatenate([kept[p] for p in np.nonzero(ids == e)[0]])))
+                        for e in active)
             rec = dict(
                 active=int(len(active)), pairs=int(P),
                 router=sh.n_experts * H * bw,
                 gateup=(int(len(active)) * (2 if self.score == "swiglu" else 1) * H * d * bw
                         + self.T * H * bw + P * d * 4),
                 up_rows=P * self.k * H * bw if self.score == "gate" else 0,
-                down_rows=P * self.k * H * bw,
+                down_rows=int(cnt.sum()) * H * bw, mean_kept=float(cnt.mean()),
                 down_union=union * H * bw,
                 down_dense=int(len(active)) * d * H * bw,
                 io=self.T * H * (bw + 4))
@@ -320,6 +349,7 @@ def measure(shape, host, dev_w0, T, args, path=None, dev_sh0=None, score="swiglu
                layer_bytes=mean("layer"), layer_min_bytes=mean("layer_min"),
                gateup_bytes=mean("gateup"), down_bytes=mean("down_rows"),
                down_union_bytes=mean("down_union"), active_experts=mean("active"),
+               mean_kept=mean("mean_kept"),
                flops_gateup=mean("flops_gateup"), flops_down_dense=mean("flops_down_dense"),
                auto_path="sparse" if wl.auto_path == 0 else "dense", kernels=kern)
     res["hbm_gbs"] = res["layer_bytes"] / sec / 1e9
@@ -549,6 +579,23 @@ def main():
             del wl
             torch.cuda.empty_cache()
         del dev_gate
+    # the page's literal mask: per-expert thresholds calibrated offline for
+    # the target sparsity, one compare pass, a kept count per pair
+    thresh = {}
+    if not args.no_variant:
+        for T in sorted(set(sweep + [args.batch])):
+            wl, res = measure(shape, host, dev_w0, T, args, score="threshold")
+            thresh[str(T)] = {"us_per_call": round(res["us_per_call"], 3),
+                              "us_per_token": round(res["us_per_token"], 3),
+                              "mean_kept": round(res["mean_kept"], 1),
+                              "layer_bytes": int(res["layer_bytes"]),
+                              "hbm_gbs": round(res["hbm_gbs"], 1),
+                              "kernels_us": {k: round(v["avg_us"], 2) for k, v in res["kernels"].items()}}
+            log(f"[bench] threshold T={T}: {res['us_per_call']:.1f} us/call, "
+                f"{res['us_per_token']:.2f} us/token, mean kept {res['mean_kept']:.1f}; kernels "
+                + ", ".join(f"{k} {v['avg_us']:.1f}" for k, v in res["kernels"].items()))
+            del wl
+            torch.cuda.empty_cache()
     cpu = None
     if not args.no_cpu:
         log("[bench] timing the CPU oracle")
@@ -583,6 +630,10 @@ def main():
         "updown_variant": {"what": "the page's own split: dense gate scores |silu(W_g x)|, "
                                    "up and down gathered on the kept rows (a different mask)",
                            "batches": updown} if updown else None,
+        "threshold_variant": {"what": "the page's literal mask: keep |h| > tau[e], tau per expert "
+                                      f"calibrated for sparsity {args.sparsity} on {CAL_TOKENS} "
+                                      f"tokens of seed {CAL_SEED}; kept count varies per pair",
+                              "batches": thresh} if thresh else None,
         "cpu_baseline": cpu,
         "batches": batches,
     }

@@ -219,8 +219,8 @@ moe_status moe_unpack_gate_up(const moe_desc *d, const void *src_packed, void *d
 
 /*
  * moe_expert_ffn_sparse_threshold -- the sparse path with the page's literal
- * masking (technical summary, Methodology: activation masking in one O(n)
- * threshold pass, without a sort, at a target sparsity): neuron j of pair
+ * masking (technical summary, Methodology: activation masking by a
+ * threshold in one O(n) pass, without a top-k sort): neuron j of pair
  * (t, e) is kept iff |h_j| > tau[e], with h = silu(W_g x) * (W_u x) as in
  * moe_expert_ffn_sparse, so the kept count varies per pair.  tau [E] fp32
  * device thresholds, e.g. from moe_calibrate_thresholds; tau[e] < 0 keeps
@@ -241,8 +241,9 @@ moe_status moe_expert_ffn_sparse_threshold(const moe_desc *d, int32_t T, const f
 
 /*
  * moe_calibrate_thresholds -- offline calibration of the thresholds for a
- * target sparsity s (the page sets the masking threshold ahead of time for
- * a target sparsity; technical summary, Methodology: activation masking).
+ * target sparsity s.  The page masks by a threshold (technical summary,
+ * Methodology: activation masking) but does not say how it is chosen; this
+ * per-expert order statistic of calibration scores is the reading taken.
  * On T calibration tokens x with their routing (from moe_route; NULL for
  * the always-on group, top_k == n_experts), with the scores
  * |h| = |silu(W_g x) * (W_u x)| of every (calibration pair, neuron):

@@ -42,9 +42,11 @@ Only kept W_u and W_d rows are read.  With k_keep = d_ff both variants are
 the dense SwiGLU MoE.
 
 Threshold variant (the page's literal masking: technical summary,
-Methodology, activation masking in one O(n) threshold pass without a sort,
-at a target sparsity): a per-expert threshold tau_e, calibrated offline,
-replaces the exact count:
+Methodology, activation masking by a threshold in one O(n) pass, without a
+top-k sort).  The page does not say how the threshold is chosen; the reading
+here is a per-expert threshold tau_e calibrated offline so that the target
+sparsity of the experiments holds on calibration tokens.  It replaces the
+exact count:
 
     K_t,e  = { j : |h_j| > tau_e }                 (variable count per pair)
     tau_e  = the (c + 1)-th largest of the m calibration scores |h| of
@@ -208,8 +210,8 @@ def threshold_neurons(h: np.ndarray, tau: float) -> np.ndarray:
     """The neurons with |h_j| > tau, ascending (a variable count).
 
     The page's literal masking: one pass comparing every activation with a
-    threshold set offline for a target sparsity, with no sort (technical
-    summary, Methodology: activation masking).  -0 and +0 score equal."""
+    threshold, with no sort (technical summary, Methodology: activation
+    masking).  -0 and +0 score equal."""
     return np.nonzero(np.abs(h) > tau)[0].astype(np.int64)
 
 
@@ -390,8 +392,9 @@ def calibrate_thresholds(x, w_router, bias, w_gate, w_up, *, top_k: int, norm_to
     expert's tau is calibrated_threshold over the scores of every
     (calibration token routed to it, neuron) pair; an expert no token reaches
     takes the value over all routed scores.  Shared experts (every token)
-    get their own.  The page sets the masking threshold offline for a target
-    sparsity (technical summary, Methodology: activation masking).
+    get their own.  The page masks by a threshold (technical summary,
+    Methodology: activation masking) without saying how it is set; this
+    calibration for the target sparsity is the reading taken here.
     ``forced_ids`` replaces the router's choice (for checking a run whose
     near-tied router logits broke the other way)."""
     xf = to_f64(x, dtype)

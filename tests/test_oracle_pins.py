@@ -483,6 +483,23 @@ def test_threshold_minus_one_is_dense_moe():
 
 
 @pytest.mark.parametrize("score", ["swiglu", "gate"])
+@pytest.mark.parametrize("k", [1, 5, 23])
+def test_threshold_at_pair_midpoint_is_the_top_k_layer(score, k):
+    # one token: each routed expert serves one pair, so a tau_e between that
+    # pair's k-th and (k+1)-th largest |score| keeps exactly its top k
+    L = _rand_layer(44 + k, T=1, H=32, E=6, d=24)
+    ref = _run(L, 3, True, k, score=score)
+    taus = np.full(6, 1e9)
+    for slot in range(3):
+        v = np.sort(np.abs(ref.h[(0, slot)]))[::-1]
+        taus[int(ref.ids[0, slot])] = 0.5 * (v[k - 1] + v[k])
+    r = _run(L, 3, True, 0, score=score, thresholds=taus)
+    for slot in range(3):
+        np.testing.assert_array_equal(r.keep[(0, slot)], ref.keep[(0, slot)])
+    np.testing.assert_allclose(r.y, ref.y, rtol=1e-13, atol=1e-15)
+
+
+@pytest.mark.parametrize("score", ["swiglu", "gate"])
 def test_calibration_hits_its_target_on_its_own_tokens(score):
     # calibrated on a token batch, the thresholds keep exactly c_e of each
     # expert's m_e scores on that batch (the scores are distinct)
