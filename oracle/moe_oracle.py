@@ -428,3 +428,75 @@ def calibrate_thresholds(x, w_router, bias, w_gate, w_up, *, top_k: int, norm_to
             tau_sh.append(calibrated_threshold(np.concatenate(sc), sparsity))
         tau_sh = np.array(tau_sh, dtype=np.float64)
     return tau, tau_sh
+
+
+# ---------------------------------------------------------------- roster routing
+# The roster rule of the page "Predatory MoE: Serving Mixture-of-Experts with
+# a Sequence-Local Expert Roster" (technical summary, section 2, the roster
+# routing rule), restated for one MoE layer at decode time.  Batch row t is
+# one sequence; usage[t, e] counts how often that sequence has selected
+# expert e at this layer so far.
+#
+# Readings (the page is silent on these):
+#   * the roster R_t is the m experts with the largest usage, ties to the
+#     lower expert id (the same tie rule as the router's);
+#   * the bias is added to the router logits before the softmax and the
+#     top-k, as any additive router bias ("score gap" of 2 delta);
+#   * pinned rows keep only roster members selectable: a bias of 0 for
+#     members and -inf for the others;
+#   * every selection of the step adds one to the row's usage, in every
+#     phase (pinned rows included).
+
+def roster(usage_row: np.ndarray, m: int) -> np.ndarray:
+    """R_t: the m most-used experts of one sequence (ties: lower id),
+    ascending."""
+    E = usage_row.shape[0]
+    order = sorted(range(E), key=lambda e: (-int(usage_row[e]), e))
+    return np.asarray(sorted(order[:m]), dtype=np.int64)
+
+
+def roster_bias(usage_row: np.ndarray, m: int, delta: float, pinned: bool) -> np.ndarray:
+    """The logit bias [E] of one sequence for this step.
+
+    Exploration (fewer than m distinct experts used so far): no bias.
+    Barrier (m or more used): +delta for roster members, -delta for the
+    rest, so a non-member must beat a member by more than 2 delta.
+    Pinned (serving after the prefix): decoding stays inside the roster."""
+    E = usage_row.shape[0]
+    R = roster(usage_row, m)
+    member = np.zeros(E, dtype=bool)
+    member[R] = True
+    if pinned:
+        return np.where(member, 0.0, -np.inf)
+    if int(np.count_nonzero(usage_row > 0)) < m:
+        return np.zeros(E)
+    return np.where(member, float(delta), -float(delta))
+
+
+def route_roster(x, w_router, bias, usage, pinned, *, m: int, delta: float, top_k: int,
+                 norm_topk: bool):
+    """One decode step of roster routing: per row, router logits plus the
+    row's roster bias, then the usual top-k and softmax weights (``route``),
+    then the usage update.  ``usage`` [T, E] is not modified; the updated
+    counts are returned.  ``pinned`` is a [T] bool array or None.  x and
+    w_router are float arrays (bf16 data goes through to_f64 first); the
+    arithmetic is float64.
+
+    Returns (ids, weights, biased logits, usage after the step)."""
+    l = router_logits(np.asarray(x, dtype=np.float64), np.asarray(w_router, dtype=np.float64),
+                      bias)
+    T, E = l.shape
+    new = np.array(usage, dtype=np.int64, copy=True)
+    ids = np.zeros((T, top_k), dtype=np.int64)
+    w = np.zeros((T, top_k), dtype=np.float64)
+    lb = np.zeros_like(l)
+    for t in range(T):
+        pin = bool(pinned[t]) if pinned is not None else False
+        lb[t] = l[t] + roster_bias(np.asarray(usage[t]), m, delta, pin)
+        p = softmax(lb[t])
+        ids[t] = top_experts(lb[t], top_k)
+        w[t] = p[ids[t]]
+        if norm_topk:
+            w[t] = w[t] / np.sum(w[t])
+        new[t, ids[t]] += 1
+    return ids, w, lb, new

@@ -535,3 +535,122 @@ def test_calibration_expert_without_tokens_takes_layer_value():
     for e in range(8):
         if e not in used:
             assert tau[e] == layer_tau
+
+
+# ------------------------------------------------------------ roster routing
+# Pins of the roster rule (Predatory MoE, technical summary, section 2).
+
+def test_roster_worked_values():
+    u = np.array([3, 0, 5, 1, 0, 2])
+    np.testing.assert_array_equal(O.roster(u, 3), [0, 2, 5])
+    np.testing.assert_array_equal(O.roster(np.array([2, 2, 2, 0]), 2), [0, 1])    # ties: lower id
+    # 4 experts used: barrier at m = 3, exploration at m = 5
+    np.testing.assert_array_equal(O.roster_bias(u, 3, 0.5, False), [.5, -.5, .5, -.5, -.5, .5])
+    np.testing.assert_array_equal(O.roster_bias(u, 5, 0.5, False), np.zeros(6))
+    np.testing.assert_array_equal(O.roster_bias(u, 4, 0.5, False), [.5, -.5, .5, .5, -.5, .5])
+    pinned = O.roster_bias(u, 2, 0.5, True)
+    assert pinned[0] == 0 and pinned[2] == 0 and np.all(np.isneginf(np.delete(pinned, [0, 2])))
+
+
+def test_roster_eviction_worked_example():
+    # E = 4, m = 2, delta = 1, top-1.  Usage (5, 1, 0, 0): barrier, R = {0, 1}.
+    # Logits (0, 0, 2.5, 0): expert 2 beats the members by 2.5 > 2 delta and
+    # is selected, but with usage 1 it ties member 1 and the lower id stays;
+    # a second such step gives it usage 2 and evicts expert 1.
+    wr = np.eye(4)
+    x = np.array([[0.0, 0.0, 2.5, 0.0]])
+    u = np.array([[5, 1, 0, 0]])
+    ids, w, lb, u1 = O.route_roster(x, wr, None, u, None, m=2, delta=1.0, top_k=1,
+                                    norm_topk=False)
+    assert ids[0, 0] == 2
+    np.testing.assert_allclose(lb[0], [1.0, 1.0, 1.5, -1.0])
+    np.testing.assert_array_equal(u1, [[5, 1, 1, 0]])
+    np.testing.assert_array_equal(O.roster(u1[0], 2), [0, 1])
+    np.testing.assert_allclose(w[0, 0], math.exp(1.5) / (2 * math.e + math.exp(1.5) + math.exp(-1)))
+    ids, _, _, u2 = O.route_roster(x, wr, None, u1, None, m=2, delta=1.0, top_k=1,
+                                   norm_topk=False)
+    assert ids[0, 0] == 2
+    np.testing.assert_array_equal(O.roster(u2[0], 2), [0, 2])
+    # a gap below 2 delta does not get through
+    ids, *_ = O.route_roster(np.array([[0.0, 0.0, 1.9, 0.0]]), wr, None, u, None, m=2,
+                             delta=1.0, top_k=1, norm_topk=False)
+    assert ids[0, 0] == 0
+
+
+@pytest.mark.parametrize("norm", [False, True])
+def test_roster_without_bias_is_the_plain_router(norm):
+    L = _rand_layer(60, T=5, H=16, E=9, d=4)
+    rng = np.random.default_rng(61)
+    usage = rng.integers(0, 4, size=(5, 9))
+    usage[0] = 0                                        # a fresh sequence
+    ids0, w0, _, _ = O.route(L["x"].astype(np.float64), L["wr"].astype(np.float64), L["bias"], 3, norm)
+    ids, w, _, new = O.route_roster(L["x"].astype(np.float64), L["wr"].astype(np.float64),
+                                    L["bias"], usage, None, m=4, delta=0.0, top_k=3, norm_topk=norm)
+    np.testing.assert_array_equal(ids, ids0)
+    np.testing.assert_allclose(w, w0, rtol=1e-15)
+    for t in range(5):                                  # one count per selection
+        d = new[t] - usage[t]
+        assert d.sum() == 3 and set(np.nonzero(d)[0]) == set(ids[t])
+    # exploration (fewer than m used) ignores delta
+    few = np.zeros((5, 9), dtype=np.int64)
+    few[:, 0] = 2
+    ids, w, _, _ = O.route_roster(L["x"].astype(np.float64), L["wr"].astype(np.float64),
+                                  L["bias"], few, None, m=4, delta=5.0, top_k=3, norm_topk=norm)
+    np.testing.assert_array_equal(ids, ids0)
+
+
+def test_roster_selection_brute_force():
+    # the top-k set maximises the sum of biased logits over all k-subsets
+    L = _rand_layer(62, T=6, H=16, E=7, d=4)
+    rng = np.random.default_rng(63)
+    usage = rng.integers(0, 5, size=(6, 7))
+    ids, _, lb, _ = O.route_roster(L["x"], L["wr"], None, usage, None, m=3, delta=0.3,
+                                   top_k=2, norm_topk=False)
+    xf, wf = L["x"].astype(np.float64), L["wr"].astype(np.float64)
+    for t in range(6):
+        bias = [0.0] * 7
+        used = sum(1 for e in range(7) if usage[t, e] > 0)
+        if used >= 3:
+            best3 = sorted(range(7), key=lambda e: (-usage[t, e], e))[:3]
+            bias = [0.3 if e in best3 else -0.3 for e in range(7)]
+        score = [sum(xf[t, h] * wf[e, h] for h in range(16)) + bias[e] for e in range(7)]
+        best = max(itertools.combinations(range(7), 2), key=lambda s: sum(score[e] for e in s))
+        assert set(ids[t]) == set(best)
+
+
+def test_roster_working_set_stays_at_m():
+    # once 2 delta exceeds every row's logit range, a sequence in the barrier
+    # phase never selects a non-member: its working set stays at m
+    rng = np.random.default_rng(64)
+    E, H, m, k = 16, 32, 4, 2
+    wr = rng.standard_normal((E, H)) / np.sqrt(H)
+    usage = np.zeros((3, E), dtype=np.int64)
+    free = np.zeros((3, E), dtype=np.int64)
+    for step in range(60):
+        x = rng.standard_normal((3, H))
+        _, _, lb, usage = O.route_roster(x, wr, None, usage, None, m=m, delta=50.0, top_k=k,
+                                         norm_topk=True)
+        _, _, _, free = O.route_roster(x, wr, None, free, None, m=m, delta=0.0, top_k=k,
+                                       norm_topk=True)
+    for t in range(3):
+        assert np.count_nonzero(usage[t]) <= m + k - 1      # m reached inside one step at most
+        assert np.count_nonzero(free[t]) > m + k
+    # ... and the experts it keeps using are exactly its roster
+    for t in range(3):
+        assert set(np.nonzero(usage[t])[0]) >= set(O.roster(usage[t], m))
+
+
+def test_roster_pinned_rows_stay_inside():
+    L = _rand_layer(65, T=4, H=16, E=8, d=4)
+    usage = np.array([[9, 0, 4, 0, 1, 0, 0, 0], [0] * 8, [1, 1, 1, 1, 1, 1, 1, 1],
+                      [0, 0, 0, 0, 0, 0, 3, 3]])
+    pinned = np.array([True, True, True, False])
+    ids, w, _, _ = O.route_roster(L["x"], L["wr"], None, usage, pinned, m=3, delta=0.1, top_k=2,
+                                  norm_topk=False)
+    l = L["x"].astype(np.float64) @ L["wr"].astype(np.float64).T
+    for t in range(3):
+        R = O.roster(usage[t], 3)
+        assert set(ids[t]) <= set(R)
+        z = sum(math.exp(l[t, e]) for e in R)          # softmax over the roster only
+        for s in range(2):
+            assert math.isclose(w[t, s], math.exp(l[t, ids[t, s]]) / z, rel_tol=1e-12)
