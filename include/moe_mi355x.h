@@ -122,6 +122,35 @@ moe_status moe_route(const moe_desc *d, int32_t T, const void *x, const void *w_
                      size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * moe_route_roster -- moe_route with the roster rule of the page "Predatory
+ * MoE: Serving Mixture-of-Experts with a Sequence-Local Expert Roster"
+ * (technical summary, section 2, the roster routing rule), for decode
+ * batches where row t is one sequence.
+ *
+ *   usage [T, E] int32, in/out: how often sequence t has selected expert e
+ *       at this layer so far (negative entries read as 0).  The caller keeps
+ *       one array per layer and zeroes a row when its slot takes a new
+ *       sequence.  Every selection of this call adds one (all phases).
+ *   R_t  = the roster_size most-used experts of row t (ties -> lower e).
+ *   bias added to l[t, :] before the softmax and the top-k:
+ *       pinned[t] != 0                      0 on R_t, -inf elsewhere
+ *       fewer than roster_size used so far  0 (exploration)
+ *       otherwise                           +delta on R_t, -delta elsewhere
+ *   So a non-member is chosen over a member only if its logit is higher by
+ *   more than 2 delta, and it displaces the least-used member once its
+ *   usage passes that member's.
+ * pinned: [T] int32 or NULL (no row pinned).  1 <= roster_size <= E, and
+ * roster_size >= top_k when pinned is given; delta finite and >= 0; else
+ * MOE_ERR_INVALID_ARG.  usage NULL -> MOE_ERR_INVALID_ARG.  Other
+ * arguments, outputs and workspace as moe_route.  Selection costs
+ * roster_size extra wavefront max rounds per token.
+ */
+moe_status moe_route_roster(const moe_desc *d, int32_t T, const void *x, const void *w_router,
+                            const float *bias, int32_t *usage, const int32_t *pinned,
+                            int32_t roster_size, float delta, const moe_routing *out,
+                            void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * moe_expert_ffn_sparse -- the expert FFN with intra-expert activation
  * sparsity, for the small-batch path.
  *

@@ -45,6 +45,8 @@ _V, _I32, _SZ, _D = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_d
 _PD, _PR = ctypes.POINTER(MoeDesc), ctypes.POINTER(MoeRouting)
 _SIGS = {
     "moe_route": (_I32, [_PD, _I32, _V, _V, _V, _PR, _V, _SZ, _V]),
+    "moe_route_roster": (_I32, [_PD, _I32, _V, _V, _V, _V, _V, _I32, ctypes.c_float, _PR, _V, _SZ,
+                                _V]),
     "moe_expert_ffn_sparse": (_I32, [_PD, _I32, _I32, _V, _V, _V, _V, _PR, _V, _I32, _V, _V, _SZ, _V]),
     "moe_expert_ffn_dense": (_I32, [_PD, _I32, _I32, _V, _V, _V, _V, _PR, _V, _I32, _V, _V, _SZ, _V]),
     "moe_expert_ffn_sparse_updown": (_I32, [_PD, _I32, _I32, _V, _V, _V, _V, _PR, _V, _I32, _V, _V, _SZ, _V]),
@@ -160,6 +162,18 @@ def moe_route(desc: MoeDesc, T: int, x, w_router, bias, routing: Routing, worksp
     _check(lib().moe_route(ctypes.byref(desc), int(T), _ptr(x), _ptr(w_router), _ptr(bias),
                            ctypes.byref(r), ws, workspace.numel() * workspace.element_size() if ws else 0,
                            _stream(stream)))
+
+
+def moe_route_roster(desc: MoeDesc, T: int, x, w_router, bias, usage, pinned, roster_size: int,
+                     delta: float, routing: Routing, workspace, stream=None):
+    """moe_route with the roster bias; usage [T, E] int32 is updated in place."""
+    r = routing.as_c()
+    ws = _ptr(workspace)
+    _check(lib().moe_route_roster(ctypes.byref(desc), int(T), _ptr(x), _ptr(w_router), _ptr(bias),
+                                  _ptr(usage), _ptr(pinned), int(roster_size), float(delta),
+                                  ctypes.byref(r), ws,
+                                  workspace.numel() * workspace.element_size() if ws else 0,
+                                  _stream(stream)))
 
 
 def _ffn(fn, desc, T, k_keep, x, w_gate, w_up, w_down, routing, y, accumulate, active_idx_out,

@@ -240,13 +240,27 @@ moe_status run_ffn(RunMode mode, const moe_desc *d, int32_t T, int32_t k_keep, c
 
 extern "C" {
 
-moe_status moe_route(const moe_desc *d, int32_t T, const void *x, const void *w_router,
-                     const float *bias, const moe_routing *out, void *workspace,
-                     size_t workspace_bytes, hipStream_t stream) {
+static moe_status route_impl(const moe_desc *d, int32_t T, const void *x, const void *w_router,
+                             const float *bias, const moe::RosterArgs &ro,
+                             const moe_routing *out, void *workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
   g_err[0] = 0;
   TRY(check_desc(d));
   TRY(check_T(T));
   if (!out) return fail(MOE_ERR_INVALID_ARG, "routing output struct is NULL");
+  if (ro.usage) {
+    if ((uintptr_t)ro.usage & 3u) return fail(MOE_ERR_MISALIGNED, "usage is not 4-byte aligned");
+    if (ro.pinned && ((uintptr_t)ro.pinned & 3u))
+      return fail(MOE_ERR_MISALIGNED, "pinned is not 4-byte aligned");
+    if (ro.m < 1 || ro.m > d->n_experts)
+      return fail(MOE_ERR_INVALID_ARG, "roster size %d outside [1, n_experts=%d]", ro.m,
+                  d->n_experts);
+    if (ro.pinned && ro.m < d->top_k)
+      return fail(MOE_ERR_INVALID_ARG, "pinned rows need roster size >= top_k (%d < %d)", ro.m,
+                  d->top_k);
+    if (!(ro.delta >= 0.f && ro.delta <= 3.0e38f))
+      return fail(MOE_ERR_INVALID_ARG, "delta must be finite and >= 0");
+  }
   if (T == 0) return MOE_OK;
   TRY(need_ptr(x, "x"));
   TRY(need_ptr(w_router, "w_router"));
@@ -272,6 +286,7 @@ moe_status moe_route(const moe_desc *d, int32_t T, const void *x, const void *w_
   a.x = x;
   a.w_router = w_router;
   a.bias = bias;
+  a.roster = ro;
   a.logits = static_cast<float *>(workspace);
   a.topk_ids = out->topk_ids;
   a.topk_w = out->topk_w;
@@ -282,6 +297,23 @@ moe_status moe_route(const moe_desc *d, int32_t T, const void *x, const void *w_
   const hipError_t e = moe::launch_route(a, stream);
   if (e != hipSuccess) return fail(MOE_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return MOE_OK;
+}
+
+moe_status moe_route(const moe_desc *d, int32_t T, const void *x, const void *w_router,
+                     const float *bias, const moe_routing *out, void *workspace,
+                     size_t workspace_bytes, hipStream_t stream) {
+  return route_impl(d, T, x, w_router, bias, moe::RosterArgs{}, out, workspace, workspace_bytes,
+                    stream);
+}
+
+moe_status moe_route_roster(const moe_desc *d, int32_t T, const void *x, const void *w_router,
+                            const float *bias, int32_t *usage, const int32_t *pinned,
+                            int32_t roster_size, float delta, const moe_routing *out,
+                            void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  g_err[0] = 0;
+  if (!usage) return fail(MOE_ERR_INVALID_ARG, "usage is NULL");
+  moe::RosterArgs ro{usage, pinned, roster_size, delta};
+  return route_impl(d, T, x, w_router, bias, ro, out, workspace, workspace_bytes, stream);
 }
 
 moe_status moe_expert_ffn_sparse(const moe_desc *d, int32_t T, int32_t k_keep, const void *x,

@@ -35,10 +35,19 @@ inline void timer_end(hipStream_t s) {
 enum { kStageLogits = 0, kStageTopk, kStageGroup, kStageGateup, kStageMask, kStageDownRows,
        kStageDownDense, kStageCombine, kStageZero, kStageUpRows };
 
+// Roster routing state (usage == nullptr: plain routing).
+struct RosterArgs {
+  int32_t *usage;          // [T, E] per-sequence expert usage, updated in place
+  const int32_t *pinned;   // [T] nonzero = pinned row, or nullptr
+  int m;                   // roster size
+  float delta;             // barrier bias
+};
+
 struct RouteArgs {
   int T, H, E, top_k, norm_topk, bf16;
   const void *x, *w_router;
   const float *bias;
+  RosterArgs roster;
   float *logits;  // workspace [kRouterSplits, T, E] partial logits
   int32_t *topk_ids;
   float *topk_w;

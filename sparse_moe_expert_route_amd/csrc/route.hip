@@ -96,6 +96,45 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const void *__restri
   }
 }
 
+// ---------------------------------------------------------------- roster bias
+// The roster rule (Predatory MoE, technical summary, section 2) for one
+// sequence's row of expert usage counts, in the wave's lane layout (expert
+// lane + 64 i): the roster is the m most-used experts (ties: lower id),
+// found by m rounds of a wavefront max over (count, ~id) keys.  Pinned rows
+// keep only members selectable (bias 0 / -inf); otherwise no bias while
+// fewer than m experts have been used, then +delta for members and -delta
+// for the rest.  Negative counts read as 0.
+template <int V>
+__device__ __forceinline__ void roster_bias_row(const int32_t *__restrict__ usage, int pinned,
+                                                int m, float delta, int E, float (&rb)[V]) {
+  const int lane = threadIdx.x & 63;
+  uint64_t key[V];
+  bool member[V];
+  float used = 0.f;
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+    const int e = lane + 64 * i;
+    const int c = e < E ? max(usage[e], 0) : 0;
+    used += c > 0 ? 1.f : 0.f;
+    key[i] = e < E ? ((uint64_t)(uint32_t)c << 32) | (uint32_t)(0xffffffffu - e) : 0ull;
+    member[i] = false;
+  }
+  used = wave_sum(used);
+  for (int r = 0; r < m; ++r) {
+    uint64_t b = 0;
+#pragma unroll
+    for (int i = 0; i < V; ++i) b = key[i] > b ? key[i] : b;
+    b = wave_max_u64(b);
+#pragma unroll
+    for (int i = 0; i < V; ++i)
+      if (b != 0ull && key[i] == b) { member[i] = true; key[i] = 0ull; }
+  }
+  const bool explore = used < (float)m;
+#pragma unroll
+  for (int i = 0; i < V; ++i)
+    rb[i] = pinned ? (member[i] ? 0.f : -INFINITY) : explore ? 0.f : (member[i] ? delta : -delta);
+}
+
 // ---------------------------------------------------------------- top-k
 // One wave selects one token's experts.  Each lane holds V logits (expert
 // lane + 64 i) as 64-bit keys (order-preserving float bits, then the
@@ -104,13 +143,20 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const void *__restri
 // descending-logit order.  Weights are the full softmax over all E experts
 // at the picks, optionally renormalised over the picks.  Lane r < top_k
 // returns slot r's (expert, weight).
-template <int V>
+// With RO, token t's roster bias (from its usage row) is added to the
+// logits before the softmax and the selection, and each selection adds one
+// to the row's usage.
+template <int V, bool RO>
 __device__ __forceinline__ void wave_topk(const float *__restrict__ part, size_t split_stride,
                                           int nsplit, const float *__restrict__ bias, int E,
-                                          int top_k, int norm_topk, int &esel, float &wsel) {
+                                          int top_k, int norm_topk, const RosterArgs &ro, int t,
+                                          int &esel, float &wsel) {
   const int lane = threadIdx.x & 63;
   float v[V];
   uint64_t key[V];
+  float rb[V];
+  if (RO) roster_bias_row<V>(ro.usage + (size_t)t * E, ro.pinned ? ro.pinned[t] : 0, ro.m, ro.delta,
+                             E, rb);
 #pragma unroll
   for (int i = 0; i < V; ++i) {
     const int e = lane + 64 * i;
@@ -124,6 +170,7 @@ __device__ __forceinline__ void wave_topk(const float *__restrict__ part, size_t
       for (int c = 0; c < kRouterSplits; ++c)
         if (c < nsplit) l += pv[c];
       if (bias) l += bias[e];
+      if (RO) l += rb[i];
     }
     v[i] = l;
     key[i] = e < E ? ((uint64_t)ordered_key(l) << 32) | (uint32_t)(0xffffffffu - e) : 0ull;
@@ -154,12 +201,15 @@ __device__ __forceinline__ void wave_topk(const float *__restrict__ part, size_t
   float denom = z;
   if (norm_topk) denom = wave_sum(lane < top_k ? psel : 0.f);
   wsel = psel / denom;
+  // usage update: the row was read above by this wave; distinct experts
+  if (RO && lane < top_k) ro.usage[(size_t)t * E + esel] += 1;
 }
 
-template <int V>
+template <int V, bool RO>
 __global__ __launch_bounds__(256) void router_topk_kernel(const float *__restrict__ part,
                                                           int nsplit, const float *__restrict__ bias,
                                                           int T, int E, int top_k, int norm_topk,
+                                                          RosterArgs ro,
                                                           int32_t *__restrict__ ids,
                                                           float *__restrict__ wout) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
@@ -167,7 +217,8 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float *__restric
   if (t >= T) return;
   int e;
   float w;
-  wave_topk<V>(part + (size_t)t * E, (size_t)T * E, nsplit, bias, E, top_k, norm_topk, e, w);
+  wave_topk<V, RO>(part + (size_t)t * E, (size_t)T * E, nsplit, bias, E, top_k, norm_topk, ro, t,
+                   e, w);
   if (lane < top_k) {
     ids[(size_t)t * top_k + lane] = e;
     wout[(size_t)t * top_k + lane] = w;
@@ -259,10 +310,10 @@ __global__ __launch_bounds__(1024) void route_group_kernel(const int32_t *__rest
 // blocks (router_topk_kernel) ahead of the grouping kernel: at T = 256 the
 // one-block form took 56 us against ~10 us for the two kernels.
 constexpr int kFusedMaxPairs = 2048;
-template <int V>
+template <int V, bool RO>
 __global__ __launch_bounds__(1024) void route_select_group_kernel(
     const float *__restrict__ part, int nsplit, const float *__restrict__ bias, int T, int E,
-    int top_k, int norm_topk,
+    int top_k, int norm_topk, RosterArgs ro,
     int32_t *__restrict__ ids, float *__restrict__ wout, int32_t *__restrict__ offsets,
     int32_t *__restrict__ pair_by_expert, int32_t *__restrict__ active,
     int32_t *__restrict__ n_active) {
@@ -274,7 +325,8 @@ __global__ __launch_bounds__(1024) void route_select_group_kernel(
   for (int t = wid; t < T; t += 16) {
     int e;
     float w;
-    wave_topk<V>(part + (size_t)t * E, (size_t)T * E, nsplit, bias, E, top_k, norm_topk, e, w);
+    wave_topk<V, RO>(part + (size_t)t * E, (size_t)T * E, nsplit, bias, E, top_k, norm_topk, ro,
+                     t, e, w);
     if (lane < top_k) {
       sids[t * top_k + lane] = e;
       ids[(size_t)t * top_k + lane] = e;
@@ -285,22 +337,21 @@ __global__ __launch_bounds__(1024) void route_select_group_kernel(
   block_group(sids, T * top_k, E, offsets, pair_by_expert, active, n_active, cursor, wcnt, tmp);
 }
 
-template <int V>
-static void launch_select(const RouteArgs &a, int nsplit, hipStream_t stream) {
+template <int V, bool RO>
+static void launch_select_ro(const RouteArgs &a, int nsplit, hipStream_t stream) {
   const int P = a.T * a.top_k;
   if (a.T <= 16 && P <= kFusedMaxPairs) {
     timer_begin(kStageTopk, stream);
-    route_select_group_kernel<V><<<1, 1024, 0, stream>>>(a.logits, nsplit, a.bias, a.T, a.E,
-                                                         a.top_k, a.norm_topk, a.topk_ids,
-                                                         a.topk_w, a.offsets, a.pair_by_expert,
-                                                         a.active, a.n_active);
+    route_select_group_kernel<V, RO><<<1, 1024, 0, stream>>>(
+        a.logits, nsplit, a.bias, a.T, a.E, a.top_k, a.norm_topk, a.roster, a.topk_ids, a.topk_w,
+        a.offsets, a.pair_by_expert, a.active, a.n_active);
     timer_end(stream);
     return;
   }
   timer_begin(kStageTopk, stream);
-  router_topk_kernel<V><<<(a.T + 3) / 4, 256, 0, stream>>>(a.logits, nsplit, a.bias, a.T, a.E,
-                                                           a.top_k, a.norm_topk, a.topk_ids,
-                                                           a.topk_w);
+  router_topk_kernel<V, RO><<<(a.T + 3) / 4, 256, 0, stream>>>(a.logits, nsplit, a.bias, a.T, a.E,
+                                                               a.top_k, a.norm_topk, a.roster,
+                                                               a.topk_ids, a.topk_w);
   timer_end(stream);
   timer_begin(kStageGroup, stream);
   route_group_kernel<<<1, 1024, 0, stream>>>(a.topk_ids, P, a.E, a.offsets, a.pair_by_expert,
@@ -308,13 +359,22 @@ static void launch_select(const RouteArgs &a, int nsplit, hipStream_t stream) {
   timer_end(stream);
 }
 
+template <int V>
+static void launch_select(const RouteArgs &a, int nsplit, hipStream_t stream) {
+  if (a.roster.usage) launch_select_ro<V, true>(a, nsplit, stream);
+  else launch_select_ro<V, false>(a, nsplit, stream);
+}
+
 // Split-K factor of the router GEMM: enough blocks to spread the router
-// matrix over many CUs, at least 4 k-steps per split, at most kRouterSplits.
+// matrix over many CUs (64 at decode batches; past one tile of tokens, two
+// rounds of the chip's 256 CUs, since each block's K loop is a serial
+// latency chain), at least 4 k-steps per split, at most kRouterSplits.
 int router_splits(int T, int H, int E, int bf16) {
   const int tg = T <= 16 ? 16 : 64;
   const int blocks = ((E + 15) / 16) * ((T + tg - 1) / tg);
   const int nsteps = H / (bf16 ? 32 : 16);
-  int sp = (64 + blocks - 1) / blocks;
+  const int target = T <= 16 ? 64 : 512;
+  int sp = (target + blocks - 1) / blocks;
   sp = sp < nsteps / 4 ? sp : nsteps / 4;
   sp = sp < kRouterSplits ? sp : kRouterSplits;
   return sp < 1 ? 1 : sp;

@@ -203,3 +203,22 @@ def test_route_validation():
     assert _route(d, 4, ws=None) == WSP
     assert _route(d, 4, wsb=B.moe_route_workspace_size(d, 4) - 1) == WSP
     assert _route(d, 0, x=None) == 0
+
+
+def test_route_roster_validation():
+    d = _desc()                       # 64 experts, top-8
+    out = B.MoeRouting(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    ws = B.moe_route_workspace_size(d, 4)
+    R = lambda usage=FAKE, pinned=None, m=8, delta=1.0, dd=d: L.moe_route_roster(
+        ctypes.byref(dd), 4, FAKE, FAKE, None, usage, pinned, m, ctypes.c_float(delta),
+        ctypes.byref(out), FAKE, ws, None)
+    assert R(usage=None) == INV
+    assert R(usage=FAKE + 2) == MISA
+    assert R(pinned=FAKE + 2) == MISA
+    assert R(m=0) == INV
+    assert R(m=65) == INV
+    assert R(pinned=FAKE, m=7) == INV             # pinned rows need m >= top_k
+    assert R(delta=-1.0) == INV
+    assert R(delta=float("nan")) == INV
+    assert R(delta=float("inf")) == INV
+    assert R(dd=_desc(hidden=100)) == UNS

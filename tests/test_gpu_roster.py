@@ -1,0 +1,117 @@
+"""GPU parity of roster routing (moe_route_roster) against the oracle.
+
+Each case runs several decode steps: the library updates the usage counts
+in place, and every step is checked against the oracle's step from the same
+usage — expert sets with the window rule on the biased logits, slot order,
+weights, and the usage update exactly.  Rows cover every phase of the rule:
+fresh, exploration, barrier and pinned.
+"""
+import numpy as np
+import pytest
+import torch
+
+import moe_synth as S
+from oracle import moe_oracle as O
+from parity import WINDOW, check_selection, to_dev
+from sparse_moe_expert_route_amd import binding as B
+
+pytestmark = pytest.mark.gpu
+
+MAXIMA = dict(hidden=128, n_experts=1024, d_ff=64, top_k=32, norm_topk=True)
+# (layer, overrides, T, roster size m, delta, steps)
+CASES = [("olmoe-like", {}, 16, 8, 0.5, 6),          # one-block select
+         ("qwen3-moe-like", {}, 40, 8, 0.3, 5),      # two-kernel select, Zipf bias
+         ("deepseek-v2-like", {}, 8, 6, 0.5, 5),     # E = 160
+         ("tiny-f32", {}, 24, 3, 0.4, 6),            # fp32, E = 8
+         ("olmoe-like", MAXIMA, 4, 40, 0.2, 3)]      # E = 1024, top-32, m > 32
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def _start_usage(rng, T, E, m):
+    """Rows by phase: t % 4 == 0 fresh, 1 exploration (m - 1 used),
+    2 and 3 barrier (m + 3 used); rows with t % 4 == 3 get pinned."""
+    u = np.zeros((T, E), dtype=np.int32)
+    for t in range(T):
+        kind = t % 4
+        if kind == 1 and m > 1:
+            few = rng.choice(E, size=m - 1, replace=False)
+            u[t, few] = rng.integers(1, 4, size=few.size)
+        elif kind >= 2:
+            many = rng.choice(E, size=min(E, m + 3), replace=False)
+            u[t, many] = rng.integers(1, 9, size=many.size)
+    return u
+
+
+def _finite(v):
+    return np.where(np.isneginf(v), -1e30, v)
+
+
+@pytest.mark.parametrize("name,over,T,m,delta,steps", CASES)
+def test_roster_steps_match_oracle(name, over, T, m, delta, steps):
+    shape = S.LAYERS[name].with_(**over) if over else S.LAYERS[name]
+    E, K, dt = shape.n_experts, shape.top_k, shape.dtype
+    say(f"[case] roster {name} E={E} top_k={K} T={T} m={m} delta={delta}")
+    wr = S.router_matrix(shape, 0)
+    bias = S.router_bias(shape)
+    desc = B.make_desc(shape.hidden, E, shape.d_ff, K, shape.norm_topk, dt)
+    rng = np.random.default_rng(7)
+    usage_h = _start_usage(rng, T, E, m)
+    pinned_h = (np.arange(T) % 4 == 3).astype(np.int32) if m >= K else None
+    wr_d = to_dev(wr)
+    bias_d = torch.from_numpy(bias).cuda() if bias is not None else None
+    usage_d = torch.from_numpy(usage_h.copy()).cuda()
+    pinned_d = torch.from_numpy(pinned_h).cuda() if pinned_h is not None else None
+    R = B.Routing.allocate(T, K, E)
+    ws = torch.empty(B.moe_route_workspace_size(desc, T), dtype=torch.uint8, device="cuda")
+    wr64 = O.to_f64(wr, dt)
+    differs = 0
+    for step in range(steps):
+        x = S.tokens(shape, 100 + step, T)
+        before = usage_d.cpu().numpy()
+        B.moe_route_roster(desc, T, to_dev(x), wr_d, bias_d, usage_d, pinned_d, m, delta, R, ws)
+        torch.cuda.synchronize()
+        ids_g = R.topk_ids.cpu().numpy()[:T]
+        w_g = R.topk_w.cpu().numpy()[:T]
+        after = usage_d.cpu().numpy()
+        ids_o, _, lb, _ = O.route_roster(O.to_f64(x, dt), wr64, bias, before,
+                                         pinned_h.astype(bool) if pinned_h is not None else None,
+                                         m=m, delta=delta, top_k=K, norm_topk=shape.norm_topk)
+        for t in range(T):
+            lf = _finite(lb[t])
+            differs += check_selection(ids_g[t], ids_o[t], lf, K, f"step {step} t={t}")
+            sl = lf[ids_g[t]]
+            assert np.all(np.diff(sl) <= WINDOW * np.abs(sl[:-1]) + 1e-30), f"slot order t={t}"
+            p = O.softmax(lb[t])[ids_g[t]]
+            want = p / p.sum() if shape.norm_topk else p
+            np.testing.assert_allclose(w_g[t], want, rtol=1e-4, atol=1e-7)
+            if pinned_h is not None and pinned_h[t]:
+                assert set(ids_g[t]) <= set(O.roster(before[t], m)), f"pinned row {t} left its roster"
+            inc = np.zeros(E, dtype=np.int64)
+            inc[ids_g[t]] = 1
+            np.testing.assert_array_equal(after[t], before[t] + inc, err_msg=f"usage row {t}")
+    say(f"   {steps} steps, {differs} rows differing on near-ties")
+
+
+def test_roster_with_zero_delta_is_moe_route():
+    # no bias (delta 0, nothing pinned): bitwise the plain router, plus counts
+    shape = S.LAYERS["olmoe-like"]
+    E, K = shape.n_experts, shape.top_k
+    desc = B.make_desc(shape.hidden, E, shape.d_ff, K, shape.norm_topk, shape.dtype)
+    wr_d = to_dev(S.router_matrix(shape, 0))
+    for T in (16, 48):
+        say(f"[case] roster delta=0 T={T}")
+        x = to_dev(S.tokens(shape, 5, T))
+        ws = torch.empty(B.moe_route_workspace_size(desc, T), dtype=torch.uint8, device="cuda")
+        R0, R1 = B.Routing.allocate(T, K, E), B.Routing.allocate(T, K, E)
+        B.moe_route(desc, T, x, wr_d, None, R0, ws)
+        usage = torch.randint(0, 5, (T, E), dtype=torch.int32, device="cuda")
+        before = usage.clone()
+        B.moe_route_roster(desc, T, x, wr_d, None, usage, None, 4, 0.0, R1, ws)
+        torch.cuda.synchronize()
+        for f in ("topk_ids", "topk_w", "expert_offsets", "pair_by_expert", "n_active"):
+            assert torch.equal(getattr(R0, f), getattr(R1, f)), f
+        inc = torch.zeros_like(before).scatter_(1, R0.topk_ids[:T].long(), 1)
+        assert torch.equal(usage, before + inc)
