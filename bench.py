@@ -291,6 +291,71 @@ def time_kernels(wl, steps, chunk=10):
             for k, v in d.items()}
 
 
+def time_stages(fn, steps, chunk=10):
+    """time_kernels for any callable that launches library kernels."""
+    import torch
+    from sparse_moe_expert_route_amd import binding as B
+    timer = B.StageTimer(capacity=steps * 8 + 8)
+    fn(0)
+    torch.cuda.synchronize()
+    spin = getattr(torch.cuda, "_sleep", None)
+    with timer:
+        for c0 in range(0, steps, chunk):
+            if spin is not None:
+                spin(10_000_000)
+            for i in range(c0, min(steps, c0 + chunk)):
+                fn(i)
+            torch.cuda.synchronize()
+    d = timer.durations()
+    timer.close()
+    return {k: round(1e3 * sum(v) / len(v), 2) for k, v in d.items()}
+
+
+def roster_variant(shape, host, dev_w0, T=16, m=8, seq_len=256, deltas=(1.0, 2.0, 4.0)):
+    """Roster routing (Predatory MoE, the roster routing rule) on this layer's
+    router: the selection kernel's cost against plain routing, and the
+    working set (distinct experts per sequence) over a synthetic decode of
+    seq_len steps for T sequences, unconstrained, in the barrier phase at
+    each delta, and pinned after a 20 % prefix."""
+    import numpy as np
+    import torch
+    import moe_synth as S
+    from sparse_moe_expert_route_amd import binding as B
+    E, K = shape.n_experts, shape.top_k
+    desc = B.make_desc(shape.hidden, E, shape.d_ff, K, shape.norm_topk, shape.dtype)
+    wr = dev_w0[0]
+    xs = [host.to_dev(S.tokens(shape, 2000 + i, T)) for i in range(seq_len)]
+    R = B.Routing.allocate(T, K, E)
+    ws = torch.empty(B.moe_route_workspace_size(desc, T), dtype=torch.uint8, device="cuda")
+    usage = torch.zeros((T, E), dtype=torch.int32, device="cuda")
+    plain = time_stages(lambda i: B.moe_route(desc, T, xs[i % seq_len], wr, None, R, ws), 50)
+    timed = time_stages(lambda i: B.moe_route_roster(desc, T, xs[i % seq_len], wr, None, usage,
+                                                     None, m, 1.0, R, ws), 50)
+
+    def working_set(delta, pin_after=None):
+        u = torch.zeros((T, E), dtype=torch.int32, device="cuda")
+        pinned = torch.zeros(T, dtype=torch.int32, device="cuda")
+        for i in range(seq_len):
+            if pin_after is not None and i == pin_after:
+                pinned.fill_(1)
+            if delta is None:
+                B.moe_route(desc, T, xs[i], wr, None, R, ws)
+                u.scatter_add_(1, R.topk_ids[:T].long(), torch.ones_like(R.topk_ids[:T]))
+            else:
+                B.moe_route_roster(desc, T, xs[i], wr, None, u, pinned if pin_after else None,
+                                   m, delta, R, ws)
+        torch.cuda.synchronize()
+        return round(float((u > 0).sum(1).float().mean()), 2)
+
+    out = {"T": T, "roster_size": m, "seq_len": seq_len,
+           "select_us": {"plain": plain.get("router_topk"), "roster": timed.get("router_topk")},
+           "working_set": {"unconstrained": working_set(None)}}
+    for d in deltas:
+        out["working_set"][f"delta_{d}"] = working_set(d)
+    out["working_set"]["pinned_after_20pct_delta_4.0"] = working_set(4.0, pin_after=seq_len // 5)
+    return out
+
+
 def cpu_baseline(shape, host, wl, seconds):
     """The oracle as it stands, on the host, over a bounded sample of steps."""
     import oracle
@@ -596,6 +661,10 @@ def main():
                 + ", ".join(f"{k} {v['avg_us']:.1f}" for k, v in res["kernels"].items()))
             del wl
             torch.cuda.empty_cache()
+    roster = None
+    if not args.no_variant:
+        roster = roster_variant(shape, host, dev_w0)
+        log(f"[bench] roster: select {roster['select_us']}, working set {roster['working_set']}")
     cpu = None
     if not args.no_cpu:
         log("[bench] timing the CPU oracle")
@@ -634,6 +703,7 @@ def main():
                                       f"calibrated for sparsity {args.sparsity} on {CAL_TOKENS} "
                                       f"tokens of seed {CAL_SEED}; kept count varies per pair",
                               "batches": thresh} if thresh else None,
+        "roster_variant": roster,
         "cpu_baseline": cpu,
         "batches": batches,
     }
