@@ -459,7 +459,7 @@ def measured_traffic(stage):
         return None
 
 
-def roofline(res, stage, bytes_key, practical=None):
+def roofline(res, stage, bytes_key, practical=None, sized=None):
     k = res["kernels"].get(stage)
     if not k:
         return None
@@ -470,7 +470,42 @@ def roofline(res, stage, bytes_key, practical=None):
            "avg_us": round(k["avg_us"], 2), "bytes_per_launch": int(res[bytes_key])}
     if practical:
         out["frac_practical"] = round(gbs / practical["gbs"], 4)
+    if sized:
+        out["size_matched_read"] = sized
+        out["frac_size_matched"] = round(gbs / sized["gbs"], 4)
     return out
+
+
+def size_matched_read(nbytes, reps=40, chunk=10):
+    """A plain streaming read (moe_stream_read) of exactly `nbytes`, timed
+    like the library's kernels: event pairs on the launch stream, queued
+    behind a GPU spin so they run back to back with the kernel.  Buffers
+    rotate over >= 1.2 GB so the reads come from HBM, not the caches.  The
+    rate a kernel of that size can reach, ramp and drain included."""
+    import torch
+    from sparse_moe_expert_route_amd import binding as B
+    nbytes = max(16, int(round(nbytes / 16)) * 16)   # the read takes 16-byte multiples
+    nb = max(2, math.ceil(1.2e9 / nbytes))
+    bufs = [torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1) for _ in range(nb)]
+    sink = torch.empty(B.STREAM_READ_SINK_WORDS, dtype=torch.int32, device="cuda")
+    for b in bufs:
+        B.moe_stream_read(b, sink)
+    torch.cuda.synchronize()
+    spin = getattr(torch.cuda, "_sleep", None)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for c0 in range(0, reps, chunk):
+        if spin is not None:
+            spin(10_000_000)
+        for i in range(c0, min(reps, c0 + chunk)):
+            ev[i][0].record()
+            B.moe_stream_read(bufs[i % nb], sink)
+            ev[i][1].record()
+        torch.cuda.synchronize()
+    us = sum(s.elapsed_time(e) for s, e in ev) * 1e3 / reps
+    del bufs
+    torch.cuda.empty_cache()
+    return {"bytes": int(nbytes), "avg_us": round(us, 2), "gbs": round(nbytes / (us * 1e-6) / 1e9, 1)}
 
 
 def practical_read_peak(gib=4, reps=5):
@@ -614,6 +649,11 @@ def main():
         batches[str(T)] = {k: (round(v, 3) if isinstance(v, float) else v)
                            for k, v in res.items() if k != "kernels"}
         batches[str(T)]["kernels_us"] = {k: round(v["avg_us"], 2) for k, v in res["kernels"].items()}
+        if "down_rows" in res["kernels"]:
+            sm = size_matched_read(res["down_bytes"])
+            dn_gbs = res["down_bytes"] / (res["kernels"]["down_rows"]["avg_us"] * 1e-6) / 1e9
+            batches[str(T)]["down_vs_size_matched_read"] = {
+                "down_gbs": round(dn_gbs, 1), "read": sm, "frac": round(dn_gbs / sm["gbs"], 4)}
         log(f"[bench] T={T}: {res['us_per_call']:.1f} us/call, {res['us_per_token']:.2f} us/token, "
             f"{res['hbm_gbs']:.0f} GB/s ({100 * res['hbm_frac']:.1f}% of 8 TB/s); kernels "
             + ", ".join(f"{k} {v['avg_us']:.1f}" for k, v in res["kernels"].items()))
@@ -693,8 +733,10 @@ def main():
         "hbm_gbs": round(r["hbm_gbs"], 1),
         "hbm_frac": round(r["hbm_frac"], 4),
         "layer_bytes": int(r["layer_bytes"]),
-        "roofline": roofline(r, "gateup_swiglu", "gateup_bytes", practical),
-        "roofline_down": roofline(r, "down_rows", "down_bytes", practical),
+        "roofline": roofline(r, "gateup_swiglu", "gateup_bytes", practical,
+                             size_matched_read(r["gateup_bytes"])),
+        "roofline_down": roofline(r, "down_rows", "down_bytes", practical,
+                                  size_matched_read(r["down_bytes"])),
         "practical_read_peak": practical,
         "updown_variant": {"what": "the page's own split: dense gate scores |silu(W_g x)|, "
                                    "up and down gathered on the kept rows (a different mask)",

@@ -355,9 +355,11 @@ int32_t moe_timer_detach(void);
 
 /* Measurement helper, not part of the layer: one plain streaming read of
  * `bytes` of device memory at `src` (16-byte aligned, bytes a positive
- * multiple of 16), with non-temporal 16-byte loads, 16384 blocks of 256
- * threads (enough loads in flight to saturate HBM).  Timing it gives the practical HBM read peak that the layer's
- * kernels are compared with.  Block b writes the XOR of its chunks to
+ * multiple of 16), with non-temporal 16-byte loads in blocks of 256
+ * threads: about 8 loads per thread, at least 1024 and at most 16384
+ * blocks, so any size has its loads in flight at once.  Timing it gives the
+ * practical HBM read rate, at 4 GiB or at a kernel's own size, that the
+ * layer's kernels are compared with.  Block b writes the XOR of its chunks to
  * sink[4b .. 4b+3]: `sink` holds MOE_STREAM_READ_SINK_WORDS uint32 of device
  * memory.  Errors as for the other calls; nothing is allocated. */
 #define MOE_STREAM_READ_SINK_WORDS 65536

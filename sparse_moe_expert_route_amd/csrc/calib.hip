@@ -23,7 +23,14 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4 *__restric
 #pragma unroll
     for (int u = 0; u < U; ++u) acc ^= q[u];
   }
-  for (; c < n_chunks; c += stride) acc ^= ld16_nt(src + c);
+  {  // the rest: fewer than U chunks of this thread, all loads in flight
+    u32x4 q[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      q[u] = c + u * stride < n_chunks ? ld16_nt(src + c + u * stride) : u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc ^= q[u];
+  }
   red[threadIdx.x] = acc;
   __syncthreads();
   for (int s = 128; s > 0; s >>= 1) {
@@ -33,9 +40,16 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4 *__restric
   if (threadIdx.x < 4) sink[4 * blockIdx.x + threadIdx.x] = red[0][threadIdx.x];
 }
 
-hipError_t launch_stream_read(const void *src, size_t bytes, uint32_t *sink, int blocks,
+// Grid sized to the read: about U chunks per thread (one unrolled round),
+// at least 1024 blocks (4 per CU, so even a few MB has every CU's loads in
+// flight at once) and at most max_blocks.
+hipError_t launch_stream_read(const void *src, size_t bytes, uint32_t *sink, int max_blocks,
                               hipStream_t stream) {
-  stream_read_kernel<<<blocks, 256, 0, stream>>>(static_cast<const u32x4 *>(src), bytes / 16, sink);
+  const size_t n = bytes / 16, per_block = 8 * 256;
+  size_t blocks = (n + per_block - 1) / per_block;
+  blocks = blocks < 1024 ? 1024 : blocks;
+  blocks = blocks > (size_t)max_blocks ? (size_t)max_blocks : blocks;
+  stream_read_kernel<<<(unsigned)blocks, 256, 0, stream>>>(static_cast<const u32x4 *>(src), n, sink);
   return hipGetLastError();
 }
 

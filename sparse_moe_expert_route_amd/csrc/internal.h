@@ -76,7 +76,7 @@ struct FfnArgs {
   void *hm;          // dense path: [P, d_ff] masked, weighted h (bf16 or fp32)
 };
 
-hipError_t launch_stream_read(const void *src, size_t bytes, uint32_t *sink, int blocks,
+hipError_t launch_stream_read(const void *src, size_t bytes, uint32_t *sink, int max_blocks,
                               hipStream_t stream);
 hipError_t launch_pack_gate_up(const void *src, void *dst, int E, int d_ff, int H, int bf16,
                                int unpack, hipStream_t stream);

@@ -298,7 +298,7 @@ def test_deterministic_and_sparse_equals_dense():
     assert rel_l2(c["y"], a["y"]) < 1e-2
 
 
-@pytest.mark.parametrize("nbytes", [16, 4096 * 16 + 48, 64 << 20])
+@pytest.mark.parametrize("nbytes", [16, 4096 * 16 + 48, 3375104, 54001664, 64 << 20, 300 << 20])
 def test_stream_read_folds_every_chunk(nbytes):
     # the calibration read touches every 16-byte chunk exactly once: the XOR
     # of all block folds equals the XOR of all chunks
