@@ -356,6 +356,84 @@ def roster_variant(shape, host, dev_w0, T=16, m=8, seq_len=256, deltas=(1.0, 2.0
     return out
 
 
+def decode_step_variant(shape, args, n_layers=8, batches=(1, 16)):
+    """A decode step through n_layers MoE layers of this shape with distinct
+    weights (seeds 0 .. n_layers - 1): per layer route -> FFN (the
+    dispatcher's path) -> residual, the whole step captured as one HIP graph.
+    Distinct layers (>= 0.5 GB of weights per step at batch 1) keep the
+    reads in HBM without rotating copies.  Replays are checked bitwise
+    against an eager step before timing."""
+    import torch
+    import moe_synth as S
+    from sparse_moe_expert_route_amd import binding as B
+    desc = B.make_desc(shape.hidden, shape.n_experts, shape.d_ff, shape.top_k, shape.norm_topk,
+                       shape.dtype)
+    to_dev = HostLayer.to_dev
+    layers = []
+    for s in range(n_layers):
+        wg, wu, wd = S.expert_weights(shape, s)
+        layers.append((to_dev(S.router_matrix(shape, s)), B.moe_pack_gate_up(desc, to_dev(wg)),
+                       B.moe_pack_gate_up(desc, to_dev(wu)), to_dev(wd)))
+        del wg, wu, wd
+    torch.cuda.synchronize()
+    E, K = shape.n_experts, shape.top_k
+    k = B.moe_keep_count(args.sparsity, shape.d_ff)
+    out = {"layers": n_layers, "what": "route -> FFN -> residual per layer, one graph per step"}
+    for T in batches:
+        path = B.moe_select_path(desc, T, k)
+        ffn = B.moe_expert_ffn_sparse if path == B.MOE_PATH_SPARSE else B.moe_expert_ffn_dense
+        x0 = to_dev(S.tokens(shape, 3000 + T, T))
+        xs = [torch.empty_like(x0) for _ in layers]
+        y = torch.empty((T, shape.hidden), dtype=torch.float32, device="cuda")
+        Rs = [B.Routing.allocate(T, K, E) for _ in layers]
+        ws_r = torch.empty(B.moe_route_workspace_size(desc, T), dtype=torch.uint8, device="cuda")
+        ws = torch.empty(B.moe_ffn_workspace_size(desc, T, k, path), dtype=torch.uint8,
+                         device="cuda")
+
+        def step():
+            x = x0
+            for (wr, wg, wu, wd), xo, R in zip(layers, xs, Rs):
+                B.moe_route(desc, T, x, wr, None, R, ws_r)
+                ffn(desc, T, k, x, wg, wu, wd, R, y, 0, None, ws)
+                B.moe_residual_add(desc, T, x, y, xo)
+                x = xo
+
+        step()
+        torch.cuda.synchronize()
+        ref = xs[-1].clone()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        torch.cuda.synchronize()
+        xs[-1].fill_(0)
+        g.replay()
+        torch.cuda.synchronize()
+        if not torch.equal(xs[-1], ref):
+            raise RuntimeError("decode-step graph replay differs from the eager step")
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            g.replay()
+        torch.cuda.synchronize()
+        us = (time.perf_counter() - t0) / args.steps * 1e6
+        out[str(T)] = {"path": "sparse" if path == B.MOE_PATH_SPARSE else "dense",
+                       "us_per_step": round(us, 1), "us_per_layer": round(us / n_layers, 2),
+                       "us_per_token_per_layer": round(us / n_layers / T, 3)}
+        del g, xs, Rs, ws, ws_r, y
+        torch.cuda.empty_cache()
+    del layers
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(shape, host, wl, seconds):
     """The oracle as it stands, on the host, over a bounded sample of steps."""
     import oracle
@@ -701,9 +779,12 @@ def main():
                 + ", ".join(f"{k} {v['avg_us']:.1f}" for k, v in res["kernels"].items()))
             del wl
             torch.cuda.empty_cache()
-    roster = None
+    roster = step = None
     if not args.no_variant:
         roster = roster_variant(shape, host, dev_w0)
+        log("[bench] decode step through 8 layers")
+        step = decode_step_variant(shape, args)
+        log(f"[bench] decode step: {step}")
         log(f"[bench] roster: select {roster['select_us']}, working set {roster['working_set']}")
     cpu = None
     if not args.no_cpu:
@@ -746,6 +827,7 @@ def main():
                                       f"tokens of seed {CAL_SEED}; kept count varies per pair",
                               "batches": thresh} if thresh else None,
         "roster_variant": roster,
+        "decode_step_variant": step,
         "cpu_baseline": cpu,
         "batches": batches,
     }

@@ -293,6 +293,20 @@ moe_status moe_calibrate_thresholds(const moe_desc *d, int32_t T, const void *x,
                                     const moe_routing *routing, double sparsity, float *tau_out,
                                     void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * moe_residual_add -- the residual stream between the layers of a decode
+ * step: x_out[t, h] = x_in[t, h] + y[t, h], rounded to desc->dtype (round to
+ * nearest even for bf16; finite values).  x_in, x_out [T, H] in desc->dtype,
+ * y [T, H] fp32 (a layer call's output); all 16-byte aligned; x_out may be
+ * x_in.  Not part of the MoE layer itself: with it a multi-layer decode step
+ * runs, and can be captured as one HIP graph, entirely in this library's
+ * kernels (the intra-expert page requires graph compatibility of its
+ * integration: technical summary, Key contributions).  Errors as for the
+ * other calls.
+ */
+moe_status moe_residual_add(const moe_desc *d, int32_t T, const void *x_in, const float *y,
+                            void *x_out, hipStream_t stream);
+
 /* Workspace bytes for moe_route over at most T tokens (0 on invalid input). */
 size_t moe_route_workspace_size(const moe_desc *d, int32_t T);
 

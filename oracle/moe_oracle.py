@@ -64,6 +64,7 @@ from dataclasses import dataclass, field
 from typing import Dict, Optional, Sequence, Tuple
 
 import numpy as np
+import torch
 
 
 # ---------------------------------------------------------------- inputs
@@ -500,3 +501,21 @@ def route_roster(x, w_router, bias, usage, pinned, *, m: int, delta: float, top_
             w[t] = w[t] / np.sum(w[t])
         new[t, ids[t]] += 1
     return ids, w, lb, new
+
+
+# ---------------------------------------------------------------- residual stream
+# Between the layers of a decode step (not part of the pages' method: the
+# glue that chains layers, needed to run a multi-layer step as one graph).
+
+def residual_stream(x, y, dtype: str) -> np.ndarray:
+    """The next layer's input: x + y in float32, rounded to the layers'
+    dtype (bf16: round to nearest, ties to even; returned as uint16 bit
+    patterns).  The sum is taken in float32 because that is the precision
+    in which the rounding to bf16 is decided (a quantisation decided in the
+    kernel's precision); torch's float32 -> bfloat16 conversion does the
+    rounding."""
+    xf = to_f64(x, dtype).astype(np.float32)
+    s = xf + np.asarray(y, dtype=np.float32)
+    if dtype == "f32":
+        return s
+    return torch.from_numpy(s).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)

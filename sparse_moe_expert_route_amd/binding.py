@@ -45,6 +45,7 @@ _V, _I32, _SZ, _D = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_d
 _PD, _PR = ctypes.POINTER(MoeDesc), ctypes.POINTER(MoeRouting)
 _SIGS = {
     "moe_route": (_I32, [_PD, _I32, _V, _V, _V, _PR, _V, _SZ, _V]),
+    "moe_residual_add": (_I32, [_PD, _I32, _V, _V, _V, _V]),
     "moe_route_roster": (_I32, [_PD, _I32, _V, _V, _V, _V, _V, _I32, ctypes.c_float, _PR, _V, _SZ,
                                 _V]),
     "moe_expert_ffn_sparse": (_I32, [_PD, _I32, _I32, _V, _V, _V, _V, _PR, _V, _I32, _V, _V, _SZ, _V]),
@@ -173,6 +174,12 @@ def moe_route_roster(desc: MoeDesc, T: int, x, w_router, bias, usage, pinned, ro
                                   _ptr(usage), _ptr(pinned), int(roster_size), float(delta),
                                   ctypes.byref(r), ws,
                                   workspace.numel() * workspace.element_size() if ws else 0,
+                                  _stream(stream)))
+
+
+def moe_residual_add(desc: MoeDesc, T: int, x_in, y, x_out, stream=None):
+    """x_out = x_in + y rounded to the layer dtype (x_out may be x_in)."""
+    _check(lib().moe_residual_add(ctypes.byref(desc), int(T), _ptr(x_in), _ptr(y), _ptr(x_out),
                                   _stream(stream)))
 
 

@@ -483,6 +483,23 @@ int32_t moe_timer_detach(void) {
   return n;
 }
 
+moe_status moe_residual_add(const moe_desc *d, int32_t T, const void *x_in, const float *y,
+                            void *x_out, hipStream_t stream) {
+  g_err[0] = 0;
+  TRY(check_desc(d));
+  TRY(check_T(T));
+  if (T == 0) return MOE_OK;
+  TRY(need_ptr(x_in, "x_in"));
+  TRY(need_ptr(y, "y"));
+  TRY(need_ptr(x_out, "x_out"));
+  if (!aligned16(x_in) || !aligned16(y) || !aligned16(x_out))
+    return fail(MOE_ERR_MISALIGNED, "x_in, y and x_out must be 16-byte aligned");
+  const hipError_t e = moe::launch_residual(x_in, y, x_out, (size_t)T * d->hidden,
+                                            d->dtype == MOE_BF16, stream);
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return MOE_OK;
+}
+
 moe_status moe_stream_read(const void *src, size_t bytes, uint32_t *sink, hipStream_t stream) {
   g_err[0] = 0;
   if (!src || !sink) return fail(MOE_ERR_INVALID_ARG, "stream_read needs src and sink");

@@ -76,6 +76,8 @@ struct FfnArgs {
   void *hm;          // dense path: [P, d_ff] masked, weighted h (bf16 or fp32)
 };
 
+hipError_t launch_residual(const void *x_in, const float *y, void *x_out, size_t n, int bf16,
+                           hipStream_t stream);
 hipError_t launch_stream_read(const void *src, size_t bytes, uint32_t *sink, int max_blocks,
                               hipStream_t stream);
 hipError_t launch_pack_gate_up(const void *src, void *dst, int E, int d_ff, int H, int bf16,

@@ -205,6 +205,21 @@ def test_route_validation():
     assert _route(d, 0, x=None) == 0
 
 
+def test_residual_validation():
+    d = _desc()
+    Rz = lambda dd=d, T=4, x=FAKE, y=FAKE, o=FAKE: L.moe_residual_add(
+        ctypes.byref(dd) if dd is not None else None, T, x, y, o, None)
+    assert Rz(dd=None) == INV
+    assert Rz(T=-1) == INV
+    assert Rz(x=None) == INV
+    assert Rz(y=None) == INV
+    assert Rz(o=None) == INV
+    assert Rz(x=MIS) == MISA
+    assert Rz(y=MIS) == MISA
+    assert Rz(o=MIS) == MISA
+    assert Rz(T=0, x=None, y=None, o=None) == 0
+
+
 def test_route_roster_validation():
     d = _desc()                       # 64 experts, top-8
     out = B.MoeRouting(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)

@@ -654,3 +654,40 @@ def test_roster_pinned_rows_stay_inside():
         z = sum(math.exp(l[t, e]) for e in R)          # softmax over the roster only
         for s in range(2):
             assert math.isclose(w[t, s], math.exp(l[t, ids[t, s]]) / z, rel_tol=1e-12)
+
+
+# ------------------------------------------------------------ residual stream
+
+def _bf16_value(bits):
+    return float(np.array([int(bits) << 16], dtype=np.uint32).view(np.float32)[0])
+
+
+def test_residual_stream_worked_ties():
+    one = np.array([0x3F80], dtype=np.uint16)          # 1.0 in bf16; its ulp is 2^-7
+    cases = [(2.0 ** -8, 0x3F80),                      # exactly half an ulp: tie, to even (1.0)
+             (3 * 2.0 ** -8, 0x3F82),                  # 1.5 ulp: tie, to even (1 + 2^-6)
+             (2.0 ** -8 + 2.0 ** -20, 0x3F81),         # just above half: up
+             (-2.0 ** -9, 0x3F80),                     # below 1 by a quarter of 1's lower ulp
+             (1.0, 0x4000)]
+    for y, want in cases:
+        got = O.residual_stream(one, np.array([y], dtype=np.float32), "bf16")
+        assert got[0] == want, (y, hex(int(got[0])), hex(want))
+    f = O.residual_stream(np.array([1.5], np.float32), np.array([2.25], np.float32), "f32")
+    assert f[0] == np.float32(3.75)
+
+
+def test_residual_stream_is_nearest_bf16():
+    # brute force: the result is a bf16 value nearest to the float32 sum, and
+    # on an exact tie the one with an even last mantissa bit
+    rng = np.random.default_rng(70)
+    x = (rng.integers(0, 1 << 16, size=4000, dtype=np.uint32) & 0x7F7F).astype(np.uint16)
+    x[x == 0] = 0x3F80
+    y = rng.standard_normal(4000).astype(np.float32)
+    got = O.residual_stream(x, y, "bf16")
+    for i in range(4000):
+        s = float(np.float32(_bf16_value(x[i])) + np.float32(y[i]))
+        g = int(got[i])
+        err = abs(_bf16_value(g) - s)
+        for nb in (g - 1, g + 1):
+            alt = abs(_bf16_value(nb & 0xFFFF) - s)
+            assert err < alt or (err == alt and g % 2 == 0), (i, hex(g), s)
