@@ -208,6 +208,20 @@ __global__ __launch_bounds__(64 * W, MT == 1 ? 8 : 1) void gateup_swiglu_kernel(
   }
 }
 
+// ---------------------------------------------------------------- XCD-aware block order
+// Workgroups go to the chip's 8 XCDs in turn (linear block id mod 8), and
+// each XCD has its own L2.  This returns a logical linear index (x fastest,
+// then y, then z) such that each XCD runs one contiguous range of it: the
+// token items that share a weight tile (same y, z; x differs) then run on
+// one XCD at about the same time and meet in its L2, instead of every XCD
+// streaming every weight tile.  A bijection for any grid size.
+__device__ __forceinline__ unsigned xcd_logical_block() {
+  const unsigned nx = gridDim.x, nxy = nx * gridDim.y, total = nxy * gridDim.z;
+  const unsigned L = blockIdx.x + nx * blockIdx.y + nxy * blockIdx.z;
+  const unsigned xcd = L & 7u, slot = L >> 3, per = total >> 3, rem = total & 7u;
+  return xcd * per + (xcd < rem ? xcd : rem) + slot;
+}
+
 // ---------------------------------------------------------------- gate / up GEMM
 // Grouped GEMM for batches where an expert holds many tokens: work item =
 // one expert and up to 128 of its tokens, block = 4 waves x 64 neurons
@@ -219,10 +233,14 @@ __global__ __launch_bounds__(64 * W, MT == 1 ? 8 : 1) void gateup_swiglu_kernel(
 // tokens and each staged token row 4 neuron tiles; x is read from L2 once
 // per 64 neurons instead of once per 16.  Epilogue: h = silu(g) * u, four
 // consecutive neurons per lane, one 16-byte store per token.
+// NTW = 2 gives each wave two neuron tiles (block = 128 neurons): every
+// token fragment read from LDS then feeds twice the MFMAs, which halves the
+// LDS traffic per flop where the contraction is MFMA-bound (many tokens
+// per expert), and doubles the weight bytes each wave has in flight.
 constexpr int kGemmTok = 128;               // tokens per work item (8 MFMA token tiles)
 constexpr int kGemmRowB = 128 + 16;         // LDS bytes per staged token row (+ pad)
 
-template <bool BF16, bool GO = false>
+template <bool BF16, bool GO = false, int NTW = 1>
 __global__ __launch_bounds__(256, 2) void gateup_gemm_kernel(const void *__restrict__ xv,
                                                              const void *__restrict__ wgv,
                                                              const void *__restrict__ wuv,
@@ -231,7 +249,9 @@ __global__ __launch_bounds__(256, 2) void gateup_gemm_kernel(const void *__restr
   __shared__ __attribute__((aligned(16))) uint8_t xs[2][kGemmTok * kGemmRowB];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   int e, q0, ntok;
-  if (!find_item<kGemmTok>(rv, blockIdx.x, e, q0, ntok)) return;  // block-uniform
+  const unsigned qb = xcd_logical_block();
+  const int bx = (int)(qb % gridDim.x), by = (int)(qb / gridDim.x);
+  if (!find_item<kGemmTok>(rv, bx, e, q0, ntok)) return;  // block-uniform
   const int ntiles = (ntok + 15) >> 4;
   constexpr int EB = BF16 ? 2 : 4;
   constexpr int KS = BF16 ? 32 : 16;        // elements per k-step (64 bytes of a row)
@@ -248,42 +268,49 @@ __global__ __launch_bounds__(256, 2) void gateup_gemm_kernel(const void *__restr
                              (size_t)(rv.pair_at(q0 + c) / rv.top_k) * H * EB + schunk * 16
                        : nullptr;
   }
-  const int nt = blockIdx.y * 4 + wid;
-  const size_t fbase = ((size_t)e * (d_ff / 16) + nt) * nsteps * 1024 + lane * 16;
+  const int nt = (by * 4 + wid) * NTW;     // this wave's first neuron tile
+  const size_t tstride = (size_t)nsteps * 1024;   // bytes of one neuron tile
+  const size_t fbase = ((size_t)e * (d_ff / 16) + nt) * tstride + lane * 16;
   const uint8_t *wg = static_cast<const uint8_t *>(wgv) + fbase;
   const uint8_t *wu = static_cast<const uint8_t *>(wuv) + fbase;
 
-  f32x4 accg[8], accu[8];
+  f32x4 accg[NTW][8], accu[NTW][8];
 #pragma unroll
-  for (int tl = 0; tl < 8; ++tl) { accg[tl] = f32x4{0, 0, 0, 0}; accu[tl] = f32x4{0, 0, 0, 0}; }
+  for (int j = 0; j < NTW; ++j)
+#pragma unroll
+    for (int tl = 0; tl < 8; ++tl) { accg[j][tl] = f32x4{0, 0, 0, 0}; accu[j][tl] = f32x4{0, 0, 0, 0}; }
 
-  u32x4 stg[4], ag[2], au[2];
+  u32x4 stg[4], ag[NTW][2], au[NTW][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i) stg[i] = xrow[i] ? ld16(xrow[i]) : u32x4{0, 0, 0, 0};
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     *reinterpret_cast<u32x4 *>(&xs[0][(srow + 32 * i) * kGemmRowB + schunk * 16]) = stg[i];
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    ag[k] = ld16_nt(wg + (size_t)k * 1024);
-    if (!GO) au[k] = ld16_nt(wu + (size_t)k * 1024);
-  }
+  for (int j = 0; j < NTW; ++j)
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      ag[j][k] = ld16_nt(wg + j * tstride + (size_t)k * 1024);
+      if (!GO) au[j][k] = ld16_nt(wu + j * tstride + (size_t)k * 1024);
+    }
   __syncthreads();
 
   const int r = lane & 15, g = lane >> 4;
   for (int it = 0; it < nit; ++it) {
     const int cur = it & 1;
     const bool more = it + 1 < nit;
-    u32x4 ng[2], nu[2];
+    u32x4 ng[NTW][2], nu[NTW][2];
     if (more) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         stg[i] = xrow[i] ? ld16(xrow[i] + (size_t)(it + 1) * 128) : u32x4{0, 0, 0, 0};
 #pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        ng[k] = ld16_nt(wg + (size_t)(2 * it + 2 + k) * 1024);
-        if (!GO) nu[k] = ld16_nt(wu + (size_t)(2 * it + 2 + k) * 1024);
-      }
+      for (int j = 0; j < NTW; ++j)
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          ng[j][k] = ld16_nt(wg + j * tstride + (size_t)(2 * it + 2 + k) * 1024);
+          if (!GO) nu[j][k] = ld16_nt(wu + j * tstride + (size_t)(2 * it + 2 + k) * 1024);
+        }
     }
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
@@ -292,14 +319,20 @@ __global__ __launch_bounds__(256, 2) void gateup_gemm_kernel(const void *__restr
         if (tl < ntiles) {
           const u32x4 b = *reinterpret_cast<const u32x4 *>(
               &xs[cur][(tl * 16 + r) * kGemmRowB + k * 64 + g * 16]);
-          if (BF16) {
-            accg[tl] = mfma_bf16(ag[k], b, accg[tl]);
-            if (!GO) accu[tl] = mfma_bf16(au[k], b, accu[tl]);
-          } else {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              accg[tl] = mfma_f32(__uint_as_float(ag[k][j]), __uint_as_float(b[j]), accg[tl]);
-              if (!GO) accu[tl] = mfma_f32(__uint_as_float(au[k][j]), __uint_as_float(b[j]), accu[tl]);
+          for (int j = 0; j < NTW; ++j) {
+            if (BF16) {
+              accg[j][tl] = mfma_bf16(ag[j][k], b, accg[j][tl]);
+              if (!GO) accu[j][tl] = mfma_bf16(au[j][k], b, accu[j][tl]);
+            } else {
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                accg[j][tl] = mfma_f32(__uint_as_float(ag[j][k][q]), __uint_as_float(b[q]),
+                                       accg[j][tl]);
+                if (!GO)
+                  accu[j][tl] = mfma_f32(__uint_as_float(au[j][k][q]), __uint_as_float(b[q]),
+                                         accu[j][tl]);
+              }
             }
           }
         }
@@ -310,21 +343,27 @@ __global__ __launch_bounds__(256, 2) void gateup_gemm_kernel(const void *__restr
       for (int i = 0; i < 4; ++i)
         *reinterpret_cast<u32x4 *>(&xs[cur ^ 1][(srow + 32 * i) * kGemmRowB + schunk * 16]) = stg[i];
 #pragma unroll
-      for (int k = 0; k < 2; ++k) { ag[k] = ng[k]; if (!GO) au[k] = nu[k]; }
+      for (int j = 0; j < NTW; ++j)
+#pragma unroll
+        for (int k = 0; k < 2; ++k) { ag[j][k] = ng[j][k]; if (!GO) au[j][k] = nu[j][k]; }
     }
     __syncthreads();
   }
 
-  const int neuron0 = nt * 16 + 4 * g;
 #pragma unroll
-  for (int tl = 0; tl < 8; ++tl) {
-    const int c = tl * 16 + r;
-    if (tl < ntiles && c < ntok) {
-      const int p = rv.pair_at(q0 + c);
-      f32x4 hv;
+  for (int j = 0; j < NTW; ++j) {
+    const int neuron0 = (nt + j) * 16 + 4 * g;
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) hv[rr] = GO ? silu(accg[tl][rr]) : silu(accg[tl][rr]) * accu[tl][rr];
-      *reinterpret_cast<f32x4 *>(hout + (size_t)p * d_ff + neuron0) = hv;
+    for (int tl = 0; tl < 8; ++tl) {
+      const int c = tl * 16 + r;
+      if (tl < ntiles && c < ntok) {
+        const int p = rv.pair_at(q0 + c);
+        f32x4 hv;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+          hv[rr] = GO ? silu(accg[j][tl][rr]) : silu(accg[j][tl][rr]) * accu[j][tl][rr];
+        *reinterpret_cast<f32x4 *>(hout + (size_t)p * d_ff + neuron0) = hv;
+      }
     }
   }
 }
@@ -1047,9 +1086,11 @@ __global__ __launch_bounds__(256, 2) void down_dense_gemm_kernel(const uint16_t 
   __shared__ __attribute__((aligned(16))) uint32_t bs[2][kDnCols * kDnBrow / 4];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   int e, q0, ntok;
-  if (!find_item<kDnTok>(rv, blockIdx.x, e, q0, ntok)) return;  // block-uniform
-  const int col0 = blockIdx.y * kDnCols;
-  const int S = gridDim.z, sidx = blockIdx.z;
+  const unsigned qb = xcd_logical_block();
+  const int bx = (int)(qb % gridDim.x), by = (int)(qb / gridDim.x % gridDim.y);
+  if (!find_item<kDnTok>(rv, bx, e, q0, ntok)) return;  // block-uniform
+  const int col0 = by * kDnCols;
+  const int S = gridDim.z, sidx = (int)(qb / (gridDim.x * gridDim.y));
   const int k0 = sidx * kchunk;
   const int nit = (min(d_ff, k0 + kchunk) - k0) / kDnK;
   const int ntiles = (ntok + 15) >> 4;
@@ -1271,11 +1312,19 @@ static void launch_gateup(const FfnArgs &a, const RouteView &rv, hipStream_t str
     else { if (gate_only) MOE_GU(false, true); else MOE_GU(false, false); }
 #undef MOE_GU
   } else {
-    dim3 grid(n_items(a, kGemmTok), a.d_ff / 64);
-#define MOE_GG(BF, GOV) \
-  gateup_gemm_kernel<BF, GOV><<<grid, 256, 0, stream>>>(a.x, a.w_gate, a.w_up, rv, a.H, a.d_ff, a.h)
-    if (a.bf16) { if (gate_only) MOE_GG(true, true); else MOE_GG(true, false); }
-    else { if (gate_only) MOE_GG(false, true); else MOE_GG(false, false); }
+    // two neuron tiles per wave for the bf16 SwiGLU contraction when d_ff
+    // allows (a multiple of 128)
+    const bool wide = a.bf16 && !gate_only && a.d_ff % 128 == 0;
+    dim3 grid(n_items(a, kGemmTok), a.d_ff / (wide ? 128 : 64));
+#define MOE_GG(BF, GOV, N) \
+  gateup_gemm_kernel<BF, GOV, N><<<grid, 256, 0, stream>>>(a.x, a.w_gate, a.w_up, rv, a.H, a.d_ff, a.h)
+    if (a.bf16) {
+      if (gate_only) MOE_GG(true, true, 1);
+      else if (wide) MOE_GG(true, false, 2);
+      else MOE_GG(true, false, 1);
+    } else {
+      if (gate_only) MOE_GG(false, true, 1); else MOE_GG(false, false, 1);
+    }
 #undef MOE_GG
   }
   timer_end(stream);
