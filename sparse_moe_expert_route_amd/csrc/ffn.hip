@@ -509,9 +509,11 @@ __global__ __launch_bounds__(64 * NW) void neuron_topk_seg_kernel(const float *_
   const bool keep_all = k >= d_ff;
   uint32_t tau = 0, pmask = 0;
   int krem = k;
+  bool whole = false;  // the last selected digit's bucket is kept entirely
   if (!keep_all && k > 0) {
 #pragma unroll
     for (int pass = 0; pass < 4; ++pass) {
+      if (whole) continue;  // block-uniform: every wave read the same histograms
       const int shift = pass == 0 ? 23 : pass == 1 ? 15 : pass == 2 ? 7 : 0;
       const uint32_t dmask = pass == 3 ? 0x7fu : 0xffu;
 #pragma unroll
@@ -533,20 +535,32 @@ __global__ __launch_bounds__(64 * NW) void neuron_topk_seg_kernel(const float *_
         local += n;
       }
       int run = wave_incl_scan(local) - local;  // keys with a larger digit
-      int dsel = -1, knew = 0;
+      int dsel = -1, knew = 0, csel = 0;
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
-        if (dsel < 0 && run + c[b] >= krem && run < krem) { dsel = 255 - 4 * lane - b; knew = krem - run; }
+        if (dsel < 0 && run + c[b] >= krem && run < krem) {
+          dsel = 255 - 4 * lane - b;
+          knew = krem - run;
+          csel = c[b];
+        }
         run += c[b];
       }
       const uint64_t m = __ballot(dsel >= 0);
       const int L = __ffsll((unsigned long long)m) - 1;  // exactly one lane (counts are exact)
       dsel = lane_value(dsel, L);
       knew = lane_value(knew, L);
+      csel = lane_value(csel, L);
       tau |= (uint32_t)dsel << shift;
       pmask |= dmask << shift;
       krem = knew;
+      // Keeping the whole bucket settles the set: every key whose prefix is
+      // >= tau's, with no ties left to break.  The lower digits need no pass.
+      whole = csel == knew && tau != 0u;
       __syncthreads();  // every wave has read the histograms before the next pass clears them
+    }
+    if (whole) {  // keep key >= tau (its lower bits are zero): key > tau - 1, no equal ones
+      tau -= 1u;
+      krem = 0;
     }
   }
   int ngt = 0, neq = 0;
