@@ -1327,9 +1327,12 @@ static void launch_gateup(const FfnArgs &a, const RouteView &rv, hipStream_t str
 #undef MOE_GU
   } else {
     // two neuron tiles per wave for the bf16 SwiGLU contraction when d_ff
-    // allows (a multiple of 128)
-    const bool wide = a.bf16 && !gate_only && a.d_ff % 128 == 0;
-    dim3 grid(n_items(a, kGemmTok), a.d_ff / (wide ? 128 : 64));
+    // allows (a multiple of 128) and the grid still has >= 2 blocks per CU
+    // (few items, e.g. a shared expert at T = 256, keep the narrow blocks)
+    const int items = n_items(a, kGemmTok);
+    const bool wide = a.bf16 && !gate_only && a.d_ff % 128 == 0 &&
+                      (long)items * (a.d_ff / 128) >= 512;
+    dim3 grid(items, a.d_ff / (wide ? 128 : 64));
 #define MOE_GG(BF, GOV, N) \
   gateup_gemm_kernel<BF, GOV, N><<<grid, 256, 0, stream>>>(a.x, a.w_gate, a.w_up, rv, a.H, a.d_ff, a.h)
     if (a.bf16) {
