@@ -727,11 +727,13 @@ def main():
         batches[str(T)] = {k: (round(v, 3) if isinstance(v, float) else v)
                            for k, v in res.items() if k != "kernels"}
         batches[str(T)]["kernels_us"] = {k: round(v["avg_us"], 2) for k, v in res["kernels"].items()}
-        if "down_rows" in res["kernels"]:
-            sm = size_matched_read(res["down_bytes"])
-            dn_gbs = res["down_bytes"] / (res["kernels"]["down_rows"]["avg_us"] * 1e-6) / 1e9
-            batches[str(T)]["down_vs_size_matched_read"] = {
-                "down_gbs": round(dn_gbs, 1), "read": sm, "frac": round(dn_gbs / sm["gbs"], 4)}
+        for stage, key, name in (("down_rows", "down_bytes", "down"),
+                                 ("gateup_swiglu", "gateup_bytes", "gateup")):
+            if stage in res["kernels"]:
+                sm = size_matched_read(res[key])
+                gbs = res[key] / (res["kernels"][stage]["avg_us"] * 1e-6) / 1e9
+                batches[str(T)][f"{name}_vs_size_matched_read"] = {
+                    f"{name}_gbs": round(gbs, 1), "read": sm, "frac": round(gbs / sm["gbs"], 4)}
         log(f"[bench] T={T}: {res['us_per_call']:.1f} us/call, {res['us_per_token']:.2f} us/token, "
             f"{res['hbm_gbs']:.0f} GB/s ({100 * res['hbm_frac']:.1f}% of 8 TB/s); kernels "
             + ", ".join(f"{k} {v['avg_us']:.1f}" for k, v in res["kernels"].items()))
