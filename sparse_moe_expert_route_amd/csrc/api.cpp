@@ -223,7 +223,8 @@ moe_status run_ffn(RunMode mode, const moe_desc *d, int32_t T, int32_t k_keep, c
     case kRunUpdown: e = moe::launch_ffn_updown(a, stream); break;
     case kRunThreshold:
       e = moe::launch_ffn_threshold(
-          a, m.tau, m.counts ? m.counts : reinterpret_cast<int32_t *>(ws + L.counts), stream);
+          a, m.tau, m.counts ? m.counts : reinterpret_cast<int32_t *>(ws + L.counts),
+          m.counts != nullptr, active_idx_out != nullptr, stream);
       break;
     case kRunCalibrate:
       e = moe::launch_calibrate(a, m.sparsity, m.tau_out, reinterpret_cast<float *>(ws + L.counts),

@@ -987,6 +987,179 @@ __global__ __launch_bounds__(1024) void down_var_token_kernel(const void *__rest
   }
 }
 
+// ---------------------------------------------------------------- fused threshold mask + down
+// Decode batches: the threshold compare is one cheap pass, so each down
+// block redoes it for its token instead of reading a mask kernel's output,
+// and the mask launch disappears.  A token's pairs' activations are one
+// contiguous run h[t * top_k * d_ff ..) in (slot, neuron) order; thread i
+// owns the C elements [i C, i C + C) (C a multiple of 4, 16-byte loads).
+// Pass 1 counts kept elements per thread (|h| > tau[e], or all if tau < 0)
+// and per slot; a block scan gives each thread its place in the token's
+// kept list, which is then staged into LDS chunk by chunk (pass 2 re-reads
+// the thread's elements, from L2) and streamed as in down_token_kernel.
+// Blocks of column chunk 0 also write the kept counts and ids if asked.
+template <bool BF16, int SW>
+__global__ __launch_bounds__(1024) void down_thr_token_kernel(
+    const void *__restrict__ wdv, const float *__restrict__ h, const float *__restrict__ tau,
+    RouteView rv, int H, int d_ff, int accumulate, float *__restrict__ y,
+    int32_t *__restrict__ counts_out, int32_t *__restrict__ idx_out) {
+  constexpr int VEC = BF16 ? 8 : 4;
+  constexpr int LPR = SW / VEC;
+  constexpr int RPI = 64 / LPR;
+  __shared__ float red[kDownWaves][SW];
+  __shared__ uint32_t srow[kDownStage];
+  __shared__ float scoef[kDownStage];
+  __shared__ uint32_t skey[32], sbase[32];
+  __shared__ float sw[32];
+  __shared__ int scnt[32], spref[33], tmp[16];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int t = blockIdx.x, col0 = blockIdx.y * SW;
+  const int top_k = rv.top_k, n = top_k * d_ff;
+  const int C = ((n + 4095) / 4096) * 4;  // elements per thread
+  if (tid < top_k) {
+    const int p = t * top_k + tid, e = rv.expert_of_pair(p);
+    const float te = tau[e];
+    skey[tid] = te < 0.f ? 0xffffffffu : __float_as_uint(fabsf(te));  // ~0: keep all
+    sbase[tid] = (uint32_t)e * (uint32_t)d_ff;
+    sw[tid] = rv.weight(p);
+    scnt[tid] = 0;
+  }
+  __syncthreads();
+  const float *ht = h + (size_t)t * n;
+  const int q0 = tid * C;
+  auto kept = [&](uint32_t bits, int s) {
+    const uint32_t k = skey[s];
+    return k == 0xffffffffu || (bits & 0x7fffffffu) > k;
+  };
+  // The thread's first 4 KC elements stay in registers between the passes
+  // (all of them for up to 64 K elements per token); the rest are re-read.
+  constexpr int KC = 4;
+  u32x4 cache[KC];
+  auto elems = [&](int c) {  // the 4 elements at offset c of the thread's range
+    u32x4 v;
+#pragma unroll
+    for (int r = 0; r < KC; ++r)
+      if (c == 4 * r) v = cache[r];
+    return c < 4 * KC ? v : ld16(ht + q0 + c);
+  };
+  // pass 1: per-thread count, per-slot counts
+  int cnt = 0;
+#pragma unroll
+  for (int r = 0; r < KC; ++r)
+    if (4 * r < C && q0 + 4 * r < n) cache[r] = ld16(ht + q0 + 4 * r);
+  for (int c = 0; c < C && q0 + c < n; c += 4) {
+    const u32x4 v = elems(c);
+    const int s = (q0 + c) / d_ff;  // 4 elements never straddle slots (d_ff % 64 == 0)
+    int m = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) m += kept(v[u], s);
+    if (m) atomicAdd(&scnt[s], m);
+    cnt += m;
+  }
+  int total = 0;
+  const int incl = block_incl_scan<1024>(cnt, tmp, &total);
+  const int my0 = incl - cnt;
+  if (tid == 0) {
+    spref[0] = 0;
+    for (int s = 0; s < top_k; ++s) spref[s + 1] = spref[s] + scnt[s];
+  }
+  __syncthreads();
+  if (blockIdx.y == 0) {  // the token's counts and kept ids, for the caller
+    if (counts_out && tid < top_k) counts_out[t * top_k + tid] = scnt[tid];
+    if (idx_out && cnt) {
+      int pos = my0;
+      for (int c = 0; c < C && q0 + c < n; c += 4) {
+        const u32x4 v = elems(c);
+        const int s = (q0 + c) / d_ff;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          if (kept(v[u], s)) {
+            const int j = q0 + c + u - s * d_ff;
+            idx_out[(size_t)(t * top_k + s) * d_ff + (pos - spref[s])] = j;
+            ++pos;
+          }
+        }
+      }
+    }
+  }
+  const int sub = lane % LPR, rsel = lane / LPR;
+  const size_t colo = (size_t)col0 + sub * VEC;
+  float acc[VEC];
+#pragma unroll
+  for (int v = 0; v < VEC; ++v) acc[v] = 0.f;
+  for (int base = 0; base < total; base += kDownStage) {
+    const int nr = min(kDownStage, total - base);
+    // pass 2: stage the kept rows whose list positions fall in this chunk
+    if (cnt && my0 < base + nr && my0 + cnt > base) {
+      int pos = my0;
+      for (int c = 0; c < C && q0 + c < n; c += 4) {
+        const u32x4 v = elems(c);
+        const int s = (q0 + c) / d_ff;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          if (kept(v[u], s)) {
+            if (pos >= base && pos < base + nr) {
+              const int j = q0 + c + u - s * d_ff;
+              srow[pos - base] = sbase[s] + (uint32_t)j;
+              scoef[pos - base] = sw[s] * __uint_as_float(v[u]);
+            }
+            ++pos;
+          }
+        }
+      }
+    }
+    __syncthreads();
+    constexpr int U = 4;
+    for (int b0 = wid; b0 * RPI < nr; b0 += kDownWaves * U) {
+      u32x4 qv[U];
+      float cf[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int qq = (b0 + kDownWaves * u) * RPI + rsel;
+        cf[u] = 0.f;
+        qv[u] = u32x4{0, 0, 0, 0};
+        if (qq < nr) {
+          const size_t off = (size_t)srow[qq] * H + colo;
+          cf[u] = scoef[qq];
+          qv[u] = BF16 ? ld16(static_cast<const uint16_t *>(wdv) + off)
+                       : ld16(static_cast<const float *>(wdv) + off);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (BF16) {
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            acc[2 * jj] = fmaf(cf[u], bf16lo(qv[u][jj]), acc[2 * jj]);
+            acc[2 * jj + 1] = fmaf(cf[u], bf16hi(qv[u][jj]), acc[2 * jj + 1]);
+          }
+        } else {
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) acc[jj] = fmaf(cf[u], __uint_as_float(qv[u][jj]), acc[jj]);
+        }
+      }
+    }
+    __syncthreads();  // the chunk is consumed before the next is staged
+  }
+#pragma unroll
+  for (int o = LPR; o < 64; o <<= 1) {
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) acc[v] += __shfl_xor(acc[v], o, 64);
+  }
+  if (rsel == 0) {
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) red[wid][sub * VEC + v] = acc[v];
+  }
+  __syncthreads();
+  if (tid < SW) {
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < kDownWaves; ++w) v += red[w][tid];
+    float *yp = y + (size_t)t * H + col0 + tid;
+    *yp = accumulate ? *yp + v : v;
+  }
+}
+
 // ---------------------------------------------------------------- threshold calibration
 // tau for one score set: the (c + 1)-th largest |h| of its m scores, c =
 // ceil((1 - s) m - 1e-9) (the keep count), or -1 when c >= m.  Block b < E
@@ -1430,10 +1603,25 @@ bool threshold_supported(int d_ff) {
 // The page's literal masking: gate/up, one compare pass against tau[e],
 // then the variable-count sparse down projection.
 hipError_t launch_ffn_threshold(const FfnArgs &a, const float *tau, int32_t *counts,
-                                hipStream_t stream) {
+                                bool want_counts, bool want_idx, hipStream_t stream) {
   if (a.T == 0) return hipSuccess;
   const RouteView rv = make_view(a);
   launch_gateup(a, rv, stream);
+  if (a.T <= 16) {  // decode batches: the compare runs inside the down kernel
+    const int sw = down_block_cols(a.T, a.H);
+    dim3 grid(a.T, a.H / sw);
+    int32_t *co = want_counts ? counts : nullptr;
+    int32_t *io = want_idx ? a.idx : nullptr;
+    timer_begin(kStageDownRows, stream);
+#define MOE_DT(BF, SWV)                                                                         \
+  down_thr_token_kernel<BF, SWV><<<grid, 1024, 0, stream>>>(a.w_down, a.h, tau, rv, a.H, a.d_ff, \
+                                                            a.accumulate, a.y, co, io)
+    if (a.bf16) { if (sw == 128) MOE_DT(true, 128); else MOE_DT(true, 64); }
+    else { if (sw == 128) MOE_DT(false, 128); else MOE_DT(false, 64); }
+#undef MOE_DT
+    timer_end(stream);
+    return hipGetLastError();
+  }
   const int P = a.T * a.top_k;
   timer_begin(kStageMask, stream);
   switch (a.d_ff) {

@@ -119,8 +119,9 @@ class DeviceLayer:
         return out
 
 
-    def run_threshold(self, x_host: np.ndarray, tau, tau_sh=None):
-        """One layer call with threshold masking (tau: device float32 [E])."""
+    def run_threshold(self, x_host: np.ndarray, tau, tau_sh=None, outputs=True):
+        """One layer call with threshold masking (tau: device float32 [E]);
+        outputs=False asks the library for neither kept counts nor ids."""
         sh = self.inp.shape
         T = x_host.shape[0]
         x = to_dev(x_host)
@@ -133,7 +134,8 @@ class DeviceLayer:
         cnt = torch.full((P,), -1, dtype=torch.int32, device="cuda")
         ws = torch.empty(B.moe_ffn_threshold_workspace_size(self.desc, T), dtype=torch.uint8,
                          device="cuda")
-        B.moe_expert_ffn_sparse_threshold(self.desc, T, tau, x, *self.w, R, y, 0, cnt, idx, ws)
+        B.moe_expert_ffn_sparse_threshold(self.desc, T, tau, x, *self.w, R, y, 0,
+                                          cnt if outputs else None, idx if outputs else None, ws)
         out = dict(T=T)
         if self.desc_sh is not None:
             ds = self.desc_sh

@@ -148,9 +148,12 @@ def test_updown_reads_only_kept_up_and_down_rows_and_is_reproducible():
 
 # ------------------------------------------------------------------ threshold masking
 
+# batches up to 16 run the compare inside the down kernel, larger ones the
+# separate mask kernel
 THRESH = [("tiny-f32", 8, 4, 0.9), ("olmoe-like", 32, 16, 0.9), ("olmoe-like", 32, 4, 0.5),
           ("qwen3-moe-like", 64, 8, 0.9), ("deepseek-v2-like", 8, 4, 0.9),
-          ("llama4-like", 4, 2, 0.9)]
+          ("llama4-like", 4, 2, 0.9), ("olmoe-like", 32, 33, 0.7), ("qwen3-moe-like", 64, 40, 0.9),
+          ("tiny-f32", 8, 24, 0.5)]
 
 
 @pytest.mark.parametrize("name,T_cal,T,s", THRESH)
@@ -191,6 +194,13 @@ def test_threshold_extremes_and_calibration_target():
     # a huge tau keeps nothing: y == 0
     none = dev.run_threshold(x, torch.full((E,), 1e30, device="cuda"))
     assert np.all(none["cnt"] == 0) and np.all(none["y"] == 0)
+    # the kept counts and ids are optional outputs; y does not depend on them
+    tau_mid = torch.full((E,), 0.05, device="cuda")
+    for T in (16, 40):
+        xt = inp.tokens(T, 24)
+        a = dev.run_threshold(xt, tau_mid)
+        b = dev.run_threshold(xt, tau_mid, outputs=False)
+        np.testing.assert_array_equal(a["y"], b["y"])
     # calibrated on these very tokens, each expert keeps its target count
     for s in (0.5, 0.9):
         tau = dev.calibrate(x, s)
