@@ -1011,7 +1011,7 @@ __global__ __launch_bounds__(1024) void down_thr_token_kernel(
   __shared__ float scoef[kDownStage];
   __shared__ uint32_t skey[32], sbase[32];
   __shared__ float sw[32];
-  __shared__ int scnt[32], spref[33], tmp[16];
+  __shared__ int spref[33], tmp[16];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int t = blockIdx.x, col0 = blockIdx.y * SW;
   const int top_k = rv.top_k, n = top_k * d_ff;
@@ -1022,7 +1022,6 @@ __global__ __launch_bounds__(1024) void down_thr_token_kernel(
     skey[tid] = te < 0.f ? 0xffffffffu : __float_as_uint(fabsf(te));  // ~0: keep all
     sbase[tid] = (uint32_t)e * (uint32_t)d_ff;
     sw[tid] = rv.weight(p);
-    scnt[tid] = 0;
   }
   __syncthreads();
   const float *ht = h + (size_t)t * n;
@@ -1042,30 +1041,31 @@ __global__ __launch_bounds__(1024) void down_thr_token_kernel(
       if (c == 4 * r) v = cache[r];
     return c < 4 * KC ? v : ld16(ht + q0 + c);
   };
-  // pass 1: per-thread count, per-slot counts
-  int cnt = 0;
+  // pass 1: per-thread count.  A slot starts at a multiple of d_ff, and a
+  // thread's range (C < d_ff elements) holds at most one such start: that
+  // thread notes how many of its kept elements precede it, which after the
+  // scan gives the slot's offset in the token's kept list.
+  int cnt = 0, my_s = -1, my_before = 0;
 #pragma unroll
   for (int r = 0; r < KC; ++r)
     if (4 * r < C && q0 + 4 * r < n) cache[r] = ld16(ht + q0 + 4 * r);
   for (int c = 0; c < C && q0 + c < n; c += 4) {
     const u32x4 v = elems(c);
     const int s = (q0 + c) / d_ff;  // 4 elements never straddle slots (d_ff % 64 == 0)
+    if (q0 + c == s * d_ff) { my_s = s; my_before = cnt; }
     int m = 0;
 #pragma unroll
     for (int u = 0; u < 4; ++u) m += kept(v[u], s);
-    if (m) atomicAdd(&scnt[s], m);
     cnt += m;
   }
   int total = 0;
   const int incl = block_incl_scan<1024>(cnt, tmp, &total);
   const int my0 = incl - cnt;
-  if (tid == 0) {
-    spref[0] = 0;
-    for (int s = 0; s < top_k; ++s) spref[s + 1] = spref[s] + scnt[s];
-  }
+  if (my_s >= 0) spref[my_s] = my0 + my_before;
+  if (tid == 0) spref[top_k] = total;
   __syncthreads();
   if (blockIdx.y == 0) {  // the token's counts and kept ids, for the caller
-    if (counts_out && tid < top_k) counts_out[t * top_k + tid] = scnt[tid];
+    if (counts_out && tid < top_k) counts_out[t * top_k + tid] = spref[tid + 1] - spref[tid];
     if (idx_out && cnt) {
       int pos = my0;
       for (int c = 0; c < C && q0 + c < n; c += 4) {
