@@ -681,25 +681,37 @@ __global__ __launch_bounds__(64) void up_rows_kernel(const void *__restrict__ wu
   float acc[kUpRows];
 #pragma unroll
   for (int r = 0; r < kUpRows; ++r) acc[r] = 0.f;
-  for (int off = lane * 16; off < row_bytes; off += 1024) {
-    const u32x4 xq = ld16(xr + off);
-    u32x4 q[kUpRows];
+  // two 1 KB steps of every row in flight at once (row_bytes is a multiple
+  // of 128, so a step may be partial: lanes past the row end load nothing)
+  for (int off0 = 0; off0 < row_bytes; off0 += 2048) {
+    u32x4 xq[2], q[2][kUpRows];
 #pragma unroll
-    for (int r = 0; r < kUpRows; ++r) q[r] = i0 + r < k ? ld16(rows[r] + off) : u32x4{0, 0, 0, 0};
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const int off = off0 + 1024 * h2 + lane * 16;
+      const bool in = off < row_bytes;
+      xq[h2] = in ? ld16(xr + off) : u32x4{0, 0, 0, 0};
 #pragma unroll
-    for (int r = 0; r < kUpRows; ++r) {
-      float a = 0.f;
-      if (BF16) {
+      for (int r = 0; r < kUpRows; ++r)
+        q[h2][r] = in && i0 + r < k ? ld16(rows[r] + off) : u32x4{0, 0, 0, 0};
+    }
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          a = fmaf(bf16lo(q[r][c]), bf16lo(xq[c]), a);
-          a = fmaf(bf16hi(q[r][c]), bf16hi(xq[c]), a);
+    for (int h2 = 0; h2 < 2; ++h2) {
+#pragma unroll
+      for (int r = 0; r < kUpRows; ++r) {
+        float a = 0.f;
+        if (BF16) {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            a = fmaf(bf16lo(q[h2][r][c]), bf16lo(xq[h2][c]), a);
+            a = fmaf(bf16hi(q[h2][r][c]), bf16hi(xq[h2][c]), a);
+          }
+        } else {
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            a = fmaf(__uint_as_float(q[h2][r][c]), __uint_as_float(xq[h2][c]), a);
         }
-      } else {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) a = fmaf(__uint_as_float(q[r][c]), __uint_as_float(xq[c]), a);
+        acc[r] += a;
       }
-      acc[r] += a;
     }
   }
 #pragma unroll
