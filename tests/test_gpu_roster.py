@@ -115,3 +115,38 @@ def test_roster_with_zero_delta_is_moe_route():
             assert torch.equal(getattr(R0, f), getattr(R1, f)), f
         inc = torch.zeros_like(before).scatter_(1, R0.topk_ids[:T].long(), 1)
         assert torch.equal(usage, before + inc)
+
+
+def test_roster_graph_replays_follow_the_eager_steps():
+    # the usage counts are state: replaying a captured roster step must walk
+    # through the same states as eager steps, replay after replay
+    shape = S.LAYERS["olmoe-like"]
+    E, K, T = shape.n_experts, shape.top_k, 16
+    desc = B.make_desc(shape.hidden, E, shape.d_ff, K, shape.norm_topk, shape.dtype)
+    wr_d = to_dev(S.router_matrix(shape, 0))
+    x = to_dev(S.tokens(shape, 9, T))
+    ws = torch.empty(B.moe_route_workspace_size(desc, T), dtype=torch.uint8, device="cuda")
+    R, R2 = B.Routing.allocate(T, K, E), B.Routing.allocate(T, K, E)
+    u0 = torch.from_numpy(_start_usage(np.random.default_rng(5), T, E, 4)).cuda()
+    usage = u0.clone()
+    say("[case] roster graph replays")
+    eager = []
+    for _ in range(4):
+        B.moe_route_roster(desc, T, x, wr_d, None, usage, None, 4, 0.7, R, ws)
+        torch.cuda.synchronize()
+        eager.append((R.topk_ids.clone(), usage.clone()))
+    usage.copy_(u0)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        B.moe_route_roster(desc, T, x, wr_d, None, usage, None, 4, 0.7, R, ws)
+    torch.cuda.synchronize()
+    usage.copy_(u0)
+    torch.cuda.synchronize()
+    for i, (ids, u) in enumerate(eager):
+        R.topk_ids.fill_(-1)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(R.topk_ids, ids), f"replay {i}: expert ids"
+        assert torch.equal(usage, u), f"replay {i}: usage"
+        B.moe_route(desc, T, x, wr_d, None, R2, ws)          # eager work between replays
+        torch.cuda.synchronize()
