@@ -293,6 +293,58 @@ __device__ __forceinline__ void block_group(const int32_t *ids, int P, int E,
   }
 }
 
+// The same grouping by one wave, for the few pairs of a decode batch: no
+// block barriers (they dominated the block version at T <= 16).  Counts by
+// LDS atomics, offsets and the active list by wave scans over 64 experts at
+// a time, then placement 64 pairs at a time with ballot matching on the
+// expert id bits; `cur` (LDS, >= E ints) holds the per-expert cursors.
+// Same result as block_group: a stable sort by (expert, pair id).
+__device__ __forceinline__ void wave_group(const int32_t *ids, int P, int E,
+                                           int32_t *__restrict__ offsets,
+                                           int32_t *__restrict__ pair_by_expert,
+                                           int32_t *__restrict__ active,
+                                           int32_t *__restrict__ n_active, int *cur) {
+  const int lane = threadIdx.x & 63;
+  for (int e = lane; e < E; e += 64) cur[e] = 0;
+  for (int p = lane; p < P; p += 64) atomicAdd(&cur[ids[p]], 1);
+  int base = 0, abase = 0;
+  for (int e0 = 0; e0 < E; e0 += 64) {
+    const int e = e0 + lane;
+    const int c = e < E ? cur[e] : 0;
+    const int incl = wave_incl_scan(c);
+    const int flag = c > 0 ? 1 : 0;
+    const int aincl = wave_incl_scan(flag);
+    if (e < E) {
+      offsets[e] = base + incl - c;
+      cur[e] = base + incl - c;  // the expert's cursor starts at its offset
+    }
+    if (flag) active[abase + aincl - 1] = e;
+    base += lane_value(incl, 63);
+    abase += lane_value(aincl, 63);
+  }
+  if (lane == 0) {
+    offsets[E] = base;
+    *n_active = abase;
+  }
+  const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
+  const uint64_t lt_mask = (1ull << lane) - 1ull;
+  for (int p0 = 0; p0 < P; p0 += 64) {
+    const int p = p0 + lane;
+    const bool valid = p < P;
+    const int e = valid ? ids[p] : 0;
+    uint64_t peers = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+      const int bit = (e >> b) & 1;
+      const uint64_t m = __ballot(valid && bit);
+      peers &= bit ? m : ~m;
+    }
+    const int rank = __popcll(peers & lt_mask);
+    const int at = valid ? cur[e] : 0;  // every lane reads before the leader writes
+    if (valid) pair_by_expert[at + rank] = p;
+    if (valid && rank == 0) cur[e] = at + __popcll(peers);
+  }
+}
+
 __global__ __launch_bounds__(1024) void route_group_kernel(const int32_t *__restrict__ ids, int P,
                                                            int E, int32_t *__restrict__ offsets,
                                                            int32_t *__restrict__ pair_by_expert,
@@ -334,7 +386,11 @@ __global__ __launch_bounds__(1024) void route_select_group_kernel(
     }
   }
   __syncthreads();
-  block_group(sids, T * top_k, E, offsets, pair_by_expert, active, n_active, cursor, wcnt, tmp);
+  if (T * top_k <= 256) {
+    if (threadIdx.x < 64) wave_group(sids, T * top_k, E, offsets, pair_by_expert, active, n_active, cursor);
+  } else {
+    block_group(sids, T * top_k, E, offsets, pair_by_expert, active, n_active, cursor, wcnt, tmp);
+  }
 }
 
 template <int V, bool RO>
