@@ -65,7 +65,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-variant", action="store_true",
-                    help="skip the gate-score split variant (moe_expert_ffn_sparse_updown)")
+                    help="skip the variants beside the headline (split, thresholds, roster, decode step)")
     ap.add_argument("--crossover", action="store_true",
                     help="sparse-vs-dense sweep of the Llama-4-like layer (its own JSON line)")
     ap.add_argument("--layer", default=None, help="layer of the crossover sweep")
@@ -92,7 +92,8 @@ class Workload:
         self.auto_path = B.moe_select_path(self.desc, T, self.k)
         self.path = self.auto_path if forced is None else forced
         self.score = score
-        if score in ("gate", "threshold"):   # these masks have a sparse form only
+        thr = score in ("threshold", "gate_threshold")
+        if score != "swiglu":   # these masks have a sparse form only
             self.path = B.MOE_PATH_SPARSE
         # always-on shared experts (routing NULL, accumulated into y)
         self.desc_sh = None
@@ -126,7 +127,7 @@ class Workload:
                               dtype=torch.uint8, device="cuda")
         self.y = [torch.empty((T, sh.hidden), dtype=torch.float32, device="cuda") for _ in range(self.L)]
         self.idx = torch.empty((T * K, max(1, self.k)), dtype=torch.int32, device="cuda")
-        if score == "threshold":
+        if thr:
             # per-expert tau for the target sparsity, calibrated once offline on
             # tokens of another seed (the thresholds are fixed before serving)
             x_cal = host_w.to_dev(S.tokens(sh, CAL_SEED, CAL_TOKENS))
@@ -137,8 +138,12 @@ class Workload:
             ws_c = torch.empty(B.moe_calibrate_workspace_size(self.desc, CAL_TOKENS),
                                dtype=torch.uint8, device="cuda")
             self.tau = torch.empty(E, dtype=torch.float32, device="cuda")
-            B.moe_calibrate_thresholds(self.desc, CAL_TOKENS, x_cal, dev_w0[1], dev_w0[2], r_cal,
-                                       sparsity, self.tau, ws_c)
+            if score == "gate_threshold":   # on the split's scores |silu(W_g x)|
+                B.moe_calibrate_thresholds_gate(self.desc, CAL_TOKENS, x_cal, dev_w0[1], r_cal,
+                                                sparsity, self.tau, ws_c)
+            else:
+                B.moe_calibrate_thresholds(self.desc, CAL_TOKENS, x_cal, dev_w0[1], dev_w0[2],
+                                           r_cal, sparsity, self.tau, ws_c)
             torch.cuda.synchronize()
             del ws_c, r_cal, x_cal
             self.ws = torch.empty(B.moe_ffn_threshold_workspace_size(self.desc, T),
@@ -148,11 +153,12 @@ class Workload:
         self.ffn = B.moe_expert_ffn_sparse if self.path == B.MOE_PATH_SPARSE else B.moe_expert_ffn_dense
         if score == "gate":   # the page's own split (w_up row-major in dev_w0)
             self.ffn = B.moe_expert_ffn_sparse_updown
-        if score == "threshold":  # the page's literal mask: |h| > tau[e], counts vary
+        if thr:  # the page's literal mask: a score above tau[e], counts vary
+            fn = (B.moe_expert_ffn_sparse_updown_threshold if score == "gate_threshold"
+                  else B.moe_expert_ffn_sparse_threshold)
             self.ffn = lambda d, T_, k, x, wg, wu, wd, r, y, acc, idx, ws: \
-                B.moe_expert_ffn_sparse_threshold(d, T_, self.tau, x, wg, wu, wd, r, y, acc,
-                                                  self.counts if idx is not None else None,
-                                                  idx, ws)
+                fn(d, T_, self.tau, x, wg, wu, wd, r, y, acc,
+                   self.counts if idx is not None else None, idx, ws)
         self.graphs = []
 
     def step(self, i, idx=None):
@@ -215,17 +221,18 @@ class Workload:
             P = ids.shape[0]
             bw = 2 if sh.dtype == "bf16" else 4
             H, d = sh.hidden, sh.d_ff
-            cnt = (self.counts.cpu().numpy() if self.score == "threshold"
+            cnt = (self.counts.cpu().numpy() if self.score in ("threshold", "gate_threshold")
                    else np.full(P, self.k, dtype=np.int64))
+            gate_only = self.score in ("gate", "gate_threshold")
             kept = [idx[p, :cnt[p]] for p in range(P)]
             union = sum(len(np.unique(np.concatenate([kept[p] for p in np.nonzero(ids == e)[0]])))
                         for e in active)
             rec = dict(
                 active=int(len(active)), pairs=int(P),
                 router=sh.n_experts * H * bw,
-                gateup=(int(len(active)) * (2 if self.score == "swiglu" else 1) * H * d * bw
+                gateup=(int(len(active)) * (1 if gate_only else 2) * H * d * bw
                         + self.T * H * bw + P * d * 4),
-                up_rows=P * self.k * H * bw if self.score == "gate" else 0,
+                up_rows=int(cnt.sum()) * H * bw if gate_only else 0,
                 down_rows=int(cnt.sum()) * H * bw, mean_kept=float(cnt.mean()),
                 down_union=union * H * bw,
                 down_dense=int(len(active)) * d * H * bw,
@@ -746,41 +753,31 @@ def main():
     log("[bench] practical read peak")
     practical = practical_read_peak()
     log(f"[bench] moe_stream_read: {practical['gbs']:.0f} GB/s")
-    # the page's own split (gate-only scores, sparse up and down rows): a
-    # different mask, so reported beside the headline rather than as it
-    updown = {}
+    # the variants beside the headline (different masks, same layer):
+    #   updown          the page's own split: gate-only scores, sparse up and down
+    #   threshold       the page's literal mask on |h|: calibrated tau, counts vary
+    #   updown_threshold the split with the threshold mask: the page's pipeline
+    variants = {"updown": {}, "threshold": {}, "updown_threshold": {}}
     if not args.no_variant:
         dev_gate = (dev_w0[0], dev_w0[1], host.to_dev(host.wu), dev_w0[3])
-        for T in sorted(set(sweep + [args.batch])):
-            wl, res = measure(shape, host, dev_gate, T, args, score="gate")
-            updown[str(T)] = {"us_per_call": round(res["us_per_call"], 3),
-                              "us_per_token": round(res["us_per_token"], 3),
-                              "layer_bytes": int(res["layer_bytes"]),
-                              "hbm_gbs": round(res["hbm_gbs"], 1),
-                              "kernels_us": {k: round(v["avg_us"], 2) for k, v in res["kernels"].items()}}
-            log(f"[bench] updown T={T}: {res['us_per_call']:.1f} us/call, "
-                f"{res['us_per_token']:.2f} us/token; kernels "
-                + ", ".join(f"{k} {v['avg_us']:.1f}" for k, v in res["kernels"].items()))
-            del wl
-            torch.cuda.empty_cache()
+        runs = (("updown", dev_gate, "gate"), ("threshold", dev_w0, "threshold"),
+                ("updown_threshold", dev_gate, "gate_threshold"))
+        for name, weights, score in runs:
+            for T in sorted(set(sweep + [args.batch])):
+                wl, res = measure(shape, host, weights, T, args, score=score)
+                variants[name][str(T)] = {
+                    "us_per_call": round(res["us_per_call"], 3),
+                    "us_per_token": round(res["us_per_token"], 3),
+                    "mean_kept": round(res["mean_kept"], 1),
+                    "layer_bytes": int(res["layer_bytes"]),
+                    "hbm_gbs": round(res["hbm_gbs"], 1),
+                    "kernels_us": {k: round(v["avg_us"], 2) for k, v in res["kernels"].items()}}
+                log(f"[bench] {name} T={T}: {res['us_per_call']:.1f} us/call, "
+                    f"{res['us_per_token']:.2f} us/token, mean kept {res['mean_kept']:.1f}; kernels "
+                    + ", ".join(f"{k} {v['avg_us']:.1f}" for k, v in res["kernels"].items()))
+                del wl
+                torch.cuda.empty_cache()
         del dev_gate
-    # the page's literal mask: per-expert thresholds calibrated offline for
-    # the target sparsity, one compare pass, a kept count per pair
-    thresh = {}
-    if not args.no_variant:
-        for T in sorted(set(sweep + [args.batch])):
-            wl, res = measure(shape, host, dev_w0, T, args, score="threshold")
-            thresh[str(T)] = {"us_per_call": round(res["us_per_call"], 3),
-                              "us_per_token": round(res["us_per_token"], 3),
-                              "mean_kept": round(res["mean_kept"], 1),
-                              "layer_bytes": int(res["layer_bytes"]),
-                              "hbm_gbs": round(res["hbm_gbs"], 1),
-                              "kernels_us": {k: round(v["avg_us"], 2) for k, v in res["kernels"].items()}}
-            log(f"[bench] threshold T={T}: {res['us_per_call']:.1f} us/call, "
-                f"{res['us_per_token']:.2f} us/token, mean kept {res['mean_kept']:.1f}; kernels "
-                + ", ".join(f"{k} {v['avg_us']:.1f}" for k, v in res["kernels"].items()))
-            del wl
-            torch.cuda.empty_cache()
     roster = step = None
     if not args.no_variant:
         roster = roster_variant(shape, host, dev_w0)
@@ -823,11 +820,15 @@ def main():
         "practical_read_peak": practical,
         "updown_variant": {"what": "the page's own split: dense gate scores |silu(W_g x)|, "
                                    "up and down gathered on the kept rows (a different mask)",
-                           "batches": updown} if updown else None,
+                           "batches": variants["updown"]} if variants["updown"] else None,
         "threshold_variant": {"what": "the page's literal mask: keep |h| > tau[e], tau per expert "
                                       f"calibrated for sparsity {args.sparsity} on {CAL_TOKENS} "
                                       f"tokens of seed {CAL_SEED}; kept count varies per pair",
-                              "batches": thresh} if thresh else None,
+                              "batches": variants["threshold"]} if variants["threshold"] else None,
+        "updown_threshold_variant": {
+            "what": "the page's pipeline: dense gate scores, keep |silu(g)| > tau[e] (calibrated "
+                    f"on the gate scores, sparsity {args.sparsity}), up and down on the kept rows",
+            "batches": variants["updown_threshold"]} if variants["updown_threshold"] else None,
         "roster_variant": roster,
         "decode_step_variant": step,
         "cpu_baseline": cpu,

@@ -294,6 +294,39 @@ moe_status moe_calibrate_thresholds(const moe_desc *d, int32_t T, const void *x,
                                     void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * moe_expert_ffn_sparse_updown_threshold -- the page's own pipeline with its
+ * threshold mask (technical summary, Methodology: the gate projection runs
+ * densely and gives the activation scores, a single-pass threshold mask
+ * replaces the top-k sort, and the fused up-down projection gathers only
+ * the active neurons' weights): per pair (t, e), s = silu(W_g x) densely,
+ * neuron j kept iff |s_j| > tau[e] (tau[e] < 0 keeps all), and for kept j
+ * only h_j = s_j * (W_u[j] . x), then the sparse down projection of
+ * moe_expert_ffn_sparse.  w_gate packed (moe_pack_gate_up), w_up and w_down
+ * row-major.  tau [E] fp32 device, e.g. from moe_calibrate_thresholds_gate.
+ * counts_out, active_idx_out, workspace (moe_ffn_threshold_workspace_size),
+ * outputs and errors as moe_expert_ffn_sparse_threshold.
+ */
+moe_status moe_expert_ffn_sparse_updown_threshold(const moe_desc *d, int32_t T, const float *tau,
+                                                  const void *x, const void *w_gate,
+                                                  const void *w_up, const void *w_down,
+                                                  const moe_routing *routing, float *y,
+                                                  int32_t accumulate, int32_t *counts_out,
+                                                  int32_t *active_idx_out, void *workspace,
+                                                  size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * moe_calibrate_thresholds_gate -- moe_calibrate_thresholds on the split's
+ * scores |silu(W_g x)| (no up projection is run or needed), for
+ * moe_expert_ffn_sparse_updown_threshold.  Arguments, workspace
+ * (moe_calibrate_workspace_size) and errors as moe_calibrate_thresholds
+ * without w_up.
+ */
+moe_status moe_calibrate_thresholds_gate(const moe_desc *d, int32_t T, const void *x,
+                                         const void *w_gate, const moe_routing *routing,
+                                         double sparsity, float *tau_out, void *workspace,
+                                         size_t workspace_bytes, hipStream_t stream);
+
+/*
  * moe_residual_add -- the residual stream between the layers of a decode
  * step: x_out[t, h] = x_in[t, h] + y[t, h], rounded to desc->dtype (round to
  * nearest even for bf16; finite values).  x_in, x_out [T, H] in desc->dtype,

@@ -46,6 +46,9 @@ _PD, _PR = ctypes.POINTER(MoeDesc), ctypes.POINTER(MoeRouting)
 _SIGS = {
     "moe_route": (_I32, [_PD, _I32, _V, _V, _V, _PR, _V, _SZ, _V]),
     "moe_residual_add": (_I32, [_PD, _I32, _V, _V, _V, _V]),
+    "moe_expert_ffn_sparse_updown_threshold": (_I32, [_PD, _I32, _V, _V, _V, _V, _V, _PR, _V, _I32,
+                                                      _V, _V, _V, _SZ, _V]),
+    "moe_calibrate_thresholds_gate": (_I32, [_PD, _I32, _V, _V, _PR, _D, _V, _V, _SZ, _V]),
     "moe_route_roster": (_I32, [_PD, _I32, _V, _V, _V, _V, _V, _I32, ctypes.c_float, _PR, _V, _SZ,
                                 _V]),
     "moe_expert_ffn_sparse": (_I32, [_PD, _I32, _I32, _V, _V, _V, _V, _PR, _V, _I32, _V, _V, _SZ, _V]),
@@ -232,6 +235,30 @@ def moe_calibrate_thresholds(desc, T, x, w_gate, w_up, routing, sparsity, tau_ou
     ws = _ptr(workspace)
     _check(lib().moe_calibrate_thresholds(
         ctypes.byref(desc), int(T), _ptr(x), _ptr(w_gate), _ptr(w_up),
+        ctypes.byref(r) if r is not None else None, float(sparsity), _ptr(tau_out), ws,
+        workspace.numel() * workspace.element_size() if ws else 0, _stream(stream)))
+
+
+def moe_expert_ffn_sparse_updown_threshold(desc, T, tau, x, w_gate, w_up, w_down, routing, y,
+                                           accumulate=0, counts_out=None, active_idx_out=None,
+                                           workspace=None, stream=None):
+    """The split with threshold masks on the gate scores (w_up row-major)."""
+    r = routing.as_c() if routing is not None else None
+    ws = _ptr(workspace)
+    _check(lib().moe_expert_ffn_sparse_updown_threshold(
+        ctypes.byref(desc), int(T), _ptr(tau), _ptr(x), _ptr(w_gate), _ptr(w_up), _ptr(w_down),
+        ctypes.byref(r) if r is not None else None, _ptr(y), int(accumulate), _ptr(counts_out),
+        _ptr(active_idx_out), ws, workspace.numel() * workspace.element_size() if ws else 0,
+        _stream(stream)))
+
+
+def moe_calibrate_thresholds_gate(desc, T, x, w_gate, routing, sparsity, tau_out,
+                                  workspace=None, stream=None):
+    """Per-expert thresholds on the gate scores |silu(W_g x)|."""
+    r = routing.as_c() if routing is not None else None
+    ws = _ptr(workspace)
+    _check(lib().moe_calibrate_thresholds_gate(
+        ctypes.byref(desc), int(T), _ptr(x), _ptr(w_gate),
         ctypes.byref(r) if r is not None else None, float(sparsity), _ptr(tau_out), ws,
         workspace.numel() * workspace.element_size() if ws else 0, _stream(stream)))
 

@@ -82,7 +82,11 @@ struct FfnLayout {
 };
 
 // What an FFN-shaped call does (all share validation and the carve-up).
-enum RunMode { kRunSparse, kRunDense, kRunUpdown, kRunThreshold, kRunCalibrate };
+enum RunMode {
+  kRunSparse, kRunDense, kRunUpdown, kRunThreshold, kRunCalibrate,
+  kRunUpdownThreshold,  // the split with threshold masks on the gate scores
+  kRunCalibrateGate     // calibration on the gate scores (no w_up)
+};
 
 FfnLayout ffn_layout(const moe_desc *d, int32_t T, int32_t k, moe_path path) {
   const size_t P = (size_t)T * d->top_k;
@@ -139,7 +143,8 @@ moe_status run_ffn(RunMode mode, const moe_desc *d, int32_t T, int32_t k_keep, c
   TRY(check_desc(d));
   TRY(check_T(T));
   const moe_path path = mode == kRunDense ? MOE_PATH_DENSE : MOE_PATH_SPARSE;
-  const bool thr = mode == kRunThreshold, cal = mode == kRunCalibrate;
+  const bool thr = mode == kRunThreshold || mode == kRunUpdownThreshold;
+  const bool cal = mode == kRunCalibrate || mode == kRunCalibrateGate;
   if (thr || cal) k_keep = d->d_ff;
   if (k_keep < 0 || k_keep > d->d_ff)
     return fail(MOE_ERR_INVALID_ARG, "k_keep %d outside [0, d_ff=%d]", k_keep, d->d_ff);
@@ -167,7 +172,7 @@ moe_status run_ffn(RunMode mode, const moe_desc *d, int32_t T, int32_t k_keep, c
   if (T == 0) return MOE_OK;
   TRY(need_ptr(x, "x"));
   TRY(need_ptr(w_gate, "w_gate"));
-  TRY(need_ptr(w_up, "w_up"));
+  if (mode != kRunCalibrateGate) TRY(need_ptr(w_up, "w_up"));
   if (!cal) {
     TRY(need_ptr(w_down, "w_down"));
     TRY(need_ptr(y, "y"));
@@ -226,9 +231,14 @@ moe_status run_ffn(RunMode mode, const moe_desc *d, int32_t T, int32_t k_keep, c
           a, m.tau, m.counts ? m.counts : reinterpret_cast<int32_t *>(ws + L.counts),
           m.counts != nullptr, active_idx_out != nullptr, stream);
       break;
+    case kRunUpdownThreshold:
+      e = moe::launch_ffn_updown_threshold(
+          a, m.tau, m.counts ? m.counts : reinterpret_cast<int32_t *>(ws + L.counts), stream);
+      break;
     case kRunCalibrate:
+    case kRunCalibrateGate:
       e = moe::launch_calibrate(a, m.sparsity, m.tau_out, reinterpret_cast<float *>(ws + L.counts),
-                                stream);
+                                mode == kRunCalibrateGate, stream);
       break;
     case kRunDense: e = moe::launch_ffn_dense(a, stream); break;
     default: e = moe::launch_ffn_sparse(a, stream);
@@ -356,6 +366,31 @@ moe_status moe_expert_ffn_sparse_threshold(const moe_desc *d, int32_t T, const f
   m.counts = counts_out;
   return run_ffn(kRunThreshold, d, T, 0, x, w_gate, w_up, w_down, routing, y, accumulate,
                  active_idx_out, workspace, workspace_bytes, stream, m);
+}
+
+moe_status moe_expert_ffn_sparse_updown_threshold(const moe_desc *d, int32_t T, const float *tau,
+                                                  const void *x, const void *w_gate,
+                                                  const void *w_up, const void *w_down,
+                                                  const moe_routing *routing, float *y,
+                                                  int32_t accumulate, int32_t *counts_out,
+                                                  int32_t *active_idx_out, void *workspace,
+                                                  size_t workspace_bytes, hipStream_t stream) {
+  ModeArgs m;
+  m.tau = tau;
+  m.counts = counts_out;
+  return run_ffn(kRunUpdownThreshold, d, T, 0, x, w_gate, w_up, w_down, routing, y, accumulate,
+                 active_idx_out, workspace, workspace_bytes, stream, m);
+}
+
+moe_status moe_calibrate_thresholds_gate(const moe_desc *d, int32_t T, const void *x,
+                                         const void *w_gate, const moe_routing *routing,
+                                         double sparsity, float *tau_out, void *workspace,
+                                         size_t workspace_bytes, hipStream_t stream) {
+  ModeArgs m;
+  m.sparsity = sparsity;
+  m.tau_out = tau_out;
+  return run_ffn(kRunCalibrateGate, d, T, 0, x, w_gate, nullptr, nullptr, routing, nullptr, 0,
+                 nullptr, workspace, workspace_bytes, stream, m);
 }
 
 moe_status moe_calibrate_thresholds(const moe_desc *d, int32_t T, const void *x,

@@ -656,23 +656,23 @@ __global__ __launch_bounds__(64 * NW) void neuron_topk_seg_kernel(const float *_
 // down projection's w * h_j.
 constexpr int kUpRows = 8;
 
+// Rows i0 .. i0 + kUpRows - 1 (those below n) of pair p's kept list: ids
+// idx_row[i], coefficients coef_row[i] multiplied in place by u = W_u row . x.
 template <bool BF16>
-__global__ __launch_bounds__(64) void up_rows_kernel(const void *__restrict__ wuv,
-                                                     const void *__restrict__ xv, RouteView rv,
-                                                     int H, int d_ff, int k,
-                                                     const int32_t *__restrict__ idx,
-                                                     float *__restrict__ coef) {
+__device__ __forceinline__ void up_rows_group(const void *__restrict__ wuv,
+                                              const void *__restrict__ xv, const RouteView &rv,
+                                              int H, int d_ff, int p, int i0, int n,
+                                              const int32_t *__restrict__ idx_row,
+                                              float *__restrict__ coef_row) {
   constexpr int EB = BF16 ? 2 : 4;
-  const int lane = threadIdx.x;
-  const int p = blockIdx.x;
-  const int i0 = blockIdx.y * kUpRows;
+  const int lane = threadIdx.x & 63;
   const int t = p / rv.top_k;
   const size_t e = (size_t)rv.expert_of_pair(p);
   const uint8_t *rows[kUpRows];
 #pragma unroll
   for (int r = 0; r < kUpRows; ++r) {
     const int i = i0 + r;
-    int j = i < k ? idx[(size_t)p * k + i] : 0;
+    int j = i < n ? idx_row[i] : 0;
     j = (unsigned)j < (unsigned)d_ff ? j : 0;
     rows[r] = static_cast<const uint8_t *>(wuv) + (e * d_ff + j) * H * EB;
   }
@@ -692,7 +692,7 @@ __global__ __launch_bounds__(64) void up_rows_kernel(const void *__restrict__ wu
       xq[h2] = in ? ld16(xr + off) : u32x4{0, 0, 0, 0};
 #pragma unroll
       for (int r = 0; r < kUpRows; ++r)
-        q[h2][r] = in && i0 + r < k ? ld16(rows[r] + off) : u32x4{0, 0, 0, 0};
+        q[h2][r] = in && i0 + r < n ? ld16(rows[r] + off) : u32x4{0, 0, 0, 0};
     }
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
@@ -718,8 +718,38 @@ __global__ __launch_bounds__(64) void up_rows_kernel(const void *__restrict__ wu
   for (int r = 0; r < kUpRows; ++r) {
     const float u = wave_sum(acc[r]);
     const int i = i0 + r;
-    if (lane == 0 && i < k) coef[(size_t)p * k + i] *= u;
+    if (lane == 0 && i < n) coef_row[i] *= u;
   }
+}
+
+// Fixed count k per pair (top-k masks): block (p, g) takes rows 8 g ...
+template <bool BF16>
+__global__ __launch_bounds__(64) void up_rows_kernel(const void *__restrict__ wuv,
+                                                     const void *__restrict__ xv, RouteView rv,
+                                                     int H, int d_ff, int k,
+                                                     const int32_t *__restrict__ idx,
+                                                     float *__restrict__ coef) {
+  const int p = blockIdx.x;
+  up_rows_group<BF16>(wuv, xv, rv, H, d_ff, p, blockIdx.y * kUpRows, k, idx + (size_t)p * k,
+                      coef + (size_t)p * k);
+}
+
+// Per-pair counts (threshold masks), lists at row stride d_ff: block (p, g)
+// takes row groups g, g + G, ... below the pair's count (G = gridDim.y), so
+// the grid does not depend on the data.
+template <bool BF16>
+__global__ __launch_bounds__(64) void up_rows_var_kernel(const void *__restrict__ wuv,
+                                                         const void *__restrict__ xv,
+                                                         RouteView rv, int H, int d_ff,
+                                                         const int32_t *__restrict__ counts,
+                                                         const int32_t *__restrict__ idx,
+                                                         float *__restrict__ coef) {
+  const int p = blockIdx.x;
+  int n = counts[p];
+  n = n < 0 ? 0 : (n > d_ff ? d_ff : n);
+  for (int i0 = blockIdx.y * kUpRows; i0 < n; i0 += gridDim.y * kUpRows)
+    up_rows_group<BF16>(wuv, xv, rv, H, d_ff, p, i0, n, idx + (size_t)p * d_ff,
+                        coef + (size_t)p * d_ff);
 }
 
 // ---------------------------------------------------------------- sparse down
@@ -1612,28 +1642,10 @@ bool threshold_supported(int d_ff) {
   return d_ff % 512 == 0 && d_ff <= 8192;
 }
 
-// The page's literal masking: gate/up, one compare pass against tau[e],
-// then the variable-count sparse down projection.
-hipError_t launch_ffn_threshold(const FfnArgs &a, const float *tau, int32_t *counts,
-                                bool want_counts, bool want_idx, hipStream_t stream) {
-  if (a.T == 0) return hipSuccess;
-  const RouteView rv = make_view(a);
-  launch_gateup(a, rv, stream);
-  if (a.T <= 16) {  // decode batches: the compare runs inside the down kernel
-    const int sw = down_block_cols(a.T, a.H);
-    dim3 grid(a.T, a.H / sw);
-    int32_t *co = want_counts ? counts : nullptr;
-    int32_t *io = want_idx ? a.idx : nullptr;
-    timer_begin(kStageDownRows, stream);
-#define MOE_DT(BF, SWV)                                                                         \
-  down_thr_token_kernel<BF, SWV><<<grid, 1024, 0, stream>>>(a.w_down, a.h, tau, rv, a.H, a.d_ff, \
-                                                            a.accumulate, a.y, co, io)
-    if (a.bf16) { if (sw == 128) MOE_DT(true, 128); else MOE_DT(true, 64); }
-    else { if (sw == 128) MOE_DT(false, 128); else MOE_DT(false, 64); }
-#undef MOE_DT
-    timer_end(stream);
-    return hipGetLastError();
-  }
+// The one-pass threshold mask over the scores in a.h: kept ids and w * score
+// at row stride d_ff, and a count per pair.
+static hipError_t launch_threshold_mask(const FfnArgs &a, const RouteView &rv, const float *tau,
+                                        int32_t *counts, hipStream_t stream) {
   const int P = a.T * a.top_k;
   timer_begin(kStageMask, stream);
   switch (a.d_ff) {
@@ -1659,6 +1671,12 @@ hipError_t launch_ffn_threshold(const FfnArgs &a, const float *tau, int32_t *cou
       return hipErrorInvalidValue;  // excluded by threshold_supported()
   }
   timer_end(stream);
+  return hipSuccess;
+}
+
+// The variable-count sparse down projection over a threshold mask's lists.
+static void launch_down_var(const FfnArgs &a, const RouteView &rv, const int32_t *counts,
+                            hipStream_t stream) {
   const int sw = down_block_cols(a.T, a.H);
   dim3 grid(a.T, a.H / sw);
   timer_begin(kStageDownRows, stream);
@@ -1669,16 +1687,71 @@ hipError_t launch_ffn_threshold(const FfnArgs &a, const float *tau, int32_t *cou
   else { if (sw == 128) MOE_DV(false, 128); else MOE_DV(false, 64); }
 #undef MOE_DV
   timer_end(stream);
-  return hipGetLastError();
 }
 
-// Calibration: gate/up on the calibration tokens, then the per-expert
-// order statistic (and the layer-wide one for experts without tokens).
-hipError_t launch_calibrate(const FfnArgs &a, double sparsity, float *tau, float *tau_all,
-                            hipStream_t stream) {
+// The page's literal masking: gate/up, one compare pass against tau[e],
+// then the variable-count sparse down projection.
+hipError_t launch_ffn_threshold(const FfnArgs &a, const float *tau, int32_t *counts,
+                                bool want_counts, bool want_idx, hipStream_t stream) {
   if (a.T == 0) return hipSuccess;
   const RouteView rv = make_view(a);
   launch_gateup(a, rv, stream);
+  if (a.T <= 16) {  // decode batches: the compare runs inside the down kernel
+    const int sw = down_block_cols(a.T, a.H);
+    dim3 grid(a.T, a.H / sw);
+    int32_t *co = want_counts ? counts : nullptr;
+    int32_t *io = want_idx ? a.idx : nullptr;
+    timer_begin(kStageDownRows, stream);
+#define MOE_DT(BF, SWV)                                                                         \
+  down_thr_token_kernel<BF, SWV><<<grid, 1024, 0, stream>>>(a.w_down, a.h, tau, rv, a.H, a.d_ff, \
+                                                            a.accumulate, a.y, co, io)
+    if (a.bf16) { if (sw == 128) MOE_DT(true, 128); else MOE_DT(true, 64); }
+    else { if (sw == 128) MOE_DT(false, 128); else MOE_DT(false, 64); }
+#undef MOE_DT
+    timer_end(stream);
+    return hipGetLastError();
+  }
+  const hipError_t e = launch_threshold_mask(a, rv, tau, counts, stream);
+  if (e != hipSuccess) return e;
+  launch_down_var(a, rv, counts, stream);
+  return hipGetLastError();
+}
+
+// The page's own pipeline with its threshold mask: dense gate scores
+// silu(W_g x), one compare pass against tau[e], then the up and down
+// projections over the kept rows only (w_up row-major).
+hipError_t launch_ffn_updown_threshold(const FfnArgs &a, const float *tau, int32_t *counts,
+                                       hipStream_t stream) {
+  if (a.T == 0) return hipSuccess;
+  const RouteView rv = make_view(a);
+  launch_gateup(a, rv, stream, true);
+  const hipError_t e = launch_threshold_mask(a, rv, tau, counts, stream);
+  if (e != hipSuccess) return e;
+  const int P = a.T * a.top_k;
+  const int groups = (a.d_ff + kUpRows - 1) / kUpRows;
+  int G = (2048 + P - 1) / P;  // about 2048 one-wave blocks in all
+  G = G < 1 ? 1 : (G > groups ? groups : G);
+  dim3 grid(P, G);
+  timer_begin(kStageUpRows, stream);
+  if (a.bf16)
+    up_rows_var_kernel<true><<<grid, 64, 0, stream>>>(a.w_up, a.x, rv, a.H, a.d_ff, counts, a.idx,
+                                                      a.hact);
+  else
+    up_rows_var_kernel<false><<<grid, 64, 0, stream>>>(a.w_up, a.x, rv, a.H, a.d_ff, counts, a.idx,
+                                                       a.hact);
+  timer_end(stream);
+  launch_down_var(a, rv, counts, stream);
+  return hipGetLastError();
+}
+
+// Calibration: gate/up (or the gate alone, for the split's scores) on the
+// calibration tokens, then the per-expert order statistic (and the
+// layer-wide one for experts without tokens).
+hipError_t launch_calibrate(const FfnArgs &a, double sparsity, float *tau, float *tau_all,
+                            bool gate_only, hipStream_t stream) {
+  if (a.T == 0) return hipSuccess;
+  const RouteView rv = make_view(a);
+  launch_gateup(a, rv, stream, gate_only);
   calibrate_kernel<<<a.E + 1, 1024, 0, stream>>>(a.h, rv, a.d_ff, sparsity, tau, tau_all);
   calibrate_fill_kernel<<<1, 64, 0, stream>>>(rv, tau_all, tau);
   return hipGetLastError();

@@ -92,6 +92,8 @@ bool threshold_supported(int d_ff);
 hipError_t launch_ffn_threshold(const FfnArgs &a, const float *tau, int32_t *counts,
                                 bool want_counts, bool want_idx, hipStream_t stream);
 hipError_t launch_calibrate(const FfnArgs &a, double sparsity, float *tau, float *tau_all,
-                            hipStream_t stream);
+                            bool gate_only, hipStream_t stream);
+hipError_t launch_ffn_updown_threshold(const FfnArgs &a, const float *tau, int32_t *counts,
+                                       hipStream_t stream);
 
 }  // namespace moe

@@ -134,8 +134,10 @@ class DeviceLayer:
         cnt = torch.full((P,), -1, dtype=torch.int32, device="cuda")
         ws = torch.empty(B.moe_ffn_threshold_workspace_size(self.desc, T), dtype=torch.uint8,
                          device="cuda")
-        B.moe_expert_ffn_sparse_threshold(self.desc, T, tau, x, *self.w, R, y, 0,
-                                          cnt if outputs else None, idx if outputs else None, ws)
+        fn = (B.moe_expert_ffn_sparse_updown_threshold if self.score == "gate"
+              else B.moe_expert_ffn_sparse_threshold)
+        fn(self.desc, T, tau, x, *self.w, R, y, 0, cnt if outputs else None,
+           idx if outputs else None, ws)
         out = dict(T=T)
         if self.desc_sh is not None:
             ds = self.desc_sh
@@ -143,7 +145,7 @@ class DeviceLayer:
             cnt_sh = torch.full((T * ds.top_k,), -1, dtype=torch.int32, device="cuda")
             ws2 = torch.empty(B.moe_ffn_threshold_workspace_size(ds, T), dtype=torch.uint8,
                               device="cuda")
-            B.moe_expert_ffn_sparse_threshold(ds, T, tau_sh, x, *self.w_sh, None, y, 1, cnt_sh,
+            fn(ds, T, tau_sh, x, *self.w_sh, None, y, 1, cnt_sh,
                                               idx_sh, ws2)
             torch.cuda.synchronize()
             out.update(idx_sh=idx_sh.cpu().numpy(), cnt_sh=cnt_sh.cpu().numpy())
@@ -175,7 +177,10 @@ class DeviceLayer:
             B.moe_route(desc, T, x, self.w_router, self.bias, R, ws_r)
         tau = torch.full((desc.n_experts,), float("nan"), dtype=torch.float32, device="cuda")
         ws = torch.empty(B.moe_calibrate_workspace_size(desc, T), dtype=torch.uint8, device="cuda")
-        B.moe_calibrate_thresholds(desc, T, x, w[0], w[1], R, sparsity, tau, ws)
+        if self.score == "gate":
+            B.moe_calibrate_thresholds_gate(desc, T, x, w[0], R, sparsity, tau, ws)
+        else:
+            B.moe_calibrate_thresholds(desc, T, x, w[0], w[1], R, sparsity, tau, ws)
         torch.cuda.synchronize()
         return tau.cpu().numpy()
 
@@ -304,9 +309,10 @@ def check_threshold_selection(got, scores, tau, what):
     return bool(diff)
 
 
-def compare_threshold_layer(inp: LayerInputs, x_host, got, tau, tau_sh=None, tokens=None):
+def compare_threshold_layer(inp: LayerInputs, x_host, got, tau, tau_sh=None, tokens=None,
+                            score="swiglu"):
     """Check a threshold-masked GPU layer against the oracle given the same
-    (float32) thresholds; returns the rel L2 error."""
+    (float32) thresholds and mask score; returns the rel L2 error."""
     sh = inp.shape
     T = x_host.shape[0]
     tokens = np.arange(T) if tokens is None else np.asarray(tokens)
@@ -314,7 +320,7 @@ def compare_threshold_layer(inp: LayerInputs, x_host, got, tau, tau_sh=None, tok
     tau64 = np.asarray(tau, dtype=np.float64)
     tsh64 = None if tau_sh is None else np.asarray(tau_sh, dtype=np.float64)
     kw = dict(top_k=sh.top_k, norm_topk=sh.norm_topk, k_keep=0, dtype=sh.dtype,
-              shared=inp.shared, thresholds=tau64, thresholds_shared=tsh64)
+              shared=inp.shared, thresholds=tau64, thresholds_shared=tsh64, score=score)
     ids_g = got["ids"][tokens]
     check_routing(inp, xs, ids_g, tokens)
     r1 = oracle.moe_layer(xs, inp.w_router, inp.bias, inp.wg, inp.wu, inp.wd,

@@ -168,6 +168,21 @@ def test_threshold_and_calibration_validation():
     assert C(d, wsb=B.moe_calibrate_workspace_size(d, 4) - 1) == WSP
     assert C(_desc(d_ff=2112)) == UNS
     assert B.moe_calibrate_workspace_size(_desc(hidden=100), 4) == 0
+    # the split with thresholds, and calibration on the gate scores (no w_up)
+    U = lambda dd, tau=FAKE, wu=FAKE, wsb=ws: L.moe_expert_ffn_sparse_updown_threshold(
+        ctypes.byref(dd), 4, tau, FAKE, FAKE, wu, FAKE, ctypes.byref(r), FAKE, 0, None, None,
+        FAKE, wsb, None)
+    assert U(d, tau=None) == INV
+    assert U(d, tau=FAKE + 2) == MISA
+    assert U(d, wu=None) == INV
+    assert U(d, wsb=ws - 1) == WSP
+    assert U(_desc(d_ff=2112)) == UNS
+    CG = lambda dd, s=0.9, tau=FAKE, wsb=1 << 34: L.moe_calibrate_thresholds_gate(
+        ctypes.byref(dd), 4, FAKE, FAKE, ctypes.byref(r), s, tau, FAKE, wsb, None)
+    assert CG(d, s=-0.1) == INV
+    assert CG(d, tau=None) == INV
+    assert CG(d, wsb=B.moe_calibrate_workspace_size(d, 4) - 1) == WSP
+    assert CG(_desc(d_ff=2112)) == UNS
 
 
 def test_pack_validation():

@@ -181,6 +181,60 @@ def test_threshold_calibration_and_masking(name, T_cal, T, s):
     say(f"   rel_l2={err:.3e} mean kept {got['cnt'].mean():.1f}")
 
 
+# the page's own pipeline: dense gate scores, threshold mask, sparse up + down
+THRESH_SPLIT = [("tiny-f32", 8, 4, 0.9), ("olmoe-like", 32, 16, 0.9), ("olmoe-like", 32, 1, 0.5),
+                ("olmoe-like", 32, 33, 0.7), ("qwen3-moe-like", 64, 8, 0.9),
+                ("deepseek-v2-like", 8, 4, 0.9), ("llama4-like", 4, 2, 0.9)]
+
+
+@pytest.mark.parametrize("name,T_cal,T,s", THRESH_SPLIT)
+def test_split_threshold_calibration_and_masking(name, T_cal, T, s):
+    inp, dev = layer(name, "gate")
+    sh = inp.shape
+    x_cal = inp.tokens(T_cal, 25)
+    say(f"[case] split threshold {name} T_cal={T_cal} T={T} s={s}")
+    tau = dev.calibrate(x_cal, s)
+    tau_sh = dev.calibrate(x_cal, s, shared=True) if sh.n_shared else None
+    ids_cal = dev.route_ids(x_cal)
+    check_routing(inp, x_cal, ids_cal)
+    t_or, t_or_sh = O.calibrate_thresholds(x_cal, inp.w_router, inp.bias, inp.wg, inp.wu,
+                                           top_k=sh.top_k, norm_topk=sh.norm_topk,
+                                           dtype=sh.dtype, sparsity=s, shared=inp.shared,
+                                           score="gate", forced_ids=ids_cal)
+    np.testing.assert_allclose(tau, t_or, rtol=1e-4, atol=1e-7)
+    if tau_sh is not None:
+        np.testing.assert_allclose(tau_sh, t_or_sh, rtol=1e-4, atol=1e-7)
+    x = inp.tokens(T, 26)
+    got = dev.run_threshold(x, torch.from_numpy(tau).cuda(),
+                            torch.from_numpy(tau_sh).cuda() if tau_sh is not None else None)
+    err = compare_threshold_layer(inp, x, got, tau, tau_sh, tokens=_sample(T, 6), score="gate")
+    say(f"   rel_l2={err:.3e} mean kept {got['cnt'].mean():.1f}")
+
+
+def test_split_threshold_reads_only_kept_rows():
+    # NaN in every W_u and W_d row no pair keeps under the threshold: same bits
+    inp, dev = layer("olmoe-like", "gate")
+    x = inp.tokens(4, 27)
+    tau = torch.full((64,), 0.02, device="cuda")
+    say("[case] split threshold, NaN-poisoned unkept rows")
+    a = dev.run_threshold(x, tau)
+    keep = np.zeros((64, 1024), dtype=bool)
+    for p, e in enumerate(a["ids"].reshape(-1)):
+        keep[e, a["idx"][p, :a["cnt"][p]]] = True
+    poison = torch.from_numpy(~keep).cuda()
+    w_saved = dev.w
+    wu, wd = dev.w[1].clone(), dev.w[2].clone()
+    wu[poison] = float("nan")
+    wd[poison] = float("nan")
+    try:
+        dev.w = (dev.w[0], wu, wd)
+        c = dev.run_threshold(x, tau)
+    finally:
+        dev.w = w_saved
+    assert np.all(np.isfinite(c["y"]))
+    np.testing.assert_array_equal(a["y"], c["y"])
+
+
 def test_threshold_extremes_and_calibration_target():
     inp, dev = layer("olmoe-like")
     x = inp.tokens(16, 23)
