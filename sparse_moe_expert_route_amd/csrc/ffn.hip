@@ -1,12 +1,20 @@
 // Expert FFN kernels of the intra-expert-sparse MoE layer (gfx950).
 //
-//   gateup_swiglu   h = silu(W_g x) * (W_u x), dense, MFMA, per (expert, <=64 tokens)
+//   gateup_swiglu   h = silu(W_g x) * (W_u x), dense, MFMA, per active-expert
+//                   slot (T <= 16); gateup_gemm, the grouped GEMM past that
 //   neuron_topk     exact top-k of |h| per pair (radix select + one threshold pass),
 //                   compacted ascending kept-neuron list, weights folded in
-//   down_rows       y_p = sum over kept rows j of hact_j * W_d[j, :], streaming
-//                   only those rows (the sparse down projection)
+//   down_token      y_t = sum over the token's pairs and kept rows j of
+//                   hact_j * W_d[j, :], streaming only those rows (the sparse
+//                   down projection, with the combine in a fixed order)
 //   down_dense      dense-path down GEMM (MFMA) over every row of W_d
 //   combine         y[t] (+)= sum of a token's partials in fixed order
+//   up_rows         the split's sparse up projection: u_j = W_u[j] . x for
+//                   kept j only (gate-only scores from gateup_swiglu)
+//   neuron_threshold / down_var_token / down_thr_token
+//                   threshold masking (a kept count per pair) and the down
+//                   projection over variable-length lists; calibrate_kernel
+//                   sets the per-expert thresholds offline
 //
 // Method: the page "Uncovering Intra-expert Activation Sparsity for
 // Efficient Mixture-of-Expert Model Execution", technical summary,
