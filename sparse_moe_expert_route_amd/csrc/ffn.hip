@@ -320,29 +320,40 @@ __global__ __launch_bounds__(256, 2) void gateup_gemm_kernel(const void *__restr
           if (!GO) nu[j][k] = ld16_nt(wu + j * tstride + (size_t)(2 * it + 2 + k) * 1024);
         }
     }
+    auto bfrag = [&](int k, int tl) {
+      return *reinterpret_cast<const u32x4 *>(
+          &xs[cur][(tl * 16 + r) * kGemmRowB + k * 64 + g * 16]);
+    };
+    auto tile = [&](int k, int tl, const u32x4 &b) {
+#pragma unroll
+      for (int j = 0; j < NTW; ++j) {
+        if (BF16) {
+          accg[j][tl] = mfma_bf16(ag[j][k], b, accg[j][tl]);
+          if (!GO) accu[j][tl] = mfma_bf16(au[j][k], b, accu[j][tl]);
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            accg[j][tl] = mfma_f32(__uint_as_float(ag[j][k][q]), __uint_as_float(b[q]),
+                                   accg[j][tl]);
+            if (!GO)
+              accu[j][tl] = mfma_f32(__uint_as_float(au[j][k][q]), __uint_as_float(b[q]),
+                                     accu[j][tl]);
+          }
+        }
+      }
+    };
+    // Each token fragment is read from LDS one tile ahead of its MFMAs, so
+    // the LDS latency overlaps the matrix work instead of stalling it (rows
+    // past the item's tokens hold zeros, so the read ahead is harmless).
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
+      u32x4 b = bfrag(k, 0);
 #pragma unroll
       for (int tl = 0; tl < 8; ++tl) {
-        if (tl < ntiles) {
-          const u32x4 b = *reinterpret_cast<const u32x4 *>(
-              &xs[cur][(tl * 16 + r) * kGemmRowB + k * 64 + g * 16]);
-#pragma unroll
-          for (int j = 0; j < NTW; ++j) {
-            if (BF16) {
-              accg[j][tl] = mfma_bf16(ag[j][k], b, accg[j][tl]);
-              if (!GO) accu[j][tl] = mfma_bf16(au[j][k], b, accu[j][tl]);
-            } else {
-#pragma unroll
-              for (int q = 0; q < 4; ++q) {
-                accg[j][tl] = mfma_f32(__uint_as_float(ag[j][k][q]), __uint_as_float(b[q]),
-                                       accg[j][tl]);
-                if (!GO)
-                  accu[j][tl] = mfma_f32(__uint_as_float(au[j][k][q]), __uint_as_float(b[q]),
-                                         accu[j][tl]);
-              }
-            }
-          }
+        if (tl < ntiles) {  // block-uniform
+          const u32x4 bn = bfrag(k, tl < 7 ? tl + 1 : 7);
+          tile(k, tl, b);
+          b = bn;
         }
       }
     }
@@ -1388,14 +1399,20 @@ __global__ __launch_bounds__(256, 2) void down_dense_gemm_kernel(const uint16_t 
         const int w0 = (ks * 16 + 4 * g) ^ dn_swz(col);  // 4 k-pairs = this lane's 8 k
         b[j] = *reinterpret_cast<const u32x4 *>(&bs[cur][col * (kDnBrow / 4) + w0]);
       }
+      auto afrag = [&](int i) {
+        return *reinterpret_cast<const u32x4 *>(
+            &as[cur][((4 * wt + i) * 16 + r) * kDnArow + ks * 64 + g * 16]);
+      };
+      // A fragments read one tile ahead of their MFMAs (rows past the
+      // item's tokens hold zeros, so the read ahead is harmless)
+      u32x4 av = afrag(0);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int tl = 4 * wt + i;
-        if (tl < ntiles) {
-          const u32x4 av = *reinterpret_cast<const u32x4 *>(
-              &as[cur][(tl * 16 + r) * kDnArow + ks * 64 + g * 16]);
+        if (4 * wt + i < ntiles) {  // wave-uniform
+          const u32x4 an = afrag(i < 3 ? i + 1 : 3);
           acc[i][0] = mfma_bf16(av, b[0], acc[i][0]);
           acc[i][1] = mfma_bf16(av, b[1], acc[i][1]);
+          av = an;
         }
       }
     }
