@@ -220,6 +220,7 @@ moe_status run_ffn(RunMode mode, const moe_desc *d, int32_t T, int32_t k_keep, c
   a.y = y;
   a.h = reinterpret_cast<float *>(ws + L.h);
   a.idx = active_idx_out ? active_idx_out : reinterpret_cast<int32_t *>(ws + L.idx);
+  a.want_idx = active_idx_out != nullptr;
   a.hact = path == MOE_PATH_SPARSE ? reinterpret_cast<float *>(ws + L.hact) : nullptr;
   a.partial = reinterpret_cast<float *>(ws + L.partial);
   a.hm = path == MOE_PATH_DENSE ? static_cast<void *>(ws + L.hm) : nullptr;

@@ -1048,6 +1048,171 @@ __global__ __launch_bounds__(1024) void down_var_token_kernel(const void *__rest
   }
 }
 
+// ---------------------------------------------------------------- fused top-k mask + down
+// The smallest batches: each down block selects its own token's kept neurons, one
+// wave per pair (exact top-k of |h|: the radix select of
+// neuron_topk_seg_kernel with NW = 1, V = d_ff / 64 values per lane, its own
+// LDS histogram, no block barriers), and writes the kept rows straight into
+// the LDS row list at the pair's fixed offset s * k.  The mask kernel and
+// its launch go away; the select is repeated by the token's H / SW blocks,
+// which costs a read of the token's activations from the caches each.
+// Blocks of column chunk 0 also write the kept ids (the caller's
+// active_idx_out) if asked.  Requires top_k <= 16, 0 < k < d_ff and
+// top_k * k <= kDownStage.
+template <bool BF16, int SW, int V>
+__global__ __launch_bounds__(1024) void down_topk_token_kernel(
+    const void *__restrict__ wdv, const float *__restrict__ h, RouteView rv, int H, int d_ff,
+    int k, int accumulate, float *__restrict__ y, int32_t *__restrict__ idx_out) {
+  constexpr int VEC = BF16 ? 8 : 4;
+  constexpr int LPR = SW / VEC;
+  constexpr int RPI = 64 / LPR;
+  __shared__ float red[kDownWaves][SW];
+  __shared__ uint32_t srow[kDownStage];
+  __shared__ float scoef[kDownStage];
+  __shared__ int hist[kDownWaves][256];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int t = blockIdx.x, col0 = blockIdx.y * SW;
+  const int top_k = rv.top_k;
+  if (wid < top_k) {  // wave-uniform: this wave selects slot wid's neurons
+    const int p = t * top_k + wid;
+    const float w = rv.weight(p);
+    const uint32_t rbase = (uint32_t)rv.expert_of_pair(p) * (uint32_t)d_ff;
+    const int seg = lane * V;
+    const float *hp = h + (size_t)p * d_ff + seg;
+    uint32_t bits[V];
+#pragma unroll
+    for (int i = 0; i < V; i += 4) {
+      const u32x4 q = ld16(hp + i);
+      bits[i] = q[0]; bits[i + 1] = q[1]; bits[i + 2] = q[2]; bits[i + 3] = q[3];
+    }
+    uint32_t tau = 0, pmask = 0;
+    int krem = k;
+    bool whole = false;
+    int *hw = hist[wid];
+#pragma unroll
+    for (int pass = 0; pass < 4; ++pass) {
+      if (whole) continue;  // wave-uniform
+      const int shift = pass == 0 ? 23 : pass == 1 ? 15 : pass == 2 ? 7 : 0;
+      const uint32_t dmask = pass == 3 ? 0x7fu : 0xffu;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) hw[lane * 4 + b] = 0;
+#pragma unroll
+      for (int i = 0; i < V; ++i) {
+        const uint32_t key = bits[i] & 0x7fffffffu;
+        if ((key & pmask) == tau) atomicAdd(&hw[(key >> shift) & dmask], 1);
+      }
+      // lane owns digits 255 - 4 lane - b, b = 0..3 (descending)
+      int c[4], local = 0;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        c[b] = hw[255 - 4 * lane - b];
+        local += c[b];
+      }
+      int run = wave_incl_scan(local) - local;
+      int dsel = -1, knew = 0, csel = 0;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        if (dsel < 0 && run + c[b] >= krem && run < krem) {
+          dsel = 255 - 4 * lane - b;
+          knew = krem - run;
+          csel = c[b];
+        }
+        run += c[b];
+      }
+      const uint64_t m = __ballot(dsel >= 0);
+      const int L = __ffsll((unsigned long long)m) - 1;  // exactly one lane (counts are exact)
+      dsel = lane_value(dsel, L);
+      knew = lane_value(knew, L);
+      csel = lane_value(csel, L);
+      tau |= (uint32_t)dsel << shift;
+      pmask |= dmask << shift;
+      krem = knew;
+      whole = csel == knew && tau != 0u;
+    }
+    if (whole) {  // keep key >= tau: key > tau - 1, no equal ones
+      tau -= 1u;
+      krem = 0;
+    }
+    int ngt = 0, neq = 0;
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      const uint32_t key = bits[i] & 0x7fffffffu;
+      ngt += key > tau;
+      neq += key == tau;
+    }
+    const int eq_before = wave_incl_scan(neq) - neq;
+    int pos = wave_incl_scan(ngt) - ngt + min(eq_before, krem);
+    int eq_seen = eq_before;
+    const int obase = wid * k;
+    int32_t *io = (idx_out && blockIdx.y == 0) ? idx_out + (size_t)p * k : nullptr;
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      const uint32_t key = bits[i] & 0x7fffffffu;
+      const bool keep = key > tau || (key == tau && eq_seen++ < krem);
+      if (keep) {
+        srow[obase + pos] = rbase + (uint32_t)(seg + i);
+        scoef[obase + pos] = w * __uint_as_float(bits[i]);
+        if (io) io[pos] = seg + i;
+        ++pos;
+      }
+    }
+  }
+  __syncthreads();
+  const int nr = top_k * k;
+  const int sub = lane % LPR, rsel = lane / LPR;
+  const size_t colo = (size_t)col0 + sub * VEC;
+  float acc[VEC];
+#pragma unroll
+  for (int v = 0; v < VEC; ++v) acc[v] = 0.f;
+  constexpr int U = 4;
+  for (int b0 = wid; b0 * RPI < nr; b0 += kDownWaves * U) {
+    u32x4 qv[U];
+    float cf[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int qq = (b0 + kDownWaves * u) * RPI + rsel;
+      cf[u] = 0.f;
+      qv[u] = u32x4{0, 0, 0, 0};
+      if (qq < nr) {
+        const size_t off = (size_t)srow[qq] * H + colo;
+        cf[u] = scoef[qq];
+        qv[u] = BF16 ? ld16(static_cast<const uint16_t *>(wdv) + off)
+                     : ld16(static_cast<const float *>(wdv) + off);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (BF16) {
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          acc[2 * jj] = fmaf(cf[u], bf16lo(qv[u][jj]), acc[2 * jj]);
+          acc[2 * jj + 1] = fmaf(cf[u], bf16hi(qv[u][jj]), acc[2 * jj + 1]);
+        }
+      } else {
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) acc[jj] = fmaf(cf[u], __uint_as_float(qv[u][jj]), acc[jj]);
+      }
+    }
+  }
+#pragma unroll
+  for (int o = LPR; o < 64; o <<= 1) {
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) acc[v] += __shfl_xor(acc[v], o, 64);
+  }
+  if (rsel == 0) {
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) red[wid][sub * VEC + v] = acc[v];
+  }
+  __syncthreads();
+  if (tid < SW) {
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < kDownWaves; ++w) v += red[w][tid];
+    float *yp = y + (size_t)t * H + col0 + tid;
+    *yp = accumulate ? *yp + v : v;
+  }
+}
+
 // ---------------------------------------------------------------- fused threshold mask + down
 // Decode batches: the threshold compare is one cheap pass, so each down
 // block redoes it for its token instead of reading a mask kernel's output,
@@ -1628,11 +1793,48 @@ static void launch_down_token(const FfnArgs &a, const RouteView &rv, const int32
   timer_end(stream);
 }
 
+// Whether the kernel that selects inside the down projection takes this
+// call: the smallest batches (at T = 16 the repeated selects cost as much as
+// the mask launch they save), one wave per pair, d_ff / 64 values per lane
+// (a multiple of 4 up to 32), the token's kept lists in one LDS stage.
+constexpr int kFusedTopkMaxTokens = 4;
+static bool fused_topk_ok(const FfnArgs &a) {
+  const int V = a.d_ff / 64;
+  return a.T <= kFusedTopkMaxTokens && a.top_k <= kDownWaves && a.d_ff % 256 == 0 && V <= 32 &&
+         a.k_keep > 0 && a.k_keep < a.d_ff && a.top_k * a.k_keep <= kDownStage;
+}
+
 hipError_t launch_ffn_sparse(const FfnArgs &a, hipStream_t stream) {
   if (a.T == 0) return hipSuccess;
   if (zero_contribution(a, stream)) return hipGetLastError();
   const RouteView rv = make_view(a);
   launch_gateup(a, rv, stream);
+  if (fused_topk_ok(a)) {
+    const int sw = down_block_cols(a.T, a.H);
+    dim3 grid(a.T, a.H / sw);
+    int32_t *io = a.want_idx ? a.idx : nullptr;
+    timer_begin(kStageDownRows, stream);
+#define MOE_DK(BF, SWV, VV)                                                                   \
+  down_topk_token_kernel<BF, SWV, VV><<<grid, 1024, 0, stream>>>(a.w_down, a.h, rv, a.H, a.d_ff, \
+                                                                 a.k_keep, a.accumulate, a.y, io)
+#define MOE_DK_V(BF, SWV)                                                                     \
+  switch (a.d_ff / 64) {                                                                      \
+    case 4: MOE_DK(BF, SWV, 4); break;                                                        \
+    case 8: MOE_DK(BF, SWV, 8); break;                                                        \
+    case 12: MOE_DK(BF, SWV, 12); break;                                                      \
+    case 16: MOE_DK(BF, SWV, 16); break;                                                      \
+    case 20: MOE_DK(BF, SWV, 20); break;                                                      \
+    case 24: MOE_DK(BF, SWV, 24); break;                                                      \
+    case 28: MOE_DK(BF, SWV, 28); break;                                                      \
+    default: MOE_DK(BF, SWV, 32); break;                                                      \
+  }
+    if (a.bf16) { if (sw == 128) { MOE_DK_V(true, 128) } else { MOE_DK_V(true, 64) } }
+    else { if (sw == 128) { MOE_DK_V(false, 128) } else { MOE_DK_V(false, 64) } }
+#undef MOE_DK_V
+#undef MOE_DK
+    timer_end(stream);
+    return hipGetLastError();
+  }
   launch_mask(a, rv, a.idx, a.hact, nullptr, 0, stream);
   launch_down_token(a, rv, a.idx, a.hact, a.k_keep, stream);
   return hipGetLastError();

@@ -71,6 +71,7 @@ struct FfnArgs {
   // workspace carve-up
   float *h;          // [P, d_ff] fp32
   int32_t *idx;      // [P, k_keep]
+  int want_idx;      // idx is the caller's active_idx_out (must be written)
   float *hact;       // [P, k_keep]   w * h at the kept neurons
   float *partial;    // dense bf16 path: [P, H] per-pair down outputs
   void *hm;          // dense path: [P, d_ff] masked, weighted h (bf16 or fp32)
