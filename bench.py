@@ -483,9 +483,10 @@ class HostLayer:
         return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
-def measure(shape, host, dev_w0, T, args, path=None, dev_sh0=None, score="swiglu"):
-    wl = Workload(shape, host, dev_w0, T, args.sparsity, path or args.path, dev_sh0=dev_sh0,
-                  score=score)
+def measure(shape, host, dev_w0, T, args, path=None, dev_sh0=None, score="swiglu",
+            sparsity=None):
+    wl = Workload(shape, host, dev_w0, T, args.sparsity if sparsity is None else sparsity,
+                  path or args.path, dev_sh0=dev_sh0, score=score)
     log(f"[bench] {shape.name} T={T} k={wl.k} path={'sparse' if wl.path == 0 else 'dense'} "
         f"copies={wl.L}")
     wl.capture()
@@ -778,6 +779,20 @@ def main():
                 del wl
                 torch.cuda.empty_cache()
         del dev_gate
+    # the layer across the sparsity sweep of this workload (s = 0 is the
+    # unmasked dense SwiGLU MoE, which the dispatcher sends to the dense path)
+    sweep_s = {}
+    if not args.no_variant:
+        for s in (0.0, 0.5, 0.75):
+            for T in (1, args.batch):
+                wl, res = measure(shape, host, dev_w0, T, args, sparsity=s)
+                sweep_s[f"s={s},T={T}"] = {"k": res["k"], "path": res["path"],
+                                           "us_per_call": round(res["us_per_call"], 3),
+                                           "us_per_token": round(res["us_per_token"], 3)}
+                log(f"[bench] sparsity {s} T={T}: k={res['k']} {res['path']}, "
+                    f"{res['us_per_call']:.1f} us/call")
+                del wl
+                torch.cuda.empty_cache()
     roster = step = None
     if not args.no_variant:
         roster = roster_variant(shape, host, dev_w0)
@@ -829,6 +844,7 @@ def main():
             "what": "the page's pipeline: dense gate scores, keep |silu(g)| > tau[e] (calibrated "
                     f"on the gate scores, sparsity {args.sparsity}), up and down on the kept rows",
             "batches": variants["updown_threshold"]} if variants["updown_threshold"] else None,
+        "sparsity_sweep": sweep_s or None,
         "roster_variant": roster,
         "decode_step_variant": step,
         "cpu_baseline": cpu,
