@@ -460,3 +460,79 @@ def test_layer_class_matches_direct_calls():
     got = dev.run(x_host, k, SP, k_sh, SP)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(y.cpu().numpy(), got["y"])
+
+
+# ------------------------------------------------------------------ canaries
+
+def _pad(dtype):  # 256 bytes of canary before and after every buffer
+    return 256 // torch.empty((), dtype=dtype).element_size()
+
+
+def _canaried(n, dtype, fill):
+    pad = _pad(dtype)
+    full = torch.full((n + 2 * pad,), fill, dtype=dtype, device="cuda")
+    return full, full[pad:pad + n]
+
+
+def _intact(full, n, fill, what):
+    torch.cuda.synchronize()
+    pad = _pad(full.dtype)
+    head, tail = full[:pad], full[pad + n:]
+    assert torch.all(head == fill) and torch.all(tail == fill), f"{what}: canary overwritten"
+
+
+@pytest.mark.parametrize("T", [1, 4, 16, 40])
+def test_no_write_outside_any_buffer(T):
+    # every entry point, on buffers sized exactly as the header states, with
+    # canaries around each output and workspace
+    inp, dev = layer("olmoe-like")
+    inp_g, dev_g = layer("olmoe-like", "gate")
+    sh = inp.shape
+    E, K, H, d = sh.n_experts, sh.top_k, sh.hidden, sh.d_ff
+    P, k = T * K, O.keep_count(0.9, d)
+    say(f"[case] canaries T={T}")
+    x = to_dev(inp.tokens(T, 31))
+    bufs = []
+
+    def buf(n, dtype=torch.int32, fill=-7):
+        full, view = _canaried(n, dtype, fill)
+        bufs.append((full, n, fill, f"buffer {len(bufs)}"))
+        return view
+
+    def ws(nbytes):
+        return buf(nbytes, torch.uint8, 0x5A)
+
+    R = B.Routing(buf(P).view(T, K), buf(P, torch.float32, -7.0).view(T, K), buf(E + 1), buf(P),
+                  buf(E), buf(1))
+    B.moe_route(dev.desc, T, x, dev.w_router, None, R, ws(B.moe_route_workspace_size(dev.desc, T)))
+    usage = buf(T * E).view(T, E)
+    usage.zero_()
+    B.moe_route_roster(dev.desc, T, x, dev.w_router, None, usage, None, 8, 0.5, R,
+                       ws(B.moe_route_workspace_size(dev.desc, T)))
+    for path in (SP, DN):
+        fn = B.moe_expert_ffn_sparse if path == SP else B.moe_expert_ffn_dense
+        fn(dev.desc, T, k, x, *dev.w, R, buf(T * H, torch.float32, -7.0).view(T, H), 0,
+           buf(P * k).view(P, k), ws(B.moe_ffn_workspace_size(dev.desc, T, k, path)))
+    B.moe_expert_ffn_sparse_updown(dev_g.desc, T, k, x, *dev_g.w, R,
+                                   buf(T * H, torch.float32, -7.0).view(T, H), 0,
+                                   buf(P * k).view(P, k),
+                                   ws(B.moe_ffn_workspace_size(dev_g.desc, T, k, SP)))
+    tau = buf(E, torch.float32, -7.0)
+    B.moe_calibrate_thresholds(dev.desc, T, x, dev.w[0], dev.w[1], R, 0.9, tau,
+                               ws(B.moe_calibrate_workspace_size(dev.desc, T)))
+    B.moe_expert_ffn_sparse_threshold(dev.desc, T, tau, x, *dev.w, R,
+                                      buf(T * H, torch.float32, -7.0).view(T, H), 0, buf(P),
+                                      buf(P * d).view(P, d),
+                                      ws(B.moe_ffn_threshold_workspace_size(dev.desc, T)))
+    tau_g = buf(E, torch.float32, -7.0)
+    B.moe_calibrate_thresholds_gate(dev_g.desc, T, x, dev_g.w[0], R, 0.9, tau_g,
+                                    ws(B.moe_calibrate_workspace_size(dev_g.desc, T)))
+    B.moe_expert_ffn_sparse_updown_threshold(dev_g.desc, T, tau_g, x, *dev_g.w, R,
+                                             buf(T * H, torch.float32, -7.0).view(T, H), 0,
+                                             buf(P), buf(P * d).view(P, d),
+                                             ws(B.moe_ffn_threshold_workspace_size(dev_g.desc, T)))
+    y = buf(T * H, torch.float32, 0.0).view(T, H)
+    xo = buf(T * H // 2, torch.int32, -7).view(torch.bfloat16).view(T, H)
+    B.moe_residual_add(dev.desc, T, x, y, xo)
+    for full, n, fill, what in bufs:
+        _intact(full, n, fill, what)
