@@ -298,6 +298,33 @@ def time_kernels(wl, steps, chunk=10):
             for k, v in d.items()}
 
 
+def event_pair_overhead(reps=50, chunk=10):
+    """What an event pair adds, measured the way time_kernels measures:
+    pairs queued behind a GPU spin, around nothing and around a 16-byte
+    moe_stream_read (a kernel that does almost nothing)."""
+    import torch
+    from sparse_moe_expert_route_amd import binding as B
+    buf = torch.zeros(16, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(B.STREAM_READ_SINK_WORDS, dtype=torch.int32, device="cuda")
+    spin = getattr(torch.cuda, "_sleep", None)
+    out = {}
+    for name, work in (("empty_pair_us", lambda: None),
+                       ("tiny_kernel_pair_us", lambda: B.moe_stream_read(buf, sink))):
+        work()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        for c0 in range(0, reps, chunk):
+            if spin is not None:
+                spin(10_000_000)
+            for i in range(c0, min(reps, c0 + chunk)):
+                ev[i][0].record()
+                work()
+                ev[i][1].record()
+            torch.cuda.synchronize()
+        out[name] = round(sum(s.elapsed_time(e) for s, e in ev) * 1e3 / reps, 2)
+    return out
+
+
 def time_stages(fn, steps, chunk=10):
     """time_kernels for any callable that launches library kernels."""
     import torch
@@ -833,6 +860,7 @@ def main():
         "roofline_down": roofline(r, "down_rows", "down_bytes", practical,
                                   size_matched_read(r["down_bytes"])),
         "practical_read_peak": practical,
+        "event_overhead": event_pair_overhead(),
         "updown_variant": {"what": "the page's own split: dense gate scores |silu(W_g x)|, "
                                    "up and down gathered on the kept rows (a different mask)",
                            "batches": variants["updown"]} if variants["updown"] else None,
