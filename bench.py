@@ -477,21 +477,34 @@ def cpu_baseline(shape, host, wl, seconds):
         cores = max([i.get("num_threads", 1) for i in info] or [1])
     except Exception:  # pragma: no cover
         cores = 1
+    import numpy as np
     T = wl.T
+    wl.step(0)                           # the timed batch 0 once more, for the parity check
+    wl.torch.cuda.synchronize()
+    y_gpu = wl.y[0].cpu().numpy().astype(np.float64)
     done, t0 = 0, time.perf_counter()
+    y_first = None
     while True:
         x = wl.x_host[done % wl.L]
-        oracle.moe_layer(x, host.w_router, None, host.wg, host.wu, host.wd, top_k=shape.top_k,
-                         norm_topk=shape.norm_topk, k_keep=wl.k, dtype=shape.dtype, keep_h=False)
+        r = oracle.moe_layer(x, host.w_router, None, host.wg, host.wu, host.wd, top_k=shape.top_k,
+                             norm_topk=shape.norm_topk, k_keep=wl.k, dtype=shape.dtype,
+                             keep_h=False)
+        if y_first is None:
+            y_first = r.y
         done += 1
         el = time.perf_counter() - t0
         if el >= seconds or done >= 50:
             break
     us_per_token = el * 1e6 / (done * T)
+    # the oracle's own routing and masks, no forcing: a near-tie that breaks
+    # the other way would show here as a larger error (tests/ apply the
+    # window rule; this is a sanity gate on the timed workload)
+    rel = float(np.linalg.norm(y_gpu - y_first) / max(np.linalg.norm(y_first), 1e-300))
     return {"value": round(us_per_token, 1), "unit": "us/token", "cores": int(cores),
             "kind": "oracle",
             "sample": f"{done} layer calls of {T} tokens ({done * T} tokens) of the same layer, "
-                      f"{el:.1f} s, float64 numpy oracle"}
+                      f"{el:.1f} s, float64 numpy oracle",
+            "parity_rel_l2_batch0": float(f"{rel:.3e}")}
 
 
 class HostLayer:
