@@ -36,7 +36,7 @@ def flags() -> list:
         f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
         # packed fp32 VALU ops are kept out of every kernel
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-        "-Wall", "-Wno-unused-function",
+        "-Wall", "-Wextra", "-Wno-unused-function",
         "-I", INCLUDE, "-I", CSRC,
     ]
 

@@ -965,7 +965,7 @@ __global__ __launch_bounds__(1024) void down_var_token_kernel(const void *__rest
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int t = blockIdx.x, col0 = blockIdx.y * SW;
   const int top_k = rv.top_k;
-  if (threadIdx.x < top_k) {
+  if ((int)threadIdx.x < top_k) {
     const int c = counts[t * top_k + threadIdx.x];
     pref[threadIdx.x + 1] = c < 0 ? 0 : (c > d_ff ? d_ff : c);
   }
