@@ -549,6 +549,7 @@ def measure(shape, host, dev_w0, T, args, path=None, dev_sh0=None, score="swiglu
 
 
 KERNEL_SOURCES = ("sparse_moe_expert_route_amd/csrc/ffn.hip",
+                  "sparse_moe_expert_route_amd/csrc/ffn_common.h",
                   "sparse_moe_expert_route_amd/csrc/device_common.h")
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "olmoe_like_T16_pmc_traffic.txt")
 
