@@ -70,6 +70,10 @@ def parse():
                     help="sparse-vs-dense sweep of the Llama-4-like layer (its own JSON line)")
     ap.add_argument("--layer", default=None, help="layer of the crossover sweep")
     ap.add_argument("--batches", default=None, help="batches of the crossover sweep")
+    ap.add_argument("--paths", default="sparse,dense,auto",
+                    help="paths of the crossover sweep (sparse, dense, auto)")
+    ap.add_argument("--sparsity-shared", type=float, default=None,
+                    help="shared-expert sparsity of the crossover sweep (default: --sparsity)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration) and exit")
     return ap.parse_args()
@@ -471,40 +475,61 @@ def decode_step_variant(shape, args, n_layers=8, batches=(1, 16)):
 def cpu_baseline(shape, host, wl, seconds):
     """The oracle as it stands, on the host, over a bounded sample of steps."""
     import oracle
-    try:
-        import threadpoolctl
-        info = threadpoolctl.threadpool_info()
-        cores = max([i.get("num_threads", 1) for i in info] or [1])
-    except Exception:  # pragma: no cover
-        cores = 1
+    import threadpoolctl
+    info = threadpoolctl.threadpool_info()
+    cores = max([i.get("num_threads", 1) for i in info] or [1])
     import numpy as np
     T = wl.T
     wl.step(0)                           # the timed batch 0 once more, for the parity check
     wl.torch.cuda.synchronize()
     y_gpu = wl.y[0].cpu().numpy().astype(np.float64)
-    done, t0 = 0, time.perf_counter()
-    y_first = None
+
+    def call(i):
+        x = wl.x_host[i % wl.L]
+        return oracle.moe_layer(x, host.w_router, None, host.wg, host.wu, host.wd, top_k=shape.top_k,
+                                norm_topk=shape.norm_topk, k_keep=wl.k, dtype=shape.dtype,
+                                keep_h=False)
+
+    times, y_first, t0 = [], None, time.perf_counter()
     while True:
-        x = wl.x_host[done % wl.L]
-        r = oracle.moe_layer(x, host.w_router, None, host.wg, host.wu, host.wd, top_k=shape.top_k,
-                             norm_topk=shape.norm_topk, k_keep=wl.k, dtype=shape.dtype,
-                             keep_h=False)
+        c0 = time.perf_counter()
+        r = call(len(times))
+        times.append(time.perf_counter() - c0)
         if y_first is None:
             y_first = r.y
-        done += 1
         el = time.perf_counter() - t0
-        if el >= seconds or done >= 50:
+        if el >= seconds or len(times) >= 50:
             break
-    us_per_token = el * 1e6 / (done * T)
+    done = len(times)
+    med = float(np.median(times))
+    # one BLAS thread, a few calls (bounded to about a fifth of the sample's time)
+    t1 = []
+    try:
+        with threadpoolctl.threadpool_limits(limits=1):
+            s0 = time.perf_counter()
+            while len(t1) < 3 and (not t1 or time.perf_counter() - s0 < seconds / 5):
+                c0 = time.perf_counter()
+                call(len(t1))
+                t1.append(time.perf_counter() - c0)
+    except Exception:  # pragma: no cover
+        t1 = []
+    bpc = wl.bytes_per_call()
+    layer_bytes = sum(r["layer"] for r in bpc) / len(bpc)
     # the oracle's own routing and masks, no forcing: a near-tie that breaks
     # the other way would show here as a larger error (tests/ apply the
     # window rule; this is a sanity gate on the timed workload)
     rel = float(np.linalg.norm(y_gpu - y_first) / max(np.linalg.norm(y_first), 1e-300))
-    return {"value": round(us_per_token, 1), "unit": "us/token", "cores": int(cores),
-            "kind": "oracle",
-            "sample": f"{done} layer calls of {T} tokens ({done * T} tokens) of the same layer, "
-                      f"{el:.1f} s, float64 numpy oracle",
-            "parity_rel_l2_batch0": float(f"{rel:.3e}")}
+    out = {"value": round(med * 1e6 / T, 1), "unit": "us/token", "cores": int(cores),
+           "kind": "oracle",
+           "sample": f"{done} layer calls of {T} tokens ({done * T} tokens) of the same layer, "
+                     f"{el:.1f} s, float64 numpy oracle; value = median call / T",
+           "tokens_per_s": round(T / med, 2),
+           "implied_gbs": round(layer_bytes / med / 1e9, 3),
+           "parity_rel_l2_batch0": float(f"{rel:.3e}")}
+    if t1:
+        out["one_thread"] = {"us_per_token": round(float(np.median(t1)) * 1e6 / T, 1),
+                             "calls": len(t1)}
+    return out
 
 
 class HostLayer:
@@ -524,9 +549,10 @@ class HostLayer:
 
 
 def measure(shape, host, dev_w0, T, args, path=None, dev_sh0=None, score="swiglu",
-            sparsity=None):
+            sparsity=None, sparsity_shared=None):
     wl = Workload(shape, host, dev_w0, T, args.sparsity if sparsity is None else sparsity,
-                  path or args.path, dev_sh0=dev_sh0, score=score)
+                  path or args.path, dev_sh0=dev_sh0, score=score,
+                  sparsity_shared=sparsity_shared)
     log(f"[bench] {shape.name} T={T} k={wl.k} path={'sparse' if wl.path == 0 else 'dense'} "
         f"copies={wl.L}")
     wl.capture()
@@ -706,16 +732,23 @@ def crossover(args):
     dev_w0, dev_sh0 = dev_layer(shape, host, B)
     host.wg = host.wu = host.wd = host.shared = None     # device copies suffice from here on
     torch.cuda.synchronize()
+    paths = [p for p in args.paths.split(",") if p]
+    assert paths and all(p in ("sparse", "dense", "auto") for p in paths), args.paths
     rows = []
     for T in batches:
         row = {"T": T}
-        for path in ("sparse", "dense", "auto"):
-            wl, res = measure(shape, host, dev_w0, T, args, path=path, dev_sh0=dev_sh0)
+        for path in paths:
+            wl, res = measure(shape, host, dev_w0, T, args, path=path, dev_sh0=dev_sh0,
+                              sparsity_shared=args.sparsity_shared)
             kern = {k: round(v["per_step_us"], 2) for k, v in res["kernels"].items()}
             ent = {"us_per_call": round(res["us_per_call"], 2),
                    "us_per_token": round(res["us_per_token"], 3),
                    "layer_bytes": int(res["layer_bytes"]),
-                   "hbm_gbs": round(res["hbm_gbs"], 1), "kernels_us_per_step": kern}
+                   "hbm_gbs": round(res["hbm_gbs"], 1),
+                   "hbm_frac": round(res["hbm_frac"], 4),
+                   "active_experts": round(res["active_experts"], 2),
+                   "down_bytes": int(res["down_bytes"]),
+                   "kernels_us_per_step": kern}
             if path == "dense" and "down_dense" in res["kernels"]:
                 k = res["kernels"]["down_dense"]
                 ent["down_dense_tflops"] = round(res["flops_down_dense"] / (k["per_step_us"] * 1e-6) / 1e12, 2)
@@ -731,12 +764,17 @@ def crossover(args):
                 + ", ".join(f"{k} {v}" for k, v in kern.items()))
             del wl
             torch.cuda.empty_cache()
-        row["faster"] = "sparse" if row["sparse"]["us_per_call"] <= row["dense"]["us_per_call"] else "dense"
-        best = min(row["sparse"]["us_per_call"], row["dense"]["us_per_call"])
-        row["auto_vs_best"] = round(row["auto"]["us_per_call"] / best, 3)
+        if "sparse" in row and "dense" in row:
+            row["faster"] = ("sparse" if row["sparse"]["us_per_call"] <= row["dense"]["us_per_call"]
+                             else "dense")
+            best = min(row["sparse"]["us_per_call"], row["dense"]["us_per_call"])
+            if "auto" in row:
+                row["auto_vs_best"] = round(row["auto"]["us_per_call"] / best, 3)
         rows.append(row)
     print(json.dumps({"metric": "sparse-vs-dense crossover: MoE-layer us/call per forced path",
                       "layer": shape.name, "sparsity": args.sparsity,
+                      "sparsity_shared": (args.sparsity if args.sparsity_shared is None
+                                          else args.sparsity_shared),
                       "steps": args.steps, "warmup": args.warmup, "launch": "hip-graph replay per step",
                       "rows": rows}), flush=True)
 
