@@ -83,7 +83,7 @@ inline int n_items(const FfnArgs &a, int TG) {
 
 
 // The grouped GEMMs of dense.hip.  launch_gateup_gemm: h (or the gate
-// scores alone) for calls past 16 tokens, on the caller's stream, untimed.
+// scores alone) for calls past 64 tokens, on the caller's stream, untimed.
 // launch_down_dense: the dense-path down projection of bf16 masked rows
 // a.hm into per-pair partials, then their combine into y.
 void launch_gateup_gemm(const FfnArgs &a, const RouteView &rv, bool gate_only, hipStream_t stream);

@@ -81,6 +81,28 @@ def test_olmoe_like_dense(T):
     run_case("olmoe-like", T, 0.9, DN)
 
 
+@pytest.mark.parametrize("T", [1, 2, 16])
+def test_olmoe_like_dense_unmasked(T):
+    # k = d_ff on the dense path: a token's 8 x 1024 rows exceed one row
+    # stage, so every batch takes the grouped GEMM
+    run_case("olmoe-like", T, 0.0, DN)
+
+
+@pytest.mark.parametrize("T", [1, 2, 3])
+def test_dense_unmasked_rows(T):
+    # k = d_ff on the dense path with a token's rows within one stage (4 x 512)
+    # and about one token per expert: every row streamed per pair, weights
+    # applied while staging (T = 3 on 64 experts is still under 2 per expert)
+    run_case("olmoe-like", T, 0.0, DN, top_k=4, d_ff=512)
+
+
+@pytest.mark.parametrize("T", [1, 2, 8])
+def test_deepseek_v2_like_shared_dense_unmasked(T):
+    # the always-on experts at sparsity 0 on the dense path: rows per pair at
+    # T <= 2 tokens per expert, the grouped GEMM at T = 8
+    run_case("deepseek-v2-like", T, 0.9, SP, s_sh=0.0, path_sh=DN)
+
+
 @pytest.mark.parametrize("T,path", [(1, SP), (4, SP), (16, SP), (32, SP), (64, SP), (64, DN)])
 def test_qwen3_like_zipf(T, path):
     got = run_case("qwen3-moe-like", T, 0.9, path)
