@@ -29,11 +29,15 @@ namespace moe {
 
 // ---------------------------------------------------------------- gate / up
 // Block = one work item (an expert and up to 16 * MT of its tokens) x 16
-// neurons; 4 waves split K (H) by interleaved steps so that at any moment
-// the block reads contiguous 256-byte runs of each weight row.  Each wave
-// keeps 16x16 MFMA accumulators for gate and up for MT token tiles; weights
-// are loaded once, token rows (16 B per lane) come from L2.  The wave
-// partials meet in LDS, where h = silu(g) * u is formed and written per pair.
+// neurons; W waves split K (H) by interleaved steps so that at any moment
+// the block reads contiguous runs of each weight row.  Each wave keeps
+// 16x16 MFMA accumulators for gate and up for MT token tiles; weights are
+// loaded once, token rows (16 B per lane) come from L2.  The wave partials
+// meet in LDS, where h = silu(g) * u is formed and written per pair.
+// The weight stream depends only on the item's expert, so a wave issues
+// its first round of weight loads before it resolves the item's tokens
+// (expert offsets, then the pair list): those dependent lookups overlap
+// the first HBM round trip instead of preceding it.
 template <bool BF16, int MT, int W, bool GO = false>
 __global__ __launch_bounds__(64 * W, MT == 1 ? 8 : 1) void gateup_swiglu_kernel(const void *__restrict__ xv,
                                                             const void *__restrict__ wgv,
@@ -42,22 +46,45 @@ __global__ __launch_bounds__(64 * W, MT == 1 ? 8 : 1) void gateup_swiglu_kernel(
                                                             float *__restrict__ hout) {
   __shared__ float red[W][2][MT][4][64];
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  int e, q0, ntok;
-  if (MT == 1 && rv.T <= 16) {
+  const bool slot = MT == 1 && rv.T <= 16;  // uniform
+  int e, q0 = 0, ntok = 0;
+  if (slot) {
     // every active expert holds <= T <= 16 tokens: work item == active slot
+    // (s < min(E, P) <= E, so the slot's entry is read with the count)
     const int s = blockIdx.x;
-    if (s >= rv.nact()) return;  // block-uniform
+    const int na = rv.nact();
     e = rv.expert(s);
-    q0 = rv.begin(e);
-    ntok = rv.end(e) - q0;
+    if (s >= na) return;  // block-uniform
   } else if (!find_item<16 * MT>(rv, blockIdx.x, e, q0, ntok)) {
     return;  // block-uniform
   }
-  const int ntiles = (ntok + 15) >> 4;
   const int r = lane & 15, g = lane >> 4;
   const int row0 = blockIdx.y * 16;
   // packed weights: fragment (e, neuron tile, k-step) is 1 KB, lane-ordered
   const size_t ftile = (size_t)e * (d_ff / 16) + blockIdx.y;
+  constexpr int EPF = BF16 ? 512 : 256;     // elements per 1 KB fragment
+  constexpr int KPS = BF16 ? 32 : 16;       // k per step
+  const int nsteps = H / KPS;
+  const uint8_t *wg = static_cast<const uint8_t *>(wgv) + (ftile * nsteps * EPF + lane * (EPF / 64)) * (BF16 ? 2 : 4);
+  const uint8_t *wu = static_cast<const uint8_t *>(wuv) + (ftile * nsteps * EPF + lane * (EPF / 64)) * (BF16 ? 2 : 4);
+  constexpr int U = 4;  // k-steps in flight per wave
+  u32x4 ag[U], au[U];
+  auto load_round = [&](int s0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int ks = s0 + W * u;
+      if (ks < nsteps) {
+        ag[u] = ld16_nt(wg + (size_t)ks * 1024);
+        if (!GO) au[u] = ld16_nt(wu + (size_t)ks * 1024);
+      }
+    }
+  };
+  load_round(wid);
+  if (slot) {
+    q0 = rv.begin(e);
+    ntok = rv.end(e) - q0;
+  }
+  const int ntiles = (ntok + 15) >> 4;
 
   size_t xoff[MT];
   bool xval[MT];
@@ -72,27 +99,15 @@ __global__ __launch_bounds__(64 * W, MT == 1 ? 8 : 1) void gateup_swiglu_kernel(
 #pragma unroll
   for (int tl = 0; tl < MT; ++tl) { accg[tl] = f32x4{0, 0, 0, 0}; accu[tl] = f32x4{0, 0, 0, 0}; }
 
-  constexpr int U = 4;  // k-steps in flight per wave
-  if (BF16) {
-    const int nsteps = H / 32;
-    const uint16_t *wg = static_cast<const uint16_t *>(wgv) + ftile * nsteps * 512 + lane * 8;
-    const uint16_t *wu = static_cast<const uint16_t *>(wuv) + ftile * nsteps * 512 + lane * 8;
-    const uint16_t *x = static_cast<const uint16_t *>(xv);
-    for (int s = wid; s < nsteps; s += W * U) {
-      u32x4 ag[U], au[U];
+  for (int s = wid; s < nsteps; s += W * U) {
+    if (s != wid) load_round(s);  // round s (the first was issued above)
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int ks = s + W * u;
-        if (ks < nsteps) {
-          ag[u] = ld16_nt(wg + (size_t)ks * 512);
-          if (!GO) au[u] = ld16_nt(wu + (size_t)ks * 512);
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int ks = s + W * u;
-        if (ks < nsteps) {
+    for (int u = 0; u < U; ++u) {
+      const int ks = s + W * u;
+      if (ks < nsteps) {
+        if (BF16) {
           const int k = ks * 32 + g * 8;
+          const uint16_t *x = static_cast<const uint16_t *>(xv);
 #pragma unroll
           for (int tl = 0; tl < MT; ++tl) {
             if (tl < ntiles) {
@@ -101,29 +116,9 @@ __global__ __launch_bounds__(64 * W, MT == 1 ? 8 : 1) void gateup_swiglu_kernel(
               if (!GO) accu[tl] = mfma_bf16(au[u], b, accu[tl]);
             }
           }
-        }
-      }
-    }
-  } else {
-    const int nsteps = H / 16;
-    const float *wg = static_cast<const float *>(wgv) + ftile * nsteps * 256 + lane * 4;
-    const float *wu = static_cast<const float *>(wuv) + ftile * nsteps * 256 + lane * 4;
-    const float *x = static_cast<const float *>(xv);
-    for (int s = wid; s < nsteps; s += W * U) {
-      u32x4 ag[U], au[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int ks = s + W * u;
-        if (ks < nsteps) {
-          ag[u] = ld16_nt(wg + (size_t)ks * 256);
-          if (!GO) au[u] = ld16_nt(wu + (size_t)ks * 256);
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int ks = s + W * u;
-        if (ks < nsteps) {
+        } else {
           const int k = ks * 16 + g * 4;
+          const float *x = static_cast<const float *>(xv);
 #pragma unroll
           for (int tl = 0; tl < MT; ++tl) {
             if (tl < ntiles) {
