@@ -416,7 +416,9 @@ def decode_step_variant(shape, args, n_layers=8, batches=(1, 16)):
     torch.cuda.synchronize()
     E, K = shape.n_experts, shape.top_k
     k = B.moe_keep_count(args.sparsity, shape.d_ff)
-    out = {"layers": n_layers, "what": "route -> FFN -> residual per layer, one graph per step"}
+    out = {"layers": n_layers, "what": "route -> FFN -> residual per layer, one graph per step; "
+           "the sparse FFN call writes the next layer's input in its epilogue "
+           "(moe_expert_ffn_sparse_residual), 'unfused' runs moe_residual_add after it"}
     for T in batches:
         path = B.moe_select_path(desc, T, k)
         ffn = B.moe_expert_ffn_sparse if path == B.MOE_PATH_SPARSE else B.moe_expert_ffn_dense
@@ -428,44 +430,53 @@ def decode_step_variant(shape, args, n_layers=8, batches=(1, 16)):
         ws = torch.empty(B.moe_ffn_workspace_size(desc, T, k, path), dtype=torch.uint8,
                          device="cuda")
 
-        def step():
+        def step(fused):
             x = x0
             for (wr, wg, wu, wd), xo, R in zip(layers, xs, Rs):
                 B.moe_route(desc, T, x, wr, None, R, ws_r)
-                ffn(desc, T, k, x, wg, wu, wd, R, y, 0, None, ws)
-                B.moe_residual_add(desc, T, x, y, xo)
+                if fused and path == B.MOE_PATH_SPARSE:
+                    B.moe_expert_ffn_sparse_residual(desc, T, k, x, wg, wu, wd, R, y, x, xo, 0,
+                                                     None, ws)
+                else:
+                    ffn(desc, T, k, x, wg, wu, wd, R, y, 0, None, ws)
+                    B.moe_residual_add(desc, T, x, y, xo)
                 x = xo
 
-        step()
+        step(False)
         torch.cuda.synchronize()
         ref = xs[-1].clone()
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            step()
-        torch.cuda.current_stream().wait_stream(side)
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            step()
-        torch.cuda.synchronize()
-        xs[-1].fill_(0)
-        g.replay()
-        torch.cuda.synchronize()
-        if not torch.equal(xs[-1], ref):
-            raise RuntimeError("decode-step graph replay differs from the eager step")
-        for _ in range(args.warmup):
+        timed = {}
+        for fused in (True, False):
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                step(fused)
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(fused)
+            torch.cuda.synchronize()
+            xs[-1].fill_(0)
             g.replay()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(args.steps):
-            g.replay()
-        torch.cuda.synchronize()
-        us = (time.perf_counter() - t0) / args.steps * 1e6
+            torch.cuda.synchronize()
+            if not torch.equal(xs[-1], ref):
+                raise RuntimeError("decode-step graph replay differs from the eager step")
+            for _ in range(args.warmup):
+                g.replay()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(args.steps):
+                g.replay()
+            torch.cuda.synchronize()
+            timed[fused] = (time.perf_counter() - t0) / args.steps * 1e6
+            del g
+        us = timed[True]
         out[str(T)] = {"path": "sparse" if path == B.MOE_PATH_SPARSE else "dense",
                        "us_per_step": round(us, 1), "us_per_layer": round(us / n_layers, 2),
-                       "us_per_token_per_layer": round(us / n_layers / T, 3)}
-        del g, xs, Rs, ws, ws_r, y
+                       "us_per_token_per_layer": round(us / n_layers / T, 3),
+                       "unfused_us_per_layer": round(timed[False] / n_layers, 2)}
+        del xs, Rs, ws, ws_r, y
         torch.cuda.empty_cache()
     del layers
     torch.cuda.empty_cache()

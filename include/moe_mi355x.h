@@ -185,6 +185,28 @@ moe_status moe_expert_ffn_sparse(const moe_desc *d, int32_t T, int32_t k_keep, c
                                  size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * moe_expert_ffn_sparse_residual -- moe_expert_ffn_sparse followed by the
+ * residual stream of a decode step (as moe_residual_add), fused into the
+ * down projection's epilogue: once a y element is final, the block that
+ * wrote it also writes x_next[t, h] = x_res[t, h] + y[t, h], summed in fp32
+ * and rounded to desc->dtype (round to nearest even for bf16).  One launch
+ * fewer per layer; the results equal moe_expert_ffn_sparse then
+ * moe_residual_add bit for bit.  It must be a layer's last FFN call (after
+ * any routed call whose output it accumulates onto): no later call may read
+ * x if x_next aliases it.  x_res and x_next [T, H] in desc->dtype, 16-byte
+ * aligned, non-NULL when T > 0 (else MOE_ERR_INVALID_ARG /
+ * MOE_ERR_MISALIGNED); x_next may be x_res or x.  Other arguments, outputs,
+ * workspace and errors as moe_expert_ffn_sparse.  With k_keep == 0 the
+ * residual runs as its own pass.
+ */
+moe_status moe_expert_ffn_sparse_residual(const moe_desc *d, int32_t T, int32_t k_keep,
+                                          const void *x, const void *w_gate, const void *w_up,
+                                          const void *w_down, const moe_routing *routing,
+                                          float *y, int32_t accumulate, int32_t *active_idx_out,
+                                          const void *x_res, void *x_next, void *workspace,
+                                          size_t workspace_bytes, hipStream_t stream);
+
+/*
  * moe_expert_ffn_dense -- the same layer function on the dense path the
  * page switches to at large batch (technical summary, Methodology: dynamic
  * switch between sparse and dense code paths by batch size).  Gate/up and

@@ -52,6 +52,8 @@ _SIGS = {
     "moe_route_roster": (_I32, [_PD, _I32, _V, _V, _V, _V, _V, _I32, ctypes.c_float, _PR, _V, _SZ,
                                 _V]),
     "moe_expert_ffn_sparse": (_I32, [_PD, _I32, _I32, _V, _V, _V, _V, _PR, _V, _I32, _V, _V, _SZ, _V]),
+    "moe_expert_ffn_sparse_residual": (_I32, [_PD, _I32, _I32, _V, _V, _V, _V, _PR, _V, _I32, _V,
+                                              _V, _V, _V, _SZ, _V]),
     "moe_expert_ffn_dense": (_I32, [_PD, _I32, _I32, _V, _V, _V, _V, _PR, _V, _I32, _V, _V, _SZ, _V]),
     "moe_expert_ffn_sparse_updown": (_I32, [_PD, _I32, _I32, _V, _V, _V, _V, _PR, _V, _I32, _V, _V, _SZ, _V]),
     "moe_expert_ffn_sparse_threshold": (_I32, [_PD, _I32, _V, _V, _V, _V, _V, _PR, _V, _I32, _V, _V, _V, _SZ, _V]),
@@ -200,6 +202,20 @@ def moe_expert_ffn_sparse(desc, T, k_keep, x, w_gate, w_up, w_down, routing, y, 
                           active_idx_out=None, workspace=None, stream=None):
     _ffn(lib().moe_expert_ffn_sparse, desc, T, k_keep, x, w_gate, w_up, w_down, routing, y,
          accumulate, active_idx_out, workspace, stream)
+
+
+def moe_expert_ffn_sparse_residual(desc, T, k_keep, x, w_gate, w_up, w_down, routing, y, x_res,
+                                   x_next, accumulate=0, active_idx_out=None, workspace=None,
+                                   stream=None):
+    """moe_expert_ffn_sparse, then x_next = x_res + y (rounded to the layer
+    dtype) in the down projection's epilogue; the last FFN call of a layer."""
+    r = routing.as_c() if routing is not None else None
+    ws = _ptr(workspace)
+    _check(lib().moe_expert_ffn_sparse_residual(
+        ctypes.byref(desc), int(T), int(k_keep), _ptr(x), _ptr(w_gate), _ptr(w_up), _ptr(w_down),
+        ctypes.byref(r) if r is not None else None, _ptr(y), int(accumulate),
+        _ptr(active_idx_out), _ptr(x_res), _ptr(x_next), ws,
+        workspace.numel() * workspace.element_size() if ws else 0, _stream(stream)))
 
 
 def moe_expert_ffn_dense(desc, T, k_keep, x, w_gate, w_up, w_down, routing, y, accumulate=0,

@@ -132,6 +132,8 @@ struct ModeArgs {
   int32_t *counts = nullptr;    // threshold: optional [P] kept counts (device)
   double sparsity = 0.0;        // calibrate: target sparsity
   float *tau_out = nullptr;     // calibrate: [E] thresholds (device)
+  const void *xres = nullptr;   // sparse: residual epilogue input [T, H] (device)
+  void *xnext = nullptr;        // sparse: residual epilogue output [T, H] (device)
 };
 
 moe_status run_ffn(RunMode mode, const moe_desc *d, int32_t T, int32_t k_keep, const void *x,
@@ -224,6 +226,8 @@ moe_status run_ffn(RunMode mode, const moe_desc *d, int32_t T, int32_t k_keep, c
   a.hact = path == MOE_PATH_SPARSE ? reinterpret_cast<float *>(ws + L.hact) : nullptr;
   a.partial = reinterpret_cast<float *>(ws + L.partial);
   a.hm = path == MOE_PATH_DENSE ? static_cast<void *>(ws + L.hm) : nullptr;
+  a.xres = m.xres;
+  a.xnext = m.xnext;
   hipError_t e;
   switch (mode) {
     case kRunUpdown: e = moe::launch_ffn_updown(a, stream); break;
@@ -335,6 +339,25 @@ moe_status moe_expert_ffn_sparse(const moe_desc *d, int32_t T, int32_t k_keep, c
                                  size_t workspace_bytes, hipStream_t stream) {
   return run_ffn(kRunSparse, d, T, k_keep, x, w_gate, w_up, w_down, routing, y, accumulate,
                  active_idx_out, workspace, workspace_bytes, stream);
+}
+
+moe_status moe_expert_ffn_sparse_residual(const moe_desc *d, int32_t T, int32_t k_keep,
+                                          const void *x, const void *w_gate, const void *w_up,
+                                          const void *w_down, const moe_routing *routing,
+                                          float *y, int32_t accumulate, int32_t *active_idx_out,
+                                          const void *x_res, void *x_next, void *workspace,
+                                          size_t workspace_bytes, hipStream_t stream) {
+  g_err[0] = 0;
+  if (T > 0) {
+    if (!x_res || !x_next) return fail(MOE_ERR_INVALID_ARG, "x_res and x_next must be non-NULL");
+    if (!aligned16(x_res) || !aligned16(x_next))
+      return fail(MOE_ERR_MISALIGNED, "x_res and x_next must be 16-byte aligned");
+  }
+  ModeArgs m;
+  m.xres = x_res;
+  m.xnext = x_next;
+  return run_ffn(kRunSparse, d, T, k_keep, x, w_gate, w_up, w_down, routing, y, accumulate,
+                 active_idx_out, workspace, workspace_bytes, stream, m);
 }
 
 moe_status moe_expert_ffn_dense(const moe_desc *d, int32_t T, int32_t k_keep, const void *x,

@@ -638,6 +638,18 @@ __global__ __launch_bounds__(64) void up_rows_var_kernel(const void *__restrict_
 constexpr int kDownWaves = 16;
 constexpr int kDownStage = 4096;     // row-list entries staged in LDS
 
+// The residual stream's element o of the next layer's input: x_res + y
+// summed in fp32, rounded to the layer dtype (as residual_kernel does).
+template <bool BF16>
+__device__ __forceinline__ void residual_store(const void *xres, void *xnext, size_t o, float y) {
+  if (BF16) {
+    const uint32_t xb = static_cast<const uint16_t *>(xres)[o];
+    static_cast<uint16_t *>(xnext)[o] = (uint16_t)f32_to_bf16_bits(bf16lo(xb) + y);
+  } else {
+    static_cast<float *>(xnext)[o] = static_cast<const float *>(xres)[o] + y;
+  }
+}
+
 template <bool BF16, int SW, int U>
 __device__ __forceinline__ void stream_rows_u(const void *__restrict__ wdv,
                                               const uint32_t *srow, const float *scoef, int n,
@@ -708,7 +720,8 @@ __global__ __launch_bounds__(1024) void down_token_kernel(const void *__restrict
                                                           const float *__restrict__ coef,
                                                           RouteView rv, int H, int d_ff, int k,
                                                           int weighted, int accumulate,
-                                                          float *__restrict__ y) {
+                                                          float *__restrict__ y,
+                                                          const void *xres, void *xnext) {
   constexpr int VEC = BF16 ? 8 : 4;   // elements per 16-byte load
   constexpr int LPR = SW / VEC;       // lanes per row
   static_assert(LPR <= 64 && 64 % LPR == 0, "a row run must fit one wave");
@@ -755,8 +768,10 @@ __global__ __launch_bounds__(1024) void down_token_kernel(const void *__restrict
     float v = 0.f;
 #pragma unroll
     for (int w = 0; w < kDownWaves; ++w) v += red[w][threadIdx.x];
-    float *yp = y + (size_t)t * H + col0 + threadIdx.x;
-    *yp = accumulate ? *yp + v : v;
+    const size_t o = (size_t)t * H + col0 + threadIdx.x;
+    const float out = accumulate ? y[o] + v : v;
+    y[o] = out;
+    if (xnext) residual_store<BF16>(xres, xnext, o, out);
   }
 }
 
@@ -910,7 +925,8 @@ __global__ __launch_bounds__(1024) void down_var_token_kernel(const void *__rest
 template <bool BF16, int SW, int V>
 __global__ __launch_bounds__(1024) void down_topk_token_kernel(
     const void *__restrict__ wdv, const float *__restrict__ h, RouteView rv, int H, int d_ff,
-    int k, int accumulate, float *__restrict__ y, int32_t *__restrict__ idx_out) {
+    int k, int accumulate, float *__restrict__ y, int32_t *__restrict__ idx_out,
+    const void *xres, void *xnext) {
   constexpr int VEC = BF16 ? 8 : 4;
   constexpr int LPR = SW / VEC;
   constexpr int RPI = 64 / LPR;
@@ -1027,8 +1043,10 @@ __global__ __launch_bounds__(1024) void down_topk_token_kernel(
     float v = 0.f;
 #pragma unroll
     for (int w = 0; w < kDownWaves; ++w) v += red[w][tid];
-    float *yp = y + (size_t)t * H + col0 + tid;
-    *yp = accumulate ? *yp + v : v;
+    const size_t o = (size_t)t * H + col0 + tid;
+    const float out = accumulate ? y[o] + v : v;
+    y[o] = out;
+    if (xnext) residual_store<BF16>(xres, xnext, o, out);
   }
 }
 
@@ -1365,7 +1383,8 @@ static void launch_down_token(const FfnArgs &a, const RouteView &rv, const int32
   timer_begin(kStageDownRows, stream);
 #define MOE_DOWN(BF, SWV)                                                                     \
   down_token_kernel<BF, SWV><<<grid, 1024, 0, stream>>>(a.w_down, idx, coef, rv, a.H, a.d_ff, k, \
-                                                        weighted, a.accumulate, a.y)
+                                                        weighted, a.accumulate, a.y, a.xres,    \
+                                                        a.xnext)
   if (a.bf16) {
     if (sw == 128) MOE_DOWN(true, 128); else MOE_DOWN(true, 64);
   } else {
@@ -1388,7 +1407,10 @@ static bool fused_topk_ok(const FfnArgs &a) {
 
 hipError_t launch_ffn_sparse(const FfnArgs &a, hipStream_t stream) {
   if (a.T == 0) return hipSuccess;
-  if (zero_contribution(a, stream)) return hipGetLastError();
+  if (zero_contribution(a, stream)) {
+    if (a.xnext) return launch_residual(a.xres, a.y, a.xnext, (size_t)a.T * a.H, a.bf16, stream);
+    return hipGetLastError();
+  }
   const RouteView rv = make_view(a);
   launch_gateup(a, rv, stream);
   if (fused_topk_ok(a)) {
@@ -1398,7 +1420,8 @@ hipError_t launch_ffn_sparse(const FfnArgs &a, hipStream_t stream) {
     timer_begin(kStageDownRows, stream);
 #define MOE_DK(BF, SWV, VV)                                                                   \
   down_topk_token_kernel<BF, SWV, VV><<<grid, 1024, 0, stream>>>(a.w_down, a.h, rv, a.H, a.d_ff, \
-                                                                 a.k_keep, a.accumulate, a.y, io)
+                                                                 a.k_keep, a.accumulate, a.y, io, \
+                                                                 a.xres, a.xnext)
 #define MOE_DK_V(BF, SWV)                                                                     \
   switch (a.d_ff / 64) {                                                                      \
     case 4: MOE_DK(BF, SWV, 4); break;                                                        \

@@ -75,6 +75,10 @@ struct FfnArgs {
   float *hact;       // [P, k_keep]   w * h at the kept neurons
   float *partial;    // dense bf16 path: [P, H] per-pair down outputs
   void *hm;          // dense path: [P, d_ff] masked, weighted h (bf16 or fp32)
+  // optional residual epilogue (sparse path): x_next = x_res + y, rounded to
+  // the layer dtype, written where each y element is final; null to skip
+  const void *xres;
+  void *xnext;
 };
 
 hipError_t launch_residual(const void *x_in, const float *y, void *x_out, size_t n, int bf16,

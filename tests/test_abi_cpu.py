@@ -147,6 +147,27 @@ def test_ffn_validation(fn_name):
     assert B.moe_last_error() == ""
 
 
+def test_ffn_residual_validation():
+    fn = L.moe_expert_ffn_sparse_residual
+    d = _desc()
+
+    def R(T=4, k=10, xr=FAKE, xn=FAKE, x=FAKE, ws=FAKE, acc=0):
+        r = B.MoeRouting(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+        return fn(ctypes.byref(d), T, k, x, FAKE, FAKE, FAKE, ctypes.byref(r), FAKE, acc, None,
+                  xr, xn, ws, 1 << 34, None)
+    assert R(xr=None) == INV
+    assert R(xn=None) == INV
+    assert R(xr=MIS) == MISA
+    assert R(xn=MIS) == MISA
+    assert "x_res" in B.moe_last_error()
+    # the rest is validated as for moe_expert_ffn_sparse
+    assert R(k=-1) == INV
+    assert R(x=None) == INV
+    assert R(acc=2) == INV
+    assert R(ws=None) == WSP
+    assert R(T=0, xr=None, xn=None, x=None, ws=None) == 0
+
+
 def test_threshold_and_calibration_validation():
     d = _desc()
     r = B.MoeRouting(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
