@@ -125,10 +125,18 @@ class Workload:
             self.copies_sh = [dev_sh0] + [tuple(w.clone() for w in dev_sh0) for _ in range(self.L - 1)]
         self.x_host = [S.tokens(sh, 1 + i, T) for i in range(self.L)]
         self.x = [host_w.to_dev(x) for x in self.x_host]
+        # the layer's router bias (the Zipf skew of the Qwen3-MoE-like layer), or None
+        self.bias = host_w.to_dev(host_w.bias) if host_w.bias is not None else None
         self.routing = [B.Routing.allocate(T, K, E) for _ in range(self.L)]
         self.ws_r = torch.empty(B.moe_route_workspace_size(self.desc, T), dtype=torch.uint8, device="cuda")
         self.ws = torch.empty(B.moe_ffn_workspace_size(self.desc, T, self.k, self.path),
                               dtype=torch.uint8, device="cuda")
+        # plain routed layers on the sparse path run as one moe_layer_sparse
+        # call (the same kernels as moe_route + moe_expert_ffn_sparse, and at
+        # one token the selection runs inside the gate/up kernel)
+        self.layer_call = score == "swiglu" and self.path == B.MOE_PATH_SPARSE and dev_sh0 is None
+        self.ws_l = (torch.empty(B.moe_layer_workspace_size(self.desc, T, self.k), dtype=torch.uint8,
+                                 device="cuda") if self.layer_call else None)
         self.y = [torch.empty((T, sh.hidden), dtype=torch.float32, device="cuda") for _ in range(self.L)]
         self.idx = torch.empty((T * K, max(1, self.k)), dtype=torch.int32, device="cuda")
         if thr:
@@ -138,7 +146,7 @@ class Workload:
             r_cal = B.Routing.allocate(CAL_TOKENS, K, E)
             ws_c = torch.empty(B.moe_route_workspace_size(self.desc, CAL_TOKENS), dtype=torch.uint8,
                                device="cuda")
-            B.moe_route(self.desc, CAL_TOKENS, x_cal, dev_w0[0], None, r_cal, ws_c)
+            B.moe_route(self.desc, CAL_TOKENS, x_cal, dev_w0[0], self.bias, r_cal, ws_c)
             ws_c = torch.empty(B.moe_calibrate_workspace_size(self.desc, CAL_TOKENS),
                                dtype=torch.uint8, device="cuda")
             self.tau = torch.empty(E, dtype=torch.float32, device="cuda")
@@ -169,7 +177,11 @@ class Workload:
         B = self.B
         j = i % self.L
         wr, wg, wu, wd = self.copies[j]
-        B.moe_route(self.desc, self.T, self.x[j], wr, None, self.routing[j], self.ws_r)
+        if self.layer_call:
+            B.moe_layer_sparse(self.desc, self.T, self.k, self.x[j], wr, self.bias, wg, wu, wd,
+                               self.routing[j], self.y[j], 0, idx, self.ws_l)
+            return
+        B.moe_route(self.desc, self.T, self.x[j], wr, self.bias, self.routing[j], self.ws_r)
         self.ffn(self.desc, self.T, self.k, self.x[j], wg, wu, wd, self.routing[j], self.y[j], 0,
                  idx, self.ws)
         if self.copies_sh is not None:
@@ -497,7 +509,7 @@ def cpu_baseline(shape, host, wl, seconds):
 
     def call(i):
         x = wl.x_host[i % wl.L]
-        return oracle.moe_layer(x, host.w_router, None, host.wg, host.wu, host.wd, top_k=shape.top_k,
+        return oracle.moe_layer(x, host.w_router, host.bias, host.wg, host.wu, host.wd, top_k=shape.top_k,
                                 norm_topk=shape.norm_topk, k_keep=wl.k, dtype=shape.dtype,
                                 keep_h=False)
 
@@ -547,6 +559,7 @@ class HostLayer:
     def __init__(self, shape, shared=False):
         import moe_synth as S
         self.w_router = S.router_matrix(shape, 0)
+        self.bias = S.router_bias(shape)
         self.wg, self.wu, self.wd = S.expert_weights(shape, 0)
         self.shared = S.expert_weights(shape, 0, group=S.SHARED) if shared else None
 

@@ -207,6 +207,33 @@ moe_status moe_expert_ffn_sparse_residual(const moe_desc *d, int32_t T, int32_t 
                                           size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * moe_layer_sparse -- a whole routed layer in one call: moe_route (no bias
+ * roster) then moe_expert_ffn_sparse, or moe_expert_ffn_sparse_residual
+ * when x_res and x_next are given (both or neither; then the layer's last
+ * FFN call), with the same outputs bit for bit (routing_out filled as
+ * moe_route fills it, y as the FFN call writes it).
+ * For a single token (T == 1, E <= 256, 0 < k_keep < d_ff and the shapes
+ * of the small-batch select) it runs as three kernels instead of four: the
+ * gate/up blocks repeat the router's top-k selection on the logits and each
+ * takes its own expert, so the select-and-group launch goes away (the page
+ * asks its integration to work with kernel fusion and graph capture:
+ * technical summary, Key contributions); other calls run the two calls'
+ * kernels in turn.  Arguments as moe_route and moe_expert_ffn_sparse; one
+ * workspace of moe_layer_workspace_size(d, T, k_keep) bytes.  Every
+ * argument is checked before anything is enqueued.
+ */
+moe_status moe_layer_sparse(const moe_desc *d, int32_t T, int32_t k_keep, const void *x,
+                            const void *w_router, const float *bias, const void *w_gate,
+                            const void *w_up, const void *w_down, const moe_routing *routing_out,
+                            float *y, int32_t accumulate, int32_t *active_idx_out,
+                            const void *x_res, void *x_next, void *workspace,
+                            size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes for moe_layer_sparse over at most T tokens with this
+ * k_keep (0 on invalid input). */
+size_t moe_layer_workspace_size(const moe_desc *d, int32_t T, int32_t k_keep);
+
+/*
  * moe_expert_ffn_dense -- the same layer function on the dense path the
  * page switches to at large batch (technical summary, Methodology: dynamic
  * switch between sparse and dense code paths by batch size).  Gate/up and

@@ -54,6 +54,9 @@ _SIGS = {
     "moe_expert_ffn_sparse": (_I32, [_PD, _I32, _I32, _V, _V, _V, _V, _PR, _V, _I32, _V, _V, _SZ, _V]),
     "moe_expert_ffn_sparse_residual": (_I32, [_PD, _I32, _I32, _V, _V, _V, _V, _PR, _V, _I32, _V,
                                               _V, _V, _V, _SZ, _V]),
+    "moe_layer_sparse": (_I32, [_PD, _I32, _I32, _V, _V, _V, _V, _V, _V, _PR, _V, _I32, _V, _V,
+                                _V, _V, _SZ, _V]),
+    "moe_layer_workspace_size": (_SZ, [_PD, _I32, _I32]),
     "moe_expert_ffn_dense": (_I32, [_PD, _I32, _I32, _V, _V, _V, _V, _PR, _V, _I32, _V, _V, _SZ, _V]),
     "moe_expert_ffn_sparse_updown": (_I32, [_PD, _I32, _I32, _V, _V, _V, _V, _PR, _V, _I32, _V, _V, _SZ, _V]),
     "moe_expert_ffn_sparse_threshold": (_I32, [_PD, _I32, _V, _V, _V, _V, _V, _PR, _V, _I32, _V, _V, _V, _SZ, _V]),
@@ -216,6 +219,24 @@ def moe_expert_ffn_sparse_residual(desc, T, k_keep, x, w_gate, w_up, w_down, rou
         ctypes.byref(r) if r is not None else None, _ptr(y), int(accumulate),
         _ptr(active_idx_out), _ptr(x_res), _ptr(x_next), ws,
         workspace.numel() * workspace.element_size() if ws else 0, _stream(stream)))
+
+
+def moe_layer_sparse(desc, T, k_keep, x, w_router, bias, w_gate, w_up, w_down, routing, y,
+                     accumulate=0, active_idx_out=None, workspace=None, stream=None, x_res=None,
+                     x_next=None):
+    """moe_route then moe_expert_ffn_sparse (or, with x_res and x_next, the
+    residual-fused FFN) in one call; fused further at one token."""
+    r = routing.as_c()
+    ws = _ptr(workspace)
+    _check(lib().moe_layer_sparse(
+        ctypes.byref(desc), int(T), int(k_keep), _ptr(x), _ptr(w_router), _ptr(bias), _ptr(w_gate),
+        _ptr(w_up), _ptr(w_down), ctypes.byref(r), _ptr(y), int(accumulate), _ptr(active_idx_out),
+        _ptr(x_res), _ptr(x_next), ws, workspace.numel() * workspace.element_size() if ws else 0,
+        _stream(stream)))
+
+
+def moe_layer_workspace_size(desc, T, k_keep):
+    return int(lib().moe_layer_workspace_size(ctypes.byref(desc), int(T), int(k_keep)))
 
 
 def moe_expert_ffn_dense(desc, T, k_keep, x, w_gate, w_up, w_down, routing, y, accumulate=0,

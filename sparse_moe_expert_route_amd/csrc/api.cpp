@@ -134,6 +134,8 @@ struct ModeArgs {
   float *tau_out = nullptr;     // calibrate: [E] thresholds (device)
   const void *xres = nullptr;   // sparse: residual epilogue input [T, H] (device)
   void *xnext = nullptr;        // sparse: residual epilogue output [T, H] (device)
+  bool validate_only = false;   // check every argument, enqueue nothing
+  const moe::RouteArgs *layer_route = nullptr;  // sparse: run the router first (whole layer)
 };
 
 moe_status run_ffn(RunMode mode, const moe_desc *d, int32_t T, int32_t k_keep, const void *x,
@@ -195,6 +197,7 @@ moe_status run_ffn(RunMode mode, const moe_desc *d, int32_t T, int32_t k_keep, c
   if (!aligned16(workspace)) return fail(MOE_ERR_MISALIGNED, "workspace is not 16-byte aligned");
   if (workspace_bytes < L.total)
     return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, L.total);
+  if (m.validate_only) return MOE_OK;
 
   char *ws = static_cast<char *>(workspace);
   moe::FfnArgs a{};
@@ -246,7 +249,13 @@ moe_status run_ffn(RunMode mode, const moe_desc *d, int32_t T, int32_t k_keep, c
                                 mode == kRunCalibrateGate, stream);
       break;
     case kRunDense: e = moe::launch_ffn_dense(a, stream); break;
-    default: e = moe::launch_ffn_sparse(a, stream);
+    default:
+      if (m.layer_route && moe::layer_t1_ok(*m.layer_route, a)) {
+        e = moe::launch_layer_t1(*m.layer_route, a, stream);
+      } else {
+        e = m.layer_route ? moe::launch_route(*m.layer_route, stream) : hipSuccess;
+        if (e == hipSuccess) e = moe::launch_ffn_sparse(a, stream);
+      }
   }
   if (e != hipSuccess) return fail(MOE_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return MOE_OK;
@@ -256,11 +265,9 @@ moe_status run_ffn(RunMode mode, const moe_desc *d, int32_t T, int32_t k_keep, c
 
 extern "C" {
 
-static moe_status route_impl(const moe_desc *d, int32_t T, const void *x, const void *w_router,
-                             const float *bias, const moe::RosterArgs &ro,
-                             const moe_routing *out, void *workspace, size_t workspace_bytes,
-                             hipStream_t stream) {
-  g_err[0] = 0;
+static moe_status route_check(const moe_desc *d, int32_t T, const void *x, const void *w_router,
+                              const float *bias, const moe::RosterArgs &ro,
+                              const moe_routing *out, void *workspace, size_t workspace_bytes) {
   TRY(check_desc(d));
   TRY(check_T(T));
   if (!out) return fail(MOE_ERR_INVALID_ARG, "routing output struct is NULL");
@@ -292,6 +299,13 @@ static moe_status route_impl(const moe_desc *d, int32_t T, const void *x, const 
   if (!aligned16(workspace)) return fail(MOE_ERR_MISALIGNED, "workspace is not 16-byte aligned");
   if (workspace_bytes < need)
     return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+  return MOE_OK;
+}
+
+static moe::RouteArgs route_args(const moe_desc *d, int32_t T, const void *x,
+                                 const void *w_router, const float *bias,
+                                 const moe::RosterArgs &ro, const moe_routing *out,
+                                 void *workspace) {
   moe::RouteArgs a{};
   a.T = T;
   a.H = d->hidden;
@@ -310,6 +324,17 @@ static moe_status route_impl(const moe_desc *d, int32_t T, const void *x, const 
   a.pair_by_expert = out->pair_by_expert;
   a.active = out->active_experts;
   a.n_active = out->n_active;
+  return a;
+}
+
+static moe_status route_impl(const moe_desc *d, int32_t T, const void *x, const void *w_router,
+                             const float *bias, const moe::RosterArgs &ro,
+                             const moe_routing *out, void *workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
+  g_err[0] = 0;
+  TRY(route_check(d, T, x, w_router, bias, ro, out, workspace, workspace_bytes));
+  if (T == 0) return MOE_OK;
+  const moe::RouteArgs a = route_args(d, T, x, w_router, bias, ro, out, workspace);
   const hipError_t e = moe::launch_route(a, stream);
   if (e != hipSuccess) return fail(MOE_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return MOE_OK;
@@ -358,6 +383,50 @@ moe_status moe_expert_ffn_sparse_residual(const moe_desc *d, int32_t T, int32_t 
   m.xnext = x_next;
   return run_ffn(kRunSparse, d, T, k_keep, x, w_gate, w_up, w_down, routing, y, accumulate,
                  active_idx_out, workspace, workspace_bytes, stream, m);
+}
+
+size_t moe_layer_workspace_size(const moe_desc *d, int32_t T, int32_t k_keep) {
+  const size_t r = moe_route_workspace_size(d, T);
+  const size_t f = moe_ffn_workspace_size(d, T, k_keep, MOE_PATH_SPARSE);
+  if (check_desc(d) != MOE_OK || T < 0 || k_keep < 0 || k_keep > d->d_ff) return 0;
+  return up(r) + f;
+}
+
+moe_status moe_layer_sparse(const moe_desc *d, int32_t T, int32_t k_keep, const void *x,
+                            const void *w_router, const float *bias, const void *w_gate,
+                            const void *w_up, const void *w_down, const moe_routing *routing_out,
+                            float *y, int32_t accumulate, int32_t *active_idx_out,
+                            const void *x_res, void *x_next, void *workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+  g_err[0] = 0;
+  TRY(check_desc(d));
+  TRY(check_T(T));
+  if (T == 0) return MOE_OK;
+  if ((x_res == nullptr) != (x_next == nullptr))
+    return fail(MOE_ERR_INVALID_ARG, "x_res and x_next must both be given or both be NULL");
+  if (x_res && (!aligned16(x_res) || !aligned16(x_next)))
+    return fail(MOE_ERR_MISALIGNED, "x_res and x_next must be 16-byte aligned");
+  if (!workspace) return fail(MOE_ERR_WORKSPACE, "workspace is NULL");
+  if (!aligned16(workspace)) return fail(MOE_ERR_MISALIGNED, "workspace is not 16-byte aligned");
+  const size_t need = moe_layer_workspace_size(d, T, k_keep);
+  if (need == 0) return fail(MOE_ERR_INVALID_ARG, "k_keep %d outside [0, d_ff=%d]", k_keep, d->d_ff);
+  if (workspace_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+  const size_t rws = up(moe_route_workspace_size(d, T));
+  char *ws = static_cast<char *>(workspace);
+  // every argument of both halves is checked before anything is enqueued
+  TRY(route_check(d, T, x, w_router, bias, moe::RosterArgs{}, routing_out, ws, rws));
+  ModeArgs m;
+  m.validate_only = true;
+  m.xres = x_res;
+  m.xnext = x_next;
+  TRY(run_ffn(kRunSparse, d, T, k_keep, x, w_gate, w_up, w_down, routing_out, y, accumulate,
+              active_idx_out, ws + rws, workspace_bytes - rws, stream, m));
+  const moe::RouteArgs ra = route_args(d, T, x, w_router, bias, moe::RosterArgs{}, routing_out, ws);
+  m.validate_only = false;
+  m.layer_route = &ra;
+  return run_ffn(kRunSparse, d, T, k_keep, x, w_gate, w_up, w_down, routing_out, y, accumulate,
+                 active_idx_out, ws + rws, workspace_bytes - rws, stream, m);
 }
 
 moe_status moe_expert_ffn_dense(const moe_desc *d, int32_t T, int32_t k_keep, const void *x,

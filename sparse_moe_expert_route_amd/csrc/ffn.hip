@@ -24,6 +24,7 @@
 #include <cmath>
 
 #include "ffn_common.h"
+#include "route_common.h"
 
 namespace moe {
 
@@ -48,17 +49,65 @@ namespace moe {
 // never stored).  Measured per layer call (OLMoE-like): 36.4 -> 35.6 us at
 // one token; the plain form stays 1 us faster at two tokens and 0.5 us at
 // 4 and 16.
-template <bool BF16, int MT, int W, bool GO = false, bool PF = false>
+// VSEL > 0 (single-token calls, with PF): the block selects its own expert.
+// Every wave runs the router's top-k selection on the logit partials (V =
+// VSEL logits per lane, the same arithmetic as the router's selection), and
+// block slot s takes the s-th smallest selected expert id; block (0, 0)
+// writes the routing outputs (ids and weights in slot order, the grouping).
+// The routing arrays in rv are then written, not read, by this kernel.
+struct LayerSel {
+  const float *part;       // [nsplit, 1, E] logit partials
+  int nsplit, norm_topk;
+  const float *bias;       // [E] or null
+};
+
+template <bool BF16, int MT, int W, bool GO = false, bool PF = false, int VSEL = 0>
 __global__ __launch_bounds__(64 * W, MT == 1 ? 8 : 1) void gateup_swiglu_kernel(const void *__restrict__ xv,
                                                             const void *__restrict__ wgv,
                                                             const void *__restrict__ wuv,
                                                             RouteView rv, int H, int d_ff,
-                                                            float *__restrict__ hout) {
+                                                            float *__restrict__ hout,
+                                                            LayerSel sel = LayerSel{}) {
+  static_assert(VSEL == 0 || (PF && MT == 1 && !GO), "selection runs in the single-token form");
   __shared__ float red[W][2][MT][4][64];
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const bool slot = MT == 1 && rv.T <= 16;  // uniform
   int e, q0 = 0, ntok = 0;
-  if (slot) {
+  int pair_sel = 0;
+  if constexpr (VSEL > 0) {
+    int esel;
+    float wsel;
+    wave_topk<VSEL, false>(sel.part, (size_t)rv.E, sel.nsplit, sel.bias, rv.E, rv.top_k,
+                           sel.norm_topk, RosterArgs{}, 0, esel, wsel);
+    const int K = rv.top_k;
+    int rank = 0;  // lane r < K: how many picks have a smaller id (picks are distinct)
+    for (int r2 = 0; r2 < K; ++r2) rank += lane_value(esel, r2) < esel ? 1 : 0;
+    const int s = blockIdx.x;
+    const uint64_t m = __ballot(lane < K && rank == s);
+    if (m == 0ull) return;  // block-uniform (the grid holds K slots)
+    pair_sel = __ffsll((unsigned long long)m) - 1;
+    e = lane_value(esel, pair_sel);
+    ntok = 1;
+    if (blockIdx.x == 0 && blockIdx.y == 0 && wid == 0) {
+      int32_t *ids = const_cast<int32_t *>(rv.topk_ids);
+      float *wts = const_cast<float *>(rv.topk_w);
+      int32_t *act = const_cast<int32_t *>(rv.active);
+      int32_t *pbe = const_cast<int32_t *>(rv.pair_by_expert);
+      int32_t *off = const_cast<int32_t *>(rv.offsets);
+      if (lane < K) {
+        ids[lane] = esel;
+        wts[lane] = wsel;
+        act[rank] = esel;
+        pbe[rank] = lane;
+      }
+      for (int ee = lane; ee <= rv.E; ee += 64) {  // CSR: picks with a smaller id
+        int c = 0;
+        for (int r2 = 0; r2 < K; ++r2) c += lane_value(esel, r2) < ee ? 1 : 0;
+        off[ee] = c;
+      }
+      if (lane == 0) *const_cast<int32_t *>(rv.n_active) = K;
+    }
+  } else if (slot) {
     // every active expert holds <= T <= 16 tokens: work item == active slot
     // (s < min(E, P) <= E, so the slot's entry is read with the count)
     const int s = blockIdx.x;
@@ -100,7 +149,7 @@ __global__ __launch_bounds__(64 * W, MT == 1 ? 8 : 1) void gateup_swiglu_kernel(
       }
     };
     load_w(wv);
-    if (slot) {
+    if (VSEL == 0 && slot) {
       q0 = rv.begin(e);
       ntok = rv.end(e) - q0;
     }
@@ -111,7 +160,7 @@ __global__ __launch_bounds__(64 * W, MT == 1 ? 8 : 1) void gateup_swiglu_kernel(
 #pragma unroll
     for (int tl = 0; tl < MT; ++tl) {
       const int c = tl * 16 + r;
-      const int t = rv.pair_at(q0 + (c < ntok ? c : 0)) / rv.top_k;
+      const int t = VSEL > 0 ? 0 : rv.pair_at(q0 + (c < ntok ? c : 0)) / rv.top_k;
       xoff[tl] = ((uint32_t)t * (uint32_t)H + (uint32_t)g * (16 / EB)) * EB;
     }
     for (int s = wv; s < nsteps; s += W * U) {
@@ -234,7 +283,7 @@ __global__ __launch_bounds__(64 * W, MT == 1 ? 8 : 1) void gateup_swiglu_kernel(
         if (!GO) us += red[w][1][tl][rr][ln];
       }
       const int neuron = row0 + 4 * (ln >> 4) + rr;
-      const int p = rv.pair_at(q0 + c);
+      const int p = VSEL > 0 ? pair_sel : rv.pair_at(q0 + c);
       hout[(size_t)p * d_ff + neuron] = GO ? silu(gs) : silu(gs) * us;
     }
   }
@@ -1405,6 +1454,34 @@ static bool fused_topk_ok(const FfnArgs &a) {
          a.k_keep > 0 && a.k_keep < a.d_ff && a.top_k * a.k_keep <= kDownStage;
 }
 
+// The fused select + down kernel of the smallest batches (fused_topk_ok).
+static void launch_down_topk(const FfnArgs &a, const RouteView &rv, hipStream_t stream) {
+  const int sw = down_block_cols(a.T, a.H);
+  dim3 grid(a.T, a.H / sw);
+  int32_t *io = a.want_idx ? a.idx : nullptr;
+  timer_begin(kStageDownRows, stream);
+#define MOE_DK(BF, SWV, VV)                                                                   \
+  down_topk_token_kernel<BF, SWV, VV><<<grid, 1024, 0, stream>>>(a.w_down, a.h, rv, a.H, a.d_ff, \
+                                                               a.k_keep, a.accumulate, a.y, io, \
+                                                               a.xres, a.xnext)
+#define MOE_DK_V(BF, SWV)                                                                     \
+  switch (a.d_ff / 64) {                                                                      \
+  case 4: MOE_DK(BF, SWV, 4); break;                                                        \
+  case 8: MOE_DK(BF, SWV, 8); break;                                                        \
+  case 12: MOE_DK(BF, SWV, 12); break;                                                      \
+  case 16: MOE_DK(BF, SWV, 16); break;                                                      \
+  case 20: MOE_DK(BF, SWV, 20); break;                                                      \
+  case 24: MOE_DK(BF, SWV, 24); break;                                                      \
+  case 28: MOE_DK(BF, SWV, 28); break;                                                      \
+  default: MOE_DK(BF, SWV, 32); break;                                                      \
+  }
+  if (a.bf16) { if (sw == 128) { MOE_DK_V(true, 128) } else { MOE_DK_V(true, 64) } }
+  else { if (sw == 128) { MOE_DK_V(false, 128) } else { MOE_DK_V(false, 64) } }
+#undef MOE_DK_V
+#undef MOE_DK
+  timer_end(stream);
+}
+
 hipError_t launch_ffn_sparse(const FfnArgs &a, hipStream_t stream) {
   if (a.T == 0) return hipSuccess;
   if (zero_contribution(a, stream)) {
@@ -1414,34 +1491,41 @@ hipError_t launch_ffn_sparse(const FfnArgs &a, hipStream_t stream) {
   const RouteView rv = make_view(a);
   launch_gateup(a, rv, stream);
   if (fused_topk_ok(a)) {
-    const int sw = down_block_cols(a.T, a.H);
-    dim3 grid(a.T, a.H / sw);
-    int32_t *io = a.want_idx ? a.idx : nullptr;
-    timer_begin(kStageDownRows, stream);
-#define MOE_DK(BF, SWV, VV)                                                                   \
-  down_topk_token_kernel<BF, SWV, VV><<<grid, 1024, 0, stream>>>(a.w_down, a.h, rv, a.H, a.d_ff, \
-                                                                 a.k_keep, a.accumulate, a.y, io, \
-                                                                 a.xres, a.xnext)
-#define MOE_DK_V(BF, SWV)                                                                     \
-  switch (a.d_ff / 64) {                                                                      \
-    case 4: MOE_DK(BF, SWV, 4); break;                                                        \
-    case 8: MOE_DK(BF, SWV, 8); break;                                                        \
-    case 12: MOE_DK(BF, SWV, 12); break;                                                      \
-    case 16: MOE_DK(BF, SWV, 16); break;                                                      \
-    case 20: MOE_DK(BF, SWV, 20); break;                                                      \
-    case 24: MOE_DK(BF, SWV, 24); break;                                                      \
-    case 28: MOE_DK(BF, SWV, 28); break;                                                      \
-    default: MOE_DK(BF, SWV, 32); break;                                                      \
-  }
-    if (a.bf16) { if (sw == 128) { MOE_DK_V(true, 128) } else { MOE_DK_V(true, 64) } }
-    else { if (sw == 128) { MOE_DK_V(false, 128) } else { MOE_DK_V(false, 64) } }
-#undef MOE_DK_V
-#undef MOE_DK
-    timer_end(stream);
+    launch_down_topk(a, rv, stream);
     return hipGetLastError();
   }
   launch_mask(a, rv, a.idx, a.hact, nullptr, 0, stream);
   launch_down_token(a, rv, a.idx, a.hact, a.k_keep, stream);
+  return hipGetLastError();
+}
+
+// The single-token layer: logits, then gate/up blocks that select their
+// own expert from the logit partials (block (0, 0) writes the routing
+// outputs), then the down kernel with the mask.  The router's select-and-
+// group launch goes away; every output equals moe_route followed by
+// launch_ffn_sparse bit for bit (the selection is the router's own code).
+bool layer_t1_ok(const RouteArgs &r, const FfnArgs &a) {
+  return a.T == 1 && r.T == 1 && !a.implicit && r.roster.usage == nullptr && r.E <= 256 &&
+         a.E == r.E && a.top_k == r.top_k && fused_topk_ok(a);
+}
+
+hipError_t launch_layer_t1(const RouteArgs &r, const FfnArgs &a, hipStream_t stream) {
+  if (!layer_t1_ok(r, a)) return hipErrorInvalidValue;
+  const int nsplit = launch_router_logits(r, stream);
+  const RouteView rv = make_view(a);
+  const LayerSel sel{r.logits, nsplit, r.norm_topk, r.bias};
+  dim3 grid(a.top_k, a.d_ff / 16);
+  timer_begin(kStageGateup, stream);
+#define MOE_GS(BF, V)                                                                         \
+  gateup_swiglu_kernel<BF, 1, 8, false, true, V><<<grid, 512, 0, stream>>>(a.x, a.w_gate, a.w_up, \
+                                                                          rv, a.H, a.d_ff, a.h, sel)
+#define MOE_GS_V(BF) \
+  if (r.E <= 64) MOE_GS(BF, 1); else if (r.E <= 128) MOE_GS(BF, 2); else MOE_GS(BF, 4);
+  if (a.bf16) { MOE_GS_V(true) } else { MOE_GS_V(false) }
+#undef MOE_GS_V
+#undef MOE_GS
+  timer_end(stream);
+  launch_down_topk(a, rv, stream);
   return hipGetLastError();
 }
 

@@ -58,6 +58,9 @@ struct RouteArgs {
 constexpr int kRouterSplits = 8;
 int router_splits(int T, int H, int E, int bf16);
 hipError_t launch_route(const RouteArgs &a, hipStream_t stream);
+// The logits kernel alone (split-K partials into a.logits); returns the
+// number of splits.
+int launch_router_logits(const RouteArgs &a, hipStream_t stream);
 
 // One FFN call (routed group, or an implicit shared group).
 struct FfnArgs {
@@ -91,6 +94,11 @@ hipError_t launch_pack_gate_up(const void *src, void *dst, int E, int d_ff, int 
 // Rows of the dense-path down GEMM's partial buffer for calls of at most T tokens.
 size_t dense_down_partial_rows(int T, int E, int top_k, int H);
 hipError_t launch_ffn_sparse(const FfnArgs &a, hipStream_t stream);
+// A whole single-token layer (moe_route then launch_ffn_sparse, same bits)
+// in three kernels: logits, gate/up selecting its own expert, down with the
+// mask.  layer_t1_ok: whether these shapes take it.
+bool layer_t1_ok(const RouteArgs &r, const FfnArgs &a);
+hipError_t launch_layer_t1(const RouteArgs &r, const FfnArgs &a, hipStream_t stream);
 hipError_t launch_ffn_dense(const FfnArgs &a, hipStream_t stream);
 hipError_t launch_ffn_updown(const FfnArgs &a, hipStream_t stream);
 bool threshold_supported(int d_ff);

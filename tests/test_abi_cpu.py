@@ -168,6 +168,39 @@ def test_ffn_residual_validation():
     assert R(T=0, xr=None, xn=None, x=None, ws=None) == 0
 
 
+def test_layer_validation():
+    fn = L.moe_layer_sparse
+    d = _desc()
+
+    def Ly(dd=d, T=4, k=10, x=FAKE, wr=FAKE, bias=None, wg=FAKE, wd=FAKE, out="ok", y=FAKE,
+           acc=0, xr=None, xn=None, ws=FAKE, wsb=1 << 34):
+        r = B.MoeRouting(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE) if out == "ok" else out
+        return fn(ctypes.byref(dd) if dd is not None else None, T, k, x, wr, bias, wg, FAKE, wd,
+                  ctypes.byref(r) if r is not None else None, y, acc, None, xr, xn, ws, wsb, None)
+    assert Ly(xr=FAKE) == INV                   # x_res and x_next: both or neither
+    assert Ly(xn=FAKE) == INV
+    assert Ly(xr=MIS, xn=FAKE) == MISA
+    assert Ly(dd=None) == INV
+    assert Ly(T=-1) == INV
+    assert Ly(k=-1) == INV
+    assert Ly(k=1025) == INV
+    assert Ly(x=None) == INV
+    assert Ly(wr=None) == INV
+    assert Ly(wd=None) == INV
+    assert Ly(y=None) == INV
+    assert Ly(out=None) == INV
+    assert Ly(out=B.MoeRouting(FAKE, None, FAKE, FAKE, FAKE, FAKE)) == INV
+    assert Ly(bias=MIS + 1) == MISA
+    assert Ly(acc=2) == INV
+    assert Ly(ws=None) == WSP
+    assert Ly(ws=MIS) == MISA
+    need = B.moe_layer_workspace_size(d, 4, 10)
+    assert need >= B.moe_route_workspace_size(d, 4) + B.moe_ffn_workspace_size(d, 4, 10, 0)
+    assert Ly(wsb=need - 1) == WSP
+    assert B.moe_layer_workspace_size(d, 4, 1025) == 0
+    assert Ly(T=0, x=None, y=None, ws=None) == 0
+
+
 def test_threshold_and_calibration_validation():
     d = _desc()
     r = B.MoeRouting(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
