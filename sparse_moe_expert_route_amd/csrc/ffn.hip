@@ -35,6 +35,9 @@ namespace moe {
 // 16x16 MFMA accumulators for gate and up for MT token tiles; weights are
 // loaded once, token rows (16 B per lane) come from L2.  The wave partials
 // meet in LDS, where h = silu(g) * u is formed and written per pair.
+// Grid: x = neuron tile, y = item.  Blocks dispatch x-fastest, so every
+// tile of the occupied items starts first and the grid's unoccupied item
+// slots (sized from shapes, not from the routing) trail behind them.
 // The weight stream depends only on the item's expert, so a wave issues
 // its first round of weight loads before it resolves the item's tokens
 // (expert offsets, then the pair list): those dependent lookups overlap
@@ -82,13 +85,13 @@ __global__ __launch_bounds__(64 * W, MT == 1 ? 8 : 1) void gateup_swiglu_kernel(
     const int K = rv.top_k;
     int rank = 0;  // lane r < K: how many picks have a smaller id (picks are distinct)
     for (int r2 = 0; r2 < K; ++r2) rank += lane_value(esel, r2) < esel ? 1 : 0;
-    const int s = blockIdx.x;
+    const int s = blockIdx.y;
     const uint64_t m = __ballot(lane < K && rank == s);
     if (m == 0ull) return;  // block-uniform (the grid holds K slots)
     pair_sel = __ffsll((unsigned long long)m) - 1;
     e = lane_value(esel, pair_sel);
     ntok = 1;
-    if (blockIdx.x == 0 && blockIdx.y == 0 && wid == 0) {
+    if (blockIdx.y == 0 && blockIdx.x == 0 && wid == 0) {
       int32_t *ids = const_cast<int32_t *>(rv.topk_ids);
       float *wts = const_cast<float *>(rv.topk_w);
       int32_t *act = const_cast<int32_t *>(rv.active);
@@ -110,17 +113,17 @@ __global__ __launch_bounds__(64 * W, MT == 1 ? 8 : 1) void gateup_swiglu_kernel(
   } else if (slot) {
     // every active expert holds <= T <= 16 tokens: work item == active slot
     // (s < min(E, P) <= E, so the slot's entry is read with the count)
-    const int s = blockIdx.x;
+    const int s = blockIdx.y;
     const int na = rv.nact();
     e = rv.expert(s);
     if (s >= na) return;  // block-uniform
-  } else if (!find_item<16 * MT>(rv, blockIdx.x, e, q0, ntok)) {
+  } else if (!find_item<16 * MT>(rv, blockIdx.y, e, q0, ntok)) {
     return;  // block-uniform
   }
   const int r = lane & 15, g = lane >> 4;
-  const int row0 = blockIdx.y * 16;
+  const int row0 = blockIdx.x * 16;
   // packed weights: fragment (e, neuron tile, k-step) is 1 KB, lane-ordered
-  const size_t ftile = (size_t)e * (d_ff / 16) + blockIdx.y;
+  const size_t ftile = (size_t)e * (d_ff / 16) + blockIdx.x;
   constexpr int EB = BF16 ? 2 : 4;
   constexpr int KPS = BF16 ? 32 : 16;       // k per step (one 1 KB fragment)
   const int nsteps = H / KPS;
@@ -1393,7 +1396,7 @@ static void launch_gateup(const FfnArgs &a, const RouteView &rv, hipStream_t str
     // T <= 16: an item is an active-expert slot, at most min(E, P) of them;
     // past that an item is an expert and up to 16 of its tokens
     const int P = a.T * a.top_k;
-    dim3 grid(a.T <= 16 ? (a.implicit ? a.E : (a.E < P ? a.E : P)) : n_items(a, 16), a.d_ff / 16);
+    dim3 grid(a.d_ff / 16, a.T <= 16 ? (a.implicit ? a.E : (a.E < P ? a.E : P)) : n_items(a, 16));
 #define MOE_GU(BF, GOV, PFV) \
   gateup_swiglu_kernel<BF, 1, 8, GOV, PFV><<<grid, 512, 0, stream>>>(a.x, a.w_gate, a.w_up, rv, a.H, a.d_ff, a.h)
 #define MOE_GU_PF(BF, GOV) \
@@ -1514,7 +1517,7 @@ hipError_t launch_layer_t1(const RouteArgs &r, const FfnArgs &a, hipStream_t str
   const int nsplit = launch_router_logits(r, stream);
   const RouteView rv = make_view(a);
   const LayerSel sel{r.logits, nsplit, r.norm_topk, r.bias};
-  dim3 grid(a.top_k, a.d_ff / 16);
+  dim3 grid(a.d_ff / 16, a.top_k);
   timer_begin(kStageGateup, stream);
 #define MOE_GS(BF, V)                                                                         \
   gateup_swiglu_kernel<BF, 1, 8, false, true, V><<<grid, 512, 0, stream>>>(a.x, a.w_gate, a.w_up, \
