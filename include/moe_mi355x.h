@@ -212,10 +212,10 @@ moe_status moe_expert_ffn_sparse_residual(const moe_desc *d, int32_t T, int32_t 
  * when x_res and x_next are given (both or neither; then the layer's last
  * FFN call), with the same outputs bit for bit (routing_out filled as
  * moe_route fills it, y as the FFN call writes it).
- * For a single token (T == 1, E <= 256, 0 < k_keep < d_ff and the shapes
- * of the small-batch select) it runs as three kernels instead of four: the
- * gate/up blocks repeat the router's top-k selection on the logits and each
- * takes its own expert, so the select-and-group launch goes away (the page
+ * Up to 2 tokens (E <= 256, top_k <= 16, k_keep > 0) the gate/up blocks
+ * repeat the router's top-k selection on the logits (one wave per token)
+ * and each takes its own expert, so the select-and-group launch goes away
+ * (three kernels instead of four; the page
  * asks its integration to work with kernel fusion and graph capture:
  * technical summary, Key contributions); other calls run the two calls'
  * kernels in turn.  Arguments as moe_route and moe_expert_ffn_sparse; one

@@ -250,8 +250,8 @@ moe_status run_ffn(RunMode mode, const moe_desc *d, int32_t T, int32_t k_keep, c
       break;
     case kRunDense: e = moe::launch_ffn_dense(a, stream); break;
     default:
-      if (m.layer_route && moe::layer_t1_ok(*m.layer_route, a)) {
-        e = moe::launch_layer_t1(*m.layer_route, a, stream);
+      if (m.layer_route && moe::layer_small_ok(*m.layer_route, a)) {
+        e = moe::launch_layer_small(*m.layer_route, a, stream);
       } else {
         e = m.layer_route ? moe::launch_route(*m.layer_route, stream) : hipSuccess;
         if (e == hipSuccess) e = moe::launch_ffn_sparse(a, stream);

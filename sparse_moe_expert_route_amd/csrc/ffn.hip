@@ -52,17 +52,26 @@ namespace moe {
 // never stored).  Measured per layer call (OLMoE-like): 36.4 -> 35.6 us at
 // one token; the plain form stays 1 us faster at two tokens and 0.5 us at
 // 4 and 16.
-// VSEL > 0 (single-token calls, with PF): the block selects its own expert.
-// Every wave runs the router's top-k selection on the logit partials (V =
-// VSEL logits per lane, the same arithmetic as the router's selection), and
-// block slot s takes the s-th smallest selected expert id; block (0, 0)
-// writes the routing outputs (ids and weights in slot order, the grouping).
-// The routing arrays in rv are then written, not read, by this kernel.
+// VSEL > 0 (calls of T <= W tokens): the block selects its own expert.
+// Wave t < T runs the router's top-k selection for token t on the logit
+// partials (V = VSEL logits per lane, the router's own device function, so
+// the same bits); the picks meet in LDS as per-token lists, a bitmask of
+// the picked experts and per-expert counts.  Block slot s takes the s-th
+// smallest picked expert id and its tokens in ascending order; block
+// (0, 0) writes the routing outputs (ids and weights in slot order, the
+// grouping sorted by (expert, pair)).  The routing arrays in rv are then
+// written, not read, by this kernel.
 struct LayerSel {
-  const float *part;       // [nsplit, 1, E] logit partials
+  const float *part;       // [nsplit, T, E] logit partials
   int nsplit, norm_topk;
   const float *bias;       // [E] or null
 };
+
+// Position of the n-th (0-based) set bit of w; w has more than n set bits.
+__device__ __forceinline__ int nth_set_bit(uint64_t w, int n) {
+  for (int i = 0; i < n; ++i) w &= w - 1;
+  return __ffsll((unsigned long long)w) - 1;
+}
 
 template <bool BF16, int MT, int W, bool GO = false, bool PF = false, int VSEL = 0>
 __global__ __launch_bounds__(64 * W, MT == 1 ? 8 : 1) void gateup_swiglu_kernel(const void *__restrict__ xv,
@@ -71,44 +80,91 @@ __global__ __launch_bounds__(64 * W, MT == 1 ? 8 : 1) void gateup_swiglu_kernel(
                                                             RouteView rv, int H, int d_ff,
                                                             float *__restrict__ hout,
                                                             LayerSel sel = LayerSel{}) {
-  static_assert(VSEL == 0 || (PF && MT == 1 && !GO), "selection runs in the single-token form");
+  static_assert(VSEL == 0 || (MT == 1 && !GO), "selection runs in the one-tile form");
   __shared__ float red[W][2][MT][4][64];
+  __shared__ int32_t s_pairc[16];  // VSEL: the pair of each tile column
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const bool slot = MT == 1 && rv.T <= 16;  // uniform
-  int e, q0 = 0, ntok = 0;
-  int pair_sel = 0;
+  int e = 0, q0 = 0, ntok = 0;
+  int xtok = 0;  // VSEL: the token of tile column lane & 15
   if constexpr (VSEL > 0) {
-    int esel;
-    float wsel;
-    wave_topk<VSEL, false>(sel.part, (size_t)rv.E, sel.nsplit, sel.bias, rv.E, rv.top_k,
-                           sel.norm_topk, RosterArgs{}, 0, esel, wsel);
-    const int K = rv.top_k;
-    int rank = 0;  // lane r < K: how many picks have a smaller id (picks are distinct)
-    for (int r2 = 0; r2 < K; ++r2) rank += lane_value(esel, r2) < esel ? 1 : 0;
+    __shared__ int32_t s_pick[W][16];
+    __shared__ uint32_t s_mask[8];
+    __shared__ int32_t s_cnt[256 + 1];
+    const int T = rv.T, K = rv.top_k, E = rv.E;
+    const bool writer = blockIdx.x == 0 && blockIdx.y == 0;  // uniform
+    if (threadIdx.x < 8) s_mask[threadIdx.x] = 0u;
+    if (writer)
+      for (int i = threadIdx.x; i < E; i += 64 * W) s_cnt[i] = 0;
+    __syncthreads();
+    if (wid < T) {  // wave-uniform
+      int esel;
+      float wsel;
+      wave_topk<VSEL, false>(sel.part + (size_t)wid * E, (size_t)T * E, sel.nsplit, sel.bias, E, K,
+                             sel.norm_topk, RosterArgs{}, wid, esel, wsel);
+      if (lane < K) {
+        s_pick[wid][lane] = esel;
+        atomicOr(&s_mask[esel >> 5], 1u << (esel & 31));
+        if (writer) {
+          atomicAdd(&s_cnt[esel], 1);
+          const_cast<int32_t *>(rv.topk_ids)[wid * K + lane] = esel;
+          const_cast<float *>(rv.topk_w)[wid * K + lane] = wsel;
+        }
+      }
+    }
+    __syncthreads();
+    // the slot's expert: the s-th smallest picked id (lanes 0..7 hold the mask words)
     const int s = blockIdx.y;
-    const uint64_t m = __ballot(lane < K && rank == s);
-    if (m == 0ull) return;  // block-uniform (the grid holds K slots)
-    pair_sel = __ffsll((unsigned long long)m) - 1;
-    e = lane_value(esel, pair_sel);
-    ntok = 1;
-    if (blockIdx.y == 0 && blockIdx.x == 0 && wid == 0) {
-      int32_t *ids = const_cast<int32_t *>(rv.topk_ids);
-      float *wts = const_cast<float *>(rv.topk_w);
+    const uint32_t mw = lane < 8 ? s_mask[lane] : 0u;
+    const int cw = __popc(mw);
+    const int incl = wave_incl_scan(cw);
+    const int nact = lane_value(incl, 63);
+    if (s >= nact) return;  // block-uniform
+    const uint64_t wsel_m = __ballot(lane < 8 && incl > s && incl - cw <= s);
+    const int L = __ffsll((unsigned long long)wsel_m) - 1;
+    e = 32 * L + nth_set_bit(lane_value((int)mw, L), s - (lane_value(incl, L) - lane_value(cw, L)));
+    // its tokens, ascending: lane t < T holds the slot of e in token t's picks
+    int my_slot = -1;
+    if (lane < T)
+      for (int r2 = 0; r2 < K; ++r2) my_slot = s_pick[lane][r2] == e ? r2 : my_slot;
+    const uint64_t tm = __ballot(lane < T && my_slot >= 0);
+    ntok = __popcll(tm);
+    const int c = lane & 15;
+    const int tc = nth_set_bit(tm, c < ntok ? c : 0);
+    xtok = tc;
+    const int pc = tc * K + __shfl(my_slot, tc, 64);  // tc varies by lane: a permute, not a readlane
+    if (wid == 0 && lane < 16) s_pairc[lane] = pc;  // read after the reduction barrier
+    if (writer && wid == 0) {
+      // grouping: CSR offsets, ascending active list, pairs by (expert, pair id)
+      int32_t *off = const_cast<int32_t *>(rv.offsets);
       int32_t *act = const_cast<int32_t *>(rv.active);
       int32_t *pbe = const_cast<int32_t *>(rv.pair_by_expert);
-      int32_t *off = const_cast<int32_t *>(rv.offsets);
-      if (lane < K) {
-        ids[lane] = esel;
-        wts[lane] = wsel;
-        act[rank] = esel;
-        pbe[rank] = lane;
+      int base = 0, abase = 0;
+      for (int e0 = 0; e0 < E; e0 += 64) {
+        const int ee = e0 + lane;
+        const int cnt = ee < E ? s_cnt[ee] : 0;
+        const int ci = wave_incl_scan(cnt);
+        const int fi = wave_incl_scan(cnt > 0 ? 1 : 0);
+        if (ee < E) {
+          off[ee] = base + ci - cnt;
+          s_cnt[ee] = base + ci - cnt;  // becomes the expert's cursor
+        }
+        if (cnt > 0) act[abase + fi - 1] = ee;
+        base += lane_value(ci, 63);
+        abase += lane_value(fi, 63);
       }
-      for (int ee = lane; ee <= rv.E; ee += 64) {  // CSR: picks with a smaller id
-        int c = 0;
-        for (int r2 = 0; r2 < K; ++r2) c += lane_value(esel, r2) < ee ? 1 : 0;
-        off[ee] = c;
+      if (lane == 0) {
+        off[E] = base;
+        *const_cast<int32_t *>(rv.n_active) = abase;
       }
-      if (lane == 0) *const_cast<int32_t *>(rv.n_active) = K;
+      for (int t = 0; t < T; ++t) {  // tokens in order: each expert's pairs ascend
+        if (lane < K) {
+          const int ee = s_pick[t][lane];
+          const int at = s_cnt[ee];
+          s_cnt[ee] = at + 1;  // distinct experts within a token
+          pbe[at] = t * K + lane;
+        }
+      }
     }
   } else if (slot) {
     // every active expert holds <= T <= 16 tokens: work item == active slot
@@ -163,7 +219,7 @@ __global__ __launch_bounds__(64 * W, MT == 1 ? 8 : 1) void gateup_swiglu_kernel(
 #pragma unroll
     for (int tl = 0; tl < MT; ++tl) {
       const int c = tl * 16 + r;
-      const int t = VSEL > 0 ? 0 : rv.pair_at(q0 + (c < ntok ? c : 0)) / rv.top_k;
+      const int t = VSEL > 0 ? xtok : rv.pair_at(q0 + (c < ntok ? c : 0)) / rv.top_k;
       xoff[tl] = ((uint32_t)t * (uint32_t)H + (uint32_t)g * (16 / EB)) * EB;
     }
     for (int s = wv; s < nsteps; s += W * U) {
@@ -213,7 +269,7 @@ __global__ __launch_bounds__(64 * W, MT == 1 ? 8 : 1) void gateup_swiglu_kernel(
       }
     };
     load_round(wid);
-    if (slot) {
+    if (VSEL == 0 && slot) {
       q0 = rv.begin(e);
       ntok = rv.end(e) - q0;
     }
@@ -224,7 +280,7 @@ __global__ __launch_bounds__(64 * W, MT == 1 ? 8 : 1) void gateup_swiglu_kernel(
     for (int tl = 0; tl < MT; ++tl) {
       const int c = tl * 16 + r;
       xval[tl] = c < ntok;
-      const int t = xval[tl] ? rv.pair_at(q0 + c) / rv.top_k : 0;
+      const int t = !xval[tl] ? 0 : VSEL > 0 ? xtok : rv.pair_at(q0 + c) / rv.top_k;
       xoff[tl] = (size_t)t * H;
     }
     for (int s = wid; s < nsteps; s += W * U) {
@@ -286,7 +342,7 @@ __global__ __launch_bounds__(64 * W, MT == 1 ? 8 : 1) void gateup_swiglu_kernel(
         if (!GO) us += red[w][1][tl][rr][ln];
       }
       const int neuron = row0 + 4 * (ln >> 4) + rr;
-      const int p = VSEL > 0 ? pair_sel : rv.pair_at(q0 + c);
+      const int p = VSEL > 0 ? s_pairc[c] : rv.pair_at(q0 + c);
       hout[(size_t)p * d_ff + neuron] = GO ? silu(gs) : silu(gs) * us;
     }
   }
@@ -1502,33 +1558,52 @@ hipError_t launch_ffn_sparse(const FfnArgs &a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// The single-token layer: logits, then gate/up blocks that select their
+// Layers of up to 8 tokens: logits, then gate/up blocks that select their
 // own expert from the logit partials (block (0, 0) writes the routing
-// outputs), then the down kernel with the mask.  The router's select-and-
-// group launch goes away; every output equals moe_route followed by
-// launch_ffn_sparse bit for bit (the selection is the router's own code).
-bool layer_t1_ok(const RouteArgs &r, const FfnArgs &a) {
-  return a.T == 1 && r.T == 1 && !a.implicit && r.roster.usage == nullptr && r.E <= 256 &&
-         a.E == r.E && a.top_k == r.top_k && fused_topk_ok(a);
+// outputs), then the mask and down kernels as launch_ffn_sparse runs them.
+// The router's select-and-group launch goes away; every output equals
+// moe_route followed by launch_ffn_sparse bit for bit (the selection is the
+// router's own code, the grouping its stable order).
+// One gate/up wave per token, so up to 8 tokens can select in-kernel; it
+// pays only up to 2 (measured per layer call, OLMoE-like: 45.6-47.1 ->
+// 44.4 us at 2 tokens, but 62.4 -> 62.8 us at 4 and 84.1 -> 89.2 us at 8,
+// where every block rereads T tokens' logit partials and waits on T
+// selections; 1 token stays within noise).  The selection code is
+// parity-tested up to 8 tokens.
+constexpr int kLayerSelMaxTokens = 2;
+bool layer_small_ok(const RouteArgs &r, const FfnArgs &a) {
+  return a.T >= 1 && a.T <= kLayerSelMaxTokens && r.T == a.T && !a.implicit &&
+         r.roster.usage == nullptr && r.E <= 256 && a.E == r.E && a.top_k == r.top_k &&
+         a.top_k <= 16 && a.k_keep > 0;
 }
 
-hipError_t launch_layer_t1(const RouteArgs &r, const FfnArgs &a, hipStream_t stream) {
-  if (!layer_t1_ok(r, a)) return hipErrorInvalidValue;
+hipError_t launch_layer_small(const RouteArgs &r, const FfnArgs &a, hipStream_t stream) {
+  if (!layer_small_ok(r, a)) return hipErrorInvalidValue;
   const int nsplit = launch_router_logits(r, stream);
   const RouteView rv = make_view(a);
   const LayerSel sel{r.logits, nsplit, r.norm_topk, r.bias};
-  dim3 grid(a.d_ff / 16, a.top_k);
+  const int P = a.T * a.top_k;
+  dim3 grid(a.d_ff / 16, a.E < P ? a.E : P);
   timer_begin(kStageGateup, stream);
-#define MOE_GS(BF, V)                                                                         \
-  gateup_swiglu_kernel<BF, 1, 8, false, true, V><<<grid, 512, 0, stream>>>(a.x, a.w_gate, a.w_up, \
-                                                                          rv, a.H, a.d_ff, a.h, sel)
-#define MOE_GS_V(BF) \
-  if (r.E <= 64) MOE_GS(BF, 1); else if (r.E <= 128) MOE_GS(BF, 2); else MOE_GS(BF, 4);
-  if (a.bf16) { MOE_GS_V(true) } else { MOE_GS_V(false) }
+#define MOE_GS(BF, PFV, V)                                                                      \
+  gateup_swiglu_kernel<BF, 1, 8, false, PFV, V><<<grid, 512, 0, stream>>>(a.x, a.w_gate, a.w_up, \
+                                                                         rv, a.H, a.d_ff, a.h, sel)
+#define MOE_GS_V(BF, PFV) \
+  if (r.E <= 64) MOE_GS(BF, PFV, 1); else if (r.E <= 128) MOE_GS(BF, PFV, 2); else MOE_GS(BF, PFV, 4);
+  if (a.bf16) {
+    if (a.T == 1) { MOE_GS_V(true, true) } else { MOE_GS_V(true, false) }
+  } else {
+    if (a.T == 1) { MOE_GS_V(false, true) } else { MOE_GS_V(false, false) }
+  }
 #undef MOE_GS_V
 #undef MOE_GS
   timer_end(stream);
-  launch_down_topk(a, rv, stream);
+  if (fused_topk_ok(a)) {
+    launch_down_topk(a, rv, stream);
+  } else {
+    launch_mask(a, rv, a.idx, a.hact, nullptr, 0, stream);
+    launch_down_token(a, rv, a.idx, a.hact, a.k_keep, stream);
+  }
   return hipGetLastError();
 }
 

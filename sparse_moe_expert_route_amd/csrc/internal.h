@@ -94,11 +94,12 @@ hipError_t launch_pack_gate_up(const void *src, void *dst, int E, int d_ff, int 
 // Rows of the dense-path down GEMM's partial buffer for calls of at most T tokens.
 size_t dense_down_partial_rows(int T, int E, int top_k, int H);
 hipError_t launch_ffn_sparse(const FfnArgs &a, hipStream_t stream);
-// A whole single-token layer (moe_route then launch_ffn_sparse, same bits)
-// in three kernels: logits, gate/up selecting its own expert, down with the
-// mask.  layer_t1_ok: whether these shapes take it.
-bool layer_t1_ok(const RouteArgs &r, const FfnArgs &a);
-hipError_t launch_layer_t1(const RouteArgs &r, const FfnArgs &a, hipStream_t stream);
+// A whole small-batch layer (moe_route then launch_ffn_sparse, same bits)
+// without the router's select-and-group launch: logits, gate/up selecting
+// its own expert, then mask and down.  layer_small_ok: whether these shapes
+// take it.
+bool layer_small_ok(const RouteArgs &r, const FfnArgs &a);
+hipError_t launch_layer_small(const RouteArgs &r, const FfnArgs &a, hipStream_t stream);
 hipError_t launch_ffn_dense(const FfnArgs &a, hipStream_t stream);
 hipError_t launch_ffn_updown(const FfnArgs &a, hipStream_t stream);
 bool threshold_supported(int d_ff);

@@ -1,7 +1,9 @@
 """GPU tests of moe_layer_sparse: moe_route then moe_expert_ffn_sparse in one
-call.  At one token the gate/up kernel repeats the router's selection and the
-select-and-group launch goes away; every output must equal the two calls'
-bits (routing outputs, kept ids, y), also when captured in a graph."""
+call.  Up to 2 tokens the gate/up kernel repeats the router's selection (one
+wave per token) and the select-and-group launch goes away; every output must
+equal the two calls' bits (routing outputs, kept ids, y), also when captured
+in a graph.  Larger batches run the two calls' kernels through the same
+entry point."""
 import numpy as np
 import pytest
 import torch
@@ -53,7 +55,8 @@ def _run(L, shape, T, k, fused, acc=0, y0=None):
 
 
 @pytest.mark.parametrize("key", list(SHAPES))
-@pytest.mark.parametrize("T,s", [(1, 0.9), (1, 0.5), (4, 0.9), (1, 0.0)])
+@pytest.mark.parametrize("T,s", [(1, 0.9), (1, 0.5), (2, 0.9), (4, 0.9), (5, 0.9), (8, 0.9),
+                                 (8, 0.0), (1, 0.0), (16, 0.9)])
 def test_layer_matches_route_then_ffn(key, T, s):
     name, over = SHAPES[key]
     shape = S.LAYERS[name].with_(**over) if over else S.LAYERS[name]
@@ -111,7 +114,7 @@ def test_layer_graph_replays():
         torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("T", [1, 16])
+@pytest.mark.parametrize("T", [1, 6, 16])
 def test_layer_with_residual(T):
     # x_next = x + y in the down epilogue: equals route, FFN, then moe_residual_add
     shape = S.LAYERS["olmoe-like"]
