@@ -739,10 +739,9 @@ __global__ __launch_bounds__(64) void up_rows_var_kernel(const void *__restrict_
 // at column colo.  Wave wid takes row groups wid, wid + kDownWaves, ...
 // (RPI rows per group, one per LPR-lane slice) and issues U groups' 16-byte
 // loads before folding any of them into acc, so a lane has up to U loads in
-// flight.  U is 8 when a wave has more than 4 load instructions to issue,
-// else 4: a round costs a full HBM latency, so deeper rounds mean fewer of
-// them (8 keeps a slot's data, address and coefficient within the 128
-// VGPRs of a 1024-thread block without spills).
+// flight.  U = 4: deeper rounds (8) measured no faster at decode batches
+// and raise the kernels to ~78 VGPRs, which halves the blocks a CU holds
+// at large batches (Llama-4-like T = 256 sparse: 1082 -> 1156 us).
 constexpr int kDownWaves = 16;
 constexpr int kDownStage = 4096;     // row-list entries staged in LDS
 
@@ -800,12 +799,7 @@ template <bool BF16, int SW>
 __device__ __forceinline__ void stream_rows(const void *__restrict__ wdv, const uint32_t *srow,
                                             const float *scoef, int n, int H, size_t colo,
                                             int wid, int rsel, float (&acc)[BF16 ? 8 : 4]) {
-  constexpr int RPI = 64 / (SW / (BF16 ? 8 : 4));
-  const int per_wave = (n + kDownWaves * RPI - 1) / (kDownWaves * RPI);  // uniform
-  if (per_wave > 4)
-    stream_rows_u<BF16, SW, 8>(wdv, srow, scoef, n, H, colo, wid, rsel, acc);
-  else
-    stream_rows_u<BF16, SW, 4>(wdv, srow, scoef, n, H, colo, wid, rsel, acc);
+  stream_rows_u<BF16, SW, 4>(wdv, srow, scoef, n, H, colo, wid, rsel, acc);
 }
 
 // y[t, cols] (+)= sum over the token's pairs (slot order) and their kept rows
