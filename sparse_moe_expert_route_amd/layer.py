@@ -1,8 +1,9 @@
 """MoELayer: the decode MoE layer as a sequence of C-ABI calls.
 
 route -> routed experts (sparse or dense path, overwriting y) -> always-on
-shared experts (accumulating into y).  Torch provides device memory and the
-stream; every step runs in libmoe_mi355x's kernels.
+shared experts (accumulating into y); on the sparse path the first two run
+as one moe_layer_sparse call.  Torch provides device memory and the stream;
+every step runs in libmoe_mi355x's kernels.
 """
 from __future__ import annotations
 
@@ -60,11 +61,17 @@ class MoELayer:
         d = self.desc
         if y is None:
             y = torch.empty((T, d.hidden), dtype=torch.float32, device=x.device)
-        routing = self.route(x, routing)
         path = self.select_path(T, k_keep) if path is None else path
-        fn = B.moe_expert_ffn_sparse if path == B.MOE_PATH_SPARSE else B.moe_expert_ffn_dense
-        ws = self._workspace(("ffn", path), B.moe_ffn_workspace_size(d, T, k_keep, path), x.device)
-        fn(d, T, k_keep, x, *self.w, routing, y, 0, active_idx, ws)
+        if path == B.MOE_PATH_SPARSE:   # route + routed FFN in one call
+            routing = routing or B.Routing.allocate(T, d.top_k, d.n_experts, x.device)
+            ws = self._workspace("layer", B.moe_layer_workspace_size(d, T, k_keep), x.device)
+            B.moe_layer_sparse(d, T, k_keep, x, self.w_router, self.bias, *self.w, routing, y, 0,
+                               active_idx, ws)
+        else:
+            routing = self.route(x, routing)
+            ws = self._workspace(("ffn", path), B.moe_ffn_workspace_size(d, T, k_keep, path),
+                                 x.device)
+            B.moe_expert_ffn_dense(d, T, k_keep, x, *self.w, routing, y, 0, active_idx, ws)
         if self.shared is not None:
             ds = self.desc_shared
             ks = ds.d_ff if k_keep_shared is None else k_keep_shared

@@ -468,16 +468,18 @@ def test_errors_leave_outputs_untouched():
     assert torch.all(y == 7.0)
 
 
-def test_layer_class_matches_direct_calls():
+@pytest.mark.parametrize("T", [1, 2, 4])
+def test_layer_class_matches_direct_calls(T):
+    # MoELayer runs moe_layer_sparse (the selection inside gate/up at T <= 2)
     from sparse_moe_expert_route_amd.layer import MoELayer
     inp, dev = layer("deepseek-v2-like")
     sh = inp.shape
-    x_host = inp.tokens(4, 11)
+    x_host = inp.tokens(T, 11)
     k, k_sh = O.keep_count(0.9, sh.d_ff), O.keep_count(0.5, sh.d_ff_shared)
     m = MoELayer(hidden=sh.hidden, n_experts=sh.n_experts, d_ff=sh.d_ff, top_k=sh.top_k,
                  norm_topk=sh.norm_topk, dtype=sh.dtype, w_router=dev.w_router,
                  w_gate=dev.w[0], w_up=dev.w[1], w_down=dev.w[2], shared=dev.w_sh, packed=True)
-    say("[case] MoELayer deepseek-v2-like T=4")
+    say(f"[case] MoELayer deepseek-v2-like T={T}")
     y = m.forward(to_dev(x_host), k, k_sh, path=SP, path_shared=SP)
     got = dev.run(x_host, k, SP, k_sh, SP)
     torch.cuda.synchronize()
