@@ -90,7 +90,8 @@ class Workload:
         self.B, self.torch = B, torch
         self.shape, self.T = shape, T
         sh = shape
-        self.desc = B.make_desc(sh.hidden, sh.n_experts, sh.d_ff, sh.top_k, sh.norm_topk, sh.dtype)
+        self.desc = B.make_desc(sh.hidden, sh.n_experts, sh.d_ff, sh.top_k, sh.norm_topk, sh.dtype,
+                                gate_up_layout="packed")
         self.k = B.moe_keep_count(sparsity, sh.d_ff)
         forced = {"sparse": B.MOE_PATH_SPARSE, "dense": B.MOE_PATH_DENSE}.get(path_arg)
         self.auto_path = B.moe_select_path(self.desc, T, self.k)
@@ -103,7 +104,8 @@ class Workload:
         self.desc_sh = None
         if dev_sh0 is not None:
             n_sh, d_sh = sh.n_shared, sh.d_ff_shared
-            self.desc_sh = B.make_desc(sh.hidden, n_sh, d_sh, n_sh, False, sh.dtype)
+            self.desc_sh = B.make_desc(sh.hidden, n_sh, d_sh, n_sh, False, sh.dtype,
+                                       gate_up_layout="packed")
             s_sh = sparsity if sparsity_shared is None else sparsity_shared
             self.k_sh = B.moe_keep_count(s_sh, d_sh)
             self.auto_path_sh = B.moe_select_path(self.desc_sh, T, self.k_sh)
@@ -372,7 +374,8 @@ def roster_variant(shape, host, dev_w0, T=16, m=8, seq_len=256, deltas=(1.0, 2.0
     import moe_synth as S
     from sparse_moe_expert_route_amd import binding as B
     E, K = shape.n_experts, shape.top_k
-    desc = B.make_desc(shape.hidden, E, shape.d_ff, K, shape.norm_topk, shape.dtype)
+    desc = B.make_desc(shape.hidden, E, shape.d_ff, K, shape.norm_topk, shape.dtype,
+                       gate_up_layout="packed")
     wr = dev_w0[0]
     xs = [host.to_dev(S.tokens(shape, 2000 + i, T)) for i in range(seq_len)]
     R = B.Routing.allocate(T, K, E)
@@ -417,7 +420,7 @@ def decode_step_variant(shape, args, n_layers=8, batches=(1, 16)):
     import moe_synth as S
     from sparse_moe_expert_route_amd import binding as B
     desc = B.make_desc(shape.hidden, shape.n_experts, shape.d_ff, shape.top_k, shape.norm_topk,
-                       shape.dtype)
+                       shape.dtype, gate_up_layout="packed")
     to_dev = HostLayer.to_dev
     layers = []
     for s in range(n_layers):
@@ -499,8 +502,11 @@ def cpu_baseline(shape, host, wl, seconds):
     """The oracle as it stands, on the host, over a bounded sample of steps."""
     import oracle
     import threadpoolctl
+    # the host cores this process may run on, and the BLAS pool the oracle's
+    # products actually use (the box caps pools by OMP_NUM_THREADS)
+    cores = len(os.sched_getaffinity(0))
     info = threadpoolctl.threadpool_info()
-    cores = max([i.get("num_threads", 1) for i in info] or [1])
+    blas_threads = max([i.get("num_threads", 1) for i in info] or [1])
     import numpy as np
     T = wl.T
     wl.step(0)                           # the timed batch 0 once more, for the parity check
@@ -543,7 +549,7 @@ def cpu_baseline(shape, host, wl, seconds):
     # window rule; this is a sanity gate on the timed workload)
     rel = float(np.linalg.norm(y_gpu - y_first) / max(np.linalg.norm(y_first), 1e-300))
     out = {"value": round(med * 1e6 / T, 1), "unit": "us/token", "cores": int(cores),
-           "kind": "oracle",
+           "blas_threads": int(blas_threads), "kind": "oracle",
            "sample": f"{done} layer calls of {T} tokens ({done * T} tokens) of the same layer, "
                      f"{el:.1f} s, float64 numpy oracle; value = median call / T",
            "tokens_per_s": round(T / med, 2),
@@ -730,13 +736,14 @@ def calibrate_copy():
 
 def dev_layer(shape, host, B):
     desc = B.make_desc(shape.hidden, shape.n_experts, shape.d_ff, shape.top_k, shape.norm_topk,
-                       shape.dtype)
+                       shape.dtype, gate_up_layout="packed")
     dev_w0 = (host.to_dev(host.w_router), B.moe_pack_gate_up(desc, host.to_dev(host.wg)),
               B.moe_pack_gate_up(desc, host.to_dev(host.wu)), host.to_dev(host.wd))
     dev_sh0 = None
     if host.shared is not None:
         n_sh = shape.n_shared
-        dsh = B.make_desc(shape.hidden, n_sh, shape.d_ff_shared, n_sh, False, shape.dtype)
+        dsh = B.make_desc(shape.hidden, n_sh, shape.d_ff_shared, n_sh, False, shape.dtype,
+                          gate_up_layout="packed")
         g, u, d = host.shared
         dev_sh0 = (B.moe_pack_gate_up(dsh, host.to_dev(g)), B.moe_pack_gate_up(dsh, host.to_dev(u)),
                    host.to_dev(d))

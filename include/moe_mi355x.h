@@ -27,14 +27,18 @@
  *   failed; the stream's contents are then unspecified.
  * - T == 0 is a valid no-op returning MOE_OK.
  * - NaN or Inf in x or weights gives unspecified (but memory-safe) results.
- * - Every tensor base pointer must be 16-byte aligned (MOE_ERR_MISALIGNED).
+ * - Every tensor base pointer must be 16-byte aligned (MOE_ERR_MISALIGNED);
+ *   256-byte aligned pointers (torch's allocations) always qualify.
  * - Layouts are row-major.  Expert weights are [E, d_ff, H] NEURON-MAJOR for
  *   gate, up AND down: row j of the down matrix is neuron j's H-vector
  *   contribution (the transpose of a torch down_proj.weight [H, d_ff]), so
  *   a kept neuron's down row is one contiguous H * elem_bytes stream.
  *   The FFN calls read gate and up in the PACKED layout that
  *   moe_pack_gate_up produces from that row-major form (once, at load time);
- *   down and the router matrix stay row-major.
+ *   down and the router matrix stay row-major.  The descriptor says which
+ *   layout the caller passes (moe_desc.gate_up_layout): a descriptor left at
+ *   MOE_LAYOUT_ROWMAJOR (zero) is refused by every FFN call with
+ *   MOE_ERR_UNSUPPORTED, so an unpacked tensor is never misread.
  * - dtype MOE_BF16: x, router and expert weights are bf16 (raw bits,
  *   round-to-nearest-even), every accumulation is fp32; MOE_F32: all fp32.
  *   Router logits, softmax weights, h and y are fp32 in both.
@@ -66,6 +70,10 @@ typedef enum {
 
 typedef enum { MOE_PATH_SPARSE = 0, MOE_PATH_DENSE = 1 } moe_path;
 
+/* Layout of the gate (and up) tensors a caller passes to the FFN calls.
+ * ROWMAJOR: [E, d_ff, H] as loaded; PACKED: after moe_pack_gate_up. */
+typedef enum { MOE_LAYOUT_ROWMAJOR = 0, MOE_LAYOUT_PACKED = 1 } moe_layout;
+
 /* Limits (MOE_ERR_UNSUPPORTED outside them). */
 #define MOE_MAX_HIDDEN 16384   /* H: multiple of 64                        */
 #define MOE_MAX_EXPERTS 1024   /* E                                        */
@@ -82,6 +90,11 @@ typedef struct {
                          it must equal n_experts                                  */
   int32_t norm_topk;  /* 1: renormalise the selected softmax weights to sum 1    */
   int32_t dtype;      /* moe_dtype                                                */
+  int32_t gate_up_layout; /* moe_layout of w_gate, and of w_up where the call reads
+                             it densely; the FFN calls need MOE_LAYOUT_PACKED (else
+                             MOE_ERR_UNSUPPORTED); moe_route and the packing calls
+                             ignore it; a value outside moe_layout ->
+                             MOE_ERR_INVALID_ARG                                   */
 } moe_desc;
 
 /* Routing of a token batch, written by moe_route, read by the FFN calls.
@@ -402,9 +415,19 @@ size_t moe_ffn_workspace_size(const moe_desc *d, int32_t T, int32_t k_keep, moe_
 size_t moe_ffn_threshold_workspace_size(const moe_desc *d, int32_t T);
 size_t moe_calibrate_workspace_size(const moe_desc *d, int32_t T);
 
-/* Kept neurons per (token, expert) at sparsity s: ceil((1 - s) * d_ff),
- * computed as ceil((1 - s) * d_ff - 1e-9) so that exact products do not
- * round up, clamped to [0, d_ff]; -1 if d_ff < 0 or s is not finite. */
+/* One workspace size for a whole layer over at most T_max tokens: enough
+ * for moe_route, for the FFN call on `path` with this k_keep, and (sparse
+ * path) for moe_layer_sparse, so one buffer serves every call of the layer
+ * in turn (0 on invalid input). */
+size_t moe_workspace_size(const moe_desc *d, int32_t T_max, int32_t k_keep, moe_path path);
+
+/* Kept neurons per (token, expert) at sparsity s: ceil((1 - s) * d_ff).  The
+ * page zeroes the lowest-scoring fraction of each selected expert's neurons
+ * (technical summary, Methodology: empirical analysis; Results: the
+ * sparsity levels that keep 95 % of the baseline accuracy), so s is the
+ * fraction zeroed and the rest is kept, rounded up.  Computed as
+ * ceil((1 - s) * d_ff - 1e-9) so that exact products do not round up,
+ * clamped to [0, d_ff]; -1 if d_ff < 0 or s is not finite. */
 int32_t moe_keep_count(double sparsity, int32_t d_ff);
 
 /* Host-side, shape-only choice between the sparse and dense paths for T

@@ -202,9 +202,10 @@ def kept_neurons(h: np.ndarray, k: int) -> np.ndarray:
     page, technical summary, Methodology: empirical analysis and activation
     masking).  -0 and +0 score equal."""
     d = h.shape[0]
-    a = np.abs(h)
-    order = sorted(range(d), key=lambda j: (-float(a[j]), j))
-    return np.asarray(sorted(order[:k]), dtype=np.int64)
+    a = np.abs(np.asarray(h, dtype=np.float64))
+    # a stable sort on (-|h|, j): the last key given to lexsort is the primary one
+    order = np.lexsort((np.arange(d), -a))
+    return np.sort(order[:max(0, min(k, d))]).astype(np.int64)
 
 
 def threshold_neurons(h: np.ndarray, tau: float) -> np.ndarray:
@@ -263,16 +264,33 @@ def _select(scores, k_keep, tau, forced):
     return kept_neurons(scores, k_keep)
 
 
-def _pair_output(x_t, wg, wu, wd, k_keep, forced, score, tau=None):
+def expert_scores_batch(X: np.ndarray, w_gate_e: np.ndarray, w_up_e: np.ndarray,
+                        score: str) -> np.ndarray:
+    """The selection scores of several tokens of one expert at once  ->  [n, d_ff].
+
+    Row i equals expert_activation(X[i], ...) (score="swiglu") or
+    gate_scores(X[i], ...) (score="gate"): the same definition, with the
+    expert's projections of its tokens taken as one matrix product."""
+    g = X @ w_gate_e.T
+    if score == "gate":
+        return silu(g)
+    if score == "swiglu":
+        return silu(g) * (X @ w_up_e.T)
+    raise ValueError(f"unknown score {score!r}")
+
+
+def _pair_output(x_t, wg, wu, wd, k_keep, forced, score, tau=None, sc=None):
     """One (token, expert) pair: (its contribution before the routing
     weight [H], the selection scores [d_ff], the kept set).  ``tau`` (the
-    expert's calibrated threshold) replaces the exact count when given."""
+    expert's calibrated threshold) replaces the exact count when given;
+    ``sc`` passes the pair's scores when they were computed with the other
+    tokens of the expert (expert_scores_batch)."""
     if score == "swiglu":
-        h = expert_activation(x_t, wg, wu)
+        h = expert_activation(x_t, wg, wu) if sc is None else sc
         keep = _select(h, k_keep, tau, forced)
         return sparse_down(h, keep, wd), h, keep
     if score == "gate":
-        sc = gate_scores(x_t, wg)
+        sc = gate_scores(x_t, wg) if sc is None else sc
         keep = _select(sc, k_keep, tau, forced)
         h = np.zeros_like(sc)
         h[keep] = sparse_up(x_t, sc, keep, wu)
@@ -299,10 +317,12 @@ def routed_experts(x, ids, weights, w_gate, w_up, w_down, k_keep, dtype,
             by_expert.setdefault(int(ids[t, s]), []).append((t, s))
     for e in sorted(by_expert):
         wg, wu, wd = (to_f64(w[e], dtype) for w in (w_gate, w_up, w_down))
-        for (t, s) in by_expert[e]:
+        pairs = by_expert[e]
+        scores = expert_scores_batch(x[[t for t, _ in pairs]], wg, wu, score)
+        for i, (t, s) in enumerate(pairs):
             forced = forced_keep.get((t, s)) if forced_keep is not None else None
             tau = None if thresholds is None else float(thresholds[e])
-            out, sc, keep = _pair_output(x[t], wg, wu, wd, k_keep, forced, score, tau)
+            out, sc, keep = _pair_output(x[t], wg, wu, wd, k_keep, forced, score, tau, scores[i])
             y[t] += weights[t, s] * out
             if keep_h:
                 hs[(t, s)] = sc
@@ -323,10 +343,11 @@ def shared_experts(x, w_gate, w_up, w_down, n_shared, k_keep, dtype,
     hs, keeps = {}, {}
     for j in range(n_shared):
         wg, wu, wd = (to_f64(w[j], dtype) for w in (w_gate, w_up, w_down))
+        scores = expert_scores_batch(x, wg, wu, score)
         for t in range(T):
             forced = forced_keep.get((t, j)) if forced_keep is not None else None
             tau = None if thresholds is None else float(thresholds[j])
-            out, sc, keep = _pair_output(x[t], wg, wu, wd, k_keep, forced, score, tau)
+            out, sc, keep = _pair_output(x[t], wg, wu, wd, k_keep, forced, score, tau, scores[t])
             y[t] += out
             if keep_h:
                 hs[(t, j)] = sc
@@ -412,9 +433,7 @@ def calibrate_thresholds(x, w_router, bias, w_gate, w_up, *, top_k: int, norm_to
             continue
         wg = to_f64(w_gate[e], dtype)
         wu = to_f64(w_up[e], dtype)
-        for t in rows:
-            per[e].append(gate_scores(xf[t], wg) if score == "gate"
-                          else expert_activation(xf[t], wg, wu))
+        per[e].extend(expert_scores_batch(xf[rows], wg, wu, score))
     everything = [v for e in range(E) for v in per[e]]
     tau_all = calibrated_threshold(np.concatenate(everything), sparsity) if everything else -1.0
     tau = np.array([calibrated_threshold(np.concatenate(per[e]), sparsity) if per[e] else tau_all
@@ -424,9 +443,8 @@ def calibrate_thresholds(x, w_router, bias, w_gate, w_up, *, top_k: int, norm_to
         tau_sh = []
         for j in range(len(shared[0])):
             wg, wu = to_f64(shared[0][j], dtype), to_f64(shared[1][j], dtype)
-            sc = [gate_scores(xf[t], wg) if score == "gate" else expert_activation(xf[t], wg, wu)
-                  for t in range(xf.shape[0])]
-            tau_sh.append(calibrated_threshold(np.concatenate(sc), sparsity))
+            sc = expert_scores_batch(xf, wg, wu, score)
+            tau_sh.append(calibrated_threshold(sc.ravel(), sparsity))
         tau_sh = np.array(tau_sh, dtype=np.float64)
     return tau, tau_sh
 

@@ -17,6 +17,7 @@ from .build import INCLUDE, LIB_PATH
 
 MOE_F32, MOE_BF16 = 0, 1
 MOE_PATH_SPARSE, MOE_PATH_DENSE = 0, 1
+MOE_LAYOUT_ROWMAJOR, MOE_LAYOUT_PACKED = 0, 1
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_MISALIGNED", 3: "MOE_ERR_WORKSPACE",
           4: "MOE_ERR_UNSUPPORTED", 5: "MOE_ERR_HIP"}
 HEADER = os.path.join(INCLUDE, "moe_mi355x.h")
@@ -32,7 +33,8 @@ class MoeError(RuntimeError):
 class MoeDesc(ctypes.Structure):
     _fields_ = [("hidden", ctypes.c_int32), ("n_experts", ctypes.c_int32),
                 ("d_ff", ctypes.c_int32), ("top_k", ctypes.c_int32),
-                ("norm_topk", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+                ("norm_topk", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("gate_up_layout", ctypes.c_int32)]
 
 
 class MoeRouting(ctypes.Structure):
@@ -67,6 +69,7 @@ _SIGS = {
     "moe_unpack_gate_up": (_I32, [_PD, _V, _V, _V]),
     "moe_route_workspace_size": (_SZ, [_PD, _I32]),
     "moe_ffn_workspace_size": (_SZ, [_PD, _I32, _I32, _I32]),
+    "moe_workspace_size": (_SZ, [_PD, _I32, _I32, _I32]),
     "moe_keep_count": (_I32, [_D, _I32]),
     "moe_select_path": (_I32, [_PD, _I32, _I32]),
     "moe_timer_attach": (_I32, [ctypes.POINTER(_V), ctypes.POINTER(_I32), _I32]),
@@ -112,9 +115,15 @@ def _check(status: int):
         raise MoeError(status, lib().moe_last_error().decode())
 
 
-def make_desc(hidden, n_experts, d_ff, top_k, norm_topk, dtype) -> MoeDesc:
+def make_desc(hidden, n_experts, d_ff, top_k, norm_topk, dtype,
+              gate_up_layout="rowmajor") -> MoeDesc:
+    """moe_desc; gate_up_layout says how w_gate / w_up are passed to the FFN
+    calls ("packed" after moe_pack_gate_up; "rowmajor" ones are refused)."""
     dt = {"f32": MOE_F32, "bf16": MOE_BF16, MOE_F32: MOE_F32, MOE_BF16: MOE_BF16}[dtype]
-    return MoeDesc(int(hidden), int(n_experts), int(d_ff), int(top_k), int(bool(norm_topk)), dt)
+    lay = {"rowmajor": MOE_LAYOUT_ROWMAJOR, "packed": MOE_LAYOUT_PACKED,
+           MOE_LAYOUT_ROWMAJOR: MOE_LAYOUT_ROWMAJOR, MOE_LAYOUT_PACKED: MOE_LAYOUT_PACKED}
+    return MoeDesc(int(hidden), int(n_experts), int(d_ff), int(top_k), int(bool(norm_topk)), dt,
+                   lay.get(gate_up_layout, gate_up_layout))
 
 
 # ------------------------------------------------------------ tensor marshalling
@@ -330,6 +339,10 @@ def moe_route_workspace_size(desc: MoeDesc, T: int) -> int:
 
 def moe_ffn_workspace_size(desc: MoeDesc, T: int, k_keep: int, path: int) -> int:
     return int(lib().moe_ffn_workspace_size(ctypes.byref(desc), int(T), int(k_keep), int(path)))
+
+
+def moe_workspace_size(desc: MoeDesc, T_max: int, k_keep: int, path: int) -> int:
+    return int(lib().moe_workspace_size(ctypes.byref(desc), int(T_max), int(k_keep), int(path)))
 
 
 def moe_keep_count(sparsity: float, d_ff: int) -> int:

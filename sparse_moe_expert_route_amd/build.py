@@ -51,14 +51,17 @@ def _run(cmd, verbose):
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every source to an object under lib/obj, link the shared library."""
+    """Compile every source to an object under lib/obj (in parallel), link
+    the shared library."""
+    from concurrent.futures import ThreadPoolExecutor
     obj_dir = os.path.join(LIB_DIR, "obj")
     os.makedirs(obj_dir, exist_ok=True)
-    objs = []
-    for s in SOURCES:
-        obj = os.path.join(obj_dir, s + ".o")
-        _run([hipcc()] + flags() + ["-c", os.path.join(CSRC, s), "-o", obj], verbose)
-        objs.append(obj)
+    objs = [os.path.join(obj_dir, s + ".o") for s in SOURCES]
+    jobs = max(1, min(len(SOURCES), len(os.sched_getaffinity(0)), 8))
+    with ThreadPoolExecutor(jobs) as ex:
+        list(ex.map(lambda so: _run([hipcc()] + flags() + ["-c", os.path.join(CSRC, so[0]), "-o",
+                                                           so[1]], verbose),
+                    zip(SOURCES, objs)))
     tmp = LIB_PATH + ".tmp"
     _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC"] + objs + ["-o", tmp], verbose)
     os.replace(tmp, LIB_PATH)

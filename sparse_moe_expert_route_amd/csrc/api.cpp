@@ -44,6 +44,8 @@ moe_status check_desc(const moe_desc *d) {
     return fail(MOE_ERR_INVALID_ARG, "top_k %d exceeds n_experts %d", d->top_k, d->n_experts);
   if (d->norm_topk != 0 && d->norm_topk != 1)
     return fail(MOE_ERR_INVALID_ARG, "norm_topk must be 0 or 1");
+  if (d->gate_up_layout != MOE_LAYOUT_ROWMAJOR && d->gate_up_layout != MOE_LAYOUT_PACKED)
+    return fail(MOE_ERR_INVALID_ARG, "gate_up_layout %d is not a moe_layout", d->gate_up_layout);
   if (d->hidden > MOE_MAX_HIDDEN || d->hidden % 64)
     return fail(MOE_ERR_UNSUPPORTED, "hidden %d: need a multiple of 64 up to %d", d->hidden,
                 MOE_MAX_HIDDEN);
@@ -146,6 +148,11 @@ moe_status run_ffn(RunMode mode, const moe_desc *d, int32_t T, int32_t k_keep, c
   g_err[0] = 0;
   TRY(check_desc(d));
   TRY(check_T(T));
+  if (d->gate_up_layout != MOE_LAYOUT_PACKED)
+    return fail(MOE_ERR_UNSUPPORTED, "the FFN calls read w_gate%s packed by moe_pack_gate_up: pack "
+                "it and set desc->gate_up_layout = MOE_LAYOUT_PACKED",
+                mode == kRunUpdown || mode == kRunUpdownThreshold || mode == kRunCalibrateGate
+                    ? "" : " and w_up");
   const moe_path path = mode == kRunDense ? MOE_PATH_DENSE : MOE_PATH_SPARSE;
   const bool thr = mode == kRunThreshold || mode == kRunUpdownThreshold;
   const bool cal = mode == kRunCalibrate || mode == kRunCalibrateGate;
@@ -532,6 +539,15 @@ size_t moe_ffn_workspace_size(const moe_desc *d, int32_t T, int32_t k_keep, moe_
   if (k_keep < 0 || k_keep > d->d_ff) return 0;
   if (path != MOE_PATH_SPARSE && path != MOE_PATH_DENSE) return 0;
   return ffn_layout(d, T > 0 ? T : 1, k_keep, path).total;
+}
+
+size_t moe_workspace_size(const moe_desc *d, int32_t T_max, int32_t k_keep, moe_path path) {
+  const size_t r = moe_route_workspace_size(d, T_max);
+  const size_t f = moe_ffn_workspace_size(d, T_max, k_keep, path);
+  if (r == 0 || f == 0) return 0;
+  // route's region first, then the FFN's: the layout moe_layer_sparse uses,
+  // and a superset of what moe_route or the FFN call alone needs
+  return up(r) + f;
 }
 
 size_t moe_ffn_threshold_workspace_size(const moe_desc *d, int32_t T) {

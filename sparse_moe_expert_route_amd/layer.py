@@ -22,7 +22,8 @@ class MoELayer:
         """Weights are device tensors [E, d_ff, H] (router [E, H]).  Gate and
         up are packed here with moe_pack_gate_up unless `packed` says the
         caller already did."""
-        self.desc = B.make_desc(hidden, n_experts, d_ff, top_k, norm_topk, dtype)
+        self.desc = B.make_desc(hidden, n_experts, d_ff, top_k, norm_topk, dtype,
+                                gate_up_layout="packed")
         self.w_router, self.bias = w_router, bias
         pk = (lambda d, w: w) if packed else B.moe_pack_gate_up
         self.w = (pk(self.desc, w_gate), pk(self.desc, w_up), w_down)
@@ -31,7 +32,8 @@ class MoELayer:
         if shared is not None:
             g, u, dn = shared
             n_sh = g.shape[0]
-            self.desc_shared = B.make_desc(hidden, n_sh, d_ff_shared or g.shape[1], n_sh, False, dtype)
+            self.desc_shared = B.make_desc(hidden, n_sh, d_ff_shared or g.shape[1], n_sh, False, dtype,
+                                           gate_up_layout="packed")
             self.shared = (pk(self.desc_shared, g), pk(self.desc_shared, u), dn)
         self._ws = {}
 

@@ -59,7 +59,8 @@ class DeviceLayer:
         self.inp = inp
         self.score = score
         sh = inp.shape
-        self.desc = B.make_desc(sh.hidden, sh.n_experts, sh.d_ff, sh.top_k, sh.norm_topk, sh.dtype)
+        self.desc = B.make_desc(sh.hidden, sh.n_experts, sh.d_ff, sh.top_k, sh.norm_topk, sh.dtype,
+                                gate_up_layout="packed")
         self.w_router = to_dev(inp.w_router)
         self.bias = to_dev(inp.bias) if inp.bias is not None else None
         pk_up = B.moe_pack_gate_up if score == "swiglu" else (lambda d, w: w)
@@ -70,7 +71,7 @@ class DeviceLayer:
         self.desc_sh = None
         if inp.shared is not None:
             self.desc_sh = B.make_desc(sh.hidden, sh.n_shared, sh.d_ff_shared, sh.n_shared, False,
-                                       sh.dtype)
+                                       sh.dtype, gate_up_layout="packed")
             g, u, d = inp.shared
             self.w_sh = (B.moe_pack_gate_up(self.desc_sh, to_dev(g)),
                          pk_up(self.desc_sh, to_dev(u)), to_dev(d))

@@ -61,7 +61,8 @@ def test_keep_count_matches_exact_rationals():
 
 
 def _desc(**kw):
-    base = dict(hidden=2048, n_experts=64, d_ff=1024, top_k=8, norm_topk=False, dtype="bf16")
+    base = dict(hidden=2048, n_experts=64, d_ff=1024, top_k=8, norm_topk=False, dtype="bf16",
+                gate_up_layout="packed")
     base.update(kw)
     return B.make_desc(**base)
 
@@ -91,6 +92,57 @@ def test_workspace_sizes():
     assert B.moe_ffn_workspace_size(d, 4, 2000, 0) == 0
     assert B.moe_ffn_workspace_size(_desc(hidden=100), 4, 10, 0) == 0
     assert B.moe_route_workspace_size(d, 16) >= 16 * 64 * 4
+
+
+def test_layer_workspace_size_covers_every_call():
+    # moe_workspace_size: one buffer for moe_route, the FFN call on the path
+    # and (sparse) moe_layer_sparse, for any T up to T_max
+    d = _desc()
+    for path in (B.MOE_PATH_SPARSE, B.MOE_PATH_DENSE):
+        for T in (1, 4, 16, 64, 1024):
+            w = B.moe_workspace_size(d, T, 103, path)
+            assert w > 0 and w % 256 == 0
+            assert w >= B.moe_route_workspace_size(d, T)
+            assert w >= B.moe_ffn_workspace_size(d, T, 103, path)
+            if path == B.MOE_PATH_SPARSE:
+                assert w >= B.moe_layer_workspace_size(d, T, 103)
+            assert all(B.moe_workspace_size(d, t, 103, path) <= w for t in range(1, T + 1, 7))
+    assert B.moe_workspace_size(d, 4, 2000, 0) == 0
+    assert B.moe_workspace_size(d, 4, 10, 7) == 0
+    assert B.moe_workspace_size(_desc(hidden=100), 4, 10, 0) == 0
+
+
+ROWMAJOR_REFUSED = ["moe_expert_ffn_sparse", "moe_expert_ffn_dense", "moe_expert_ffn_sparse_updown"]
+
+
+@pytest.mark.parametrize("fn_name", ROWMAJOR_REFUSED)
+def test_rowmajor_gate_up_is_refused(fn_name):
+    # a descriptor left at MOE_LAYOUT_ROWMAJOR (zero) never reaches a kernel:
+    # the FFN calls read packed gate/up and say so instead of misreading
+    fn = getattr(L, fn_name)
+    assert _ffn(fn, _desc(gate_up_layout="rowmajor"), 4, 10) == UNS
+    assert "moe_pack_gate_up" in B.moe_last_error()
+    assert _ffn(fn, _desc(gate_up_layout=7), 4, 10) == INV
+    assert _ffn(fn, _desc(), 4, 10) != UNS      # packed: validation goes on (fake pointers)
+
+
+def test_rowmajor_refused_by_the_other_ffn_calls():
+    d = _desc(gate_up_layout="rowmajor")
+    r = B.MoeRouting(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    assert L.moe_expert_ffn_sparse_residual(ctypes.byref(d), 4, 10, FAKE, FAKE, FAKE, FAKE,
+                                            ctypes.byref(r), FAKE, 0, None, FAKE, FAKE, FAKE,
+                                            1 << 34, None) == UNS
+    assert L.moe_layer_sparse(ctypes.byref(d), 4, 10, FAKE, FAKE, None, FAKE, FAKE, FAKE,
+                              ctypes.byref(r), FAKE, 0, None, None, None, FAKE, 1 << 34, None) == UNS
+    for name in ("moe_expert_ffn_sparse_threshold", "moe_expert_ffn_sparse_updown_threshold"):
+        assert getattr(L, name)(ctypes.byref(d), 4, FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.byref(r),
+                                FAKE, 0, None, None, FAKE, 1 << 34, None) == UNS
+    assert L.moe_calibrate_thresholds(ctypes.byref(d), 4, FAKE, FAKE, FAKE, ctypes.byref(r), 0.9,
+                                      FAKE, FAKE, 1 << 34, None) == UNS
+    assert L.moe_calibrate_thresholds_gate(ctypes.byref(d), 4, FAKE, FAKE, ctypes.byref(r), 0.9,
+                                           FAKE, FAKE, 1 << 34, None) == UNS
+    # the router does not read gate/up: a row-major descriptor validates there
+    assert _route(d, 4, wsb=0) == WSP
 
 
 def _route(d, T, x=FAKE, w=FAKE, bias=None, out="ok", ws=FAKE, wsb=1 << 30):

@@ -56,7 +56,7 @@ def test_roster_steps_match_oracle(name, over, T, m, delta, steps):
     say(f"[case] roster {name} E={E} top_k={K} T={T} m={m} delta={delta}")
     wr = S.router_matrix(shape, 0)
     bias = S.router_bias(shape)
-    desc = B.make_desc(shape.hidden, E, shape.d_ff, K, shape.norm_topk, dt)
+    desc = B.make_desc(shape.hidden, E, shape.d_ff, K, shape.norm_topk, dt, gate_up_layout="packed")
     rng = np.random.default_rng(7)
     usage_h = _start_usage(rng, T, E, m)
     pinned_h = (np.arange(T) % 4 == 3).astype(np.int32) if m >= K else None
@@ -99,7 +99,8 @@ def test_roster_with_zero_delta_is_moe_route():
     # no bias (delta 0, nothing pinned): bitwise the plain router, plus counts
     shape = S.LAYERS["olmoe-like"]
     E, K = shape.n_experts, shape.top_k
-    desc = B.make_desc(shape.hidden, E, shape.d_ff, K, shape.norm_topk, shape.dtype)
+    desc = B.make_desc(shape.hidden, E, shape.d_ff, K, shape.norm_topk, shape.dtype,
+                       gate_up_layout="packed")
     wr_d = to_dev(S.router_matrix(shape, 0))
     for T in (16, 48):
         say(f"[case] roster delta=0 T={T}")
@@ -122,7 +123,8 @@ def test_roster_graph_replays_follow_the_eager_steps():
     # through the same states as eager steps, replay after replay
     shape = S.LAYERS["olmoe-like"]
     E, K, T = shape.n_experts, shape.top_k, 16
-    desc = B.make_desc(shape.hidden, E, shape.d_ff, K, shape.norm_topk, shape.dtype)
+    desc = B.make_desc(shape.hidden, E, shape.d_ff, K, shape.norm_topk, shape.dtype,
+                       gate_up_layout="packed")
     wr_d = to_dev(S.router_matrix(shape, 0))
     x = to_dev(S.tokens(shape, 9, T))
     ws = torch.empty(B.moe_route_workspace_size(desc, T), dtype=torch.uint8, device="cuda")

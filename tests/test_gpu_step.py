@@ -26,7 +26,8 @@ def say(*a):
 def test_residual_add_matches_oracle(dtype, T):
     shape = S.LAYERS["olmoe-like"].with_(dtype=dtype)
     say(f"[case] residual {dtype} T={T}")
-    desc = B.make_desc(shape.hidden, shape.n_experts, shape.d_ff, shape.top_k, False, dtype)
+    desc = B.make_desc(shape.hidden, shape.n_experts, shape.d_ff, shape.top_k, False, dtype,
+                       gate_up_layout="packed")
     x = S.tokens(shape, 30 + T, T)
     y = (np.random.default_rng(T).standard_normal((T, shape.hidden)) * 0.3).astype(np.float32)
     want = O.residual_stream(x, y, dtype)

@@ -164,6 +164,25 @@ def test_expert_activation_against_torch():
     assert not np.allclose(O.expert_activation(x, wu, wg), want)
 
 
+def test_expert_scores_batch_against_torch():
+    # several tokens of one expert at once: each row is the per-token
+    # definition (SwiGLU product, or the gate-only score of the split)
+    rng = np.random.default_rng(4)
+    n, H, d = 5, 48, 40
+    X = rng.standard_normal((n, H))
+    wg, wu = rng.standard_normal((d, H)), rng.standard_normal((d, H))
+    g = F.linear(torch.from_numpy(X), torch.from_numpy(wg))
+    u = F.linear(torch.from_numpy(X), torch.from_numpy(wu))
+    np.testing.assert_allclose(O.expert_scores_batch(X, wg, wu, "swiglu"), (F.silu(g) * u).numpy(),
+                               rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(O.expert_scores_batch(X, wg, wu, "gate"), F.silu(g).numpy(),
+                               rtol=1e-12, atol=1e-14)
+    # row order follows the tokens; gate and up are not interchangeable
+    np.testing.assert_allclose(O.expert_scores_batch(X[::-1], wg, wu, "swiglu")[::-1],
+                               (F.silu(g) * u).numpy(), rtol=1e-12, atol=1e-14)
+    assert not np.allclose(O.expert_scores_batch(X, wu, wg, "swiglu"), (F.silu(g) * u).numpy())
+
+
 def test_sparse_down_reads_only_kept_rows():
     rng = np.random.default_rng(4)
     d, H = 20, 16
