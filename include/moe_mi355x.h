@@ -43,7 +43,8 @@
  *   round-to-nearest-even), every accumulation is fp32; MOE_F32: all fp32.
  *   Router logits, softmax weights, h and y are fp32 in both.
  * - The library holds no global state and is reentrant; two calls that
- *   share a workspace must be ordered on one stream.
+ *   share a workspace must be ordered on one stream.  The one exception is
+ *   moe_layer_sparse_noalloc, whose workspace is a static per-device array.
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H
@@ -245,6 +246,30 @@ moe_status moe_layer_sparse(const moe_desc *d, int32_t T, int32_t k_keep, const 
 /* Workspace bytes for moe_layer_sparse over at most T tokens with this
  * k_keep (0 on invalid input). */
 size_t moe_layer_workspace_size(const moe_desc *d, int32_t T, int32_t k_keep);
+
+/*
+ * moe_layer_sparse_noalloc -- moe_layer_sparse for callers that cannot
+ * allocate: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Same arguments, outputs and bits as
+ * moe_layer_sparse, without the workspace arguments: the workspace is a
+ * static array of MOE_NOALLOC_SCRATCH_BYTES in the library's device code,
+ * one per GPU, held until the process ends.  Nothing is allocated (no
+ * hipMalloc, hipFree or allocating library routine); the first call on a
+ * device looks the array's device address up once.  A call whose
+ * moe_layer_workspace_size(d, T, k_keep) exceeds MOE_NOALLOC_SCRATCH_BYTES
+ * returns MOE_ERR_WORKSPACE with nothing enqueued (use moe_layer_sparse
+ * with a caller workspace then).  Every call on a GPU shares that GPU's
+ * array and the array keeps the last call's contents (nothing in it must
+ * start at zero): calls that overlap on one GPU (different streams, or
+ * different host threads without ordering) race and must not be issued.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES (16u << 20)
+moe_status moe_layer_sparse_noalloc(const moe_desc *d, int32_t T, int32_t k_keep, const void *x,
+                                    const void *w_router, const float *bias, const void *w_gate,
+                                    const void *w_up, const void *w_down,
+                                    const moe_routing *routing_out, float *y, int32_t accumulate,
+                                    int32_t *active_idx_out, const void *x_res, void *x_next,
+                                    hipStream_t stream);
 
 /*
  * moe_expert_ffn_dense -- the same layer function on the dense path the

@@ -59,6 +59,8 @@ _SIGS = {
     "moe_layer_sparse": (_I32, [_PD, _I32, _I32, _V, _V, _V, _V, _V, _V, _PR, _V, _I32, _V, _V,
                                 _V, _V, _SZ, _V]),
     "moe_layer_workspace_size": (_SZ, [_PD, _I32, _I32]),
+    "moe_layer_sparse_noalloc": (_I32, [_PD, _I32, _I32, _V, _V, _V, _V, _V, _V, _PR, _V, _I32,
+                                        _V, _V, _V, _V]),
     "moe_expert_ffn_dense": (_I32, [_PD, _I32, _I32, _V, _V, _V, _V, _PR, _V, _I32, _V, _V, _SZ, _V]),
     "moe_expert_ffn_sparse_updown": (_I32, [_PD, _I32, _I32, _V, _V, _V, _V, _PR, _V, _I32, _V, _V, _SZ, _V]),
     "moe_expert_ffn_sparse_threshold": (_I32, [_PD, _I32, _V, _V, _V, _V, _V, _PR, _V, _I32, _V, _V, _V, _SZ, _V]),
@@ -242,6 +244,21 @@ def moe_layer_sparse(desc, T, k_keep, x, w_router, bias, w_gate, w_up, w_down, r
         _ptr(w_up), _ptr(w_down), ctypes.byref(r), _ptr(y), int(accumulate), _ptr(active_idx_out),
         _ptr(x_res), _ptr(x_next), ws, workspace.numel() * workspace.element_size() if ws else 0,
         _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def moe_layer_sparse_noalloc(desc, T, k_keep, x, w_router, bias, w_gate, w_up, w_down, routing, y,
+                             accumulate=0, active_idx_out=None, stream=None, x_res=None,
+                             x_next=None):
+    """moe_layer_sparse with the library's static per-device scratch as its
+    workspace: nothing is allocated.  Calls that overlap on one GPU race."""
+    r = routing.as_c()
+    _check(lib().moe_layer_sparse_noalloc(
+        ctypes.byref(desc), int(T), int(k_keep), _ptr(x), _ptr(w_router), _ptr(bias), _ptr(w_gate),
+        _ptr(w_up), _ptr(w_down), ctypes.byref(r), _ptr(y), int(accumulate), _ptr(active_idx_out),
+        _ptr(x_res), _ptr(x_next), _stream(stream)))
 
 
 def moe_layer_workspace_size(desc, T, k_keep):

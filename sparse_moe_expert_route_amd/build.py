@@ -20,7 +20,8 @@ LIB_DIR = os.path.join(PKG, "lib")
 LIB_NAME = "libmoe_mi355x.so"
 LIB_PATH = os.path.join(LIB_DIR, LIB_NAME)
 
-SOURCES = ["route.hip", "ffn.hip", "dense.hip", "pack.hip", "calib.hip", "residual.hip", "api.cpp"]
+SOURCES = ["ffn.hip", "route.hip", "dense.hip", "pack.hip", "calib.hip", "residual.hip",
+           "noalloc.hip", "api.cpp"]
 ARCH = "gfx950"
 
 

@@ -436,6 +436,31 @@ moe_status moe_layer_sparse(const moe_desc *d, int32_t T, int32_t k_keep, const 
                  active_idx_out, ws + rws, workspace_bytes - rws, stream, m);
 }
 
+moe_status moe_layer_sparse_noalloc(const moe_desc *d, int32_t T, int32_t k_keep, const void *x,
+                                    const void *w_router, const float *bias, const void *w_gate,
+                                    const void *w_up, const void *w_down,
+                                    const moe_routing *routing_out, float *y, int32_t accumulate,
+                                    int32_t *active_idx_out, const void *x_res, void *x_next,
+                                    hipStream_t stream) {
+  g_err[0] = 0;
+  TRY(check_desc(d));
+  TRY(check_T(T));
+  if (T == 0) return MOE_OK;
+  const size_t need = moe_layer_workspace_size(d, T, k_keep);
+  if (need == 0) return fail(MOE_ERR_INVALID_ARG, "k_keep %d outside [0, d_ff=%d]", k_keep, d->d_ff);
+  if (need > (size_t)MOE_NOALLOC_SCRATCH_BYTES)
+    return fail(MOE_ERR_WORKSPACE,
+                "this call needs %zu bytes of scratch; the static scratch holds %zu (call "
+                "moe_layer_sparse with a caller workspace)", need, (size_t)MOE_NOALLOC_SCRATCH_BYTES);
+  void *ws = nullptr;
+  const hipError_t e = moe::noalloc_scratch(&ws);
+  if (e != hipSuccess)
+    return fail(MOE_ERR_HIP, "device address of the static scratch: %s", hipGetErrorString(e));
+  return moe_layer_sparse(d, T, k_keep, x, w_router, bias, w_gate, w_up, w_down, routing_out, y,
+                          accumulate, active_idx_out, x_res, x_next, ws,
+                          (size_t)MOE_NOALLOC_SCRATCH_BYTES, stream);
+}
+
 moe_status moe_expert_ffn_dense(const moe_desc *d, int32_t T, int32_t k_keep, const void *x,
                                 const void *w_gate, const void *w_up, const void *w_down,
                                 const moe_routing *routing, float *y, int32_t accumulate,

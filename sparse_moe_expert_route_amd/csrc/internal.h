@@ -84,6 +84,10 @@ struct FfnArgs {
   void *xnext;
 };
 
+// Device address of the static scratch of moe_layer_sparse_noalloc on the
+// current device (looked up once per device).
+hipError_t noalloc_scratch(void **out);
+
 hipError_t launch_residual(const void *x_in, const float *y, void *x_out, size_t n, int bf16,
                            hipStream_t stream);
 hipError_t launch_stream_read(const void *src, size_t bytes, uint32_t *sink, int max_blocks,
