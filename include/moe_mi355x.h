@@ -482,7 +482,8 @@ typedef enum {
   MOE_STAGE_COMBINE = 7,
   MOE_STAGE_ZERO = 8,
   MOE_STAGE_UP_ROWS = 9,
-  MOE_N_STAGES = 10
+  MOE_STAGE_FUSED_FFN = 10, /* gate/up, masks, down and combine in one launch */
+  MOE_N_STAGES = 11
 } moe_stage;
 
 /* While attached, every kernel the library launches from this thread is

@@ -80,7 +80,7 @@ size_t elem_bytes(const moe_desc *d) { return d->dtype == MOE_BF16 ? 2 : 4; }
 
 // FFN workspace layout (each segment 256-byte aligned).
 struct FfnLayout {
-  size_t h, idx, hact, partial, hm, counts, total;
+  size_t h, idx, hact, partial, hm, fpart, sync, counts, total;
 };
 
 // What an FFN-shaped call does (all share validation and the carve-up).
@@ -97,6 +97,12 @@ FfnLayout ffn_layout(const moe_desc *d, int32_t T, int32_t k, moe_path path) {
   size_t off = 0;
   L.h = off;
   off += up(P * d->d_ff * 4);
+  // the fused decode-batch FFN's counters, directly after h (its gate/up
+  // blocks find them from h's address), then its per-pair partial outputs
+  L.sync = off;
+  if (path == MOE_PATH_SPARSE) off += up(moe::fused_sync_words(T, d->n_experts, d->hidden) * 4);
+  L.fpart = off;
+  if (path == MOE_PATH_SPARSE) off += up(P * d->hidden * 4);
   L.idx = off;
   off += up(P * (size_t)k * 4);
   L.hact = off;
@@ -238,6 +244,9 @@ moe_status run_ffn(RunMode mode, const moe_desc *d, int32_t T, int32_t k_keep, c
   a.hm = path == MOE_PATH_DENSE ? static_cast<void *>(ws + L.hm) : nullptr;
   a.xres = m.xres;
   a.xnext = m.xnext;
+  a.fpart = path == MOE_PATH_SPARSE ? reinterpret_cast<float *>(ws + L.fpart) : nullptr;
+  a.sync = path == MOE_PATH_SPARSE ? reinterpret_cast<int32_t *>(ws + L.sync) : nullptr;
+  a.sync_zeroed = 0;
   hipError_t e;
   switch (mode) {
     case kRunUpdown: e = moe::launch_ffn_updown(a, stream); break;
@@ -259,9 +268,17 @@ moe_status run_ffn(RunMode mode, const moe_desc *d, int32_t T, int32_t k_keep, c
     default:
       if (m.layer_route && moe::layer_small_ok(*m.layer_route, a)) {
         e = moe::launch_layer_small(*m.layer_route, a, stream);
-      } else {
-        e = m.layer_route ? moe::launch_route(*m.layer_route, stream) : hipSuccess;
+      } else if (m.layer_route) {
+        moe::RouteArgs r = *m.layer_route;
+        if (moe::fused_ffn_ok(a)) {  // the router zeroes the fused FFN's counters
+          r.zero = a.sync;
+          r.nzero = (int)moe::fused_sync_words(T, d->n_experts, d->hidden);
+          a.sync_zeroed = 1;
+        }
+        e = moe::launch_route(r, stream);
         if (e == hipSuccess) e = moe::launch_ffn_sparse(a, stream);
+      } else {
+        e = moe::launch_ffn_sparse(a, stream);
       }
   }
   if (e != hipSuccess) return fail(MOE_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));

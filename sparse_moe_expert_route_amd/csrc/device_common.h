@@ -39,6 +39,56 @@ __device__ __forceinline__ u32x4 buf_ld16_nt(__amdgpu_buffer_rsrc_t r, uint32_t 
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 2));
 }
 
+// ---- device-coherent (agent-scope) accesses, for data handed between
+// blocks inside one kernel.  Each XCD has its own L2 and they are not kept
+// coherent with one another: a plain store may sit in the writer's L2 and a
+// plain load may hit a stale line in the reader's.  Agent-scope accesses
+// carry the sc1 bit (write through / read past the non-coherent L2), and
+// the writer waits for its stores to complete (wait_stores) before it
+// signals with an atomic; read-modify-write atomics are device-coherent as
+// issued.  No release/acquire fence is used: on this chip each one writes
+// back or invalidates the whole L2 of the XCD, serialised per block.
+__device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void compiler_barrier() { asm volatile("" ::: "memory"); }
+__device__ __forceinline__ void st_agent(float *p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_agent(const float *p) {
+  return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int ld_agent(const int32_t *p) {
+  return __hip_atomic_load(const_cast<int32_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent(int32_t *p, int32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// 16 bytes at voff + soff of a buffer resource, read coherently (sc1)
+__device__ __forceinline__ u32x4 buf_ld16_agent(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 16));
+}
+
+// Bounded wait (one lane): until *cnt >= target.  Gives up after about one
+// second of the 100 MHz real-time counter or once another block has given
+// up (*abort != 0), sets *abort and returns false; a wait that cannot be
+// satisfied therefore ends the kernel with wrong outputs, never a hang.
+// Polls back off from ~0.1 to ~1.5 us apart, so that many waiting blocks
+// do not crowd the memory channel of the polled line.
+__device__ __forceinline__ bool wait_count(const int32_t *cnt, int target, int32_t *abort) {
+  if (ld_agent(cnt) >= target) return true;
+  const uint64_t t0 = wall_clock64();
+  for (uint32_t it = 0;; ++it) {
+    if (it < 4) __builtin_amdgcn_s_sleep(4);
+    else if (it < 12) __builtin_amdgcn_s_sleep(16);
+    else __builtin_amdgcn_s_sleep(56);
+    if (ld_agent(cnt) >= target) return true;
+    if (ld_agent(abort) != 0) return false;
+    if (wall_clock64() - t0 > 100000000ull || it > (1u << 26)) {
+      st_agent(abort, 1);
+      return false;
+    }
+  }
+}
+
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 

@@ -28,6 +28,294 @@
 
 namespace moe {
 
+// ---------------------------------------------------------------- sparse down rows
+// The down kernels share one inner loop: a block of NWV (kDownWaves) waves
+// streams n staged rows (srow[q] = expert * d_ff + row, scoef[q] its
+// coefficient, both in LDS) of W_d, each row contributing one SW-element run
+// at column colo.  Wave wid takes row groups wid, wid + kDownWaves, ...
+// (RPI rows per group, one per LPR-lane slice) and issues U groups' 16-byte
+// loads before folding any of them into acc, so a lane has up to U loads in
+// flight.  U = 4: deeper rounds (8) measured no faster at decode batches
+// and raise the kernels to ~78 VGPRs, which halves the blocks a CU holds
+// at large batches (Llama-4-like T = 256 sparse: 1082 -> 1156 us).
+constexpr int kDownWaves = 16;
+constexpr int kDownStage = 4096;     // row-list entries staged in LDS
+
+// The residual stream's element o of the next layer's input: x_res + y
+// summed in fp32, rounded to the layer dtype (as residual_kernel does).
+template <bool BF16>
+__device__ __forceinline__ void residual_store(const void *xres, void *xnext, size_t o, float y) {
+  if (BF16) {
+    const uint32_t xb = static_cast<const uint16_t *>(xres)[o];
+    static_cast<uint16_t *>(xnext)[o] = (uint16_t)f32_to_bf16_bits(bf16lo(xb) + y);
+  } else {
+    static_cast<float *>(xnext)[o] = static_cast<const float *>(xres)[o] + y;
+  }
+}
+
+template <bool BF16, int SW, int U, int NWV = kDownWaves>
+__device__ __forceinline__ void stream_rows_u(const void *__restrict__ wdv,
+                                              const uint32_t *srow, const float *scoef, int n,
+                                              int H, size_t colo, int wid, int rsel,
+                                              float (&acc)[BF16 ? 8 : 4]) {
+  constexpr int VEC = BF16 ? 8 : 4;
+  constexpr int RPI = 64 / (SW / VEC);
+  for (int b0 = wid; b0 * RPI < n; b0 += NWV * U) {
+    u32x4 qv[U];
+    float cf[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int qq = (b0 + NWV * u) * RPI + rsel;
+      cf[u] = 0.f;
+      qv[u] = u32x4{0, 0, 0, 0};
+      if (qq < n) {
+        const size_t off = (size_t)srow[qq] * H + colo;
+        cf[u] = scoef[qq];
+        qv[u] = BF16 ? ld16(static_cast<const uint16_t *>(wdv) + off)
+                     : ld16(static_cast<const float *>(wdv) + off);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (BF16) {
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          acc[2 * jj] = fmaf(cf[u], bf16lo(qv[u][jj]), acc[2 * jj]);
+          acc[2 * jj + 1] = fmaf(cf[u], bf16hi(qv[u][jj]), acc[2 * jj + 1]);
+        }
+      } else {
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) acc[jj] = fmaf(cf[u], __uint_as_float(qv[u][jj]), acc[jj]);
+      }
+    }
+  }
+}
+
+template <bool BF16, int SW>
+__device__ __forceinline__ void stream_rows(const void *__restrict__ wdv, const uint32_t *srow,
+                                            const float *scoef, int n, int H, size_t colo,
+                                            int wid, int rsel, float (&acc)[BF16 ? 8 : 4]) {
+  stream_rows_u<BF16, SW, 4>(wdv, srow, scoef, n, H, colo, wid, rsel, acc);
+}
+
+struct LayerSel {
+  const float *part;       // [nsplit, T, E] logit partials
+  int nsplit, norm_topk;
+  const float *bias;       // [E] or null
+};
+
+// Position of the n-th (0-based) set bit of w; w has more than n set bits.
+__device__ __forceinline__ int nth_set_bit(uint64_t w, int n) {
+  for (int i = 0; i < n; ++i) w &= w - 1;
+  return __ffsll((unsigned long long)w) - 1;
+}
+
+// ---------------------------------------------------------------- fused layer tail
+// The single-launch sparse FFN of decode batches (T <= 16): the gate/up
+// kernel's grid gets extra rows of "down units" (launch_ffn_fused), and the
+// two kinds of block meet through device-coherent memory instead of a
+// kernel boundary:
+//
+//   gate/up block (slot s, neuron tile)  writes its h tile with agent-scope
+//       stores, waits for them, then adds one to cnt_e[e] (e = the slot's
+//       expert); d_ff / 16 arrivals mean the expert's h is complete;
+//   down unit (pair p, column block c)   finds p's expert e, waits (bounded)
+//       for cnt_e[e] == d_ff / 16, selects the pair's k largest |h| with one
+//       wave (the exact radix select of the mask kernels), stages those rows
+//       in LDS, streams SW columns of each kept W_d row, and writes the
+//       weighted partial sum part[p, cols]; it then adds one to
+//       cnt_tc[t, c], and the unit that completes the token's top_k pairs
+//       sums their partials in slot order into y[t, cols] (+ the residual).
+//
+// Every wait is on blocks with lower linear ids (gate/up rows come first in
+// the grid), and each XCD dispatches its blocks in id order, so every waited
+// tile is dispatched ahead of its waiters and never waits itself: no
+// deadlock at any occupancy.  Waits are bounded anyway (wait_count).  The
+// counters are zeroed by the kernel before this launch on the same stream.
+// Down units run in pair order (routing from an earlier kernel: grouped by
+// expert, so the earliest experts' rows stream while later experts' gate/up
+// tiles still run; selection inside gate/up (VSEL): token-major).
+struct FusedArgs {
+  int gu_rows;           // grid rows of gate/up blocks; later rows are down units
+  int ncb;               // column blocks per pair (H / SW)
+  int npairs;            // T * top_k
+  int k;                 // kept neurons per pair (0 < k < d_ff, k <= kFusedMaxK)
+  const void *wd;        // W_d [E, d_ff, H]
+  float *part;           // [P, H] per-pair partial outputs (agent-coherent)
+  int32_t *cnt_e;        // [E * kCounterStride] finished gate/up tiles per expert
+  int32_t *cnt_tc;       // [T * ncb] finished pairs per (token, column block)
+  int32_t *abort_flag;   // [1] set when a bounded wait gives up
+  float *y;
+  int accumulate;
+  const void *xres;
+  void *xnext;
+  int32_t *idx_out;      // optional kept ids [P, k]
+};
+constexpr int kFusedMaxK = 1024;
+
+template <bool BF16, int SW, int V, int NWV>
+__device__ __forceinline__ void fused_down_unit(const FusedArgs &fa, const RouteView &rv,
+                                                const float *h, int H, int d_ff, int unit) {
+  constexpr int VEC = BF16 ? 8 : 4;
+  constexpr int LPR = SW / VEC;
+  static_assert(LPR <= 64 && 64 % LPR == 0, "a row run must fit one wave");
+  __shared__ uint32_t srow[kFusedMaxK];
+  __shared__ float scoef[kFusedMaxK];
+  __shared__ int hist[256];
+  __shared__ float red[NWV][SW];
+  __shared__ int s_ok, s_last;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  if (unit >= fa.npairs * fa.ncb) return;  // block-uniform
+  const int q = unit / fa.ncb, c = unit - q * fa.ncb;
+  const int K = rv.top_k, k = fa.k;
+  const int col0 = c * SW;
+  if (wid == 0) {
+    // the pair (routing from an earlier kernel, pairs grouped by expert), its
+    // expert and routing weight
+    int p = rv.pair_at(q);
+    p = (unsigned)p < (unsigned)fa.npairs ? p : 0;  // a corrupt routing stays in bounds
+    int e = rv.expert_of_pair(p);
+    e = (unsigned)e < (unsigned)rv.E ? e : 0;
+    const float w = rv.weight(p);
+    bool ok = true;
+    if (lane == 0) ok = wait_count(fa.cnt_e + (size_t)e * kCounterStride, d_ff / 16, fa.abort_flag);
+    ok = __shfl(ok ? 1 : 0, 0, 64) != 0;
+    compiler_barrier();
+    if (lane == 0) s_ok = ok ? p : -1;
+    if (ok) {
+      // the pair's activations, read coherently: lane holds V consecutive
+      const __amdgpu_buffer_rsrc_t rh = buf_rsrc(h + (size_t)p * d_ff, (uint32_t)d_ff * 4);
+      uint32_t bits[V];
+#pragma unroll
+      for (int i = 0; i < V; i += 4) {
+        const u32x4 qv = buf_ld16_agent(rh, (uint32_t)lane * V * 4, (uint32_t)i * 4);
+        bits[i] = qv[0]; bits[i + 1] = qv[1]; bits[i + 2] = qv[2]; bits[i + 3] = qv[3];
+      }
+      // exact k-th |h| by MSB-first radix passes over the float fields
+      uint32_t tau = 0, pmask = 0;
+      int krem = k;
+      bool whole = false;
+#pragma unroll
+      for (int pass = 0; pass < 4; ++pass) {
+        if (whole) continue;  // wave-uniform
+        const int shift = pass == 0 ? 23 : pass == 1 ? 15 : pass == 2 ? 7 : 0;
+        const uint32_t dmask = pass == 3 ? 0x7fu : 0xffu;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) hist[lane * 4 + b] = 0;
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+          const uint32_t key = bits[i] & 0x7fffffffu;
+          if ((key & pmask) == tau) atomicAdd(&hist[(key >> shift) & dmask], 1);
+        }
+        int cb[4], local = 0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          cb[b] = hist[255 - 4 * lane - b];
+          local += cb[b];
+        }
+        int run = wave_incl_scan(local) - local;
+        int dsel = -1, knew = 0, csel = 0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          if (dsel < 0 && run + cb[b] >= krem && run < krem) {
+            dsel = 255 - 4 * lane - b;
+            knew = krem - run;
+            csel = cb[b];
+          }
+          run += cb[b];
+        }
+        const uint64_t m = __ballot(dsel >= 0);
+        const int L = __ffsll((unsigned long long)m) - 1;  // exactly one lane
+        dsel = lane_value(dsel, L);
+        knew = lane_value(knew, L);
+        csel = lane_value(csel, L);
+        tau |= (uint32_t)dsel << shift;
+        pmask |= dmask << shift;
+        krem = knew;
+        whole = csel == knew && tau != 0u;
+      }
+      if (whole) {  // keep key >= tau: key > tau - 1, no equal ones
+        tau -= 1u;
+        krem = 0;
+      }
+      int ngt = 0, neq = 0;
+#pragma unroll
+      for (int i = 0; i < V; ++i) {
+        const uint32_t key = bits[i] & 0x7fffffffu;
+        ngt += key > tau;
+        neq += key == tau;
+      }
+      const int eq_before = wave_incl_scan(neq) - neq;
+      int pos = wave_incl_scan(ngt) - ngt + min(eq_before, krem);
+      int eq_seen = eq_before;
+      const uint32_t rbase = (uint32_t)e * (uint32_t)d_ff;
+      int32_t *io = (fa.idx_out && c == 0) ? fa.idx_out + (size_t)p * k : nullptr;
+      const int seg = lane * V;
+#pragma unroll
+      for (int i = 0; i < V; ++i) {
+        const uint32_t key = bits[i] & 0x7fffffffu;
+        const bool keep = key > tau || (key == tau && eq_seen++ < krem);
+        if (keep) {
+          if (pos < k) {  // always: exactly k keys are kept
+            srow[pos] = rbase + (uint32_t)(seg + i);
+            scoef[pos] = w * __uint_as_float(bits[i]);
+            if (io) io[pos] = seg + i;
+          }
+          ++pos;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  const int p = s_ok;
+  if (p < 0) return;  // block-uniform: a bounded wait gave up
+  const int sub = lane % LPR, rsel = lane / LPR;
+  const size_t colo = (size_t)col0 + sub * VEC;
+  float acc[VEC];
+#pragma unroll
+  for (int v = 0; v < VEC; ++v) acc[v] = 0.f;
+  stream_rows_u<BF16, SW, 4, NWV>(fa.wd, srow, scoef, k, H, colo, wid, rsel, acc);
+#pragma unroll
+  for (int o = LPR; o < 64; o <<= 1) {
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) acc[v] += __shfl_xor(acc[v], o, 64);
+  }
+  if (rsel == 0) {
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) red[wid][sub * VEC + v] = acc[v];
+  }
+  __syncthreads();
+  const int t = p / K;
+  if (tid < SW) {
+    float v = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < NWV; ++ww) v += red[ww][tid];
+    st_agent(fa.part + (size_t)p * H + col0 + tid, v);
+    wait_stores();
+  }
+  __syncthreads();
+  if (tid == 0) s_last = atomicAdd(fa.cnt_tc + (size_t)t * fa.ncb + c, 1) == K - 1;
+  __syncthreads();
+  if (!s_last) return;  // block-uniform
+  // the token's last pair for these columns: its top_k partials in slot order
+  compiler_barrier();
+  if (tid < SW) {
+    const size_t col = (size_t)col0 + tid;
+    float pv[16];  // top_k <= 16: every load in flight, then summed in slot order
+#pragma unroll
+    for (int s2 = 0; s2 < 16; ++s2)
+      pv[s2] = s2 < K ? ld_agent(fa.part + ((size_t)t * K + s2) * H + col) : 0.f;
+    float v = 0.f;
+#pragma unroll
+    for (int s2 = 0; s2 < 16; ++s2)
+      if (s2 < K) v += pv[s2];
+    const size_t o = (size_t)t * H + col;
+    const float out = fa.accumulate ? fa.y[o] + v : v;
+    fa.y[o] = out;
+    if (fa.xnext) residual_store<BF16>(fa.xres, fa.xnext, o, out);
+  }
+}
+
 // ---------------------------------------------------------------- gate / up
 // Block = one work item (an expert and up to 16 * MT of its tokens) x 16
 // neurons; W waves split K (H) by interleaved steps so that at any moment
@@ -61,26 +349,28 @@ namespace moe {
 // (0, 0) writes the routing outputs (ids and weights in slot order, the
 // grouping sorted by (expert, pair)).  The routing arrays in rv are then
 // written, not read, by this kernel.
-struct LayerSel {
-  const float *part;       // [nsplit, T, E] logit partials
-  int nsplit, norm_topk;
-  const float *bias;       // [E] or null
-};
-
-// Position of the n-th (0-based) set bit of w; w has more than n set bits.
-__device__ __forceinline__ int nth_set_bit(uint64_t w, int n) {
-  for (int i = 0; i < n; ++i) w &= w - 1;
-  return __ffsll((unsigned long long)w) - 1;
-}
-
-template <bool BF16, int MT, int W, bool GO = false, bool PF = false, int VSEL = 0>
+// FU (the fused tail above, FSW output columns per down unit, FV = d_ff / 64
+// activations per lane in its select): grid rows past fa.gu_rows are down
+// units; the gate/up blocks write h coherently and count their tiles.
+template <bool BF16, int MT, int W, bool GO = false, bool PF = false, int VSEL = 0, bool FU = false,
+          int FSW = 64, int FV = 16>
 __global__ __launch_bounds__(64 * W, MT == 1 ? 8 : 1) void gateup_swiglu_kernel(const void *__restrict__ xv,
                                                             const void *__restrict__ wgv,
                                                             const void *__restrict__ wuv,
                                                             RouteView rv, int H, int d_ff,
                                                             float *__restrict__ hout,
-                                                            LayerSel sel = LayerSel{}) {
+                                                            LayerSel sel = LayerSel{},
+                                                            FusedArgs fa = FusedArgs{}) {
   static_assert(VSEL == 0 || (MT == 1 && !GO), "selection runs in the one-tile form");
+  static_assert(!FU || (MT == 1 && !GO && VSEL == 0), "the fused tail follows the one-tile SwiGLU form");
+  if constexpr (FU) {
+    if ((int)blockIdx.y >= fa.gu_rows) {  // block-uniform: a down unit
+      fused_down_unit<BF16, FSW, FV, W>(fa, rv, hout, H, d_ff,
+                                        ((int)blockIdx.y - fa.gu_rows) * (int)gridDim.x +
+                                            (int)blockIdx.x);
+      return;
+    }
+  }
   __shared__ float red[W][2][MT][4][64];
   __shared__ int32_t s_pairc[16];  // VSEL: the pair of each tile column
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
@@ -343,8 +633,20 @@ __global__ __launch_bounds__(64 * W, MT == 1 ? 8 : 1) void gateup_swiglu_kernel(
       }
       const int neuron = row0 + 4 * (ln >> 4) + rr;
       const int p = VSEL > 0 ? s_pairc[c] : rv.pair_at(q0 + c);
-      hout[(size_t)p * d_ff + neuron] = GO ? silu(gs) : silu(gs) * us;
+      const float hv = GO ? silu(gs) : silu(gs) * us;
+      if (FU) st_agent(hout + (size_t)p * d_ff + neuron, hv);
+      else hout[(size_t)p * d_ff + neuron] = hv;
     }
+  }
+  if constexpr (FU) {  // this tile of expert e is complete and visible
+    // the counters follow h in the workspace: their address comes from hout,
+    // so the streaming loop above keeps no extra pointer live
+    const int eu = __builtin_amdgcn_readfirstlane(e);
+    wait_stores();
+    __syncthreads();
+    if (threadIdx.x == 0)
+      atomicAdd(reinterpret_cast<int32_t *>(hout + (size_t)rv.T * rv.top_k * d_ff) +
+                    (size_t)eu * kCounterStride, 1);
   }
 }
 
@@ -730,76 +1032,6 @@ __global__ __launch_bounds__(64) void up_rows_var_kernel(const void *__restrict_
   for (int i0 = blockIdx.y * kUpRows; i0 < n; i0 += gridDim.y * kUpRows)
     up_rows_group<BF16>(wuv, xv, rv, H, d_ff, p, i0, n, idx + (size_t)p * d_ff,
                         coef + (size_t)p * d_ff);
-}
-
-// ---------------------------------------------------------------- sparse down
-// The down kernels below share one inner loop: a block of kDownWaves waves
-// streams n staged rows (srow[q] = expert * d_ff + row, scoef[q] its
-// coefficient, both in LDS) of W_d, each row contributing one SW-element run
-// at column colo.  Wave wid takes row groups wid, wid + kDownWaves, ...
-// (RPI rows per group, one per LPR-lane slice) and issues U groups' 16-byte
-// loads before folding any of them into acc, so a lane has up to U loads in
-// flight.  U = 4: deeper rounds (8) measured no faster at decode batches
-// and raise the kernels to ~78 VGPRs, which halves the blocks a CU holds
-// at large batches (Llama-4-like T = 256 sparse: 1082 -> 1156 us).
-constexpr int kDownWaves = 16;
-constexpr int kDownStage = 4096;     // row-list entries staged in LDS
-
-// The residual stream's element o of the next layer's input: x_res + y
-// summed in fp32, rounded to the layer dtype (as residual_kernel does).
-template <bool BF16>
-__device__ __forceinline__ void residual_store(const void *xres, void *xnext, size_t o, float y) {
-  if (BF16) {
-    const uint32_t xb = static_cast<const uint16_t *>(xres)[o];
-    static_cast<uint16_t *>(xnext)[o] = (uint16_t)f32_to_bf16_bits(bf16lo(xb) + y);
-  } else {
-    static_cast<float *>(xnext)[o] = static_cast<const float *>(xres)[o] + y;
-  }
-}
-
-template <bool BF16, int SW, int U>
-__device__ __forceinline__ void stream_rows_u(const void *__restrict__ wdv,
-                                              const uint32_t *srow, const float *scoef, int n,
-                                              int H, size_t colo, int wid, int rsel,
-                                              float (&acc)[BF16 ? 8 : 4]) {
-  constexpr int VEC = BF16 ? 8 : 4;
-  constexpr int RPI = 64 / (SW / VEC);
-  for (int b0 = wid; b0 * RPI < n; b0 += kDownWaves * U) {
-    u32x4 qv[U];
-    float cf[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int qq = (b0 + kDownWaves * u) * RPI + rsel;
-      cf[u] = 0.f;
-      qv[u] = u32x4{0, 0, 0, 0};
-      if (qq < n) {
-        const size_t off = (size_t)srow[qq] * H + colo;
-        cf[u] = scoef[qq];
-        qv[u] = BF16 ? ld16(static_cast<const uint16_t *>(wdv) + off)
-                     : ld16(static_cast<const float *>(wdv) + off);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (BF16) {
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          acc[2 * jj] = fmaf(cf[u], bf16lo(qv[u][jj]), acc[2 * jj]);
-          acc[2 * jj + 1] = fmaf(cf[u], bf16hi(qv[u][jj]), acc[2 * jj + 1]);
-        }
-      } else {
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) acc[jj] = fmaf(cf[u], __uint_as_float(qv[u][jj]), acc[jj]);
-      }
-    }
-  }
-}
-
-template <bool BF16, int SW>
-__device__ __forceinline__ void stream_rows(const void *__restrict__ wdv, const uint32_t *srow,
-                                            const float *scoef, int n, int H, size_t colo,
-                                            int wid, int rsel, float (&acc)[BF16 ? 8 : 4]) {
-  stream_rows_u<BF16, SW, 4>(wdv, srow, scoef, n, H, colo, wid, rsel, acc);
 }
 
 // y[t, cols] (+)= sum over the token's pairs (slot order) and their kept rows
@@ -1535,6 +1767,107 @@ static void launch_down_topk(const FfnArgs &a, const RouteView &rv, hipStream_t 
   timer_end(stream);
 }
 
+// ---- the fused decode-batch FFN: gate/up, masks, down and combine in one
+// launch, from kFusedMinTokens tokens.  Measured per layer call against the
+// separate gate/up, mask and down kernels (OLMoE-like, same box, runs
+// alternating): 73.7 vs 75.5 us at 6 tokens, 82.7 vs 84.3 us at 8 and
+// 103.8 vs 107.3 us at 16, but 36.7 vs 34.4 us at one token: there the down
+// units wait resident through the whole weight stream and their polls slow
+// it, and the per-token down kernel that selects its own masks is as fast
+// as the units without the wait (34.3 us, measured and dropped).
+constexpr int kFusedMinTokens = 5;
+constexpr int kFusedMaxTokens = 16;
+static bool tail_units_shape_ok(const FfnArgs &a) {
+  const int V = a.d_ff / 64;
+  // d_ff 512, 768, 1024, 1536 (at 2048 the fused kernel spills in its loop)
+  return !a.implicit && a.T >= 1 && a.T <= kFusedMaxTokens && a.top_k <= 16 &&
+         a.d_ff % 256 == 0 && (V == 8 || V == 12 || V == 16 || V == 24) &&
+         a.k_keep > 0 && a.k_keep < a.d_ff && a.k_keep <= kFusedMaxK && a.H % 64 == 0 &&
+         a.fpart != nullptr &&
+         // the gate/up blocks find the counters right after h
+         a.sync == reinterpret_cast<int32_t *>(a.h + (size_t)a.T * a.top_k * a.d_ff);
+}
+bool fused_ffn_ok(const FfnArgs &a) { return tail_units_shape_ok(a) && a.T >= kFusedMinTokens; }
+
+// Output columns per down unit: at least 512 units where the hidden size
+// allows (each unit streams SW columns of the pair's k rows), never below
+// 128-byte runs; 64 columns at one or two tokens.
+static int fused_cols(const FfnArgs &a) {
+  const long P = (long)a.T * a.top_k;
+  if (a.T > 2 && a.H % 256 == 0 && P * (a.H / 256) >= 512) return 256;
+  if (a.T > 2 && a.H % 128 == 0 && P * (a.H / 128) >= 512) return 128;
+  return 64;
+}
+
+__global__ __launch_bounds__(256) void zero_i32_kernel(int32_t *__restrict__ p, int n) {
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) p[i] = 0;
+}
+
+template <bool BF, int SWV, int FVV>
+static void fused_inst(const FfnArgs &a, const RouteView &rv, const FusedArgs &fa, dim3 grid,
+                       hipStream_t stream) {
+  gateup_swiglu_kernel<BF, 1, 8, false, true, 0, true, SWV, FVV><<<grid, 512, 0, stream>>>(
+      a.x, a.w_gate, a.w_up, rv, a.H, a.d_ff, a.h, LayerSel{}, fa);
+}
+template <bool BF, int SWV>
+static void fused_v(const FfnArgs &a, const RouteView &rv, const FusedArgs &fa, dim3 grid,
+                    hipStream_t stream) {
+  switch (a.d_ff / 64) {
+    case 8: fused_inst<BF, SWV, 8>(a, rv, fa, grid, stream); break;
+    case 12: fused_inst<BF, SWV, 12>(a, rv, fa, grid, stream); break;
+    case 16: fused_inst<BF, SWV, 16>(a, rv, fa, grid, stream); break;
+    default: fused_inst<BF, SWV, 24>(a, rv, fa, grid, stream); break;
+  }
+}
+template <bool BF>
+static void fused_sw(const FfnArgs &a, const RouteView &rv, const FusedArgs &fa, int sw,
+                     dim3 grid, hipStream_t stream) {
+  if (sw == 256) fused_v<BF, 256>(a, rv, fa, grid, stream);
+  else if (sw == 128) fused_v<BF, 128>(a, rv, fa, grid, stream);
+  else fused_v<BF, 64>(a, rv, fa, grid, stream);
+}
+
+static FusedArgs fused_args(const FfnArgs &a, int gu_rows, int ncb) {
+  FusedArgs fa;
+  fa.gu_rows = gu_rows;
+  fa.ncb = ncb;
+  fa.npairs = a.T * a.top_k;
+  fa.k = a.k_keep;
+  fa.wd = a.w_down;
+  fa.part = a.fpart;
+  fa.cnt_e = a.sync;
+  fa.cnt_tc = a.sync + (size_t)a.E * kCounterStride;
+  fa.abort_flag = fa.cnt_tc + (size_t)a.T * (a.H / 64);
+  fa.y = a.y;
+  fa.accumulate = a.accumulate;
+  fa.xres = a.xres;
+  fa.xnext = a.xnext;
+  fa.idx_out = a.want_idx ? a.idx : nullptr;
+  return fa;
+}
+
+// The fused launch (fused_ffn_ok); the routing comes from an earlier kernel.
+static hipError_t launch_ffn_fused(const FfnArgs &a, const RouteView &rv, hipStream_t stream) {
+  const int P = a.T * a.top_k;
+  const int sw = fused_cols(a);
+  const int nt = a.d_ff / 16;
+  const int gu_rows = a.E < P ? a.E : P;
+  const int ncb = a.H / sw;
+  const int down_rows = (P * ncb + nt - 1) / nt;
+  const int nsync = (int)fused_sync_words(a.T, a.E, a.H);
+  if (!a.sync_zeroed) zero_i32_kernel<<<(nsync + 255) / 256, 256, 0, stream>>>(a.sync, nsync);
+  const FusedArgs fa = fused_args(a, gu_rows, ncb);
+  dim3 grid(nt, gu_rows + down_rows);
+  // the gate/up blocks load through buffer resources at every batch here:
+  // the plain form sits at the 64-register limit and, with the fused tail
+  // in the same kernel, spilled inside its streaming loop
+  timer_begin(kStageFused, stream);
+  if (a.bf16) fused_sw<true>(a, rv, fa, sw, grid, stream);
+  else fused_sw<false>(a, rv, fa, sw, grid, stream);
+  timer_end(stream);
+  return hipGetLastError();
+}
+
 hipError_t launch_ffn_sparse(const FfnArgs &a, hipStream_t stream) {
   if (a.T == 0) return hipSuccess;
   if (zero_contribution(a, stream)) {
@@ -1542,6 +1875,7 @@ hipError_t launch_ffn_sparse(const FfnArgs &a, hipStream_t stream) {
     return hipGetLastError();
   }
   const RouteView rv = make_view(a);
+  if (fused_ffn_ok(a)) return launch_ffn_fused(a, rv, stream);
   launch_gateup(a, rv, stream);
   if (fused_topk_ok(a)) {
     launch_down_topk(a, rv, stream);
@@ -1573,8 +1907,8 @@ bool layer_small_ok(const RouteArgs &r, const FfnArgs &a) {
 
 hipError_t launch_layer_small(const RouteArgs &r, const FfnArgs &a, hipStream_t stream) {
   if (!layer_small_ok(r, a)) return hipErrorInvalidValue;
-  const int nsplit = launch_router_logits(r, stream);
   const RouteView rv = make_view(a);
+  const int nsplit = launch_router_logits(r, stream);
   const LayerSel sel{r.logits, nsplit, r.norm_topk, r.bias};
   const int P = a.T * a.top_k;
   dim3 grid(a.d_ff / 16, a.E < P ? a.E : P);

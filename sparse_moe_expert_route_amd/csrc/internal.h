@@ -33,7 +33,7 @@ inline void timer_end(hipStream_t s) {
 
 // Stage ids (mirror moe_stage in the public header).
 enum { kStageLogits = 0, kStageTopk, kStageGroup, kStageGateup, kStageMask, kStageDownRows,
-       kStageDownDense, kStageCombine, kStageZero, kStageUpRows };
+       kStageDownDense, kStageCombine, kStageZero, kStageUpRows, kStageFused };
 
 // Roster routing state (usage == nullptr: plain routing).
 struct RosterArgs {
@@ -52,6 +52,10 @@ struct RouteArgs {
   int32_t *topk_ids;
   float *topk_w;
   int32_t *offsets, *pair_by_expert, *active, *n_active;
+  // optional: words the logits kernel zeroes (the counters of a fused FFN
+  // launch that follows on the stream); null to skip
+  int32_t *zero = nullptr;
+  int nzero = 0;
 };
 
 // Router split-K: logits are written as kRouterSplits-at-most partials.
@@ -82,7 +86,24 @@ struct FfnArgs {
   // the layer dtype, written where each y element is final; null to skip
   const void *xres;
   void *xnext;
+  // the fused decode-batch FFN (sparse path): per-pair partial outputs
+  // [P, H] and its counters (kFusedSyncWords(T, E, H) words), zero before
+  // the launch; sync_zeroed says an earlier kernel of the call zeroed them
+  float *fpart;
+  int32_t *sync;
+  int sync_zeroed;
 };
+
+// Counter words of the fused FFN: per expert (each on its own 256-byte
+// line: waiting blocks poll them, and pollers of one line all land on one
+// memory channel), per (token, 64-column block), and one abort flag.
+constexpr int kCounterStride = 64;
+inline size_t fused_sync_words(int T, int E, int H) {
+  return (size_t)E * kCounterStride + (size_t)T * (H / 64) + 1;
+}
+// Whether the fused single-launch FFN takes a sparse call with these shapes
+// (then an earlier kernel of the call may zero its counters).
+bool fused_ffn_ok(const FfnArgs &a);
 
 // Device address of the static scratch of moe_layer_sparse_noalloc on the
 // current device (looked up once per device).

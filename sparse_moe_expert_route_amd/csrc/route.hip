@@ -21,8 +21,13 @@ template <bool BF16, int MT>
 __global__ __launch_bounds__(256) void router_logits_kernel(const void *__restrict__ xv,
                                                             const void *__restrict__ wv, int T,
                                                             int H, int E,
-                                                            float *__restrict__ partial) {
+                                                            float *__restrict__ partial,
+                                                            int32_t *__restrict__ zero = nullptr,
+                                                            int nzero = 0) {
   __shared__ float red[4][MT][4][64];
+  // the fused FFN kernel that follows on this stream counts into these words
+  if (zero && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0)
+    for (int i = threadIdx.x; i < nzero; i += 256) zero[i] = 0;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int e0 = blockIdx.x * 16, t0 = blockIdx.y * 16 * MT;
@@ -334,11 +339,11 @@ int launch_router_logits(const RouteArgs &a, hipStream_t stream) {
   dim3 g1((a.E + 15) / 16, (a.T + (one ? 16 : 64) - 1) / (one ? 16 : 64), nsplit);
   timer_begin(kStageLogits, stream);
   if (a.bf16) {
-    if (one) router_logits_kernel<true, 1><<<g1, 256, 0, stream>>>(a.x, a.w_router, a.T, a.H, a.E, a.logits);
-    else router_logits_kernel<true, 4><<<g1, 256, 0, stream>>>(a.x, a.w_router, a.T, a.H, a.E, a.logits);
+    if (one) router_logits_kernel<true, 1><<<g1, 256, 0, stream>>>(a.x, a.w_router, a.T, a.H, a.E, a.logits, a.zero, a.nzero);
+    else router_logits_kernel<true, 4><<<g1, 256, 0, stream>>>(a.x, a.w_router, a.T, a.H, a.E, a.logits, a.zero, a.nzero);
   } else {
-    if (one) router_logits_kernel<false, 1><<<g1, 256, 0, stream>>>(a.x, a.w_router, a.T, a.H, a.E, a.logits);
-    else router_logits_kernel<false, 4><<<g1, 256, 0, stream>>>(a.x, a.w_router, a.T, a.H, a.E, a.logits);
+    if (one) router_logits_kernel<false, 1><<<g1, 256, 0, stream>>>(a.x, a.w_router, a.T, a.H, a.E, a.logits, a.zero, a.nzero);
+    else router_logits_kernel<false, 4><<<g1, 256, 0, stream>>>(a.x, a.w_router, a.T, a.H, a.E, a.logits, a.zero, a.nzero);
   }
   timer_end(stream);
   return nsplit;
