@@ -401,7 +401,8 @@ class StageTimer:
     plumbing for measurement; events come from the process's HIP runtime."""
 
     STAGES = ["router_logits", "router_topk", "route_group", "gateup_swiglu", "neuron_topk",
-              "down_rows", "down_dense", "combine", "zero", "up_rows", "fused_ffn"]
+              "down_rows", "down_dense", "combine", "zero", "up_rows", "fused_ffn",
+              "union_rows", "down_union"]
 
     def __init__(self, capacity: int):
         lib()

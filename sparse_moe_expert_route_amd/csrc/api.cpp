@@ -80,7 +80,8 @@ size_t elem_bytes(const moe_desc *d) { return d->dtype == MOE_BF16 ? 2 : 4; }
 
 // FFN workspace layout (each segment 256-byte aligned).
 struct FfnLayout {
-  size_t h, idx, hact, partial, hm, fpart, sync, counts, total;
+  size_t h, idx, hact, partial, hm, fpart, sync, urow, ucnt, hmu, ubuf, counts, total;
+  bool has_union;
 };
 
 // What an FFN-shaped call does (all share validation and the carve-up).
@@ -107,8 +108,20 @@ FfnLayout ffn_layout(const moe_desc *d, int32_t T, int32_t k, moe_path path) {
   off += up(P * (size_t)k * 4);
   L.hact = off;
   if (path == MOE_PATH_SPARSE) off += up(P * (size_t)k * 4);
+  // the packed-rows down projection of the sparse path (larger batches):
+  // union lists, union counts, compacted coefficients, and the partials
+  // the dense-path down GEMM also uses
+  L.has_union = path == MOE_PATH_SPARSE && moe::union_layout_ok(T, d->hidden, d->d_ff, bf16);
+  L.urow = off;
+  if (L.has_union) off += up((size_t)d->n_experts * d->d_ff * 4);
+  L.ucnt = off;
+  if (L.has_union) off += up((size_t)d->n_experts * 4);
+  L.hmu = off;
+  if (L.has_union) off += up(P * d->d_ff * 2);
+  L.ubuf = off;
+  if (L.has_union) off += up(moe::union_scratch_words(T, d->n_experts, d->d_ff) * 4);
   L.partial = off;
-  if (path == MOE_PATH_DENSE && bf16)
+  if ((path == MOE_PATH_DENSE && bf16) || L.has_union)
     off += up(moe::dense_down_partial_rows(T, d->n_experts, d->top_k, d->hidden) * d->hidden * 4);
   L.hm = off;
   if (path == MOE_PATH_DENSE) off += up(P * d->d_ff * elem_bytes(d));
@@ -247,6 +260,12 @@ moe_status run_ffn(RunMode mode, const moe_desc *d, int32_t T, int32_t k_keep, c
   a.fpart = path == MOE_PATH_SPARSE ? reinterpret_cast<float *>(ws + L.fpart) : nullptr;
   a.sync = path == MOE_PATH_SPARSE ? reinterpret_cast<int32_t *>(ws + L.sync) : nullptr;
   a.sync_zeroed = 0;
+  if (L.has_union) {
+    a.urow = reinterpret_cast<int32_t *>(ws + L.urow);
+    a.ucnt = reinterpret_cast<int32_t *>(ws + L.ucnt);
+    a.hmu = reinterpret_cast<uint16_t *>(ws + L.hmu);
+    a.ubuf = reinterpret_cast<uint32_t *>(ws + L.ubuf);
+  }
   hipError_t e;
   switch (mode) {
     case kRunUpdown: e = moe::launch_ffn_updown(a, stream); break;

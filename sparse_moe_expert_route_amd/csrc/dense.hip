@@ -29,6 +29,12 @@ __device__ __forceinline__ unsigned xcd_logical_block() {
   return xcd * per + (xcd < rem ? xcd : rem) + slot;
 }
 
+// A compile-time int for the kernels' step lambdas.
+template <int V>
+struct SkIc {
+  static constexpr int value = V;
+};
+
 // ---------------------------------------------------------------- gate / up GEMM
 // Grouped GEMM for batches where an expert holds many tokens: work item =
 // one expert and up to 128 of its tokens, block = 4 waves x 64 neurons
@@ -65,15 +71,17 @@ __global__ __launch_bounds__(256, 2) void gateup_gemm_kernel(const void *__restr
   const int nsteps = H / KS;                // even: H is a multiple of 64
   const int nit = nsteps / 2;               // stages of two k-steps
 
-  // staging map: token rows tid / 8 + 32 i (i < 4), 16-byte chunk tid % 8
+  // staging map: token rows tid / 8 + 32 i (i < 4), 16-byte chunk tid % 8.
+  // Rows past the item's tokens stage the first token's row (every load is
+  // issued unconditionally, so that the compiler's waits count the loads in
+  // flight); they only feed accumulator rows that are never stored.
   const int srow = tid >> 3, schunk = tid & 7;
   const uint8_t *xrow[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int c = srow + 32 * i;
-    xrow[i] = c < ntok ? static_cast<const uint8_t *>(xv) +
-                             (size_t)(rv.pair_at(q0 + c) / rv.top_k) * H * EB + schunk * 16
-                       : nullptr;
+    xrow[i] = static_cast<const uint8_t *>(xv) +
+              (size_t)(rv.pair_at(q0 + (c < ntok ? c : 0)) / rv.top_k) * H * EB + schunk * 16;
   }
   const int nt = (by * 4 + wid) * NTW;     // this wave's first neuron tile
   const size_t tstride = (size_t)nsteps * 1024;   // bytes of one neuron tile
@@ -89,7 +97,7 @@ __global__ __launch_bounds__(256, 2) void gateup_gemm_kernel(const void *__restr
 
   u32x4 stg[4], ag[NTW][2], au[NTW][2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) stg[i] = xrow[i] ? ld16(xrow[i]) : u32x4{0, 0, 0, 0};
+  for (int i = 0; i < 4; ++i) stg[i] = ld16(xrow[i]);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     *reinterpret_cast<u32x4 *>(&xs[0][(srow + 32 * i) * kGemmRowB + schunk * 16]) = stg[i];
@@ -103,14 +111,14 @@ __global__ __launch_bounds__(256, 2) void gateup_gemm_kernel(const void *__restr
   __syncthreads();
 
   const int r = lane & 15, g = lane >> 4;
-  for (int it = 0; it < nit; ++it) {
+  // steady steps (it + 1 < nit: no branch around the loads), then the last
+  auto step = [&](int it, auto steadyc) {
+    constexpr bool more = decltype(steadyc)::value;
     const int cur = it & 1;
-    const bool more = it + 1 < nit;
     u32x4 ng[NTW][2], nu[NTW][2];
     if (more) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        stg[i] = xrow[i] ? ld16(xrow[i] + (size_t)(it + 1) * 128) : u32x4{0, 0, 0, 0};
+      for (int i = 0; i < 4; ++i) stg[i] = ld16(xrow[i] + (size_t)(it + 1) * 128);
 #pragma unroll
       for (int j = 0; j < NTW; ++j)
 #pragma unroll
@@ -142,8 +150,8 @@ __global__ __launch_bounds__(256, 2) void gateup_gemm_kernel(const void *__restr
       }
     };
     // Each token fragment is read from LDS one tile ahead of its MFMAs, so
-    // the LDS latency overlaps the matrix work instead of stalling it (rows
-    // past the item's tokens hold zeros, so the read ahead is harmless).
+    // the LDS latency overlaps the matrix work instead of stalling it (a
+    // read past the item's last tile feeds no MFMA).
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       u32x4 b = bfrag(k, 0);
@@ -166,8 +174,17 @@ __global__ __launch_bounds__(256, 2) void gateup_gemm_kernel(const void *__restr
         for (int k = 0; k < 2; ++k) { ag[j][k] = ng[j][k]; if (!GO) au[j][k] = nu[j][k]; }
     }
     __syncthreads();
-  }
+  };
+  for (int it = 0; it + 1 < nit; ++it) step(it, SkIc<1>{});
+  if (nit > 0) step(nit - 1, SkIc<0>{});
 
+  // the pair ids of the lane's 8 token columns, all read before the stores
+  int prow[8];
+#pragma unroll
+  for (int tl = 0; tl < 8; ++tl) {
+    const int c = tl * 16 + r;
+    prow[tl] = rv.pair_at(q0 + (c < ntok ? c : 0));
+  }
 #pragma unroll
   for (int j = 0; j < NTW; ++j) {
     const int neuron0 = (nt + j) * 16 + 4 * g;
@@ -175,7 +192,7 @@ __global__ __launch_bounds__(256, 2) void gateup_gemm_kernel(const void *__restr
     for (int tl = 0; tl < 8; ++tl) {
       const int c = tl * 16 + r;
       if (tl < ntiles && c < ntok) {
-        const int p = rv.pair_at(q0 + c);
+        const int p = prow[tl];
         f32x4 hv;
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr)
@@ -205,11 +222,20 @@ constexpr int kDnBrow = kDnK * 2;           // LDS bytes per transposed W_d colu
 
 __device__ __forceinline__ int dn_swz(int col) { return 4 * ((col & 7) ^ ((col >> 3) & 7)); }
 
+// UNION: the sparse path's packed-rows form.  k runs over the union of the
+// kept rows of the item's expert (urow[e * d_ff ..], ascending, ucnt[e] of
+// them) instead of every row: B gathers those W_d rows (two row indices per
+// thread per stage, loaded one stage ahead), A is the masked activations
+// compacted to the same positions (hm = the union kernel's hmu, zero-padded
+// to a multiple of kDnK).  Rows past the union are never read.
+template <bool UNION = false>
 __global__ __launch_bounds__(256, 2) void down_dense_gemm_kernel(const uint16_t *__restrict__ wd,
                                                                  const uint16_t *__restrict__ hm,
                                                                  RouteView rv, int H, int d_ff,
                                                                  int kchunk,
-                                                                 float *__restrict__ partial) {
+                                                                 float *__restrict__ partial,
+                                                                 const int32_t *__restrict__ urow = nullptr,
+                                                                 const int32_t *__restrict__ ucnt = nullptr) {
   __shared__ __attribute__((aligned(16))) uint8_t as[2][kDnTok * kDnArow];
   __shared__ __attribute__((aligned(16))) uint32_t bs[2][kDnCols * kDnBrow / 4];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -219,28 +245,77 @@ __global__ __launch_bounds__(256, 2) void down_dense_gemm_kernel(const uint16_t 
   if (!find_item<kDnTok>(rv, bx, e, q0, ntok)) return;  // block-uniform
   const int col0 = by * kDnCols;
   const int S = gridDim.z, sidx = (int)(qb / (gridDim.x * gridDim.y));
+  int uc = d_ff, kend = d_ff;
+  if (UNION) {  // the chunks split the union, whose size only the device knows
+    uc = ucnt[e];
+    uc = uc < 0 ? 0 : (uc > d_ff ? d_ff : uc);
+    kend = (uc + kDnK - 1) / kDnK * kDnK;  // hm is zero past uc up to here
+    kchunk = ((uc + S - 1) / S + kDnK - 1) / kDnK * kDnK;
+  }
   const int k0 = sidx * kchunk;
-  const int nit = (min(d_ff, k0 + kchunk) - k0) / kDnK;
+  const int nit = max(0, (min(kend, k0 + kchunk) - k0) / kDnK);
   const int ntiles = (ntok + 15) >> 4;
 
+  // Every load is issued unconditionally, so that the compiler's waits
+  // count the loads in flight instead of draining them.  A rows past the
+  // item's tokens read the first token's row: they only feed accumulator
+  // rows that are never stored.
   // A staging: rows tid / 8 + 32 i (i < 4), 16-byte chunk tid % 8 (8 k)
   const int arow = tid >> 3, achunk = tid & 7;
   const uint16_t *ap[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int c = arow + 32 * i;
-    ap[i] = c < ntok ? hm + (size_t)rv.pair_at(q0 + c) * d_ff + k0 + achunk * 8 : nullptr;
+    ap[i] = hm + (size_t)rv.pair_at(q0 + (c < ntok ? c : 0)) * d_ff + k0 + achunk * 8;
   }
   // B staging: k-pair kp = tid / 8 (rows 2 kp, 2 kp + 1), columns 8 cg .. 8 cg + 7
   const int kp = tid >> 3, cg = tid & 7;
   const uint16_t *bp = wd + ((size_t)e * d_ff + k0 + 2 * kp) * H + col0 + 8 * cg;
+  // UNION: the stage's two union rows, their ids read one stage ahead;
+  // positions past the union count read the union's first row and are
+  // staged as zeros
+  const uint16_t *bcol = wd + (size_t)e * d_ff * H + col0 + 8 * cg;
+  const int32_t *ur = UNION ? urow + (size_t)e * d_ff : nullptr;
+  int row0 = 0;
+  if (UNION && uc > 0) row0 = min(max(ur[0], 0), d_ff - 1);
+  int rn[2] = {0, 0};  // row ids of the next stage, in flight
+  int rw[2] = {0, 0};  // row ids of the stage being loaded
+  uint32_t rok = 0u, sok = 0u;  // their validity bits (rw, then the staged set)
+  auto fetch_rows = [&](int it) {  // q + 1 < kend <= d_ff: inside e's list
+    const int q = k0 + it * kDnK + 2 * kp;
+    rn[0] = ur[q];
+    rn[1] = ur[q + 1];
+  };
+  auto take_rows = [&](int it) {
+    const int q = k0 + it * kDnK + 2 * kp;
+    rok = 0u;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const bool ok = q + i < uc && (unsigned)rn[i] < (unsigned)d_ff;
+      rw[i] = ok ? rn[i] : row0;
+      rok |= ok ? 1u << i : 0u;
+    }
+  };
+  if (UNION && nit > 0) {
+    fetch_rows(0);
+    take_rows(0);
+    fetch_rows(min(1, nit - 1));
+  }
 
   u32x4 sa[4], sb[2];
   auto load_stage = [&](int it) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sa[i] = ap[i] ? ld16(ap[i] + it * kDnK) : u32x4{0, 0, 0, 0};
-    sb[0] = ld16_nt(bp + (size_t)it * kDnK * H);
-    sb[1] = ld16_nt(bp + (size_t)it * kDnK * H + H);
+    for (int i = 0; i < 4; ++i) sa[i] = ld16(ap[i] + it * kDnK);
+    if (UNION) {
+      sb[0] = ld16_nt(bcol + (size_t)rw[0] * H);
+      sb[1] = ld16_nt(bcol + (size_t)rw[1] * H);
+      sok = rok;
+      take_rows(min(it + 1, nit - 1));
+      fetch_rows(min(it + 2, nit - 1));
+    } else {
+      sb[0] = ld16_nt(bp + (size_t)it * kDnK * H);
+      sb[1] = ld16_nt(bp + (size_t)it * kDnK * H + H);
+    }
   };
   auto store_stage = [&](int buf) {
 #pragma unroll
@@ -248,8 +323,12 @@ __global__ __launch_bounds__(256, 2) void down_dense_gemm_kernel(const uint16_t 
       *reinterpret_cast<u32x4 *>(&as[buf][(arow + 32 * i) * kDnArow + achunk * 16]) = sa[i];
 #pragma unroll
     for (int c = 0; c < 8; ++c) {  // column 8 cg + c gets the pair (row 2 kp, row 2 kp + 1)
-      const uint32_t lo = (sb[0][c >> 1] >> (16 * (c & 1))) & 0xffffu;
-      const uint32_t hi = (sb[1][c >> 1] >> (16 * (c & 1))) & 0xffffu;
+      uint32_t lo = (sb[0][c >> 1] >> (16 * (c & 1))) & 0xffffu;
+      uint32_t hi = (sb[1][c >> 1] >> (16 * (c & 1))) & 0xffffu;
+      if (UNION) {
+        lo = sok & 1u ? lo : 0u;
+        hi = sok & 2u ? hi : 0u;
+      }
       const int col = 8 * cg + c;
       bs[buf][col * (kDnBrow / 4) + (kp ^ dn_swz(col))] = lo | (hi << 16);
     }
@@ -266,9 +345,10 @@ __global__ __launch_bounds__(256, 2) void down_dense_gemm_kernel(const uint16_t 
     store_stage(0);
   }
   __syncthreads();
-  for (int it = 0; it < nit; ++it) {
+  // steady steps (it + 1 < nit: no branch around the loads), then the last
+  auto step = [&](int it, auto steadyc) {
+    constexpr bool more = decltype(steadyc)::value;
     const int cur = it & 1;
-    const bool more = it + 1 < nit;
     if (more) load_stage(it + 1);
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
@@ -298,8 +378,19 @@ __global__ __launch_bounds__(256, 2) void down_dense_gemm_kernel(const uint16_t 
     }
     if (more) store_stage(cur ^ 1);
     __syncthreads();
-  }
-  // D: lane holds column r of each column tile, token rows 4 g + rr of each token tile
+  };
+  for (int it = 0; it + 1 < nit; ++it) step(it, SkIc<1>{});
+  if (nit > 0) step(nit - 1, SkIc<0>{});
+  // D: lane holds column r of each column tile, token rows 4 g + rr of each
+  // token tile; the rows' pair ids are all read before the first store
+  int prow[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int c = (4 * wt + i) * 16 + 4 * g + rr;
+      prow[i][rr] = rv.pair_at(q0 + (c < ntok ? c : 0));
+    }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int tl = 4 * wt + i;
@@ -308,13 +399,285 @@ __global__ __launch_bounds__(256, 2) void down_dense_gemm_kernel(const uint16_t 
     for (int rr = 0; rr < 4; ++rr) {
       const int c = tl * 16 + 4 * g + rr;
       if (c < ntok) {
-        const size_t row = (size_t)rv.pair_at(q0 + c) * S + sidx;
+        const size_t row = (size_t)prow[i][rr] * S + sidx;
 #pragma unroll
         for (int j = 0; j < 2; ++j)
           partial[row * H + col0 + (2 * wc + j) * 16 + r] = acc[i][j][rr];
       }
     }
   }
+}
+
+// ---------------------------------------------------------------- skinny down GEMM
+// The down product for items of at most 16 * MT tokens of one expert (a few
+// tokens per expert: HBM-bound on W_d).  Block = 4 waves x 256 output
+// columns x one K chunk; stage = 64 W_d rows x 256 columns (32 KB).  Each
+// thread loads 8 rows x 8 columns (8 x 16 B, one stage ahead in registers,
+// so a block keeps 32 KB in flight), transposes them in registers into 8
+// k-contiguous 16-byte column fragments (the MFMA B layout) and writes
+// those to LDS: column stride 144 B, 16-byte slot = k-chunk ^ ((col >> 4) &
+// 7), which keeps both the writes and the fragment reads free of bank
+// conflicts.  The coefficients (A: token rows, k-contiguous) come straight
+// from global memory in the MFMA layout, also one stage ahead.  Wave w
+// owns columns 64 w .. 64 w + 63 (4 column tiles) for all MT token tiles.
+// UNION: as in down_dense_gemm_kernel, k runs over the expert's union of
+// kept rows (urow, ucnt), whose row ids each thread fetches two stages
+// ahead; hm is then the compacted coefficient rows (hmu).
+constexpr int kSkCols = 256;   // output columns per block
+constexpr int kSkK = 64;       // k per stage
+constexpr int kSkColB = 144;   // LDS bytes per staged column (128 + 16 pad)
+#ifndef MOE_SKINNY_DEPTH
+#define MOE_SKINNY_DEPTH 2
+#endif
+// W_d stages in flight per thread (one where two would spill registers)
+template <int MT, bool UNION>
+constexpr int sk_depth() { return MT == 4 && UNION ? 1 : MOE_SKINNY_DEPTH; }
+
+__device__ __forceinline__ int sk_off(int col, int chunk) {
+  return col * kSkColB + ((chunk ^ ((col >> 4) & 7)) << 4);
+}
+
+template <int MT, bool UNION, int DEPTH>
+__global__ __launch_bounds__(256, 2) void down_skinny_kernel(const uint16_t *__restrict__ wd,
+                                                             const uint16_t *__restrict__ hm,
+                                                             RouteView rv, int H, int d_ff,
+                                                             int kchunk,
+                                                             float *__restrict__ partial,
+                                                             const int32_t *__restrict__ urow,
+                                                             const int32_t *__restrict__ ucnt) {
+  __shared__ __attribute__((aligned(16))) uint8_t bs[2][kSkCols * kSkColB];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  int e, q0, ntok;
+  const unsigned qb = xcd_logical_block();
+  const int bx = (int)(qb % gridDim.x), by = (int)(qb / gridDim.x % gridDim.y);
+  if (!find_item<16 * MT>(rv, bx, e, q0, ntok)) return;  // block-uniform
+  const int col0 = by * kSkCols;
+  const int S = gridDim.z, sidx = (int)(qb / (gridDim.x * gridDim.y));
+  int uc = d_ff, kend = d_ff;
+  if (UNION) {  // the chunks split the union, whose size only the device knows
+    uc = ucnt[e];
+    uc = uc < 0 ? 0 : (uc > d_ff ? d_ff : uc);
+    kend = (uc + kSkK - 1) / kSkK * kSkK;  // hm is zero past uc up to here
+    kchunk = ((uc + S - 1) / S + kSkK - 1) / kSkK * kSkK;
+  }
+  const int k0 = sidx * kchunk;
+  const int nit = max(0, (min(kend, k0 + kchunk) - k0) / kSkK);
+
+  // B: rows 8 rg .. 8 rg + 7 of a stage, columns col0 + 8 cg .. + 7
+  const int rg = tid >> 5, cg = tid & 31;
+  // Every load below is issued unconditionally (lanes without work read a
+  // valid stand-in address), so that the compiler's waits can count the
+  // loads still in flight instead of draining them all.  Columns past H
+  // (H is a multiple of 64) read column block col0 and only feed output
+  // columns that are never stored; token rows past the item read the first
+  // token's row and only feed accumulator rows that are never stored.
+  const bool colok = col0 + 8 * cg < H;
+  const uint16_t *bcol = wd + (size_t)e * d_ff * H + (colok ? col0 + 8 * cg : col0);
+  // A: token 16 mt + r of the item, k = 8 g .. 8 g + 7 of each 32-k step
+  const int r = lane & 15, g = lane >> 4;
+  const uint16_t *ap[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int c = 16 * mt + r;
+    ap[mt] = hm + (size_t)rv.pair_at(q0 + (c < ntok ? c : 0)) * d_ff + k0 + 8 * g;
+  }
+  // UNION: positions past the union count (up to the 64-row stage) read the
+  // union's first row, and their W_d values are replaced by zeros
+  const int32_t *ur = UNION ? urow + (size_t)e * d_ff : nullptr;
+  int row0 = 0;
+  if (UNION && uc > 0) row0 = min(max(ur[0], 0), d_ff - 1);
+  int rows[8];           // UNION: row ids of the stage to load next
+  uint32_t rvalid = 0u;  // UNION: bit i: rows[i] lies inside the union
+  u32x4 rn[2];      // UNION: row ids of the stage after that, in flight
+  auto fetch_rows = [&](int it) {  // q + 8 <= kend <= d_ff: inside e's list
+    const int q = k0 + it * kSkK + 8 * rg;
+    rn[0] = ld16(ur + q);
+    rn[1] = ld16(ur + q + 4);
+  };
+  auto take_rows = [&](int it) {
+    const int q = k0 + it * kSkK + 8 * rg;
+    rvalid = 0u;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int v = (int)rn[i >> 2][i & 3];
+      const bool ok = q + i < uc && (unsigned)v < (unsigned)d_ff;
+      rows[i] = ok ? v : row0;
+      rvalid |= ok ? 1u << i : 0u;
+    }
+  };
+
+  // W_d stages in flight: DEPTH register sets (stage it + DEPTH is issued
+  // while stage it is multiplied); coefficients one stage ahead
+  u32x4 sb[DEPTH][8], sa[MT][2];
+  auto load_b = [&](int it, u32x4 (&dst)[8]) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int row = UNION ? rows[i] : k0 + it * kSkK + 8 * rg + i;
+      dst[i] = ld16_nt(bcol + (size_t)row * H);
+    }
+  };
+  auto load_a = [&](int it) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        sa[mt][ks] = ld16(ap[mt] + it * kSkK + 32 * ks);
+  };
+  // column 8 cg + c gets rows 8 rg .. 8 rg + 7 as one k-contiguous fragment
+  // (UNION: zeros for rows outside the union, valid = that stage's rvalid)
+  auto store_b = [&](int buf, const u32x4 (&src)[8], uint32_t valid) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const int j = c >> 1;
+      u32x4 o;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        uint32_t lo = src[2 * w][j], hi = src[2 * w + 1][j];
+        if (UNION) {
+          lo = (valid >> (2 * w)) & 1u ? lo : 0u;
+          hi = (valid >> (2 * w + 1)) & 1u ? hi : 0u;
+        }
+        o[w] = (c & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+      }
+      *reinterpret_cast<u32x4 *>(&bs[buf][sk_off(8 * cg + c, rg)]) = o;
+    }
+  };
+
+  f32x4 acc[MT][4];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) acc[mt][ct] = f32x4{0, 0, 0, 0};
+
+  u32x4 a_cur[MT][2];
+  uint32_t vb[DEPTH];  // UNION: rvalid of the stage in each register set
+  if (nit > 0) {
+    if (UNION) {
+      fetch_rows(0);
+      take_rows(0);
+      fetch_rows(min(1, nit - 1));
+    }
+    vb[0] = rvalid;
+    load_b(0, sb[0]);
+    load_a(0);
+    if (DEPTH == 2 && nit > 1) {
+      if (UNION) {
+        take_rows(1);
+        fetch_rows(min(2, nit - 1));
+      }
+      vb[DEPTH - 1] = rvalid;
+      load_b(1, sb[DEPTH - 1]);
+    }
+    store_b(0, sb[0], vb[0]);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) { a_cur[mt][0] = sa[mt][0]; a_cur[mt][1] = sa[mt][1]; }
+  }
+  __syncthreads();
+  // One step: multiply stage it (LDS buffer it & 1, coefficients a_cur),
+  // with stage it + 1's coefficients and stage it + DEPTH's W_d rows (into
+  // register set SL = it % DEPTH, whose stage is already in LDS) issued
+  // first, then stage it + 1 written from its register set to the other
+  // buffer.  STEADY: every load and store is in range (no branch around a
+  // load, so the compiler's waits count the loads in flight exactly).
+  auto step = [&](int it, auto slc, auto steadyc) {
+    constexpr int SL = decltype(slc)::value;
+    constexpr bool STEADY = decltype(steadyc)::value;
+    const int cur = it & 1;
+    const int ahead = it + DEPTH;
+    if (STEADY || it + 1 < nit) load_a(it + 1);
+    if (STEADY || ahead < nit) {
+      if (UNION) {
+        take_rows(ahead);
+        fetch_rows(min(ahead + 1, nit - 1));
+      }
+      vb[SL] = rvalid;
+      load_b(ahead, sb[SL]);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      u32x4 b[4];
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+        b[ct] = *reinterpret_cast<const u32x4 *>(&bs[cur][sk_off(64 * wid + 16 * ct + r, 4 * ks + g)]);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        if (16 * mt < ntok)  // block-uniform
+#pragma unroll
+          for (int ct = 0; ct < 4; ++ct) acc[mt][ct] = mfma_bf16(a_cur[mt][ks], b[ct], acc[mt][ct]);
+    }
+    if (STEADY || it + 1 < nit) {
+      store_b(cur ^ 1, sb[(SL + 1) % DEPTH], vb[(SL + 1) % DEPTH]);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) { a_cur[mt][0] = sa[mt][0]; a_cur[mt][1] = sa[mt][1]; }
+    }
+    __syncthreads();
+  };
+  int it = 0;
+  for (; it + DEPTH + 1 < nit; it += DEPTH) {
+    step(it, SkIc<0>{}, SkIc<1>{});
+    if (DEPTH == 2) step(it + 1, SkIc<1 % DEPTH>{}, SkIc<1>{});
+  }
+  for (; it < nit; it += DEPTH) {
+    step(it, SkIc<0>{}, SkIc<0>{});
+    if (DEPTH == 2 && it + 1 < nit) step(it + 1, SkIc<1 % DEPTH>{}, SkIc<0>{});
+  }
+  // D: lane holds column r of each column tile, token rows 4 g + rr of each
+  // token tile; the rows' pair ids are all read before the first store
+  int prow[MT][4];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int c = 16 * mt + 4 * g + rr;
+      prow[mt][rr] = rv.pair_at(q0 + (c < ntok ? c : 0));
+    }
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int c = 16 * mt + 4 * g + rr;
+      if (c < ntok) {
+        const size_t row = (size_t)prow[mt][rr] * S + sidx;
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+          const int col = col0 + 64 * wid + 16 * ct + r;
+          if (col < H) partial[row * H + col] = acc[mt][ct][rr];
+        }
+      }
+    }
+  }
+}
+
+// Token tiles per skinny item for this call (0: the 128-token GEMM instead).
+// An expert with more tokens than one item holds is split over items that
+// each stream its rows again, so the tiles cover well past the average
+// count n (the busiest expert of a routed batch holds about n + 3 sqrt(n):
+// 28 at n = 16); tiles past an item's tokens cost no MFMA.
+#ifndef MOE_SKINNY_MT2_MAX
+#define MOE_SKINNY_MT2_MAX 16  // routed: average tokens per expert for 2 tiles
+#endif
+#ifndef MOE_SKINNY_MT4_MAX
+#define MOE_SKINNY_MT4_MAX 40  // routed: ... for 4 tiles
+#endif
+static int skinny_tiles(int T, int E, int top_k, int implicit) {
+  const long P = (long)T * top_k;
+  const long per_expert = implicit ? T : P / (E < P ? E : P);
+  if (implicit) return per_expert <= 32 ? 2 : (per_expert <= 64 ? 4 : 0);
+  return per_expert <= MOE_SKINNY_MT2_MAX ? 2 : (per_expert <= MOE_SKINNY_MT4_MAX ? 4 : 0);
+}
+
+// K chunks of the skinny GEMM: up to 4, while the grid has fewer than 1024
+// blocks and each chunk keeps >= 512 rows.
+static int skinny_splits(int T, int E, int top_k, int implicit, int H, int d_ff, int mt) {
+  const long P = (long)T * top_k;
+  const long items = implicit ? (long)E * ((T + 16 * mt - 1) / (16 * mt))
+                              : (E < P ? E : P) + P / (16 * mt);
+  const long base = items * ((H + kSkCols - 1) / kSkCols);
+  long S = (1024 + base - 1) / base;
+  const long smax = d_ff / 512 > 0 ? d_ff / 512 : 1;
+  if (S > smax) S = smax;
+  if (S > 4) S = 4;
+  return S < 1 ? 1 : (int)S;
 }
 
 // K chunks of the dense down GEMM: enough blocks to fill the chip when few
@@ -339,15 +702,172 @@ static int dense_down_kchunk(int T, int E, int top_k, int H, int d_ff) {
 size_t dense_down_partial_rows(int T, int E, int top_k, int H) {
   const size_t P = (size_t)T * top_k;
   const size_t per_item = P > (size_t)E ? (P + E - 1) / E : 1;
-  return P + (size_t)((65536 + H - 1) / H) * per_item;
+  const size_t wide = P + (size_t)((65536 + H - 1) / H) * per_item;
+  return wide > 4 * P ? wide : 4 * P;  // the skinny GEMM writes at most 4 chunks
+}
+
+// ---------------------------------------------------------------- union of kept rows
+// The sparse path's packed-rows form, for experts that hold several tokens
+// (the page's fused projection gathers the active neurons' down weights
+// once into a dense matrix and runs a dense product over them).  Two short
+// launches build, from the mask kernel's kept lists:
+//   union_bits   slot s (expert e), group g of 8 of its pairs: the OR of
+//                their kept ids as a d_ff-bit map, pbits[e, g] (only where
+//                experts hold over 8 tokens on average)
+//   union_coef   pair p (expert e): the OR of e's group maps (or of all its
+//                pairs' kept ids) and its prefix
+//                counts per 32-bit word; e's first pair writes the
+//                ascending union urow[e, 0 .. ucnt[e]); every pair writes
+//                its coefficients (w * h at its kept ids, fp32) at their
+//                union positions (prefix + popcount within the word),
+//                rounded to bf16, as hmu[p, 0 .. upad) with zeros elsewhere
+//                (upad = the union count rounded up to 64)
+// for the gathering down GEMM.
+constexpr int kUnionMaxDff = 8192;
+constexpr int kUnionGroup = 8;  // pairs per union_bits block
+
+__global__ __launch_bounds__(256) void union_bits_kernel(const int32_t *__restrict__ idx, int k,
+                                                         RouteView rv, int d_ff, int G,
+                                                         uint32_t *__restrict__ pbits) {
+  __shared__ uint32_t bits[kUnionMaxDff / 32];
+  const int tid = threadIdx.x;
+  const int s = blockIdx.x, g = blockIdx.y;
+  if (s >= rv.nact()) return;  // block-uniform
+  const int e = rv.expert(s);
+  const int q0 = rv.begin(e), np = rv.end(e) - q0;
+  if (g * kUnionGroup >= np) return;
+  const int ng = min(kUnionGroup, np - g * kUnionGroup);
+  const int nw = d_ff / 32;
+  for (int w = tid; w < nw; w += 256) bits[w] = 0u;
+  __syncthreads();
+  // pair pi's ids are read by the threads of sub-group pi % 8 (32 threads
+  // each), 4 loads in flight per thread before their LDS updates
+  const int sg = tid >> 5, st = tid & 31;
+  if (sg < ng) {
+    const int32_t *ip = idx + (size_t)rv.pair_at(q0 + g * kUnionGroup + sg) * k;
+    for (int i0 = st; i0 < k; i0 += 128) {
+      int v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = i0 + 32 * u < k ? ip[i0 + 32 * u] : -1;
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if ((unsigned)v[u] < (unsigned)d_ff) atomicOr(&bits[v[u] >> 5], 1u << (v[u] & 31));
+    }
+  }
+  __syncthreads();
+  uint32_t *o = pbits + ((size_t)e * G + g) * nw;
+  for (int w = tid; w < nw; w += 256) o[w] = bits[w];
+}
+
+__global__ __launch_bounds__(256) void union_coef_kernel(const int32_t *__restrict__ idx,
+                                                         const float *__restrict__ hact, int k,
+                                                         RouteView rv, int d_ff, int G,
+                                                         const uint32_t *__restrict__ pbits,
+                                                         int32_t *__restrict__ urow,
+                                                         int32_t *__restrict__ ucnt,
+                                                         uint16_t *__restrict__ hmu) {
+  __shared__ uint32_t bits[kUnionMaxDff / 32];
+  __shared__ int pre[kUnionMaxDff / 32];
+  __shared__ int wtot[4];
+  __shared__ __attribute__((aligned(16))) uint16_t crow[kUnionMaxDff];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int p = blockIdx.x;
+  const int e = rv.expert_of_pair(p);
+  const int q0 = rv.begin(e), np = rv.end(e) - q0;
+  const bool first = rv.pair_at(q0) == p;
+  // the expert's map (thread w owns word w, nw <= 256): the OR of its
+  // groups' maps (8 loads in flight), or, without union_bits (G == 0), of
+  // its pairs' kept ids straight from the lists
+  const int nw = d_ff / 32;
+  uint32_t wb = 0u;
+  if (G > 0) {
+    const int ngr = (np + kUnionGroup - 1) / kUnionGroup;
+    if (tid < nw) {
+      const uint32_t *pb = pbits + (size_t)e * G * nw + tid;
+      for (int g0 = 0; g0 < ngr; g0 += 8) {
+        uint32_t v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = g0 + u < ngr ? pb[(size_t)(g0 + u) * nw] : 0u;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) wb |= v[u];
+      }
+    }
+  } else {
+    for (int w = tid; w < nw; w += 256) bits[w] = 0u;
+    __syncthreads();
+    // pair pi's ids are read by the threads of sub-group pi % 8 (32 each)
+    const int sg = tid >> 5, st = tid & 31;
+    for (int pi = sg; pi < np; pi += 8) {
+      const int32_t *ip = idx + (size_t)rv.pair_at(q0 + pi) * k;
+      for (int i0 = st; i0 < k; i0 += 128) {
+        int v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = i0 + 32 * u < k ? ip[i0 + 32 * u] : -1;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if ((unsigned)v[u] < (unsigned)d_ff) atomicOr(&bits[v[u] >> 5], 1u << (v[u] & 31));
+      }
+    }
+    __syncthreads();
+    if (tid < nw) wb = bits[tid];
+    __syncthreads();  // bits is rewritten below
+  }
+  const int c = __popc(wb);
+  const int incl = wave_incl_scan(c);
+  if (lane == 63) wtot[wid] = incl;
+  __syncthreads();
+  int base = incl - c;
+  for (int ww = 0; ww < wid; ++ww) base += wtot[ww];
+  const int uc = wtot[0] + wtot[1] + wtot[2] + wtot[3];
+  if (tid < nw) {
+    bits[tid] = wb;
+    pre[tid] = base;
+  }
+  if (first) {  // the expert's first pair writes its union list
+    int32_t *ur = urow + (size_t)e * d_ff;
+    uint32_t m = wb;
+    int o = base;
+    while (m) {
+      const int b = __ffs(m) - 1;
+      m &= m - 1;
+      ur[o++] = tid * 32 + b;
+    }
+    if (tid == 0) ucnt[e] = uc;
+  }
+  const int upad = (uc + kDnK - 1) / kDnK * kDnK;
+  for (int q = tid; q < upad; q += 256) crow[q] = 0;
+  __syncthreads();
+  for (int i = tid; i < k; i += 256) {
+    const int j = idx[(size_t)p * k + i];
+    if ((unsigned)j < (unsigned)d_ff) {
+      const int pos = pre[j >> 5] + __popc(bits[j >> 5] & ((1u << (j & 31)) - 1u));
+      if (pos < upad) crow[pos] = (uint16_t)f32_to_bf16_bits(hact[(size_t)p * k + i]);
+    }
+  }
+  __syncthreads();
+  uint16_t *o = hmu + (size_t)p * d_ff;
+  for (int q = 8 * tid; q < upad; q += 8 * 256)
+    *reinterpret_cast<u32x4 *>(o + q) = *reinterpret_cast<const u32x4 *>(&crow[q]);
+}
+
+// Words of the union build's scratch (the groups' maps) for at most T
+// tokens on E experts (at most E active slots).
+size_t union_scratch_words(int T, int E, int d_ff) {
+  const size_t G = (T + kUnionGroup - 1) / kUnionGroup;
+  return (size_t)E * G * (d_ff / 32);
 }
 
 // ---------------------------------------------------------------- combine
 // y[t, :] = (accumulate ? y[t, :] : 0) + sum over slots, then chunks, of
 // the token's partial rows: a fixed order, so reruns are bitwise equal.
+// With xnext: also x_next = x_res + y, rounded to the layer dtype (bf16
+// when BF16), as the sparse path's residual epilogue.
+template <bool BF16 = true>
 __global__ __launch_bounds__(64) void combine_kernel(const float *__restrict__ partial, int H,
                                                       int top_k, int n_chunks, int accumulate,
-                                                      float *__restrict__ y) {
+                                                      float *__restrict__ y,
+                                                      const void *__restrict__ xres = nullptr,
+                                                      void *__restrict__ xnext = nullptr) {
   const int t = blockIdx.x;
   const int col = (blockIdx.y * 64 + threadIdx.x) * 4;
   if (col >= H) return;
@@ -365,6 +885,19 @@ __global__ __launch_bounds__(64) void combine_kernel(const float *__restrict__ p
   }
   for (; i < rows; ++i) s += *reinterpret_cast<const f32x4 *>(pp + (size_t)i * H);
   *reinterpret_cast<f32x4 *>(y + (size_t)t * H + col) = s;
+  if (xnext) {
+    const size_t o = (size_t)t * H + col;
+    if (BF16) {
+      const uint2 xb = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(xres) + o);
+      uint2 ob;
+      ob.x = f32_to_bf16_bits(bf16lo(xb.x) + s[0]) | (f32_to_bf16_bits(bf16hi(xb.x) + s[1]) << 16);
+      ob.y = f32_to_bf16_bits(bf16lo(xb.y) + s[2]) | (f32_to_bf16_bits(bf16hi(xb.y) + s[3]) << 16);
+      *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(xnext) + o) = ob;
+    } else {
+      const f32x4 xv = *reinterpret_cast<const f32x4 *>(static_cast<const float *>(xres) + o);
+      *reinterpret_cast<f32x4 *>(static_cast<float *>(xnext) + o) = xv + s;
+    }
+  }
 }
 
 // ---------------------------------------------------------------- host side
@@ -389,20 +922,102 @@ void launch_gateup_gemm(const FfnArgs &a, const RouteView &rv, bool gate_only, h
 #undef MOE_GG
 }
 
-hipError_t launch_down_dense(const FfnArgs &a, const RouteView &rv, hipStream_t stream) {
-  const int kc = dense_down_kchunk(a.T, a.E, a.top_k, a.H, a.d_ff);
-  const int S = (a.d_ff + kc - 1) / kc;
-  if ((size_t)a.T * a.top_k * S > dense_down_partial_rows(a.T, a.E, a.top_k, a.H))
-    return hipErrorInvalidValue;  // cannot happen: the bound covers every split count
-  dim3 grid(n_items(a, kDnTok), a.H / kDnCols, S);
-  timer_begin(kStageDownDense, stream);
-  down_dense_gemm_kernel<<<grid, 256, 0, stream>>>(static_cast<const uint16_t *>(a.w_down),
-                                                   static_cast<const uint16_t *>(a.hm), rv, a.H,
-                                                   a.d_ff, kc, a.partial);
+bool union_layout_ok(int T, int H, int d_ff, int bf16) {
+  return bf16 && H % kDnCols == 0 && d_ff % kDnK == 0 && d_ff <= kUnionMaxDff &&
+         T >= kUnionMinTokens;
+}
+
+bool union_down_ok(const FfnArgs &a) {
+  if (!a.hmu || !a.urow || !a.ucnt || !a.ubuf || a.k_keep <= 0) return false;
+  if (!union_layout_ok(a.T, a.H, a.d_ff, a.bf16)) return false;
+  const long P = (long)a.T * a.top_k;
+  const long per_expert = a.implicit ? a.T : P / (a.E < P ? a.E : P);
+  return per_expert >= kUnionMinTokens;
+}
+
+// The sparse path's packed-rows form (bf16): the union kernel, then the down
+// GEMM over each expert's union of kept rows, then the combine.  a.idx and
+// a.hact hold the mask kernel's kept lists; a.hmu, a.urow and a.ucnt receive
+// the union.
+hipError_t launch_down_union(const FfnArgs &a, const RouteView &rv, hipStream_t stream) {
+  const int P = a.T * a.top_k;
+  const int slots = a.implicit ? a.E : (a.E < P ? a.E : P);
+  const int G = (a.T + kUnionGroup - 1) / kUnionGroup;
+  uint32_t *pbits = a.ubuf;
+  timer_begin(kStageUnionRows, stream);
+  // experts of a few tokens: each pair's block ORs its expert's lists itself
+  // (one launch; measured 11.3 -> 7.9 us at 8 tokens per expert, but 35 ->
+  // 40 us at 16); past 8 tokens per expert on average, per-group maps first
+  const long per_expert = a.implicit ? a.T : P / slots;
+  const int Gl = per_expert > 8 ? G : 0;
+  if (Gl > 0)
+    union_bits_kernel<<<dim3(slots, G), 256, 0, stream>>>(a.idx, a.k_keep, rv, a.d_ff, G, pbits);
+  union_coef_kernel<<<P, 256, 0, stream>>>(a.idx, a.hact, a.k_keep, rv, a.d_ff, Gl, pbits, a.urow,
+                                           a.ucnt, a.hmu);
+  timer_end(stream);
+  const int mt = skinny_tiles(a.T, a.E, a.top_k, a.implicit);
+  int S;
+  timer_begin(kStageDownUnion, stream);
+  if (mt > 0) {
+    S = skinny_splits(a.T, a.E, a.top_k, a.implicit, a.H, a.d_ff, mt);
+    if ((size_t)P * S > dense_down_partial_rows(a.T, a.E, a.top_k, a.H)) return hipErrorInvalidValue;
+    dim3 grid(n_items(a, 16 * mt), (a.H + kSkCols - 1) / kSkCols, S);
+    const uint16_t *wd = static_cast<const uint16_t *>(a.w_down);
+    if (mt == 2)
+      down_skinny_kernel<2, true, sk_depth<2, true>()><<<grid, 256, 0, stream>>>(wd, a.hmu, rv, a.H, a.d_ff, 0, a.partial,
+                                                            a.urow, a.ucnt);
+    else
+      down_skinny_kernel<4, true, sk_depth<4, true>()><<<grid, 256, 0, stream>>>(wd, a.hmu, rv, a.H, a.d_ff, 0, a.partial,
+                                                            a.urow, a.ucnt);
+  } else {
+    const int kc = dense_down_kchunk(a.T, a.E, a.top_k, a.H, a.d_ff);
+    S = (a.d_ff + kc - 1) / kc;
+    if ((size_t)P * S > dense_down_partial_rows(a.T, a.E, a.top_k, a.H)) return hipErrorInvalidValue;
+    dim3 grid(n_items(a, kDnTok), a.H / kDnCols, S);
+    down_dense_gemm_kernel<true><<<grid, 256, 0, stream>>>(static_cast<const uint16_t *>(a.w_down),
+                                                           a.hmu, rv, a.H, a.d_ff, kc, a.partial,
+                                                           a.urow, a.ucnt);
+  }
   timer_end(stream);
   dim3 cgrid(a.T, (a.H + 255) / 256);
   timer_begin(kStageCombine, stream);
-  combine_kernel<<<cgrid, 64, 0, stream>>>(a.partial, a.H, a.top_k, S, a.accumulate, a.y);
+  combine_kernel<true><<<cgrid, 64, 0, stream>>>(a.partial, a.H, a.top_k, S, a.accumulate, a.y,
+                                                 a.xres, a.xnext);
+  timer_end(stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_down_dense(const FfnArgs &a, const RouteView &rv, hipStream_t stream) {
+  const int mt = skinny_tiles(a.T, a.E, a.top_k, a.implicit);
+  const size_t P = (size_t)a.T * a.top_k;
+  const uint16_t *wd = static_cast<const uint16_t *>(a.w_down);
+  const uint16_t *hm = static_cast<const uint16_t *>(a.hm);
+  int S;
+  timer_begin(kStageDownDense, stream);
+  if (mt > 0) {  // few tokens per expert: the skinny GEMM over all d_ff rows
+    S = skinny_splits(a.T, a.E, a.top_k, a.implicit, a.H, a.d_ff, mt);
+    const int per = (a.d_ff + S - 1) / S;
+    const int kc = (per + kSkK - 1) / kSkK * kSkK;
+    if (P * S > dense_down_partial_rows(a.T, a.E, a.top_k, a.H)) return hipErrorInvalidValue;
+    dim3 grid(n_items(a, 16 * mt), (a.H + kSkCols - 1) / kSkCols, S);
+    if (mt == 2)
+      down_skinny_kernel<2, false, sk_depth<2, false>()><<<grid, 256, 0, stream>>>(wd, hm, rv, a.H, a.d_ff, kc, a.partial,
+                                                             nullptr, nullptr);
+    else
+      down_skinny_kernel<4, false, sk_depth<4, false>()><<<grid, 256, 0, stream>>>(wd, hm, rv, a.H, a.d_ff, kc, a.partial,
+                                                             nullptr, nullptr);
+  } else {
+    const int kc = dense_down_kchunk(a.T, a.E, a.top_k, a.H, a.d_ff);
+    S = (a.d_ff + kc - 1) / kc;
+    if (P * S > dense_down_partial_rows(a.T, a.E, a.top_k, a.H))
+      return hipErrorInvalidValue;  // cannot happen: the bound covers every split count
+    dim3 grid(n_items(a, kDnTok), a.H / kDnCols, S);
+    down_dense_gemm_kernel<false><<<grid, 256, 0, stream>>>(wd, hm, rv, a.H, a.d_ff, kc, a.partial);
+  }
+  timer_end(stream);
+  dim3 cgrid(a.T, (a.H + 255) / 256);
+  timer_begin(kStageCombine, stream);
+  combine_kernel<true><<<cgrid, 64, 0, stream>>>(a.partial, a.H, a.top_k, S, a.accumulate, a.y);
   timer_end(stream);
   return hipGetLastError();
 }

@@ -1877,6 +1877,10 @@ hipError_t launch_ffn_sparse(const FfnArgs &a, hipStream_t stream) {
   const RouteView rv = make_view(a);
   if (fused_ffn_ok(a)) return launch_ffn_fused(a, rv, stream);
   launch_gateup(a, rv, stream);
+  if (union_down_ok(a)) {
+    launch_mask(a, rv, a.idx, a.hact, nullptr, 0, stream);
+    return launch_down_union(a, rv, stream);
+  }
   if (fused_topk_ok(a)) {
     launch_down_topk(a, rv, stream);
     return hipGetLastError();

@@ -88,5 +88,8 @@ inline int n_items(const FfnArgs &a, int TG) {
 // a.hm into per-pair partials, then their combine into y.
 void launch_gateup_gemm(const FfnArgs &a, const RouteView &rv, bool gate_only, hipStream_t stream);
 hipError_t launch_down_dense(const FfnArgs &a, const RouteView &rv, hipStream_t stream);
+// launch_down_union: the sparse path's packed-rows down projection (union
+// kernel, gathering down GEMM, combine) from the mask kernel's kept lists
+hipError_t launch_down_union(const FfnArgs &a, const RouteView &rv, hipStream_t stream);
 
 }  // namespace moe

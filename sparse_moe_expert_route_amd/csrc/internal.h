@@ -33,7 +33,8 @@ inline void timer_end(hipStream_t s) {
 
 // Stage ids (mirror moe_stage in the public header).
 enum { kStageLogits = 0, kStageTopk, kStageGroup, kStageGateup, kStageMask, kStageDownRows,
-       kStageDownDense, kStageCombine, kStageZero, kStageUpRows, kStageFused };
+       kStageDownDense, kStageCombine, kStageZero, kStageUpRows, kStageFused, kStageUnionRows,
+       kStageDownUnion };
 
 // Roster routing state (usage == nullptr: plain routing).
 struct RosterArgs {
@@ -92,7 +93,27 @@ struct FfnArgs {
   float *fpart;
   int32_t *sync;
   int sync_zeroed;
+  // the packed-rows down projection (sparse path, bf16, experts holding
+  // several tokens): per-expert ascending union of kept rows [E, d_ff] and
+  // its count [E], and the coefficients at union positions [P, d_ff] bf16;
+  // null when the workspace carries no such segments
+  int32_t *urow = nullptr, *ucnt = nullptr;
+  uint16_t *hmu = nullptr;
+  uint32_t *ubuf = nullptr;  // the union build's scratch (union_scratch_words)
 };
+
+// The packed-rows down projection takes experts that hold at least this
+// many tokens on average (shape only: P / min(E, P) routed, T shared).
+#ifndef MOE_UNION_MIN_TOKENS
+#define MOE_UNION_MIN_TOKENS 4
+#endif
+constexpr int kUnionMinTokens = MOE_UNION_MIN_TOKENS;
+// Whether a sparse workspace for T tokens carries the packed-rows segments.
+bool union_layout_ok(int T, int H, int d_ff, int bf16);
+// Whether this sparse call takes the packed-rows down projection.
+bool union_down_ok(const FfnArgs &a);
+// 32-bit words of that projection's scratch for at most T tokens.
+size_t union_scratch_words(int T, int E, int d_ff);
 
 // Counter words of the fused FFN: per expert (each on its own 256-byte
 // line: waiting blocks poll them, and pollers of one line all land on one
