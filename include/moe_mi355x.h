@@ -184,13 +184,14 @@ moe_status moe_route_roster(const moe_desc *d, int32_t T, const void *x, const v
  * y [T, H] fp32 is overwritten (accumulate == 0) or added to (== 1); the sum
  * over a token's experts runs in slot order with no atomics, so results are
  * bitwise reproducible.
- * Where the experts of a bf16 call hold 4 or more tokens on average (T * top_k
- * / min(E, T * top_k) routed, T for a shared group), the down projection
- * takes the page's packed-rows form: each active expert's union of kept rows
- * is read once and multiplied with all of its tokens (MFMA), the weighted
- * activations rounded to bf16 for that product (fp32 accumulation); rows
- * outside the union are still never read.  Smaller batches multiply each
- * token's kept rows with its fp32 activations.
+ * Where the experts of a bf16 call hold many tokens on average (n = T * top_k
+ * / min(E, T * top_k) routed, T for a shared group: n >= 8, 32 or 128 as the
+ * expected active experts' W_d is >= 512 MB, >= 128 MB or smaller), the down
+ * projection takes the page's packed-rows form: each active expert's union
+ * of kept rows is read once and multiplied with all of its tokens (MFMA),
+ * the weighted activations rounded to bf16 for that product (fp32
+ * accumulation); rows outside the union are still never read.  Otherwise
+ * each token's kept rows are multiplied with its fp32 activations.
  *
  * k_keep in [0, d_ff]; k_keep == d_ff keeps every neuron, 0 adds nothing.
  * x [T, H] and w_down [E, d_ff, H] in desc->dtype; w_gate and w_up the

@@ -108,10 +108,13 @@ FfnLayout ffn_layout(const moe_desc *d, int32_t T, int32_t k, moe_path path) {
   off += up(P * (size_t)k * 4);
   L.hact = off;
   if (path == MOE_PATH_SPARSE) off += up(P * (size_t)k * 4);
-  // the packed-rows down projection of the sparse path (larger batches):
-  // union lists, union counts, compacted coefficients, and the partials
-  // the dense-path down GEMM also uses
-  L.has_union = path == MOE_PATH_SPARSE && moe::union_layout_ok(T, d->hidden, d->d_ff, bf16);
+  // the packed-rows down projection of the sparse path (larger batches;
+  // its shape rule grows monotonically with T, so a workspace for T serves
+  // every smaller call): union lists, union counts, compacted
+  // coefficients, the build's scratch, and the partials the dense-path
+  // down GEMM also uses
+  L.has_union = path == MOE_PATH_SPARSE && moe::union_layout_ok(T, d->hidden, d->d_ff, bf16) &&
+                moe::union_form(T, d->n_experts, d->top_k, d->hidden, d->d_ff);
   L.urow = off;
   if (L.has_union) off += up((size_t)d->n_experts * d->d_ff * 4);
   L.ucnt = off;
@@ -645,15 +648,21 @@ moe_path moe_select_path(const moe_desc *d, int32_t T, int32_t k_keep) {
   // per expert come from HBM, the repeats mostly from the caches.  Measured
   // sparse-vs-dense sweeps (OLMoE-, Qwen3-MoE-, DeepSeek-V2- and Llama-4-like
   // layers, T = 1 .. 1024) fit a repeat cost of 0.3 row and a dense-GEMM
-  // cost of 1.2 rows per row.  Without masking (k_keep == d_ff) the dense
-  // path always wins.
+  // cost of 1.2 rows per row (costs in rows of H weights).  Without masking
+  // (k_keep == d_ff) the dense path always wins.
   if (k_keep >= d->d_ff) return MOE_PATH_DENSE;
   const double E = d->n_experts, K = d->top_k, D = d->d_ff;
   const double active = E * (1.0 - pow(1.0 - K / E, (double)T));
   const double n_e = (double)T * K / active;
   const double total = (double)T * K * k_keep;
   const double unique = active * D * (1.0 - pow(1.0 - (double)k_keep / D, n_e));
-  const double sparse_cost = unique + 0.3 * (total - unique);
+  double sparse_cost = unique + 0.3 * (total - unique);
+  // Where it takes the packed-rows form (bf16, many tokens per expert) the
+  // sparse path reads each expert's union of kept rows once, through a
+  // gathering GEMM (measured ~1.1x the dense GEMM's cost per row), after a
+  // union build of ~12 us (~72 MB of streaming).
+  if (d->dtype == MOE_BF16 && moe::union_form(T, d->n_experts, d->top_k, d->hidden, d->d_ff))
+    sparse_cost = 1.32 * unique + 72e6 / (2.0 * d->hidden);
   const double dense_cost = 1.2 * active * D;
   return sparse_cost < dense_cost ? MOE_PATH_SPARSE : MOE_PATH_DENSE;
 }

@@ -666,17 +666,21 @@ static int skinny_tiles(int T, int E, int top_k, int implicit) {
   return per_expert <= MOE_SKINNY_MT2_MAX ? 2 : (per_expert <= MOE_SKINNY_MT4_MAX ? 4 : 0);
 }
 
-// K chunks of the skinny GEMM: up to 4, while the grid has fewer than 1024
-// blocks and each chunk keeps >= 512 rows.
+// K chunks of the skinny GEMM: enough for ~2048 blocks (a lone shared
+// expert at a few tokens has only H / 256 column blocks), each chunk >= 256
+// rows, at most 16, and at most max(4, 1024 / P) so that the partial rows
+// stay within dense_down_partial_rows.
 static int skinny_splits(int T, int E, int top_k, int implicit, int H, int d_ff, int mt) {
   const long P = (long)T * top_k;
   const long items = implicit ? (long)E * ((T + 16 * mt - 1) / (16 * mt))
                               : (E < P ? E : P) + P / (16 * mt);
   const long base = items * ((H + kSkCols - 1) / kSkCols);
-  long S = (1024 + base - 1) / base;
-  const long smax = d_ff / 512 > 0 ? d_ff / 512 : 1;
+  long S = (2048 + base - 1) / base;
+  const long smax = d_ff / 256 > 0 ? d_ff / 256 : 1;
   if (S > smax) S = smax;
-  if (S > 4) S = 4;
+  if (S > 16) S = 16;
+  const long pmax = P > 0 && 1024 / P > 4 ? 1024 / P : 4;
+  if (S > pmax) S = pmax;
   return S < 1 ? 1 : (int)S;
 }
 
@@ -703,7 +707,9 @@ size_t dense_down_partial_rows(int T, int E, int top_k, int H) {
   const size_t P = (size_t)T * top_k;
   const size_t per_item = P > (size_t)E ? (P + E - 1) / E : 1;
   const size_t wide = P + (size_t)((65536 + H - 1) / H) * per_item;
-  return wide > 4 * P ? wide : 4 * P;  // the skinny GEMM writes at most 4 chunks
+  // the skinny GEMM writes at most max(4, 1024 / P) chunks per pair
+  const size_t skinny = 4 * P > 1024 ? 4 * P : (P > 0 ? 1024 : 0);
+  return wide > skinny ? wide : skinny;
 }
 
 // ---------------------------------------------------------------- union of kept rows
@@ -922,17 +928,24 @@ void launch_gateup_gemm(const FfnArgs &a, const RouteView &rv, bool gate_only, h
 #undef MOE_GG
 }
 
+bool union_form(int T, int E, int top_k, int H, int d_ff) {
+  if (T <= 0 || E <= 0 || top_k <= 0) return false;
+  const long P = (long)T * top_k;
+  const long per_expert = P / (E < P ? E : P);  // T for a shared group (top_k == E)
+  const double active = E * (1.0 - pow(1.0 - (double)top_k / E, (double)T));
+  const double bytes = active * d_ff * H * 2.0;  // the active experts' W_d
+  return per_expert >= union_min_tokens(bytes);
+}
+
 bool union_layout_ok(int T, int H, int d_ff, int bf16) {
   return bf16 && H % kDnCols == 0 && d_ff % kDnK == 0 && d_ff <= kUnionMaxDff &&
-         T >= kUnionMinTokens;
+         T >= kUnionMinTokensLarge;
 }
 
 bool union_down_ok(const FfnArgs &a) {
   if (!a.hmu || !a.urow || !a.ucnt || !a.ubuf || a.k_keep <= 0) return false;
   if (!union_layout_ok(a.T, a.H, a.d_ff, a.bf16)) return false;
-  const long P = (long)a.T * a.top_k;
-  const long per_expert = a.implicit ? a.T : P / (a.E < P ? a.E : P);
-  return per_expert >= kUnionMinTokens;
+  return union_form(a.T, a.E, a.top_k, a.H, a.d_ff);
 }
 
 // The sparse path's packed-rows form (bf16): the union kernel, then the down

@@ -102,12 +102,25 @@ struct FfnArgs {
   uint32_t *ubuf = nullptr;  // the union build's scratch (union_scratch_words)
 };
 
-// The packed-rows down projection takes experts that hold at least this
-// many tokens on average (shape only: P / min(E, P) routed, T shared).
-#ifndef MOE_UNION_MIN_TOKENS
-#define MOE_UNION_MIN_TOKENS 4
+// The packed-rows down projection takes experts that hold at least
+// union_min_tokens(W) tokens on average (shape only: P / min(E, P) routed,
+// T shared), W = the expected active experts' W_d bytes.  Below that, each
+// token's kept rows are streamed on their own and the rows the expert's
+// other tokens also keep come back from the caches (L2, and the 256 MB
+// last-level cache while W fits it), which beat the union's build; measured
+// on four layer families (union vs per-token rows, per layer call: e.g.
+// Llama-4-like, W = 1.3 GB: 791 vs 799 us at 8 tokens per expert, 902 vs
+// 1003 at 16; OLMoE-like, W = 268 MB: 192 vs 184 at 16, 227 vs 236 at 32;
+// a lone shared expert of 84 MB loses at 32 tokens).
+#ifndef MOE_UNION_MIN_TOKENS_LARGE
+#define MOE_UNION_MIN_TOKENS_LARGE 8  // W >= 512 MB
 #endif
-constexpr int kUnionMinTokens = MOE_UNION_MIN_TOKENS;
+constexpr int kUnionMinTokensLarge = MOE_UNION_MIN_TOKENS_LARGE;
+inline int union_min_tokens(double w_bytes) {
+  return w_bytes >= 512e6 ? kUnionMinTokensLarge : (w_bytes >= 128e6 ? 32 : 128);
+}
+// Whether a sparse bf16 call of these shapes takes the packed-rows form.
+bool union_form(int T, int E, int top_k, int H, int d_ff);
 // Whether a sparse workspace for T tokens carries the packed-rows segments.
 bool union_layout_ok(int T, int H, int d_ff, int bf16);
 // Whether this sparse call takes the packed-rows down projection.

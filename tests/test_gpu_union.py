@@ -1,10 +1,12 @@
 """GPU tests of the sparse path's packed-rows down projection.
 
-When the experts of a bf16 sparse call hold several tokens each (on average
-at least 4: P / min(E, P) routed, T for a shared group), the down projection
-gathers each active expert's union of kept W_d rows once and multiplies it
-with all of that expert's tokens (the page's fused projection over the
-active neurons), instead of streaming every token's kept rows on its own.
+When the experts of a bf16 sparse call hold many tokens each (on average,
+P / min(E, P) routed or T for a shared group, at least 8, 32 or 128 as the
+active experts' W_d is >= 512 MB, >= 128 MB or smaller), the down
+projection gathers each active expert's union of kept W_d rows once and
+multiplies it with all of that expert's tokens (the page's fused
+projection over the active neurons), instead of streaming every token's
+kept rows on its own.
 These tests check which calls take that form, its parity with the oracle at
 the edges of the union (k = 1, union sizes on and off the 64-row stage,
 k = d_ff), that rows outside an expert's union are never read, and its
@@ -74,15 +76,16 @@ def _stages_of_ffn(dev, T, k, x_host, routed=True):
 
 
 @pytest.mark.parametrize("name,T,routed,want", [
-    ("olmoe-like", 4, True, False),      # 0.5 tokens per expert
-    ("olmoe-like", 16, True, False),     # 2 per expert: the fused launch
-    ("olmoe-like", 64, True, True),      # 8 per expert
-    ("qwen3-moe-like", 32, True, False),  # 2 per expert
-    ("qwen3-moe-like", 64, True, True),  # 4 per expert
-    ("llama4-like", 8, True, False),     # 8 pairs on 16 experts
-    ("llama4-like", 8, False, True),     # the shared expert holds all 8 tokens
-    ("llama4-like", 64, True, True),     # 4 per expert
-    ("deepseek-v2-like", 2, False, False),
+    ("olmoe-like", 16, True, False),      # 2 per expert: the fused launch
+    ("olmoe-like", 128, True, False),     # 16 per expert, W = 268 MB: needs 32
+    ("olmoe-like", 256, True, True),      # 32 per expert
+    ("qwen3-moe-like", 256, True, False),  # 16 per expert, W = 403 MB
+    ("qwen3-moe-like", 512, True, True),  # 32 per expert
+    ("llama4-like", 64, True, False),     # 4 per expert, W = 1.3 GB: needs 8
+    ("llama4-like", 128, True, True),     # 8 per expert
+    ("llama4-like", 64, False, False),    # a lone 84 MB shared expert: needs 128
+    ("llama4-like", 128, False, True),
+    ("deepseek-v2-like", 8, False, False),
 ])
 def test_union_taken_where_expected(name, T, routed, want):
     inp, dev = _layer(name)
@@ -99,11 +102,12 @@ def test_union_taken_where_expected(name, T, routed, want):
 
 @pytest.mark.parametrize("k", [1, 5, 63, 64, 65, 128, 191, 192])
 def test_union_keep_extremes_ragged(k):
-    # H = 320 (5 column blocks), d_ff = 192 (3 row stages), 12 experts of
-    # which about 37 * 3 / 12 = 9 tokens each: union counts from a few rows
-    # to all 192, on and off the 64-row stage; shared group of d_ff 128
+    # H = 320 (5 column blocks), d_ff = 192 (3 row stages), 12 small experts
+    # of 520 * 3 / 12 = 130 tokens each (past the 128-token GEMM item): union
+    # counts from a few rows to all 192, on and off the 64-row stage; shared
+    # group of d_ff 128
     inp, dev = _layer("olmoe-like", **RAGGED)
-    x = inp.tokens(37, 3)
+    x = inp.tokens(520, 3)
     k_sh = min(k, 128)
     say(f"[case] union ragged bf16 k={k} k_sh={k_sh}")
     got = dev.run(x, k, SP, k_sh=k_sh, path_sh=SP)
@@ -121,7 +125,7 @@ def test_union_single_expert_all_tokens():
     compare_layer(inp, x, got, 40, k_sh=100)
 
 
-@pytest.mark.parametrize("name,T", [("olmoe-like", 64), ("llama4-like", 64)])
+@pytest.mark.parametrize("name,T", [("olmoe-like", 256), ("llama4-like", 128)])
 def test_union_reads_only_union_rows(name, T):
     # NaN in every W_d row that no token of its expert keeps: the same bits
     # (a row outside the union loaded and multiplied by zero would give NaN)
@@ -148,7 +152,7 @@ def test_union_layer_residual_in_place():
     # x_next = x + y (rounded to bf16) written by the combine, in place over
     # the layer input; equals route, FFN, then moe_residual_add
     shape = S.LAYERS["olmoe-like"]
-    T, k = 64, B.moe_keep_count(0.9, shape.d_ff)
+    T, k = 256, B.moe_keep_count(0.9, shape.d_ff)
     say(f"[case] union layer + residual T={T}")
     L = DeviceLayer(LayerInputs(shape, seed=0))
     x = to_dev(S.tokens(shape, 131, T))
@@ -172,9 +176,10 @@ def test_union_layer_residual_in_place():
 
 
 @pytest.mark.parametrize("name,T,over", [
-    ("olmoe-like", 100, RAGGED),          # 25 tokens per expert: two token tiles per item
+    ("olmoe-like", 100, RAGGED),          # 25 tokens per expert: four token tiles per item
     ("olmoe-like", 256, {}),              # 32 per expert, H = 2048 (8 column blocks)
-    ("llama4-like", 256, {}),             # 16 per expert, d_ff 8192, H = 5120
+    ("llama4-like", 128, {}),             # 8 per expert, d_ff 8192, H = 5120
+    ("llama4-like", 256, {}),             # 16 per expert
 ])
 @pytest.mark.parametrize("path", [SP, B.MOE_PATH_DENSE])
 def test_skinny_items_both_paths(name, T, over, path):
