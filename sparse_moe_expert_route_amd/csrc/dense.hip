@@ -1,9 +1,13 @@
-// Dense-path grouped GEMMs of the MoE expert FFN (gfx950, MFMA), for
-// batches where an expert holds many tokens and the contraction is dense:
+// Grouped GEMMs of the MoE expert FFN (gfx950, MFMA), for batches where
+// experts hold several tokens:
 //
 //   gateup_gemm   h = silu(W_g x) * (W_u x) per (expert, <= 128 tokens) item,
 //                 weights in the packed fragment layout, tokens staged in LDS
-//   down_dense    partial[pair, chunk] = hm . W_d over one K chunk (MFMA)
+//   down_skinny   partial[pair, chunk] = hm . W_d over one K chunk, items of
+//                 <= 32 or 64 tokens (HBM-bound)
+//   down_wide     the same for items of <= 128 tokens
+//   union_*       the sparse path's packed-rows form: each active expert's
+//                 union of kept rows, for the two down GEMMs to gather
 //   combine       y[t] (+)= the token's partials in a fixed order
 //
 // Method: the page "Uncovering Intra-expert Activation Sparsity for
@@ -203,211 +207,6 @@ __global__ __launch_bounds__(256, 2) void gateup_gemm_kernel(const void *__restr
   }
 }
 
-// ---------------------------------------------------------------- dense down (bf16)
-// Dense-path down GEMM: partial[pair, chunk, col] = sum over the chunk's k of
-// hm[pair, k] * W_d[e][k, col], for a work item (expert, <= 128 of its
-// tokens) x 64 output columns x one K chunk (blockIdx.z).  MFMA A = the
-// masked h rows (k-contiguous, staged through LDS in padded rows); MFMA B
-// needs k-contiguous columns of the row-major W_d, so each stage of 64 rows
-// is packed into bf16 k-pairs and written transposed ([col][k]) into LDS.
-// The k-pair slot is XOR-swizzled by the column, so the transposing writes
-// and the 16-byte fragment reads both reach the 2-way minimum of bank
-// conflicts.  Waves form a 2 x 2 grid: each owns 4 token tiles x 2 column
-// tiles.  Both LDS tiles are double-buffered with one register stage.
-constexpr int kDnTok = 128;                 // tokens per work item
-constexpr int kDnCols = 64;                 // output columns per block
-constexpr int kDnK = 64;                    // k per stage
-constexpr int kDnArow = kDnK * 2 + 16;      // LDS bytes per staged hm row (+ pad)
-constexpr int kDnBrow = kDnK * 2;           // LDS bytes per transposed W_d column
-
-__device__ __forceinline__ int dn_swz(int col) { return 4 * ((col & 7) ^ ((col >> 3) & 7)); }
-
-// UNION: the sparse path's packed-rows form.  k runs over the union of the
-// kept rows of the item's expert (urow[e * d_ff ..], ascending, ucnt[e] of
-// them) instead of every row: B gathers those W_d rows (two row indices per
-// thread per stage, loaded one stage ahead), A is the masked activations
-// compacted to the same positions (hm = the union kernel's hmu, zero-padded
-// to a multiple of kDnK).  Rows past the union are never read.
-template <bool UNION = false>
-__global__ __launch_bounds__(256, 2) void down_dense_gemm_kernel(const uint16_t *__restrict__ wd,
-                                                                 const uint16_t *__restrict__ hm,
-                                                                 RouteView rv, int H, int d_ff,
-                                                                 int kchunk,
-                                                                 float *__restrict__ partial,
-                                                                 const int32_t *__restrict__ urow = nullptr,
-                                                                 const int32_t *__restrict__ ucnt = nullptr) {
-  __shared__ __attribute__((aligned(16))) uint8_t as[2][kDnTok * kDnArow];
-  __shared__ __attribute__((aligned(16))) uint32_t bs[2][kDnCols * kDnBrow / 4];
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  int e, q0, ntok;
-  const unsigned qb = xcd_logical_block();
-  const int bx = (int)(qb % gridDim.x), by = (int)(qb / gridDim.x % gridDim.y);
-  if (!find_item<kDnTok>(rv, bx, e, q0, ntok)) return;  // block-uniform
-  const int col0 = by * kDnCols;
-  const int S = gridDim.z, sidx = (int)(qb / (gridDim.x * gridDim.y));
-  int uc = d_ff, kend = d_ff;
-  if (UNION) {  // the chunks split the union, whose size only the device knows
-    uc = ucnt[e];
-    uc = uc < 0 ? 0 : (uc > d_ff ? d_ff : uc);
-    kend = (uc + kDnK - 1) / kDnK * kDnK;  // hm is zero past uc up to here
-    kchunk = ((uc + S - 1) / S + kDnK - 1) / kDnK * kDnK;
-  }
-  const int k0 = sidx * kchunk;
-  const int nit = max(0, (min(kend, k0 + kchunk) - k0) / kDnK);
-  const int ntiles = (ntok + 15) >> 4;
-
-  // Every load is issued unconditionally, so that the compiler's waits
-  // count the loads in flight instead of draining them.  A rows past the
-  // item's tokens read the first token's row: they only feed accumulator
-  // rows that are never stored.
-  // A staging: rows tid / 8 + 32 i (i < 4), 16-byte chunk tid % 8 (8 k)
-  const int arow = tid >> 3, achunk = tid & 7;
-  const uint16_t *ap[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c = arow + 32 * i;
-    ap[i] = hm + (size_t)rv.pair_at(q0 + (c < ntok ? c : 0)) * d_ff + k0 + achunk * 8;
-  }
-  // B staging: k-pair kp = tid / 8 (rows 2 kp, 2 kp + 1), columns 8 cg .. 8 cg + 7
-  const int kp = tid >> 3, cg = tid & 7;
-  const uint16_t *bp = wd + ((size_t)e * d_ff + k0 + 2 * kp) * H + col0 + 8 * cg;
-  // UNION: the stage's two union rows, their ids read one stage ahead;
-  // positions past the union count read the union's first row and are
-  // staged as zeros
-  const uint16_t *bcol = wd + (size_t)e * d_ff * H + col0 + 8 * cg;
-  const int32_t *ur = UNION ? urow + (size_t)e * d_ff : nullptr;
-  int row0 = 0;
-  if (UNION && uc > 0) row0 = min(max(ur[0], 0), d_ff - 1);
-  int rn[2] = {0, 0};  // row ids of the next stage, in flight
-  int rw[2] = {0, 0};  // row ids of the stage being loaded
-  uint32_t rok = 0u, sok = 0u;  // their validity bits (rw, then the staged set)
-  auto fetch_rows = [&](int it) {  // q + 1 < kend <= d_ff: inside e's list
-    const int q = k0 + it * kDnK + 2 * kp;
-    rn[0] = ur[q];
-    rn[1] = ur[q + 1];
-  };
-  auto take_rows = [&](int it) {
-    const int q = k0 + it * kDnK + 2 * kp;
-    rok = 0u;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const bool ok = q + i < uc && (unsigned)rn[i] < (unsigned)d_ff;
-      rw[i] = ok ? rn[i] : row0;
-      rok |= ok ? 1u << i : 0u;
-    }
-  };
-  if (UNION && nit > 0) {
-    fetch_rows(0);
-    take_rows(0);
-    fetch_rows(min(1, nit - 1));
-  }
-
-  u32x4 sa[4], sb[2];
-  auto load_stage = [&](int it) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) sa[i] = ld16(ap[i] + it * kDnK);
-    if (UNION) {
-      sb[0] = ld16_nt(bcol + (size_t)rw[0] * H);
-      sb[1] = ld16_nt(bcol + (size_t)rw[1] * H);
-      sok = rok;
-      take_rows(min(it + 1, nit - 1));
-      fetch_rows(min(it + 2, nit - 1));
-    } else {
-      sb[0] = ld16_nt(bp + (size_t)it * kDnK * H);
-      sb[1] = ld16_nt(bp + (size_t)it * kDnK * H + H);
-    }
-  };
-  auto store_stage = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<u32x4 *>(&as[buf][(arow + 32 * i) * kDnArow + achunk * 16]) = sa[i];
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {  // column 8 cg + c gets the pair (row 2 kp, row 2 kp + 1)
-      uint32_t lo = (sb[0][c >> 1] >> (16 * (c & 1))) & 0xffffu;
-      uint32_t hi = (sb[1][c >> 1] >> (16 * (c & 1))) & 0xffffu;
-      if (UNION) {
-        lo = sok & 1u ? lo : 0u;
-        hi = sok & 2u ? hi : 0u;
-      }
-      const int col = 8 * cg + c;
-      bs[buf][col * (kDnBrow / 4) + (kp ^ dn_swz(col))] = lo | (hi << 16);
-    }
-  };
-
-  const int r = lane & 15, g = lane >> 4;
-  const int wt = wid >> 1, wc = wid & 1;  // token tiles 4 wt .. 4 wt + 3, column tiles 2 wc, 2 wc + 1
-  f32x4 acc[4][2];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) { acc[i][0] = f32x4{0, 0, 0, 0}; acc[i][1] = f32x4{0, 0, 0, 0}; }
-
-  if (nit > 0) {
-    load_stage(0);
-    store_stage(0);
-  }
-  __syncthreads();
-  // steady steps (it + 1 < nit: no branch around the loads), then the last
-  auto step = [&](int it, auto steadyc) {
-    constexpr bool more = decltype(steadyc)::value;
-    const int cur = it & 1;
-    if (more) load_stage(it + 1);
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      u32x4 b[2];
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int col = (2 * wc + j) * 16 + r;
-        const int w0 = (ks * 16 + 4 * g) ^ dn_swz(col);  // 4 k-pairs = this lane's 8 k
-        b[j] = *reinterpret_cast<const u32x4 *>(&bs[cur][col * (kDnBrow / 4) + w0]);
-      }
-      auto afrag = [&](int i) {
-        return *reinterpret_cast<const u32x4 *>(
-            &as[cur][((4 * wt + i) * 16 + r) * kDnArow + ks * 64 + g * 16]);
-      };
-      // A fragments read one tile ahead of their MFMAs (rows past the
-      // item's tokens hold zeros, so the read ahead is harmless)
-      u32x4 av = afrag(0);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (4 * wt + i < ntiles) {  // wave-uniform
-          const u32x4 an = afrag(i < 3 ? i + 1 : 3);
-          acc[i][0] = mfma_bf16(av, b[0], acc[i][0]);
-          acc[i][1] = mfma_bf16(av, b[1], acc[i][1]);
-          av = an;
-        }
-      }
-    }
-    if (more) store_stage(cur ^ 1);
-    __syncthreads();
-  };
-  for (int it = 0; it + 1 < nit; ++it) step(it, SkIc<1>{});
-  if (nit > 0) step(nit - 1, SkIc<0>{});
-  // D: lane holds column r of each column tile, token rows 4 g + rr of each
-  // token tile; the rows' pair ids are all read before the first store
-  int prow[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int c = (4 * wt + i) * 16 + 4 * g + rr;
-      prow[i][rr] = rv.pair_at(q0 + (c < ntok ? c : 0));
-    }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int tl = 4 * wt + i;
-    if (tl >= ntiles) continue;
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int c = tl * 16 + 4 * g + rr;
-      if (c < ntok) {
-        const size_t row = (size_t)prow[i][rr] * S + sidx;
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          partial[row * H + col0 + (2 * wc + j) * 16 + r] = acc[i][j][rr];
-      }
-    }
-  }
-}
-
 // ---------------------------------------------------------------- skinny down GEMM
 // The down product for items of at most 16 * MT tokens of one expert (a few
 // tokens per expert: HBM-bound on W_d).  Block = 4 waves x 256 output
@@ -420,9 +219,11 @@ __global__ __launch_bounds__(256, 2) void down_dense_gemm_kernel(const uint16_t 
 // conflicts.  The coefficients (A: token rows, k-contiguous) come straight
 // from global memory in the MFMA layout, also one stage ahead.  Wave w
 // owns columns 64 w .. 64 w + 63 (4 column tiles) for all MT token tiles.
-// UNION: as in down_dense_gemm_kernel, k runs over the expert's union of
-// kept rows (urow, ucnt), whose row ids each thread fetches two stages
-// ahead; hm is then the compacted coefficient rows (hmu).
+// UNION (the sparse path's packed-rows form): k runs over the expert's
+// union of kept rows (urow[e * d_ff ..], ascending, ucnt[e] of them), whose
+// row ids each thread fetches two stages ahead, and hm is then the
+// coefficients compacted to the same positions (hmu, zero-padded to a
+// multiple of 64).  Rows past the union are never read.
 constexpr int kSkCols = 256;   // output columns per block
 constexpr int kSkK = 64;       // k per stage
 constexpr int kSkColB = 144;   // LDS bytes per staged column (128 + 16 pad)
@@ -684,20 +485,249 @@ static int skinny_splits(int T, int E, int top_k, int implicit, int H, int d_ff,
   return S < 1 ? 1 : (int)S;
 }
 
-// K chunks of the dense down GEMM: enough blocks to fill the chip when few
-// work items exist (small batches), each chunk a multiple of 64 rows and at
-// least 256.  A function of the shape only, so the workspace size and the
-// launch agree.
-static int dense_down_kchunk(int T, int E, int top_k, int H, int d_ff) {
+// ---------------------------------------------------------------- wide down GEMM
+// The down product for items of up to 128 tokens of one expert (many
+// tokens per expert: the MFMA-bound shared expert at large batches, routed
+// experts past the skinny GEMM's range).  Block = 4 waves in a 2 x 2 grid x
+// 128 output columns x one K chunk; wave (wt, wc) owns tokens 64 wt ..
+// 64 wt + 63 (4 token tiles) x columns 64 wc .. 64 wc + 63 (4 column
+// tiles), so each k-step reads 4 + 4 fragments for 16 MFMAs.  Stage = 64
+// k: the coefficient rows (A, k-contiguous) are staged to LDS as they are
+// (rows padded to 144 bytes); the W_d rows (B) are transposed in registers,
+// each thread holding 4 rows x 8 columns, into 8-byte k-runs written to a
+// column-major LDS tile (column stride 144 bytes, 16-byte slot = k-chunk ^
+// ((col >> 4) & 7): no bank conflicts for the writes or the fragment reads).
+// Both tiles are double-buffered; DEPTH register stages are in flight (the
+// k loop is latency-bound with one); every load is issued unconditionally
+// (see down_skinny_kernel).  UNION as there.
+constexpr int kWdTok = 128;   // tokens per work item
+constexpr int kWdCols = 128;  // output columns per block
+constexpr int kWdK = 64;      // k per stage
+constexpr int kWdRowB = 144;  // LDS bytes per staged coefficient row / W_d column
+// Register stages in flight.  Measured at Llama-4-like T = 1024 (shared
+// expert / routed experts): one stage 159 / 317 us, two 156 / 318 us, two
+// with cached instead of non-temporal W_d loads 152 / 331 us; the stage
+// is not latency-bound, so one it is.
+constexpr int kWdDepth = 1;
+
+template <bool UNION, int DEPTH>
+__global__ __launch_bounds__(256, 2) void down_wide_kernel(const uint16_t *__restrict__ wd,
+                                                           const uint16_t *__restrict__ hm,
+                                                           RouteView rv, int H, int d_ff,
+                                                           int kchunk,
+                                                           float *__restrict__ partial,
+                                                           const int32_t *__restrict__ urow,
+                                                           const int32_t *__restrict__ ucnt) {
+  __shared__ __attribute__((aligned(16))) uint8_t as[2][kWdTok * kWdRowB];
+  __shared__ __attribute__((aligned(16))) uint8_t bs[2][kWdCols * kWdRowB];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  int e, q0, ntok;
+  const unsigned qb = xcd_logical_block();
+  const int bx = (int)(qb % gridDim.x), by = (int)(qb / gridDim.x % gridDim.y);
+  if (!find_item<kWdTok>(rv, bx, e, q0, ntok)) return;  // block-uniform
+  const int col0 = by * kWdCols;
+  const int S = gridDim.z, sidx = (int)(qb / (gridDim.x * gridDim.y));
+  int uc = d_ff, kend = d_ff;
+  if (UNION) {  // the chunks split the union, whose size only the device knows
+    uc = ucnt[e];
+    uc = uc < 0 ? 0 : (uc > d_ff ? d_ff : uc);
+    kend = (uc + kWdK - 1) / kWdK * kWdK;  // hm is zero past uc up to here
+    kchunk = ((uc + S - 1) / S + kWdK - 1) / kWdK * kWdK;
+  }
+  const int k0 = sidx * kchunk;
+  const int nit = max(0, (min(kend, k0 + kchunk) - k0) / kWdK);
+  const int ntiles = (ntok + 15) >> 4;
+
+  // A staging: rows tid / 8 + 32 i (i < 4), 16-byte chunk tid % 8; rows past
+  // the item's tokens stage the first token's row (never-stored accumulators)
+  const int arow = tid >> 3, achunk = tid & 7;
+  const uint16_t *ap[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = arow + 32 * i;
+    ap[i] = hm + (size_t)rv.pair_at(q0 + (c < ntok ? c : 0)) * d_ff + k0 + achunk * 8;
+  }
+  // B staging: rows 4 rg .. 4 rg + 3 of a stage, columns col0 + 8 cg .. + 7
+  // (columns past H, a multiple of 64, read column block col0 and feed only
+  // never-stored outputs)
+  const int rg = tid >> 4, cg = tid & 15;
+  const bool colok = col0 + 8 * cg < H;
+  const uint16_t *bcol = wd + (size_t)e * d_ff * H + (colok ? col0 + 8 * cg : col0);
+  const int32_t *ur = UNION ? urow + (size_t)e * d_ff : nullptr;
+  int row0 = 0;
+  if (UNION && uc > 0) row0 = min(max(ur[0], 0), d_ff - 1);
+  int rows[4];
+  uint32_t rvalid = 0u;
+  u32x4 rn = u32x4{0, 0, 0, 0};  // UNION: row ids of the next stage, in flight
+  auto fetch_rows = [&](int it) {  // q + 4 <= kend <= d_ff: inside e's list
+    rn = ld16(ur + k0 + it * kWdK + 4 * rg);
+  };
+  auto take_rows = [&](int it) {
+    const int q = k0 + it * kWdK + 4 * rg;
+    rvalid = 0u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int v = (int)rn[i];
+      const bool ok = q + i < uc && (unsigned)v < (unsigned)d_ff;
+      rows[i] = ok ? v : row0;
+      rvalid |= ok ? 1u << i : 0u;
+    }
+  };
+
+  // DEPTH register sets of staged loads: stage it + DEPTH is issued while
+  // stage it is multiplied
+  u32x4 sa[DEPTH][4], sb[DEPTH][4];
+  uint32_t svalid[DEPTH];
+  auto load_stage = [&](int it, u32x4 (&da)[4], u32x4 (&db)[4], uint32_t &dv) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) da[i] = ld16(ap[i] + it * kWdK);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = UNION ? rows[i] : k0 + it * kWdK + 4 * rg + i;
+      db[i] = ld16_nt(bcol + (size_t)row * H);
+    }
+    dv = rvalid;
+  };
+  auto store_stage = [&](int buf, const u32x4 (&ra)[4], const u32x4 (&rb)[4], uint32_t vv) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<u32x4 *>(&as[buf][(arow + 32 * i) * kWdRowB + achunk * 16]) = ra[i];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {  // column 8 cg + c gets rows 4 rg .. 4 rg + 3 (one 8-byte k-run)
+      const int j = c >> 1;
+      uint32_t v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t w = rb[i][j];
+        v[i] = (c & 1) ? (w >> 16) : (w & 0xffffu);
+        if (UNION) v[i] = (vv >> i) & 1u ? v[i] : 0u;
+      }
+      const int col = 8 * cg + c;
+      const int off = col * kWdRowB + ((((rg >> 1) ^ ((col >> 4) & 7))) << 4) + (rg & 1) * 8;
+      uint2 o;
+      o.x = v[0] | (v[1] << 16);
+      o.y = v[2] | (v[3] << 16);
+      *reinterpret_cast<uint2 *>(&bs[buf][off]) = o;
+    }
+  };
+
+  const int r = lane & 15, g = lane >> 4;
+  const int wt = wid >> 1, wc = wid & 1;
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0, 0, 0, 0};
+
+  if (nit > 0) {
+    if (UNION) {
+      fetch_rows(0);
+      take_rows(0);
+      fetch_rows(min(1, nit - 1));
+    }
+    load_stage(0, sa[0], sb[0], svalid[0]);
+    if (DEPTH == 2 && nit > 1) {
+      if (UNION) {
+        take_rows(1);
+        fetch_rows(min(2, nit - 1));
+      }
+      load_stage(1, sa[DEPTH - 1], sb[DEPTH - 1], svalid[DEPTH - 1]);
+    }
+    store_stage(0, sa[0], sb[0], svalid[0]);
+  }
+  __syncthreads();
+  // One step: stage it + DEPTH into register set SL = it % DEPTH (whose
+  // stage is already in LDS), multiply stage it, write stage it + 1 from
+  // its register set to the other buffer.  STEADY: all of it in range, no
+  // branch around a load.
+  auto step = [&](int it, auto slc, auto steadyc) {
+    constexpr int SL = decltype(slc)::value;
+    constexpr bool STEADY = decltype(steadyc)::value;
+    const int cur = it & 1;
+    const int ahead = it + DEPTH;
+    if (STEADY || ahead < nit) {
+      if (UNION) {
+        take_rows(ahead);
+        fetch_rows(min(ahead + 1, nit - 1));
+      }
+      load_stage(ahead, sa[SL], sb[SL], svalid[SL]);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      u32x4 b[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int col = 64 * wc + 16 * j + r;
+        b[j] = *reinterpret_cast<const u32x4 *>(
+            &bs[cur][col * kWdRowB + (((4 * ks + g) ^ ((col >> 4) & 7)) << 4)]);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (4 * wt + i < ntiles) {  // wave-uniform
+          const u32x4 a = *reinterpret_cast<const u32x4 *>(
+              &as[cur][((4 * wt + i) * 16 + r) * kWdRowB + ks * 64 + g * 16]);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[i][j] = mfma_bf16(a, b[j], acc[i][j]);
+        }
+      }
+    }
+    if (STEADY || it + 1 < nit) {
+      constexpr int NX = (SL + 1) % DEPTH;
+      store_stage(cur ^ 1, sa[NX], sb[NX], svalid[NX]);
+    }
+    __syncthreads();
+  };
+  int it = 0;
+  for (; it + DEPTH + 1 < nit; it += DEPTH) {
+    step(it, SkIc<0>{}, SkIc<1>{});
+    if (DEPTH == 2) step(it + 1, SkIc<1 % DEPTH>{}, SkIc<1>{});
+  }
+  for (; it < nit; it += DEPTH) {
+    step(it, SkIc<0>{}, SkIc<0>{});
+    if (DEPTH == 2 && it + 1 < nit) step(it + 1, SkIc<1 % DEPTH>{}, SkIc<0>{});
+  }
+
+  // D: lane holds column r of each column tile, token rows 4 g + rr of each
+  // token tile; the rows' pair ids are all read before the first store
+  int prow[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int c = (4 * wt + i) * 16 + 4 * g + rr;
+      prow[i][rr] = rv.pair_at(q0 + (c < ntok ? c : 0));
+    }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (4 * wt + i >= ntiles) continue;
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int c = (4 * wt + i) * 16 + 4 * g + rr;
+      if (c < ntok) {
+        const size_t row = (size_t)prow[i][rr] * S + sidx;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int col = col0 + 64 * wc + 16 * j + r;
+          if (col < H) partial[row * H + col] = acc[i][j][rr];
+        }
+      }
+    }
+  }
+}
+
+// K chunks of the wide down GEMM: enough for ~1024 blocks, each chunk >= 256
+// rows, and P * chunks within dense_down_partial_rows.
+static int wide_splits(int T, int E, int top_k, int implicit, int H, int d_ff) {
   const long P = (long)T * top_k;
-  const long items = (E < P ? E : P) + P / kDnTok;
-  const long base = items * (H / kDnCols);
+  const long items = implicit ? (long)E * ((T + kWdTok - 1) / kWdTok)
+                              : (E < P ? E : P) + P / kWdTok;
+  const long base = items * ((H + kWdCols - 1) / kWdCols);
   long S = (1024 + base - 1) / base;
   const long smax = d_ff / 256 > 0 ? d_ff / 256 : 1;
   if (S > smax) S = smax;
-  if (S < 1) S = 1;
-  const long per = (d_ff + S - 1) / S;
-  return (int)((per + kDnK - 1) / kDnK * kDnK);
+  const long bound = P > 0 ? (long)(dense_down_partial_rows(T, E, top_k, H) / P) : 1;
+  if (S > bound) S = bound;
+  return S < 1 ? 1 : (int)S;
 }
 
 // Partial rows the dense down GEMM may write at most T tokens: P * chunks
@@ -840,7 +870,7 @@ __global__ __launch_bounds__(256) void union_coef_kernel(const int32_t *__restri
     }
     if (tid == 0) ucnt[e] = uc;
   }
-  const int upad = (uc + kDnK - 1) / kDnK * kDnK;
+  const int upad = (uc + kWdK - 1) / kWdK * kWdK;
   for (int q = tid; q < upad; q += 256) crow[q] = 0;
   __syncthreads();
   for (int i = tid; i < k; i += 256) {
@@ -938,7 +968,7 @@ bool union_form(int T, int E, int top_k, int H, int d_ff) {
 }
 
 bool union_layout_ok(int T, int H, int d_ff, int bf16) {
-  return bf16 && H % kDnCols == 0 && d_ff % kDnK == 0 && d_ff <= kUnionMaxDff &&
+  return bf16 && H % 64 == 0 && d_ff % kWdK == 0 && d_ff <= kUnionMaxDff &&
          T >= kUnionMinTokensLarge;
 }
 
@@ -983,13 +1013,11 @@ hipError_t launch_down_union(const FfnArgs &a, const RouteView &rv, hipStream_t 
       down_skinny_kernel<4, true, sk_depth<4, true>()><<<grid, 256, 0, stream>>>(wd, a.hmu, rv, a.H, a.d_ff, 0, a.partial,
                                                             a.urow, a.ucnt);
   } else {
-    const int kc = dense_down_kchunk(a.T, a.E, a.top_k, a.H, a.d_ff);
-    S = (a.d_ff + kc - 1) / kc;
+    S = wide_splits(a.T, a.E, a.top_k, a.implicit, a.H, a.d_ff);
     if ((size_t)P * S > dense_down_partial_rows(a.T, a.E, a.top_k, a.H)) return hipErrorInvalidValue;
-    dim3 grid(n_items(a, kDnTok), a.H / kDnCols, S);
-    down_dense_gemm_kernel<true><<<grid, 256, 0, stream>>>(static_cast<const uint16_t *>(a.w_down),
-                                                           a.hmu, rv, a.H, a.d_ff, kc, a.partial,
-                                                           a.urow, a.ucnt);
+    dim3 grid(n_items(a, kWdTok), (a.H + kWdCols - 1) / kWdCols, S);
+    down_wide_kernel<true, kWdDepth><<<grid, 256, 0, stream>>>(
+        static_cast<const uint16_t *>(a.w_down), a.hmu, rv, a.H, a.d_ff, 0, a.partial, a.urow, a.ucnt);
   }
   timer_end(stream);
   dim3 cgrid(a.T, (a.H + 255) / 256);
@@ -1019,13 +1047,15 @@ hipError_t launch_down_dense(const FfnArgs &a, const RouteView &rv, hipStream_t 
     else
       down_skinny_kernel<4, false, sk_depth<4, false>()><<<grid, 256, 0, stream>>>(wd, hm, rv, a.H, a.d_ff, kc, a.partial,
                                                              nullptr, nullptr);
-  } else {
-    const int kc = dense_down_kchunk(a.T, a.E, a.top_k, a.H, a.d_ff);
+  } else {  // many tokens per expert: the 128 x 128 GEMM over all d_ff rows
+    S = wide_splits(a.T, a.E, a.top_k, a.implicit, a.H, a.d_ff);
+    const int per = (a.d_ff + S - 1) / S;
+    const int kc = (per + kWdK - 1) / kWdK * kWdK;
     S = (a.d_ff + kc - 1) / kc;
-    if (P * S > dense_down_partial_rows(a.T, a.E, a.top_k, a.H))
-      return hipErrorInvalidValue;  // cannot happen: the bound covers every split count
-    dim3 grid(n_items(a, kDnTok), a.H / kDnCols, S);
-    down_dense_gemm_kernel<false><<<grid, 256, 0, stream>>>(wd, hm, rv, a.H, a.d_ff, kc, a.partial);
+    if (P * S > dense_down_partial_rows(a.T, a.E, a.top_k, a.H)) return hipErrorInvalidValue;
+    dim3 grid(n_items(a, kWdTok), (a.H + kWdCols - 1) / kWdCols, S);
+    down_wide_kernel<false, kWdDepth><<<grid, 256, 0, stream>>>(wd, hm, rv, a.H, a.d_ff, kc,
+                                                                a.partial, nullptr, nullptr);
   }
   timer_end(stream);
   dim3 cgrid(a.T, (a.H + 255) / 256);
