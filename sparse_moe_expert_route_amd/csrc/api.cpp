@@ -100,10 +100,12 @@ FfnLayout ffn_layout(const moe_desc *d, int32_t T, int32_t k, moe_path path) {
   off += up(P * d->d_ff * 4);
   // the fused decode-batch FFN's counters, directly after h (its gate/up
   // blocks find them from h's address), then its per-pair partial outputs
+  // (sized for min(T, kFusedMaxTokens): the fused launch takes no larger batch)
+  const int Tf = T < moe::kFusedMaxTokens ? T : moe::kFusedMaxTokens;
   L.sync = off;
-  if (path == MOE_PATH_SPARSE) off += up(moe::fused_sync_words(T, d->n_experts, d->hidden) * 4);
+  if (path == MOE_PATH_SPARSE) off += up(moe::fused_sync_words(Tf, d->n_experts, d->hidden) * 4);
   L.fpart = off;
-  if (path == MOE_PATH_SPARSE) off += up(P * d->hidden * 4);
+  if (path == MOE_PATH_SPARSE) off += up((size_t)Tf * d->top_k * d->hidden * 4);
   L.idx = off;
   off += up(P * (size_t)k * 4);
   L.hact = off;

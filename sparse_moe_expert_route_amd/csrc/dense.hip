@@ -469,8 +469,8 @@ static int skinny_tiles(int T, int E, int top_k, int implicit) {
 
 // K chunks of the skinny GEMM: enough for ~2048 blocks (a lone shared
 // expert at a few tokens has only H / 256 column blocks), each chunk >= 256
-// rows, at most 16, and at most max(4, 1024 / P) so that the partial rows
-// stay within dense_down_partial_rows.
+// rows, at most 16, and at most max(4, 1024 / P) (dense_down_partial_rows
+// bounds the partial rows this gives).
 static int skinny_splits(int T, int E, int top_k, int implicit, int H, int d_ff, int mt) {
   const long P = (long)T * top_k;
   const long items = implicit ? (long)E * ((T + 16 * mt - 1) / (16 * mt))
@@ -730,15 +730,24 @@ static int wide_splits(int T, int E, int top_k, int implicit, int H, int d_ff) {
   return S < 1 ? 1 : (int)S;
 }
 
-// Partial rows the dense down GEMM may write at most T tokens: P * chunks
-// <= P + 65536 P / (items H) with items >= min(E, P), so this bound holds for
-// every smaller T too (a workspace sized for T serves any shorter call).
+// Partial rows the down GEMMs may write for at most T tokens (P pairs).
+// Wide: chunks = ceil(1024 / base), base = items * cb (cb = ceil(H / 128)
+// column blocks) with items >= max(1, P / 128), so P * chunks <= P + 1024 *
+// min(P, 128) / cb.  Skinny: chunks = ceil(2048 / base), base = items * cs
+// (cs = ceil(H / 256)) with items >= max(1, P / 64), and at most
+// max(4, 1024 / P) chunks, so P * chunks <= min(max(4 P, 1024), P + 2048 *
+// min(P, 64) / cs).  Each grows with T, so a workspace sized for T serves
+// any shorter call.
 size_t dense_down_partial_rows(int T, int E, int top_k, int H) {
+  (void)E;
   const size_t P = (size_t)T * top_k;
-  const size_t per_item = P > (size_t)E ? (P + E - 1) / E : 1;
-  const size_t wide = P + (size_t)((65536 + H - 1) / H) * per_item;
-  // the skinny GEMM writes at most max(4, 1024 / P) chunks per pair
-  const size_t skinny = 4 * P > 1024 ? 4 * P : (P > 0 ? 1024 : 0);
+  if (P == 0) return 0;
+  const size_t cb = ((size_t)H + kWdCols - 1) / kWdCols;
+  const size_t wide = P + (1024 * (P < kWdTok ? P : (size_t)kWdTok) + cb - 1) / cb;
+  const size_t cs = ((size_t)H + kSkCols - 1) / kSkCols;
+  const size_t sk_a = 4 * P > 1024 ? 4 * P : 1024;
+  const size_t sk_b = P + (2048 * (P < 64 ? P : (size_t)64) + cs - 1) / cs;
+  const size_t skinny = sk_a < sk_b ? sk_a : sk_b;
   return wide > skinny ? wide : skinny;
 }
 

@@ -1776,7 +1776,6 @@ static void launch_down_topk(const FfnArgs &a, const RouteView &rv, hipStream_t 
 // it, and the per-token down kernel that selects its own masks is as fast
 // as the units without the wait (34.3 us, measured and dropped).
 constexpr int kFusedMinTokens = 5;
-constexpr int kFusedMaxTokens = 16;
 static bool tail_units_shape_ok(const FfnArgs &a) {
   const int V = a.d_ff / 64;
   // d_ff 512, 768, 1024, 1536 (at 2048 the fused kernel spills in its loop)

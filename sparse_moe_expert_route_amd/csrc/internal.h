@@ -132,6 +132,9 @@ size_t union_scratch_words(int T, int E, int d_ff);
 // line: waiting blocks poll them, and pollers of one line all land on one
 // memory channel), per (token, 64-column block), and one abort flag.
 constexpr int kCounterStride = 64;
+// Largest batch of the fused launch (its workspace segments are sized for
+// min(T, this) tokens).
+constexpr int kFusedMaxTokens = 16;
 inline size_t fused_sync_words(int T, int E, int H) {
   return (size_t)E * kCounterStride + (size_t)T * (H / 64) + 1;
 }

@@ -194,3 +194,37 @@ def test_skinny_items_both_paths(name, T, over, path):
     got = dev.run(x, k, path, k_sh=k_sh, path_sh=path)
     err = compare_layer(inp, x, got, k, k_sh=k_sh)
     say(f"   rel_l2={err:.3e}")
+
+
+NARROW = dict(n_experts=4, d_ff=128, top_k=2, norm_topk=False, n_shared=1, d_ff_shared=64,
+              zipf_bias=None, dtype="bf16")
+
+
+@pytest.mark.parametrize("H", [64, 192])
+@pytest.mark.parametrize("T,path", [(20, B.MOE_PATH_DENSE), (300, B.MOE_PATH_DENSE), (300, SP)])
+def test_narrow_hidden_column_blocks(H, T, path):
+    # H = 64 and 192: the skinny GEMM's 256-column and the wide GEMM's
+    # 128-column blocks end past H (the columns past it read a stand-in and
+    # are never stored); d_ff = 128 and 64 (shared): one or two 64-row
+    # stages.  T = 20: 10 tokens per expert (skinny); T = 300: 150 (wide, and
+    # the packed-rows form on the sparse path)
+    inp, dev = _layer("olmoe-like", **dict(NARROW, hidden=H))
+    x = inp.tokens(T, 17)
+    k, k_sh = 13, 40
+    say(f"[case] narrow H={H} T={T} path={path}")
+    got = dev.run(x, k, path, k_sh=k_sh, path_sh=path)
+    err = compare_layer(inp, x, got, k, k_sh=k_sh)
+    say(f"   rel_l2={err:.3e}")
+
+
+def test_union_at_max_tokens():
+    # the ABI's largest token count on a small bf16 layer: 65536 * 3 pairs on
+    # 12 experts take the packed-rows form (16384 tokens each, 128 token
+    # items, 8192 groups of 8 pairs per expert, 196608 coefficient rows)
+    inp, dev = _layer("olmoe-like", **RAGGED)
+    x = inp.tokens(65536, 19)
+    k = O.keep_count(0.7, 192)
+    say("[case] union T=65536")
+    got = dev.run(x, k, SP, k_sh=64, path_sh=SP)
+    err = compare_layer(inp, x, got, k, k_sh=64)
+    say(f"   rel_l2={err:.3e}")
