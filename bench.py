@@ -71,7 +71,8 @@ def parse():
     ap.add_argument("--layer", default=None, help="layer of the crossover sweep")
     ap.add_argument("--batches", default=None, help="batches of the crossover sweep")
     ap.add_argument("--paths", default="sparse,dense,auto",
-                    help="paths of the crossover sweep (sparse, dense, auto)")
+                    help="paths of the crossover sweep (sparse, dense, auto; dense-pk and "
+                         "auto-pk: the dense groups read W_d packed by moe_pack_down)")
     ap.add_argument("--sparsity-shared", type=float, default=None,
                     help="shared-expert sparsity of the crossover sweep (default: --sparsity)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -83,7 +84,7 @@ class Workload:
     """Device-resident layer copies and token batches for one batch size."""
 
     def __init__(self, shape, host_w, dev_w0, T, sparsity, path_arg, dev_sh0=None,
-                 sparsity_shared=None, score="swiglu"):
+                 sparsity_shared=None, score="swiglu", packed_down=False):
         import torch
         import moe_synth as S
         from sparse_moe_expert_route_amd import binding as B
@@ -173,7 +174,26 @@ class Workload:
             self.ffn = lambda d, T_, k, x, wg, wu, wd, r, y, acc, idx, ws: \
                 fn(d, T_, self.tau, x, wg, wu, wd, r, y, acc,
                    self.counts if idx is not None else None, idx, ws)
+        if packed_down and sh.dtype == "bf16":
+            self._pack_down()
         self.graphs = []
+
+    def _pack_down(self):
+        """The groups on the dense path read W_d packed by moe_pack_down (a
+        deployment that serves both paths keeps both copies)."""
+        B, sh = self.B, self.shape
+        if self.path == B.MOE_PATH_DENSE:
+            self.desc = B.make_desc(sh.hidden, sh.n_experts, sh.d_ff, sh.top_k, sh.norm_topk,
+                                    sh.dtype, gate_up_layout="packed", down_layout="packed")
+            self.copies = [(wr, wg, wu, B.moe_pack_down(self.desc, wd))
+                           for wr, wg, wu, wd in self.copies]
+        if self.desc_sh is not None and self.path_sh == B.MOE_PATH_DENSE:
+            n_sh = sh.n_shared
+            self.desc_sh = B.make_desc(sh.hidden, n_sh, sh.d_ff_shared, n_sh, False, sh.dtype,
+                                       gate_up_layout="packed", down_layout="packed")
+            self.copies_sh = [(sg, su, B.moe_pack_down(self.desc_sh, sd))
+                              for sg, su, sd in self.copies_sh]
+        self.torch.cuda.synchronize()
 
     def step(self, i, idx=None):
         B = self.B
@@ -579,10 +599,10 @@ class HostLayer:
 
 
 def measure(shape, host, dev_w0, T, args, path=None, dev_sh0=None, score="swiglu",
-            sparsity=None, sparsity_shared=None):
+            sparsity=None, sparsity_shared=None, packed_down=False):
     wl = Workload(shape, host, dev_w0, T, args.sparsity if sparsity is None else sparsity,
                   path or args.path, dev_sh0=dev_sh0, score=score,
-                  sparsity_shared=sparsity_shared)
+                  sparsity_shared=sparsity_shared, packed_down=packed_down)
     log(f"[bench] {shape.name} T={T} k={wl.k} path={'sparse' if wl.path == 0 else 'dense'} "
         f"copies={wl.L}")
     wl.capture()
@@ -797,13 +817,15 @@ def crossover(args):
     host.wg = host.wu = host.wd = host.shared = None     # device copies suffice from here on
     torch.cuda.synchronize()
     paths = [p for p in args.paths.split(",") if p]
-    assert paths and all(p in ("sparse", "dense", "auto") for p in paths), args.paths
+    assert paths and all(p in ("sparse", "dense", "auto", "dense-pk", "auto-pk")
+                         for p in paths), args.paths
     rows = []
     for T in batches:
         row = {"T": T}
         for path in paths:
-            wl, res = measure(shape, host, dev_w0, T, args, path=path, dev_sh0=dev_sh0,
-                              sparsity_shared=args.sparsity_shared)
+            wl, res = measure(shape, host, dev_w0, T, args, path=path.split("-")[0],
+                              dev_sh0=dev_sh0, sparsity_shared=args.sparsity_shared,
+                              packed_down=path.endswith("-pk"))
             kern = {k: round(v["per_step_us"], 2) for k, v in res["kernels"].items()}
             ent = {"us_per_call": round(res["us_per_call"], 2),
                    "us_per_token": round(res["us_per_token"], 3),
@@ -813,13 +835,13 @@ def crossover(args):
                    "active_experts": round(res["active_experts"], 2),
                    "down_bytes": int(res["down_bytes"]),
                    "kernels_us_per_step": kern}
-            if path == "dense" and "down_dense" in res["kernels"]:
+            if path.startswith("dense") and "down_dense" in res["kernels"]:
                 k = res["kernels"]["down_dense"]
                 ent["down_dense_tflops"] = round(res["flops_down_dense"] / (k["per_step_us"] * 1e-6) / 1e12, 2)
             if "gateup_swiglu" in res["kernels"]:
                 k = res["kernels"]["gateup_swiglu"]
                 ent["gateup_tflops"] = round(res["flops_gateup"] / (k["per_step_us"] * 1e-6) / 1e12, 2)
-            if path == "auto":   # the dispatcher's own choice, per routed / shared call
+            if path.startswith("auto"):   # the dispatcher's own choice, per routed / shared call
                 ent["routed"] = res["auto_path"]
                 if wl.desc_sh is not None:
                     ent["shared"] = "sparse" if wl.auto_path_sh == 0 else "dense"
@@ -834,6 +856,9 @@ def crossover(args):
             best = min(row["sparse"]["us_per_call"], row["dense"]["us_per_call"])
             if "auto" in row:
                 row["auto_vs_best"] = round(row["auto"]["us_per_call"] / best, 3)
+        if "dense" in row and "dense-pk" in row:
+            row["dense_pk_vs_dense"] = round(row["dense-pk"]["us_per_call"] /
+                                             row["dense"]["us_per_call"], 3)
         rows.append(row)
     print(json.dumps({"metric": "sparse-vs-dense crossover: MoE-layer us/call per forced path",
                       "layer": shape.name, "sparsity": args.sparsity,

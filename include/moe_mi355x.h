@@ -96,6 +96,11 @@ typedef struct {
                              MOE_ERR_UNSUPPORTED); moe_route and the packing calls
                              ignore it; a value outside moe_layout ->
                              MOE_ERR_INVALID_ARG                                   */
+  int32_t down_layout;    /* moe_layout of w_down: ROWMAJOR (zero) for every call;
+                             PACKED (moe_pack_down) is taken by moe_expert_ffn_dense
+                             only, bf16 only (the sparse calls gather W_d rows and
+                             refuse it with MOE_ERR_UNSUPPORTED, as the dense call
+                             does for fp32); outside moe_layout -> INVALID_ARG       */
 } moe_desc;
 
 /* Routing of a token batch, written by moe_route, read by the FFN calls.
@@ -287,6 +292,9 @@ moe_status moe_layer_sparse_noalloc(const moe_desc *d, int32_t T, int32_t k_keep
  * k_keep mask is applied to h in between, so the result equals
  * moe_expert_ffn_sparse's up to fp32 rounding order (bf16: h is rounded to
  * bf16 for the down GEMM).  k_keep == d_ff is the plain dense MoE.
+ * w_down: row-major, or (bf16, desc->down_layout = MOE_LAYOUT_PACKED) the
+ * copy moe_pack_down makes, which the down GEMM streams without staging
+ * the weights through LDS.
  * Parameters as moe_expert_ffn_sparse;
  * workspace: moe_ffn_workspace_size(d, T, k_keep, MOE_PATH_DENSE).
  */
@@ -340,6 +348,26 @@ moe_status moe_pack_gate_up(const moe_desc *d, const void *src_rowmajor, void *d
                             hipStream_t stream);
 moe_status moe_unpack_gate_up(const moe_desc *d, const void *src_packed, void *dst_rowmajor,
                               hipStream_t stream);
+
+/*
+ * moe_pack_down -- a copy of a bf16 down tensor [E, d_ff, H] in the layout
+ * moe_expert_ffn_dense reads with desc->down_layout = MOE_LAYOUT_PACKED: W_d
+ * transposed into MFMA operand fragments, so the dense down GEMM streams its
+ * weights as the gate/up GEMM does (page: technical summary, Methodology,
+ * the dense path at large batch).  For each expert e, column tile ct (16
+ * columns of H) and k-step ks (32 rows of d_ff), one contiguous 1 KB
+ * fragment holds W_d[e, 32 ks + 8 g + i, 16 ct + r] at element offset
+ * 8 (r + 16 g) + i, for r < 16, g < 4, i < 8; fragment index
+ * (e * H/16 + ct) * (d_ff/32) + ks.  The sparse calls need the row-major
+ * tensor (they read kept rows), so a caller using both paths keeps both
+ * copies.  Exact (bits are copied).  bf16 only (else MOE_ERR_UNSUPPORTED);
+ * src and dst must not overlap; both E * d_ff * H elements.
+ * moe_unpack_down is the inverse.
+ */
+moe_status moe_pack_down(const moe_desc *d, const void *src_rowmajor, void *dst_packed,
+                         hipStream_t stream);
+moe_status moe_unpack_down(const moe_desc *d, const void *src_packed, void *dst_rowmajor,
+                           hipStream_t stream);
 
 /*
  * moe_expert_ffn_sparse_threshold -- the sparse path with the page's literal

@@ -34,7 +34,7 @@ class MoeDesc(ctypes.Structure):
     _fields_ = [("hidden", ctypes.c_int32), ("n_experts", ctypes.c_int32),
                 ("d_ff", ctypes.c_int32), ("top_k", ctypes.c_int32),
                 ("norm_topk", ctypes.c_int32), ("dtype", ctypes.c_int32),
-                ("gate_up_layout", ctypes.c_int32)]
+                ("gate_up_layout", ctypes.c_int32), ("down_layout", ctypes.c_int32)]
 
 
 class MoeRouting(ctypes.Structure):
@@ -69,6 +69,8 @@ _SIGS = {
     "moe_calibrate_workspace_size": (_SZ, [_PD, _I32]),
     "moe_pack_gate_up": (_I32, [_PD, _V, _V, _V]),
     "moe_unpack_gate_up": (_I32, [_PD, _V, _V, _V]),
+    "moe_pack_down": (_I32, [_PD, _V, _V, _V]),
+    "moe_unpack_down": (_I32, [_PD, _V, _V, _V]),
     "moe_route_workspace_size": (_SZ, [_PD, _I32]),
     "moe_ffn_workspace_size": (_SZ, [_PD, _I32, _I32, _I32]),
     "moe_workspace_size": (_SZ, [_PD, _I32, _I32, _I32]),
@@ -118,14 +120,16 @@ def _check(status: int):
 
 
 def make_desc(hidden, n_experts, d_ff, top_k, norm_topk, dtype,
-              gate_up_layout="rowmajor") -> MoeDesc:
+              gate_up_layout="rowmajor", down_layout="rowmajor") -> MoeDesc:
     """moe_desc; gate_up_layout says how w_gate / w_up are passed to the FFN
-    calls ("packed" after moe_pack_gate_up; "rowmajor" ones are refused)."""
+    calls ("packed" after moe_pack_gate_up; "rowmajor" ones are refused);
+    down_layout how w_down is ("packed" after moe_pack_down: the dense bf16
+    call only)."""
     dt = {"f32": MOE_F32, "bf16": MOE_BF16, MOE_F32: MOE_F32, MOE_BF16: MOE_BF16}[dtype]
     lay = {"rowmajor": MOE_LAYOUT_ROWMAJOR, "packed": MOE_LAYOUT_PACKED,
            MOE_LAYOUT_ROWMAJOR: MOE_LAYOUT_ROWMAJOR, MOE_LAYOUT_PACKED: MOE_LAYOUT_PACKED}
     return MoeDesc(int(hidden), int(n_experts), int(d_ff), int(top_k), int(bool(norm_topk)), dt,
-                   lay.get(gate_up_layout, gate_up_layout))
+                   lay.get(gate_up_layout, gate_up_layout), lay.get(down_layout, down_layout))
 
 
 # ------------------------------------------------------------ tensor marshalling
@@ -347,6 +351,23 @@ def moe_unpack_gate_up(desc: MoeDesc, src, dst=None, stream=None):
     import torch
     dst = torch.empty_like(src) if dst is None else dst
     _check(lib().moe_unpack_gate_up(ctypes.byref(desc), _ptr(src), _ptr(dst), _stream(stream)))
+    return dst
+
+
+def moe_pack_down(desc: MoeDesc, src, dst=None, stream=None):
+    """Pack a row-major bf16 down tensor [E, d_ff, H] for the dense call
+    (desc.down_layout = packed); returns dst."""
+    import torch
+    dst = torch.empty_like(src) if dst is None else dst
+    _check(lib().moe_pack_down(ctypes.byref(desc), _ptr(src), _ptr(dst), _stream(stream)))
+    return dst
+
+
+def moe_unpack_down(desc: MoeDesc, src, dst=None, stream=None):
+    """Inverse of moe_pack_down; returns dst."""
+    import torch
+    dst = torch.empty_like(src) if dst is None else dst
+    _check(lib().moe_unpack_down(ctypes.byref(desc), _ptr(src), _ptr(dst), _stream(stream)))
     return dst
 
 

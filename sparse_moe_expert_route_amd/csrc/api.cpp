@@ -46,6 +46,8 @@ moe_status check_desc(const moe_desc *d) {
     return fail(MOE_ERR_INVALID_ARG, "norm_topk must be 0 or 1");
   if (d->gate_up_layout != MOE_LAYOUT_ROWMAJOR && d->gate_up_layout != MOE_LAYOUT_PACKED)
     return fail(MOE_ERR_INVALID_ARG, "gate_up_layout %d is not a moe_layout", d->gate_up_layout);
+  if (d->down_layout != MOE_LAYOUT_ROWMAJOR && d->down_layout != MOE_LAYOUT_PACKED)
+    return fail(MOE_ERR_INVALID_ARG, "down_layout %d is not a moe_layout", d->down_layout);
   if (d->hidden > MOE_MAX_HIDDEN || d->hidden % 64)
     return fail(MOE_ERR_UNSUPPORTED, "hidden %d: need a multiple of 64 up to %d", d->hidden,
                 MOE_MAX_HIDDEN);
@@ -178,6 +180,13 @@ moe_status run_ffn(RunMode mode, const moe_desc *d, int32_t T, int32_t k_keep, c
                 mode == kRunUpdown || mode == kRunUpdownThreshold || mode == kRunCalibrateGate
                     ? "" : " and w_up");
   const moe_path path = mode == kRunDense ? MOE_PATH_DENSE : MOE_PATH_SPARSE;
+  if (d->down_layout == MOE_LAYOUT_PACKED && mode != kRunCalibrate && mode != kRunCalibrateGate) {
+    if (path != MOE_PATH_DENSE)
+      return fail(MOE_ERR_UNSUPPORTED, "the sparse calls read kept rows of the row-major w_down: "
+                  "set desc->down_layout = MOE_LAYOUT_ROWMAJOR (moe_pack_down is for the dense call)");
+    if (d->dtype != MOE_BF16)
+      return fail(MOE_ERR_UNSUPPORTED, "a packed w_down is bf16 only");
+  }
   const bool thr = mode == kRunThreshold || mode == kRunUpdownThreshold;
   const bool cal = mode == kRunCalibrate || mode == kRunCalibrateGate;
   if (thr || cal) k_keep = d->d_ff;
@@ -239,6 +248,7 @@ moe_status run_ffn(RunMode mode, const moe_desc *d, int32_t T, int32_t k_keep, c
   a.top_k = d->top_k;
   a.k_keep = k_keep;
   a.bf16 = d->dtype == MOE_BF16;
+  a.down_packed = d->down_layout == MOE_LAYOUT_PACKED;
   a.implicit = routing == nullptr;
   a.accumulate = accumulate;
   a.x = x;
@@ -588,6 +598,31 @@ static moe_status pack_impl(const moe_desc *d, const void *src, void *dst, int u
 moe_status moe_pack_gate_up(const moe_desc *d, const void *src_rowmajor, void *dst_packed,
                             hipStream_t stream) {
   return pack_impl(d, src_rowmajor, dst_packed, 0, stream);
+}
+
+static moe_status pack_down_impl(const moe_desc *d, const void *src, void *dst, int unpack,
+                                 hipStream_t stream) {
+  g_err[0] = 0;
+  TRY(check_desc(d));
+  if (d->dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "a packed w_down is bf16 only");
+  if (!src || !dst) return fail(MOE_ERR_INVALID_ARG, "src and dst must be non-NULL");
+  if (!aligned16(src) || !aligned16(dst)) return fail(MOE_ERR_MISALIGNED, "src and dst must be 16-byte aligned");
+  const size_t bytes = (size_t)d->n_experts * d->d_ff * d->hidden * 2;
+  const char *s = static_cast<const char *>(src), *t = static_cast<const char *>(dst);
+  if (s < t + bytes && t < s + bytes) return fail(MOE_ERR_INVALID_ARG, "src and dst overlap");
+  const hipError_t e = moe::launch_pack_down(src, dst, d->n_experts, d->d_ff, d->hidden, unpack, stream);
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return MOE_OK;
+}
+
+moe_status moe_pack_down(const moe_desc *d, const void *src_rowmajor, void *dst_packed,
+                         hipStream_t stream) {
+  return pack_down_impl(d, src_rowmajor, dst_packed, 0, stream);
+}
+
+moe_status moe_unpack_down(const moe_desc *d, const void *src_packed, void *dst_rowmajor,
+                           hipStream_t stream) {
+  return pack_down_impl(d, src_packed, dst_rowmajor, 1, stream);
 }
 
 moe_status moe_unpack_gate_up(const moe_desc *d, const void *src_packed, void *dst_rowmajor,

@@ -207,6 +207,158 @@ __global__ __launch_bounds__(256, 2) void gateup_gemm_kernel(const void *__restr
   }
 }
 
+// ---------------------------------------------------------------- packed down GEMM
+// The dense path's down product when the caller passes W_d packed
+// (moe_pack_down): the gate/up GEMM's structure with W_d^T as the MFMA A
+// operand, so the weights stream straight from memory in fragment order and
+// no weight tile passes through LDS.  Work item = one expert and up to
+// 16 * MT of its tokens; block = 4 waves x NTW column tiles of 16 each;
+// blockIdx.z = one chunk of d_ff.  Per stage of two k-steps the block
+// stages the item's coefficient rows (masked, weighted h, bf16,
+// k-contiguous) into a double-buffered LDS tile, read one tile ahead of the
+// MFMAs as in the gate/up GEMM; each wave streams its own W_d fragments
+// DEPTH stages ahead through a ring of DEPTH + 1 register sets (the set a
+// stage's MFMAs read is never a load target meanwhile).  Items of 128
+// tokens are bound by the matrix work and keep one stage in flight (their
+// accumulators fill the registers); items of 32 or 64 tokens stream W_d at
+// a few flops per byte, where two stages in flight keep more bytes moving.
+// Epilogue: 4 consecutive columns per lane, one 16-byte store per token.
+template <int NTW, int MT, int DEPTH>
+__global__ __launch_bounds__(256, 2) void down_packed_kernel(const uint8_t *__restrict__ wdp,
+                                                             const uint16_t *__restrict__ hm,
+                                                             RouteView rv, int H, int d_ff,
+                                                             int kchunk,
+                                                             float *__restrict__ partial) {
+  constexpr int TOK = 16 * MT;       // tokens per item
+  constexpr int SR = MT / 2;         // staged 16-byte chunks per thread (rows tid / 8 + 32 i)
+  // W_d register sets: one stage in flight goes to a temporary set that
+  // replaces the current one after its MFMAs (the compiler renames it, and
+  // a two-set ring unrolled by two spilled at 128 tokens x 64 columns)
+  constexpr int R = DEPTH == 1 ? 1 : DEPTH + 1;
+  __shared__ __attribute__((aligned(16))) uint8_t xs[2][TOK * kGemmRowB];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  int e, q0, ntok;
+  const unsigned qb = xcd_logical_block();
+  const int bx = (int)(qb % gridDim.x), by = (int)(qb / gridDim.x % gridDim.y);
+  if (!find_item<TOK>(rv, bx, e, q0, ntok)) return;  // block-uniform
+  const int S = gridDim.z, sidx = (int)(qb / (gridDim.x * gridDim.y));
+  const int ntiles = (ntok + 15) >> 4;
+  const int k0 = sidx * kchunk;                                  // a multiple of 64
+  const int nit = max(0, (min(d_ff, k0 + kchunk) - k0) / 64);    // stages of two k-steps
+
+  // staging map: coefficient rows tid / 8 + 32 i (i < SR), 16-byte chunk
+  // tid % 8; rows past the item's tokens stage the first token's row (they
+  // only feed accumulator columns that are never stored)
+  const int srow = tid >> 3, schunk = tid & 7;
+  const uint8_t *xrow[SR];
+#pragma unroll
+  for (int i = 0; i < SR; ++i) {
+    const int c = srow + 32 * i;
+    xrow[i] = reinterpret_cast<const uint8_t *>(
+                  hm + (size_t)rv.pair_at(q0 + (c < ntok ? c : 0)) * d_ff + k0) + schunk * 16;
+  }
+  const int nt = (by * 4 + wid) * NTW;             // this wave's first column tile
+  const size_t tstride = (size_t)(d_ff / 32) * 1024;  // bytes of one column tile
+  const uint8_t *wa = wdp + ((size_t)e * (H / 16) + nt) * tstride + (size_t)(k0 / 32) * 1024 + lane * 16;
+
+  f32x4 acc[NTW][MT];
+#pragma unroll
+  for (int j = 0; j < NTW; ++j)
+#pragma unroll
+    for (int tl = 0; tl < MT; ++tl) acc[j][tl] = f32x4{0, 0, 0, 0};
+
+  u32x4 stg[SR], aw[R][NTW][2];
+  auto load_w = [&](int it, u32x4 (&dst)[NTW][2]) {
+#pragma unroll
+    for (int j = 0; j < NTW; ++j)
+#pragma unroll
+      for (int k = 0; k < 2; ++k) dst[j][k] = ld16_nt(wa + j * tstride + (size_t)(2 * it + k) * 1024);
+  };
+  if (nit > 0) {
+#pragma unroll
+    for (int i = 0; i < SR; ++i) stg[i] = ld16(xrow[i]);
+#pragma unroll
+    for (int i = 0; i < SR; ++i)
+      *reinterpret_cast<u32x4 *>(&xs[0][(srow + 32 * i) * kGemmRowB + schunk * 16]) = stg[i];
+    load_w(0, aw[0]);
+    if (DEPTH > 1 && nit > 1) load_w(1, aw[1]);
+  }
+  __syncthreads();
+
+  const int r = lane & 15, g = lane >> 4;
+  // Step it reads W_d set SL = it % R; STEADY: stage it + DEPTH exists (so
+  // every load is issued unconditionally and the compiler's waits count
+  // the loads in flight instead of draining them)
+  auto step = [&](int it, auto slc, auto steadyc) {
+    constexpr int SL = decltype(slc)::value;
+    constexpr bool STEADY = decltype(steadyc)::value;
+    const int cur = it & 1;
+    const bool more = STEADY || it + 1 < nit;
+    if (more) {
+#pragma unroll
+      for (int i = 0; i < SR; ++i) stg[i] = ld16(xrow[i] + (size_t)(it + 1) * 128);
+    }
+    u32x4 nw[NTW][2];
+    if (STEADY || it + DEPTH < nit) load_w(it + DEPTH, DEPTH == 1 ? nw : aw[(SL + DEPTH) % R]);
+    auto bfrag = [&](int k, int tl) {
+      return *reinterpret_cast<const u32x4 *>(&xs[cur][(tl * 16 + r) * kGemmRowB + k * 64 + g * 16]);
+    };
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      u32x4 b = bfrag(k, 0);
+#pragma unroll
+      for (int tl = 0; tl < MT; ++tl) {
+        if (tl < ntiles) {  // block-uniform
+          const u32x4 bn = bfrag(k, tl < MT - 1 ? tl + 1 : MT - 1);
+#pragma unroll
+          for (int j = 0; j < NTW; ++j) acc[j][tl] = mfma_bf16(aw[SL][j][k], b, acc[j][tl]);
+          b = bn;
+        }
+      }
+    }
+    if (more) {
+#pragma unroll
+      for (int i = 0; i < SR; ++i)
+        *reinterpret_cast<u32x4 *>(&xs[cur ^ 1][(srow + 32 * i) * kGemmRowB + schunk * 16]) = stg[i];
+      if (DEPTH == 1) {
+#pragma unroll
+        for (int j = 0; j < NTW; ++j) { aw[0][j][0] = nw[j][0]; aw[0][j][1] = nw[j][1]; }
+      }
+    }
+    __syncthreads();
+  };
+  int it = 0;
+  for (; it + R - 1 + DEPTH < nit; it += R) {
+    step(it, SkIc<0>{}, SkIc<1>{});
+    if (R > 1) step(it + 1, SkIc<1 % R>{}, SkIc<1>{});
+    if (R > 2) step(it + 2, SkIc<2 % R>{}, SkIc<1>{});
+  }
+  for (; it < nit; it += R) {
+    step(it, SkIc<0>{}, SkIc<0>{});
+    if (R > 1 && it + 1 < nit) step(it + 1, SkIc<1 % R>{}, SkIc<0>{});
+    if (R > 2 && it + 2 < nit) step(it + 2, SkIc<2 % R>{}, SkIc<0>{});
+  }
+
+  // D: lane holds token column r of each token tile, output columns 4 g ..
+  // 4 g + 3 of each column tile; the pair ids are all read before the stores
+  int prow[MT];
+#pragma unroll
+  for (int tl = 0; tl < MT; ++tl) {
+    const int c = tl * 16 + r;
+    prow[tl] = rv.pair_at(q0 + (c < ntok ? c : 0));
+  }
+#pragma unroll
+  for (int j = 0; j < NTW; ++j) {
+    const int col = (nt + j) * 16 + 4 * g;
+#pragma unroll
+    for (int tl = 0; tl < MT; ++tl) {
+      const int c = tl * 16 + r;
+      if (tl < ntiles && c < ntok)
+        *reinterpret_cast<f32x4 *>(partial + ((size_t)prow[tl] * S + sidx) * H + col) = acc[j][tl];
+    }
+  }
+}
+
 // ---------------------------------------------------------------- skinny down GEMM
 // The down product for items of at most 16 * MT tokens of one expert (a few
 // tokens per expert: HBM-bound on W_d).  Block = 4 waves x 256 output
@@ -1037,7 +1189,89 @@ hipError_t launch_down_union(const FfnArgs &a, const RouteView &rv, hipStream_t 
   return hipGetLastError();
 }
 
+#ifndef MOE_PACKED_NTW_MAX
+#define MOE_PACKED_NTW_MAX 4
+#endif
+// The dense down GEMM over a packed W_d.  Item size: 32, 64 or 128 tokens,
+// the skinny GEMM's token tiles (routed experts: 2 or 4 tiles up to 16 or
+// 40 tokens per expert on average, so the busiest expert still fits one
+// item; always-on experts: T <= 32, <= 64); 64-token items at 64 tokens
+// per expert split the busier experts in two and read their W_d twice (381
+// us against 268 us with 128-token items on the 1024-token Llama-4-like
+// routed experts).  16 * NTW columns per wave, NTW the largest of 4, 2, 1
+// that divides H / 64.  K chunks S:
+//  - always-on experts of 128-token items (the matrix-bound shape, item
+//    counts exact): the grid runs in rounds of `slots` resident blocks (2,
+//    3 or 4 per CU as NTW = 4, 2, 1 allow: registers, LDS) and each block
+//    takes kc / 64 stages, so S minimises rounds x stages (the smallest
+//    such S, which also writes the fewest partial rows).  A partial last
+//    round costs a whole one: on the 1024-token Llama-4-like shared expert,
+//    640 blocks (1.25 rounds of 32 stages) took 139.5 us, 480 blocks (one
+//    round of 43 stages) 103.2 us.
+//  - otherwise (streaming W_d at a few flops per byte): ~1024 blocks to keep
+//    bytes in flight (~2048 for a lone always-on item of <= 64 tokens);
+//    fewer lost (24 x 20 x 1 blocks: 296 us against 268 us at S = 3 on the
+//    routed experts of the same layer at 1024 tokens), and so did more,
+//    whose partial rows cost more than they gained (routed experts at 16
+//    tokens each: 251.5 us at S = 5 against 237.1 us at S = 3).
+// Chunks are >= 256 rows and a multiple of 64, P * S within
+// dense_down_partial_rows.
+static hipError_t launch_down_packed(const FfnArgs &a, const RouteView &rv, hipStream_t stream) {
+  const int ntw = (a.H % 256 == 0 && MOE_PACKED_NTW_MAX >= 4) ? 4
+                  : (a.H % 128 == 0 && MOE_PACKED_NTW_MAX >= 2) ? 2 : 1;
+  const size_t P = (size_t)a.T * a.top_k;
+  const int skt = skinny_tiles(a.T, a.E, a.top_k, a.implicit);
+  const int mt = skt > 0 ? skt : 8;
+  const int items = n_items(a, 16 * mt);
+  const long base = (long)items * (a.H / (64 * ntw));
+  long smax = a.d_ff / 256 > 0 ? a.d_ff / 256 : 1;
+  const long bound = (long)(dense_down_partial_rows(a.T, a.E, a.top_k, a.H) / P);
+  if (smax > bound) smax = bound;
+  auto chunk = [&](long S) { return (int)((a.d_ff + S - 1) / S + 63) / 64 * 64; };
+  int kc;
+  if (a.implicit && mt == 8) {
+    const long slots = 256L * (ntw == 4 ? 2 : ntw == 2 ? 3 : 4);
+    long best = -1;
+    kc = a.d_ff;
+    for (long S = 1; S <= smax; ++S) {
+      const int k = chunk(S);
+      const long n = (a.d_ff + k - 1) / k;
+      const long est = (base * n + slots - 1) / slots * (k / 64);
+      if (best < 0 || est < best) { best = est; kc = k; }
+    }
+  } else {
+    const long target = a.implicit && mt < 8 ? 2048 : 1024;
+    long S = (target + base - 1) / base;
+    if (S > smax) S = smax;
+    if (S > 16) S = 16;
+    kc = chunk(S < 1 ? 1 : S);
+  }
+  const int Sc = (a.d_ff + kc - 1) / kc;
+  if (P * Sc > dense_down_partial_rows(a.T, a.E, a.top_k, a.H)) return hipErrorInvalidValue;
+  const uint8_t *wdp = static_cast<const uint8_t *>(a.w_down);
+  const uint16_t *hm = static_cast<const uint16_t *>(a.hm);
+  dim3 grid(items, a.H / (64 * ntw), Sc);
+  timer_begin(kStageDownDense, stream);
+#define MOE_PK(N, M, D) \
+  down_packed_kernel<N, M, D><<<grid, 256, 0, stream>>>(wdp, hm, rv, a.H, a.d_ff, kc, a.partial)
+  if (mt == 8) {
+    if (ntw == 4) MOE_PK(4, 8, 1); else if (ntw == 2) MOE_PK(2, 8, 1); else MOE_PK(1, 8, 1);
+  } else if (mt == 4) {
+    if (ntw == 4) MOE_PK(4, 4, 2); else if (ntw == 2) MOE_PK(2, 4, 2); else MOE_PK(1, 4, 2);
+  } else {
+    if (ntw == 4) MOE_PK(4, 2, 2); else if (ntw == 2) MOE_PK(2, 2, 2); else MOE_PK(1, 2, 2);
+  }
+#undef MOE_PK
+  timer_end(stream);
+  dim3 cgrid(a.T, (a.H + 255) / 256);
+  timer_begin(kStageCombine, stream);
+  combine_kernel<true><<<cgrid, 64, 0, stream>>>(a.partial, a.H, a.top_k, Sc, a.accumulate, a.y);
+  timer_end(stream);
+  return hipGetLastError();
+}
+
 hipError_t launch_down_dense(const FfnArgs &a, const RouteView &rv, hipStream_t stream) {
+  if (a.down_packed) return launch_down_packed(a, rv, stream);
   const int mt = skinny_tiles(a.T, a.E, a.top_k, a.implicit);
   const size_t P = (size_t)a.T * a.top_k;
   const uint16_t *wd = static_cast<const uint16_t *>(a.w_down);

@@ -2092,9 +2092,11 @@ hipError_t launch_calibrate(const FfnArgs &a, double sparsity, float *tau, float
 // A row block holds one token, so a token's rows must also stay within one
 // LDS stage: past that, T x H / 64 blocks stream too many bytes each (a
 // single token's 8192 rows took 1.4-2x the GEMM route's time on 32 and 80
-// blocks; 3072 rows on 80 blocks saved 30 % of the down stage).
+// blocks; 3072 rows on 80 blocks saved 30 % of the down stage).  The row
+// kernel reads row-major W_d, so a packed W_d always takes the GEMM.
 static bool dense_rows_ok(const FfnArgs &a) {
-  if (!a.bf16 || a.k_keep != a.d_ff || (long)a.top_k * a.d_ff > kDownStage) return false;
+  if (!a.bf16 || a.down_packed || a.k_keep != a.d_ff || (long)a.top_k * a.d_ff > kDownStage)
+    return false;
   double n_e = a.T;
   if (!a.implicit) {
     const double E = a.E, K = a.top_k;

@@ -70,6 +70,7 @@ int launch_router_logits(const RouteArgs &a, hipStream_t stream);
 // One FFN call (routed group, or an implicit shared group).
 struct FfnArgs {
   int T, H, E, d_ff, top_k, k_keep, bf16, implicit, accumulate;
+  int down_packed = 0;  // dense path: w_down in the moe_pack_down layout
   const void *x, *w_gate, *w_up, *w_down;
   // routing (ignored when implicit)
   const int32_t *topk_ids;
@@ -152,6 +153,8 @@ hipError_t launch_stream_read(const void *src, size_t bytes, uint32_t *sink, int
                               hipStream_t stream);
 hipError_t launch_pack_gate_up(const void *src, void *dst, int E, int d_ff, int H, int bf16,
                                int unpack, hipStream_t stream);
+hipError_t launch_pack_down(const void *src, void *dst, int E, int d_ff, int H, int unpack,
+                            hipStream_t stream);
 
 // Rows of the dense-path down GEMM's partial buffer for calls of at most T tokens.
 size_t dense_down_partial_rows(int T, int E, int top_k, int H);

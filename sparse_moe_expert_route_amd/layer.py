@@ -18,23 +18,37 @@ class MoELayer:
     def __init__(self, *, hidden: int, n_experts: int, d_ff: int, top_k: int, norm_topk: bool,
                  dtype: str, w_router, w_gate, w_up, w_down, bias=None,
                  shared: Optional[Sequence] = None, d_ff_shared: Optional[int] = None,
-                 packed: bool = False):
+                 packed: bool = False, pack_down: bool = False):
         """Weights are device tensors [E, d_ff, H] (router [E, H]).  Gate and
         up are packed here with moe_pack_gate_up unless `packed` says the
-        caller already did."""
+        caller already did.  pack_down (bf16): also keep a copy of each W_d
+        packed by moe_pack_down, which the dense path then reads (the sparse
+        path reads the row-major one)."""
         self.desc = B.make_desc(hidden, n_experts, d_ff, top_k, norm_topk, dtype,
                                 gate_up_layout="packed")
         self.w_router, self.bias = w_router, bias
         pk = (lambda d, w: w) if packed else B.moe_pack_gate_up
         self.w = (pk(self.desc, w_gate), pk(self.desc, w_up), w_down)
+        pack_down = pack_down and dtype == "bf16"
+        self.dense = (self.desc, self.w)   # descriptor and weights of the dense calls
+        if pack_down:
+            dd = B.make_desc(hidden, n_experts, d_ff, top_k, norm_topk, dtype,
+                             gate_up_layout="packed", down_layout="packed")
+            self.dense = (dd, (self.w[0], self.w[1], B.moe_pack_down(dd, w_down)))
         self.shared = None
         self.desc_shared = None
         if shared is not None:
             g, u, dn = shared
             n_sh = g.shape[0]
-            self.desc_shared = B.make_desc(hidden, n_sh, d_ff_shared or g.shape[1], n_sh, False, dtype,
+            d_sh = d_ff_shared or g.shape[1]
+            self.desc_shared = B.make_desc(hidden, n_sh, d_sh, n_sh, False, dtype,
                                            gate_up_layout="packed")
             self.shared = (pk(self.desc_shared, g), pk(self.desc_shared, u), dn)
+            self.dense_shared = (self.desc_shared, self.shared)
+            if pack_down:
+                ds = B.make_desc(hidden, n_sh, d_sh, n_sh, False, dtype, gate_up_layout="packed",
+                                 down_layout="packed")
+                self.dense_shared = (ds, (self.shared[0], self.shared[1], B.moe_pack_down(ds, dn)))
         self._ws = {}
 
     def _workspace(self, key, nbytes: int, device):
@@ -73,12 +87,16 @@ class MoELayer:
             routing = self.route(x, routing)
             ws = self._workspace(("ffn", path), B.moe_ffn_workspace_size(d, T, k_keep, path),
                                  x.device)
-            B.moe_expert_ffn_dense(d, T, k_keep, x, *self.w, routing, y, 0, active_idx, ws)
+            dd, wd = self.dense
+            B.moe_expert_ffn_dense(dd, T, k_keep, x, *wd, routing, y, 0, active_idx, ws)
         if self.shared is not None:
             ds = self.desc_shared
             ks = ds.d_ff if k_keep_shared is None else k_keep_shared
             ps = self.select_path(T, ks, shared=True) if path_shared is None else path_shared
-            fs = B.moe_expert_ffn_sparse if ps == B.MOE_PATH_SPARSE else B.moe_expert_ffn_dense
             wss = self._workspace(("shared", ps), B.moe_ffn_workspace_size(ds, T, ks, ps), x.device)
-            fs(ds, T, ks, x, *self.shared, None, y, 1, None, wss)
+            if ps == B.MOE_PATH_SPARSE:
+                B.moe_expert_ffn_sparse(ds, T, ks, x, *self.shared, None, y, 1, None, wss)
+            else:
+                dd, wd = self.dense_shared
+                B.moe_expert_ffn_dense(dd, T, ks, x, *wd, None, y, 1, None, wss)
         return y

@@ -77,6 +77,22 @@ class DeviceLayer:
                          pk_up(self.desc_sh, to_dev(u)), to_dev(d))
         torch.cuda.synchronize()
 
+    def packed_down(self):
+        """Descriptors with down_layout = packed and W_d copies packed by
+        moe_pack_down (routed, shared or None), made on first use."""
+        if getattr(self, "_pd", None) is None:
+            sh = self.inp.shape
+            d = B.make_desc(sh.hidden, sh.n_experts, sh.d_ff, sh.top_k, sh.norm_topk, sh.dtype,
+                            gate_up_layout="packed", down_layout="packed")
+            pd = [d, B.moe_pack_down(d, self.w[2]), None, None]
+            if self.desc_sh is not None:
+                ds = B.make_desc(sh.hidden, sh.n_shared, sh.d_ff_shared, sh.n_shared, False,
+                                 sh.dtype, gate_up_layout="packed", down_layout="packed")
+                pd[2:] = [ds, B.moe_pack_down(ds, self.w_sh[2])]
+            torch.cuda.synchronize()
+            self._pd = tuple(pd)
+        return self._pd
+
     def _fn(self, path):
         if self.score == "gate":
             assert path == B.MOE_PATH_SPARSE, "the gate-score split has no dense form"
@@ -84,8 +100,9 @@ class DeviceLayer:
         return B.moe_expert_ffn_sparse if path == B.MOE_PATH_SPARSE else B.moe_expert_ffn_dense
 
     def run(self, x_host: np.ndarray, k: int, path: int, k_sh=None, path_sh=None,
-            poison_rows=None, poison_up=None):
-        """One layer call; returns host copies of routing, masks and y."""
+            poison_rows=None, poison_up=None, packed_down=False):
+        """One layer call; returns host copies of routing, masks and y.
+        packed_down: the dense calls take W_d packed by moe_pack_down."""
         sh = self.inp.shape
         T = x_host.shape[0]
         x = to_dev(x_host)
@@ -98,7 +115,10 @@ class DeviceLayer:
         fn = self._fn(path)
         wd = self.w[2] if poison_rows is None else poison_rows
         wu = self.w[1] if poison_up is None else poison_up
-        fn(self.desc, T, k, x, self.w[0], wu, wd, R, y, 0, idx if k > 0 else None, ws)
+        desc = self.desc
+        if packed_down and path == B.MOE_PATH_DENSE:
+            desc, wd = self.packed_down()[:2]
+        fn(desc, T, k, x, self.w[0], wu, wd, R, y, 0, idx if k > 0 else None, ws)
         out = dict(T=T, k=k)
         idx_sh = None
         if self.desc_sh is not None:
@@ -108,7 +128,11 @@ class DeviceLayer:
             idx_sh = torch.full((max(1, T * ds.top_k), max(1, k_sh)), -1, dtype=torch.int32, device="cuda")
             ws2 = torch.empty(B.moe_ffn_workspace_size(ds, T, k_sh, path_sh), dtype=torch.uint8, device="cuda")
             fs = self._fn(path_sh)
-            fs(ds, T, k_sh, x, *self.w_sh, None, y, 1, idx_sh if k_sh > 0 else None, ws2)
+            wsh = self.w_sh
+            if packed_down and path_sh == B.MOE_PATH_DENSE:
+                ds, wd_sh = self.packed_down()[2:]
+                wsh = (wsh[0], wsh[1], wd_sh)
+            fs(ds, T, k_sh, x, *wsh, None, y, 1, idx_sh if k_sh > 0 else None, ws2)
             out["k_sh"] = k_sh
         torch.cuda.synchronize()
         out.update(ids=R.topk_ids.cpu().numpy()[:T], w=R.topk_w.cpu().numpy()[:T],
@@ -220,6 +244,16 @@ def pack_reference(w: np.ndarray, dtype: str) -> np.ndarray:
     q = KS // 4
     v = w.reshape(E, d // 16, 16, H // KS, 4, q)          # e, nt, r, ks, group, c%q
     v = v.transpose(0, 1, 3, 4, 2, 5)                      # e, nt, ks, group, r, c%q
+    return np.ascontiguousarray(v).reshape(E, d, H)
+
+
+def pack_down_reference(w: np.ndarray) -> np.ndarray:
+    """numpy statement of the packed down layout (the header's formula):
+    fragment (e, ct, ks) holds W_d[e, 32 ks + 8 g + i, 16 ct + r] at element
+    8 (r + 16 g) + i."""
+    E, d, H = w.shape
+    v = w.reshape(E, d // 32, 4, 8, H // 16, 16)           # e, ks, g, i, ct, r
+    v = v.transpose(0, 4, 1, 2, 5, 3)                      # e, ct, ks, g, r, i
     return np.ascontiguousarray(v).reshape(E, d, H)
 
 

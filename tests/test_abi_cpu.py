@@ -145,6 +145,37 @@ def test_rowmajor_refused_by_the_other_ffn_calls():
     assert _route(d, 4, wsb=0) == WSP
 
 
+def test_packed_down_only_on_the_dense_bf16_call():
+    # moe_pack_down's layout is read by the dense bf16 down GEMM alone; the
+    # sparse calls gather row-major W_d rows and refuse it before any launch
+    d = _desc(down_layout="packed")
+    for name in ("moe_expert_ffn_sparse", "moe_expert_ffn_sparse_updown"):
+        assert _ffn(getattr(L, name), d, 4, 10) == UNS, name
+        assert "moe_pack_down" in B.moe_last_error()
+    r = B.MoeRouting(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    assert L.moe_layer_sparse(ctypes.byref(d), 4, 10, FAKE, FAKE, None, FAKE, FAKE, FAKE,
+                              ctypes.byref(r), FAKE, 0, None, None, None, FAKE, 1 << 34, None) == UNS
+    for name in ("moe_expert_ffn_sparse_threshold", "moe_expert_ffn_sparse_updown_threshold"):
+        assert getattr(L, name)(ctypes.byref(d), 4, FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.byref(r),
+                                FAKE, 0, None, None, FAKE, 1 << 34, None) == UNS
+    assert _ffn(L.moe_expert_ffn_dense, _desc(down_layout="packed", dtype="f32"), 4, 10) == UNS
+    assert _ffn(L.moe_expert_ffn_dense, _desc(down_layout=7), 4, 10) == INV
+    # the dense bf16 call validates on (fake pointers: stops at the workspace)
+    assert _ffn(L.moe_expert_ffn_dense, d, 4, 10, wsb=0) == WSP
+    # calibration reads no W_d: the packed descriptor is fine there
+    assert L.moe_calibrate_thresholds(ctypes.byref(d), 4, FAKE, FAKE, FAKE, ctypes.byref(r), 0.9,
+                                      FAKE, FAKE, 0, None) == WSP
+
+
+def test_pack_down_validation():
+    d = _desc(down_layout="packed")
+    assert L.moe_pack_down(ctypes.byref(_desc(dtype="f32")), FAKE, FAKE + (1 << 32), None) == UNS
+    assert L.moe_pack_down(ctypes.byref(d), FAKE, FAKE + 64, None) == INV       # overlap
+    assert L.moe_unpack_down(ctypes.byref(d), FAKE, None, None) == INV
+    assert L.moe_pack_down(ctypes.byref(d), MIS, FAKE + (1 << 32), None) == MISA
+    assert L.moe_pack_down(None, FAKE, FAKE + (1 << 32), None) == INV
+
+
 def _route(d, T, x=FAKE, w=FAKE, bias=None, out="ok", ws=FAKE, wsb=1 << 30):
     r = B.MoeRouting(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE) if out == "ok" else out
     return L.moe_route(ctypes.byref(d) if d is not None else None, T, x, w, bias,
