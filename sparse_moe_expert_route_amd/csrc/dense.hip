@@ -217,11 +217,13 @@ __global__ __launch_bounds__(256, 2) void gateup_gemm_kernel(const void *__restr
 // stages the item's coefficient rows (masked, weighted h, bf16,
 // k-contiguous) into a double-buffered LDS tile, read one tile ahead of the
 // MFMAs as in the gate/up GEMM; each wave streams its own W_d fragments
-// DEPTH stages ahead through a ring of DEPTH + 1 register sets (the set a
-// stage's MFMAs read is never a load target meanwhile).  Items of 128
-// tokens are bound by the matrix work and keep one stage in flight (their
-// accumulators fill the registers); items of 32 or 64 tokens stream W_d at
-// a few flops per byte, where two stages in flight keep more bytes moving.
+// DEPTH stages ahead: DEPTH = 2 through a ring of 3 register sets (the set
+// a stage's MFMAs read is never a load target meanwhile), DEPTH = 1 into a
+// temporary set that replaces the current one after the stage's MFMAs.
+// Items of 128 tokens are bound by the matrix work and keep one stage in
+// flight (their accumulators fill the registers); items of 32 or 64 tokens
+// stream W_d at a few flops per byte, where two stages in flight keep more
+// bytes moving.
 // Epilogue: 4 consecutive columns per lane, one 16-byte store per token.
 template <int NTW, int MT, int DEPTH>
 __global__ __launch_bounds__(256, 2) void down_packed_kernel(const uint8_t *__restrict__ wdp,
@@ -231,9 +233,9 @@ __global__ __launch_bounds__(256, 2) void down_packed_kernel(const uint8_t *__re
                                                              float *__restrict__ partial) {
   constexpr int TOK = 16 * MT;       // tokens per item
   constexpr int SR = MT / 2;         // staged 16-byte chunks per thread (rows tid / 8 + 32 i)
-  // W_d register sets: one stage in flight goes to a temporary set that
-  // replaces the current one after its MFMAs (the compiler renames it, and
-  // a two-set ring unrolled by two spilled at 128 tokens x 64 columns)
+  // W_d register sets (DEPTH = 1: a two-set ring unrolled by two spilled
+  // at 128 tokens x 64 columns, or, with the loads held at the stage's top,
+  // ran slower; the temporary set is renamed by the compiler instead)
   constexpr int R = DEPTH == 1 ? 1 : DEPTH + 1;
   __shared__ __attribute__((aligned(16))) uint8_t xs[2][TOK * kGemmRowB];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
