@@ -1667,6 +1667,12 @@ static void launch_mask(const FfnArgs &a, const RouteView &rv, int32_t *idx, flo
 // staged token tiles only pay off once experts hold many tokens (measured
 // on four layer families at T = 32 and 64: 13-22 % faster layers where
 // experts hold 1-4 tokens, equal on the OLMoE-like layer at T = 64).
+// Always-on (implicit) experts past 16 tokens hold every token, so 16-token
+// items stream each expert's weights T / 16 times: bf16 calls take the
+// grouped GEMM there, which reads them once per 128 tokens, where its grid
+// still has >= 128 blocks (Llama-4-like shared expert, d_ff 8192, T = 64:
+// 122.8 -> 61.4 us; DeepSeek-V2-like, two of d_ff 1536, 48 GEMM blocks:
+// 27.9 us on 16-token items against 60.0 on the GEMM at T = 32).
 // gate_only: the page's own split, h <- silu(W_g x) (the scores), up skipped.
 #ifndef MOE_SWIGLU_MAX_T
 #define MOE_SWIGLU_MAX_T 64
@@ -1674,7 +1680,9 @@ static void launch_mask(const FfnArgs &a, const RouteView &rv, int32_t *idx, flo
 static void launch_gateup(const FfnArgs &a, const RouteView &rv, hipStream_t stream,
                           bool gate_only = false) {
   timer_begin(kStageGateup, stream);
-  if (a.T <= MOE_SWIGLU_MAX_T) {
+  const bool shared_gemm = a.implicit && a.bf16 && a.T > 16 &&
+                           (long)n_items(a, 128) * (a.d_ff / 64) >= 128;
+  if (a.T <= MOE_SWIGLU_MAX_T && !shared_gemm) {
     // T <= 16: an item is an active-expert slot, at most min(E, P) of them;
     // past that an item is an expert and up to 16 of its tokens
     const int P = a.T * a.top_k;
