@@ -322,8 +322,13 @@ static void launch_select(const RouteArgs &a, int nsplit, hipStream_t stream) {
 // matrix over many CUs (64 at decode batches; past one tile of tokens, two
 // rounds of the chip's 256 CUs, since each block's K loop is a serial
 // latency chain), at least 4 k-steps per split, at most kRouterSplits.
+// Tokens per logits block: 64 past one 16-token tile, except with at most
+// two 16-expert tiles, where 64-token blocks leave too few blocks (the
+// Llama-4-like router, 16 experts: 8 blocks at T = 64, 14.7 us).
+static int router_token_group(int T, int E) { return T <= 16 || E <= 32 ? 16 : 64; }
+
 int router_splits(int T, int H, int E, int bf16) {
-  const int tg = T <= 16 ? 16 : 64;
+  const int tg = router_token_group(T, E);
   const int blocks = ((E + 15) / 16) * ((T + tg - 1) / tg);
   const int nsteps = H / (bf16 ? 32 : 16);
   const int target = T <= 16 ? 64 : 512;
@@ -334,7 +339,7 @@ int router_splits(int T, int H, int E, int bf16) {
 }
 
 int launch_router_logits(const RouteArgs &a, hipStream_t stream) {
-  const bool one = a.T <= 16;
+  const bool one = router_token_group(a.T, a.E) == 16;
   const int nsplit = router_splits(a.T, a.H, a.E, a.bf16);
   dim3 g1((a.E + 15) / 16, (a.T + (one ? 16 : 64) - 1) / (one ? 16 : 64), nsplit);
   timer_begin(kStageLogits, stream);
