@@ -318,15 +318,15 @@ static void launch_select(const RouteArgs &a, int nsplit, hipStream_t stream) {
   else launch_select_ro<V, false>(a, nsplit, stream);
 }
 
-// Split-K factor of the router GEMM: enough blocks to spread the router
-// matrix over many CUs (64 at decode batches; past one tile of tokens, two
-// rounds of the chip's 256 CUs, since each block's K loop is a serial
-// latency chain), at least 4 k-steps per split, at most kRouterSplits.
 // Tokens per logits block: 64 past one 16-token tile, except with at most
 // two 16-expert tiles, where 64-token blocks leave too few blocks (the
 // Llama-4-like router, 16 experts: 8 blocks at T = 64, 14.7 us).
 static int router_token_group(int T, int E) { return T <= 16 || E <= 32 ? 16 : 64; }
 
+// Split-K factor of the router GEMM: enough blocks to spread the router
+// matrix over many CUs (64 at decode batches; past one tile of tokens, two
+// rounds of the chip's 256 CUs, since each block's K loop is a serial
+// latency chain), at least 4 k-steps per split, at most kRouterSplits.
 int router_splits(int T, int H, int E, int bf16) {
   const int tg = router_token_group(T, E);
   const int blocks = ((E + 15) / 16) * ((T + tg - 1) / tg);
