@@ -127,7 +127,8 @@ UPDOWN = [("tiny-f32", 4, 0.9, None), ("tiny-f32", 4, 0.0, None), ("olmoe-like",
           ("olmoe-like", 4, 0.9, None), ("olmoe-like", 16, 0.9, None), ("olmoe-like", 16, 0.5, None),
           ("qwen3-moe-like", 4, 0.9, None), ("qwen3-moe-like", 32, 0.9, None),
           ("deepseek-v2-like", 1, 0.9, 0.5), ("deepseek-v2-like", 8, 0.9, 0.0),
-          ("llama4-like", 1, 0.9, 0.9), ("llama4-like", 64, 0.9, 0.9)]
+          ("llama4-like", 1, 0.9, 0.9), ("llama4-like", 64, 0.9, 0.9),
+          ("llama4-like", 256, 0.9, 0.9)]   # shared gate scores on the GEMM's weight ring
 
 
 @pytest.mark.parametrize("name,T,s,s_sh", UPDOWN)
