@@ -115,6 +115,13 @@ def test_deepseek_v2_like_dense():
     run_case("deepseek-v2-like", 32, 0.9, DN, s_sh=0.5, path_sh=DN)
 
 
+@pytest.mark.parametrize("path", [SP, DN])
+def test_deepseek_v2_like_large_batch(path):
+    # 256 tokens: the two shared experts' gate/up on the grouped GEMM with
+    # its weight ring (96 blocks), routed experts at ~10 tokens each
+    run_case("deepseek-v2-like", 256, 0.9, path, s_sh=0.5, path_sh=DN)
+
+
 @pytest.mark.parametrize("T", [1, 8, 64, 256, 1024])
 @pytest.mark.parametrize("path", [SP, DN])
 def test_llama4_like(T, path):
