@@ -318,10 +318,14 @@ static void launch_select(const RouteArgs &a, int nsplit, hipStream_t stream) {
   else launch_select_ro<V, false>(a, nsplit, stream);
 }
 
-// Tokens per logits block: 64 past one 16-token tile, except with at most
-// two 16-expert tiles, where 64-token blocks leave too few blocks (the
-// Llama-4-like router, 16 experts: 8 blocks at T = 64, 14.7 us).
-static int router_token_group(int T, int E) { return T <= 16 || E <= 32 ? 16 : 64; }
+// Tokens per logits block: 16, or 64 once 64-token blocks (with the full
+// split) still give two blocks per CU; fewer, larger blocks are slower
+// (the 16-expert Llama-4-like router on 8 of them at T = 64: 14.7 against
+// 5.8 us; the 64-expert OLMoE-like one at T = 64: 7.8 against 4.3 us).
+static int router_token_group(int T, int E) {
+  const long tiles64 = (long)((E + 15) / 16) * ((T + 63) / 64);
+  return T > 16 && tiles64 * kRouterSplits >= 512 ? 64 : 16;
+}
 
 // Split-K factor of the router GEMM: enough blocks to spread the router
 // matrix over many CUs (64 at decode batches; past one tile of tokens, two
