@@ -33,6 +33,16 @@ __device__ __forceinline__ unsigned xcd_logical_block() {
   return xcd * per + (xcd < rem ? xcd : rem) + slot;
 }
 
+// The GEMMs that feed MFMAs straight from weight registers (gate/up, the
+// packed down) raise their wave priority over each stage's MFMA run, so
+// that of two waves sharing a SIMD the one with matrix work ready keeps
+// issuing it (1024-token Llama-4-like shared expert, alternating runs:
+// gate/up 187-190 -> 175 us, packed down 109-110 -> 103-104 us; the
+// row-major down GEMMs, which stage weights through LDS, gained <= 1 %).
+#ifndef MOE_GEMM_SETPRIO
+#define MOE_GEMM_SETPRIO 1
+#endif
+
 // A compile-time int for the kernels' step lambdas.
 template <int V>
 struct SkIc {
@@ -168,6 +178,7 @@ __global__ __launch_bounds__(256, 2) void gateup_gemm_kernel(const void *__restr
     // Each token fragment is read from LDS one tile ahead of its MFMAs, so
     // the LDS latency overlaps the matrix work instead of stalling it (a
     // read past the item's last tile feeds no MFMA).
+    if (MOE_GEMM_SETPRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       u32x4 b = bfrag(k, 0);
@@ -180,6 +191,7 @@ __global__ __launch_bounds__(256, 2) void gateup_gemm_kernel(const void *__restr
         }
       }
     }
+    if (MOE_GEMM_SETPRIO) __builtin_amdgcn_s_setprio(0);
     if (more) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -338,6 +350,7 @@ __global__ __launch_bounds__(256, 2) void down_packed_kernel(const uint8_t *__re
     auto bfrag = [&](int k, int tl) {
       return *reinterpret_cast<const u32x4 *>(&xs[cur][(tl * 16 + r) * kGemmRowB + k * 64 + g * 16]);
     };
+    if (MOE_GEMM_SETPRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       u32x4 b = bfrag(k, 0);
@@ -351,6 +364,7 @@ __global__ __launch_bounds__(256, 2) void down_packed_kernel(const uint8_t *__re
         }
       }
     }
+    if (MOE_GEMM_SETPRIO) __builtin_amdgcn_s_setprio(0);
     if (more) {
 #pragma unroll
       for (int i = 0; i < SR; ++i)
