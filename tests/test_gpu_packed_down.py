@@ -158,3 +158,21 @@ def test_layer_class_pack_down():
     ys = m.forward(x, k, k, path=B.MOE_PATH_SPARSE, path_shared=DN)
     want = dev.run(x_host, k, B.MOE_PATH_SPARSE, k_sh=k, path_sh=DN, packed_down=True)
     np.testing.assert_array_equal(ys.cpu().numpy(), want["y"])
+
+
+NARROW = dict(n_experts=4, d_ff=128, top_k=2, norm_topk=False, n_shared=1, d_ff_shared=64,
+              zipf_bias=None, dtype="bf16")
+
+
+@pytest.mark.parametrize("H", [64, 192])
+@pytest.mark.parametrize("T", [1, 20, 300])
+def test_dense_packed_down_narrow(H, T):
+    # one or three 64-column blocks (16 columns per wave), d_ff 128 and 64
+    # (two and one 64-row stages), a single token to 150 per expert
+    inp, dev = _layer("olmoe-like", **dict(NARROW, hidden=H))
+    x = inp.tokens(T, 43)
+    say(f"[case] dense packed-down narrow H={H} T={T}")
+    got = dev.run(x, 13, DN, k_sh=40, packed_down=True)
+    compare_layer(inp, x, got, 13, k_sh=40)
+    ref = dev.run(x, 13, DN, k_sh=40)
+    assert rel_l2(got["y"], ref["y"]) < 1e-5
