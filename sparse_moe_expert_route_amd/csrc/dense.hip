@@ -6,6 +6,9 @@
 //   down_skinny   partial[pair, chunk] = hm . W_d over one K chunk, items of
 //                 <= 32 or 64 tokens (HBM-bound)
 //   down_wide     the same for items of <= 128 tokens
+//   down_packed   the same over a W_d copy packed in MFMA fragment order
+//                 (moe_pack_down): weights straight into registers, items of
+//                 32, 64 or 128 tokens
 //   union_*       the sparse path's packed-rows form: each active expert's
 //                 union of kept rows, for the two down GEMMs to gather
 //   combine       y[t] (+)= the token's partials in a fixed order
