@@ -127,8 +127,9 @@ __device__ __forceinline__ int nth_set_bit(uint64_t w, int n) {
 //       cnt_tc[t, c], and the unit that completes the token's top_k pairs
 //       sums their partials in slot order into y[t, cols] (+ the residual).
 //
-// Every wait is on blocks with lower linear ids (gate/up rows come first in
-// the grid), and each XCD dispatches its blocks in id order, so every waited
+// Every wait is on blocks with lower linear ids (the first n_active grid
+// rows are the gate/up blocks of the active slots, the down units follow
+// directly), and each XCD dispatches its blocks in id order, so every waited
 // tile is dispatched ahead of its waiters and never waits itself: no
 // deadlock at any occupancy.  Waits are bounded anyway (wait_count).  The
 // counters are zeroed by the kernel before this launch on the same stream.
@@ -136,7 +137,8 @@ __device__ __forceinline__ int nth_set_bit(uint64_t w, int n) {
 // expert, so the earliest experts' rows stream while later experts' gate/up
 // tiles still run; selection inside gate/up (VSEL): token-major).
 struct FusedArgs {
-  int gu_rows;           // grid rows of gate/up blocks; later rows are down units
+  int gu_rows;           // grid rows for gate/up blocks, min(E, P); the first
+                         // n_active of them run gate/up, the rest down units
   int ncb;               // column blocks per pair (H / SW)
   int npairs;            // T * top_k
   int k;                 // kept neurons per pair (0 < k < d_ff, k <= kFusedMaxK)
@@ -350,8 +352,9 @@ __device__ __forceinline__ void fused_down_unit(const FusedArgs &fa, const Route
 // grouping sorted by (expert, pair)).  The routing arrays in rv are then
 // written, not read, by this kernel.
 // FU (the fused tail above, FSW output columns per down unit, FV = d_ff / 64
-// activations per lane in its select): grid rows past fa.gu_rows are down
-// units; the gate/up blocks write h coherently and count their tiles.
+// activations per lane in its select): grid rows past the active-expert
+// count are down units; the gate/up blocks write h coherently and count
+// their tiles.
 template <bool BF16, int MT, int W, bool GO = false, bool PF = false, int VSEL = 0, bool FU = false,
           int FSW = 64, int FV = 16>
 __global__ __launch_bounds__(64 * W, MT == 1 ? 8 : 1) void gateup_swiglu_kernel(const void *__restrict__ xv,
@@ -364,9 +367,12 @@ __global__ __launch_bounds__(64 * W, MT == 1 ? 8 : 1) void gateup_swiglu_kernel(
   static_assert(VSEL == 0 || (MT == 1 && !GO), "selection runs in the one-tile form");
   static_assert(!FU || (MT == 1 && !GO && VSEL == 0), "the fused tail follows the one-tile SwiGLU form");
   if constexpr (FU) {
-    if ((int)blockIdx.y >= fa.gu_rows) {  // block-uniform: a down unit
+    // rows below the active-expert count are gate/up blocks, the rows after
+    // them down units (no row of inactive slots between the two)
+    const int nrows = min(rv.nact(), fa.gu_rows);
+    if ((int)blockIdx.y >= nrows) {  // block-uniform: a down unit
       fused_down_unit<BF16, FSW, FV, W>(fa, rv, hout, H, d_ff,
-                                        ((int)blockIdx.y - fa.gu_rows) * (int)gridDim.x +
+                                        ((int)blockIdx.y - nrows) * (int)gridDim.x +
                                             (int)blockIdx.x);
       return;
     }

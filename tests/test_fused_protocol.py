@@ -1,8 +1,9 @@
 """Host model of the fused decode-batch FFN launch's block protocol.
 
 The fused kernel (launch_ffn_fused in ffn.hip) is one grid: d_ff / 16
-columns, min(E, P) rows of gate/up blocks (slot s, neuron tile), then rows
-of down units (pair position q, column block c).  A gate/up block of an
+columns, min(E, P) + down_rows rows; the first n_active rows are gate/up
+blocks (slot s, neuron tile), the rows right after them down units (pair
+position q, column block c), the trailing rows empty.  A gate/up block of an
 active slot adds one to cnt_e[expert]; a down unit waits until cnt_e of its
 pair's expert reaches d_ff / 16, then adds one to cnt_tc[t, c]; the unit
 that brings it to top_k combines the token's partials.
@@ -36,8 +37,10 @@ def fused_cols(T, top_k, H):
 
 
 def grid(T, E, top_k, d_ff, H, ids):
-    """Blocks of the fused launch in linear id order: ("gu", expert or None)
-    or ("down", pair, token, column block)."""
+    """Blocks of the fused launch in linear id order: ("gu", expert), ("down",
+    pair, token, column block, expert) or ("none",).  The grid has min(E, P)
+    + down_rows rows; the first n_active rows run gate/up, the down units
+    follow directly, and the trailing rows are empty."""
     P = T * top_k
     nt = d_ff // 16
     gu_rows = min(E, P)
@@ -45,15 +48,16 @@ def grid(T, E, top_k, d_ff, H, ids):
     ncb = H // sw
     down_rows = -(-P * ncb // nt)
     active = sorted(set(int(e) for e in ids.ravel()))
+    nrows = min(len(active), gu_rows)
     # pairs grouped by expert, then pair id (the router's stable order)
     pairs = sorted(range(P), key=lambda p: (int(ids.ravel()[p]), p))
     blocks = []
     for y in range(gu_rows + down_rows):
         for x in range(nt):
-            if y < gu_rows:
-                blocks.append(("gu", active[y] if y < len(active) else None))
+            if y < nrows:
+                blocks.append(("gu", active[y]))
             else:
-                u = (y - gu_rows) * nt + x
+                u = (y - nrows) * nt + x
                 if u >= P * ncb:
                     blocks.append(("none",))
                     continue
