@@ -278,7 +278,10 @@ __device__ __forceinline__ void fused_down_unit(const FusedArgs &fa, const Route
       const uint32_t rbase = (uint32_t)e * (uint32_t)d_ff;
       int32_t *io = (fa.idx_out && c == 0) ? fa.idx_out + (size_t)p * k : nullptr;
       const int seg = lane * V;
-      if (io) {
+      // the per-value branches stay for 24 activations per lane: there the
+      // branch-free list made the fused launch slower (DeepSeek-V2-like
+      // layer, 16 tokens: 410 -> 423 us), at 16 per lane it is level or faster
+      if (io || V > 16) {
 #pragma unroll
         for (int i = 0; i < V; ++i) {
           const uint32_t key = bits[i] & 0x7fffffffu;
@@ -287,7 +290,7 @@ __device__ __forceinline__ void fused_down_unit(const FusedArgs &fa, const Route
             if (pos < k) {  // always: exactly k keys are kept
               srow[pos] = rbase + (uint32_t)(seg + i);
               scoef[pos] = w * __uint_as_float(bits[i]);
-              io[pos] = seg + i;
+              if (io) io[pos] = seg + i;
             }
             ++pos;
           }
