@@ -100,9 +100,11 @@ class DeviceLayer:
         return B.moe_expert_ffn_sparse if path == B.MOE_PATH_SPARSE else B.moe_expert_ffn_dense
 
     def run(self, x_host: np.ndarray, k: int, path: int, k_sh=None, path_sh=None,
-            poison_rows=None, poison_up=None, packed_down=False):
+            poison_rows=None, poison_up=None, packed_down=False, want_idx=True):
         """One layer call; returns host copies of routing, masks and y.
-        packed_down: the dense calls take W_d packed by moe_pack_down."""
+        packed_down: the dense calls take W_d packed by moe_pack_down.
+        want_idx=False: no active_idx_out (the kept lists stay internal; the
+        returned masks are then all -1)."""
         sh = self.inp.shape
         T = x_host.shape[0]
         x = to_dev(x_host)
@@ -118,7 +120,7 @@ class DeviceLayer:
         desc = self.desc
         if packed_down and path == B.MOE_PATH_DENSE:
             desc, wd = self.packed_down()[:2]
-        fn(desc, T, k, x, self.w[0], wu, wd, R, y, 0, idx if k > 0 else None, ws)
+        fn(desc, T, k, x, self.w[0], wu, wd, R, y, 0, idx if k > 0 and want_idx else None, ws)
         out = dict(T=T, k=k)
         idx_sh = None
         if self.desc_sh is not None:
@@ -132,7 +134,7 @@ class DeviceLayer:
             if packed_down and path_sh == B.MOE_PATH_DENSE:
                 ds, wd_sh = self.packed_down()[2:]
                 wsh = (wsh[0], wsh[1], wd_sh)
-            fs(ds, T, k_sh, x, *wsh, None, y, 1, idx_sh if k_sh > 0 else None, ws2)
+            fs(ds, T, k_sh, x, *wsh, None, y, 1, idx_sh if k_sh > 0 and want_idx else None, ws2)
             out["k_sh"] = k_sh
         torch.cuda.synchronize()
         out.update(ids=R.topk_ids.cpu().numpy()[:T], w=R.topk_w.cpu().numpy()[:T],
