@@ -155,6 +155,54 @@ struct FusedArgs {
 };
 constexpr int kFusedMaxK = 1024;
 
+// Pass 0 of the one-wave exact select (the exponent digit, bits 30..23 of
+// |h|) from registers instead of the LDS histogram: each lane counts its
+// keys in the eight binades at and below the wave's largest exponent in
+// packed 8-bit fields (at most V <= 32 per field), the wave adds them as
+// 16-bit fields with DPP, and the digit of the krem-th largest key follows
+// from the eight totals, as the histogram pass would find it.  Returns
+// false, with nothing written, when that key lies below those binades; the
+// histogram pass then runs.  (The histogram pass's LDS atomics cost ~1.3 us
+// per pass with eight selecting waves per block, in a stand-alone timing
+// copy, much the same however few lanes are active.)
+template <int V>
+__device__ __forceinline__ bool exp_digit_regs(const uint32_t (&bits)[V], int krem, uint32_t &tau,
+                                               uint32_t &pmask, int &krem_out, bool &whole) {
+  static_assert(V <= 32, "per-lane counts must fit 8 bits");
+  uint32_t emax = 0;
+#pragma unroll
+  for (int i = 0; i < V; ++i) emax = max(emax, (bits[i] & 0x7fffffffu) >> 23);
+  emax = wave_max_u32(emax);
+  uint32_t a = 0, b = 0;  // binades emax - 0 .. 3 and emax - 4 .. 7, a byte each
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+    const uint32_t d = emax - ((bits[i] & 0x7fffffffu) >> 23);  // >= 0
+    const uint32_t one = 1u << (8 * (d & 3u));
+    a += d < 4u ? one : 0u;
+    b += d - 4u < 4u ? one : 0u;  // d in 4 .. 7
+  }
+  const uint32_t w[4] = {(a & 0xffu) | ((a & 0xff00u) << 8), ((a >> 16) & 0xffu) | ((a >> 8) & 0xff0000u),
+                         (b & 0xffu) | ((b & 0xff00u) << 8), ((b >> 16) & 0xffu) | ((b >> 8) & 0xff0000u)};
+  int run = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t tot = (uint32_t)lane_value(wave_incl_scan((int)w[q]), 63);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int c = (int)((tot >> (16 * h)) & 0xffffu);
+      if (run + c >= krem) {  // wave-uniform; run < krem here
+        tau = (emax - (uint32_t)(2 * q + h)) << 23;
+        pmask = 0xffu << 23;
+        krem_out = krem - run;
+        whole = c == krem_out && tau != 0u;
+        return true;
+      }
+      run += c;
+    }
+  }
+  return false;
+}
+
 // The kept list of one lane's V activations (the exact select's tau, krem
 // and the lane's position and equal-key count before it), written to LDS at
 // base + position without a branch per value: every value is stored, a
@@ -222,9 +270,13 @@ __device__ __forceinline__ void fused_down_unit(const FusedArgs &fa, const Route
       uint32_t tau = 0, pmask = 0;
       int krem = k;
       bool whole = false;
+      // (the register pass only up to 16 activations per lane: at 24 it
+      // pushed this kernel past its 64 registers)
+      bool p0 = false;
+      if constexpr (V <= 16) p0 = exp_digit_regs<V>(bits, k, tau, pmask, krem, whole);
 #pragma unroll
       for (int pass = 0; pass < 4; ++pass) {
-        if (whole) continue;  // wave-uniform
+        if (whole || (pass == 0 && p0)) continue;  // wave-uniform
         const int shift = pass == 0 ? 23 : pass == 1 ? 15 : pass == 2 ? 7 : 0;
         const uint32_t dmask = pass == 3 ? 0x7fu : 0xffu;
 #pragma unroll
@@ -1345,9 +1397,10 @@ __global__ __launch_bounds__(1024) void down_topk_token_kernel(
     int krem = k;
     bool whole = false;
     int *hw = hist[wid];
+    const bool p0 = exp_digit_regs<V>(bits, k, tau, pmask, krem, whole);
 #pragma unroll
     for (int pass = 0; pass < 4; ++pass) {
-      if (whole) continue;  // wave-uniform
+      if (whole || (pass == 0 && p0)) continue;  // wave-uniform
       const int shift = pass == 0 ? 23 : pass == 1 ? 15 : pass == 2 ? 7 : 0;
       const uint32_t dmask = pass == 3 ? 0x7fu : 0xffu;
 #pragma unroll
