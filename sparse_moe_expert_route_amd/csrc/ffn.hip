@@ -837,6 +837,61 @@ __global__ __launch_bounds__(256) void neuron_topk_kernel(const float *__restric
   }
 }
 
+// exp_digit_regs over a block of NW waves that share one pair: the largest
+// exponent and the eight binade counts are combined across the waves
+// through xch (LDS, NW x 5 words, written once), two block barriers in all.
+template <int V, int NW>
+__device__ __forceinline__ bool exp_digit_regs_block(const uint32_t (&bits)[V], int krem,
+                                                     uint32_t (*xch)[5], uint32_t &tau,
+                                                     uint32_t &pmask, int &krem_out, bool &whole) {
+  static_assert(V <= 32, "per-lane counts must fit 8 bits");
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  uint32_t emax = 0;
+#pragma unroll
+  for (int i = 0; i < V; ++i) emax = max(emax, (bits[i] & 0x7fffffffu) >> 23);
+  emax = wave_max_u32(emax);
+  if (lane == 0) xch[wid][0] = emax;
+  __syncthreads();
+#pragma unroll
+  for (int ww = 0; ww < NW; ++ww) emax = max(emax, xch[ww][0]);
+  uint32_t a = 0, b = 0;  // binades emax - 0 .. 3 and emax - 4 .. 7, a byte each
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+    const uint32_t d = emax - ((bits[i] & 0x7fffffffu) >> 23);  // >= 0
+    const uint32_t one = 1u << (8 * (d & 3u));
+    a += d < 4u ? one : 0u;
+    b += d - 4u < 4u ? one : 0u;  // d in 4 .. 7
+  }
+  const uint32_t w[4] = {(a & 0xffu) | ((a & 0xff00u) << 8), ((a >> 16) & 0xffu) | ((a >> 8) & 0xff0000u),
+                         (b & 0xffu) | ((b & 0xff00u) << 8), ((b >> 16) & 0xffu) | ((b >> 8) & 0xff0000u)};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t tot = (uint32_t)lane_value(wave_incl_scan((int)w[q]), 63);
+    if (lane == 0) xch[wid][1 + q] = tot;  // 16-bit fields: at most d_ff per field
+  }
+  __syncthreads();
+  int run = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    uint32_t tot = 0;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) tot += xch[ww][1 + q];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int c = (int)((tot >> (16 * h)) & 0xffffu);
+      if (run + c >= krem) {  // block-uniform; run < krem here
+        tau = (emax - (uint32_t)(2 * q + h)) << 23;
+        pmask = 0xffu << 23;
+        krem_out = krem - run;
+        whole = c == krem_out && tau != 0u;
+        return true;
+      }
+      run += c;
+    }
+  }
+  return false;
+}
+
 // Register-resident variant for d_ff = 64 * V * NW: a block of NW waves per
 // pair, each lane holding V activations of one contiguous index segment
 // (lane-major within a wave, waves in order), so the kept list comes out in
@@ -859,6 +914,7 @@ __global__ __launch_bounds__(64 * NW) void neuron_topk_seg_kernel(const float *_
                                                                   int hm_bf16) {
   __shared__ int hist[NW][256];
   __shared__ int wtot[2][NW];
+  __shared__ uint32_t xch[NW][5];
   constexpr int SN = 64 * V * NW < kMaskStage ? 64 * V * NW : kMaskStage;  // k <= d_ff
   __shared__ int s_idx[SN + 64 * NW];  // + a spare slot per thread
   __shared__ float s_val[SN + 64 * NW];
@@ -884,9 +940,11 @@ __global__ __launch_bounds__(64 * NW) void neuron_topk_seg_kernel(const float *_
   int krem = k;
   bool whole = false;  // the last selected digit's bucket is kept entirely
   if (!keep_all && k > 0) {
+    const bool p0 = exp_digit_regs_block<V, NW>(bits, k, xch, tau, pmask, krem, whole);
 #pragma unroll
     for (int pass = 0; pass < 4; ++pass) {
-      if (whole) continue;  // block-uniform: every wave read the same histograms
+      // block-uniform: every wave read the same counts and histograms
+      if (whole || (pass == 0 && p0)) continue;
       const int shift = pass == 0 ? 23 : pass == 1 ? 15 : pass == 2 ? 7 : 0;
       const uint32_t dmask = pass == 3 ? 0x7fu : 0xffu;
 #pragma unroll
