@@ -75,32 +75,38 @@ constexpr int kGemmRowB = 128 + 16;         // LDS bytes per staged token row (+
 // that a grid of a few hundred waves still keeps enough bytes in flight
 // (three stages, always-on experts at 256 tokens: Llama-4-like 90.0 -> 81.3
 // us, the DeepSeek-V2-like pair 85.3 -> 76.6 us).
-template <bool BF16, bool GO = false, int NTW = 1, int DEPTH = 1>
+// MT = token tiles per work item (8: 128 tokens).  The few-item SwiGLU grids
+// take MT = 4 (64-token items): an expert past 64 tokens then streams its
+// weight tile once per 64 tokens, but such a grid (under 2 blocks per CU)
+// gains more from the extra blocks in flight.
+template <bool BF16, bool GO = false, int NTW = 1, int DEPTH = 1, int MT = 8>
 __global__ __launch_bounds__(256, 2) void gateup_gemm_kernel(const void *__restrict__ xv,
                                                              const void *__restrict__ wgv,
                                                              const void *__restrict__ wuv,
                                                              RouteView rv, int H, int d_ff,
                                                              float *__restrict__ hout) {
-  __shared__ __attribute__((aligned(16))) uint8_t xs[2][kGemmTok * kGemmRowB];
+  constexpr int TOK = 16 * MT;  // tokens per work item
+  constexpr int SR = MT / 2;     // staged 16-byte chunks per thread
+  __shared__ __attribute__((aligned(16))) uint8_t xs[2][TOK * kGemmRowB];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   int e, q0, ntok;
   const unsigned qb = xcd_logical_block();
   const int bx = (int)(qb % gridDim.x), by = (int)(qb / gridDim.x);
-  if (!find_item<kGemmTok>(rv, bx, e, q0, ntok)) return;  // block-uniform
+  if (!find_item<TOK>(rv, bx, e, q0, ntok)) return;  // block-uniform
   const int ntiles = (ntok + 15) >> 4;
   constexpr int EB = BF16 ? 2 : 4;
   constexpr int KS = BF16 ? 32 : 16;        // elements per k-step (64 bytes of a row)
   const int nsteps = H / KS;                // even: H is a multiple of 64
   const int nit = nsteps / 2;               // stages of two k-steps
 
-  // staging map: token rows tid / 8 + 32 i (i < 4), 16-byte chunk tid % 8.
+  // staging map: token rows tid / 8 + 32 i (i < SR), 16-byte chunk tid % 8.
   // Rows past the item's tokens stage the first token's row (every load is
   // issued unconditionally, so that the compiler's waits count the loads in
   // flight); they only feed accumulator rows that are never stored.
   const int srow = tid >> 3, schunk = tid & 7;
-  const uint8_t *xrow[4];
+  const uint8_t *xrow[SR];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < SR; ++i) {
     const int c = srow + 32 * i;
     xrow[i] = static_cast<const uint8_t *>(xv) +
               (size_t)(rv.pair_at(q0 + (c < ntok ? c : 0)) / rv.top_k) * H * EB + schunk * 16;
@@ -111,14 +117,14 @@ __global__ __launch_bounds__(256, 2) void gateup_gemm_kernel(const void *__restr
   const uint8_t *wg = static_cast<const uint8_t *>(wgv) + fbase;
   const uint8_t *wu = static_cast<const uint8_t *>(wuv) + fbase;
 
-  f32x4 accg[NTW][8], accu[NTW][8];
+  f32x4 accg[NTW][MT], accu[NTW][MT];
 #pragma unroll
   for (int j = 0; j < NTW; ++j)
 #pragma unroll
-    for (int tl = 0; tl < 8; ++tl) { accg[j][tl] = f32x4{0, 0, 0, 0}; accu[j][tl] = f32x4{0, 0, 0, 0}; }
+    for (int tl = 0; tl < MT; ++tl) { accg[j][tl] = f32x4{0, 0, 0, 0}; accu[j][tl] = f32x4{0, 0, 0, 0}; }
 
   constexpr int R = DEPTH == 1 ? 1 : DEPTH + 1;  // weight register sets
-  u32x4 stg[4], ag[R][NTW][2], au[R][NTW][2];
+  u32x4 stg[SR], ag[R][NTW][2], au[R][NTW][2];
   auto load_w = [&](int it, u32x4 (&g)[NTW][2], u32x4 (&u)[NTW][2]) {
 #pragma unroll
     for (int j = 0; j < NTW; ++j)
@@ -129,9 +135,9 @@ __global__ __launch_bounds__(256, 2) void gateup_gemm_kernel(const void *__restr
       }
   };
 #pragma unroll
-  for (int i = 0; i < 4; ++i) stg[i] = ld16(xrow[i]);
+  for (int i = 0; i < SR; ++i) stg[i] = ld16(xrow[i]);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < SR; ++i)
     *reinterpret_cast<u32x4 *>(&xs[0][(srow + 32 * i) * kGemmRowB + schunk * 16]) = stg[i];
   load_w(0, ag[0], au[0]);
 #pragma unroll
@@ -151,7 +157,7 @@ __global__ __launch_bounds__(256, 2) void gateup_gemm_kernel(const void *__restr
     u32x4 ng[NTW][2], nu[NTW][2];
     if (more) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) stg[i] = ld16(xrow[i] + (size_t)(it + 1) * 128);
+      for (int i = 0; i < SR; ++i) stg[i] = ld16(xrow[i] + (size_t)(it + 1) * 128);
       if (DEPTH == 1) load_w(it + 1, ng, nu);
     }
     if (DEPTH > 1 && (STEADY || it + DEPTH < nit))
@@ -186,9 +192,9 @@ __global__ __launch_bounds__(256, 2) void gateup_gemm_kernel(const void *__restr
     for (int k = 0; k < 2; ++k) {
       u32x4 b = bfrag(k, 0);
 #pragma unroll
-      for (int tl = 0; tl < 8; ++tl) {
+      for (int tl = 0; tl < MT; ++tl) {
         if (tl < ntiles) {  // block-uniform
-          const u32x4 bn = bfrag(k, tl < 7 ? tl + 1 : 7);
+          const u32x4 bn = bfrag(k, tl < MT - 1 ? tl + 1 : MT - 1);
           tile(k, tl, b);
           b = bn;
         }
@@ -197,7 +203,7 @@ __global__ __launch_bounds__(256, 2) void gateup_gemm_kernel(const void *__restr
     if (MOE_GEMM_SETPRIO) __builtin_amdgcn_s_setprio(0);
     if (more) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < SR; ++i)
         *reinterpret_cast<u32x4 *>(&xs[cur ^ 1][(srow + 32 * i) * kGemmRowB + schunk * 16]) = stg[i];
       if (DEPTH == 1) {
 #pragma unroll
@@ -230,10 +236,10 @@ __global__ __launch_bounds__(256, 2) void gateup_gemm_kernel(const void *__restr
     }
   }
 
-  // the pair ids of the lane's 8 token columns, all read before the stores
-  int prow[8];
+  // the pair ids of the lane's MT token columns, all read before the stores
+  int prow[MT];
 #pragma unroll
-  for (int tl = 0; tl < 8; ++tl) {
+  for (int tl = 0; tl < MT; ++tl) {
     const int c = tl * 16 + r;
     prow[tl] = rv.pair_at(q0 + (c < ntok ? c : 0));
   }
@@ -241,7 +247,7 @@ __global__ __launch_bounds__(256, 2) void gateup_gemm_kernel(const void *__restr
   for (int j = 0; j < NTW; ++j) {
     const int neuron0 = (nt + j) * 16 + 4 * g;
 #pragma unroll
-    for (int tl = 0; tl < 8; ++tl) {
+    for (int tl = 0; tl < MT; ++tl) {
       const int c = tl * 16 + r;
       if (tl < ntiles && c < ntok) {
         const int p = prow[tl];
@@ -1173,12 +1179,19 @@ void launch_gateup_gemm(const FfnArgs &a, const RouteView &rv, bool gate_only, h
                     (long)items * (a.d_ff / 128) >= 512;
   // a grid of under 2 blocks per CU keeps more weight stages in flight
   const bool deep = a.bf16 && !wide && (long)items * (a.d_ff / 64) < 512;
-  dim3 grid(items, a.d_ff / (wide ? 128 : 64));
+#ifndef MOE_GEMM_HALF_ITEMS
+#define MOE_GEMM_HALF_ITEMS 1
+#endif
+  const bool half = MOE_GEMM_HALF_ITEMS && deep && !gate_only;
+  dim3 grid(half ? n_items(a, kGemmTok / 2) : items, a.d_ff / (wide ? 128 : 64));
 #define MOE_GG(BF, GOV, N, D) \
   gateup_gemm_kernel<BF, GOV, N, D><<<grid, 256, 0, stream>>>(a.x, a.w_gate, a.w_up, rv, a.H, a.d_ff, a.h)
   if (a.bf16) {
     if (gate_only) { if (deep) MOE_GG(true, true, 1, MOE_GEMM_DEEP); else MOE_GG(true, true, 1, 1); }
     else if (wide) MOE_GG(true, false, 2, 1);
+    else if (half)
+      gateup_gemm_kernel<true, false, 1, MOE_GEMM_DEEP, 4><<<grid, 256, 0, stream>>>(a.x, a.w_gate, a.w_up,
+                                                                                  rv, a.H, a.d_ff, a.h);
     else if (deep) MOE_GG(true, false, 1, MOE_GEMM_DEEP);
     else MOE_GG(true, false, 1, 1);
   } else {
