@@ -234,6 +234,7 @@ __device__ __forceinline__ void fused_down_unit(const FusedArgs &fa, const Route
   constexpr int VEC = BF16 ? 8 : 4;
   constexpr int LPR = SW / VEC;
   static_assert(LPR <= 64 && 64 % LPR == 0, "a row run must fit one wave");
+  static_assert(V <= 16, "up to 16 activations per lane (d_ff <= 1024)");
   __shared__ uint32_t srow[kFusedMaxK + 64];  // + one spare slot per lane
   __shared__ float scoef[kFusedMaxK + 64];
   __shared__ int hist[256];
@@ -270,10 +271,7 @@ __device__ __forceinline__ void fused_down_unit(const FusedArgs &fa, const Route
       uint32_t tau = 0, pmask = 0;
       int krem = k;
       bool whole = false;
-      // (the register pass only up to 16 activations per lane: at 24 it
-      // pushed this kernel past its 64 registers)
-      bool p0 = false;
-      if constexpr (V <= 16) p0 = exp_digit_regs<V>(bits, k, tau, pmask, krem, whole);
+      const bool p0 = exp_digit_regs<V>(bits, k, tau, pmask, krem, whole);
 #pragma unroll
       for (int pass = 0; pass < 4; ++pass) {
         if (whole || (pass == 0 && p0)) continue;  // wave-uniform
@@ -330,10 +328,7 @@ __device__ __forceinline__ void fused_down_unit(const FusedArgs &fa, const Route
       const uint32_t rbase = (uint32_t)e * (uint32_t)d_ff;
       int32_t *io = (fa.idx_out && c == 0) ? fa.idx_out + (size_t)p * k : nullptr;
       const int seg = lane * V;
-      // the per-value branches stay for 24 activations per lane: there the
-      // branch-free list made the fused launch slower (DeepSeek-V2-like
-      // layer, 16 tokens: 410 -> 423 us), at 16 per lane it is level or faster
-      if (io || V > 16) {
+      if (io) {
 #pragma unroll
         for (int i = 0; i < V; ++i) {
           const uint32_t key = bits[i] & 0x7fffffffu;
@@ -1950,19 +1945,21 @@ static void launch_down_topk(const FfnArgs &a, const RouteView &rv, hipStream_t 
 }
 
 // ---- the fused decode-batch FFN: gate/up, masks, down and combine in one
-// launch, from kFusedMinTokens tokens.  Measured per layer call against the
-// separate gate/up, mask and down kernels (OLMoE-like, same box, runs
-// alternating): 73.7 vs 75.5 us at 6 tokens, 82.7 vs 84.3 us at 8 and
-// 103.8 vs 107.3 us at 16, but 36.7 vs 34.4 us at one token: there the down
-// units wait resident through the whole weight stream and their polls slow
-// it, and the per-token down kernel that selects its own masks is as fast
-// as the units without the wait (34.3 us, measured and dropped).
-constexpr int kFusedMinTokens = 5;
+// launch, from kFusedMinTokens tokens and for d_ff up to 1024.  Measured per
+// layer call against the separate gate/up, mask and down kernels (same box,
+// runs alternating), OLMoE-like: 74.7 vs 75.7 us at 6 tokens, 83.5 vs 84.6 at
+// 8, 103.1 vs 106.7 at 16, level at 5, slower below (3 tokens: 58.4 vs 52.8);
+// Qwen3-MoE-like: 52.6 vs 47.5 at 5, level at 6, 54.0 vs 56.2 at 8, 64.5 vs
+// 68.3 at 16.  Below that the down units wait resident through the whole
+// weight stream and their polls slow it.  At d_ff 1536 (DeepSeek-V2-like,
+// 24 activations per lane) the separate kernels were as fast or faster at
+// every batch (5 tokens: 191.5 vs 196.5 us, 16: 407.2 vs 412.1).
+constexpr int kFusedMinTokens = 6;
 static bool tail_units_shape_ok(const FfnArgs &a) {
   const int V = a.d_ff / 64;
-  // d_ff 512, 768, 1024, 1536 (at 2048 the fused kernel spills in its loop)
+  // d_ff 512, 768, 1024 (at 2048 the fused kernel spills in its loop)
   return !a.implicit && a.T >= 1 && a.T <= kFusedMaxTokens && a.top_k <= 16 &&
-         a.d_ff % 256 == 0 && (V == 8 || V == 12 || V == 16 || V == 24) &&
+         a.d_ff % 256 == 0 && (V == 8 || V == 12 || V == 16) &&
          a.k_keep > 0 && a.k_keep < a.d_ff && a.k_keep <= kFusedMaxK && a.H % 64 == 0 &&
          a.fpart != nullptr &&
          // the gate/up blocks find the counters right after h
@@ -1996,8 +1993,7 @@ static void fused_v(const FfnArgs &a, const RouteView &rv, const FusedArgs &fa, 
   switch (a.d_ff / 64) {
     case 8: fused_inst<BF, SWV, 8>(a, rv, fa, grid, stream); break;
     case 12: fused_inst<BF, SWV, 12>(a, rv, fa, grid, stream); break;
-    case 16: fused_inst<BF, SWV, 16>(a, rv, fa, grid, stream); break;
-    default: fused_inst<BF, SWV, 24>(a, rv, fa, grid, stream); break;
+    default: fused_inst<BF, SWV, 16>(a, rv, fa, grid, stream); break;
   }
 }
 template <bool BF>

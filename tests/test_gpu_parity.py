@@ -71,6 +71,14 @@ def test_olmoe_like_sparse(T, s):
     run_case("olmoe-like", T, s, SP)
 
 
+@pytest.mark.parametrize("name,T", [("olmoe-like", 5), ("olmoe-like", 6),
+                                    ("qwen3-moe-like", 5), ("qwen3-moe-like", 6)])
+def test_fused_launch_boundary(name, T):
+    # the last batch on the separate gate/up, mask and down kernels and the
+    # first on the fused FFN launch
+    run_case(name, T, 0.9, SP)
+
+
 @pytest.mark.parametrize("T", [1, 16])
 def test_olmoe_like_dense(T):
     run_case("olmoe-like", T, 0.9, DN)

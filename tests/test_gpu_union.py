@@ -7,7 +7,9 @@ projection gathers each active expert's union of kept W_d rows once and
 multiplies it with all of that expert's tokens (the page's fused
 projection over the active neurons), instead of streaming every token's
 kept rows on its own.
-These tests check which calls take that form, its parity with the oracle at
+These tests check which calls take that form (and, beside it, which take
+the fused FFN launch: 6-16 tokens at d_ff up to 1024), its parity with the
+oracle at
 the edges of the union (k = 1, union sizes on and off the 64-row stage,
 k = d_ff), that rows outside an expert's union are never read, and its
 residual epilogue.  The workload parity tests (test_gpu_parity.py) cover it
@@ -98,6 +100,22 @@ def test_union_taken_where_expected(name, T, routed, want):
     assert ("union_rows" in names) == want, names
     if want:
         assert "down_rows" not in names and "fused_ffn" not in names, names
+
+
+@pytest.mark.parametrize("name,T,want", [
+    ("olmoe-like", 5, False),         # below the fused launch's batches
+    ("olmoe-like", 6, True),
+    ("olmoe-like", 16, True),
+    ("qwen3-moe-like", 6, True),      # d_ff 768
+    ("deepseek-v2-like", 8, False),   # d_ff 1536: the separate kernels
+    ("deepseek-v2-like", 16, False),
+])
+def test_fused_launch_taken_where_expected(name, T, want):
+    inp, dev = _layer(name)
+    k = O.keep_count(0.9, inp.shape.d_ff)
+    say(f"[case] fused launch {name} T={T}")
+    names = _stages_of_ffn(dev, T, k, inp.tokens(T, 5), True)
+    assert ("fused_ffn" in names) == want, names
 
 
 @pytest.mark.parametrize("k", [1, 5, 63, 64, 65, 128, 191, 192])
