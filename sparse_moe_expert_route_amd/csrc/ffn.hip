@@ -1906,13 +1906,21 @@ static void launch_down_token(const FfnArgs &a, const RouteView &rv, const int32
 }
 
 // Whether the kernel that selects inside the down projection takes this
-// call: the smallest batches (at T = 16 the repeated selects cost as much as
-// the mask launch they save), one wave per pair, d_ff / 64 values per lane
-// (a multiple of 4 up to 32), the token's kept lists in one LDS stage.
-constexpr int kFusedTopkMaxTokens = 4;
+// call: one wave per pair, d_ff / 64 values per lane (a multiple of 4 up to
+// 32), the token's kept lists in one LDS stage, and the batches where its
+// repeated selects (every column block of a token selects again) cost less
+// than the mask launch they save.  Per layer call against the mask and down
+// kernels (alternating runs on one box): OLMoE-like 5 tokens 68.3 vs 65.8
+// us, Qwen3-MoE-like 47.8 vs 45.1; up to 8 tokens it also beats the fused
+// launch (below).  With 24 values per lane (DeepSeek-V2-like, d_ff 1536)
+// it wins up to 3 tokens (1: 84.0 vs 86.5 us) and loses from 4 (179.0 vs
+// 175.7; 16: 417.5 vs 408.4).
+constexpr int kTopkMaxTokens = 8;      // d_ff <= 1024
+constexpr int kTopkMaxTokensWide = 3;  // d_ff 1280 .. 2048
 static bool fused_topk_ok(const FfnArgs &a) {
   const int V = a.d_ff / 64;
-  return a.T <= kFusedTopkMaxTokens && a.top_k <= kDownWaves && a.d_ff % 256 == 0 && V <= 32 &&
+  return a.T <= (V <= 16 ? kTopkMaxTokens : kTopkMaxTokensWide) && a.top_k <= kDownWaves &&
+         a.d_ff % 256 == 0 && V <= 32 &&
          a.k_keep > 0 && a.k_keep < a.d_ff && a.top_k * a.k_keep <= kDownStage;
 }
 
@@ -1946,15 +1954,16 @@ static void launch_down_topk(const FfnArgs &a, const RouteView &rv, hipStream_t 
 
 // ---- the fused decode-batch FFN: gate/up, masks, down and combine in one
 // launch, from kFusedMinTokens tokens and for d_ff up to 1024.  Measured per
-// layer call against the separate gate/up, mask and down kernels (same box,
-// runs alternating), OLMoE-like: 74.7 vs 75.7 us at 6 tokens, 83.5 vs 84.6 at
-// 8, 103.1 vs 106.7 at 16, level at 5, slower below (3 tokens: 58.4 vs 52.8);
-// Qwen3-MoE-like: 52.6 vs 47.5 at 5, level at 6, 54.0 vs 56.2 at 8, 64.5 vs
-// 68.3 at 16.  Below that the down units wait resident through the whole
-// weight stream and their polls slow it.  At d_ff 1536 (DeepSeek-V2-like,
-// 24 activations per lane) the separate kernels were as fast or faster at
-// every batch (5 tokens: 191.5 vs 196.5 us, 16: 407.2 vs 412.1).
-constexpr int kFusedMinTokens = 6;
+// layer call against the separate kernels that select inside the down
+// projection (same box, runs alternating), OLMoE-like: 73.9 vs 71.9 us at 6
+// tokens, 83.1 vs 82.1 at 8, 95.4 vs 99.7 at 12, 103.4 vs 104.5 at 16;
+// Qwen3-MoE-like: 50.2 vs 47.4 at 6, 54.1 vs 53.6 at 8, 56.5 vs 58.2 at 12,
+// 64.4 vs 65.8 at 16.  Below that the down units wait resident through the
+// whole weight stream and their polls slow it.  At d_ff 1536
+// (DeepSeek-V2-like, 24 activations per lane) the separate mask and down
+// kernels were as fast or faster at every batch (5 tokens: 191.5 vs 196.5
+// us, 16: 407.2 vs 412.1).
+constexpr int kFusedMinTokens = 9;
 static bool tail_units_shape_ok(const FfnArgs &a) {
   const int V = a.d_ff / 64;
   // d_ff 512, 768, 1024 (at 2048 the fused kernel spills in its loop)

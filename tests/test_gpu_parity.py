@@ -71,11 +71,13 @@ def test_olmoe_like_sparse(T, s):
     run_case("olmoe-like", T, s, SP)
 
 
-@pytest.mark.parametrize("name,T", [("olmoe-like", 5), ("olmoe-like", 6),
-                                    ("qwen3-moe-like", 5), ("qwen3-moe-like", 6)])
-def test_fused_launch_boundary(name, T):
-    # the last batch on the separate gate/up, mask and down kernels and the
-    # first on the fused FFN launch
+@pytest.mark.parametrize("name,T", [("olmoe-like", 8), ("olmoe-like", 9),
+                                    ("qwen3-moe-like", 8), ("qwen3-moe-like", 9),
+                                    ("deepseek-v2-like", 3), ("deepseek-v2-like", 4)])
+def test_dispatch_boundaries(name, T):
+    # the last batch that selects inside the down kernel and the first on
+    # the fused FFN launch (d_ff up to 1024), or on the mask and down
+    # kernels (d_ff 1536)
     run_case(name, T, 0.9, SP)
 
 

@@ -8,7 +8,7 @@ multiplies it with all of that expert's tokens (the page's fused
 projection over the active neurons), instead of streaming every token's
 kept rows on its own.
 These tests check which calls take that form (and, beside it, which take
-the fused FFN launch: 6-16 tokens at d_ff up to 1024), its parity with the
+the fused FFN launch: 9-16 tokens at d_ff up to 1024), its parity with the
 oracle at
 the edges of the union (k = 1, union sizes on and off the 64-row stage,
 k = d_ff), that rows outside an expert's union are never read, and its
@@ -103,10 +103,10 @@ def test_union_taken_where_expected(name, T, routed, want):
 
 
 @pytest.mark.parametrize("name,T,want", [
-    ("olmoe-like", 5, False),         # below the fused launch's batches
-    ("olmoe-like", 6, True),
+    ("olmoe-like", 8, False),         # below the fused launch's batches
+    ("olmoe-like", 9, True),
     ("olmoe-like", 16, True),
-    ("qwen3-moe-like", 6, True),      # d_ff 768
+    ("qwen3-moe-like", 9, True),      # d_ff 768
     ("deepseek-v2-like", 8, False),   # d_ff 1536: the separate kernels
     ("deepseek-v2-like", 16, False),
 ])
