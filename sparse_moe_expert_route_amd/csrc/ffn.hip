@@ -1099,15 +1099,17 @@ __global__ __launch_bounds__(64 * NW) void neuron_topk_seg_kernel(const float *_
 // and dotted with it; each row's partial is then summed over the wave in a
 // fixed DPP order and over the waves in wave order (two waves instead of
 // one: OLMoE-like split layer 38.6 -> 37.1 us at one token, 87.0 -> 85.9 us
-// at 16; up-rows kernel 8.5 -> 6.8 us at one token).  The kept coefficient
+// at 16, up-rows kernel 8.5 -> 6.8 us at one token; four waves of 1 KB
+// segments: up-rows 6.9 -> 6.5 us).  The kept coefficient
 // (w * silu(g_j), from the mask) is multiplied by u_j in place, giving the
 // down projection's w * h_j.
 constexpr int kUpRows = 8;
 
 // Rows i0 .. i0 + kUpRows - 1 (those below n) of pair p's kept list: ids
 // idx_row[i], coefficients coef_row[i] multiplied in place by u = W_u row . x.
-// NWU waves share the rows: wave w takes the 2 KB row segments w, w + NWU,
-// ...; the per-wave sums meet in LDS and are added in wave order (a fixed
+// NWU waves share the rows: wave w takes the row segments w, w + NWU, ...
+// (2 KB, or 1 KB from four waves); the per-wave sums meet in LDS and are
+// added in wave order (a fixed
 // order, so reruns give the same bits).  Called by all NWU waves alike.
 template <bool BF16, int NWU = 1>
 __device__ __forceinline__ void up_rows_group(const void *__restrict__ wuv,
@@ -1132,12 +1134,14 @@ __device__ __forceinline__ void up_rows_group(const void *__restrict__ wuv,
   float acc[kUpRows];
 #pragma unroll
   for (int r = 0; r < kUpRows; ++r) acc[r] = 0.f;
-  // two 1 KB steps of every row in flight at once (row_bytes is a multiple
-  // of 128, so a step may be partial: lanes past the row end load nothing)
-  for (int off0 = 2048 * wid; off0 < row_bytes; off0 += 2048 * NWU) {
-    u32x4 xq[2], q[2][kUpRows];
+  // ST 1 KB steps of every row in flight at once per wave: two with one or
+  // two waves, one with four (row_bytes is a multiple of 128, so a step may
+  // be partial: lanes past the row end load nothing)
+  constexpr int ST = NWU >= 4 ? 1 : 2;
+  for (int off0 = 1024 * ST * wid; off0 < row_bytes; off0 += 1024 * ST * NWU) {
+    u32x4 xq[ST], q[ST][kUpRows];
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
+    for (int h2 = 0; h2 < ST; ++h2) {
       const int off = off0 + 1024 * h2 + lane * 16;
       const bool in = off < row_bytes;
       xq[h2] = in ? ld16(xr + off) : u32x4{0, 0, 0, 0};
@@ -1146,7 +1150,7 @@ __device__ __forceinline__ void up_rows_group(const void *__restrict__ wuv,
         q[h2][r] = in && i0 + r < n ? ld16(rows[r] + off) : u32x4{0, 0, 0, 0};
     }
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
+    for (int h2 = 0; h2 < ST; ++h2) {
 #pragma unroll
       for (int r = 0; r < kUpRows; ++r) {
         float a = 0.f;
@@ -1194,7 +1198,7 @@ __device__ __forceinline__ void up_rows_group(const void *__restrict__ wuv,
 // Fixed count k per pair (top-k masks): block (p, g) takes rows 8 g ...
 // with kUpWaves waves splitting each row's bytes.
 #ifndef MOE_UP_WAVES
-#define MOE_UP_WAVES 2
+#define MOE_UP_WAVES 4
 #endif
 constexpr int kUpWaves = MOE_UP_WAVES;
 template <bool BF16>
