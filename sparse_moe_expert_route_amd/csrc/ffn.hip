@@ -1948,12 +1948,16 @@ static void launch_down_token(const FfnArgs &a, const RouteView &rv, const int32
 // us, Qwen3-MoE-like 47.8 vs 45.1; up to 8 tokens it also beats the fused
 // launch (below).  With 24 values per lane (DeepSeek-V2-like, d_ff 1536)
 // it wins up to 3 tokens (1: 84.0 vs 86.5 us) and loses from 4 (179.0 vs
-// 175.7; 16: 417.5 vs 408.4).
-constexpr int kTopkMaxTokens = 8;      // d_ff <= 1024
-constexpr int kTopkMaxTokensWide = 3;  // d_ff 1280 .. 2048
+// 175.7; 16: 417.5 vs 408.4).  With at most 12 values per lane the select is
+// cheap enough past the fused launch's batches too (Qwen3-MoE-like, d_ff
+// 768: 17 tokens 68.7 vs 66.0 us, 32: 85.4 vs 83.0, level at 48 and 64).
+constexpr int kTopkMaxTokensNarrow = 32;  // d_ff <= 768 (9-16 tokens: the fused launch)
+constexpr int kTopkMaxTokens = 8;         // d_ff 1024
+constexpr int kTopkMaxTokensWide = 3;     // d_ff 1280 .. 2048
 static bool fused_topk_ok(const FfnArgs &a) {
   const int V = a.d_ff / 64;
-  return a.T <= (V <= 16 ? kTopkMaxTokens : kTopkMaxTokensWide) && a.top_k <= kDownWaves &&
+  const int tmax = V <= 12 ? kTopkMaxTokensNarrow : V <= 16 ? kTopkMaxTokens : kTopkMaxTokensWide;
+  return a.T <= tmax && a.top_k <= kDownWaves &&
          a.d_ff % 256 == 0 && V <= 32 &&
          a.k_keep > 0 && a.k_keep < a.d_ff && a.top_k * a.k_keep <= kDownStage;
 }

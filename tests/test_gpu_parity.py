@@ -73,11 +73,13 @@ def test_olmoe_like_sparse(T, s):
 
 @pytest.mark.parametrize("name,T", [("olmoe-like", 8), ("olmoe-like", 9),
                                     ("qwen3-moe-like", 8), ("qwen3-moe-like", 9),
+                                    ("qwen3-moe-like", 17), ("qwen3-moe-like", 33),
                                     ("deepseek-v2-like", 3), ("deepseek-v2-like", 4)])
 def test_dispatch_boundaries(name, T):
     # the last batch that selects inside the down kernel and the first on
     # the fused FFN launch (d_ff up to 1024), or on the mask and down
-    # kernels (d_ff 1536)
+    # kernels (d_ff 1536); past 16 tokens at d_ff 768 the down kernel
+    # selects again, up to 32
     run_case(name, T, 0.9, SP)
 
 

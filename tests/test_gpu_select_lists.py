@@ -6,8 +6,9 @@ also asked for the kept ids (active_idx_out), which keeps the per-value
 branches.  So every case here runs twice, with and without the ids, and
 the outputs must agree bit for bit; the run with ids is compared with the
 oracle.  Cases: the one-wave select of the down kernel at 1-8 tokens (1-3
-at d_ff 1536), the fused FFN's down units at 9-16 tokens (12 and 16
-activations per lane), the mask kernel's eight-wave select (one routed
+at d_ff 1536, also 17-32 at d_ff 768), the fused FFN's down units at 9-16
+tokens (12 and 16 activations per lane), the mask kernel's eight-wave
+select (one routed
 slot per token over experts of d_ff 8192, a shared expert of d_ff 4096:
 1-4 tokens, keep fractions 0.5 and 0.01), and an all-zero token there,
 whose kept lists must be the lowest indices.
